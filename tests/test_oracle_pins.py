@@ -1,0 +1,385 @@
+"""Pins of the CPU oracle against things other than itself (no GPU needed).
+
+Each test ties one oracle function to an independent route: numpy's own
+binary16 conversion, numpy ``unpackbits`` for the bitstream order, exact
+rationals, brute-force sorting, a dense fp64 numpy evaluation of every
+expert, closed forms and invariants, and the hand-worked blocks in
+``tests/golden/blocks.json``.
+"""
+import json
+import math
+import os
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import moe_inputs as mi
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# independent decoders used only by the pins
+# ---------------------------------------------------------------------------
+def np_decode(canon, rows, cols, bits):
+    """Dequantised fp64 weights via numpy's fp16 view and unpackbits (bit order 'little')."""
+    bb = 2 + 4 * bits
+    blk = np.asarray(canon, dtype=np.uint8).reshape(rows, cols // 32, bb)
+    scale = np.ascontiguousarray(blk[..., :2]).view(np.float16)[..., 0].astype(np.float64)
+    bitarr = np.unpackbits(blk[..., 2:], axis=-1, bitorder="little").astype(np.int64)
+    q = (bitarr.reshape(rows, cols // 32, 32, bits) * (1 << np.arange(bits))).sum(-1)
+    c = q - (1 << (bits - 1))
+    return (scale[..., None] * c).reshape(rows, cols), c.reshape(rows, cols)
+
+
+def np_expert(canon, d, I, bits):
+    bb = 2 + 4 * bits
+    g = I * (d // 32) * bb
+    dn = d * (I // 32) * bb
+    c = np.asarray(canon, dtype=np.uint8)
+    Wg = np_decode(c[:g], I, d, bits)[0]
+    Wu = np_decode(c[g:2 * g], I, d, bits)[0]
+    Wd = np_decode(c[2 * g:2 * g + dn], d, I, bits)[0]
+    return Wg, Wu, Wd
+
+
+def np_ffn(Wg, Wu, Wd, x):
+    g = Wg @ x
+    u = Wu @ x
+    h = g / (1.0 + np.exp(-g)) * u
+    return Wd @ h
+
+
+# ---------------------------------------------------------------------------
+# fp16
+# ---------------------------------------------------------------------------
+def test_half_to_double_all_patterns(orc):
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = pats.view(np.float16).astype(np.float64)
+    got = np.array([orc.half_to_double(int(p)) for p in pats])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_double_to_half_matches_numpy(orc):
+    g = np.random.default_rng(1)
+    vals = np.concatenate([
+        g.standard_normal(4000) * 10.0 ** g.integers(-9, 6, 4000),
+        # exact ties between neighbouring fp16 values, normal and subnormal
+        (np.arange(0, 2048, dtype=np.float64) + 0.5) * 2.0 ** -24,
+        (np.arange(1024, 2048, dtype=np.float64) + 0.5) * 2.0 ** -10,
+        [65504.0, 65519.99, 65520.0, 1e6, -65520.0, 2.0 ** -25, 2.0 ** -25 * 1.0000001, 0.0, -0.0],
+    ])
+    ref = vals.astype(np.float16).view(np.uint16)
+    got = np.array([orc.double_to_half(float(v)) for v in vals], dtype=np.uint16)
+    assert np.array_equal(got, ref)
+
+
+# ---------------------------------------------------------------------------
+# unpack
+# ---------------------------------------------------------------------------
+def test_golden_blocks(orc):
+    with open(os.path.join(GOLDEN, "blocks.json")) as f:
+        cases = json.load(f)["cases"]
+    for case in cases:
+        blk = bytes.fromhex(case["bytes"].replace(" ", ""))
+        codes, scale = orc.unpack_block(blk, case["bits"])
+        assert scale == case["scale"], case["note"]
+        assert codes.tolist() == case["codes"], case["note"]
+
+
+def test_unpack_2bit_all_bytes(orc):
+    # every byte value at every code position: 256 blocks x 8 positions
+    blocks = np.zeros((256 * 8, 10), dtype=np.uint8)
+    blocks[:, 0:2] = np.frombuffer(np.float16(1.0).tobytes(), dtype=np.uint8)
+    for pos in range(8):
+        blocks[pos * 256:(pos + 1) * 256, 2 + pos] = np.arange(256)
+    rows = blocks.shape[0]
+    codes, scales = orc.unpack_matrix(blocks.reshape(-1), rows, 32, 2)
+    _, ref = np_decode(blocks.reshape(-1), rows, 32, 2)
+    assert np.array_equal(codes, ref)
+    assert np.all(scales == 1.0)
+    assert set(np.unique(codes).tolist()) == {-2, -1, 0, 1}
+
+
+@pytest.mark.slow
+def test_unpack_3bit_all_24bit_groups(orc):
+    # all 2^24 three-byte groups (eight 3-bit codes each), four groups per block
+    n = 1 << 24
+    v = np.arange(n, dtype=np.uint32)
+    grp = np.stack([v & 0xFF, (v >> 8) & 0xFF, v >> 16], axis=1).astype(np.uint8).reshape(-1, 12)
+    nblk = grp.shape[0]
+    chunk = 1 << 19
+    for c0 in range(0, nblk, chunk):
+        g = grp[c0:c0 + chunk]
+        blocks = np.zeros((g.shape[0], 14), dtype=np.uint8)
+        blocks[:, 0:2] = np.frombuffer(np.float16(-0.5).tobytes(), dtype=np.uint8)
+        blocks[:, 2:] = g
+        codes, scales = orc.unpack_matrix(blocks.reshape(-1), g.shape[0], 32, 3)
+        _, ref = np_decode(blocks.reshape(-1), g.shape[0], 32, 3)
+        assert np.array_equal(codes, ref)
+        assert np.all(scales == -0.5)
+
+
+def test_unpack_generated_matrices(orc):
+    for bits in (2, 3):
+        wl = mi.small(mi.WORKLOADS["tiny"], bits=bits)
+        ex = mi.expert_canon(wl, 0, 7).numpy()
+        gate, up, down = orc.split_expert(ex, wl.d, wl.I, bits)
+        for canon, rows, cols in ((gate, wl.I, wl.d), (up, wl.I, wl.d), (down, wl.d, wl.I)):
+            codes, _ = orc.unpack_matrix(canon, rows, cols, bits)
+            w = orc.dequant_matrix(canon, rows, cols, bits)
+            wref, cref = np_decode(canon, rows, cols, bits)
+            assert np.array_equal(codes, cref)
+            assert np.array_equal(w, wref)
+            lo, hi = -(1 << (bits - 1)), (1 << (bits - 1)) - 1
+            assert codes.min() == lo and codes.max() == hi
+
+
+def test_dequant_all_scales_exact(orc):
+    # every finite positive fp16 scale times every 3-bit code; the product of
+    # an 11-bit significand and |c| <= 4 is exact in fp64 and in fp32
+    s = np.arange(1, 0x7C00, dtype=np.uint16)
+    blocks = np.zeros((s.size, 14), dtype=np.uint8)
+    blocks[:, 0] = s & 0xFF
+    blocks[:, 1] = s >> 8
+    blocks[:, 2:] = np.frombuffer(bytes.fromhex("88c6fa" * 4), dtype=np.uint8)
+    w = orc.dequant_matrix(blocks.reshape(-1), s.size, 32, 3)
+    sf = s.view(np.float16).astype(np.float64)
+    codes = np.tile(np.arange(-4, 4), 4)
+    exact = [Fraction(float(a)) * int(c) for a, c in zip(sf[::997], codes[:1].repeat(1))]
+    assert np.array_equal(w, sf[:, None] * codes[None, :])
+    assert all(Fraction(float(v)) == e for v, e in zip(w[::997, 0], exact))
+    assert np.array_equal(w.astype(np.float32).astype(np.float64), w)
+
+
+# ---------------------------------------------------------------------------
+# exp64
+# ---------------------------------------------------------------------------
+def test_exp64_constants_are_nearest(orc):
+    coeff = orc.exp64_coefficients()
+    for i, c in enumerate(coeff):
+        assert c == float(Fraction(1, math.factorial(i))), i
+    getcontext().prec = 60
+    ln2 = Decimal(2).ln()
+    hi, lo, inv = orc.exp64_ln2_parts()
+    assert hi == float(ln2)
+    assert lo == float(ln2 - Decimal(hi))
+    assert inv == float(1 / ln2)
+
+
+def test_exp64_vs_libm(orc):
+    g = np.random.default_rng(2)
+    z = np.concatenate([-g.random(3000) * 745.0, -g.random(2000) * 30.0, -g.random(1000) * 1e-3,
+                        [0.0, -0.0, -1e-300, -708.0, -744.0, -1.0, -math.log(2.0) * 10]])
+    got = orc.exp64(z)
+    ref = np.exp(z)
+    ulp = np.spacing(np.abs(ref))
+    assert np.all(np.abs(got - ref) <= ulp * 1.0 + 0.0)
+    assert orc.exp64(np.array([0.0]))[0] == 1.0
+    assert orc.exp64(np.array([-2000.0]))[0] == 0.0
+
+
+# ---------------------------------------------------------------------------
+# router, top-k, gate weights
+# ---------------------------------------------------------------------------
+def test_router_vs_numpy_and_one_hot(orc):
+    wl = mi.WORKLOADS["tiny"]
+    W, _ = mi.router(wl, 0)
+    bias = np.linspace(-1, 1, wl.E).astype(np.float32)
+    x = mi.activations(wl, T=9)
+    got = orc.router_logits(x, W, bias)
+    ref = (x.astype(np.float64) @ W.astype(np.float64).T + bias.astype(np.float64)).astype(np.float32)
+    diff = np.abs(got.astype(np.float64) - ref.astype(np.float64))
+    assert np.all(diff <= np.spacing(np.abs(ref)).astype(np.float64))
+    assert np.mean(got == ref) > 0.99
+    # one-hot activation picks out a column of W plus the bias exactly
+    xo = np.zeros((wl.d, wl.d), dtype=np.float32)
+    np.fill_diagonal(xo, 1.0)
+    lo = orc.router_logits(xo[:40], W, bias)
+    exact = (W[:, :40].T.astype(np.float64) + bias.astype(np.float64)).astype(np.float32)
+    assert np.array_equal(lo, exact)
+
+
+def _brute_topk(l, k):
+    order = sorted(range(len(l)), key=lambda e: (-float(l[e]), e))
+    return order[:k]
+
+
+def test_topk_brute_force_and_ties(orc):
+    g = np.random.default_rng(3)
+    cases = [g.standard_normal((50, 64)).astype(np.float32),
+             g.integers(0, 3, (200, 40)).astype(np.float32),       # heavy ties
+             np.where(g.random((50, 33)) < 0.5, -0.0, 0.0).astype(np.float32),
+             mi.direct_logits(mi.WORKLOADS["layer_t1"], T=64)]
+    for l in cases:
+        for k in (1, 2, 7, min(10, l.shape[1])):
+            idx, w = orc.topk(l, k)
+            for t in range(l.shape[0]):
+                assert idx[t].tolist() == _brute_topk(l[t], k)
+            assert np.all(w > 0)
+            assert np.all(np.abs(w.astype(np.float64).sum(1) - 1.0) <= k * 2.0 ** -24)
+
+
+def test_gate_weight_closed_forms(orc):
+    g = np.random.default_rng(4)
+    l = g.standard_normal((400, 20)).astype(np.float32) * 3
+    idx, w = orc.topk(l, 2)
+    l0 = l[np.arange(400), idx[:, 0]].astype(np.float64)
+    l1 = l[np.arange(400), idx[:, 1]].astype(np.float64)
+    w0 = 1.0 / (1.0 + np.exp(l1 - l0))
+    assert np.all(np.abs(w[:, 0] - w0) <= np.spacing(w0.astype(np.float32)))
+    # all-equal logits: every weight is fp32(1/k)
+    for k in (1, 3, 7, 10):
+        le = np.full((3, 16), 0.25, dtype=np.float32)
+        _, we = orc.topk(le, k)
+        assert np.all(we == np.float32(1.0 / k))
+
+
+def test_topk_rejects_nonfinite(orc):
+    l = np.zeros((2, 8), dtype=np.float32)
+    l[1, 3] = np.nan
+    with pytest.raises(RuntimeError):
+        orc.topk(l, 2)
+
+
+# ---------------------------------------------------------------------------
+# expert FFN and layer
+# ---------------------------------------------------------------------------
+def test_expert_ffn_vs_dense_numpy(orc):
+    for bits in (2, 3):
+        wl = mi.small(mi.WORKLOADS["tiny"], bits=bits)
+        ex = mi.expert_canon(wl, 0, 2).numpy()
+        x = mi.activations(wl, T=1)[0].astype(np.float64)
+        got = orc.expert_ffn(ex, wl.d, wl.I, bits, x)
+        ref = np_ffn(*np_expert(ex, wl.d, wl.I, bits), x)
+        assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def _tiny_layer(orc, wl, layer=0, shared=False):
+    W, bias = mi.router(wl, layer)
+    allx = mi.layer_experts_canon(wl, layer).numpy()
+    eb = wl.expert_bytes()
+    experts = {e: allx[e * eb:(e + 1) * eb] for e in range(wl.E)}
+    sh = mi.expert_canon(wl, layer, -1).numpy() if wl.Is else None
+    return orc.Layer(wl.d, wl.E, wl.I, wl.Is, wl.k, wl.bits, W, bias, experts, sh)
+
+
+def test_layer_vs_dense_masked_all_experts(orc):
+    for wl in (mi.WORKLOADS["tiny"],
+               mi.small(mi.WORKLOADS["tiny"], bits=3, Is=96, k=3, zipf_s=1.1, T=6)):
+        L = _tiny_layer(orc, wl)
+        x = mi.activations(wl)
+        y, logits, idx, w = orc.layer_forward(L, x)
+        # dense: every expert evaluated, gate g_e = w if selected else 0
+        xd = x.astype(np.float64)
+        eb = wl.expert_bytes()
+        dense = [np_expert(L.experts[e], wl.d, wl.I, wl.bits) for e in range(wl.E)]
+        ref = np.zeros((x.shape[0], wl.d))
+        for t in range(x.shape[0]):
+            gate = np.zeros(wl.E)
+            gate[idx[t]] = w[t]
+            for e in range(wl.E):
+                ref[t] += gate[e] * np_ffn(*dense[e], xd[t])
+            if wl.Is:
+                ref[t] += np_ffn(*np_expert(L.shared, wl.d, wl.Is, wl.bits), xd[t])
+        assert np.max(np.abs(y - ref)) <= 4 * np.spacing(np.float32(np.max(np.abs(ref))))
+        # routing equals brute force on the oracle's own logits
+        for t in range(x.shape[0]):
+            assert idx[t].tolist() == _brute_topk(logits[t], wl.k)
+        assert eb > 0
+
+
+def test_single_expert_is_textbook_swiglu(orc):
+    wl = mi.small(mi.WORKLOADS["tiny"], E=1, k=1)
+    L = _tiny_layer(orc, wl)
+    x = mi.activations(wl)
+    y, _, idx, w = orc.layer_forward(L, x)
+    assert np.all(idx == 0) and np.all(w == 1.0)
+    Wg, Wu, Wd = np_expert(L.experts[0], wl.d, wl.I, wl.bits)
+    for t in range(x.shape[0]):
+        ref = np_ffn(Wg, Wu, Wd, x[t].astype(np.float64))
+        assert np.max(np.abs(y[t] - ref)) <= 2 * np.spacing(np.float32(np.max(np.abs(ref))))
+
+
+def test_unused_experts_do_not_change_output(orc):
+    wl = mi.WORKLOADS["tiny"]
+    L = _tiny_layer(orc, wl)
+    x = mi.activations(wl)
+    y, _, idx, _ = orc.layer_forward(L, x)
+    used = set(idx.reshape(-1).tolist())
+    g = np.random.default_rng(5)
+    for e in range(wl.E):
+        if e not in used:
+            L.experts[e] = g.integers(0, 256, L.experts[e].size).astype(np.uint8)
+    y2, _, idx2, _ = orc.layer_forward(L, x)
+    assert np.array_equal(idx, idx2)
+    assert np.array_equal(y, y2)
+    # and they may be absent altogether
+    for e in range(wl.E):
+        if e not in used:
+            del L.experts[e]
+    y3, _, _, _ = orc.layer_forward(L, x)
+    assert np.array_equal(y, y3)
+
+
+def test_row_independence_and_forcing(orc):
+    wl = mi.small(mi.WORKLOADS["tiny"], Is=64)
+    L = _tiny_layer(orc, wl)
+    x = mi.activations(wl, T=5)
+    y, _, idx, w = orc.layer_forward(L, x)
+    for t in range(5):
+        yt, _, it, wt = orc.layer_forward(L, x[t:t + 1])
+        assert np.array_equal(yt[0], y[t]) and np.array_equal(it[0], idx[t]) and np.array_equal(wt[0], w[t])
+    yf, _, _, _ = orc.layer_forward(L, x, force_idx=idx, force_w=w)
+    assert np.array_equal(yf, y)
+
+
+def test_zero_scale_expert_and_shared_linearity(orc):
+    wl = mi.small(mi.WORKLOADS["tiny"], Is=64)
+    L = _tiny_layer(orc, wl)
+    x = mi.activations(wl)
+    y, _, idx, w = orc.layer_forward(L, x)
+    # zero every scale of the rank-0 expert of token 0: its term vanishes
+    e0 = int(idx[0, 0])
+    z = L.experts[e0].copy().reshape(-1, 2 + 4 * wl.bits)
+    z[:, :2] = 0
+    L.experts[e0] = z.reshape(-1)
+    yz, _, _, _ = orc.layer_forward(L, x, force_idx=idx, force_w=w)
+    ffn0 = orc.expert_ffn(_tiny_layer(orc, wl).experts[e0], wl.d, wl.I, wl.bits, x[0].astype(np.float64))
+    assert np.max(np.abs((y[0] - yz[0]) - w[0, 0] * ffn0)) <= 1e-5 * np.max(np.abs(y[0]))
+    # removing the shared expert subtracts exactly its FFN
+    L2 = _tiny_layer(orc, wl)
+    Lns = orc.Layer(wl.d, wl.E, wl.I, 0, wl.k, wl.bits, L2.router_w, L2.router_bias, L2.experts, None)
+    yn, _, _, _ = orc.layer_forward(Lns, x, force_idx=idx, force_w=w)
+    for t in range(x.shape[0]):
+        fs = orc.expert_ffn(L2.shared, wl.d, wl.Is, wl.bits, x[t].astype(np.float64))
+        assert np.max(np.abs((y[t].astype(np.float64) - yn[t]) - fs)) <= 1e-5 * np.max(np.abs(y[t]))
+
+
+def test_rmsnorm_closed_forms(orc):
+    d = 64
+    for c in (1.0, -3.5, 1e-4):
+        x = np.full((2, d), c, dtype=np.float32)
+        y = orc.rmsnorm(x, 1e-6)
+        assert np.all(y == np.float32(c / math.sqrt(c * c + 1e-6)))
+    x = mi.activations(mi.WORKLOADS["tiny"], T=3)
+    y = orc.rmsnorm(x, 1e-6)
+    xd = x.astype(np.float64)
+    ref = xd / np.sqrt((xd * xd).mean(1, keepdims=True) + 1e-6)
+    assert np.max(np.abs(y - ref)) <= np.spacing(np.float32(np.abs(ref).max()))
+
+
+def test_generator_is_deterministic_and_device_agnostic_shape():
+    wl = mi.WORKLOADS["tiny"]
+    a = mi.layer_experts_canon(wl, 3)
+    b = mi.layer_experts_canon(wl, 3)
+    assert a.dtype == b.dtype and bool((a == b).all())
+    c = mi.layer_experts_canon(wl, 4)
+    assert not bool((a == c).all())
+    eb = wl.expert_bytes()
+    assert bool((mi.expert_canon(wl, 3, 5) == a[5 * eb:6 * eb]).all())
