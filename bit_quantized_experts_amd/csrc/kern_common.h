@@ -1,0 +1,118 @@
+// kern_common.h -- device helpers shared by the HIP kernels (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_internal.h"
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+#define DEVI __device__ __forceinline__
+
+// ---------------------------------------------------------------------------
+// Fragment decode.
+//
+// A fragment is 8 codes (one MFMA B operand of 16x16x32: inputs 8q..8q+7 of
+// one weight row).  In the packed layout its codes sit in one nibble each of
+// a dword after a mask: (w >> sh) & 0x33333333 leaves q (0..3) in the low two
+// bits of every nibble.  A nibble 00qq read as an OCP fp4 (e2m1) value is
+// q/2 (0, 0.5, 1, 1.5), so the gfx950 fp4->f16 conversion with scale 2.0 (a
+// power of two: the conversion only uses the scale's exponent) yields q as an
+// exact fp16 value; the byte select picks two codes at a time, low nibble to
+// element 0.  The block offset 2^(b-1) and the fp16 block scale are applied
+// outside (accumulator seed and epilogue), so nothing here rounds.
+// ---------------------------------------------------------------------------
+DEVI half8_t nibbles_to_half8(uint32_t D, float sc) {
+  half2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(D, sc, 0);
+  half2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(D, sc, 1);
+  half2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(D, sc, 2);
+  half2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(D, sc, 3);
+  half8_t r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+// q (unsigned code, 0..3) of fragment f from the lane's 4 code dwords.
+DEVI half8_t frag_q2(const u32x4_t& w, int f) {
+  uint32_t dw = w[f >> 1];
+  uint32_t D = ((f & 1) ? (dw >> 2) : dw) & 0x33333333u;
+  return nibbles_to_half8(D, 2.0f);
+}
+
+// q (unsigned code, 0..7) of fragment f for 3-bit codes: low two bits from
+// the code dwords, high bit from the 2 high-bit dwords (fragment 4h+g at
+// bit 4e+g of dword h); 000h read as fp4 is h/2, scale 8 gives 4h.
+DEVI half8_t frag_q3(const u32x4_t& w, const u32x2_t& hbits, int f) {
+  half8_t lo = frag_q2(w, f);
+  uint32_t H = (hbits[f >> 2] >> (f & 3)) & 0x11111111u;
+  half8_t hi = nibbles_to_half8(H, 8.0f);
+  return lo + hi;
+}
+
+// ---------------------------------------------------------------------------
+// Buffer loads that bypass nothing special: plain 128/64-bit global loads.
+// ---------------------------------------------------------------------------
+DEVI u32x4_t ld128(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+DEVI u32x2_t ld64(const void* p) { return *reinterpret_cast<const u32x2_t*>(p); }
+DEVI u32x4_t ld128_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+DEVI u32x2_t ld64_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+}
+
+DEVI float half_bits_to_float(uint32_t h16) {
+  _Float16 h;
+  uint16_t b = (uint16_t)h16;
+  __builtin_memcpy(&h, &b, 2);
+  return (float)h;
+}
+
+DEVI float4_t mfma16x16x32(const half8_t& a, const half8_t& b, const float4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Swap halves: lanes 0..31 <-> 32..63; returns v + (value of the partner lane).
+DEVI float add_partner32(float v) {
+  uint32_t x = __float_as_uint(v);
+  auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+DEVI float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Deterministic fp64 exponential for the gate weights.  Steps: n = rint(z /
+// ln2); r = z - n*ln2 as two fused steps with ln2 split into a high part (the
+// double nearest ln2) and a low part (the double nearest the remainder);
+// p = sum_{i=0..13} r^i/i! by Horner with fused multiply-add, from i = 13
+// down; result = p * 2^n.  Coefficients are 1/i! rounded once to double
+// (i! <= 13! is exact in double, so 1.0 / i! is one correctly rounded
+// division).  Any IEEE fp64 implementation of the same steps returns the same
+// bits.
+// ---------------------------------------------------------------------------
+__host__ __device__ constexpr double moe_fact(int i) { return i <= 1 ? 1.0 : (double)i * moe_fact(i - 1); }
+
+DEVI double moe_exp64(double z) {
+#pragma clang fp contract(off)
+  constexpr double kInvLn2 = 1.44269504088896340735992468100189214;   // 1/ln 2
+  constexpr double kLn2Hi = 0.693147180559945309417232121458176568;   // ln 2
+  constexpr double kLn2Lo = 2.319046813846299558417771e-17;            // ln 2 - kLn2Hi
+  if (z < -1080.0) return 0.0;
+  if (z > 709.0) return __builtin_huge_val();
+  double n = __builtin_rint(z * kInvLn2);
+  double r = __builtin_fma(-n, kLn2Hi, z);
+  r = __builtin_fma(-n, kLn2Lo, r);
+  double p = 1.0 / moe_fact(13);
+#pragma unroll
+  for (int i = 12; i >= 0; --i) p = __builtin_fma(p, r, 1.0 / moe_fact(i));
+  return __builtin_ldexp(p, (int)n);
+}

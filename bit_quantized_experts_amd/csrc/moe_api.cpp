@@ -1,0 +1,561 @@
+// moe_api.cpp -- the C ABI declared in include/moe.h: argument checks, the
+// packed and workspace layouts, and the order of kernel launches.  No device
+// memory is allocated here; every launch goes to the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "moe_internal.h"
+#include "moe_launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define HIPCHK(expr)                                                                   \
+  do {                                                                                 \
+    hipError_t e_ = (expr);                                                            \
+    if (e_ != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  return (v && *v) ? atoi(v) : dflt;
+}
+
+std::once_flag g_init_once;
+hipError_t g_init_err = hipSuccess;
+void init_kernels() {
+  std::call_once(g_init_once, [] { g_init_err = moe_route_kernels_init(); });
+}
+
+int choose_bk(int nb) {
+  for (int bk : {8, 4, 2, 1})
+    if (nb % bk == 0) return bk;
+  return 1;
+}
+
+bool make_mat(int rows, int cols, int bits, moe_mat_layout* L, int bk = 0) {
+  L->rows = rows;
+  L->cols = cols;
+  L->nb = cols / 32;
+  L->BK = bk > 0 ? bk : choose_bk(L->nb);
+  if (L->nb % L->BK) return false;
+  L->RT = 8 / L->BK;
+  if (rows % (16 * L->RT) != 0) return false;
+  L->n_rg = rows / (16 * L->RT);
+  L->n_kg = L->nb / L->BK;
+  L->chunk_bytes = bits == 2 ? 1280 : 1792;
+  L->bytes = (int64_t)L->n_rg * L->n_kg * L->chunk_bytes;
+  return true;
+}
+
+// Down matrices of the routed and the shared expert share one block grouping
+// (the largest power of two <= 8 dividing both d_ff/32 and d_ff_shared/32),
+// so a row group of the down kernel has the same height for every expert.
+int down_bk(int I, int Is) {
+  int a = I / 32, b = Is > 0 ? Is / 32 : a;
+  while (b) { int t = a % b; a = b; b = t; }
+  return choose_bk(a);
+}
+
+bool make_expert(int d, int I, int bits, moe_expert_layout* X, int bk_down) {
+  if (!make_mat(I, d, bits, &X->gate) || !make_mat(I, d, bits, &X->up) || !make_mat(d, I, bits, &X->down, bk_down))
+    return false;
+  X->off_gate = 0;
+  X->off_up = moe_align256(X->gate.bytes);
+  X->off_down = X->off_up + moe_align256(X->up.bytes);
+  X->bytes = moe_align256(X->off_down + X->down.bytes);
+  return true;
+}
+
+int64_t canon_block_bytes(int bits) { return 2 + 4 * bits; }
+
+int check_desc(const moe_layer_desc* D) {
+  if (!D) return fail(MOE_ERR_ARG, "desc is NULL");
+  if (D->block != 32) return fail(MOE_ERR_UNSUPPORTED, "block must be 32 (got %d)", D->block);
+  if (D->bits != 2 && D->bits != 3) return fail(MOE_ERR_UNSUPPORTED, "bits must be 2 or 3 (got %d)", D->bits);
+  if (D->d_model <= 0 || D->d_model % 256) return fail(MOE_ERR_UNSUPPORTED, "d_model must be a positive multiple of 256 (got %d)", D->d_model);
+  if (D->d_model > 8192) return fail(MOE_ERR_UNSUPPORTED, "d_model above 8192 not supported (got %d)", D->d_model);
+  if (D->n_experts < 1 || D->n_experts > MOE_MAX_E) return fail(MOE_ERR_UNSUPPORTED, "n_experts must be in [1, %d] (got %d)", MOE_MAX_E, D->n_experts);
+  if (D->d_ff <= 0 || D->d_ff % 32) return fail(MOE_ERR_UNSUPPORTED, "d_ff must be a positive multiple of 32 (got %d)", D->d_ff);
+  if (D->d_ff_shared < 0 || D->d_ff_shared % 32) return fail(MOE_ERR_UNSUPPORTED, "d_ff_shared must be 0 or a multiple of 32 (got %d)", D->d_ff_shared);
+  if (D->top_k < 1 || D->top_k > D->n_experts || D->top_k > MOE_MAX_K)
+    return fail(MOE_ERR_ARG, "top_k must be in [1, min(n_experts, %d)] (got %d)", MOE_MAX_K, D->top_k);
+  return MOE_OK;
+}
+
+// packed buffer: [status 256 B][router_w][router_b][E experts][shared]
+struct PackedLayout {
+  int64_t off_status, off_rw, off_rb, off_ex, off_sh, total;
+};
+
+PackedLayout packed_layout(const moe_layer_desc* D, const moe_expert_layout& ex, const moe_expert_layout& sh) {
+  PackedLayout P;
+  P.off_status = 0;
+  P.off_rw = 256;
+  P.off_rb = P.off_rw + moe_align256((int64_t)D->n_experts * D->d_model * 4);
+  P.off_ex = P.off_rb + moe_align256((int64_t)D->n_experts * 4);
+  P.off_sh = P.off_ex + (int64_t)D->n_experts * ex.bytes;
+  P.total = P.off_sh + (D->d_ff_shared > 0 ? sh.bytes : 0);
+  return P;
+}
+
+// ------------------------------------------------------------- workspace ---
+struct WsLayout {
+  int64_t ctrl, logits, idx, w, n_slots, slot_expert, slot_w, xfrag, xsum, hfrag, hsum, ypart, ystack, total;
+  int max_slots, S, nbI;
+};
+
+int64_t ctrl_bytes(int d) { return moe_align256((int64_t)(1 + d / 16) * 4); }
+
+int down_splits(const moe_layer* L, int max_slots) {
+  const int n_rg = L->ex.down.n_rg;
+  int S = env_int("MOE_DOWN_SPLITS", 0);
+  if (S <= 0) S = (512 + n_rg - 1) / n_rg;
+  if (S > max_slots) S = max_slots;
+  if (S < 1) S = 1;
+  return S;
+}
+
+WsLayout ws_layout_decode(const moe_layer* L, int T) {
+  WsLayout W{};
+  const int k = L->k, E = L->E, d = L->d;
+  W.max_slots = (T * k < E ? T * k : E) + (L->Is > 0 ? 1 : 0);
+  W.nbI = (L->I > L->Is ? L->I : L->Is) / 32;
+  W.S = down_splits(L, W.max_slots);
+  int64_t o = 0;
+  auto take = [&](int64_t bytes) { int64_t r = o; o += moe_align256(bytes); return r; };
+  W.ctrl = take(ctrl_bytes(d));
+  W.logits = take((int64_t)T * E * 4);
+  W.idx = take((int64_t)T * k * 4);
+  W.w = take((int64_t)T * k * 4);
+  W.n_slots = take(4);
+  W.slot_expert = take((int64_t)W.max_slots * 4);
+  W.slot_w = take((int64_t)W.max_slots * 8 * 4);
+  W.xfrag = take((int64_t)(d / 32) * 64 * 8 * 2);
+  W.xsum = take((int64_t)(d / 32) * 16 * 4);
+  W.hfrag = take((int64_t)W.max_slots * W.nbI * 64 * 8 * 2);
+  W.hsum = take((int64_t)W.max_slots * W.nbI * 16 * 4);
+  W.ypart = take((int64_t)W.S * 8 * d * 4);
+  W.ystack = take((int64_t)2 * 8 * d * 4);
+  W.total = o;
+  return W;
+}
+
+// ---------------------------------------------------------------- timing ---
+struct Timing {
+  std::mutex mu;
+  int cls = -1;
+  int max = 0;
+  int used = 0;
+  std::vector<hipEvent_t> ev;
+} g_timing;
+
+void timed_begin(int cls, hipStream_t s, int* slot) {
+  *slot = -1;
+  if (g_timing.cls != cls) return;
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  if (g_timing.cls != cls || g_timing.used >= g_timing.max) return;
+  *slot = g_timing.used++;
+  hipEventRecord(g_timing.ev[2 * *slot], s);
+}
+void timed_end(int slot, hipStream_t s) {
+  if (slot >= 0) hipEventRecord(g_timing.ev[2 * slot + 1], s);
+}
+
+ExpertSet expert_set(const moe_layer* L) {
+  ExpertSet X;
+  X.experts = L->experts;
+  X.ex_stride = L->ex.bytes;
+  X.shared = L->shared;
+  X.off_gate = L->ex.off_gate;
+  X.off_up = L->ex.off_up;
+  X.off_down = L->ex.off_down;
+  X.sh_off_gate = L->sh.off_gate;
+  X.sh_off_up = L->sh.off_up;
+  X.sh_off_down = L->sh.off_down;
+  return X;
+}
+
+// One decode layer (T <= 8).  x may be the previous layer's output (norm = 1).
+int decode_layer(const moe_layer* L, const float* x, int norm, float eps, int T, float* y,
+                 const moe_route_io* r, uint8_t* ws, hipStream_t s) {
+  const WsLayout W = ws_layout_decode(L, T);
+  const int d = L->d, E = L->E;
+  RouteArgs ra{};
+  ra.x = x;
+  ra.norm = norm;
+  ra.eps = eps;
+  ra.Wr = L->router_w;
+  ra.br = L->router_b;
+  ra.T = T;
+  ra.d = d;
+  ra.E = E;
+  ra.k = L->k;
+  ra.has_shared = L->Is > 0;
+  ra.code_off = 1 << (L->bits - 1);
+  ra.rows_per_wg = env_int("MOE_ROUTE_ROWS", 4);
+  if (ra.rows_per_wg < 1) ra.rows_per_wg = 4;
+  const bool forced = r && r->in_idx && r->in_w;
+  ra.fidx = forced ? r->in_idx : nullptr;
+  ra.fw = forced ? r->in_w : nullptr;
+  ra.logits = reinterpret_cast<float*>(ws + W.logits);
+  ra.idx = reinterpret_cast<int32_t*>(ws + W.idx);
+  ra.w = reinterpret_cast<float*>(ws + W.w);
+  ra.out_logits = (r && !forced) ? r->out_logits : nullptr;
+  ra.out_idx = r ? r->out_idx : nullptr;
+  ra.out_w = r ? r->out_w : nullptr;
+  ra.n_slots = reinterpret_cast<int32_t*>(ws + W.n_slots);
+  ra.slot_expert = reinterpret_cast<int32_t*>(ws + W.slot_expert);
+  ra.slot_w = reinterpret_cast<float*>(ws + W.slot_w);
+  ra.xfrag = reinterpret_cast<_Float16*>(ws + W.xfrag);
+  ra.xsum = reinterpret_cast<float*>(ws + W.xsum);
+  ra.counter = reinterpret_cast<uint32_t*>(ws + W.ctrl);
+  int n_wg = forced ? (d / 32 + 3) / 4 : (E + ra.rows_per_wg - 1) / ra.rows_per_wg;
+  if (n_wg < 1) n_wg = 1;
+  int slot;
+  timed_begin(2, s, &slot);
+  HIPCHK(launch_route_decode(ra, n_wg, s));
+  timed_end(slot, s);
+
+  const ExpertSet X = expert_set(L);
+  GuArgs ga{};
+  ga.X = X;
+  ga.n_slots = ra.n_slots;
+  ga.slot_expert = ra.slot_expert;
+  ga.slot_w = ra.slot_w;
+  ga.xfrag = ra.xfrag;
+  ga.xsum = ra.xsum;
+  ga.hfrag = reinterpret_cast<_Float16*>(ws + W.hfrag);
+  ga.hsum = reinterpret_cast<float*>(ws + W.hsum);
+  ga.E = E;
+  ga.I = L->I;
+  ga.Is = L->Is;
+  ga.n_kg = d / 256;
+  ga.bits = L->bits;
+  ga.nbI = W.nbI;
+  ga.code_off = ra.code_off;
+  int gu_nw = env_int("MOE_GU_WAVES", 0);
+  if (gu_nw <= 0 || gu_nw > 8) gu_nw = ga.n_kg < 5 ? ga.n_kg : 5;
+  timed_begin(0, s, &slot);
+  HIPCHK(launch_gu_decode(ga, W.nbI, W.max_slots, gu_nw, s));
+  timed_end(slot, s);
+
+  DownArgs da{};
+  da.X = X;
+  da.n_slots = ra.n_slots;
+  da.slot_expert = ra.slot_expert;
+  da.hfrag = ga.hfrag;
+  da.hsum = ga.hsum;
+  da.E = E;
+  da.d = d;
+  da.T = T;
+  da.bits = L->bits;
+  da.nbI = W.nbI;
+  da.BK = L->ex.down.BK;
+  da.RT = L->ex.down.RT;
+  da.n_kg_r = L->ex.down.n_kg;
+  da.n_kg_s = L->Is > 0 ? L->sh.down.n_kg : 0;
+  da.S = W.S;
+  da.y = y;
+  da.ypart = reinterpret_cast<float*>(ws + W.ypart);
+  da.counters = reinterpret_cast<uint32_t*>(ws + W.ctrl) + 1;
+  int dn_nw = env_int("MOE_DOWN_WAVES", 4);
+  if (dn_nw <= 0 || dn_nw > 8) dn_nw = 4;
+  timed_begin(1, s, &slot);
+  HIPCHK(launch_down_decode(da, L->ex.down.n_rg, dn_nw, s));
+  timed_end(slot, s);
+  return MOE_OK;
+}
+
+int check_ws(const moe_layer* L, int T, void* ws, size_t ws_bytes, size_t* need) {
+  if (moe_workspace_bytes(L, T, need) != MOE_OK) return MOE_ERR_ARG;
+  if (!ws) return fail(MOE_ERR_ARG, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(MOE_ERR_ARG, "workspace must be 256-byte aligned");
+  if (ws_bytes < *need) return fail(MOE_ERR_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes, *need);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+int moe_packed_bytes(const moe_layer_desc* desc, size_t* bytes) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!bytes) return fail(MOE_ERR_ARG, "bytes is NULL");
+  moe_expert_layout ex{}, sh{};
+  const int bkd = down_bk(desc->d_ff, desc->d_ff_shared);
+  if (!make_expert(desc->d_model, desc->d_ff, desc->bits, &ex, bkd))
+    return fail(MOE_ERR_UNSUPPORTED, "expert shape not tileable");
+  if (desc->d_ff_shared > 0 && !make_expert(desc->d_model, desc->d_ff_shared, desc->bits, &sh, bkd))
+    return fail(MOE_ERR_UNSUPPORTED, "shared expert shape not tileable");
+  *bytes = (size_t)packed_layout(desc, ex, sh).total;
+  return MOE_OK;
+}
+
+int moe_pack_experts(const moe_layer_desc* desc, const void* experts_canon, const void* shared_canon,
+                     const float* router_w, const float* router_bias, void* packed, size_t packed_bytes,
+                     moe_layer** out, void* stream) {
+  size_t need = 0;
+  int rc = moe_packed_bytes(desc, &need);
+  if (rc) return rc;
+  if (!out) return fail(MOE_ERR_ARG, "out is NULL");
+  *out = nullptr;
+  if (!experts_canon || !router_w || !packed) return fail(MOE_ERR_ARG, "experts_canon, router_w and packed must be non-NULL");
+  if ((desc->d_ff_shared > 0) != (shared_canon != nullptr))
+    return fail(MOE_ERR_ARG, "shared_canon must be given exactly when d_ff_shared > 0");
+  if (!aligned(packed, 256)) return fail(MOE_ERR_ARG, "packed must be 256-byte aligned");
+  if (!aligned(router_w, 16) || (router_bias && !aligned(router_bias, 4)))
+    return fail(MOE_ERR_ARG, "router_w must be 16-byte aligned");
+  if (packed_bytes < need) return fail(MOE_ERR_ARG, "packed buffer too small: %zu < %zu", packed_bytes, need);
+  init_kernels();
+  if (g_init_err != hipSuccess) return fail(MOE_ERR_HIP, "kernel init: %s", hipGetErrorString(g_init_err));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  moe_layer* L = new (std::nothrow) moe_layer{};
+  if (!L) return fail(MOE_ERR_ARG, "out of host memory");
+  L->d = desc->d_model;
+  L->E = desc->n_experts;
+  L->I = desc->d_ff;
+  L->Is = desc->d_ff_shared;
+  L->k = desc->top_k;
+  L->bits = desc->bits;
+  const int bkd = down_bk(L->I, L->Is);
+  make_expert(L->d, L->I, L->bits, &L->ex, bkd);
+  if (L->Is > 0) make_expert(L->d, L->Is, L->bits, &L->sh, bkd);
+  const PackedLayout P = packed_layout(desc, L->ex, L->sh);
+  uint8_t* base = reinterpret_cast<uint8_t*>(packed);
+  L->packed = base;
+  L->packed_bytes = (size_t)P.total;
+  L->router_w = reinterpret_cast<const float*>(base + P.off_rw);
+  L->router_b = reinterpret_cast<const float*>(base + P.off_rb);
+  L->experts = base + P.off_ex;
+  L->shared = L->Is > 0 ? base + P.off_sh : nullptr;
+
+  auto bail = [&](int code) { delete L; return code; };
+  uint32_t* status = reinterpret_cast<uint32_t*>(base + P.off_status);
+  hipError_t e;
+  if ((e = launch_fill_u32(status, 64, 0u, s)) != hipSuccess) return bail(fail(MOE_ERR_HIP, "fill: %s", hipGetErrorString(e)));
+  if ((e = hipMemcpyAsync(base + P.off_rw, router_w, (size_t)L->E * L->d * 4, hipMemcpyDeviceToDevice, s)) != hipSuccess)
+    return bail(fail(MOE_ERR_HIP, "router copy: %s", hipGetErrorString(e)));
+  if (router_bias) {
+    if ((e = hipMemcpyAsync(base + P.off_rb, router_bias, (size_t)L->E * 4, hipMemcpyDeviceToDevice, s)) != hipSuccess)
+      return bail(fail(MOE_ERR_HIP, "bias copy: %s", hipGetErrorString(e)));
+  } else if ((e = launch_fill_u32(reinterpret_cast<uint32_t*>(base + P.off_rb), (size_t)L->E, 0u, s)) != hipSuccess) {
+    return bail(fail(MOE_ERR_HIP, "bias fill: %s", hipGetErrorString(e)));
+  }
+  const int64_t bb = canon_block_bytes(L->bits);
+  auto pack_expert = [&](const uint8_t* canon, int I, const moe_expert_layout& X, uint8_t* dst, int n) -> hipError_t {
+    const int64_t gate_b = (int64_t)I * (L->d / 32) * bb;
+    const int64_t canon_stride = 3 * gate_b;
+    hipError_t r;
+    if ((r = launch_pack_matrix(canon, canon_stride, dst + X.off_gate, X.bytes, n, X.gate, L->bits, status, s)) != hipSuccess) return r;
+    if ((r = launch_pack_matrix(canon + gate_b, canon_stride, dst + X.off_up, X.bytes, n, X.up, L->bits, status, s)) != hipSuccess) return r;
+    return launch_pack_matrix(canon + 2 * gate_b, canon_stride, dst + X.off_down, X.bytes, n, X.down, L->bits, status, s);
+  };
+  if ((e = pack_expert(reinterpret_cast<const uint8_t*>(experts_canon), L->I, L->ex, base + P.off_ex, L->E)) != hipSuccess)
+    return bail(fail(MOE_ERR_HIP, "pack: %s", hipGetErrorString(e)));
+  if (L->Is > 0 && (e = pack_expert(reinterpret_cast<const uint8_t*>(shared_canon), L->Is, L->sh, base + P.off_sh, 1)) != hipSuccess)
+    return bail(fail(MOE_ERR_HIP, "pack shared: %s", hipGetErrorString(e)));
+  uint32_t flag = 0;
+  if ((e = hipMemcpyAsync(&flag, status, 4, hipMemcpyDeviceToHost, s)) != hipSuccess)
+    return bail(fail(MOE_ERR_HIP, "status copy: %s", hipGetErrorString(e)));
+  if ((e = hipStreamSynchronize(s)) != hipSuccess) return bail(fail(MOE_ERR_HIP, "sync: %s", hipGetErrorString(e)));
+  if (flag) return bail(fail(MOE_ERR_DATA, "a block scale is inf/nan or has magnitude >= 8192"));
+  *out = L;
+  return MOE_OK;
+}
+
+int moe_layer_release(moe_layer* layer) {
+  delete layer;
+  return MOE_OK;
+}
+
+int moe_layer_get_desc(const moe_layer* L, moe_layer_desc* out) {
+  if (!L || !out) return fail(MOE_ERR_ARG, "NULL argument");
+  out->d_model = L->d;
+  out->n_experts = L->E;
+  out->d_ff = L->I;
+  out->d_ff_shared = L->Is;
+  out->top_k = L->k;
+  out->bits = L->bits;
+  out->block = 32;
+  return MOE_OK;
+}
+
+int moe_route_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w, void* stream) {
+  if (T < 0) return fail(MOE_ERR_ARG, "T must be >= 0");
+  if (E < 1 || E > MOE_MAX_E) return fail(MOE_ERR_ARG, "E must be in [1, %d]", MOE_MAX_E);
+  if (k < 1 || k > E || k > MOE_MAX_K) return fail(MOE_ERR_ARG, "k must be in [1, min(E, %d)]", MOE_MAX_K);
+  if (T == 0) return MOE_OK;
+  if (!logits || !idx || !w) return fail(MOE_ERR_ARG, "NULL pointer");
+  if (!aligned(logits, 4) || !aligned(idx, 4) || !aligned(w, 4)) return fail(MOE_ERR_ARG, "misaligned pointer");
+  HIPCHK(launch_topk(logits, T, E, k, idx, w, reinterpret_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
+int moe_workspace_bytes(const moe_layer* L, int T, size_t* bytes) {
+  if (!L || !bytes) return fail(MOE_ERR_ARG, "NULL argument");
+  if (T < 0) return fail(MOE_ERR_ARG, "T must be >= 0");
+  if (T > MOE_MAX_TOK_DECODE) return fail(MOE_ERR_UNSUPPORTED, "T > %d (prefill path) not built yet", MOE_MAX_TOK_DECODE);
+  const int Tw = T < 1 ? 1 : T;
+  *bytes = (size_t)ws_layout_decode(L, Tw).total;
+  return MOE_OK;
+}
+
+int moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws || !aligned(ws, 256)) return fail(MOE_ERR_ARG, "workspace must be non-NULL and 256-byte aligned");
+  if (ws_bytes < 256) return fail(MOE_ERR_WORKSPACE, "workspace too small");
+  // control words: the first ctrl_bytes(8192) of any workspace (largest d)
+  size_t n = (size_t)ctrl_bytes(8192);
+  if (n > ws_bytes) n = ws_bytes;
+  HIPCHK(launch_fill_u32(reinterpret_cast<uint32_t*>(ws), n / 4, 0u, reinterpret_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
+int moe_layer_forward(const moe_layer* L, const float* x, int T, float* y, const moe_route_io* route, void* ws,
+                      size_t ws_bytes, void* stream) {
+  if (!L) return fail(MOE_ERR_ARG, "layer is NULL");
+  if (T < 0) return fail(MOE_ERR_ARG, "T must be >= 0");
+  if (T == 0) return MOE_OK;
+  if (!x || !y) return fail(MOE_ERR_ARG, "x and y must be non-NULL");
+  if (!aligned(x, 16) || !aligned(y, 16)) return fail(MOE_ERR_ARG, "x and y must be 16-byte aligned");
+  const char* xb = reinterpret_cast<const char*>(x);
+  const char* yb = reinterpret_cast<const char*>(y);
+  const size_t nbytes = (size_t)T * L->d * 4;
+  if (xb < yb + nbytes && yb < xb + nbytes) return fail(MOE_ERR_ARG, "x and y must not alias");
+  if (route && ((route->in_idx == nullptr) != (route->in_w == nullptr)))
+    return fail(MOE_ERR_ARG, "in_idx and in_w must be given together");
+  size_t need;
+  int rc = check_ws(L, T, ws, ws_bytes, &need);
+  if (rc) return rc;
+  init_kernels();
+  if (g_init_err != hipSuccess) return fail(MOE_ERR_HIP, "kernel init: %s", hipGetErrorString(g_init_err));
+  return decode_layer(L, x, 0, 0.f, T, y, route, reinterpret_cast<uint8_t*>(ws), reinterpret_cast<hipStream_t>(stream));
+}
+
+int moe_stack_forward(const moe_layer* const* layers, int n_layers, const float* x, int T, float eps, float* y,
+                      float* y_layers, int32_t* idx_layers, float* w_layers, void* ws, size_t ws_bytes,
+                      void* stream) {
+  if (!layers || n_layers < 1) return fail(MOE_ERR_ARG, "need at least one layer");
+  if (T < 0) return fail(MOE_ERR_ARG, "T must be >= 0");
+  if (T == 0) return MOE_OK;
+  if (!x || !y) return fail(MOE_ERR_ARG, "x and y must be non-NULL");
+  if (!aligned(x, 16) || !aligned(y, 16) || (y_layers && !aligned(y_layers, 16)))
+    return fail(MOE_ERR_ARG, "x, y and y_layers must be 16-byte aligned");
+  if ((idx_layers == nullptr) != (w_layers == nullptr)) return fail(MOE_ERR_ARG, "idx_layers and w_layers go together");
+  const int d = layers[0] ? layers[0]->d : 0;
+  for (int l = 0; l < n_layers; ++l) {
+    if (!layers[l]) return fail(MOE_ERR_ARG, "layer %d is NULL", l);
+    if (layers[l]->d != d) return fail(MOE_ERR_ARG, "layer %d has d_model %d, expected %d", l, layers[l]->d, d);
+    size_t need;
+    int rc = check_ws(layers[l], T, ws, ws_bytes, &need);
+    if (rc) return rc;
+  }
+  if (T > MOE_MAX_TOK_DECODE) return fail(MOE_ERR_UNSUPPORTED, "stack forward supports T <= %d", MOE_MAX_TOK_DECODE);
+  init_kernels();
+  if (g_init_err != hipSuccess) return fail(MOE_ERR_HIP, "kernel init: %s", hipGetErrorString(g_init_err));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
+  const float* in = x;
+  for (int l = 0; l < n_layers; ++l) {
+    const WsLayout W = ws_layout_decode(layers[l], T);
+    float* out;
+    if (l == n_layers - 1) out = y;
+    else if (y_layers) out = y_layers + (size_t)l * T * d;
+    else out = reinterpret_cast<float*>(wsb + W.ystack) + (size_t)(l & 1) * 8 * d;
+    moe_route_io r{};
+    if (idx_layers) {
+      r.out_idx = idx_layers + (size_t)l * T * layers[l]->k;
+      r.out_w = w_layers + (size_t)l * T * layers[l]->k;
+    }
+    int rc = decode_layer(layers[l], in, l > 0, eps, T, out, &r, wsb, s);
+    if (rc) return rc;
+    if (l == n_layers - 1 && y_layers) {
+      HIPCHK(hipMemcpyAsync(y_layers + (size_t)l * T * d, y, (size_t)T * d * 4, hipMemcpyDeviceToDevice, s));
+    }
+    in = out;
+  }
+  return MOE_OK;
+}
+
+int moe_rmsnorm(const float* x, int T, int d, float eps, float* y, void* stream) {
+  if (T < 0 || d <= 0 || d % 4) return fail(MOE_ERR_ARG, "need T >= 0 and d a positive multiple of 4");
+  if (T == 0) return MOE_OK;
+  if (!x || !y || !aligned(x, 16) || !aligned(y, 16)) return fail(MOE_ERR_ARG, "x, y must be non-NULL and 16-byte aligned");
+  HIPCHK(launch_rmsnorm(x, T, d, eps, y, reinterpret_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
+int moe_debug_unpack(const moe_layer* L, int expert, int mat, int8_t* codes, float* w_f32, uint16_t* w_f16,
+                     void* stream) {
+  if (!L) return fail(MOE_ERR_ARG, "layer is NULL");
+  if (expert < -1 || expert >= L->E) return fail(MOE_ERR_ARG, "expert out of range");
+  if (expert == -1 && L->Is == 0) return fail(MOE_ERR_ARG, "layer has no shared expert");
+  if (mat < 0 || mat > 2) return fail(MOE_ERR_ARG, "mat must be 0, 1 or 2");
+  if (!codes && !w_f32 && !w_f16) return MOE_OK;
+  const moe_expert_layout& X = expert < 0 ? L->sh : L->ex;
+  const uint8_t* base = expert < 0 ? L->shared : L->experts + (int64_t)expert * L->ex.bytes;
+  const moe_mat_layout& M = mat == 0 ? X.gate : mat == 1 ? X.up : X.down;
+  const int64_t off = mat == 0 ? X.off_gate : mat == 1 ? X.off_up : X.off_down;
+  HIPCHK(launch_debug_unpack(base + off, M, L->bits, codes, w_f32, w_f16, reinterpret_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
+int moe_timing_start(int kernel_class, int max_launches) {
+  if (kernel_class < 0 || kernel_class > 4 || max_launches < 1) return fail(MOE_ERR_ARG, "bad timing arguments");
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  for (hipEvent_t e : g_timing.ev) hipEventDestroy(e);
+  g_timing.ev.assign(2 * (size_t)max_launches, nullptr);
+  for (auto& e : g_timing.ev) HIPCHK(hipEventCreate(&e));
+  g_timing.max = max_launches;
+  g_timing.used = 0;
+  g_timing.cls = kernel_class;
+  return MOE_OK;
+}
+
+int moe_timing_stop(double* total_ms, int* launches) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  const int cls = g_timing.cls;
+  g_timing.cls = -1;
+  if (cls < 0) return fail(MOE_ERR_ARG, "timing not started");
+  double tot = 0;
+  for (int i = 0; i < g_timing.used; ++i) {
+    HIPCHK(hipEventSynchronize(g_timing.ev[2 * i + 1]));
+    float ms = 0;
+    HIPCHK(hipEventElapsedTime(&ms, g_timing.ev[2 * i], g_timing.ev[2 * i + 1]));
+    tot += ms;
+  }
+  if (total_ms) *total_ms = tot;
+  if (launches) *launches = g_timing.used;
+  for (hipEvent_t e : g_timing.ev) hipEventDestroy(e);
+  g_timing.ev.clear();
+  g_timing.used = 0;
+  return MOE_OK;
+}
+
+}  // extern "C"

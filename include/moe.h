@@ -1,0 +1,197 @@
+/*
+ * moe.h -- C ABI of libmoe.so: a sparse mixture-of-experts layer computed
+ * directly from low-bit block-quantised expert weights on an MI355X (gfx950).
+ *
+ * What the layer computes.  Each token x[t] (fp32, length d) is sent to the
+ * k experts with the largest router logits out of E small SwiGLU experts, as
+ * in the 48-layer, 512-experts-per-layer model that routes about ten experts
+ * per token [cnyes profile of Strata, section "Strata 到底是什麼？"], plus
+ * one always-on shared expert kept next to the router [same page, section
+ * "三層記憶體", part 1].  Expert weights stay in their low-bit blocks and the
+ * kernels multiply from them without first expanding them to full precision
+ * [strata-mlx wiki, opening feature list, first item; devlabs blog "32GB Mac
+ * mini 6 跑 125B 大模型", section 核心技术特点].  Decode and draft
+ * verification pass up to eight tokens at once (one real token plus seven
+ * drafts) [devlabs blog, section 核心技术特点, MTP item]; prompts are read in
+ * chunks of up to 8192 tokens [agentlenshq article, section "Strata 如何让
+ * 125 B 模型适配 12-24 GB 显存", last item].
+ *
+ *   logits[t][e] = x[t] . Wr[e] + bias[e]
+ *   idx[t][0..k)  = the k largest logits, ties to the lower expert index
+ *   w[t][r]       = softmax of the k selected logits (rank order)
+ *   FFN_e(x)      = Wd_e ( silu(Wg_e x) * (Wu_e x) ),  silu(z) = z / (1 + e^-z)
+ *   y[t]          = sum_r w[t][r] FFN_{idx[t][r]}(x[t]) + FFN_shared(x[t])
+ *
+ * Canonical block format (input of moe_pack_experts).  A block holds 32
+ * consecutive weights of one matrix row: bytes [0,2) are an IEEE fp16 scale
+ * (little endian), bytes [2, 2+4b) are 32 codes of b bits (b = 2 or 3); code j
+ * is bits [b*j, b*j+b) of the little-endian bitstream of those bytes and
+ * stands for the integer q_j - 2^(b-1).  Weight = scale * (q_j - 2^(b-1)).
+ * One expert is gate [I][d], up [I][d], down [d][I] in that order, row-major,
+ * each row a run of blocks along the matrix's input dimension.  E experts are
+ * stored back to back; the shared expert is a separate buffer of the same
+ * layout with its own intermediate size.
+ *
+ * Conventions for every entry point:
+ *   - Return value: MOE_OK (0) or a positive MOE_ERR_* code.  On error,
+ *     moe_last_error() returns a message for the calling thread.  Nothing is
+ *     launched when an argument check fails.  No call aborts the process.
+ *   - Device pointers are caller-owned HIP device memory, 16-byte aligned
+ *     (checked).  The library never allocates or frees device memory.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  All GPU work is
+ *     enqueued asynchronously on it; apart from moe_pack_experts no call waits
+ *     for the GPU, and the forward calls may be captured into a HIP graph.
+ *   - Host handles (moe_layer) are immutable after packing and may be shared
+ *     between threads and streams.  A workspace must not be used by two calls
+ *     that can overlap on the GPU.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    MOE_OK = 0,
+    MOE_ERR_ARG = 1,          /* bad pointer, size, shape or alignment */
+    MOE_ERR_UNSUPPORTED = 2,  /* valid but not supported shape (see moe_packed_bytes) */
+    MOE_ERR_WORKSPACE = 3,    /* workspace smaller than moe_workspace_bytes() */
+    MOE_ERR_HIP = 4,          /* a HIP runtime call failed */
+    MOE_ERR_DATA = 5          /* input data out of contract (e.g. an fp16 scale that is inf/nan) */
+};
+
+typedef struct moe_layer_desc {
+    int32_t d_model;      /* d: hidden size; multiple of 256 */
+    int32_t n_experts;    /* E: routed experts, 1..4096 */
+    int32_t d_ff;         /* I: routed-expert intermediate size; multiple of 32 */
+    int32_t d_ff_shared;  /* shared-expert intermediate size, multiple of 32, or 0 = none */
+    int32_t top_k;        /* k: 1..min(E, 16) */
+    int32_t bits;         /* code width b: 2 or 3 */
+    int32_t block;        /* weights per block: must be 32 */
+} moe_layer_desc;
+
+/* Opaque host handle of one packed layer: shapes plus device pointers into
+ * the caller's packed buffer. */
+typedef struct moe_layer moe_layer;
+
+/* Optional routing inputs/outputs of moe_layer_forward.
+ *   in_idx/in_w   [T][k]: if both non-NULL the router is skipped and this
+ *                 routing is used (rank order; expert ids must be in [0,E)
+ *                 and distinct within a row; an entry outside [0,E) is
+ *                 skipped, i.e. contributes nothing).
+ *   out_logits    [T][E]: router logits (ignored when routing is forced).
+ *   out_idx/out_w [T][k]: the routing used.
+ * Any pointer may be NULL. */
+typedef struct moe_route_io {
+    const int32_t *in_idx;
+    const float *in_w;
+    float *out_logits;
+    int32_t *out_idx;
+    float *out_w;
+} moe_route_io;
+
+/* Message describing the last error on this thread ("" if none). */
+const char *moe_last_error(void);
+
+/* Bytes of device memory moe_pack_experts needs for one layer.
+ * Rejects (MOE_ERR_ARG / MOE_ERR_UNSUPPORTED) d % 256 != 0, d_ff % 32 != 0,
+ * d_ff_shared % 32 != 0, k < 1, k > E, k > 16, E > 4096, bits not in {2,3},
+ * block != 32. */
+int moe_packed_bytes(const moe_layer_desc *desc, size_t *bytes);
+
+/* Re-tile one layer's canonical blocks into the device layout the kernels
+ * stream (lossless integer shuffling: codes stay b-bit, scales stay fp16; no
+ * weight is expanded to full precision) and copy the router.
+ *   experts_canon  device, E * expert_bytes canonical bytes
+ *   shared_canon   device, canonical bytes of the shared expert, or NULL when
+ *                  d_ff_shared == 0
+ *   router_w       device fp32 [E][d]
+ *   router_bias    device fp32 [E], or NULL for a zero bias
+ *   packed         device, packed_bytes >= moe_packed_bytes(); must stay
+ *                  alive and unchanged while the handle is used
+ *   out            receives a new host handle (release with moe_layer_release)
+ * This call synchronises `stream` once at the end: it checks that every scale
+ * is a finite fp16 value with |scale| < 8192 (so that scale * code stays in
+ * fp16 range) and returns MOE_ERR_DATA otherwise. */
+int moe_pack_experts(const moe_layer_desc *desc, const void *experts_canon, const void *shared_canon,
+                     const float *router_w, const float *router_bias, void *packed, size_t packed_bytes,
+                     moe_layer **out, void *stream);
+
+/* Free the host handle (the packed device buffer stays the caller's). */
+int moe_layer_release(moe_layer *layer);
+
+/* Copy the layer's shape description. */
+int moe_layer_get_desc(const moe_layer *layer, moe_layer_desc *out);
+
+/* Top-k selection and gate weights on given logits (the routing step alone):
+ *   logits device fp32 [T][E], idx device int32 [T][k], w device fp32 [T][k].
+ * Order: logit descending, ties to the lower expert index (-0.0 == +0.0).
+ * Gate weights: m = largest selected logit, e_r = exp(l_r - m) computed in
+ * fp64 by a fixed argument reduction (by ln 2) and a degree-13 Taylor
+ * polynomial, S = sum of e_r in rank order, w_r = fp32(e_r / S).  Bit-exact
+ * with a CPU implementation following the same steps.  Logits must be
+ * finite (non-finite values give unspecified but in-range indices).
+ * 1 <= k <= min(E, 16), 1 <= E <= 4096, T >= 0. */
+int moe_route_topk(const float *logits, int T, int E, int k, int32_t *idx, float *w, void *stream);
+
+/* Device scratch needed by moe_layer_forward / moe_stack_forward for up to T
+ * tokens per call with this layer's shapes. */
+int moe_workspace_bytes(const moe_layer *layer, int T, size_t *bytes);
+
+/* Clear the control words of a new workspace (enqueued on `stream`).  Must be
+ * called once before a workspace is first used, and again if its memory has
+ * been used for anything else in between.  The forward calls leave the
+ * control words cleared for the next call. */
+int moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
+
+/* One layer: y[T][d] = MoE(x[T][d]).  T = 0 is a no-op.  T <= 8 runs the
+ * decode/verify kernels (experts streamed once per call with 128-bit loads
+ * and multiplied from their codes); T > 8 runs the chunked-prefill kernels
+ * (grouped matrix multiply on the matrix cores).  x and y must not alias.
+ * `route` may be NULL.  ws_bytes >= moe_workspace_bytes(layer, T). */
+int moe_layer_forward(const moe_layer *layer, const float *x, int T, float *y, const moe_route_io *route,
+                      void *ws, size_t ws_bytes, void *stream);
+
+/* A stack of layers with RMSNorm (unit weight) between consecutive layers:
+ *   h_0 = x,  y_l = MoE_l(h_l),  h_{l+1} = y_l / sqrt(mean(y_l^2) + eps),
+ *   y = y_{n-1}.
+ * All layers must have equal d_model.  Optional per-layer outputs:
+ *   y_layers   device fp32 [n][T][d] (every y_l), or NULL
+ *   idx_layers device int32 [n][T][k], w_layers device fp32 [n][T][k], or NULL.
+ * ws_bytes >= the largest moe_workspace_bytes over the layers. */
+int moe_stack_forward(const moe_layer *const *layers, int n_layers, const float *x, int T, float eps,
+                      float *y, float *y_layers, int32_t *idx_layers, float *w_layers, void *ws,
+                      size_t ws_bytes, void *stream);
+
+/* y[t] = x[t] / sqrt(mean(x[t]^2) + eps), fp32 in and out, d % 4 == 0. */
+int moe_rmsnorm(const float *x, int T, int d, float eps, float *y, void *stream);
+
+/* Test export of device-decoded weights of one matrix of one expert
+ * (expert = -1: shared expert; mat 0 = gate, 1 = up, 2 = down), read back
+ * from the packed layout:
+ *   codes  device int8 [rows][cols] signed codes, or NULL
+ *   w_f32  device fp32 [rows][cols] scale * code (exact), or NULL
+ *   w_f16  device uint16 [rows][cols] fp16 bits of scale * code (round to
+ *          nearest even; exact for 2-bit codes), or NULL
+ * rows x cols is [I][d] for gate/up and [d][I] for down. */
+int moe_debug_unpack(const moe_layer *layer, int expert, int mat, int8_t *codes, float *w_f32,
+                     uint16_t *w_f16, void *stream);
+
+/* Per-kernel timing for measurement: while enabled, the library brackets
+ * every launch of the chosen kernel class with a pair of HIP events on the
+ * launch stream.  class 0 = decode gate/up expert kernel, 1 = decode down
+ * expert kernel, 2 = router, 3 = prefill gate/up grouped GEMM, 4 = prefill
+ * down grouped GEMM.  moe_timing_stop waits for the recorded events and
+ * returns the summed duration and the number of launches. */
+int moe_timing_start(int kernel_class, int max_launches);
+int moe_timing_stop(double *total_ms, int *launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

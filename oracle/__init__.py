@@ -58,6 +58,8 @@ def _declare(L):
     L.orc_half_to_double.restype = ctypes.c_double
     L.orc_double_to_half.argtypes = [ctypes.c_double]
     L.orc_double_to_half.restype = ctypes.c_uint16
+    L.orc_double_to_half_array.argtypes = [_P, ctypes.c_long, _P]
+    L.orc_double_to_half_array.restype = None
     L.orc_unpack_block.argtypes = [_P, _I, _P, _P]
     L.orc_unpack_block.restype = None
     L.orc_unpack_matrix.argtypes = [_P, _I, _I, _I, _P, _P]
@@ -107,6 +109,14 @@ def half_to_double(bits: int) -> float:
 def double_to_half(v: float) -> int:
     """Binary16 bit pattern nearest to v (ties to even)."""
     return lib().orc_double_to_half(v)
+
+
+def double_to_half_array(v):
+    """Binary16 bit patterns (uint16) nearest to each value (ties to even)."""
+    v = _c(v, np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    lib().orc_double_to_half_array(_ptr(v), v.size, _ptr(out))
+    return out
 
 
 def exp64(z):

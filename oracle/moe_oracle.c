@@ -98,6 +98,12 @@ uint16_t orc_double_to_half(double v)
     return sign | (uint16_t)((be + 15) << 10) | fr;
 }
 
+/* Array form of orc_double_to_half. */
+void orc_double_to_half_array(const double *v, long n, uint16_t *out)
+{
+    for (long i = 0; i < n; ++i) out[i] = orc_double_to_half(v[i]);
+}
+
 /* ------------------------------------------------------------------ */
 /* Canonical block: bytes [0,2) fp16 scale (little endian), then 4*b     */
 /* bytes of codes.  Readings R1, R2.                                     */

@@ -1,0 +1,239 @@
+"""GPU parity of the decode path (T <= 8) against the CPU oracle.
+
+Bars: unpacked codes and dequantised weights bit-exact; top-k indices and
+gate weights bit-exact given the same logits; layer outputs within a global
+infinity-norm relative error of 2e-3 with the oracle fed the GPU's own
+routing (teacher forcing), per layer for stacks.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import oracle
+from moe_inputs.device import packed_layer, activations_device
+from tests.helpers import TOL_LAYER, oracle_layer, rel_err_inf, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def bqe():
+    import bit_quantized_experts_amd as m
+    m.lib()
+    return m
+
+
+def _forward(bqe, L, x_np, route=True):
+    T = x_np.shape[0]
+    d, E, k = L.desc.d_model, L.desc.n_experts, L.desc.top_k
+    x = activations_device(x_np)
+    y = torch.empty((T, d), dtype=torch.float32, device=DEV)
+    logits = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    ws = bqe.new_workspace(L.workspace_bytes(T))
+    r = bqe.RouteIO(None, None, logits.data_ptr(), idx.data_ptr(), w.data_ptr())
+    bqe.moe_layer_forward(L.handle, x, y, ws, r)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), logits.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
+
+
+def _check_layer(wl, layer, L, x_np, bqe, tag):
+    say(f"[decode] {tag}: T={x_np.shape[0]} d={wl.d} E={wl.E} k={wl.k} bits={wl.bits} Is={wl.Is}")
+    y, logits, idx, w = _forward(bqe, L, x_np)
+    # routing: bit-exact against the oracle's selection on the GPU's logits
+    oi, ow = oracle.topk(logits, wl.k)
+    assert np.array_equal(idx, oi), tag
+    assert np.array_equal(w.view(np.uint32), ow.view(np.uint32)), tag
+    # logits close to the oracle's fp64 router
+    W, b = mi.router(wl, layer)
+    ol = oracle.router_logits(x_np, W, b)
+    assert rel_err_inf(logits, ol) < 1e-5, tag
+    # layer output, teacher-forced with the GPU routing
+    OL = oracle_layer(wl, layer, idx.reshape(-1))
+    oy, _, _, _ = oracle.layer_forward(OL, x_np, force_idx=idx, force_w=w)
+    err = rel_err_inf(y, oy)
+    say(f"    rel err {err:.3e}")
+    assert err <= TOL_LAYER, (tag, err)
+    assert np.all(np.isfinite(y))
+    return y, idx, w, err
+
+
+def test_generator_cpu_equals_gpu():
+    for bits in (2, 3):
+        for first, count in ((0, 1000), (123457, 4097)):
+            a = mi.canon_blocks(0, 5, mi.STREAM_ROUTED, first, count, bits, 0.01, 0.05, device="cpu")
+            b = mi.canon_blocks(0, 5, mi.STREAM_ROUTED, first, count, bits, 0.01, 0.05, device=DEV).cpu()
+            assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+@pytest.mark.parametrize("shape", ["tiny", "full"])
+def test_debug_unpack_bitexact(bqe, bits, shape):
+    if shape == "tiny":
+        wl = mi.small(mi.WORKLOADS["tiny"], bits=bits, Is=96)
+        experts = list(range(wl.E)) + [-1]
+    else:
+        wl = mi.small(mi.WORKLOADS["layer_t1"], bits=bits, E=12)
+        experts = [0, 5, 11, -1]
+    say(f"[unpack] {shape} bits={bits}")
+    L = packed_layer(wl, 0)
+    for e in experts:
+        canon = mi.expert_canon(wl, 0, e).numpy()
+        I = wl.Is if e < 0 else wl.I
+        parts = oracle.split_expert(canon, wl.d, I, bits)
+        for mat, (rows, cols) in enumerate(((I, wl.d), (I, wl.d), (wl.d, I))):
+            codes = torch.empty((rows, cols), dtype=torch.int8, device=DEV)
+            w32 = torch.empty((rows, cols), dtype=torch.float32, device=DEV)
+            w16 = torch.empty((rows, cols), dtype=torch.int16, device=DEV)
+            bqe.moe_debug_unpack(L.handle, e, mat, codes, w32, w16)
+            torch.cuda.synchronize()
+            oc, _ = oracle.unpack_matrix(parts[mat], rows, cols, bits)
+            ow = oracle.dequant_matrix(parts[mat], rows, cols, bits)
+            assert np.array_equal(codes.cpu().numpy(), oc), (e, mat)
+            assert np.array_equal(w32.cpu().numpy().astype(np.float64), ow), (e, mat)
+            o16 = oracle.double_to_half_array(ow)
+            assert np.array_equal(w16.cpu().numpy().view(np.uint16), o16), (e, mat)
+
+
+@pytest.mark.parametrize("E,k,T", [(16, 2, 5), (512, 10, 64), (512, 16, 33), (4096, 8, 9), (3, 3, 7), (1, 1, 4)])
+def test_route_topk_bitexact(bqe, E, k, T):
+    say(f"[topk] E={E} k={k} T={T}")
+    g = np.random.default_rng(E * 31 + k)
+    cases = [g.standard_normal((T, E)).astype(np.float32) * 2,
+             g.integers(0, 3, (T, E)).astype(np.float32),
+             np.where(g.random((T, E)) < 0.5, -0.0, 0.0).astype(np.float32)]
+    if E == 512:
+        cases.append(mi.direct_logits(mi.WORKLOADS["layer_t1"], T))
+    for l in cases:
+        lt = torch.from_numpy(l).to(DEV)
+        idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+        w = torch.empty((T, k), dtype=torch.float32, device=DEV)
+        bqe.moe_route_topk(lt, k, idx, w)
+        torch.cuda.synchronize()
+        oi, ow = oracle.topk(l, k)
+        assert np.array_equal(idx.cpu().numpy(), oi)
+        assert np.array_equal(w.cpu().numpy().view(np.uint32), ow.view(np.uint32))
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+@pytest.mark.parametrize("Is", [0, 64, 96])
+def test_layer_tiny_all_T(bqe, bits, Is):
+    wl = mi.small(mi.WORKLOADS["tiny"], bits=bits, Is=Is, zipf_s=1.1 if Is else None)
+    L = packed_layer(wl, 0)
+    for T in range(1, 9):
+        x = mi.activations(wl, T=T, stream=T)
+        _check_layer(wl, 0, L, x, bqe, f"tiny bits={bits} Is={Is} T={T}")
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_layer_full_size(bqe, bits):
+    base = mi.WORKLOADS["layer_t1"] if bits == 2 else mi.WORKLOADS["stack_3bit"]
+    wl = mi.small(base, layers=1)
+    L = packed_layer(wl, 0)
+    for T in (1, 3, 8):
+        x = mi.activations(wl, T=T, stream=100 + T)
+        _check_layer(wl, 0, L, x, bqe, f"full bits={bits} T={T}")
+
+
+def test_forced_routing_and_invalid_entries(bqe):
+    wl = mi.small(mi.WORKLOADS["tiny"], Is=64)
+    L = packed_layer(wl, 0)
+    T = 6
+    x_np = mi.activations(wl, T=T, stream=7)
+    g = np.random.default_rng(9)
+    idx = np.stack([g.permutation(wl.E)[:wl.k] for _ in range(T)]).astype(np.int32)
+    w = g.random((T, wl.k)).astype(np.float32)
+    idx[2, 1] = wl.E + 5   # out of range: skipped
+    idx[4, 0] = -1         # out of range: skipped
+    x = activations_device(x_np)
+    y = torch.empty((T, wl.d), dtype=torch.float32, device=DEV)
+    fi = torch.from_numpy(idx).to(DEV)
+    fw = torch.from_numpy(w).to(DEV)
+    ws = bqe.new_workspace(L.workspace_bytes(T))
+    r = bqe.RouteIO(fi.data_ptr(), fw.data_ptr(), None, None, None)
+    bqe.moe_layer_forward(L.handle, x, y, ws, r)
+    torch.cuda.synchronize()
+    wz = w.copy()
+    wz[2, 1] = 0.0
+    wz[4, 0] = 0.0
+    iz = idx.copy()
+    iz[2, 1] = 0
+    iz[4, 0] = 0
+    OL = oracle_layer(wl, 0, iz.reshape(-1))
+    oy, _, _, _ = oracle.layer_forward(OL, x_np, force_idx=iz, force_w=wz)
+    assert rel_err_inf(y.cpu().numpy(), oy) <= TOL_LAYER
+
+
+def test_determinism_and_T8_vs_T1(bqe):
+    wl = mi.small(mi.WORKLOADS["layer_t1"], layers=1)
+    L = packed_layer(wl, 0)
+    x = mi.activations(wl, T=8, stream=55)
+    y1, _, i1, w1 = _forward(bqe, L, x)
+    y2, _, i2, w2 = _forward(bqe, L, x)
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    assert np.array_equal(i1, i2) and np.array_equal(w1, w2)
+    # verify pass == token-by-token decode (routing bit-exact, outputs within fp32 rounding)
+    for t in range(8):
+        yt, _, it, wt = _forward(bqe, L, x[t:t + 1])
+        assert np.array_equal(it[0], i1[t]) and np.array_equal(wt[0], w1[t])
+        assert rel_err_inf(yt[0], y1[t]) < 1e-5
+
+
+def test_unused_experts_do_not_change_output(bqe):
+    wl = mi.small(mi.WORKLOADS["tiny"], Is=64, zipf_s=1.1)
+    x = mi.activations(wl, T=3, stream=77)
+    L = packed_layer(wl, 0)
+    y, _, idx, w = _forward(bqe, L, x)
+    used = set(idx.reshape(-1).tolist())
+    eb = wl.expert_bytes()
+
+    def scramble(canon, shared):
+        g = torch.Generator(device="cpu").manual_seed(3)
+        for e in range(wl.E):
+            if e not in used:
+                noise = torch.randint(0, 256, (eb,), generator=g, dtype=torch.uint8)
+                blk = noise.view(-1, wl.block_bytes())
+                blk[:, 1] &= 0x3F  # keep scales finite and small
+                canon[e * eb:(e + 1) * eb] = noise.to(canon.device)
+
+    L2 = packed_layer(wl, 0, canon_hook=scramble)
+    y2, _, idx2, w2 = _forward(bqe, L2, x)
+    assert np.array_equal(idx, idx2) and np.array_equal(w, w2)
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+
+
+@pytest.mark.parametrize("which", ["tiny", "full"])
+def test_stack_teacher_forced(bqe, which):
+    if which == "tiny":
+        wl = mi.small(mi.WORKLOADS["tiny"], Is=64, zipf_s=1.1, layers=5)
+        T = 7
+    else:
+        wl = mi.small(mi.WORKLOADS["stack_t8_2bit"], layers=3)
+        T = 8
+    layers = [packed_layer(wl, l) for l in range(wl.layers)]
+    x_np = mi.activations(wl, T=T, stream=5)
+    nL, d, k = wl.layers, wl.d, wl.k
+    x = activations_device(x_np)
+    y = torch.empty((T, d), dtype=torch.float32, device=DEV)
+    yl = torch.empty((nL, T, d), dtype=torch.float32, device=DEV)
+    il = torch.empty((nL, T, k), dtype=torch.int32, device=DEV)
+    wlr = torch.empty((nL, T, k), dtype=torch.float32, device=DEV)
+    ws = bqe.new_workspace(max(L.workspace_bytes(T) for L in layers))
+    say(f"[stack] {which} layers={nL} T={T}")
+    bqe.moe_stack_forward([L.handle for L in layers], x, y, ws, 1e-6, yl, il, wlr)
+    torch.cuda.synchronize()
+    yl, il, wlr = yl.cpu().numpy(), il.cpu().numpy(), wlr.cpu().numpy()
+    assert np.array_equal(y.cpu().numpy(), yl[-1])
+    h = x_np
+    for l in range(nL):
+        if l > 0:
+            h = oracle.rmsnorm(yl[l - 1], 1e-6)
+        OL = oracle_layer(wl, l, il[l].reshape(-1))
+        oy, ologits, _, _ = oracle.layer_forward(OL, h, force_idx=il[l], force_w=wlr[l])
+        err = rel_err_inf(yl[l], oy)
+        say(f"    layer {l}: rel err {err:.3e}")
+        assert err <= TOL_LAYER, (l, err)
