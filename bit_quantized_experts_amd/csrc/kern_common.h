@@ -90,29 +90,89 @@ DEVI float wave_sum(float v) {
 }
 
 // ---------------------------------------------------------------------------
+// Cross-lane moves that stay in the vector ALU (DPP and the gfx950 permlane
+// swaps), for reductions whose operator is commutative: every step pairs
+// each lane with a lane of the other half of a growing group, so after the
+// six steps every lane holds the result over all 64 lanes.
+//   quad_perm [1,0,3,2] and [2,3,0,1]: partners inside a group of 4 lanes,
+//   row_half_mirror: lane i <-> 7-i inside 8, row_mirror: i <-> 15-i inside
+//   16, permlane16 swap: row 0 <-> row 1 and row 2 <-> row 3, permlane32
+//   swap: lanes 0..31 <-> 32..63.
+// ---------------------------------------------------------------------------
+DEVI uint32_t dpp_perm(uint32_t v, int step) {
+  switch (step) {
+    case 0: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
+    case 1: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);
+    case 2: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, true);
+    default: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, true);
+  }
+}
+
+DEVI uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+DEVI uint64_t u64_of(uint32_t lo, uint32_t hi) { return ((uint64_t)hi << 32) | lo; }
+
+// Maximum of a 64-bit key over the wavefront, in every lane.
+DEVI uint64_t wave_max_u64(uint64_t k) {
+#pragma unroll
+  for (int st = 0; st < 4; ++st) k = umax64(k, u64_of(dpp_perm((uint32_t)k, st), dpp_perm((uint32_t)(k >> 32), st)));
+  {
+    auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)k, (uint32_t)k, false, false);
+    auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(k >> 32), (uint32_t)(k >> 32), false, false);
+    k = umax64(u64_of(lo[0], hi[0]), u64_of(lo[1], hi[1]));
+  }
+  {
+    auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)k, (uint32_t)k, false, false);
+    auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(k >> 32), (uint32_t)(k >> 32), false, false);
+    k = umax64(u64_of(lo[0], hi[0]), u64_of(lo[1], hi[1]));
+  }
+  return k;
+}
+
+// Sum over the 16 lanes of a row, in every lane of the row (fixed order).
+DEVI float row16_sum(float v) {
+#pragma unroll
+  for (int st = 0; st < 4; ++st) v += __uint_as_float(dpp_perm(__float_as_uint(v), st));
+  return v;
+}
+
+// ---------------------------------------------------------------------------
 // Deterministic fp64 exponential for the gate weights.  Steps: n = rint(z /
 // ln2); r = z - n*ln2 as two fused steps with ln2 split into a high part (the
 // double nearest ln2) and a low part (the double nearest the remainder);
 // p = sum_{i=0..13} r^i/i! by Horner with fused multiply-add, from i = 13
 // down; result = p * 2^n.  Coefficients are 1/i! rounded once to double
 // (i! <= 13! is exact in double, so 1.0 / i! is one correctly rounded
-// division).  Any IEEE fp64 implementation of the same steps returns the same
-// bits.
+// division, done at compile time).  Any IEEE fp64 implementation of the same
+// steps returns the same bits.
 // ---------------------------------------------------------------------------
-__host__ __device__ constexpr double moe_fact(int i) { return i <= 1 ? 1.0 : (double)i * moe_fact(i - 1); }
+struct MoeExpCoeffs {
+  double c[14];
+};
+// 1/i! for i = 0..13, evaluated at compile time: i! is built by exact
+// multiplications (13! < 2^53) and divided into 1.0 once.
+__host__ __device__ constexpr MoeExpCoeffs moe_exp_coeffs() {
+  MoeExpCoeffs r{};
+  double f = 1.0;
+  for (int i = 0; i < 14; ++i) {
+    if (i > 1) f *= (double)i;
+    r.c[i] = 1.0 / f;
+  }
+  return r;
+}
 
 DEVI double moe_exp64(double z) {
 #pragma clang fp contract(off)
   constexpr double kInvLn2 = 1.44269504088896340735992468100189214;   // 1/ln 2
   constexpr double kLn2Hi = 0.693147180559945309417232121458176568;   // ln 2
   constexpr double kLn2Lo = 2.319046813846299558417771e-17;            // ln 2 - kLn2Hi
+  constexpr MoeExpCoeffs C = moe_exp_coeffs();
   if (z < -1080.0) return 0.0;
   if (z > 709.0) return __builtin_huge_val();
   double n = __builtin_rint(z * kInvLn2);
   double r = __builtin_fma(-n, kLn2Hi, z);
   r = __builtin_fma(-n, kLn2Lo, r);
-  double p = 1.0 / moe_fact(13);
+  double p = C.c[13];
 #pragma unroll
-  for (int i = 12; i >= 0; --i) p = __builtin_fma(p, r, 1.0 / moe_fact(i));
+  for (int i = 12; i >= 0; --i) p = __builtin_fma(p, r, C.c[i]);
   return __builtin_ldexp(p, (int)n);
 }

@@ -123,17 +123,19 @@ PackedLayout packed_layout(const moe_layer_desc* D, const moe_expert_layout& ex,
 
 // ------------------------------------------------------------- workspace ---
 struct WsLayout {
-  int64_t ctrl, logits, idx, w, n_slots, slot_expert, slot_w, xfrag, xsum, hfrag, hsum, ypart, ystack, total;
-  int max_slots, S, nbI;
+  int64_t ctrl, lp, ss_part, rnorm, logits, idx, w, n_slots, slot_expert, slot_w, xfrag, xsum, hfrag, hsum, ypart,
+      total;
+  int max_slots, S, nbI, n_cs;
 };
 
-int64_t ctrl_bytes(int d) { return moe_align256((int64_t)(1 + d / 16) * 4); }
+int64_t ctrl_bytes() { return 256; }
 
 int down_splits(const moe_layer* L, int max_slots) {
   const int n_rg = L->ex.down.n_rg;
   int S = env_int("MOE_DOWN_SPLITS", 0);
   if (S <= 0) S = (512 + n_rg - 1) / n_rg;
   if (S > max_slots) S = max_slots;
+  if (S > MOE_MAX_IN_SPLITS) S = MOE_MAX_IN_SPLITS;
   if (S < 1) S = 1;
   return S;
 }
@@ -144,9 +146,13 @@ WsLayout ws_layout_decode(const moe_layer* L, int T) {
   W.max_slots = (T * k < E ? T * k : E) + (L->Is > 0 ? 1 : 0);
   W.nbI = (L->I > L->Is ? L->I : L->Is) / 32;
   W.S = down_splits(L, W.max_slots);
+  W.n_cs = d / MOE_ROUTE_COLS;
   int64_t o = 0;
   auto take = [&](int64_t bytes) { int64_t r = o; o += moe_align256(bytes); return r; };
-  W.ctrl = take(ctrl_bytes(d));
+  W.ctrl = take(ctrl_bytes());
+  W.lp = take((int64_t)W.n_cs * T * E * 4);
+  W.ss_part = take((int64_t)W.n_cs * T * 4);
+  W.rnorm = take(8 * 4);
   W.logits = take((int64_t)T * E * 4);
   W.idx = take((int64_t)T * k * 4);
   W.w = take((int64_t)T * k * 4);
@@ -158,7 +164,6 @@ WsLayout ws_layout_decode(const moe_layer* L, int T) {
   W.hfrag = take((int64_t)W.max_slots * W.nbI * 64 * 8 * 2);
   W.hsum = take((int64_t)W.max_slots * W.nbI * 16 * 4);
   W.ypart = take((int64_t)W.S * 8 * d * 4);
-  W.ystack = take((int64_t)2 * 8 * d * 4);
   W.total = o;
   return W;
 }
@@ -198,53 +203,75 @@ ExpertSet expert_set(const moe_layer* L) {
   return X;
 }
 
-// One decode layer (T <= 8).  x may be the previous layer's output (norm = 1).
-int decode_layer(const moe_layer* L, const float* x, int norm, float eps, int T, float* y,
-                 const moe_route_io* r, uint8_t* ws, hipStream_t s) {
+// Input of a decode layer: the caller's x (S = 1) or the previous layer's
+// down partials in the workspace (S splits, RMSNorm applied).
+struct LayerInput {
+  const float* p;
+  int S;
+  int64_t stride;
+  int norm;
+};
+
+// One decode layer (T <= 8): route -> select -> gate/up -> down.  The result
+// is left as split partials in the workspace (ypart, W.S splits).
+int decode_layer(const moe_layer* L, const LayerInput& in, float eps, int T, float* y_prev_out,
+                 const moe_route_io* r, uint8_t* ws, hipStream_t s, int* S_out) {
   const WsLayout W = ws_layout_decode(L, T);
   const int d = L->d, E = L->E;
+  const bool forced = r && r->in_idx && r->in_w;
+  int slot;
+
   RouteArgs ra{};
-  ra.x = x;
-  ra.norm = norm;
-  ra.eps = eps;
+  ra.in = in.p;
+  ra.S_in = in.S;
+  ra.in_stride = in.stride;
   ra.Wr = L->router_w;
-  ra.br = L->router_b;
   ra.T = T;
   ra.d = d;
   ra.E = E;
-  ra.k = L->k;
-  ra.has_shared = L->Is > 0;
   ra.code_off = 1 << (L->bits - 1);
-  ra.rows_per_wg = env_int("MOE_ROUTE_ROWS", 4);
-  if (ra.rows_per_wg < 1) ra.rows_per_wg = 4;
-  const bool forced = r && r->in_idx && r->in_w;
-  ra.fidx = forced ? r->in_idx : nullptr;
-  ra.fw = forced ? r->in_w : nullptr;
-  ra.logits = reinterpret_cast<float*>(ws + W.logits);
-  ra.idx = reinterpret_cast<int32_t*>(ws + W.idx);
-  ra.w = reinterpret_cast<float*>(ws + W.w);
-  ra.out_logits = (r && !forced) ? r->out_logits : nullptr;
-  ra.out_idx = r ? r->out_idx : nullptr;
-  ra.out_w = r ? r->out_w : nullptr;
-  ra.n_slots = reinterpret_cast<int32_t*>(ws + W.n_slots);
-  ra.slot_expert = reinterpret_cast<int32_t*>(ws + W.slot_expert);
-  ra.slot_w = reinterpret_cast<float*>(ws + W.slot_w);
+  ra.do_logits = !forced;
+  ra.lp = reinterpret_cast<float*>(ws + W.lp);
+  ra.ss_part = reinterpret_cast<float*>(ws + W.ss_part);
   ra.xfrag = reinterpret_cast<_Float16*>(ws + W.xfrag);
   ra.xsum = reinterpret_cast<float*>(ws + W.xsum);
-  ra.counter = reinterpret_cast<uint32_t*>(ws + W.ctrl);
-  int n_wg = forced ? (d / 32 + 3) / 4 : (E + ra.rows_per_wg - 1) / ra.rows_per_wg;
-  if (n_wg < 1) n_wg = 1;
-  int slot;
+  ra.y_out = y_prev_out;
   timed_begin(2, s, &slot);
-  HIPCHK(launch_route_decode(ra, n_wg, s));
+  HIPCHK(launch_route(ra, s));
   timed_end(slot, s);
+
+  SelectArgs sa{};
+  sa.lp = ra.lp;
+  sa.ss_part = ra.ss_part;
+  sa.br = L->router_b;
+  sa.n_cs = W.n_cs;
+  sa.T = T;
+  sa.d = d;
+  sa.E = E;
+  sa.k = L->k;
+  sa.norm = in.norm;
+  sa.eps = eps;
+  sa.fidx = forced ? r->in_idx : nullptr;
+  sa.fw = forced ? r->in_w : nullptr;
+  sa.logits = reinterpret_cast<float*>(ws + W.logits);
+  sa.idx = reinterpret_cast<int32_t*>(ws + W.idx);
+  sa.w = reinterpret_cast<float*>(ws + W.w);
+  sa.rnorm = reinterpret_cast<float*>(ws + W.rnorm);
+  sa.out_logits = (r && !forced) ? r->out_logits : nullptr;
+  sa.out_idx = r ? r->out_idx : nullptr;
+  sa.out_w = r ? r->out_w : nullptr;
+  HIPCHK(launch_select(sa, s));
 
   const ExpertSet X = expert_set(L);
   GuArgs ga{};
   ga.X = X;
-  ga.n_slots = ra.n_slots;
-  ga.slot_expert = ra.slot_expert;
-  ga.slot_w = ra.slot_w;
+  ga.idx = sa.idx;
+  ga.w = sa.w;
+  ga.k = L->k;
+  ga.n_slots = reinterpret_cast<int32_t*>(ws + W.n_slots);
+  ga.slot_expert = reinterpret_cast<int32_t*>(ws + W.slot_expert);
+  ga.slot_w = reinterpret_cast<float*>(ws + W.slot_w);
+  ga.rnorm = sa.rnorm;
   ga.xfrag = ra.xfrag;
   ga.xsum = ra.xsum;
   ga.hfrag = reinterpret_cast<_Float16*>(ws + W.hfrag);
@@ -252,20 +279,27 @@ int decode_layer(const moe_layer* L, const float* x, int norm, float eps, int T,
   ga.E = E;
   ga.I = L->I;
   ga.Is = L->Is;
+  ga.T = T;
   ga.n_kg = d / 256;
   ga.bits = L->bits;
   ga.nbI = W.nbI;
   ga.code_off = ra.code_off;
-  int gu_nw = env_int("MOE_GU_WAVES", 0);
-  if (gu_nw <= 0 || gu_nw > 8) gu_nw = ga.n_kg < 5 ? ga.n_kg : 5;
-  timed_begin(0, s, &slot);
-  HIPCHK(launch_gu_decode(ga, W.nbI, W.max_slots, gu_nw, s));
+  ga.has_shared = L->Is > 0;
+  {
+    const int max_items = (W.max_slots - (ga.has_shared ? 1 : 0)) * ((L->I / 16 + 3) / 4) +
+                          (ga.has_shared ? (L->Is / 16 + 3) / 4 : 0);
+    int n_wg = env_int("MOE_GU_WGS", 256);
+    if (n_wg > max_items) n_wg = max_items;
+    if (n_wg < 1) n_wg = 1;
+    timed_begin(0, s, &slot);
+    HIPCHK(launch_gu_decode(ga, n_wg, s));
+  }
   timed_end(slot, s);
 
   DownArgs da{};
   da.X = X;
-  da.n_slots = ra.n_slots;
-  da.slot_expert = ra.slot_expert;
+  da.n_slots = ga.n_slots;
+  da.slot_expert = ga.slot_expert;
   da.hfrag = ga.hfrag;
   da.hsum = ga.hsum;
   da.E = E;
@@ -278,14 +312,14 @@ int decode_layer(const moe_layer* L, const float* x, int norm, float eps, int T,
   da.n_kg_r = L->ex.down.n_kg;
   da.n_kg_s = L->Is > 0 ? L->sh.down.n_kg : 0;
   da.S = W.S;
-  da.y = y;
+  da.has_shared = L->Is > 0;
   da.ypart = reinterpret_cast<float*>(ws + W.ypart);
-  da.counters = reinterpret_cast<uint32_t*>(ws + W.ctrl) + 1;
-  int dn_nw = env_int("MOE_DOWN_WAVES", 4);
-  if (dn_nw <= 0 || dn_nw > 8) dn_nw = 4;
+  int dn_nw = env_int("MOE_DOWN_WAVES", 8);
+  if (dn_nw <= 0 || dn_nw > 8) dn_nw = 8;
   timed_begin(1, s, &slot);
   HIPCHK(launch_down_decode(da, L->ex.down.n_rg, dn_nw, s));
   timed_end(slot, s);
+  *S_out = W.S;
   return MOE_OK;
 }
 
@@ -430,8 +464,8 @@ int moe_workspace_bytes(const moe_layer* L, int T, size_t* bytes) {
 int moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
   if (!ws || !aligned(ws, 256)) return fail(MOE_ERR_ARG, "workspace must be non-NULL and 256-byte aligned");
   if (ws_bytes < 256) return fail(MOE_ERR_WORKSPACE, "workspace too small");
-  // control words: the first ctrl_bytes(8192) of any workspace (largest d)
-  size_t n = (size_t)ctrl_bytes(8192);
+  // control words: the first ctrl_bytes() of any workspace
+  size_t n = (size_t)ctrl_bytes();
   if (n > ws_bytes) n = ws_bytes;
   HIPCHK(launch_fill_u32(reinterpret_cast<uint32_t*>(ws), n / 4, 0u, reinterpret_cast<hipStream_t>(stream)));
   return MOE_OK;
@@ -455,7 +489,14 @@ int moe_layer_forward(const moe_layer* L, const float* x, int T, float* y, const
   if (rc) return rc;
   init_kernels();
   if (g_init_err != hipSuccess) return fail(MOE_ERR_HIP, "kernel init: %s", hipGetErrorString(g_init_err));
-  return decode_layer(L, x, 0, 0.f, T, y, route, reinterpret_cast<uint8_t*>(ws), reinterpret_cast<hipStream_t>(stream));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
+  int S = 1;
+  rc = decode_layer(L, LayerInput{x, 1, 0, 0}, 0.f, T, nullptr, route, wsb, st, &S);
+  if (rc) return rc;
+  const WsLayout W = ws_layout_decode(L, T);
+  HIPCHK(launch_combine(reinterpret_cast<const float*>(wsb + W.ypart), S, (int64_t)8 * L->d, T, L->d, y, st));
+  return MOE_OK;
 }
 
 int moe_stack_forward(const moe_layer* const* layers, int n_layers, const float* x, int T, float eps, float* y,
@@ -481,25 +522,23 @@ int moe_stack_forward(const moe_layer* const* layers, int n_layers, const float*
   if (g_init_err != hipSuccess) return fail(MOE_ERR_HIP, "kernel init: %s", hipGetErrorString(g_init_err));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
-  const float* in = x;
+  LayerInput in{x, 1, 0, 0};
   for (int l = 0; l < n_layers; ++l) {
-    const WsLayout W = ws_layout_decode(layers[l], T);
-    float* out;
-    if (l == n_layers - 1) out = y;
-    else if (y_layers) out = y_layers + (size_t)l * T * d;
-    else out = reinterpret_cast<float*>(wsb + W.ystack) + (size_t)(l & 1) * 8 * d;
     moe_route_io r{};
     if (idx_layers) {
       r.out_idx = idx_layers + (size_t)l * T * layers[l]->k;
       r.out_w = w_layers + (size_t)l * T * layers[l]->k;
     }
-    int rc = decode_layer(layers[l], in, l > 0, eps, T, out, &r, wsb, s);
+    float* prev_out = (l > 0 && y_layers) ? y_layers + (size_t)(l - 1) * T * d : nullptr;
+    int S = 1;
+    int rc = decode_layer(layers[l], in, eps, T, prev_out, &r, wsb, s, &S);
     if (rc) return rc;
-    if (l == n_layers - 1 && y_layers) {
-      HIPCHK(hipMemcpyAsync(y_layers + (size_t)l * T * d, y, (size_t)T * d * 4, hipMemcpyDeviceToDevice, s));
-    }
-    in = out;
+    const WsLayout W = ws_layout_decode(layers[l], T);
+    in = LayerInput{reinterpret_cast<const float*>(wsb + W.ypart), S, (int64_t)8 * d, 1};
   }
+  HIPCHK(launch_combine(in.p, in.S, in.stride, T, d, y, s));
+  if (y_layers)
+    HIPCHK(hipMemcpyAsync(y_layers + (size_t)(n_layers - 1) * T * d, y, (size_t)T * d * 4, hipMemcpyDeviceToDevice, s));
   return MOE_OK;
 }
 
