@@ -288,7 +288,7 @@ int decode_layer(const moe_layer* L, const LayerInput& in, float eps, int T, flo
   {
     const int max_items = (W.max_slots - (ga.has_shared ? 1 : 0)) * ((L->I / 16 + 3) / 4) +
                           (ga.has_shared ? (L->Is / 16 + 3) / 4 : 0);
-    int n_wg = env_int("MOE_GU_WGS", 256);
+    int n_wg = env_int("MOE_GU_WGS", 160);
     if (n_wg > max_items) n_wg = max_items;
     if (n_wg < 1) n_wg = 1;
     timed_begin(0, s, &slot);
