@@ -78,6 +78,8 @@ def _declare(L):
     L.orc_expert_ffn.argtypes = [_P, _I, _I, _I, _P, _P]
     L.orc_layer_forward.argtypes = [_P, _P, _I, _P, _P, _P, _P, _P, _P]
     L.orc_rmsnorm.argtypes = [_P, _I, _I, ctypes.c_double, _P]
+    L.orc_group_tokens.argtypes = [_P, _I, _I, _I, _P, _P, _P]
+    L.orc_group_tokens.restype = None
     L.orc_rmsnorm.restype = None
 
 
@@ -270,3 +272,16 @@ def rmsnorm(x, eps: float = 1e-6):
     y = np.empty_like(x)
     lib().orc_rmsnorm(_ptr(x), T, d, float(eps), _ptr(y))
     return y
+
+
+def group_tokens(idx, E: int):
+    """Counting sort of the (token, slot) pairs of a routing idx [T][k] by
+    expert (see orc_group_tokens): returns (counts [E], offsets [E+1],
+    perm [T*k]) as int32 arrays."""
+    idx = _c(idx, np.int32)
+    T, k = idx.shape
+    counts = np.zeros(E, np.int32)
+    offsets = np.zeros(E + 1, np.int32)
+    perm = np.zeros(T * k, np.int32)
+    lib().orc_group_tokens(_ptr(idx), T, E, k, _ptr(counts), _ptr(offsets), _ptr(perm))
+    return counts, offsets, perm

@@ -19,7 +19,7 @@
  *   - block unpacking follows the ggml block types [strata-mlx wiki, credits
  *     list, llama.cpp/ggml entry].
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *   R1 block = {fp16 scale, 32 codes of b bits}; code j occupies bits
  *      [b*j, b*j+b) of the little-endian bitstream formed by the code bytes.
  *   R2 signed code c = q - 2^(b-1) (offset binary).
@@ -31,8 +31,8 @@
  *   R5 shared expert has weight 1 and no gate.
  *   R6 stack glue = RMSNorm with unit weight and eps 1e-6 between layers.
  *
- * Parity status of each function is stated in the design doc and next to the
- * function; every function here is pinned by a CPU test.
+ * Every function here is pinned by a CPU test (values fixed by the
+ * mathematics, brute force, closed forms and invariants).
  */
 #include <math.h>
 #include <stdint.h>
@@ -395,5 +395,39 @@ void orc_rmsnorm(const float *x, int T, int d, double eps, float *y)
         }
         double den = sqrt(ss / (double)d + eps);
         for (int j = 0; j < d; ++j) y[(size_t)t * d + j] = (float)((double)x[(size_t)t * d + j] / den);
+    }
+}
+
+/* Grouping of (token, slot) pairs by expert: the token-to-expert counting
+ * sort that precedes the per-expert matrix products when many tokens are
+ * processed at once (prompt chunks of up to 8192 tokens [agentlenshq
+ * article, section "Strata 如何让 125 B 模型适配 12-24 GB 显存", last
+ * item]).  Pair (t, r) names expert idx[t][r]; it is used unless that id is
+ * outside [0, E) or repeats an id of an earlier slot of the same token.
+ *   counts[e]    number of used pairs naming e
+ *   offsets[e]   sum of counts of experts below e; offsets[E] = all used pairs
+ *   perm[j]      t*k + r of the used pairs, by expert ascending, and by token
+ *                ascending within one expert; -1 after offsets[E]
+ * Plain definition, one pass per expert. */
+void orc_group_tokens(const int32_t *idx, int T, int E, int k,
+                      int32_t *counts, int32_t *offsets, int32_t *perm)
+{
+    long n = (long)T * k, pos = 0;
+    for (long j = 0; j < n; ++j) perm[j] = -1;
+    offsets[0] = 0;
+    for (int e = 0; e < E; ++e) {
+        int32_t c = 0;
+        for (int t = 0; t < T; ++t) {
+            for (int r = 0; r < k; ++r) {
+                if (idx[(long)t * k + r] != e) continue;
+                int earlier = 0;
+                for (int q = 0; q < r; ++q) earlier |= idx[(long)t * k + q] == e;
+                if (earlier) continue;
+                perm[pos++] = (int32_t)((long)t * k + r);
+                ++c;
+            }
+        }
+        counts[e] = c;
+        offsets[e + 1] = offsets[e] + c;
     }
 }

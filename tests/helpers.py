@@ -32,5 +32,5 @@ def oracle_layer(wl: mi.Workload, layer: int, experts) -> oracle.Layer:
     return oracle.Layer(wl.d, wl.E, wl.I, wl.Is, wl.k, wl.bits, W, b, ex, sh)
 
 
-# layer-output tolerance: global infinity-norm relative error
+# layer-output tolerance: global infinity-norm relative error max|y - ref| / max|ref|
 TOL_LAYER = 2e-3

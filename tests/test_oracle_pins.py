@@ -383,3 +383,62 @@ def test_generator_is_deterministic_and_device_agnostic_shape():
     assert not bool((a == c).all())
     eb = wl.expert_bytes()
     assert bool((mi.expert_canon(wl, 3, 5) == a[5 * eb:6 * eb]).all())
+
+
+def _group_brute(idx, E):
+    """Brute force: list every used (t, r), sort by (expert, token)."""
+    T, k = idx.shape
+    pairs = []
+    for t in range(T):
+        seen = set()
+        for r in range(k):
+            e = int(idx[t, r])
+            if 0 <= e < E and e not in seen:
+                pairs.append((e, t, t * k + r))
+            seen.add(e)
+    pairs.sort()
+    counts = np.bincount([p[0] for p in pairs], minlength=E).astype(np.int32)
+    perm = np.full(T * k, -1, np.int32)
+    perm[:len(pairs)] = [p[2] for p in pairs]
+    return counts, perm
+
+
+def test_group_tokens_brute_force(orc):
+    rng = np.random.default_rng(11)
+    for T, E, k in ((1, 4, 2), (37, 16, 2), (300, 512, 10), (64, 3, 3)):
+        # distinct experts per token, Zipf-like skew
+        p = 1.0 / np.arange(1, E + 1) ** 1.1
+        p /= p.sum()
+        idx = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+        counts, offsets, perm = orc.group_tokens(idx, E)
+        bc, bp = _group_brute(idx, E)
+        assert np.array_equal(counts, bc)
+        assert np.array_equal(offsets, np.concatenate([[0], np.cumsum(bc)]).astype(np.int32))
+        assert np.array_equal(perm, bp)
+        assert offsets[E] == T * k
+
+
+def test_group_tokens_invalid_and_repeated_entries(orc):
+    # ids outside [0, E) and repeats within a token are left out
+    idx = np.array([[2, 2, 5], [-1, 0, 7], [1, 3, 1], [0, 9, 0]], np.int32)
+    E = 8
+    counts, offsets, perm = orc.group_tokens(idx, E)
+    bc, bp = _group_brute(idx, E)
+    assert np.array_equal(counts, bc) and np.array_equal(perm, bp)
+    # hand count: expert 0 <- (1,1),(3,0); 1 <- (2,0); 2 <- (0,0); 3 <- (2,1); 5 <- (0,2); 7 <- (1,2)
+    assert counts.tolist() == [2, 1, 1, 1, 0, 1, 0, 1]
+    assert perm.tolist() == [4, 9, 6, 0, 7, 2, 5, -1, -1, -1, -1, -1]
+    assert offsets[E] == 7
+
+
+def test_group_tokens_closed_form(orc):
+    # token t routes to experts (t + r) mod E: expert e gets the tokens with
+    # (e - t) mod E < k, in token order
+    T, E, k = 50, 7, 3
+    idx = np.array([[(t + r) % E for r in range(k)] for t in range(T)], np.int32)
+    counts, offsets, perm = orc.group_tokens(idx, E)
+    for e in range(E):
+        toks = [t for t in range(T) if (e - t) % E < k]
+        assert counts[e] == len(toks)
+        got = perm[offsets[e]:offsets[e + 1]]
+        assert got.tolist() == [t * k + (e - t) % E for t in toks]
