@@ -80,22 +80,160 @@ def cpu_baseline_stack(wl, T, x_np, n_layers_sample):
     return T / (per_layer * wl.layers), per_layer
 
 
+def cpu_baseline_prefill(wl, x_np, n_tok):
+    """Time the oracle (single-threaded fp64 C) on the first n_tok tokens of
+    the prefill chunk: router, top-k and the layer; expert generation untimed."""
+    import moe_inputs as mi
+    import oracle
+
+    W, b = mi.router(wl, 0)
+    h = x_np[:n_tok]
+    t0 = time.perf_counter()
+    logits = oracle.router_logits(h, W, b)
+    idx, w = oracle.topk(logits, wl.k)
+    t_total = time.perf_counter() - t0
+    ex = {int(e): mi.expert_canon(wl, 0, int(e)).numpy() for e in np.unique(idx)}
+    sh = mi.expert_canon(wl, 0, -1).numpy() if wl.Is else None
+    OL = oracle.Layer(wl.d, wl.E, wl.I, wl.Is, wl.k, wl.bits, W, b, ex, sh)
+    t0 = time.perf_counter()
+    oracle.layer_forward(OL, h, force_idx=idx, force_w=w)
+    t_total += time.perf_counter() - t0
+    return n_tok / t_total, t_total
+
+
+def bench_prefill(args):
+    """One MoE layer over a prompt chunk of T tokens (default 8192)."""
+    import torch
+
+    import bit_quantized_experts_amd as bqe
+    import moe_inputs as mi
+    from moe_inputs.device import activations_device, packed_layer
+
+    wl = mi.WORKLOADS["prefill"]
+    T = args.T or wl.T
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    L = packed_layer(wl, 0, dev)
+    x_np = mi.activations(wl, T=T, stream=1)
+    x = activations_device(x_np, dev)
+    y = torch.empty((T, wl.d), dtype=torch.float32, device=dev)
+    ws = bqe.new_workspace(L.workspace_bytes(T), dev)
+    idx = torch.empty((T, wl.k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, wl.k), dtype=torch.float32, device=dev)
+    rio = bqe.RouteIO(None, None, None, idx.data_ptr(), w.data_ptr())
+
+    def run_pass():
+        bqe.moe_layer_forward(L.handle, x, y, ws, rio)
+
+    run_pass()
+    torch.cuda.synchronize()
+    idx_np = idx.cpu().numpy()
+    kdur = {}
+    for cls, name in ((bqe.TIMING_PREFILL_GATE_UP, "gate_up"), (bqe.TIMING_PREFILL_DOWN, "down"),
+                      (bqe.TIMING_PREFILL_ROUTER, "router")):
+        tot, n = 0.0, 0
+        for _ in range(5):
+            bqe.moe_timing_start(cls, 1)
+            run_pass()
+            ms, cnt = bqe.moe_timing_stop()
+            tot += ms
+            n += cnt
+        kdur[name] = (tot / n) * 1e-3
+
+    graph = None
+    if not args.no_graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for _ in range(2):
+                run_pass()
+        torch.cuda.current_stream().wait_stream(s)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run_pass()
+        torch.cuda.synchronize()
+    step = graph.replay if graph is not None else run_pass
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    sec_per_step = e0.elapsed_time(e1) * 1e-3 / args.steps
+
+    # algorithmic matrix-core work from the routing taken: 2 flops per
+    # multiply-add, gate+up (2 d I) and down (d I) per routed pair, the
+    # shared expert once per token; the router GEMM is counted apart
+    pairs = int((idx_np >= 0).sum())
+    gu_flops = 2.0 * pairs * 2 * wl.d * wl.I + 2.0 * T * 2 * wl.d * wl.Is
+    dn_flops = 2.0 * pairs * wl.d * wl.I + 2.0 * T * wl.d * wl.Is
+    rt_flops = 2.0 * T * wl.E * wl.d
+    flops = {"gate_up": gu_flops, "down": dn_flops, "router": rt_flops}
+    kernels = {n: {"avg_us": kdur[n] * 1e6, "flops_per_launch": flops[n],
+                   "TFLOPs": flops[n] / kdur[n] / 1e12} for n in kdur}
+    dom = max(("gate_up", "down"), key=lambda n: kdur[n])
+    achieved = flops[dom] / kdur[dom] / 1e12
+    gemm_util = (gu_flops + dn_flops) / (kdur["gate_up"] + kdur["down"]) / 1e12 / MFMA_F16_PEAK_TFLOPS
+    counts = np.bincount(idx_np.reshape(-1), minlength=wl.E)
+
+    cpu = None
+    if args.cpu_tokens > 0:
+        log(f"timing the CPU oracle on {args.cpu_tokens} tokens ...")
+        tps, tsec = cpu_baseline_prefill(wl, x_np, args.cpu_tokens)
+        cpu = {"value": tps, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"first {args.cpu_tokens} of {T} tokens of the chunk ({tsec:.1f} s: router, top-k, "
+                         f"layer), single thread; expert generation untimed"}
+    out = {
+        "metric": "MoE prefill tokens/s (one layer, chunk of T tokens)",
+        "value": T / sec_per_step,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": sec_per_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16 MFMA operands (weights s*c, activations scaled per row), fp32 accumulate",
+        "data": "synthetic (counter-hash codes/scales, N(0,1) activations, N(0,0.02) router + Zipf(1.1) log bias)",
+        "config": {"workload": wl.name, "layers": 1, "T": T, "d": wl.d, "experts": wl.E, "d_ff": wl.I,
+                   "shared_d_ff": wl.Is, "top_k": wl.k, "bits": wl.bits, "graph": graph is not None,
+                   "parallelism": "none (1 GPU)"},
+        "grouped_gemm_mfma_util": gemm_util,
+        "tokens_per_expert": {"max": int(counts.max()), "empty_experts": int((counts == 0).sum())},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / MFMA_F16_PEAK_TFLOPS, "traffic": None},
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="stack_t8_2bit", choices=["stack_t8_2bit", "stack_3bit"])
+    ap.add_argument("--workload", default="stack_t8_2bit", choices=["stack_t8_2bit", "stack_3bit", "prefill"])
     ap.add_argument("--T", type=int, default=None, help="tokens per pass (default: the workload's)")
     ap.add_argument("--layers", type=int, default=None, help="override the number of layers (testing only)")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=3, help="oracle sample size in layers (0 = skip)")
+    ap.add_argument("--cpu-tokens", type=int, default=16, help="prefill: oracle sample size in tokens (0 = skip)")
     args = ap.parse_args()
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no multi-GPU path. "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "prefill":
+        bench_prefill(args)
+        return
 
     import torch
 

@@ -18,10 +18,12 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_DATA = 0, 1, 2, 3, 4, 5
 TIMING_GATE_UP, TIMING_DOWN, TIMING_ROUTER, TIMING_PREFILL_GATE_UP, TIMING_PREFILL_DOWN = 0, 1, 2, 3, 4
+TIMING_PREFILL_ROUTER = 5
 
 EXPORTED = ("moe_last_error", "moe_packed_bytes", "moe_pack_experts", "moe_layer_release", "moe_layer_get_desc",
             "moe_route_topk", "moe_workspace_bytes", "moe_workspace_init", "moe_layer_forward",
-            "moe_stack_forward", "moe_rmsnorm", "moe_debug_unpack", "moe_timing_start", "moe_timing_stop")
+            "moe_stack_forward", "moe_rmsnorm", "moe_debug_unpack", "moe_timing_start", "moe_timing_stop",
+            "moe_group_workspace_bytes", "moe_group_tokens")
 
 
 class MoeError(RuntimeError):
@@ -67,6 +69,8 @@ def lib() -> ctypes.CDLL:
         L.moe_debug_unpack.argtypes = [P, I, I, P, P, P, P]
         L.moe_timing_start.argtypes = [I, I]
         L.moe_timing_stop.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
+        L.moe_group_workspace_bytes.argtypes = [I, I, I, ctypes.POINTER(S)]
+        L.moe_group_tokens.argtypes = [P, I, I, I, P, P, P, P, S, P]
         for name in EXPORTED:
             if name != "moe_last_error":
                 getattr(L, name).restype = ctypes.c_int
@@ -159,6 +163,18 @@ def moe_stack_forward(handles, x, y, ws, eps: float = 1e-6, y_layers=None, idx_l
     _check(lib().moe_stack_forward(arr, len(handles), _ptr(x), T, eps, _ptr(y), _ptr(y_layers), _ptr(idx_layers),
                                    _ptr(w_layers), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "moe_stack_forward")
+
+
+def moe_group_workspace_bytes(T: int, E: int, k: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().moe_group_workspace_bytes(T, E, k, ctypes.byref(n)), "moe_group_workspace_bytes")
+    return n.value
+
+
+def moe_group_tokens(idx, E: int, counts, offsets, perm, ws, stream=None):
+    T, k = idx.shape
+    _check(lib().moe_group_tokens(_ptr(idx), T, E, k, _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream)), "moe_group_tokens")
 
 
 def moe_rmsnorm(x, y, eps: float = 1e-6, stream=None):

@@ -3,6 +3,7 @@
 // memory is allocated here; every launch goes to the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -105,17 +106,24 @@ int check_desc(const moe_layer_desc* D) {
   return MOE_OK;
 }
 
-// packed buffer: [status 256 B][router_w][router_b][E experts][shared]
+// packed buffer: [status 256 B][router_w][router_b][router hi][router lo]
+// [router exponents][E experts][shared]
 struct PackedLayout {
-  int64_t off_status, off_rw, off_rb, off_ex, off_sh, total;
+  int64_t off_status, off_rw, off_rb, off_rwh, off_rwl, off_rew, off_ex, off_sh, total;
 };
+
+int e16_of(int E) { return (E + 15) / 16 * 16; }
 
 PackedLayout packed_layout(const moe_layer_desc* D, const moe_expert_layout& ex, const moe_expert_layout& sh) {
   PackedLayout P;
+  const int64_t E16 = e16_of(D->n_experts);
   P.off_status = 0;
   P.off_rw = 256;
   P.off_rb = P.off_rw + moe_align256((int64_t)D->n_experts * D->d_model * 4);
-  P.off_ex = P.off_rb + moe_align256((int64_t)D->n_experts * 4);
+  P.off_rwh = P.off_rb + moe_align256((int64_t)D->n_experts * 4);
+  P.off_rwl = P.off_rwh + moe_align256(E16 * D->d_model * 2);
+  P.off_rew = P.off_rwl + moe_align256(E16 * D->d_model * 2);
+  P.off_ex = P.off_rew + moe_align256(E16 * 4);
   P.off_sh = P.off_ex + (int64_t)D->n_experts * ex.bytes;
   P.total = P.off_sh + (D->d_ff_shared > 0 ? sh.bytes : 0);
   return P;
@@ -164,6 +172,60 @@ WsLayout ws_layout_decode(const moe_layer* L, int T) {
   W.hfrag = take((int64_t)W.max_slots * W.nbI * 64 * 8 * 2);
   W.hsum = take((int64_t)W.max_slots * W.nbI * 16 * 4);
   W.ypart = take((int64_t)W.S * 8 * d * 4);
+  W.total = o;
+  return W;
+}
+
+// Prefill workspace (T > 8).  Rows: the routed pairs grouped by expert, each
+// expert padded to a multiple of 16, then one row per token for the shared
+// expert (padded to 16).
+struct PfLayout {
+  int64_t ctrl, ex, xh, xl, logits, idx, w, tile_bm, tile_cnt, counts, offsets, n_items, item_group, item_row0,
+      item_rows, row_src, row_tok, row_w, slot_pos, hfrag, eh, ypart, total;
+  int n_tiles, R, max_items, nbH, n_nt;
+};
+
+int64_t routed_rows_max(int64_t T, int k, int E) {
+  const int64_t pairs = T * k;
+  return pairs + 15 * (pairs < E ? pairs : E);
+}
+
+PfLayout ws_layout_prefill(const moe_layer* L, int T) {
+  PfLayout W{};
+  const int k = L->k, E = L->E, d = L->d;
+  const int Imax = L->I > L->Is ? L->I : L->Is;
+  const int64_t rr = routed_rows_max(T, k, E);
+  const int64_t rs = L->Is > 0 ? (T + 15) / 16 * 16 : 0;
+  const int64_t pairs = (int64_t)T * k;
+  W.n_tiles = (T + PF_T64 - 1) / PF_T64;
+  W.R = (int)(rr + rs);
+  W.max_items = (int)((rr + PF_TM - 1) / PF_TM + (pairs < E ? pairs : E) + (rs + PF_TM - 1) / PF_TM);
+  W.nbH = Imax / 32;
+  W.n_nt = (Imax + PF_HT - 1) / PF_HT;
+  int64_t o = 0;
+  auto take = [&](int64_t bytes) { int64_t r = o; o += moe_align256(bytes); return r; };
+  W.ctrl = take(ctrl_bytes());
+  W.ex = take((int64_t)T * 4);
+  W.xh = take((int64_t)T * d * 2);
+  W.xl = take((int64_t)T * d * 2);
+  W.logits = take((int64_t)T * E * 4);
+  W.idx = take(pairs * 4);
+  W.w = take(pairs * 4);
+  W.tile_bm = take((int64_t)W.n_tiles * E * 8);
+  W.tile_cnt = take((int64_t)W.n_tiles * E * 4);
+  W.counts = take((int64_t)E * 4);
+  W.offsets = take((int64_t)(E + 2) * 4);
+  W.n_items = take(4);
+  W.item_group = take((int64_t)W.max_items * 4);
+  W.item_row0 = take((int64_t)W.max_items * 4);
+  W.item_rows = take((int64_t)W.max_items * 4);
+  W.row_src = take((int64_t)W.R * 4);
+  W.row_tok = take((int64_t)W.R * 4);
+  W.row_w = take((int64_t)W.R * 4);
+  W.slot_pos = take(pairs * 4);
+  W.hfrag = take((int64_t)W.R * Imax * 2);
+  W.eh = take((int64_t)W.n_nt * W.R * 4);
+  W.ypart = take((int64_t)W.R * d * 4);
   W.total = o;
   return W;
 }
@@ -323,6 +385,124 @@ int decode_layer(const moe_layer* L, const LayerInput& in, float eps, int T, flo
   return MOE_OK;
 }
 
+// One prefill layer (T > 8): prep -> router -> top-k -> group -> gate/up ->
+// down -> combine into y.
+int prefill_layer(const moe_layer* L, const float* x, int norm, float eps, int T, float* y, const moe_route_io* r,
+                  uint8_t* ws, hipStream_t s) {
+  const PfLayout W = ws_layout_prefill(L, T);
+  const int d = L->d, E = L->E, k = L->k;
+  const bool forced = r && r->in_idx && r->in_w;
+  int slot;
+
+  PfPrepArgs pa{};
+  pa.x = x;
+  pa.T = T;
+  pa.d = d;
+  pa.norm = norm;
+  pa.eps = eps;
+  pa.ex = reinterpret_cast<int32_t*>(ws + W.ex);
+  pa.xh = reinterpret_cast<_Float16*>(ws + W.xh);
+  pa.xl = reinterpret_cast<_Float16*>(ws + W.xl);
+  HIPCHK(launch_pf_prep(pa, s));
+
+  const int32_t* idx;
+  const float* w;
+  if (forced) {
+    idx = r->in_idx;
+    w = r->in_w;
+  } else {
+    PfRouterArgs ra{};
+    ra.xh = pa.xh;
+    ra.xl = pa.xl;
+    ra.ex = pa.ex;
+    ra.wh = L->router_wh;
+    ra.wl = L->router_wl;
+    ra.ew = L->router_ew;
+    ra.bias = L->router_b;
+    ra.T = T;
+    ra.d = d;
+    ra.E = E;
+    ra.E16 = L->E16;
+    ra.logits = (r && r->out_logits) ? r->out_logits : reinterpret_cast<float*>(ws + W.logits);
+    timed_begin(5, s, &slot);
+    HIPCHK(launch_pf_router(ra, s));
+    timed_end(slot, s);
+    int32_t* oi = (r && r->out_idx) ? r->out_idx : reinterpret_cast<int32_t*>(ws + W.idx);
+    float* ow = (r && r->out_w) ? r->out_w : reinterpret_cast<float*>(ws + W.w);
+    HIPCHK(launch_topk(ra.logits, T, E, k, oi, ow, s));
+    idx = oi;
+    w = ow;
+  }
+  if (forced && r->out_idx) HIPCHK(hipMemcpyAsync(r->out_idx, idx, (size_t)T * k * 4, hipMemcpyDeviceToDevice, s));
+  if (forced && r->out_w) HIPCHK(hipMemcpyAsync(r->out_w, w, (size_t)T * k * 4, hipMemcpyDeviceToDevice, s));
+
+  PfGroupArgs ga{};
+  ga.idx = idx;
+  ga.w = w;
+  ga.T = T;
+  ga.E = E;
+  ga.k = k;
+  ga.pad = 16;
+  ga.TM = PF_TM;
+  ga.has_shared = L->Is > 0;
+  ga.n_tiles = W.n_tiles;
+  ga.tile_bm = reinterpret_cast<uint64_t*>(ws + W.tile_bm);
+  ga.tile_cnt = reinterpret_cast<int32_t*>(ws + W.tile_cnt);
+  ga.counts = reinterpret_cast<int32_t*>(ws + W.counts);
+  ga.offsets = reinterpret_cast<int32_t*>(ws + W.offsets);
+  ga.row_src = reinterpret_cast<int32_t*>(ws + W.row_src);
+  ga.row_tok = reinterpret_cast<int32_t*>(ws + W.row_tok);
+  ga.row_w = reinterpret_cast<float*>(ws + W.row_w);
+  ga.slot_pos = reinterpret_cast<int32_t*>(ws + W.slot_pos);
+  ga.n_items = reinterpret_cast<int32_t*>(ws + W.n_items);
+  ga.item_group = reinterpret_cast<int32_t*>(ws + W.item_group);
+  ga.item_row0 = reinterpret_cast<int32_t*>(ws + W.item_row0);
+  ga.item_rows = reinterpret_cast<int32_t*>(ws + W.item_rows);
+  ga.R_fill = 0;
+  HIPCHK(launch_pf_group(ga, s));
+
+  PfGemmArgs ma{};
+  ma.X = expert_set(L);
+  ma.xh = pa.xh;
+  ma.ex = pa.ex;
+  ma.row_tok = ga.row_tok;
+  ma.row_w = ga.row_w;
+  ma.n_items = ga.n_items;
+  ma.item_group = ga.item_group;
+  ma.item_row0 = ga.item_row0;
+  ma.item_rows = ga.item_rows;
+  ma.T = T;
+  ma.d = d;
+  ma.E = E;
+  ma.I = L->I;
+  ma.Is = L->Is;
+  ma.nbH = W.nbH;
+  ma.n_nt = W.n_nt;
+  ma.R = W.R;
+  ma.hfrag = reinterpret_cast<_Float16*>(ws + W.hfrag);
+  ma.eh = reinterpret_cast<int32_t*>(ws + W.eh);
+  ma.ypart = reinterpret_cast<float*>(ws + W.ypart);
+  timed_begin(3, s, &slot);
+  HIPCHK(launch_pf_gate_up(ma, L->bits, W.max_items, s));
+  timed_end(slot, s);
+  timed_begin(4, s, &slot);
+  HIPCHK(launch_pf_down(ma, L->bits, L->ex.down.BK, W.max_items, s));
+  timed_end(slot, s);
+
+  PfCombineArgs ca{};
+  ca.ypart = ma.ypart;
+  ca.slot_pos = ga.slot_pos;
+  ca.offsets = ga.offsets;
+  ca.T = T;
+  ca.d = d;
+  ca.k = k;
+  ca.E = E;
+  ca.has_shared = L->Is > 0;
+  ca.y = y;
+  HIPCHK(launch_pf_combine(ca, s));
+  return MOE_OK;
+}
+
 int check_ws(const moe_layer* L, int T, void* ws, size_t ws_bytes, size_t* need) {
   if (moe_workspace_bytes(L, T, need) != MOE_OK) return MOE_ERR_ARG;
   if (!ws) return fail(MOE_ERR_ARG, "workspace is NULL");
@@ -387,6 +567,10 @@ int moe_pack_experts(const moe_layer_desc* desc, const void* experts_canon, cons
   L->packed_bytes = (size_t)P.total;
   L->router_w = reinterpret_cast<const float*>(base + P.off_rw);
   L->router_b = reinterpret_cast<const float*>(base + P.off_rb);
+  L->router_wh = reinterpret_cast<const _Float16*>(base + P.off_rwh);
+  L->router_wl = reinterpret_cast<const _Float16*>(base + P.off_rwl);
+  L->router_ew = reinterpret_cast<const int32_t*>(base + P.off_rew);
+  L->E16 = e16_of(L->E);
   L->experts = base + P.off_ex;
   L->shared = L->Is > 0 ? base + P.off_sh : nullptr;
 
@@ -402,6 +586,9 @@ int moe_pack_experts(const moe_layer_desc* desc, const void* experts_canon, cons
   } else if ((e = launch_fill_u32(reinterpret_cast<uint32_t*>(base + P.off_rb), (size_t)L->E, 0u, s)) != hipSuccess) {
     return bail(fail(MOE_ERR_HIP, "bias fill: %s", hipGetErrorString(e)));
   }
+  if ((e = launch_pack_router(router_w, L->E, L->d, const_cast<_Float16*>(L->router_wh),
+                              const_cast<_Float16*>(L->router_wl), const_cast<int32_t*>(L->router_ew), s)) != hipSuccess)
+    return bail(fail(MOE_ERR_HIP, "router split: %s", hipGetErrorString(e)));
   const int64_t bb = canon_block_bytes(L->bits);
   auto pack_expert = [&](const uint8_t* canon, int I, const moe_expert_layout& X, uint8_t* dst, int n) -> hipError_t {
     const int64_t gate_b = (int64_t)I * (L->d / 32) * bb;
@@ -455,9 +642,10 @@ int moe_route_topk(const float* logits, int T, int E, int k, int32_t* idx, float
 int moe_workspace_bytes(const moe_layer* L, int T, size_t* bytes) {
   if (!L || !bytes) return fail(MOE_ERR_ARG, "NULL argument");
   if (T < 0) return fail(MOE_ERR_ARG, "T must be >= 0");
-  if (T > MOE_MAX_TOK_DECODE) return fail(MOE_ERR_UNSUPPORTED, "T > %d (prefill path) not built yet", MOE_MAX_TOK_DECODE);
+  if (T > MOE_MAX_TOK_PREFILL) return fail(MOE_ERR_UNSUPPORTED, "T above %d not supported", MOE_MAX_TOK_PREFILL);
   const int Tw = T < 1 ? 1 : T;
-  *bytes = (size_t)ws_layout_decode(L, Tw).total;
+  const size_t dec = (size_t)ws_layout_decode(L, Tw < MOE_MAX_TOK_DECODE ? Tw : MOE_MAX_TOK_DECODE).total;
+  *bytes = T > MOE_MAX_TOK_DECODE ? std::max(dec, (size_t)ws_layout_prefill(L, T).total) : dec;
   return MOE_OK;
 }
 
@@ -491,6 +679,7 @@ int moe_layer_forward(const moe_layer* L, const float* x, int T, float* y, const
   if (g_init_err != hipSuccess) return fail(MOE_ERR_HIP, "kernel init: %s", hipGetErrorString(g_init_err));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
+  if (T > MOE_MAX_TOK_DECODE) return prefill_layer(L, x, 0, 0.f, T, y, route, wsb, st);
   int S = 1;
   rc = decode_layer(L, LayerInput{x, 1, 0, 0}, 0.f, T, nullptr, route, wsb, st, &S);
   if (rc) return rc;
@@ -517,11 +706,29 @@ int moe_stack_forward(const moe_layer* const* layers, int n_layers, const float*
     int rc = check_ws(layers[l], T, ws, ws_bytes, &need);
     if (rc) return rc;
   }
-  if (T > MOE_MAX_TOK_DECODE) return fail(MOE_ERR_UNSUPPORTED, "stack forward supports T <= %d", MOE_MAX_TOK_DECODE);
   init_kernels();
   if (g_init_err != hipSuccess) return fail(MOE_ERR_HIP, "kernel init: %s", hipGetErrorString(g_init_err));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
+  if (T > MOE_MAX_TOK_DECODE) {
+    // Layer l reads h_l (x, then the previous output) and writes y_layers[l]
+    // or y; the RMSNorm of the input is fused into the layer's prep step.
+    // Reading and writing y in one layer is safe: the prep step consumes its
+    // input before the combine step writes the output.
+    for (int l = 0; l < n_layers; ++l) {
+      moe_route_io r{};
+      if (idx_layers) {
+        r.out_idx = idx_layers + (size_t)l * T * layers[l]->k;
+        r.out_w = w_layers + (size_t)l * T * layers[l]->k;
+      }
+      const float* in = l == 0 ? x : (y_layers ? y_layers + (size_t)(l - 1) * T * d : y);
+      float* out = y_layers ? y_layers + (size_t)l * T * d : y;
+      int rc = prefill_layer(layers[l], in, l > 0, eps, T, out, &r, wsb, s);
+      if (rc) return rc;
+    }
+    if (y_layers) HIPCHK(hipMemcpyAsync(y, y_layers + (size_t)(n_layers - 1) * T * d, (size_t)T * d * 4, hipMemcpyDeviceToDevice, s));
+    return MOE_OK;
+  }
   LayerInput in{x, 1, 0, 0};
   for (int l = 0; l < n_layers; ++l) {
     moe_route_io r{};
@@ -539,6 +746,54 @@ int moe_stack_forward(const moe_layer* const* layers, int n_layers, const float*
   HIPCHK(launch_combine(in.p, in.S, in.stride, T, d, y, s));
   if (y_layers)
     HIPCHK(hipMemcpyAsync(y_layers + (size_t)(n_layers - 1) * T * d, y, (size_t)T * d * 4, hipMemcpyDeviceToDevice, s));
+  return MOE_OK;
+}
+
+int moe_group_workspace_bytes(int T, int E, int k, size_t* bytes) {
+  if (!bytes) return fail(MOE_ERR_ARG, "bytes is NULL");
+  if (T < 0 || T > MOE_MAX_TOK_PREFILL) return fail(MOE_ERR_ARG, "T must be in [0, %d]", MOE_MAX_TOK_PREFILL);
+  if (E < 1 || E > MOE_MAX_E) return fail(MOE_ERR_ARG, "E must be in [1, %d]", MOE_MAX_E);
+  if (k < 1 || k > MOE_MAX_K) return fail(MOE_ERR_ARG, "k must be in [1, %d]", MOE_MAX_K);
+  const int64_t n_tiles = (T + PF_T64 - 1) / PF_T64;
+  *bytes = (size_t)(moe_align256(n_tiles * E * 8) + moe_align256(n_tiles * E * 4));
+  if (*bytes == 0) *bytes = 256;
+  return MOE_OK;
+}
+
+int moe_group_tokens(const int32_t* idx, int T, int E, int k, int32_t* counts, int32_t* offsets, int32_t* perm,
+                     void* ws, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  int rc = moe_group_workspace_bytes(T, E, k, &need);
+  if (rc) return rc;
+  if (!counts || !offsets) return fail(MOE_ERR_ARG, "counts and offsets must be non-NULL");
+  if (T > 0 && (!idx || !perm)) return fail(MOE_ERR_ARG, "idx and perm must be non-NULL");
+  if (!ws || !aligned(ws, 256)) return fail(MOE_ERR_ARG, "workspace must be non-NULL and 256-byte aligned");
+  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes, need);
+  if (!aligned(idx, 4) || !aligned(counts, 4) || !aligned(offsets, 4) || !aligned(perm, 4))
+    return fail(MOE_ERR_ARG, "misaligned pointer");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int n_tiles = (T + PF_T64 - 1) / PF_T64;
+  uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
+  PfGroupArgs ga{};
+  ga.idx = idx;
+  ga.T = T;
+  ga.E = E;
+  ga.k = k;
+  ga.pad = 1;
+  ga.TM = PF_TM;
+  ga.n_tiles = n_tiles;
+  ga.tile_bm = reinterpret_cast<uint64_t*>(wsb);
+  ga.tile_cnt = reinterpret_cast<int32_t*>(wsb + moe_align256((int64_t)n_tiles * E * 8));
+  ga.counts = counts;
+  ga.offsets = offsets;
+  ga.row_src = perm;
+  ga.R_fill = T * k;
+  if (T == 0) {
+    HIPCHK(launch_fill_u32(reinterpret_cast<uint32_t*>(counts), (size_t)E, 0u, s));
+    HIPCHK(launch_fill_u32(reinterpret_cast<uint32_t*>(offsets), (size_t)E + 1, 0u, s));
+    return MOE_OK;
+  }
+  HIPCHK(launch_pf_group(ga, s));
   return MOE_OK;
 }
 
@@ -566,7 +821,7 @@ int moe_debug_unpack(const moe_layer* L, int expert, int mat, int8_t* codes, flo
 }
 
 int moe_timing_start(int kernel_class, int max_launches) {
-  if (kernel_class < 0 || kernel_class > 4 || max_launches < 1) return fail(MOE_ERR_ARG, "bad timing arguments");
+  if (kernel_class < 0 || kernel_class > 5 || max_launches < 1) return fail(MOE_ERR_ARG, "bad timing arguments");
   std::lock_guard<std::mutex> lk(g_timing.mu);
   for (hipEvent_t e : g_timing.ev) hipEventDestroy(e);
   g_timing.ev.assign(2 * (size_t)max_launches, nullptr);

@@ -26,6 +26,7 @@
 
 #define MOE_BLOCK 32
 #define MOE_MAX_TOK_DECODE 8
+#define MOE_MAX_TOK_PREFILL 65536
 #define MOE_MAX_K 16
 #define MOE_MAX_E 4096
 
@@ -52,6 +53,10 @@ struct moe_layer {
   const uint8_t* packed;  // device base
   const float* router_w;  // device [E][d]
   const float* router_b;  // device [E]
+  const _Float16* router_wh;  // device: router rows times 2^-ew, fp16 hi part, MFMA B fragments
+  const _Float16* router_wl;  // same, lo part
+  const int32_t* router_ew;   // device [E16] row exponents
+  int32_t E16;                // E rounded up to a multiple of 16
   const uint8_t* experts; // device, E * ex.bytes
   const uint8_t* shared;  // device, sh.bytes or null
   size_t packed_bytes;

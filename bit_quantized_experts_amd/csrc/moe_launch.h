@@ -104,3 +104,86 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx, f
 hipError_t launch_rmsnorm(const float* x, int T, int d, float eps, float* y, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
 hipError_t moe_route_kernels_init();
+
+// --------------------------------------------------------------- prefill ---
+// Chunked prefill (T > 8): the routed (token, slot) pairs are grouped by
+// expert into rows; each expert's rows are padded to a multiple of 16 and cut
+// into work items of up to PF_TM rows; the shared expert's rows (one per
+// token, in token order) follow the routed rows.
+#define PF_TM 128   // rows per work item
+#define PF_HT 128   // intermediate columns per gate/up workgroup (4 waves x 32)
+#define PF_DT 256   // output columns per down workgroup (4 waves x 64)
+#define PF_ET 128   // experts per router workgroup (4 waves x 32)
+#define PF_T64 64   // tokens per grouping tile
+
+struct PfPrepArgs {
+  const float* x;  // [T][d]
+  int32_t T, d, norm;
+  float eps;
+  int32_t* ex;     // [T] power-of-two exponent of the row
+  _Float16* xh;    // [T][d] fp16(x * 2^-ex)
+  _Float16* xl;    // [T][d] fp16(x * 2^-ex - xh)
+};
+
+struct PfRouterArgs {
+  const _Float16* xh;
+  const _Float16* xl;
+  const int32_t* ex;
+  const _Float16* wh;  // router hi/lo fragments [E16/16][d/32][64][8]
+  const _Float16* wl;
+  const int32_t* ew;   // [E16] row exponents
+  const float* bias;   // [E]
+  int32_t T, d, E, E16;
+  float* logits;  // [T][E]
+};
+
+struct PfGroupArgs {
+  const int32_t* idx;  // [T][k]
+  const float* w;      // [T][k] or null
+  int32_t T, E, k, pad, TM, has_shared, n_tiles;
+  uint64_t* tile_bm;   // [n_tiles][E] token bitmaps of each expert
+  int32_t* tile_cnt;   // [n_tiles][E] counts, then exclusive prefix over tiles
+  int32_t* counts;     // [E]
+  int32_t* offsets;    // [E + 2]: padded row offsets; [E] routed rows, [E+1] all rows
+  int32_t* row_src;    // [R] t*k + r of the row, -1 for padding / shared rows
+  int32_t* row_tok;    // [R] token of the row (0 for padding), or null
+  float* row_w;        // [R] gate weight of the row (shared 1, padding 0), or null
+  int32_t* slot_pos;   // [T*k] row of each pair, -1 if not used, or null
+  int32_t* n_items;    // [1] or null (no work list)
+  int32_t* item_group; // [max_items] expert (E = shared)
+  int32_t* item_row0;
+  int32_t* item_rows;  // multiple of 16, <= TM
+  int32_t R_fill;      // rows of row_src to fill with -1 beyond the routed rows (export)
+};
+
+struct PfGemmArgs {
+  ExpertSet X;
+  const _Float16* xh;     // gate/up: activation rows
+  const int32_t* ex;      // gate/up: row exponents of x
+  const int32_t* row_tok;
+  const float* row_w;
+  const int32_t* n_items;
+  const int32_t* item_group;
+  const int32_t* item_row0;
+  const int32_t* item_rows;
+  int32_t T, d, E, I, Is, nbH, n_nt, R;
+  _Float16* hfrag;   // [R/16][nbH][64][8] intermediate rows, fp16(h * 2^-eh)
+  int32_t* eh;       // [n_h_tiles][R] exponents per 128-column tile
+  float* ypart;      // [R][d] down outputs times the gate weight
+};
+
+struct PfCombineArgs {
+  const float* ypart;
+  const int32_t* slot_pos;
+  const int32_t* offsets;  // offsets[E] = first shared row
+  int32_t T, d, k, E, has_shared;
+  float* y;
+};
+
+hipError_t launch_pack_router(const float* W, int E, int d, _Float16* wh, _Float16* wl, int32_t* ew, hipStream_t s);
+hipError_t launch_pf_prep(const PfPrepArgs& a, hipStream_t s);
+hipError_t launch_pf_router(const PfRouterArgs& a, hipStream_t s);
+hipError_t launch_pf_group(const PfGroupArgs& a, hipStream_t s);
+hipError_t launch_pf_gate_up(const PfGemmArgs& a, int bits, int max_items, hipStream_t s);
+hipError_t launch_pf_down(const PfGemmArgs& a, int bits, int bk, int max_items, hipStream_t s);
+hipError_t launch_pf_combine(const PfCombineArgs& a, hipStream_t s);

@@ -1,0 +1,893 @@
+// prefill.hip -- chunked prefill (T > 8 tokens per call): the layer for a
+// prompt chunk of up to thousands of tokens [agentlenshq article, section
+// "Strata 如何让 125 B 模型适配 12-24 GB 显存", last item; cnyes profile,
+// section "速度倍增器"].
+//
+// Steps (kernels in launch order):
+//   prep      per token row: power-of-two exponent ex with 2^14 <= max|x| *
+//             2^-ex < 2^15, then x * 2^-ex split into fp16 hi + lo (the
+//             scaling is exact and keeps every row in fp16 range);
+//   router    logits = 2^(ex+ew) * (xh.wh + xh.wl + xl.wh) + bias on the
+//             matrix cores (three fp16 products, ~22-bit operands, fp32
+//             accumulation), then the shared top-k kernel;
+//   group     token-to-expert counting sort: per 64-token tile a bitmap of
+//             the tokens of each expert, a scan over tiles and experts, and a
+//             permute that places pair (t, r) at row offsets[e] + (tokens of
+//             e in earlier tiles) + (tokens of e earlier in its tile); rows of
+//             one expert are padded to a multiple of 16 and cut into work
+//             items of up to 128 rows; the shared expert's rows follow;
+//   gate_up   per item and 128 intermediate columns: G = X W_g^T, U = X W_u^T
+//             with the weights dequantized in registers to fp16 s * c (exact
+//             for 2-bit codes, one rounding for 3-bit), x rows gathered
+//             into LDS by direct-to-LDS loads, v_mfma_f32_16x16x32_f16;
+//             epilogue h = silu(g) * u in fp32, stored as fp16 with one
+//             power-of-two exponent per (row, 128-column tile);
+//   down      per item and 256 output columns: Y = H W_d^T, H rows brought to
+//             one exponent per row while they are staged into LDS; epilogue
+//             multiplies by the gate weight and writes one fp32 row per pair;
+//   combine   y[t] = sum of its pairs' rows in rank order + its shared row.
+// Every product on the matrix cores is exact; the roundings are the fp16
+// activations (x, h), 3-bit weights with a code of +-3, and fp32 accumulation.
+#include <type_traits>
+
+#include "kern_common.h"
+#include "moe_launch.h"
+
+namespace {
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+DEVI float wave_maxf(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+DEVI float row16_max(float v) {
+#pragma unroll
+  for (int st = 0; st < 4; ++st) v = fmaxf(v, __uint_as_float(dpp_perm(__float_as_uint(v), st)));
+  return v;
+}
+
+// Exponent e with 2^14 <= m * 2^-e < 2^15 (0 when m is 0 or not a number).
+DEVI int fp16_exponent_for(float m) {
+  if (!(m > 0.f)) return 0;
+  int e;
+  frexpf(m, &e);  // m = f * 2^e, 0.5 <= f < 1
+  return e - 15;
+}
+
+DEVI _Float16 half_of_bits(uint32_t b) {
+  _Float16 h;
+  const uint16_t v = (uint16_t)b;
+  __builtin_memcpy(&h, &v, 2);
+  return h;
+}
+
+// ---------------------------------------------------------------------------
+// Weight registers of one 16-row tile for up to 8 fragments (a full chunk) or
+// 4 fragments (half a chunk: codes and scales in elements [0..1], high bits
+// in hi[0]).  Fragment f: codes dword f/2 at shift 2(f%2), fp16 scale half f,
+// high bits dword f/4 at bit f%4.
+// ---------------------------------------------------------------------------
+struct WRegs {
+  u32x4_t codes;
+  u32x4_t scales;
+  u32x2_t hi;
+};
+
+template <int BITS>
+DEVI void load_full(WRegs& w, const uint8_t* chunk, int lane) {
+  w.codes = ld128(chunk + 16 * lane);
+  w.scales = ld128(chunk + 1024 + 16 * (lane & 15));
+  if constexpr (BITS == 3) w.hi = ld64(chunk + 1280 + 8 * lane);
+}
+
+// fragments 4h..4h+3 of a chunk
+template <int BITS>
+DEVI void load_half(WRegs& w, const uint8_t* chunk, int h, int lane) {
+  const u32x2_t c = ld64(chunk + 16 * lane + 8 * h);
+  const u32x2_t s = ld64(chunk + 1024 + 16 * (lane & 15) + 8 * h);
+  w.codes = u32x4_t{c[0], c[1], 0u, 0u};
+  w.scales = u32x4_t{s[0], s[1], 0u, 0u};
+  if constexpr (BITS == 3) w.hi = u32x2_t{*reinterpret_cast<const uint32_t*>(chunk + 1280 + 8 * lane + 4 * h), 0u};
+}
+
+// w = s * (q - 2^(b-1)) for the lane's 8 codes of fragment f, in fp16: q is
+// exact from the fp4 conversion, the fused multiply-add rounds once.
+template <int BITS>
+DEVI half8_t dequant(const WRegs& w, int f) {
+  const uint32_t dw = w.codes[f >> 1];
+  half8_t q = nibbles_to_half8(((f & 1) ? (dw >> 2) : dw) & 0x33333333u, 2.0f);
+  if constexpr (BITS == 3) q += nibbles_to_half8((w.hi[f >> 2] >> (f & 3)) & 0x11111111u, 8.0f);
+  const uint32_t sd = w.scales[f >> 1];
+  const _Float16 s = half_of_bits((f & 1) ? (sd >> 16) : sd);
+  const half8_t sv = s;
+  const half8_t ov = sv * (_Float16)(-(float)(1 << (BITS - 1)));
+  return __builtin_elementwise_fma(q, sv, ov);
+}
+
+// ---------------------------------------------------------------------------
+// Router weights, prepared at pack time: row exponent ew (as for x) and the
+// row times 2^-ew split into fp16 hi + lo, stored as MFMA B fragments
+// [E16/16][d/32][64 lanes][8]: lane l holds row 16*tile + l%16, inputs
+// 32*block + 8*(l/16) .. +8.  Rows E..E16-1 are zero.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pack_router_kernel(const float* W, int E, int E16, int d, _Float16* wh,
+                                                          _Float16* wl, int32_t* ew) {
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 4 + wv;
+  if (e >= E16) return;
+  const bool valid = e < E;
+  const float* row = W + (size_t)(valid ? e : 0) * d;
+  float m = 0.f;
+  if (valid)
+    for (int c = 4 * lane; c < d; c += 256) {
+      const float4_t v = *reinterpret_cast<const float4_t*>(row + c);
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+    }
+  m = wave_maxf(m);
+  const int x = fp16_exponent_for(m);
+  if (lane == 0) ew[e] = x;
+  const int nb = d / 32;
+  for (int g = lane; g < d / 8; g += 64) {
+    half8_t hi, lo;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float v = valid ? ldexpf(row[8 * g + i], -x) : 0.f;
+      const _Float16 h = (_Float16)v;
+      hi[i] = h;
+      lo[i] = (_Float16)(v - (float)h);
+    }
+    const size_t off = (((size_t)(e >> 4) * nb + (g >> 2)) * 64 + (e & 15) + 16 * (g & 3)) * 8;
+    *reinterpret_cast<half8_t*>(wh + off) = hi;
+    *reinterpret_cast<half8_t*>(wl + off) = lo;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// prep: one wave per token row.  With norm set the row is first divided by
+// sqrt(mean(x^2) + eps) (the RMSNorm between stacked layers).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pf_prep_kernel(PfPrepArgs a) {
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wv;
+  if (t >= a.T) return;
+  const float* xr = a.x + (size_t)t * a.d;
+  float m = 0.f, ss = 0.f;
+  for (int c = 4 * lane; c < a.d; c += 256) {
+    const float4_t v = *reinterpret_cast<const float4_t*>(xr + c);
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+    ss = fmaf(v[0], v[0], ss);
+    ss = fmaf(v[1], v[1], ss);
+    ss = fmaf(v[2], v[2], ss);
+    ss = fmaf(v[3], v[3], ss);
+  }
+  m = wave_maxf(m);
+  float rms = 1.f;
+  if (a.norm) {
+    ss = wave_sum(ss);
+    rms = sqrtf(ss / (float)a.d + a.eps);
+    m = m / rms;  // division is monotonic: the largest quotient is the quotient of the largest
+  }
+  const int ex = fp16_exponent_for(m);
+  if (lane == 0) a.ex[t] = ex;
+  for (int c = 4 * lane; c < a.d; c += 256) {
+    const float4_t v = *reinterpret_cast<const float4_t*>(xr + c);
+    half2_t h01, h23, l01, l23;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float s = ldexpf(a.norm ? v[i] / rms : v[i], -ex);
+      const _Float16 h = (_Float16)s;
+      const _Float16 l = (_Float16)(s - (float)h);
+      if (i < 2) { h01[i] = h; l01[i] = l; } else { h23[i - 2] = h; l23[i - 2] = l; }
+    }
+    *reinterpret_cast<half2_t*>(a.xh + (size_t)t * a.d + c) = h01;
+    *reinterpret_cast<half2_t*>(a.xh + (size_t)t * a.d + c + 2) = h23;
+    *reinterpret_cast<half2_t*>(a.xl + (size_t)t * a.d + c) = l01;
+    *reinterpret_cast<half2_t*>(a.xl + (size_t)t * a.d + c + 2) = l23;
+  }
+}
+
+template <int P>
+using ic = std::integral_constant<int, P>;
+
+// s_waitcnt immediate (gfx9 encoding): wait until at most n vector-memory
+// operations of this wave are outstanding; LDS and export counters free.
+constexpr int16_t vmcnt_imm(int n) { return (int16_t)((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8)); }
+
+// Three pipeline stages in three separate LDS arrays, so that the compiler
+// can see that a direct-to-LDS load into one stage does not alias reads of
+// another (with one array it waits for every outstanding load before each
+// LDS read).  Step s uses stage s % 3; its loads are issued two steps ahead.
+struct Stages {
+  unsigned char* s0;
+  unsigned char* s1;
+  unsigned char* s2;
+  template <int P>
+  DEVI unsigned char* get() const { return P == 0 ? s0 : P == 1 ? s1 : s2; }
+};
+
+// ---------------------------------------------------------------------------
+// router GEMM: workgroup = 128 tokens x 128 experts, wave = 128 tokens x 32
+// experts; x hi/lo fragments staged in LDS by direct loads (2 blocks per
+// step, three stages), weight fragments straight into registers.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pf_router_kernel(PfRouterArgs a) {
+  constexpr int KS = 2;
+  constexpr int STAGE = 2 * 8 * KS * 1024;  // [hi/lo][row group][block] fragments
+  __shared__ __attribute__((aligned(1024))) unsigned char st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st1[STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st2[STAGE];
+  const Stages S{st0, st1, st2};
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, n = lane & 15, q = lane >> 4;
+  const int row0 = blockIdx.x * 128;
+  const int nb = a.d / 32, n_et = a.E16 / 16;
+  const int et0 = blockIdx.y * 8 + 2 * wv;
+  const bool act0 = et0 < n_et, act1 = et0 + 1 < n_et;
+  const int etl[2] = {act0 ? et0 : 0, act1 ? et0 + 1 : 0};  // idle tiles load (and ignore) tile 0
+  int tok[8];
+#pragma unroll
+  for (int rg = 0; rg < 8; ++rg) tok[rg] = min(row0 + 16 * rg + n, a.T - 1);
+  // this wave stages part hl (hi or lo) of block kb of every row group
+  const int hl = wv >> 1, dkb = wv & 1;
+  const _Float16* asrc = hl ? a.xl : a.xh;
+
+  float4_t acc[8][2];
+#pragma unroll
+  for (int rg = 0; rg < 8; ++rg)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[rg][j] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  constexpr int LOADS = 8 + KS * 2 * 2;
+  u32x4_t bh[3][KS][2], bl[3][KS][2];
+  const int nsteps = nb / KS;
+  auto issue = [&](auto P_, int s) {
+    constexpr int P = decltype(P_)::value;
+    unsigned char* st = S.get<P>();
+#pragma unroll
+    for (int rg = 0; rg < 8; ++rg)
+      __builtin_amdgcn_global_load_lds(asrc + (size_t)tok[rg] * a.d + (KS * s + dkb) * 32 + 8 * q,
+                                       (lds_ptr_t)(st + ((hl * 8 + rg) * KS + dkb) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int kb = 0; kb < KS; ++kb)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const size_t off = (((size_t)etl[j] * nb + KS * s + kb) * 64 + lane) * 8;
+        bh[P][kb][j] = ld128(a.wh + off);
+        bl[P][kb][j] = ld128(a.wl + off);
+      }
+  };
+  auto step = [&](auto P_, int s) {
+    constexpr int P = decltype(P_)::value;
+    if (s + 1 < nsteps) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    if (s + 2 < nsteps) issue(ic<(P + 2) % 3>{}, s + 2);
+    if (act0) {
+      const unsigned char* st = S.get<P>();
+#pragma unroll
+      for (int kb = 0; kb < KS; ++kb) {
+        half8_t ah[8], al[8];
+#pragma unroll
+        for (int rg = 0; rg < 8; ++rg) {
+          ah[rg] = *reinterpret_cast<const half8_t*>(st + ((0 * 8 + rg) * KS + kb) * 1024 + 16 * lane);
+          al[rg] = *reinterpret_cast<const half8_t*>(st + ((1 * 8 + rg) * KS + kb) * 1024 + 16 * lane);
+        }
+#pragma unroll
+        for (int term = 0; term < 3; ++term)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            if (j == 0 || act1) {
+              const half8_t B = __builtin_bit_cast(half8_t, term == 1 ? bl[P][kb][j] : bh[P][kb][j]);
+#pragma unroll
+              for (int rg = 0; rg < 8; ++rg) acc[rg][j] = mfma16x16x32(term == 2 ? al[rg] : ah[rg], B, acc[rg][j]);
+            }
+      }
+    }
+  };
+  issue(ic<0>{}, 0);
+  if (nsteps > 1) issue(ic<1>{}, 1);
+  for (int s = 0; s < nsteps; s += 3) {
+    step(ic<0>{}, s);
+    if (s + 1 < nsteps) step(ic<1>{}, s + 1);
+    if (s + 2 < nsteps) step(ic<2>{}, s + 2);
+  }
+#pragma unroll
+  for (int rg = 0; rg < 8; ++rg)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int e = (et0 + j) * 16 + n;
+      if (!(j == 0 ? act0 : act1) || e >= a.E) continue;
+      const int ewe = a.ew[e];
+      const float b = a.bias[e];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = row0 + 16 * rg + 4 * q + i;
+        if (t < a.T) a.logits[(size_t)t * a.E + e] = ldexpf(acc[rg][j][i], a.ex[t] + ewe) + b;
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// grouping (token-to-expert counting sort)
+// ---------------------------------------------------------------------------
+// hist: one wave per 64-token tile; bit (t mod 64) of bm[e] is set when token
+// t names expert e (a repeated id of one token sets the same bit again).
+__global__ __launch_bounds__(64) void pf_hist_kernel(PfGroupArgs a) {
+  __shared__ unsigned long long bm[MOE_MAX_E];
+  const int lane = threadIdx.x, tile = blockIdx.x;
+  for (int e = lane; e < a.E; e += 64) bm[e] = 0ull;
+  __syncthreads();
+  const int t = tile * PF_T64 + lane;
+  if (t < a.T)
+    for (int r = 0; r < a.k; ++r) {
+      const int e = a.idx[(size_t)t * a.k + r];
+      if (e >= 0 && e < a.E) atomicOr(&bm[e], 1ull << lane);
+    }
+  __syncthreads();
+  for (int e = lane; e < a.E; e += 64) {
+    const unsigned long long v = bm[e];
+    a.tile_bm[(size_t)tile * a.E + e] = v;
+    a.tile_cnt[(size_t)tile * a.E + e] = __popcll(v);
+  }
+}
+
+// Exclusive prefix sum over the 1024 threads of the block.
+DEVI int block_exclusive_scan(int v, int* sbuf, int tid, int* total) {
+  sbuf[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int o = tid >= off ? sbuf[tid - off] : 0;
+    __syncthreads();
+    sbuf[tid] += o;
+    __syncthreads();
+  }
+  const int incl = sbuf[tid];
+  *total = sbuf[1023];
+  __syncthreads();
+  return incl - v;
+}
+
+// scan: one block of 1024 threads.  Per expert: counts over tiles (and the
+// exclusive prefix over tiles, in place); then padded row offsets, padding
+// rows, shared rows and the work-item list.
+__global__ __launch_bounds__(1024) void pf_scan_kernel(PfGroupArgs a) {
+  __shared__ int cnt[MOE_MAX_E];
+  __shared__ int sbuf[1024];
+  const int tid = threadIdx.x;
+  const int E = a.E;
+  for (int e = tid; e < E; e += 1024) {
+    int run = 0;
+    int* col = a.tile_cnt + e;
+    // 32 loads in flight per round trip
+    for (int t0 = 0; t0 < a.n_tiles; t0 += 32) {
+      int c[32];
+#pragma unroll
+      for (int u = 0; u < 32; ++u) c[u] = t0 + u < a.n_tiles ? col[(size_t)(t0 + u) * E] : 0;
+#pragma unroll
+      for (int u = 0; u < 32; ++u)
+        if (t0 + u < a.n_tiles) { col[(size_t)(t0 + u) * E] = run; run += c[u]; }
+    }
+    cnt[e] = run;
+    a.counts[e] = run;
+  }
+  __syncthreads();
+  // thread tid owns experts 4 tid .. 4 tid + 3
+  int pc[4], ni[4], rsum = 0, isum = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int e = 4 * tid + u;
+    const int c = e < E ? cnt[e] : 0;
+    pc[u] = (c + a.pad - 1) / a.pad * a.pad;
+    ni[u] = (pc[u] + a.TM - 1) / a.TM;
+    rsum += pc[u];
+    isum += ni[u];
+  }
+  int rows_routed, items_routed;
+  int roff = block_exclusive_scan(rsum, sbuf, tid, &rows_routed);
+  int ioff = block_exclusive_scan(isum, sbuf, tid, &items_routed);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int e = 4 * tid + u;
+    if (e < E) {
+      a.offsets[e] = roff;
+      for (int p = roff + cnt[e]; p < roff + pc[u]; ++p) {
+        a.row_src[p] = -1;
+        if (a.row_tok) { a.row_tok[p] = 0; a.row_w[p] = 0.f; }
+      }
+      if (a.n_items)
+        for (int j = 0; j < ni[u]; ++j) {
+          a.item_group[ioff + j] = e;
+          a.item_row0[ioff + j] = roff + j * a.TM;
+          a.item_rows[ioff + j] = min(a.TM, pc[u] - j * a.TM);
+        }
+    }
+    roff += pc[u];
+    ioff += ni[u];
+  }
+  const int rows_sh = a.has_shared ? (a.T + 15) / 16 * 16 : 0;
+  const int items_sh = (rows_sh + a.TM - 1) / a.TM;
+  if (tid == 0) {
+    a.offsets[E] = rows_routed;
+    if (a.n_items) {
+      a.offsets[E + 1] = rows_routed + rows_sh;
+      *a.n_items = items_routed + items_sh;
+    }
+  }
+  for (int t = tid; t < rows_sh; t += 1024) {
+    const int p = rows_routed + t;
+    a.row_src[p] = -1;
+    a.row_tok[p] = t < a.T ? t : 0;
+    a.row_w[p] = t < a.T ? 1.f : 0.f;
+  }
+  if (a.n_items)
+    for (int j = tid; j < items_sh; j += 1024) {
+      a.item_group[items_routed + j] = E;
+      a.item_row0[items_routed + j] = rows_routed + j * a.TM;
+      a.item_rows[items_routed + j] = min(a.TM, rows_sh - j * a.TM);
+    }
+  for (int p = rows_routed + tid; p < a.R_fill; p += 1024) a.row_src[p] = -1;
+}
+
+// permute: one thread per (t, r).  A pair is used unless its id is outside
+// [0, E) or repeats an earlier slot of the same token.
+__global__ __launch_bounds__(256) void pf_permute_kernel(PfGroupArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)a.T * a.k) return;
+  const int t = (int)(i / a.k), r = (int)(i - (int64_t)t * a.k);
+  const int e = a.idx[i];
+  bool ok = e >= 0 && e < a.E;
+  for (int u = 0; u < r && ok; ++u) ok = a.idx[(size_t)t * a.k + u] != e;
+  if (!ok) {
+    if (a.slot_pos) a.slot_pos[i] = -1;
+    return;
+  }
+  const int tile = t / PF_T64, bit = t % PF_T64;
+  const size_t te = (size_t)tile * a.E + e;
+  const int rank = __popcll(a.tile_bm[te] & ((1ull << bit) - 1ull));
+  const int p = a.offsets[e] + a.tile_cnt[te] + rank;
+  a.row_src[p] = (int32_t)i;
+  if (a.row_tok) {
+    a.row_tok[p] = t;
+    a.row_w[p] = a.w ? a.w[i] : 1.f;
+  }
+  if (a.slot_pos) a.slot_pos[i] = p;
+}
+
+// ---------------------------------------------------------------------------
+// gate/up grouped GEMM.  Workgroup: one work item (up to 128 rows of one
+// expert) x 128 intermediate columns; wave wv: all rows x columns
+// h0 = 128 nt + 32 wv .. +32 of both gate and up (4 tiles of 16 weight rows).
+// Per step of 4 blocks (128 inputs): A fragments [row group][block] in LDS
+// (wave wv stages block wv of every row group), weights of the step (half
+// a chunk per tile) in registers, double buffered.
+// ---------------------------------------------------------------------------
+constexpr int GEMM_STAGE = 8 * 4 * 1024;  // [row group][block] fragments of one step
+
+// Work-item placement.  Workgroups are dispatched to the 8 XCDs (each with its
+// own L2) in turn: workgroup b runs on XCD b % 8.  XCD x takes the x-th
+// contiguous eighth of the item list, and the n_nt column tiles of one item
+// run back to back on it, so an item's activation rows and an expert's
+// weights are fetched into one L2 and reused there.  The grid has
+// 8 * ceil(max_items / 8) * n_nt workgroups; the surplus exits at once.
+constexpr int N_XCD = 8;
+DEVI bool xcd_tile(int n_items, int n_nt, int* item, int* nt) {
+  const int x = blockIdx.x % N_XCD, j = blockIdx.x / N_XCD;
+  const int ipx = (n_items + N_XCD - 1) / N_XCD;
+  const int li = j / n_nt;
+  *item = x * ipx + li;
+  *nt = j - li * n_nt;
+  return li < ipx && *item < n_items;
+}
+
+// Scheduling hint for one block of a step: spread NV vector-ALU and ND LDS
+// reads (the next block's operands) between the NM matrix multiplies, so a
+// single wave keeps the matrix core busy while it dequantizes.
+template <int NM, int ND, int NV>
+DEVI void interleave() {
+  constexpr int VPER = (NV + NM - 1) / NM;
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    if (i < ND) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    __builtin_amdgcn_sched_group_barrier(0x002, VPER, 0);  // VALU
+  }
+}
+
+template <int BITS, int NRG>
+DEVI void gate_up_item(const PfGemmArgs& a, const Stages& S, float* amax_lds, int* ex_lds, int g, int row0,
+                       int rows, int nt) {
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, n = lane & 15, q = lane >> 4;
+  const bool shared = g == a.E;
+  const int Ig = shared ? a.Is : a.I;
+  const uint8_t* eb = shared ? a.X.shared : a.X.experts + (int64_t)g * a.X.ex_stride;
+  const int h0 = nt * PF_HT + 32 * wv;
+  const bool act = h0 < Ig;
+  const int nkg = a.d / 256;
+  constexpr int CB = BITS == 2 ? 1280 : 1792;
+  const uint8_t* cp[4];
+  {
+    const uint8_t* gate = eb + (shared ? a.X.sh_off_gate : a.X.off_gate);
+    const uint8_t* up = eb + (shared ? a.X.sh_off_up : a.X.off_up);
+    const int hr = act ? h0 : 0;  // idle waves load (and ignore) row group 0
+    cp[0] = gate + (int64_t)(hr / 16) * nkg * CB;
+    cp[1] = cp[0] + (int64_t)nkg * CB;
+    cp[2] = up + (int64_t)(hr / 16) * nkg * CB;
+    cp[3] = cp[2] + (int64_t)nkg * CB;
+  }
+  int tokr[NRG];
+#pragma unroll
+  for (int rg = 0; rg < NRG; ++rg) tokr[rg] = (16 * rg < rows) ? a.row_tok[row0 + 16 * rg + n] : 0;
+  const int my_tok = tid < rows ? a.row_tok[row0 + tid] : 0;
+
+  float4_t acc[NRG][4];
+#pragma unroll
+  for (int rg = 0; rg < NRG; ++rg)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[rg][m] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  // every wave issues the same number of loads per step: one direct-to-LDS
+  // load per row group (rows past the item read token 0) and the weight
+  // registers of its 4 row tiles
+  constexpr int LOADS = NRG + (BITS == 3 ? 12 : 8);
+  WRegs bw[3][4];
+  const int nsteps = a.d / 128;
+  auto issue = [&](auto P_, int s) {
+    constexpr int P = decltype(P_)::value;
+    unsigned char* st = S.get<P>();
+#pragma unroll
+    for (int rg = 0; rg < NRG; ++rg)
+      __builtin_amdgcn_global_load_lds(a.xh + (size_t)tokr[rg] * a.d + (4 * s + wv) * 32 + 8 * q,
+                                       (lds_ptr_t)(st + (rg * 4 + wv) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) load_half<BITS>(bw[P][m], cp[m] + (int64_t)(s >> 1) * CB, s & 1, lane);
+  };
+  auto step = [&](auto P_, int s) {
+    constexpr int P = decltype(P_)::value;
+    if (s + 1 < nsteps) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    if (s + 2 < nsteps) issue(ic<(P + 2) % 3>{}, s + 2);
+    if (act) {
+      const unsigned char* st = S.get<P>();
+      // software pipeline over the 4 blocks of the step: the A fragments and
+      // the dequantized weights of block kb + 1 are produced while the
+      // matrix cores work on block kb
+      half8_t A[NRG], B[4];
+#pragma unroll
+      for (int rg = 0; rg < NRG; ++rg) A[rg] = *reinterpret_cast<const half8_t*>(st + (rg * 4) * 1024 + 16 * lane);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) B[m] = dequant<BITS>(bw[P][m], 0);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        half8_t An[NRG], Bn[4];
+        if (kb < 3) {
+#pragma unroll
+          for (int rg = 0; rg < NRG; ++rg)
+            An[rg] = *reinterpret_cast<const half8_t*>(st + (rg * 4 + kb + 1) * 1024 + 16 * lane);
+#pragma unroll
+          for (int m = 0; m < 4; ++m) Bn[m] = dequant<BITS>(bw[P][m], kb + 1);
+        }
+#pragma unroll
+        for (int rg = 0; rg < NRG; ++rg)
+#pragma unroll
+          for (int m = 0; m < 4; ++m) acc[rg][m] = mfma16x16x32(A[rg], B[m], acc[rg][m]);
+        if (kb < 3) {
+          interleave<4 * NRG, NRG, (BITS == 3 ? 80 : 48)>();
+#pragma unroll
+          for (int rg = 0; rg < NRG; ++rg) A[rg] = An[rg];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) B[m] = Bn[m];
+        }
+      }
+    }
+  };
+  issue(ic<0>{}, 0);
+  if (nsteps > 1) issue(ic<1>{}, 1);
+  if (tid < PF_TM) ex_lds[tid] = a.ex[my_tok];  // visible after the first step's barrier
+  for (int s = 0; s < nsteps; s += 3) {
+    step(ic<0>{}, s);
+    if (s + 1 < nsteps) step(ic<1>{}, s + 1);
+    if (s + 2 < nsteps) step(ic<2>{}, s + 2);
+  }
+
+  // epilogue: h = silu(g) u with g, u scaled back by 2^ex of the row's token
+  float hv[NRG][2][4];
+#pragma unroll
+  for (int rg = 0; rg < NRG; ++rg)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * rg + 4 * q + i;
+      const int ex = ex_lds[r];
+      float m = 0.f;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float gg = ldexpf(acc[rg][j][i], ex);
+        const float uu = ldexpf(acc[rg][2 + j][i], ex);
+        const float h = gg * __builtin_amdgcn_rcpf(1.0f + __expf(-gg)) * uu;
+        hv[rg][j][i] = h;
+        m = fmaxf(m, fabsf(h));
+      }
+      m = row16_max(m);
+      if (n == 0) amax_lds[wv * PF_TM + r] = act ? m : 0.f;
+    }
+  __syncthreads();
+  if (tid < rows) {
+    const float m = fmaxf(fmaxf(amax_lds[tid], amax_lds[PF_TM + tid]), fmaxf(amax_lds[2 * PF_TM + tid], amax_lds[3 * PF_TM + tid]));
+    a.eh[(size_t)nt * a.R + row0 + tid] = fp16_exponent_for(m);
+  }
+  // h tile in MFMA A-fragment order [row group][4 blocks] (stage 0 is free:
+  // every load has landed and every wave is past its last read)
+  uint32_t* tile = reinterpret_cast<uint32_t*>(S.s0);
+  if (act)
+#pragma unroll
+    for (int rg = 0; rg < NRG; ++rg)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rg + 4 * q + i;
+        const float m = fmaxf(fmaxf(amax_lds[r], amax_lds[PF_TM + r]), fmaxf(amax_lds[2 * PF_TM + r], amax_lds[3 * PF_TM + r]));
+        const int e = fp16_exponent_for(m);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          // columns c = 16 j + n and c + 1 (lanes n, n + 1) share one dword
+          const _Float16 v = (_Float16)ldexpf(hv[rg][j][i], -e);
+          uint16_t vb;
+          __builtin_memcpy(&vb, &v, 2);
+          const uint32_t nb = (uint32_t)__builtin_amdgcn_mov_dpp((int)vb, 0xB1, 0xF, 0xF, true);  // lane n ^ 1
+          if ((n & 1) == 0) {
+            const int c = 16 * j + n;
+            tile[((rg * 4 + wv) * 64 + 4 * q + i + 16 * (c >> 3)) * 4 + ((c & 7) >> 1)] = (uint32_t)vb | (nb << 16);
+          }
+        }
+      }
+  __syncthreads();
+  if (act)
+#pragma unroll
+    for (int rg = 0; rg < NRG; ++rg)
+      if (16 * rg < rows) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(S.s0 + ((rg * 4 + wv) * 64 + lane) * 16);
+        *reinterpret_cast<u32x4_t*>(a.hfrag + (((size_t)((row0 >> 4) + rg) * a.nbH + nt * 4 + wv) * 64 + lane) * 8) = v;
+      }
+}
+
+template <int BITS>
+__global__ __launch_bounds__(256) void pf_gate_up_kernel(PfGemmArgs a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char st0[GEMM_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st1[GEMM_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st2[GEMM_STAGE];
+  __shared__ float amax_lds[4 * PF_TM];
+  __shared__ int ex_lds[PF_TM];
+  int item, nt;
+  if (!xcd_tile(*a.n_items, a.n_nt, &item, &nt)) return;
+  const int g = a.item_group[item], row0 = a.item_row0[item], rows = a.item_rows[item];
+  const int Ig = g == a.E ? a.Is : a.I;
+  if (nt * PF_HT >= Ig) return;
+  const int nrg = rows >> 4;
+  const Stages S{st0, st1, st2};
+  if (nrg > 4) gate_up_item<BITS, 8>(a, S, amax_lds, ex_lds, g, row0, rows, nt);
+  else if (nrg > 2) gate_up_item<BITS, 4>(a, S, amax_lds, ex_lds, g, row0, rows, nt);
+  else if (nrg > 1) gate_up_item<BITS, 2>(a, S, amax_lds, ex_lds, g, row0, rows, nt);
+  else gate_up_item<BITS, 1>(a, S, amax_lds, ex_lds, g, row0, rows, nt);
+}
+
+// ---------------------------------------------------------------------------
+// down grouped GEMM.  Workgroup: one work item x 256 output columns; wave wv:
+// all rows x output columns r0 = 256 nt + 64 wv .. +64 (4 tiles of 16 rows of
+// W_d).  The packed down matrix has row groups of 16 RT rows and k-groups of
+// BK blocks (RT BK = 8); per step of 4 blocks the wave holds NC chunk
+// registers:
+//   BK 8: 4 half chunks (one per row tile),   fragment (t, j) = (c t, f j)
+//   BK 4: 2 full chunks (row tiles 2c, 2c+1), fragment (t, j) = (c t/2, f 4(t%2)+j)
+//   BK 2: 2 full chunks (blocks 2c, 2c+1),    fragment (t, j) = (c j/2, f 2t+j%2)
+//   BK 1: 4 half chunks (one per block),      fragment (t, j) = (c j, f t)
+// H rows: staged through registers so that each 128-column tile is brought
+// from its own exponent to the row's largest one (an exact power-of-two
+// product, unless it underflows) before it is written to LDS.
+// ---------------------------------------------------------------------------
+template <int BK>
+struct DownMap {
+  static constexpr int NC = (BK == 4 || BK == 2) ? 2 : 4;
+  static constexpr bool HALF = (BK == 8 || BK == 1);
+  static DEVI constexpr int chunk(int t, int j) { return BK == 8 ? t : BK == 4 ? t / 2 : BK == 2 ? j / 2 : j; }
+  static DEVI constexpr int frag(int t, int j) { return BK == 8 ? j : BK == 4 ? 4 * (t % 2) + j : BK == 2 ? 2 * t + j % 2 : t; }
+};
+
+template <int BITS, int BK, int NRG>
+DEVI void down_item(const PfGemmArgs& a, unsigned char* lds, float* rowf_lds, int g, int row0, int rows, int nt) {
+  using M = DownMap<BK>;
+  constexpr int RT = 8 / BK;
+  constexpr int CB = BITS == 2 ? 1280 : 1792;
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, n = lane & 15, q = lane >> 4;
+  const bool shared = g == a.E;
+  const int Ig = shared ? a.Is : a.I;
+  const int nbK = Ig / 32, n_kg = nbK / BK, nsteps = (nbK + 3) / 4;
+  const uint8_t* dm =
+      (shared ? a.X.shared : a.X.experts + (int64_t)g * a.X.ex_stride) + (shared ? a.X.sh_off_down : a.X.off_down);
+  const int r0 = nt * PF_DT + 64 * wv;
+
+  // the row's largest intermediate-tile exponent, for the lane's staging rows
+  int eref[NRG];
+#pragma unroll
+  for (int rg = 0; rg < NRG; ++rg) {
+    int e = -1000;
+    if (16 * rg < rows)
+      for (int s = 0; s < nsteps; ++s) e = max(e, a.eh[(size_t)s * a.R + row0 + 16 * rg + n]);
+    eref[rg] = e;
+    if (wv == 0 && q == 0 && 16 * rg < rows)
+      rowf_lds[16 * rg + n] = ldexpf(a.row_w[row0 + 16 * rg + n], e);
+  }
+
+  float4_t acc[NRG][4];
+#pragma unroll
+  for (int rg = 0; rg < NRG; ++rg)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[rg][t] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  WRegs cur[M::NC], nxt[M::NC];
+  u32x4_t stg[NRG];
+  int stg_e[NRG];
+  auto issue = [&](int s) {
+    const int kb = 4 * s + wv;
+#pragma unroll
+    for (int rg = 0; rg < NRG; ++rg)
+      if (16 * rg < rows && kb < nbK) {
+        stg[rg] = ld128(a.hfrag + (((size_t)((row0 >> 4) + rg) * a.nbH + kb) * 64 + lane) * 8);
+        stg_e[rg] = a.eh[(size_t)s * a.R + row0 + 16 * rg + n];
+      }
+#pragma unroll
+    for (int c = 0; c < M::NC; ++c) {
+      if constexpr (BK == 8) {
+        load_half<BITS>(nxt[c], dm + ((int64_t)(r0 / 16 + c) * n_kg + (s >> 1)) * CB, s & 1, lane);
+      } else if constexpr (BK == 4) {
+        load_full<BITS>(nxt[c], dm + ((int64_t)(r0 / 32 + c) * n_kg + s) * CB, lane);
+      } else if constexpr (BK == 2) {
+        if (2 * s + c < n_kg) load_full<BITS>(nxt[c], dm + ((int64_t)(r0 / 64) * n_kg + 2 * s + c) * CB, lane);
+      } else {
+        if (4 * s + c < n_kg)
+          load_half<BITS>(nxt[c], dm + ((int64_t)(r0 / 128) * n_kg + 4 * s + c) * CB, (r0 / 64) & 1, lane);
+      }
+    }
+  };
+  static_assert(RT * BK == 8, "chunk shape");
+  issue(0);
+  for (int s = 0; s < nsteps; ++s) {
+    __builtin_amdgcn_s_waitcnt(0);
+    {
+      unsigned char* st = lds + (s & 1) * GEMM_STAGE;
+      const int kb = 4 * s + wv;
+#pragma unroll
+      for (int rg = 0; rg < NRG; ++rg)
+        if (16 * rg < rows && kb < nbK) {
+          const _Float16 f = (_Float16)ldexpf(1.f, stg_e[rg] - eref[rg]);
+          const half8_t v = __builtin_bit_cast(half8_t, stg[rg]) * f;
+          *reinterpret_cast<half8_t*>(st + (rg * 4 + wv) * 1024 + 16 * lane) = v;
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < M::NC; ++c) cur[c] = nxt[c];
+    if (s + 1 < nsteps) issue(s + 1);
+    __syncthreads();
+    const unsigned char* st = lds + (s & 1) * GEMM_STAGE;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (4 * s + j >= nbK) break;
+      half8_t B[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) B[t] = dequant<BITS>(cur[M::chunk(t, j)], M::frag(t, j));
+#pragma unroll
+      for (int rg = 0; rg < NRG; ++rg) {
+        const half8_t A = *reinterpret_cast<const half8_t*>(st + (rg * 4 + j) * 1024 + 16 * lane);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[rg][t] = mfma16x16x32(A, B[t], acc[rg][t]);
+      }
+    }
+  }
+#pragma unroll
+  for (int rg = 0; rg < NRG; ++rg)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * rg + 4 * q + i;
+      if (r >= rows) continue;
+      const float f = rowf_lds[r];
+      float* yrow = a.ypart + (size_t)(row0 + r) * a.d + r0 + n;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) yrow[16 * t] = acc[rg][t][i] * f;
+    }
+}
+
+template <int BITS, int BK>
+__global__ __launch_bounds__(256) void pf_down_kernel(PfGemmArgs a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * GEMM_STAGE];
+  __shared__ float rowf_lds[PF_TM];
+  int item, nt;
+  if (!xcd_tile(*a.n_items, a.d / PF_DT, &item, &nt)) return;
+  const int g = a.item_group[item], row0 = a.item_row0[item], rows = a.item_rows[item];
+  const int nrg = rows >> 4;
+  if (nrg > 4) down_item<BITS, BK, 8>(a, lds, rowf_lds, g, row0, rows, nt);
+  else if (nrg > 2) down_item<BITS, BK, 4>(a, lds, rowf_lds, g, row0, rows, nt);
+  else if (nrg > 1) down_item<BITS, BK, 2>(a, lds, rowf_lds, g, row0, rows, nt);
+  else down_item<BITS, BK, 1>(a, lds, rowf_lds, g, row0, rows, nt);
+}
+
+// ---------------------------------------------------------------------------
+// combine: y[t] = sum over the token's used pairs in rank order + shared row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pf_combine_kernel(PfCombineArgs a) {
+  __shared__ int pos[MOE_MAX_K + 1];
+  const int t = blockIdx.x;
+  if (threadIdx.x < a.k) pos[threadIdx.x] = a.slot_pos[(size_t)t * a.k + threadIdx.x];
+  if (threadIdx.x == 0) pos[MOE_MAX_K] = a.has_shared ? a.offsets[a.E] + t : -1;
+  __syncthreads();
+  for (int c = 4 * threadIdx.x; c < a.d; c += 1024) {
+    float4_t acc = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < a.k; ++r) {
+      const int p = pos[r];
+      if (p >= 0) acc += *reinterpret_cast<const float4_t*>(a.ypart + (size_t)p * a.d + c);
+    }
+    if (pos[MOE_MAX_K] >= 0) acc += *reinterpret_cast<const float4_t*>(a.ypart + (size_t)pos[MOE_MAX_K] * a.d + c);
+    *reinterpret_cast<float4_t*>(a.y + (size_t)t * a.d + c) = acc;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pack_router(const float* W, int E, int d, _Float16* wh, _Float16* wl, int32_t* ew, hipStream_t s) {
+  const int E16 = (E + 15) / 16 * 16;
+  hipLaunchKernelGGL(pack_router_kernel, dim3((E16 + 3) / 4), dim3(256), 0, s, W, E, E16, d, wh, wl, ew);
+  return hipGetLastError();
+}
+
+hipError_t launch_pf_prep(const PfPrepArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(pf_prep_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_pf_router(const PfRouterArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(pf_router_kernel, dim3((a.T + 127) / 128, (a.E16 + PF_ET - 1) / PF_ET), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_pf_group(const PfGroupArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(pf_hist_kernel, dim3(a.n_tiles), dim3(64), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(pf_scan_kernel, dim3(1), dim3(1024), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t n = (int64_t)a.T * a.k;
+  hipLaunchKernelGGL(pf_permute_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_pf_gate_up(const PfGemmArgs& a, int bits, int max_items, hipStream_t s) {
+  const dim3 grid((unsigned)((max_items + N_XCD - 1) / N_XCD * N_XCD * a.n_nt));
+  if (bits == 2) hipLaunchKernelGGL(pf_gate_up_kernel<2>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(pf_gate_up_kernel<3>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_pf_down(const PfGemmArgs& a, int bits, int bk, int max_items, hipStream_t s) {
+  const dim3 grid((unsigned)((max_items + N_XCD - 1) / N_XCD * N_XCD * (a.d / PF_DT)));
+#define PF_DOWN(B, K) hipLaunchKernelGGL((pf_down_kernel<B, K>), grid, dim3(256), 0, s, a)
+  if (bits == 2) {
+    switch (bk) {
+      case 8: PF_DOWN(2, 8); break;
+      case 4: PF_DOWN(2, 4); break;
+      case 2: PF_DOWN(2, 2); break;
+      default: PF_DOWN(2, 1); break;
+    }
+  } else {
+    switch (bk) {
+      case 8: PF_DOWN(3, 8); break;
+      case 4: PF_DOWN(3, 4); break;
+      case 2: PF_DOWN(3, 2); break;
+      default: PF_DOWN(3, 1); break;
+    }
+  }
+#undef PF_DOWN
+  return hipGetLastError();
+}
+
+hipError_t launch_pf_combine(const PfCombineArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(pf_combine_kernel, dim3(a.T), dim3(256), 0, s, a);
+  return hipGetLastError();
+}

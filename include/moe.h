@@ -150,13 +150,20 @@ int moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
 /* One layer: y[T][d] = MoE(x[T][d]).  T = 0 is a no-op.  T <= 8 runs the
  * decode/verify kernels (experts streamed once per call with 128-bit loads
- * and multiplied from their codes); T > 8 runs the chunked-prefill kernels
- * (grouped matrix multiply on the matrix cores).  x and y must not alias.
- * `route` may be NULL.  ws_bytes >= moe_workspace_bytes(layer, T). */
+ * and multiplied from their codes, activations carried as fp16 hi + lo);
+ * 8 < T <= 65536 runs the chunked-prefill kernels: the (token, slot) pairs
+ * are grouped by expert (as moe_group_tokens) and each expert's rows go
+ * through a grouped matrix multiply on the matrix cores with the weights
+ * dequantized in registers to fp16 and the activations rounded to fp16
+ * after an exact per-row power-of-two scaling (fp32 accumulation).  In the
+ * prefill path a token's routing row with a repeated expert id uses the
+ * first occurrence only.  x and y must not alias.  `route` may be NULL.
+ * ws_bytes >= moe_workspace_bytes(layer, T). */
 int moe_layer_forward(const moe_layer *layer, const float *x, int T, float *y, const moe_route_io *route,
                       void *ws, size_t ws_bytes, void *stream);
 
-/* A stack of layers with RMSNorm (unit weight) between consecutive layers:
+/* A stack of layers with RMSNorm (unit weight) between consecutive layers
+ * (T <= 8: decode kernels; T > 8: prefill kernels, one layer after another):
  *   h_0 = x,  y_l = MoE_l(h_l),  h_{l+1} = y_l / sqrt(mean(y_l^2) + eps),
  *   y = y_{n-1}.
  * All layers must have equal d_model.  Optional per-layer outputs:
@@ -166,6 +173,22 @@ int moe_layer_forward(const moe_layer *layer, const float *x, int T, float *y, c
 int moe_stack_forward(const moe_layer *const *layers, int n_layers, const float *x, int T, float eps,
                       float *y, float *y_layers, int32_t *idx_layers, float *w_layers, void *ws,
                       size_t ws_bytes, void *stream);
+
+/* Token-to-expert grouping (counting sort) of a routing idx device int32
+ * [T][k].  Pair (t, r) names expert idx[t][r]; it is used unless that id is
+ * outside [0, E) or repeats an earlier slot of the same token.  Outputs
+ * (device int32):
+ *   counts  [E]     used pairs per expert
+ *   offsets [E+1]   exclusive prefix sum of counts; offsets[E] = used pairs
+ *   perm    [T*k]   t*k + r of the used pairs, by expert ascending and token
+ *                   ascending within an expert, then -1 up to T*k
+ * Bit-exact with the plain definition.  ws: device scratch of at least
+ * moe_group_workspace_bytes(T, E, k) bytes, 256-byte aligned.  This is the
+ * step the prefill path runs before its grouped matrix multiply.
+ * 0 <= T <= 65536, 1 <= E <= 4096, 1 <= k <= 16. */
+int moe_group_workspace_bytes(int T, int E, int k, size_t *bytes);
+int moe_group_tokens(const int32_t *idx, int T, int E, int k, int32_t *counts, int32_t *offsets, int32_t *perm,
+                     void *ws, size_t ws_bytes, void *stream);
 
 /* y[t] = x[t] / sqrt(mean(x[t]^2) + eps), fp32 in and out, d % 4 == 0. */
 int moe_rmsnorm(const float *x, int T, int d, float eps, float *y, void *stream);
@@ -184,9 +207,10 @@ int moe_debug_unpack(const moe_layer *layer, int expert, int mat, int8_t *codes,
 /* Per-kernel timing for measurement: while enabled, the library brackets
  * every launch of the chosen kernel class with a pair of HIP events on the
  * launch stream.  class 0 = decode gate/up expert kernel, 1 = decode down
- * expert kernel, 2 = router, 3 = prefill gate/up grouped GEMM, 4 = prefill
- * down grouped GEMM.  moe_timing_stop waits for the recorded events and
- * returns the summed duration and the number of launches. */
+ * expert kernel, 2 = decode router, 3 = prefill gate/up grouped GEMM, 4 =
+ * prefill down grouped GEMM, 5 = prefill router GEMM.  moe_timing_stop waits
+ * for the recorded events and returns the summed duration and the number of
+ * launches. */
 int moe_timing_start(int kernel_class, int max_launches);
 int moe_timing_stop(double *total_ms, int *launches);
 

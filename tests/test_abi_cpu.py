@@ -48,9 +48,11 @@ def test_packed_bytes_matches_format(bqe):
         desc = bqe.make_desc(wl.d, wl.E, wl.I, wl.Is, wl.k, wl.bits)
         n = bqe.moe_packed_bytes(desc)
         # the packed weights are exactly the canonical bytes (no expansion),
-        # plus the router, bias, a status word and 256-byte alignment
+        # plus the router (fp32, and an fp16 hi/lo copy with row exponents for
+        # the prefill router), bias, a status word and 256-byte alignment
         weights = wl.E * wl.expert_bytes() + (wl.expert_bytes(wl.Is) if wl.Is else 0)
-        router = wl.E * wl.d * 4 + wl.E * 4
+        E16 = (wl.E + 15) // 16 * 16
+        router = wl.E * wl.d * 4 + wl.E * 4 + E16 * wl.d * 4 + E16 * 4
         assert weights + router <= n <= weights + router + 256 * (4 * wl.E + 8), name
 
 
@@ -78,6 +80,8 @@ def test_host_checks_without_gpu(bqe):
     assert L.moe_layer_forward(None, None, 1, None, None, None, 0, None) == bqe.MOE_ERR_ARG
     assert L.moe_stack_forward(None, 0, None, 1, ctypes.c_float(1e-6), None, None, None, None, None, 0, None) == bqe.MOE_ERR_ARG
     assert L.moe_timing_start(9, 1) == bqe.MOE_ERR_ARG
+    assert L.moe_group_workspace_bytes(-1, 8, 2, ctypes.byref(ctypes.c_size_t())) == bqe.MOE_ERR_ARG
+    assert L.moe_group_tokens(None, 4, 8, 2, None, None, None, None, 0, None) == bqe.MOE_ERR_ARG
     assert L.moe_timing_stop(None, None) == bqe.MOE_ERR_ARG
     assert L.moe_debug_unpack(None, 0, 0, None, None, None, None) == bqe.MOE_ERR_ARG
     n = ctypes.c_size_t()
