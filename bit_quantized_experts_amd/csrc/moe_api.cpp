@@ -109,7 +109,7 @@ int check_desc(const moe_layer_desc* D) {
 // packed buffer: [status 256 B][router_w][router_b][router hi][router lo]
 // [router exponents][E experts][shared]
 struct PackedLayout {
-  int64_t off_status, off_rw, off_rb, off_rwh, off_rwl, off_rew, off_ex, off_sh, total;
+  int64_t off_status, off_rw, off_rb, off_rwh, off_rwl, off_rew, off_hb, off_ex, off_sh, total;
 };
 
 int e16_of(int E) { return (E + 15) / 16 * 16; }
@@ -123,7 +123,8 @@ PackedLayout packed_layout(const moe_layer_desc* D, const moe_expert_layout& ex,
   P.off_rwh = P.off_rb + moe_align256((int64_t)D->n_experts * 4);
   P.off_rwl = P.off_rwh + moe_align256(E16 * D->d_model * 2);
   P.off_rew = P.off_rwl + moe_align256(E16 * D->d_model * 2);
-  P.off_ex = P.off_rew + moe_align256(E16 * 4);
+  P.off_hb = P.off_rew + moe_align256(E16 * 4);
+  P.off_ex = P.off_hb + moe_align256((int64_t)(D->n_experts + 1) * 4);
   P.off_sh = P.off_ex + (int64_t)D->n_experts * ex.bytes;
   P.total = P.off_sh + (D->d_ff_shared > 0 ? sh.bytes : 0);
   return P;
@@ -181,7 +182,7 @@ WsLayout ws_layout_decode(const moe_layer* L, int T) {
 // expert (padded to 16).
 struct PfLayout {
   int64_t ctrl, ex, xh, xl, logits, idx, w, tile_bm, tile_cnt, counts, offsets, n_items, item_group, item_row0,
-      item_rows, row_src, row_tok, row_w, slot_pos, hfrag, eh, ypart, total;
+      item_rows, row_src, row_tok, row_w, slot_pos, hfrag, ypart, total;
   int n_tiles, R, max_items, nbH, n_nt;
 };
 
@@ -224,7 +225,6 @@ PfLayout ws_layout_prefill(const moe_layer* L, int T) {
   W.row_w = take((int64_t)W.R * 4);
   W.slot_pos = take(pairs * 4);
   W.hfrag = take((int64_t)W.R * Imax * 2);
-  W.eh = take((int64_t)W.n_nt * W.R * 4);
   W.ypart = take((int64_t)W.R * d * 4);
   W.total = o;
   return W;
@@ -480,7 +480,7 @@ int prefill_layer(const moe_layer* L, const float* x, int norm, float eps, int T
   ma.n_nt = W.n_nt;
   ma.R = W.R;
   ma.hfrag = reinterpret_cast<_Float16*>(ws + W.hfrag);
-  ma.eh = reinterpret_cast<int32_t*>(ws + W.eh);
+  ma.hb = L->hbound;
   ma.ypart = reinterpret_cast<float*>(ws + W.ypart);
   timed_begin(3, s, &slot);
   HIPCHK(launch_pf_gate_up(ma, L->bits, W.max_items, s));
@@ -570,6 +570,7 @@ int moe_pack_experts(const moe_layer_desc* desc, const void* experts_canon, cons
   L->router_wh = reinterpret_cast<const _Float16*>(base + P.off_rwh);
   L->router_wl = reinterpret_cast<const _Float16*>(base + P.off_rwl);
   L->router_ew = reinterpret_cast<const int32_t*>(base + P.off_rew);
+  L->hbound = reinterpret_cast<const int32_t*>(base + P.off_hb);
   L->E16 = e16_of(L->E);
   L->experts = base + P.off_ex;
   L->shared = L->Is > 0 ? base + P.off_sh : nullptr;
@@ -590,6 +591,18 @@ int moe_pack_experts(const moe_layer_desc* desc, const void* experts_canon, cons
                               const_cast<_Float16*>(L->router_wl), const_cast<int32_t*>(L->router_ew), s)) != hipSuccess)
     return bail(fail(MOE_ERR_HIP, "router split: %s", hipGetErrorString(e)));
   const int64_t bb = canon_block_bytes(L->bits);
+  {
+    int32_t* hb = const_cast<int32_t*>(L->hbound);
+    const int64_t stride = 3 * (int64_t)L->I * (L->d / 32) * bb;
+    if ((e = launch_pack_hbound(reinterpret_cast<const uint8_t*>(experts_canon), stride, L->E, L->I, L->d, L->bits, hb, s)) != hipSuccess)
+      return bail(fail(MOE_ERR_HIP, "bound: %s", hipGetErrorString(e)));
+    if (L->Is > 0) {
+      if ((e = launch_pack_hbound(reinterpret_cast<const uint8_t*>(shared_canon), 0, 1, L->Is, L->d, L->bits, hb + L->E, s)) != hipSuccess)
+        return bail(fail(MOE_ERR_HIP, "bound: %s", hipGetErrorString(e)));
+    } else if ((e = launch_fill_u32(reinterpret_cast<uint32_t*>(hb + L->E), 1, 0u, s)) != hipSuccess) {
+      return bail(fail(MOE_ERR_HIP, "bound fill: %s", hipGetErrorString(e)));
+    }
+  }
   auto pack_expert = [&](const uint8_t* canon, int I, const moe_expert_layout& X, uint8_t* dst, int n) -> hipError_t {
     const int64_t gate_b = (int64_t)I * (L->d / 32) * bb;
     const int64_t canon_stride = 3 * gate_b;

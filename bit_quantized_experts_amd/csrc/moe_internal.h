@@ -56,6 +56,7 @@ struct moe_layer {
   const _Float16* router_wh;  // device: router rows times 2^-ew, fp16 hi part, MFMA B fragments
   const _Float16* router_wl;  // same, lo part
   const int32_t* router_ew;   // device [E16] row exponents
+  const int32_t* hbound;      // device [E + 1] exponent base of the intermediate rows (E: shared)
   int32_t E16;                // E rounded up to a multiple of 16
   const uint8_t* experts; // device, E * ex.bytes
   const uint8_t* shared;  // device, sh.bytes or null

@@ -166,9 +166,9 @@ struct PfGemmArgs {
   const int32_t* item_group;
   const int32_t* item_row0;
   const int32_t* item_rows;
+  const int32_t* hb;  // [E + 1] per-expert exponent base of the intermediate rows (index E: shared)
   int32_t T, d, E, I, Is, nbH, n_nt, R;
-  _Float16* hfrag;   // [R/16][nbH][64][8] intermediate rows, fp16(h * 2^-eh)
-  int32_t* eh;       // [n_h_tiles][R] exponents per 128-column tile
+  _Float16* hfrag;   // [R/16][nbH][64][8] intermediate rows, fp16(h * 2^-(hb + 2 ex))
   float* ypart;      // [R][d] down outputs times the gate weight
 };
 
@@ -181,6 +181,8 @@ struct PfCombineArgs {
 };
 
 hipError_t launch_pack_router(const float* W, int E, int d, _Float16* wh, _Float16* wl, int32_t* ew, hipStream_t s);
+hipError_t launch_pack_hbound(const uint8_t* canon, int64_t canon_stride, int n_experts, int I, int d, int bits,
+                              int32_t* hb, hipStream_t s);
 hipError_t launch_pf_prep(const PfPrepArgs& a, hipStream_t s);
 hipError_t launch_pf_router(const PfRouterArgs& a, hipStream_t s);
 hipError_t launch_pf_group(const PfGroupArgs& a, hipStream_t s);

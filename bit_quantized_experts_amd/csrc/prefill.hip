@@ -145,6 +145,55 @@ __global__ __launch_bounds__(256) void pack_router_kernel(const float* W, int E,
 }
 
 // ---------------------------------------------------------------------------
+// Exponent base of the intermediate rows of one expert, prepared at pack
+// time: Lg = max over gate rows of sum_j |w_ij|, Lu likewise for up.  For an
+// input row scaled to |x_j| < 2^15 (x times 2^-ex), |g| <= Lg 2^(15 + ex),
+// |u| <= Lu 2^(15 + ex) and |silu(g) u| <= |g| |u|, so with 2^e > Lg Lu the
+// value h 2^-(hb + 2 ex) with hb = e + 16 is below 2^14 (2^15 allowing for
+// the fp32 rounding of the sums): the fp16 intermediate needs no pass over
+// the row to choose its exponent.  One workgroup per expert.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pack_hbound_kernel(const uint8_t* canon, int64_t stride, int I, int d, int bits,
+                                                          int32_t* hb) {
+  __shared__ float red[2][4];
+  const uint8_t* ex = canon + (int64_t)blockIdx.x * stride;
+  const int nb = d / 32, bb = 2 + 4 * bits, off = 1 << (bits - 1);
+  float lmax[2] = {0.f, 0.f};
+  for (int m = 0; m < 2; ++m) {
+    const uint8_t* mat = ex + (int64_t)m * I * nb * bb;
+    for (int i = threadIdx.x; i < I; i += 256) {
+      float sum = 0.f;
+      for (int b = 0; b < nb; ++b) {
+        const uint8_t* B = mat + ((int64_t)i * nb + b) * bb;
+        const float sc = fabsf(half_bits_to_float((uint32_t)B[0] | ((uint32_t)B[1] << 8)));
+        int cs = 0;
+        for (int j = 0; j < 32; ++j) {
+          const int bit = bits * j, by = bit >> 3;
+          const uint32_t v = (uint32_t)B[2 + by] | (by + 1 < 4 * bits ? (uint32_t)B[3 + by] << 8 : 0u);
+          cs += abs((int)((v >> (bit & 7)) & ((1u << bits) - 1u)) - off);
+        }
+        sum += sc * (float)cs;
+      }
+      lmax[m] = fmaxf(lmax[m], sum);
+    }
+  }
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int m = 0; m < 2; ++m) {
+    const float v = wave_maxf(lmax[m]);
+    if (lane == 0) red[m][wv] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float lg = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+    const float lu = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+    const float p = lg * lu;
+    int e = 0;
+    if (p > 0.f) frexpf(p, &e);  // p < 2^e
+    hb[blockIdx.x] = e + 16;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // prep: one wave per token row.  With norm set the row is first divided by
 // sqrt(mean(x^2) + eps) (the RMSNorm between stacked layers).
 // ---------------------------------------------------------------------------
@@ -495,8 +544,7 @@ DEVI void interleave() {
 }
 
 template <int BITS, int NRG>
-DEVI void gate_up_item(const PfGemmArgs& a, const Stages& S, float* amax_lds, int* ex_lds, int g, int row0,
-                       int rows, int nt) {
+DEVI void gate_up_item(const PfGemmArgs& a, const Stages& S, int* ex_lds, int g, int row0, int rows, int nt) {
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, n = lane & 15, q = lane >> 4;
   const bool shared = g == a.E;
   const int Ig = shared ? a.Is : a.I;
@@ -515,10 +563,23 @@ DEVI void gate_up_item(const PfGemmArgs& a, const Stages& S, float* amax_lds, in
     cp[2] = up + (int64_t)(hr / 16) * nkg * CB;
     cp[3] = cp[2] + (int64_t)nkg * CB;
   }
-  int tokr[NRG];
+  // A staging: a stage holds the step's 128 inputs of every row, 256 B per
+  // row, its sixteen 16-byte slots swizzled (slot s of row r holds input
+  // slot s ^ (r & 15)) so that the MFMA reads below hit distinct banks.
+  // One direct-to-LDS load fills 4 whole rows (two full cache lines each);
+  // wave wv issues loads wv, wv + 4, ... (rows 4 (wv + 4 i) + lane / 16).
+  const int lrow = lane >> 4;
+  const int gslot = (lane & 15) ^ (((4 * wv + lrow) & 15));  // same for every i: 16 i leaves r & 15 unchanged
+  const _Float16* arow[NRG];
 #pragma unroll
-  for (int rg = 0; rg < NRG; ++rg) tokr[rg] = (16 * rg < rows) ? a.row_tok[row0 + 16 * rg + n] : 0;
-  const int my_tok = tid < rows ? a.row_tok[row0 + tid] : 0;
+  for (int i = 0; i < NRG; ++i) {
+    const int r = 4 * (wv + 4 * i) + lrow;
+    arow[i] = a.xh + (size_t)(r < rows ? a.row_tok[row0 + r] : 0) * a.d + 8 * gslot;
+  }
+  if (tid < PF_TM) ex_lds[tid] = a.ex[tid < rows ? a.row_tok[row0 + tid] : 0];
+  int xs[4];  // swizzled byte offset of the lane's A slot for each block of a step
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) xs[kb] = n * 256 + (((4 * kb + q) ^ n) << 4);
 
   float4_t acc[NRG][4];
 #pragma unroll
@@ -526,9 +587,7 @@ DEVI void gate_up_item(const PfGemmArgs& a, const Stages& S, float* amax_lds, in
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[rg][m] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  // every wave issues the same number of loads per step: one direct-to-LDS
-  // load per row group (rows past the item read token 0) and the weight
-  // registers of its 4 row tiles
+  // every wave issues the same number of loads per step
   constexpr int LOADS = NRG + (BITS == 3 ? 12 : 8);
   WRegs bw[3][4];
   const int nsteps = a.d / 128;
@@ -536,9 +595,8 @@ DEVI void gate_up_item(const PfGemmArgs& a, const Stages& S, float* amax_lds, in
     constexpr int P = decltype(P_)::value;
     unsigned char* st = S.get<P>();
 #pragma unroll
-    for (int rg = 0; rg < NRG; ++rg)
-      __builtin_amdgcn_global_load_lds(a.xh + (size_t)tokr[rg] * a.d + (4 * s + wv) * 32 + 8 * q,
-                                       (lds_ptr_t)(st + (rg * 4 + wv) * 1024), 16, 0, 0);
+    for (int i = 0; i < NRG; ++i)
+      __builtin_amdgcn_global_load_lds(arow[i] + 128 * s, (lds_ptr_t)(st + (wv + 4 * i) * 1024), 16, 0, 0);
 #pragma unroll
     for (int m = 0; m < 4; ++m) load_half<BITS>(bw[P][m], cp[m] + (int64_t)(s >> 1) * CB, s & 1, lane);
   };
@@ -555,7 +613,7 @@ DEVI void gate_up_item(const PfGemmArgs& a, const Stages& S, float* amax_lds, in
       // matrix cores work on block kb
       half8_t A[NRG], B[4];
 #pragma unroll
-      for (int rg = 0; rg < NRG; ++rg) A[rg] = *reinterpret_cast<const half8_t*>(st + (rg * 4) * 1024 + 16 * lane);
+      for (int rg = 0; rg < NRG; ++rg) A[rg] = *reinterpret_cast<const half8_t*>(st + rg * 4096 + xs[0]);
 #pragma unroll
       for (int m = 0; m < 4; ++m) B[m] = dequant<BITS>(bw[P][m], 0);
 #pragma unroll
@@ -563,8 +621,7 @@ DEVI void gate_up_item(const PfGemmArgs& a, const Stages& S, float* amax_lds, in
         half8_t An[NRG], Bn[4];
         if (kb < 3) {
 #pragma unroll
-          for (int rg = 0; rg < NRG; ++rg)
-            An[rg] = *reinterpret_cast<const half8_t*>(st + (rg * 4 + kb + 1) * 1024 + 16 * lane);
+          for (int rg = 0; rg < NRG; ++rg) An[rg] = *reinterpret_cast<const half8_t*>(st + rg * 4096 + xs[kb + 1]);
 #pragma unroll
           for (int m = 0; m < 4; ++m) Bn[m] = dequant<BITS>(bw[P][m], kb + 1);
         }
@@ -584,55 +641,35 @@ DEVI void gate_up_item(const PfGemmArgs& a, const Stages& S, float* amax_lds, in
   };
   issue(ic<0>{}, 0);
   if (nsteps > 1) issue(ic<1>{}, 1);
-  if (tid < PF_TM) ex_lds[tid] = a.ex[my_tok];  // visible after the first step's barrier
   for (int s = 0; s < nsteps; s += 3) {
     step(ic<0>{}, s);
     if (s + 1 < nsteps) step(ic<1>{}, s + 1);
     if (s + 2 < nsteps) step(ic<2>{}, s + 2);
   }
 
-  // epilogue: h = silu(g) u with g, u scaled back by 2^ex of the row's token
-  float hv[NRG][2][4];
-#pragma unroll
-  for (int rg = 0; rg < NRG; ++rg)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * rg + 4 * q + i;
-      const int ex = ex_lds[r];
-      float m = 0.f;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const float gg = ldexpf(acc[rg][j][i], ex);
-        const float uu = ldexpf(acc[rg][2 + j][i], ex);
-        const float h = gg * __builtin_amdgcn_rcpf(1.0f + __expf(-gg)) * uu;
-        hv[rg][j][i] = h;
-        m = fmaxf(m, fabsf(h));
-      }
-      m = row16_max(m);
-      if (n == 0) amax_lds[wv * PF_TM + r] = act ? m : 0.f;
-    }
-  __syncthreads();
-  if (tid < rows) {
-    const float m = fmaxf(fmaxf(amax_lds[tid], amax_lds[PF_TM + tid]), fmaxf(amax_lds[2 * PF_TM + tid], amax_lds[3 * PF_TM + tid]));
-    a.eh[(size_t)nt * a.R + row0 + tid] = fp16_exponent_for(m);
-  }
-  // h tile in MFMA A-fragment order [row group][4 blocks] (stage 0 is free:
-  // every load has landed and every wave is past its last read)
-  uint32_t* tile = reinterpret_cast<uint32_t*>(S.s0);
+  // epilogue: g, u scaled back by 2^ex of the row's token, h = silu(g) u,
+  // stored as fp16(h * 2^-eh) with eh = hb + 2 ex fixed per (expert, row):
+  // hb bounds |g| |u| for any input row scaled below 2^15, so h * 2^-eh
+  // stays below 2^14 without a pass over the row
+  const int hb = a.hb[g];
+  __syncthreads();  // every wave is past its last read of stage 0
+  uint32_t* tile = reinterpret_cast<uint32_t*>(S.s0);  // fragments [row group][4 blocks]
   if (act)
 #pragma unroll
     for (int rg = 0; rg < NRG; ++rg)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rg + 4 * q + i;
-        const float m = fmaxf(fmaxf(amax_lds[r], amax_lds[PF_TM + r]), fmaxf(amax_lds[2 * PF_TM + r], amax_lds[3 * PF_TM + r]));
-        const int e = fp16_exponent_for(m);
+        const int ex = ex_lds[r];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          // columns c = 16 j + n and c + 1 (lanes n, n + 1) share one dword
-          const _Float16 v = (_Float16)ldexpf(hv[rg][j][i], -e);
+          const float gg = ldexpf(acc[rg][j][i], ex);
+          const float uu = ldexpf(acc[rg][2 + j][i], ex);
+          const float h = gg * __builtin_amdgcn_rcpf(1.0f + __expf(-gg)) * uu;
+          const _Float16 v = (_Float16)ldexpf(h, -(hb + 2 * ex));
           uint16_t vb;
           __builtin_memcpy(&vb, &v, 2);
+          // columns c = 16 j + n and c + 1 (lanes n, n + 1) share one dword
           const uint32_t nb = (uint32_t)__builtin_amdgcn_mov_dpp((int)vb, 0xB1, 0xF, 0xF, true);  // lane n ^ 1
           if ((n & 1) == 0) {
             const int c = 16 * j + n;
@@ -655,7 +692,6 @@ __global__ __launch_bounds__(256) void pf_gate_up_kernel(PfGemmArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char st0[GEMM_STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char st1[GEMM_STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char st2[GEMM_STAGE];
-  __shared__ float amax_lds[4 * PF_TM];
   __shared__ int ex_lds[PF_TM];
   int item, nt;
   if (!xcd_tile(*a.n_items, a.n_nt, &item, &nt)) return;
@@ -664,10 +700,10 @@ __global__ __launch_bounds__(256) void pf_gate_up_kernel(PfGemmArgs a) {
   if (nt * PF_HT >= Ig) return;
   const int nrg = rows >> 4;
   const Stages S{st0, st1, st2};
-  if (nrg > 4) gate_up_item<BITS, 8>(a, S, amax_lds, ex_lds, g, row0, rows, nt);
-  else if (nrg > 2) gate_up_item<BITS, 4>(a, S, amax_lds, ex_lds, g, row0, rows, nt);
-  else if (nrg > 1) gate_up_item<BITS, 2>(a, S, amax_lds, ex_lds, g, row0, rows, nt);
-  else gate_up_item<BITS, 1>(a, S, amax_lds, ex_lds, g, row0, rows, nt);
+  if (nrg > 4) gate_up_item<BITS, 8>(a, S, ex_lds, g, row0, rows, nt);
+  else if (nrg > 2) gate_up_item<BITS, 4>(a, S, ex_lds, g, row0, rows, nt);
+  else if (nrg > 1) gate_up_item<BITS, 2>(a, S, ex_lds, g, row0, rows, nt);
+  else gate_up_item<BITS, 1>(a, S, ex_lds, g, row0, rows, nt);
 }
 
 // ---------------------------------------------------------------------------
@@ -680,22 +716,21 @@ __global__ __launch_bounds__(256) void pf_gate_up_kernel(PfGemmArgs a) {
 //   BK 4: 2 full chunks (row tiles 2c, 2c+1), fragment (t, j) = (c t/2, f 4(t%2)+j)
 //   BK 2: 2 full chunks (blocks 2c, 2c+1),    fragment (t, j) = (c j/2, f 2t+j%2)
 //   BK 1: 4 half chunks (one per block),      fragment (t, j) = (c j, f t)
-// H rows: staged through registers so that each 128-column tile is brought
-// from its own exponent to the row's largest one (an exact power-of-two
-// product, unless it underflows) before it is written to LDS.
+// The intermediate rows are stored in MFMA A-fragment order, so each
+// direct-to-LDS load moves 1 KB of consecutive bytes.
 // ---------------------------------------------------------------------------
 template <int BK>
 struct DownMap {
   static constexpr int NC = (BK == 4 || BK == 2) ? 2 : 4;
-  static constexpr bool HALF = (BK == 8 || BK == 1);
   static DEVI constexpr int chunk(int t, int j) { return BK == 8 ? t : BK == 4 ? t / 2 : BK == 2 ? j / 2 : j; }
   static DEVI constexpr int frag(int t, int j) { return BK == 8 ? j : BK == 4 ? 4 * (t % 2) + j : BK == 2 ? 2 * t + j % 2 : t; }
 };
 
 template <int BITS, int BK, int NRG>
-DEVI void down_item(const PfGemmArgs& a, unsigned char* lds, float* rowf_lds, int g, int row0, int rows, int nt) {
+DEVI void down_item(const PfGemmArgs& a, const Stages& S, float* rowf_lds, int g, int row0, int rows, int nt) {
   using M = DownMap<BK>;
   constexpr int RT = 8 / BK;
+  static_assert(RT * BK == 8, "chunk shape");
   constexpr int CB = BITS == 2 ? 1280 : 1792;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, n = lane & 15, q = lane >> 4;
   const bool shared = g == a.E;
@@ -704,17 +739,10 @@ DEVI void down_item(const PfGemmArgs& a, unsigned char* lds, float* rowf_lds, in
   const uint8_t* dm =
       (shared ? a.X.shared : a.X.experts + (int64_t)g * a.X.ex_stride) + (shared ? a.X.sh_off_down : a.X.off_down);
   const int r0 = nt * PF_DT + 64 * wv;
-
-  // the row's largest intermediate-tile exponent, for the lane's staging rows
-  int eref[NRG];
-#pragma unroll
-  for (int rg = 0; rg < NRG; ++rg) {
-    int e = -1000;
-    if (16 * rg < rows)
-      for (int s = 0; s < nsteps; ++s) e = max(e, a.eh[(size_t)s * a.R + row0 + 16 * rg + n]);
-    eref[rg] = e;
-    if (wv == 0 && q == 0 && 16 * rg < rows)
-      rowf_lds[16 * rg + n] = ldexpf(a.row_w[row0 + 16 * rg + n], e);
+  const int nrg = rows >> 4;
+  if (tid < rows) {
+    const int tok = a.row_tok[row0 + tid];
+    rowf_lds[tid] = ldexpf(a.row_w[row0 + tid], a.hb[g] + 2 * a.ex[tok]);
   }
 
   float4_t acc[NRG][4];
@@ -723,64 +751,91 @@ DEVI void down_item(const PfGemmArgs& a, unsigned char* lds, float* rowf_lds, in
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[rg][t] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  WRegs cur[M::NC], nxt[M::NC];
-  u32x4_t stg[NRG];
-  int stg_e[NRG];
-  auto issue = [&](int s) {
-    const int kb = 4 * s + wv;
+  constexpr int LOADS = NRG + M::NC * (BITS == 3 ? 3 : 2);
+  WRegs bw[3][M::NC];
+  auto issue = [&](auto P_, int s) {
+    constexpr int P = decltype(P_)::value;
+    unsigned char* st = S.get<P>();
+    // wave wv stages block 4 s + wv of every row group (clamped to valid
+    // fragments past the item or the matrix; those are never read)
+    const int kb = min(4 * s + wv, nbK - 1);
 #pragma unroll
-    for (int rg = 0; rg < NRG; ++rg)
-      if (16 * rg < rows && kb < nbK) {
-        stg[rg] = ld128(a.hfrag + (((size_t)((row0 >> 4) + rg) * a.nbH + kb) * 64 + lane) * 8);
-        stg_e[rg] = a.eh[(size_t)s * a.R + row0 + 16 * rg + n];
-      }
+    for (int rg = 0; rg < NRG; ++rg) {
+      const int rgc = rg < nrg ? rg : 0;
+      __builtin_amdgcn_global_load_lds(a.hfrag + (((size_t)((row0 >> 4) + rgc) * a.nbH + kb) * 64 + lane) * 8,
+                                       (lds_ptr_t)(st + (rg * 4 + wv) * 1024), 16, 0, 0);
+    }
 #pragma unroll
     for (int c = 0; c < M::NC; ++c) {
       if constexpr (BK == 8) {
-        load_half<BITS>(nxt[c], dm + ((int64_t)(r0 / 16 + c) * n_kg + (s >> 1)) * CB, s & 1, lane);
+        load_half<BITS>(bw[P][c], dm + ((int64_t)(r0 / 16 + c) * n_kg + (s >> 1)) * CB, s & 1, lane);
       } else if constexpr (BK == 4) {
-        load_full<BITS>(nxt[c], dm + ((int64_t)(r0 / 32 + c) * n_kg + s) * CB, lane);
+        load_full<BITS>(bw[P][c], dm + ((int64_t)(r0 / 32 + c) * n_kg + s) * CB, lane);
       } else if constexpr (BK == 2) {
-        if (2 * s + c < n_kg) load_full<BITS>(nxt[c], dm + ((int64_t)(r0 / 64) * n_kg + 2 * s + c) * CB, lane);
+        load_full<BITS>(bw[P][c], dm + ((int64_t)(r0 / 64) * n_kg + min(2 * s + c, n_kg - 1)) * CB, lane);
       } else {
-        if (4 * s + c < n_kg)
-          load_half<BITS>(nxt[c], dm + ((int64_t)(r0 / 128) * n_kg + 4 * s + c) * CB, (r0 / 64) & 1, lane);
+        load_half<BITS>(bw[P][c], dm + ((int64_t)(r0 / 128) * n_kg + min(4 * s + c, n_kg - 1)) * CB, (r0 / 64) & 1, lane);
       }
     }
   };
-  static_assert(RT * BK == 8, "chunk shape");
-  issue(0);
-  for (int s = 0; s < nsteps; ++s) {
-    __builtin_amdgcn_s_waitcnt(0);
-    {
-      unsigned char* st = lds + (s & 1) * GEMM_STAGE;
-      const int kb = 4 * s + wv;
-#pragma unroll
-      for (int rg = 0; rg < NRG; ++rg)
-        if (16 * rg < rows && kb < nbK) {
-          const _Float16 f = (_Float16)ldexpf(1.f, stg_e[rg] - eref[rg]);
-          const half8_t v = __builtin_bit_cast(half8_t, stg[rg]) * f;
-          *reinterpret_cast<half8_t*>(st + (rg * 4 + wv) * 1024 + 16 * lane) = v;
-        }
-    }
-#pragma unroll
-    for (int c = 0; c < M::NC; ++c) cur[c] = nxt[c];
-    if (s + 1 < nsteps) issue(s + 1);
+  auto step = [&](auto P_, int s) {
+    constexpr int P = decltype(P_)::value;
+    if (s + 1 < nsteps) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
-    const unsigned char* st = lds + (s & 1) * GEMM_STAGE;
+    if (s + 2 < nsteps) issue(ic<(P + 2) % 3>{}, s + 2);
+    const unsigned char* st = S.get<P>();
+    const int nj = min(4, nbK - 4 * s);
+    if (nj == 4) {
+      half8_t A[NRG], B[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (4 * s + j >= nbK) break;
-      half8_t B[4];
+      for (int rg = 0; rg < NRG; ++rg) A[rg] = *reinterpret_cast<const half8_t*>(st + (rg * 4) * 1024 + 16 * lane);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) B[t] = dequant<BITS>(cur[M::chunk(t, j)], M::frag(t, j));
+      for (int t = 0; t < 4; ++t) B[t] = dequant<BITS>(bw[P][M::chunk(t, 0)], M::frag(t, 0));
 #pragma unroll
-      for (int rg = 0; rg < NRG; ++rg) {
-        const half8_t A = *reinterpret_cast<const half8_t*>(st + (rg * 4 + j) * 1024 + 16 * lane);
+      for (int j = 0; j < 4; ++j) {
+        half8_t An[NRG], Bn[4];
+        if (j < 3) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) acc[rg][t] = mfma16x16x32(A, B[t], acc[rg][t]);
+          for (int rg = 0; rg < NRG; ++rg)
+            An[rg] = *reinterpret_cast<const half8_t*>(st + (rg * 4 + j + 1) * 1024 + 16 * lane);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) Bn[t] = dequant<BITS>(bw[P][M::chunk(t, j + 1)], M::frag(t, j + 1));
+        }
+#pragma unroll
+        for (int rg = 0; rg < NRG; ++rg)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc[rg][t] = mfma16x16x32(A[rg], B[t], acc[rg][t]);
+        if (j < 3) {
+          interleave<4 * NRG, NRG, (BITS == 3 ? 80 : 48)>();
+#pragma unroll
+          for (int rg = 0; rg < NRG; ++rg) A[rg] = An[rg];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) B[t] = Bn[t];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (j >= nj) break;
+        half8_t B[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) B[t] = dequant<BITS>(bw[P][M::chunk(t, j)], M::frag(t, j));
+#pragma unroll
+        for (int rg = 0; rg < NRG; ++rg) {
+          const half8_t A = *reinterpret_cast<const half8_t*>(st + (rg * 4 + j) * 1024 + 16 * lane);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc[rg][t] = mfma16x16x32(A, B[t], acc[rg][t]);
+        }
       }
     }
+  };
+  issue(ic<0>{}, 0);
+  if (nsteps > 1) issue(ic<1>{}, 1);
+  for (int s = 0; s < nsteps; s += 3) {
+    step(ic<0>{}, s);
+    if (s + 1 < nsteps) step(ic<1>{}, s + 1);
+    if (s + 2 < nsteps) step(ic<2>{}, s + 2);
   }
 #pragma unroll
   for (int rg = 0; rg < NRG; ++rg)
@@ -797,16 +852,19 @@ DEVI void down_item(const PfGemmArgs& a, unsigned char* lds, float* rowf_lds, in
 
 template <int BITS, int BK>
 __global__ __launch_bounds__(256) void pf_down_kernel(PfGemmArgs a) {
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * GEMM_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st0[GEMM_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st1[GEMM_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st2[GEMM_STAGE];
   __shared__ float rowf_lds[PF_TM];
   int item, nt;
   if (!xcd_tile(*a.n_items, a.d / PF_DT, &item, &nt)) return;
   const int g = a.item_group[item], row0 = a.item_row0[item], rows = a.item_rows[item];
   const int nrg = rows >> 4;
-  if (nrg > 4) down_item<BITS, BK, 8>(a, lds, rowf_lds, g, row0, rows, nt);
-  else if (nrg > 2) down_item<BITS, BK, 4>(a, lds, rowf_lds, g, row0, rows, nt);
-  else if (nrg > 1) down_item<BITS, BK, 2>(a, lds, rowf_lds, g, row0, rows, nt);
-  else down_item<BITS, BK, 1>(a, lds, rowf_lds, g, row0, rows, nt);
+  const Stages S{st0, st1, st2};
+  if (nrg > 4) down_item<BITS, BK, 8>(a, S, rowf_lds, g, row0, rows, nt);
+  else if (nrg > 2) down_item<BITS, BK, 4>(a, S, rowf_lds, g, row0, rows, nt);
+  else if (nrg > 1) down_item<BITS, BK, 2>(a, S, rowf_lds, g, row0, rows, nt);
+  else down_item<BITS, BK, 1>(a, S, rowf_lds, g, row0, rows, nt);
 }
 
 // ---------------------------------------------------------------------------
@@ -834,6 +892,13 @@ __global__ __launch_bounds__(256) void pf_combine_kernel(PfCombineArgs a) {
 hipError_t launch_pack_router(const float* W, int E, int d, _Float16* wh, _Float16* wl, int32_t* ew, hipStream_t s) {
   const int E16 = (E + 15) / 16 * 16;
   hipLaunchKernelGGL(pack_router_kernel, dim3((E16 + 3) / 4), dim3(256), 0, s, W, E, E16, d, wh, wl, ew);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_hbound(const uint8_t* canon, int64_t canon_stride, int n_experts, int I, int d, int bits,
+                              int32_t* hb, hipStream_t s) {
+  if (n_experts <= 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_hbound_kernel, dim3(n_experts), dim3(256), 0, s, canon, canon_stride, I, d, bits, hb);
   return hipGetLastError();
 }
 
