@@ -268,7 +268,7 @@ __global__ __launch_bounds__(256) void pf_router_kernel(PfRouterArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char st1[STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char st2[STAGE];
   const Stages S{st0, st1, st2};
-  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, n = lane & 15, q = lane >> 4;
+  const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, n = lane & 15, q = lane >> 4;
   const int row0 = blockIdx.x * 128;
   const int nb = a.d / 32, n_et = a.E16 / 16;
   const int et0 = blockIdx.y * 8 + 2 * wv;
@@ -543,9 +543,27 @@ DEVI void interleave() {
   }
 }
 
+// Schedule of one four-block step with NRG row groups: the first block's NRG
+// LDS reads and 4 dequantizations, then each block's 4 NRG multiplies, the
+// next block's LDS reads spread one after each of the first NRG multiplies
+// and VPER vector instructions (the next block's dequantization) after each.
+template <int NRG, int VPER>
+DEVI void step_schedule4() {
+  __builtin_amdgcn_sched_group_barrier(0x100, NRG, 0);
+  __builtin_amdgcn_sched_group_barrier(0x002, 48, 0);
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int i = 0; i < 4 * NRG; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (kb < 3 && i < NRG) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (kb < 3) __builtin_amdgcn_sched_group_barrier(0x002, VPER, 0);
+    }
+}
+
 template <int BITS, int NRG>
 DEVI void gate_up_item(const PfGemmArgs& a, const Stages& S, int* ex_lds, int g, int row0, int rows, int nt) {
-  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, n = lane & 15, q = lane >> 4;
+  const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, n = lane & 15, q = lane >> 4;
   const bool shared = g == a.E;
   const int Ig = shared ? a.Is : a.I;
   const uint8_t* eb = shared ? a.X.shared : a.X.experts + (int64_t)g * a.X.ex_stride;
@@ -608,35 +626,21 @@ DEVI void gate_up_item(const PfGemmArgs& a, const Stages& S, int* ex_lds, int g,
     if (s + 2 < nsteps) issue(ic<(P + 2) % 3>{}, s + 2);
     if (act) {
       const unsigned char* st = S.get<P>();
-      // software pipeline over the 4 blocks of the step: the A fragments and
-      // the dequantized weights of block kb + 1 are produced while the
-      // matrix cores work on block kb
-      half8_t A[NRG], B[4];
-#pragma unroll
-      for (int rg = 0; rg < NRG; ++rg) A[rg] = *reinterpret_cast<const half8_t*>(st + rg * 4096 + xs[0]);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) B[m] = dequant<BITS>(bw[P][m], 0);
+      // the 4 blocks of the step: block kb + 1's LDS reads and dequantized
+      // weights are produced in between block kb's multiplies (schedule below)
+      half8_t A[4][NRG], B[4][4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        half8_t An[NRG], Bn[4];
-        if (kb < 3) {
 #pragma unroll
-          for (int rg = 0; rg < NRG; ++rg) An[rg] = *reinterpret_cast<const half8_t*>(st + rg * 4096 + xs[kb + 1]);
+        for (int rg = 0; rg < NRG; ++rg) A[kb][rg] = *reinterpret_cast<const half8_t*>(st + rg * 4096 + xs[kb]);
 #pragma unroll
-          for (int m = 0; m < 4; ++m) Bn[m] = dequant<BITS>(bw[P][m], kb + 1);
-        }
+        for (int m = 0; m < 4; ++m) B[kb][m] = dequant<BITS>(bw[P][m], kb);
 #pragma unroll
         for (int rg = 0; rg < NRG; ++rg)
 #pragma unroll
-          for (int m = 0; m < 4; ++m) acc[rg][m] = mfma16x16x32(A[rg], B[m], acc[rg][m]);
-        if (kb < 3) {
-          interleave<4 * NRG, NRG, (BITS == 3 ? 80 : 48)>();
-#pragma unroll
-          for (int rg = 0; rg < NRG; ++rg) A[rg] = An[rg];
-#pragma unroll
-          for (int m = 0; m < 4; ++m) B[m] = Bn[m];
-        }
+          for (int m = 0; m < 4; ++m) acc[rg][m] = mfma16x16x32(A[kb][rg], B[kb][m], acc[rg][m]);
       }
+      step_schedule4<NRG, (BITS == 3 ? 20 : 12) * 4 / (4 * NRG) + 1>();
     }
   };
   issue(ic<0>{}, 0);
@@ -732,7 +736,7 @@ DEVI void down_item(const PfGemmArgs& a, const Stages& S, float* rowf_lds, int g
   constexpr int RT = 8 / BK;
   static_assert(RT * BK == 8, "chunk shape");
   constexpr int CB = BITS == 2 ? 1280 : 1792;
-  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, n = lane & 15, q = lane >> 4;
+  const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, n = lane & 15, q = lane >> 4;
   const bool shared = g == a.E;
   const int Ig = shared ? a.Is : a.I;
   const int nbK = Ig / 32, n_kg = nbK / BK, nsteps = (nbK + 3) / 4;
@@ -787,33 +791,19 @@ DEVI void down_item(const PfGemmArgs& a, const Stages& S, float* rowf_lds, int g
     const unsigned char* st = S.get<P>();
     const int nj = min(4, nbK - 4 * s);
     if (nj == 4) {
-      half8_t A[NRG], B[4];
-#pragma unroll
-      for (int rg = 0; rg < NRG; ++rg) A[rg] = *reinterpret_cast<const half8_t*>(st + (rg * 4) * 1024 + 16 * lane);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) B[t] = dequant<BITS>(bw[P][M::chunk(t, 0)], M::frag(t, 0));
+      half8_t A[4][NRG], B[4][4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        half8_t An[NRG], Bn[4];
-        if (j < 3) {
 #pragma unroll
-          for (int rg = 0; rg < NRG; ++rg)
-            An[rg] = *reinterpret_cast<const half8_t*>(st + (rg * 4 + j + 1) * 1024 + 16 * lane);
+        for (int rg = 0; rg < NRG; ++rg) A[j][rg] = *reinterpret_cast<const half8_t*>(st + (rg * 4 + j) * 1024 + 16 * lane);
 #pragma unroll
-          for (int t = 0; t < 4; ++t) Bn[t] = dequant<BITS>(bw[P][M::chunk(t, j + 1)], M::frag(t, j + 1));
-        }
+        for (int t = 0; t < 4; ++t) B[j][t] = dequant<BITS>(bw[P][M::chunk(t, j)], M::frag(t, j));
 #pragma unroll
         for (int rg = 0; rg < NRG; ++rg)
 #pragma unroll
-          for (int t = 0; t < 4; ++t) acc[rg][t] = mfma16x16x32(A[rg], B[t], acc[rg][t]);
-        if (j < 3) {
-          interleave<4 * NRG, NRG, (BITS == 3 ? 80 : 48)>();
-#pragma unroll
-          for (int rg = 0; rg < NRG; ++rg) A[rg] = An[rg];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) B[t] = Bn[t];
-        }
+          for (int t = 0; t < 4; ++t) acc[rg][t] = mfma16x16x32(A[j][rg], B[j][t], acc[rg][t]);
       }
+      step_schedule4<NRG, (BITS == 3 ? 20 : 12) * 4 / (4 * NRG) + 1>();
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
