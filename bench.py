@@ -213,18 +213,134 @@ def bench_prefill(args):
     print(json.dumps(out))
 
 
+def bench_layer_t1(args):
+    """One full-size layer, decode T = 1, over a ring of 16 input rows (the
+    routing changes from row to row).  Before each timed forward a 512 MB
+    buffer is written, so the layer's weights are not served from the 256 MB
+    Infinity Cache; each forward is bracketed by events on the stream."""
+    import torch
+
+    import bit_quantized_experts_amd as bqe
+    import moe_inputs as mi
+    from moe_inputs.device import activations_device, packed_layer
+
+    wl = mi.WORKLOADS["layer_t1"]
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    L = packed_layer(wl, 0, dev)
+    ring = 16
+    xs = [activations_device(mi.activations(wl, T=1, stream=500 + i), dev) for i in range(ring)]
+    y = torch.empty((1, wl.d), dtype=torch.float32, device=dev)
+    ws = bqe.new_workspace(L.workspace_bytes(1), dev)
+    idx = torch.empty((1, wl.k), dtype=torch.int32, device=dev)
+    w = torch.empty((1, wl.k), dtype=torch.float32, device=dev)
+    rio = bqe.RouteIO(None, None, None, idx.data_ptr(), w.data_ptr())
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    for i in range(ring):
+        bqe.moe_layer_forward(L.handle, xs[i], y, ws, rio)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(ring)]
+    times = []
+    n_rep = max(1, args.steps // ring)
+    for rep in range(args.warmup // ring + n_rep):
+        for i in range(ring):
+            flush.fill_(float(i))
+            ev[i][0].record()
+            bqe.moe_layer_forward(L.handle, xs[i], y, ws, rio)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        if rep >= args.warmup // ring:
+            times += [a.elapsed_time(b) * 1e-3 for a, b in ev]
+    sec = float(np.mean(times))
+    # algorithmic bytes: router + bias, the 10 routed experts and the shared
+    # expert, x and y
+    nbytes = wl.E * wl.d * 4 + wl.E * 4 + wl.k * wl.expert_bytes() + wl.expert_bytes(wl.Is) + 2 * wl.d * 4
+    kdur = {}
+    for cls, name in ((bqe.TIMING_GATE_UP, "gate_up"), (bqe.TIMING_DOWN, "down"), (bqe.TIMING_ROUTER, "router")):
+        tot, n = 0.0, 0
+        for i in range(ring):
+            flush.fill_(float(i))
+            bqe.moe_timing_start(cls, 1)
+            bqe.moe_layer_forward(L.handle, xs[i], y, ws, rio)
+            ms, cnt = bqe.moe_timing_stop()
+            tot += ms
+            n += cnt
+        kdur[name] = (tot / n) * 1e-3
+    gu_bytes = (wl.k + 1) * 2 * wl.I * (wl.d // 32) * wl.block_bytes()
+    dn_bytes = (wl.k + 1) * wl.d * (wl.I // 32) * wl.block_bytes()
+    per = {"gate_up": gu_bytes, "down": dn_bytes, "router": wl.E * wl.d * 4 + wl.E * 4}
+    kernels = {n: {"avg_us": kdur[n] * 1e6, "bytes_per_launch": per[n], "GBps": per[n] / kdur[n] / 1e9} for n in kdur}
+    dom = max(kdur, key=lambda n: kdur[n])
+    achieved = per[dom] / kdur[dom] / 1e9
+    cpu = None
+    if args.cpu_layers > 0:
+        tps, per_layer = cpu_baseline_stack(wl, 1, mi.activations(wl, T=1, stream=500), 1)
+        cpu = {"value": tps, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"the layer on the first row of the ring ({per_layer:.2f} s), single thread; "
+                         f"expert generation untimed"}
+    out = {
+        "metric": "MoE layer forwards/s (decode T=1, one full-size layer)",
+        "value": 1.0 / sec,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": len(times),
+        "warmup": args.warmup,
+        "ms_per_step": sec * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16 MFMA operands (codes exact, activations as fp16 hi+lo), fp32 accumulate",
+        "data": "synthetic (counter-hash codes/scales, N(0,1) activations, N(0,0.02) router + Zipf(1.1) log bias)",
+        "config": {"workload": wl.name, "layers": 1, "T": 1, "d": wl.d, "experts": wl.E, "d_ff": wl.I,
+                   "shared_d_ff": wl.Is, "top_k": wl.k, "bits": wl.bits, "ring": ring,
+                   "infinity_cache": "flushed before each forward", "parallelism": "none (1 GPU)"},
+        "hbm_GBps": nbytes / sec / 1e9,
+        "bytes_per_step": nbytes,
+        "p10_p90_us": [float(np.percentile(times, 10) * 1e6), float(np.percentile(times, 90) * 1e6)],
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+def copy_calibration(n_mib: int, reps: int):
+    """A plain device-to-device copy of n_mib MiB, reps times: the reference
+    for scaling the FETCH_SIZE / WRITE_SIZE counters to bytes (the copy reads
+    and writes exactly n_mib MiB per launch)."""
+    import torch
+
+    torch.cuda.set_device(0)
+    n = n_mib * 1024 * 1024 // 4
+    src = torch.arange(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    assert bool((dst[-4:] == src[-4:]).all())
+    print(json.dumps({"copy_calibration": {"bytes_read": n * 4, "bytes_written": n * 4, "launches": reps}}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="stack_t8_2bit", choices=["stack_t8_2bit", "stack_3bit", "prefill"])
+    ap.add_argument("--workload", default="stack_t8_2bit", choices=["stack_t8_2bit", "stack_3bit", "prefill", "layer_t1"])
     ap.add_argument("--T", type=int, default=None, help="tokens per pass (default: the workload's)")
     ap.add_argument("--layers", type=int, default=None, help="override the number of layers (testing only)")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=3, help="oracle sample size in layers (0 = skip)")
     ap.add_argument("--cpu-tokens", type=int, default=16, help="prefill: oracle sample size in tokens (0 = skip)")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
+
+    if args.copy_calib:
+        copy_calibration(args.copy_calib, 5)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no multi-GPU path. "
@@ -233,6 +349,9 @@ def main():
 
     if args.workload == "prefill":
         bench_prefill(args)
+        return
+    if args.workload == "layer_t1":
+        bench_layer_t1(args)
         return
 
     import torch

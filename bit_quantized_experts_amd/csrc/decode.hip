@@ -16,9 +16,9 @@
 // n with one fused multiply-add per output.  Every product and the offset are
 // exact; the rounding is the fp32 accumulation.
 //
-// Memory: every wave issues the loads of all the weight chunks it will use
-// before its first multiply, so each wave keeps several 128-bit loads per
-// lane in flight from HBM; activation fragments come from L2.
+// Memory: weight chunks stream from HBM into registers, several k-groups
+// ahead of the multiplies; the gate/up activation fragments are read from
+// LDS (one copy per workgroup), the down kernel's h fragments from L2.
 #include "kern_common.h"
 #include "moe_launch.h"
 
@@ -49,11 +49,13 @@ DEVI float chunk_scale(const u32x4_t& s, int f) {
   return half_bits_to_float((f & 1) ? (dw >> 16) : (dw & 0xffffu));
 }
 
-// A-fragment and accumulator seed of block b; rows of tokens that do not
-// exist (or are not routed here) are zero and are not loaded.
+// A-fragment and accumulator seed of block b of the h fragments: the seed is
+// the sum of the two 16-row tile sums the gate/up kernel wrote for the block.
 DEVI void load_a(const _Float16* frag, const float* sum, size_t b, int lane, half8_t& A, float4_t& cin) {
   A = *reinterpret_cast<const half8_t*>(frag + (b * 64 + lane) * 8);
-  cin = *reinterpret_cast<const float4_t*>(sum + b * 16 + 4 * (lane >> 4));
+  const float4_t c0 = *reinterpret_cast<const float4_t*>(sum + (2 * b) * 16 + 4 * (lane >> 4));
+  const float4_t c1 = *reinterpret_cast<const float4_t*>(sum + (2 * b + 1) * 16 + 4 * (lane >> 4));
+  cin = c0 + c1;
 }
 
 // ---------------------------------------------------------------------------
@@ -114,186 +116,225 @@ DEVI void build_slots(SlotLds& S, int r_e, float r_w, int tk, int k, int T, int 
 }
 
 // ---------------------------------------------------------------------------
-// gate/up: a work item is (slot u, group q of 64 intermediate rows = four
-// 16-row tiles; the last group of an expert may have two).  The grid is
-// persistent: workgroups stride over the items, the shared expert's first
-// (they need no routing, so they start streaming at once), then the routed
-// slots'.  Wave w of a workgroup takes k-group w (256 inputs): it issues the
-// loads of its eight weight chunks (gate/up x four row tiles) into registers
-// and copies its eight activation fragments and block sums straight into a
-// wave-private LDS area (global_load_lds), then runs the 64 MFMAs, scaling
-// each block's result as soon as it is ready.  Waves reduce through the same
-// LDS area in a fixed order.  Epilogue (row tiles spread over the waves): divide by the
-// token's rms (stacked layers), h = silu(g) * u, times the token's gate
-// weight, written as fp16 hi/lo A-fragments (with block sums) for the down
-// kernel.
+// gate/up: a work item is (slot u, tile t of 16 intermediate rows); slot 0
+// is the shared expert when there is one, and its tiles come first.  One
+// workgroup of 16 wavefronts per CU (the grid is the CU count): it copies the
+// activation fragments and block sums of the input into LDS once (one copy
+// serves all of its items), builds the slot list from the routing rows, and
+// then takes its items in rounds.  In a round, each item has KP wavefronts
+// that take every KP-th k-group (256 inputs) of it, KP in {1, 2, 4, 8} being
+// the largest that still gives every wavefront of the grid work.  A wavefront
+// keeps the gate and up chunks of two k-groups in flight ahead of the one it
+// multiplies.  The KP partial sums are added in k-part order through LDS; the
+// epilogue divides by the token's rms (stacked layers), forms h = silu(g) * u
+// times the token's gate weight and writes it as fp16 hi/lo A-fragments of
+// the down projection, with the sums of each 16-row tile.
+// Inputs wider than GU_WIN blocks are staged in windows, one after another.
 // ---------------------------------------------------------------------------
-constexpr int GU_MAXW = 10;                       // waves per workgroup
-constexpr int GU_STAGE = 8 * 1024 + 8 * 64;       // bytes staged per wave
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
+constexpr int GU_NW = 8;    // wavefronts per workgroup
+constexpr int GU_WIN = 96;  // activation blocks staged in LDS at once
+
+struct GuLds {
+  unsigned char xs[GU_WIN * 1024];  // A-fragments, [block][lane][8] fp16
+  float cs[GU_WIN * 16];            // accumulator seeds, [block][16]
+  float red[GU_NW][8][64];          // partial sums of the k-parts
+  SlotLds S;
+};
 
 template <int BITS>
-__global__ __launch_bounds__(640, 3) void gu_decode_kernel(GuArgs a) {
-  constexpr int CB = BITS == 2 ? 1280 : 1792;
-  __shared__ __attribute__((aligned(16))) unsigned char stage[GU_MAXW][GU_STAGE];
-  __shared__ float bsum_lds[4][16];
-  __shared__ SlotLds S;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, nw = blockDim.x >> 6;
+struct GroupRegs {
+  ChunkRegs<BITS> g, u;
+};
+
+// Activation blocks [b0, b0 + nblk) into LDS (plain loads and LDS stores).
+DEVI void stage_window(GuLds& L, const GuArgs& a, int b0, int nblk, int tid) {
+  constexpr int PER = GU_WIN * 64 / (64 * GU_NW);
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.xfrag + (size_t)b0 * 512);
+  u32x4_t* dst = reinterpret_cast<u32x4_t*>(L.xs);
+  const int n = nblk * 64, nc = nblk * 4;
+  u32x4_t v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int p = tid + 64 * GU_NW * i;
+    if (p < n) v[i] = src[p];
+  }
+  float4_t c{};
+  if (tid < nc) c = reinterpret_cast<const float4_t*>(a.xsum + (size_t)b0 * 16)[tid];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int p = tid + 64 * GU_NW * i;
+    if (p < n) dst[p] = v[i];
+  }
+  if (tid < nc) reinterpret_cast<float4_t*>(L.cs)[tid] = c;
+}
+
+template <int BITS>
+DEVI void issue_group(GroupRegs<BITS>& r, const uint8_t* gate, const uint8_t* up, int64_t off, int lane) {
+  load_chunk<BITS>(r.g, gate + off, lane);
+  load_chunk<BITS>(r.u, up + off, lane);
+}
+
+// Eight blocks (one k-group) of gate and up; lb = first block in the window.
+template <int BITS>
+DEVI void mul_group(const GroupRegs<BITS>& r, const GuLds& L, int lb, int lane, float4_t& accg, float4_t& accu) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const half8_t A = *reinterpret_cast<const half8_t*>(L.xs + (size_t)(lb + j) * 1024 + 16 * lane);
+    const float4_t cin = *reinterpret_cast<const float4_t*>(L.cs + (lb + j) * 16 + 4 * (lane >> 4));
+    const float4_t Cg = mfma16x16x32(A, chunk_frag<BITS>(r.g, j), cin);
+    const float4_t Cu = mfma16x16x32(A, chunk_frag<BITS>(r.u, j), cin);
+    accg += chunk_scale(r.g.scales, j) * Cg;
+    accu += chunk_scale(r.u.scales, j) * Cu;
+  }
+}
+
+// k-groups kg0, kg0 + step, ... below kg1 of one 16-row tile (chunk row
+// offset rowoff); the window starts at k-group wkg0.  A three-slot register
+// ring: each step of the main loop issues the k-group two steps ahead (the
+// last k-group again once past the end) and multiplies the oldest one; the
+// main loop has no early exit, so the loads in flight at every multiply are
+// the same and the compiler's wait counts stay exact; a tail of up to two
+// steps multiplies what is already in flight.
+template <int BITS>
+DEVI void run_tile(const uint8_t* gate, const uint8_t* up, int64_t rowoff, int kg0, int kg1, int step, int wkg0,
+                   const GuLds& L, int lane, float4_t& accg, float4_t& accu) {
+  constexpr int64_t CB = BITS == 2 ? 1280 : 1792;
+  if (kg0 >= kg1) return;
+  const int nsteps = (kg1 - 1 - kg0) / step + 1;
+  const int last = kg0 + (nsteps - 1) * step;
+  GroupRegs<BITS> r0, r1, r2;
+  int kg = kg0;
+  issue_group<BITS>(r0, gate, up, rowoff + kg * CB, lane);
+  issue_group<BITS>(r1, gate, up, rowoff + min(kg + step, last) * CB, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int it = nsteps / 3; it > 0; --it) {
+    issue_group<BITS>(r2, gate, up, rowoff + min(kg + 2 * step, last) * CB, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    mul_group<BITS>(r0, L, 8 * (kg - wkg0), lane, accg, accu);
+    kg += step;
+    issue_group<BITS>(r0, gate, up, rowoff + min(kg + 2 * step, last) * CB, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    mul_group<BITS>(r1, L, 8 * (kg - wkg0), lane, accg, accu);
+    kg += step;
+    issue_group<BITS>(r1, gate, up, rowoff + min(kg + 2 * step, last) * CB, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    mul_group<BITS>(r2, L, 8 * (kg - wkg0), lane, accg, accu);
+    kg += step;
+  }
+  const int rem = nsteps % 3;
+  if (rem >= 1) mul_group<BITS>(r0, L, 8 * (kg - wkg0), lane, accg, accu);
+  if (rem == 2) mul_group<BITS>(r1, L, 8 * (kg + step - wkg0), lane, accg, accu);
+}
+
+template <int BITS>
+__global__ __launch_bounds__(64 * GU_NW) void gu_decode_kernel(GuArgs a) {
+  constexpr int64_t CB = BITS == 2 ? 1280 : 1792;
+  __shared__ GuLds L;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: loop bounds stay scalar
   const int T = a.T, k = a.k, E = a.E, tk = a.T * a.k;
   const bool has_shared = a.has_shared != 0;
   const int base = has_shared ? 1 : 0;
   const int tiles_r = a.I / 16, tiles_s = has_shared ? a.Is / 16 : 0;
-  const int pr = (tiles_r + 3) / 4, ps = (tiles_s + 3) / 4;
   const int n_kg = a.n_kg;
-  // routing rows, fetched at once (used when the first routed item comes up)
+  const int n_win = (8 * n_kg + GU_WIN - 1) / GU_WIN;
+  const int win_kg = (n_kg + n_win - 1) / n_win;  // k-groups per window
+
   int r_e = -1;
   float r_w = 0.f;
   if (tid < tk) {
     r_e = a.idx[tid];
     r_w = a.w[tid];
   }
-  bool built = false;
+  if (n_win == 1) stage_window(L, a, 0, 8 * n_kg, tid);
+  build_slots(L.S, r_e, r_w, tk, k, T, E, has_shared);  // its barriers also publish the staging
   if (blockIdx.x == 0) {
-    build_slots(S, r_e, r_w, tk, k, T, E, has_shared);
-    built = true;
-    const int ns = base + S.n_routed;
+    const int ns = base + L.S.n_routed;
     if (tid == 0) *a.n_slots = ns;
-    for (int i = tid; i < ns; i += blockDim.x) a.slot_expert[i] = S.expert[i];
-    for (int i = tid; i < ns * 8; i += blockDim.x) a.slot_w[i] = S.w[i >> 3][i & 7];
+    for (int i = tid; i < ns; i += blockDim.x) a.slot_expert[i] = L.S.expert[i];
+    for (int i = tid; i < ns * 8; i += blockDim.x) a.slot_w[i] = L.S.w[i >> 3][i & 7];
   }
+  const int n_items = tiles_s + L.S.n_routed * tiles_r;
+  int KP = 8;
+  while (KP > 1 && (KP > n_kg || n_items * KP > (int)gridDim.x * GU_NW)) KP >>= 1;
+  const int G = GU_NW / KP, jw = wv / KP, kp = wv - jw * KP;
+  const int tok_e = 4 * ((lane >> 4) & 1);
 
-  for (int item = blockIdx.x;; item += gridDim.x) {
-    int u, q, ntile;
-    const uint8_t* ebase;
-    int64_t og, ou;
-    if (item < ps) {
-      u = 0;
-      q = item;
-      ntile = min(4, tiles_s - 4 * q);
-      ebase = a.X.shared;
-      og = a.X.sh_off_gate;
-      ou = a.X.sh_off_up;
-    } else {
-      if (!built) {
-        build_slots(S, r_e, r_w, tk, k, T, E, has_shared);
-        built = true;
+  for (int grp = blockIdx.x; grp * G < n_items; grp += gridDim.x) {
+    const int item = grp * G + jw;
+    const bool valid = item < n_items;
+    int u = 0, t = 0;
+    const uint8_t* gate = nullptr;
+    const uint8_t* up = nullptr;
+    if (valid) {
+      const uint8_t* ebase;
+      int64_t og, ou;
+      if (item < tiles_s) {
+        t = item;
+        ebase = a.X.shared;
+        og = a.X.sh_off_gate;
+        ou = a.X.sh_off_up;
+      } else {
+        const int ri = item - tiles_s;
+        u = base + ri / tiles_r;
+        t = ri - (ri / tiles_r) * tiles_r;
+        ebase = a.X.experts + (int64_t)L.S.expert[u] * a.X.ex_stride;
+        og = a.X.off_gate;
+        ou = a.X.off_up;
       }
-      const int ri = item - ps;
-      if (ri >= S.n_routed * pr) break;
-      u = base + ri / pr;
-      q = ri - (ri / pr) * pr;
-      ntile = min(4, tiles_r - 4 * q);
-      ebase = a.X.experts + (int64_t)S.expert[u] * a.X.ex_stride;
-      og = a.X.off_gate;
-      ou = a.X.off_up;
+      gate = ebase + og;
+      up = ebase + ou;
     }
-    const uint8_t* gate = ebase + og;
-    const uint8_t* up = ebase + ou;
-    // epilogue operands, fetched early: the wave's tokens and their weights
-    const int tok_e = 4 * ((lane >> 4) & 1);
-    float rn4[4], gw4[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      rn4[i] = a.rnorm[tok_e + i];
-      gw4[i] = (u == 0 && has_shared) ? (tok_e + i < T ? 1.0f : 0.f) : S.w[u][tok_e + i];
+    float4_t accg = float4_t{0.f, 0.f, 0.f, 0.f}, accu = accg;
+    for (int w = 0; w < n_win; ++w) {
+      const int kg0 = w * win_kg, kg1 = min(n_kg, kg0 + win_kg);
+      if (n_win > 1) {
+        __syncthreads();
+        stage_window(L, a, 8 * kg0, 8 * (kg1 - kg0), tid);
+        __syncthreads();
+      }
+      if (valid) run_tile<BITS>(gate, up, (int64_t)t * n_kg * CB, kg0 + kp, kg1, KP, kg0, L, lane, accg, accu);
     }
-
-    float4_t acc[4][2];
+    if (KP > 1) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+      for (int i = 0; i < 4; ++i) {
+        L.red[wv][i][lane] = accg[i];
+        L.red[wv][4 + i][lane] = accu[i];
+      }
+      __syncthreads();
+      if (kp == 0) {
+        for (int p = 1; p < KP; ++p)
 #pragma unroll
-      for (int m = 0; m < 2; ++m) acc[t][m] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-    unsigned char* st = stage[wv];
-    for (int kg = wv; kg < n_kg; kg += nw) {
-      ChunkRegs<BITS> c[4][2];
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        if (t < ntile) {
-          const int64_t ch = ((int64_t)(4 * q + t) * n_kg + kg) * CB;
-          load_chunk<BITS>(c[t][0], gate + ch, lane);
-          load_chunk<BITS>(c[t][1], up + ch, lane);
-        }
-      // activation fragments and block sums of the k-group, straight to LDS
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        __builtin_amdgcn_global_load_lds(a.xfrag + (((size_t)kg * 8 + j) * 64 + lane) * 8, (lds_ptr_t)(st + 1024 * j),
-                                         16, 0, 0);
-      if (lane < 32)
-        __builtin_amdgcn_global_load_lds(a.xsum + (size_t)kg * 8 * 16 + 4 * lane, (lds_ptr_t)(st + 8192), 16, 0, 0);
-      __builtin_amdgcn_s_waitcnt(0);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const half8_t A = *reinterpret_cast<const half8_t*>(st + 1024 * j + 16 * lane);
-        const float4_t cin = *reinterpret_cast<const float4_t*>(st + 8192 + 64 * j + 16 * (lane >> 4));
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          if (t < ntile) {
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-              const float4_t C = mfma16x16x32(A, chunk_frag<BITS>(c[t][m], j), cin);
-              acc[t][m] += chunk_scale(c[t][m].scales, j) * C;
-            }
+          for (int i = 0; i < 4; ++i) {
+            accg[i] += L.red[wv + p][i][lane];
+            accu[i] += L.red[wv + p][4 + i][lane];
           }
-        __builtin_amdgcn_sched_barrier(0);
       }
     }
-
-    // reduce the waves' partial sums in wave order (staging area reused)
-    __syncthreads();
-    float* red = reinterpret_cast<float*>(stage[wv]);  // [32][64]
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) red[((t * 2 + m) * 4 + i) * 64 + lane] = acc[t][m][i];
-    __syncthreads();
-    for (int t = wv; t < ntile; t += nw) {  // wave wv finishes row tiles wv, wv + nw, ...
-      float v[2][4];
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float part[GU_MAXW];
-#pragma unroll
-          for (int w = 0; w < GU_MAXW; ++w)
-            part[w] = reinterpret_cast<const float*>(stage[w < nw ? w : 0])[((t * 2 + m) * 4 + i) * 64 + lane];
-          float sm = part[0];
-#pragma unroll
-          for (int w = 1; w < GU_MAXW; ++w)
-            if (w < nw) sm += part[w];
-          v[m][i] = add_partner32(sm);  // hi + lo parts of the token
-        }
-      // lane l: column n = l & 15 (intermediate row 64q + 16t + n), rows
-      // m = 4(l>>4) + i, i.e. tokens tok_e + i; lanes >= 32 write the lo parts
+    if (valid && kp == 0) {
+      // lane l: intermediate row n = l & 15 of the tile, C rows 4(l>>4)+i:
+      // tokens tok_e + i, hi part in lanes < 32, lo part in lanes >= 32
       const int n = lane & 15;
       const bool lo_half = lane >= 32;
-      const int pblk = 2 * q + (t >> 1);  // 32-row block of the down projection
+      const int pblk = t >> 1, kk = 16 * (t & 1) + n;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tok = tok_e + i;
-        const float g = v[0][i] / rn4[i];
-        const float uu = v[1][i] / rn4[i];
+        const float gw = (u == 0 && has_shared) ? (tok < T ? 1.0f : 0.f) : L.S.w[u][tok];
+        const float rn = a.rnorm[tok];
+        const float g = add_partner32(accg[i]) / rn;
+        const float uu = add_partner32(accu[i]) / rn;
         const float hv = g / (1.0f + expf(-g)) * uu;
-        const float hs = (gw4[i] != 0.f) ? gw4[i] * hv : 0.f;
+        const float hs = (gw != 0.f) ? gw * hv : 0.f;
         const _Float16 hi = (_Float16)hs;
         const _Float16 val = lo_half ? (_Float16)(hs - (float)hi) : hi;
         const int mrow = tok + (lo_half ? 8 : 0);
-        const int kk = 16 * (t & 1) + n;
         a.hfrag[(((size_t)u * a.nbI + pblk) * 64 + mrow + 16 * (kk >> 3)) * 8 + (kk & 7)] = val;
         const float sm = row16_sum((float)val);
-        if (n == 0) bsum_lds[t][4 * (lane >> 4) + i] = sm;
+        if (n == 0) a.hsum[((size_t)u * 2 * a.nbI + t) * 16 + mrow] = -(float)a.code_off * sm;
       }
     }
-    __syncthreads();
-    if (tid < 16 * (ntile / 2)) {
-      const int blk = tid >> 4, mr = tid & 15;
-      const float sm = bsum_lds[2 * blk][mr] + bsum_lds[2 * blk + 1][mr];
-      a.hsum[((size_t)u * a.nbI + 2 * q + blk) * 16 + mr] = -(float)a.code_off * sm;
-    }
-    __syncthreads();
+    if (KP > 1) __syncthreads();  // red is rewritten in the next round
   }
 }
 
@@ -407,9 +448,8 @@ hipError_t launch_down_t(const DownArgs& a, int grid_x, int nw, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gu_decode(const GuArgs& a, int n_wg, hipStream_t s) {
-  int nw = a.n_kg < 10 ? a.n_kg : 10;
-  if (a.bits == 2) hipLaunchKernelGGL(gu_decode_kernel<2>, dim3(n_wg), dim3(64 * nw), 0, s, a);
-  else hipLaunchKernelGGL(gu_decode_kernel<3>, dim3(n_wg), dim3(64 * nw), 0, s, a);
+  if (a.bits == 2) hipLaunchKernelGGL(gu_decode_kernel<2>, dim3(n_wg), dim3(64 * GU_NW), 0, s, a);
+  else hipLaunchKernelGGL(gu_decode_kernel<3>, dim3(n_wg), dim3(64 * GU_NW), 0, s, a);
   return hipGetLastError();
 }
 

@@ -44,6 +44,21 @@ int env_int(const char* name, int dflt) {
   return (v && *v) ? atoi(v) : dflt;
 }
 
+// Compute units of the current device (cached per device id).
+int cu_count() {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  std::lock_guard<std::mutex> lk(mu);
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 std::once_flag g_init_once;
 hipError_t g_init_err = hipSuccess;
 void init_kernels() {
@@ -171,7 +186,7 @@ WsLayout ws_layout_decode(const moe_layer* L, int T) {
   W.xfrag = take((int64_t)(d / 32) * 64 * 8 * 2);
   W.xsum = take((int64_t)(d / 32) * 16 * 4);
   W.hfrag = take((int64_t)W.max_slots * W.nbI * 64 * 8 * 2);
-  W.hsum = take((int64_t)W.max_slots * W.nbI * 16 * 4);
+  W.hsum = take((int64_t)W.max_slots * W.nbI * 2 * 16 * 4);
   W.ypart = take((int64_t)W.S * 8 * d * 4);
   W.total = o;
   return W;
@@ -348,9 +363,10 @@ int decode_layer(const moe_layer* L, const LayerInput& in, float eps, int T, flo
   ga.code_off = ra.code_off;
   ga.has_shared = L->Is > 0;
   {
-    const int max_items = (W.max_slots - (ga.has_shared ? 1 : 0)) * ((L->I / 16 + 3) / 4) +
-                          (ga.has_shared ? (L->Is / 16 + 3) / 4 : 0);
-    int n_wg = env_int("MOE_GU_WGS", 160);
+    // one workgroup per CU (the kernel's LDS allows no more), never more
+    // workgroups than 16-row tiles
+    const int max_items = (W.max_slots - (ga.has_shared ? 1 : 0)) * (L->I / 16) + (ga.has_shared ? L->Is / 16 : 0);
+    int n_wg = env_int("MOE_GU_WGS", cu_count());
     if (n_wg > max_items) n_wg = max_items;
     if (n_wg < 1) n_wg = 1;
     timed_begin(0, s, &slot);

@@ -74,7 +74,7 @@ struct GuArgs {
   const _Float16* xfrag;
   const float* xsum;
   _Float16* hfrag;  // ws [MAX_SLOTS][nbI][64][8]
-  float* hsum;      // ws [MAX_SLOTS][nbI][16]
+  float* hsum;      // ws [MAX_SLOTS][2 nbI][16], one row of sums per 16-row tile
   int32_t E, I, Is, T, n_kg, bits, nbI, code_off, has_shared;
 };
 

@@ -20,11 +20,13 @@
 //             with the weights dequantized in registers to fp16 s * c (exact
 //             for 2-bit codes, one rounding for 3-bit), x rows gathered
 //             into LDS by direct-to-LDS loads, v_mfma_f32_16x16x32_f16;
-//             epilogue h = silu(g) * u in fp32, stored as fp16 with one
-//             power-of-two exponent per (row, 128-column tile);
-//   down      per item and 256 output columns: Y = H W_d^T, H rows brought to
-//             one exponent per row while they are staged into LDS; epilogue
-//             multiplies by the gate weight and writes one fp32 row per pair;
+//             epilogue h = silu(g) * u in fp32, stored as fp16(h 2^-eh)
+//             with eh = hb + 2 ex: hb is a per-expert bound exponent found at
+//             pack time from the row L1 norms of gate and up, so no pass over
+//             the row is needed to choose it;
+//   down      per item and 256 output columns: Y = H W_d^T with H staged into
+//             LDS by direct-to-LDS loads; the epilogue multiplies by the gate
+//             weight times 2^eh and writes one fp32 row per pair;
 //   combine   y[t] = sum of its pairs' rows in rank order + its shared row.
 // Every product on the matrix cores is exact; the roundings are the fp16
 // activations (x, h), 3-bit weights with a code of +-3, and fp32 accumulation.

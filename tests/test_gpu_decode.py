@@ -139,6 +139,21 @@ def test_layer_full_size(bqe, bits):
         _check_layer(wl, 0, L, x, bqe, f"full bits={bits} T={T}")
 
 
+def test_layer_odd_shapes(bqe):
+    # E not a multiple of 16, intermediate sizes not multiples of 64, k = E,
+    # a shared expert wider than the routed ones, and inputs wider than one
+    # LDS window of the gate/up kernel (d = 4096 and 8192: two and three
+    # windows)
+    for kw in (dict(E=20, k=3, I=96, Is=32), dict(E=1, k=1, I=32, Is=0), dict(E=5, k=5, I=160, Is=288),
+               dict(d=512, E=40, k=4, I=64, Is=64), dict(d=4096, E=32, k=4, I=64, Is=96, bits=3),
+               dict(d=8192, E=24, k=3, I=96, Is=32)):
+        wl = mi.small(mi.WORKLOADS["tiny"], zipf_s=None, **kw)
+        L = packed_layer(wl, 0)
+        for T in (1, 5, 8):
+            x = mi.activations(wl, T=T, stream=60 + T)
+            _check_layer(wl, 0, L, x, bqe, f"odd {kw} T={T}")
+
+
 def test_forced_routing_and_invalid_entries(bqe):
     wl = mi.small(mi.WORKLOADS["tiny"], Is=64)
     L = packed_layer(wl, 0)
