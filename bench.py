@@ -54,6 +54,31 @@ def algorithmic_bytes_decode(wl, idx_layers: np.ndarray, T: int):
     return total, np.array(gu, dtype=np.float64), np.array(dn, dtype=np.float64)
 
 
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of the dominant kernel as the byte counters read
+    them (profiles/traffic.json: FETCH_SIZE and WRITE_SIZE per dispatch,
+    scaled by the copy calibration), or None when no counters were taken for
+    this workload or the kernel's sources changed since."""
+    import hashlib
+
+    here = os.path.dirname(os.path.abspath(__file__))
+    try:
+        with open(os.path.join(here, "profiles", "traffic.json")) as f:
+            tab = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = tab.get(workload)
+    if not ent or ent.get("kernel") != kernel:
+        return None
+    h = hashlib.sha256()
+    for src in ent["sources"]:
+        with open(os.path.join(here, src), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != ent.get("sources_sha256"):
+        return None
+    return 1024.0 * (ent["fetch_kib"] * tab["fetch_scale"] + ent["write_kib"] * tab["write_scale"])
+
+
 def cpu_baseline_stack(wl, T, x_np, n_layers_sample):
     """Time the oracle (single-threaded fp64 C) on the first layers of the
     stack; expert generation is excluded from the timed parts."""
@@ -206,7 +231,8 @@ def bench_prefill(args):
         "grouped_gemm_mfma_util": gemm_util,
         "tokens_per_expert": {"max": int(counts.max()), "empty_experts": int((counts == 0).sum())},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / MFMA_F16_PEAK_TFLOPS, "traffic": None},
+                     "unit": "TFLOP/s", "frac": achieved / MFMA_F16_PEAK_TFLOPS,
+                     "traffic": measured_traffic(wl.name, dom) if T == wl.T else None},
         "kernels": kernels,
         "cpu_baseline": cpu,
     }
@@ -478,7 +504,8 @@ def main():
         "bytes_per_step": total_bytes,
         "distinct_experts_per_layer": {"min": min(distinct), "mean": float(np.mean(distinct)), "max": max(distinct)},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(wl.name, dom) if (T == wl.T and not args.layers) else None},
         "kernels": kernels,
         "cpu_baseline": cpu,
     }
