@@ -138,6 +138,7 @@ struct GuLds {
   unsigned char xs[GU_WIN * 1024];  // A-fragments, [block][lane][8] fp16
   float cs[GU_WIN * 16];            // accumulator seeds, [block][16]
   float red[GU_NW][8][64];          // partial sums of the k-parts
+  float rn[8];                      // rms of each token
   SlotLds S;
 };
 
@@ -246,8 +247,9 @@ __global__ __launch_bounds__(64 * GU_NW) void gu_decode_kernel(GuArgs a) {
     r_e = a.idx[tid];
     r_w = a.w[tid];
   }
+  if (tid < 8) L.rn[tid] = tid < T ? a.rnorm[tid] : 1.0f;
   if (n_win == 1) stage_window(L, a, 0, 8 * n_kg, tid);
-  build_slots(L.S, r_e, r_w, tk, k, T, E, has_shared);  // its barriers also publish the staging
+  build_slots(L.S, r_e, r_w, tk, k, T, E, has_shared);  // its barriers also publish the staging and rms
   if (blockIdx.x == 0) {
     const int ns = base + L.S.n_routed;
     if (tid == 0) *a.n_slots = ns;
@@ -321,7 +323,7 @@ __global__ __launch_bounds__(64 * GU_NW) void gu_decode_kernel(GuArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int tok = tok_e + i;
         const float gw = (u == 0 && has_shared) ? (tok < T ? 1.0f : 0.f) : L.S.w[u][tok];
-        const float rn = a.rnorm[tok];
+        const float rn = L.rn[tok];
         const float g = add_partner32(accg[i]) / rn;
         const float uu = add_partner32(accu[i]) / rn;
         const float hv = g / (1.0f + expf(-g)) * uu;

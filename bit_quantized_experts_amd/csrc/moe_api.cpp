@@ -302,7 +302,8 @@ int decode_layer(const moe_layer* L, const LayerInput& in, float eps, int T, flo
   ra.in = in.p;
   ra.S_in = in.S;
   ra.in_stride = in.stride;
-  ra.Wr = L->router_w;
+  ra.wh = L->router_wh;
+  ra.wl = L->router_wl;
   ra.T = T;
   ra.d = d;
   ra.E = E;
@@ -321,6 +322,7 @@ int decode_layer(const moe_layer* L, const LayerInput& in, float eps, int T, flo
   sa.lp = ra.lp;
   sa.ss_part = ra.ss_part;
   sa.br = L->router_b;
+  sa.ew = L->router_ew;
   sa.n_cs = W.n_cs;
   sa.T = T;
   sa.d = d;
@@ -433,8 +435,7 @@ int prefill_layer(const moe_layer* L, const float* x, int norm, float eps, int T
     ra.ex = pa.ex;
     ra.wh = L->router_wh;
     ra.wl = L->router_wl;
-    ra.ew = L->router_ew;
-    ra.bias = L->router_b;
+      ra.bias = L->router_b;
     ra.T = T;
     ra.d = d;
     ra.E = E;

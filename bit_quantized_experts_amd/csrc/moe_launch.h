@@ -13,7 +13,7 @@
 // Expert rows per route workgroup (4 waves x 16 rows).
 #define MOE_ROUTE_ROWS 64
 // Most down-projection splits (partial sums a consumer adds up).
-#define MOE_MAX_IN_SPLITS 16
+#define MOE_MAX_IN_SPLITS 8
 // Most column slices of the router (d <= 8192).
 #define MOE_MAX_CS 32
 
@@ -24,7 +24,8 @@ struct RouteArgs {
   const float* in;
   int32_t S_in;
   int64_t in_stride;  // floats between splits
-  const float* Wr;    // [E][d]
+  const _Float16* wh;  // router rows times 2^-ew, fp16 hi part, B-fragments [E16/16][d/32][64][8]
+  const _Float16* wl;  // same, lo part
   int32_t T, d, E, code_off, do_logits;
   float* lp;        // ws [d/256][T][E] partial logits
   float* ss_part;   // ws [d/256][T] partial sums of squares
@@ -37,6 +38,7 @@ struct SelectArgs {
   const float* lp;       // [n_cs][T][E]
   const float* ss_part;  // [n_cs][T]
   const float* br;       // [E]
+  const int32_t* ew;     // [E16] router row exponents (partial logits are unscaled)
   int32_t n_cs, T, d, E, k, norm;
   float eps;
   const int32_t* fidx;  // forced routing or null

@@ -34,53 +34,136 @@ DEVI float key_value(uint64_t k) {
 DEVI int key_index(uint64_t k) { return (int)(0xFFFFFFFFu - (uint32_t)k); }
 
 // Top-k of one row of E logits by one wavefront, then the gate weights.
-// Lane l holds the keys of experts l, l+64, ...; each round takes the
-// wavefront maximum and the owning lane clears that key.  Lane r (< k) keeps
-// rank r.  Gate weights: m = logit of rank 0, e_r = exp64(l_r - m), S = sum of
-// e_r in rank order, w_r = fp32(e_r / S).  NPER >= ceil(E / 64).
+// Lane l holds the keys of experts l, l+64, ...; keys are unique.
+//   1. Candidates: theta = the k-th largest of the 64 lane maxima (ranked by
+//      counting larger maxima through LDS).  At least k keys are >= theta
+//      (those k maxima), and every key of the top k is >= theta.
+//   2. If at most 64 keys are >= theta they are compacted to LDS, each is
+//      ranked by counting the larger candidates, and the first k ranks are
+//      the answer.  Otherwise (many equal logits) a radix search on the value
+//      keys finds the k-th largest value (a trial threshold is kept while at
+//      least k values reach it, stopping once exactly k do); the values above
+//      it and the tied ones in ascending expert index are taken, compacted
+//      and ranked the same way.
+// Lane r ends up with rank r (value descending, then index ascending).  Gate
+// weights: m = logit of rank 0, e_r = exp64(l_r - m), S = sum of e_r in rank
+// order, w_r = fp32(e_r / S).  `buf`: this wave's 96 LDS entries.  NPER >=
+// ceil(E / 64).
+DEVI int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+DEVI double readlane_f64(double v, int l) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)b, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(b >> 32), l);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+DEVI uint64_t readlane_u64(uint64_t v, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+constexpr int TOPK_BUF = 96;  // LDS entries per wave: 64 candidates + 32
+
 template <int NPER, typename RowT>
-DEVI void topk_wave(RowT row, int E, int k, int32_t* idx_out, float* w_out) {
+DEVI void topk_wave(RowT row, int E, int k, int32_t* idx_out, float* w_out, uint64_t* buf) {
   const int lane = threadIdx.x & 63;
   uint64_t key[NPER];
+  uint64_t lmax = 0;
 #pragma unroll
   for (int i = 0; i < NPER; ++i) {
     const int e = lane + 64 * i;
-    key[i] = (e < E) ? sel_key(row(e), e) : 0ull;
+    key[i] = (e < E) ? sel_key(row(e), e) : 0ull;  // 0: no expert
+    lmax = key[i] > lmax ? key[i] : lmax;
   }
-  float my_v = 0.f;
-  int my_e = 0;
-  for (int r = 0; r < k; ++r) {
-    uint64_t best = 0;
+  // 1. theta = k-th largest lane maximum
+  buf[lane] = lmax;
+  int rk = 0;
+  for (int j = 0; j < 64; ++j) rk += (buf[j] > lmax) ? 1 : 0;
+  const uint64_t at = __ballot(rk == k - 1 && lmax != 0ull);
+  const uint64_t theta = readlane_u64(lmax, at ? (int)__builtin_ctzll(at) : 0);
+  int c = 0;
 #pragma unroll
-    for (int i = 0; i < NPER; ++i) best = key[i] > best ? key[i] : best;
-    best = wave_max_u64(best);
-    int e = key_index(best);
-    if (best == 0ull || e < 0 || e >= E) e = 0;  // only with non-finite logits (out of contract)
+  for (int i = 0; i < NPER; ++i) c += (int)__builtin_popcountll(__ballot(key[i] >= theta));
+
+  // 2. choose the candidate set: keys >= theta, or the exact top k
+  bool exact = true;
+  uint32_t tau = 0;
+  int need = 0;
+  if (c > 64) {
+    uint32_t hv[NPER];
 #pragma unroll
-    for (int i = 0; i < NPER; ++i)
-      if (lane + 64 * i == e) key[i] = 0ull;
-    if (lane == r) {
-      my_v = key_value(best);
-      my_e = e;
+    for (int i = 0; i < NPER; ++i) hv[i] = (uint32_t)(key[i] >> 32);
+    exact = false;
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t t = tau | (1u << b);
+      int cnt = 0;
+#pragma unroll
+      for (int i = 0; i < NPER; ++i) cnt += (int)__builtin_popcountll(__ballot(hv[i] >= t));
+      if (cnt >= k) {
+        tau = t;
+        if (cnt == k) {
+          exact = true;
+          break;
+        }
+      }
+    }
+    if (!exact) {
+      int c_gt = 0;
+#pragma unroll
+      for (int i = 0; i < NPER; ++i) c_gt += (int)__builtin_popcountll(__ballot(hv[i] > tau));
+      need = k - c_gt;
     }
   }
-  const double m = (double)__shfl(my_v, 0, 64);
+  const bool radix = c > 64;
+  // compact the candidates to buf[0..n) in (slot, lane) order
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const uint32_t hv = (uint32_t)(key[i] >> 32);
+    bool take;
+    if (!radix) {
+      take = key[i] >= theta;
+    } else {
+      const bool tie = !exact && hv == tau;
+      const uint64_t tm = __ballot(tie);
+      take = exact ? (hv >= tau) : (hv > tau || (tie && lanes_below(tm) < need));
+      need -= min(need, (int)__builtin_popcountll(tm));
+    }
+    const uint64_t sm = __ballot(take);
+    const int pos = n + lanes_below(sm);
+    if (take && pos < 64) buf[pos] = key[i];
+    n += (int)__builtin_popcountll(sm);
+  }
+  n = min(n, 64);
+  // rank the candidates; the first k ranks are the result
+  const uint64_t mine = (lane < n) ? buf[lane] : 0ull;
+  int rank = 0;
+  for (int j = 0; j < n; ++j) rank += (buf[j] > mine) ? 1 : 0;
+  if (lane < n && rank < k) buf[64 + rank] = mine;
+  const uint64_t kr = (lane < k) ? buf[64 + lane] : 0ull;
+  const float my_v = key_value(kr);
+  const int my_e = key_index(kr);
+  const double m = (double)__builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(uint32_t, my_v)));
   double ev = 0.0;
   if (lane < k) ev = moe_exp64((double)my_v - m);
   double S = 0.0;
-  for (int r = 0; r < k; ++r) S += __shfl(ev, r, 64);  // rank order, same in every lane
+  for (int r = 0; r < k; ++r) S += readlane_f64(ev, r);  // rank order, same in every lane
   if (lane < k) {
-    idx_out[lane] = my_e;
+    idx_out[lane] = (my_e >= 0 && my_e < E) ? my_e : 0;  // (other only with non-finite logits, out of contract)
     w_out[lane] = (float)(ev / S);
   }
 }
 
 template <typename RowT>
-DEVI void topk_wave_any(RowT row, int E, int k, int32_t* idx_out, float* w_out) {
-  if (E <= 512) topk_wave<8>(row, E, k, idx_out, w_out);
-  else if (E <= 1024) topk_wave<16>(row, E, k, idx_out, w_out);
-  else if (E <= 2048) topk_wave<32>(row, E, k, idx_out, w_out);
-  else topk_wave<64>(row, E, k, idx_out, w_out);
+DEVI void topk_wave_any(RowT row, int E, int k, int32_t* idx_out, float* w_out, uint64_t* buf) {
+  if (E <= 512) topk_wave<8>(row, E, k, idx_out, w_out, buf);
+  else if (E <= 1024) topk_wave<16>(row, E, k, idx_out, w_out, buf);
+  else if (E <= 2048) topk_wave<32>(row, E, k, idx_out, w_out, buf);
+  else topk_wave<64>(row, E, k, idx_out, w_out, buf);
 }
 
 struct PtrRow {
@@ -90,28 +173,10 @@ struct PtrRow {
 
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                    int32_t* __restrict__ idx, float* __restrict__ w) {
+  __shared__ uint64_t buf[4][TOPK_BUF];
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  topk_wave_any(PtrRow{logits + (size_t)t * E}, E, k, idx + (size_t)t * k, w + (size_t)t * k);
-}
-
-// Sum 64 per-lane values across the wavefront so that lane l ends up with
-// the total of value index l ("reduce-scatter"): at the step of distance h,
-// a lane keeps the half of its values selected by its lane bit h and adds the
-// partner's copy of that half.
-DEVI float reduce_scatter64(float (&v)[64], int lane) {
-#pragma unroll
-  for (int h = 32; h >= 1; h >>= 1) {
-    const bool up = (lane & h) != 0;
-#pragma unroll
-    for (int j = 0; j < h; ++j) {
-      const float lo = v[j], hi = v[j + h];
-      const float send = up ? lo : hi;
-      const float keep = up ? hi : lo;
-      v[j] = keep + __shfl_xor(send, h, 64);
-    }
-  }
-  return v[0];
+  topk_wave_any(PtrRow{logits + (size_t)t * E}, E, k, idx + (size_t)t * k, w + (size_t)t * k, buf[threadIdx.x >> 6]);
 }
 
 // ---------------------------------------------------------------------------
@@ -122,40 +187,86 @@ DEVI float reduce_scatter64(float (&v)[64], int lane) {
 // MFMA A-fragments of the 8 blocks of the slice:
 //   lane L = m + 16q of block b holds row m (m < 8: token m, hi part; m >= 8:
 //   token m-8, lo part) at inputs 8q..8q+7; xsum[b][m] = -code_off * sum.
+// The partial logits run on the matrix cores: the same A-fragments (built in
+// registers by every workgroup) times the router rows prepared at pack time
+// as 2^ew (wh + wl), fp16 hi and lo B-fragments, so one wavefront's 16
+// experts over the 8 blocks take 16 v_mfma_f32_16x16x32_f16 and the hi and lo
+// rows of a token are added once at the end.  All four products of the
+// ~22-bit operands are formed exactly; the rounding is fp32 accumulation.
+// The power of two 2^ew of each router row is applied by the select kernel
+// to the summed partials (exact).
 // ---------------------------------------------------------------------------
+DEVI half8_t x_fragment(const float (*ys)[MOE_ROUTE_COLS], int bl, int lane, int T, float* sum) {
+  const int m = lane & 15, q = lane >> 4, tok = m & 7, lo = m >> 3;
+  float4_t v0 = float4_t{0.f, 0.f, 0.f, 0.f}, v1 = v0;
+  if (tok < T) {
+    v0 = *reinterpret_cast<const float4_t*>(&ys[tok][32 * bl + 8 * q]);
+    v1 = *reinterpret_cast<const float4_t*>(&ys[tok][32 * bl + 8 * q + 4]);
+  }
+  half8_t h;
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const float v = c < 4 ? v0[c] : v1[c - 4];
+    const _Float16 hi = (_Float16)v;
+    const _Float16 out = lo ? (_Float16)(v - (float)hi) : hi;
+    h[c] = out;
+    s += (float)out;
+  }
+  *sum = s;
+  return h;
+}
+
 __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   __shared__ float ys[MOE_MAX_TOK_DECODE][MOE_ROUTE_COLS];
   const int cs = blockIdx.x, rs = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int T = a.T, d = a.d, E = a.E;
   const int c0 = cs * MOE_ROUTE_COLS;
+  constexpr int NBL = MOE_ROUTE_COLS / 32;  // blocks per column slice
 
-  // router rows of this wave: issue the weight loads first (HBM latency)
-  float4_t W4[16];
-  const int e_base = rs * MOE_ROUTE_ROWS + wv * 16;
-  if (a.do_logits) {
+  // the input splits of this slice first (the previous kernel's output), then
+  // the router fragments of this wave's 16 experts and their row exponents:
+  // the wait for the inputs leaves the router loads in flight
+  // (every load is issued, rows past T and splits past S_in re-read a valid
+  // address, so the wait counts before the first add are exact)
+  const int et = rs * (MOE_ROUTE_ROWS / 16) + wv;  // 16-expert tile
+  const bool tile_ok = a.do_logits && et * 16 < E;
+  constexpr int PER = MOE_MAX_TOK_DECODE * 64 / 256;  // float4 per thread
+  float4_t v[PER][MOE_MAX_IN_SPLITS];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int e = e_base + i;
-      W4[i] = (e < E) ? __builtin_nontemporal_load(reinterpret_cast<const float4_t*>(a.Wr + (size_t)e * d + c0) + lane)
-                      : float4_t{0.f, 0.f, 0.f, 0.f};
-    }
-  }
-
-  // summed input slice into LDS (splits added in order; all loads issued first)
-  for (int i = tid; i < T * 64; i += 256) {
-    const int t = i >> 6, c4 = i & 63;
+  for (int j = 0; j < PER; ++j) {
+    const int i = tid + 256 * j, t = min(i >> 6, T - 1), c4 = i & 63;
     const float* src = a.in + (size_t)t * d + c0 + 4 * c4;
-    float4_t v[MOE_MAX_IN_SPLITS];
 #pragma unroll
     for (int s = 0; s < MOE_MAX_IN_SPLITS; ++s)
-      v[s] = *reinterpret_cast<const float4_t*>(src + (size_t)(s < a.S_in ? s : 0) * a.in_stride);
-    float4_t acc = v[0];
+      v[j][s] = *reinterpret_cast<const float4_t*>(src + (size_t)min(s, a.S_in - 1) * a.in_stride);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep the input loads ahead of the router loads
+  // (issued by every wave, tile 0 standing in for a wave without a tile, so
+  // the wait counts stay exact)
+  half8_t BH[NBL], BL[NBL];
+  {
+    const size_t base = ((size_t)(tile_ok ? et : 0) * (d / 32) + cs * NBL) * 64 * 8;
 #pragma unroll
-    for (int s = 1; s < MOE_MAX_IN_SPLITS; ++s)
-      if (s < a.S_in) acc += v[s];
-    *reinterpret_cast<float4_t*>(&ys[t][4 * c4]) = acc;
-    if (rs == 0 && a.y_out) *reinterpret_cast<float4_t*>(a.y_out + (size_t)t * d + c0 + 4 * c4) = acc;
+    for (int j = 0; j < NBL; ++j) {
+      BH[j] = __builtin_nontemporal_load(reinterpret_cast<const half8_t*>(a.wh + base + ((size_t)j * 64 + lane) * 8));
+      BL[j] = __builtin_nontemporal_load(reinterpret_cast<const half8_t*>(a.wl + base + ((size_t)j * 64 + lane) * 8));
+    }
+  }
+  // summed input slice into LDS (splits added in order)
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = tid + 256 * j, t = i >> 6, c4 = i & 63;
+    if (t < T) {
+      float4_t acc = v[j][0];
+#pragma unroll
+      for (int s = 1; s < MOE_MAX_IN_SPLITS; ++s)
+        if (s < a.S_in) acc += v[j][s];
+      *reinterpret_cast<float4_t*>(&ys[t][4 * c4]) = acc;
+      if (rs == 0 && a.y_out) *reinterpret_cast<float4_t*>(a.y_out + (size_t)t * d + c0 + 4 * c4) = acc;
+    }
   }
   __syncthreads();
 
@@ -165,19 +276,11 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
       const float ss = wave_sum(v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w);
       if (lane == 0) a.ss_part[cs * T + t] = ss;
     }
-    const int m = lane & 15, q = lane >> 4, tok = m & 7, lo = m >> 3;
-    for (int bl = wv; bl < MOE_ROUTE_COLS / 32; bl += 4) {
-      const int b = cs * (MOE_ROUTE_COLS / 32) + bl;
-      half8_t h;
-      float s = 0.f;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float v = (tok < T) ? ys[tok][32 * bl + 8 * q + c] : 0.f;
-        const _Float16 hi = (_Float16)v;
-        const _Float16 out = lo ? (_Float16)(v - (float)hi) : hi;
-        h[c] = out;
-        s += (float)out;
-      }
+    const int m = lane & 15, q = lane >> 4;
+    for (int bl = wv; bl < NBL; bl += 4) {
+      const int b = cs * NBL + bl;
+      float s;
+      const half8_t h = x_fragment(ys, bl, lane, T, &s);
       *reinterpret_cast<half8_t*>(a.xfrag + ((size_t)b * 64 + lane) * 8) = h;
       s += __shfl_xor(s, 16, 64);
       s += __shfl_xor(s, 32, 64);
@@ -185,24 +288,28 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     }
   }
 
-  if (!a.do_logits) return;
-  float4 y4[MOE_MAX_TOK_DECODE];
+  if (!tile_ok) return;
+  half8_t A[NBL];
 #pragma unroll
-  for (int t = 0; t < MOE_MAX_TOK_DECODE; ++t)
-    y4[t] = (t < T) ? *reinterpret_cast<const float4*>(&ys[t][4 * lane]) : float4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < NBL; ++j) {
+    float s;
+    A[j] = x_fragment(ys, j, lane, T, &s);
+  }
+  float4_t acc = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    float v[64];
+  for (int j = 0; j < NBL; ++j) {
+    acc = mfma16x16x32(A[j], BH[j], acc);
+    acc = mfma16x16x32(A[j], BL[j], acc);
+  }
+  // lane l: expert et*16 + (l & 15), C rows 4(l>>4)+i: token 4((l>>4)&1)+i,
+  // hi part in lanes < 32, lo part in lanes >= 32.  The partial logits are
+  // left without the row factor 2^ew; the select kernel applies it to the sum.
+  const int e = et * 16 + (lane & 15);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const float4_t w = W4[half * 8 + i];
-        v[i * 8 + t] = w.x * y4[t].x + w.y * y4[t].y + w.z * y4[t].z + w.w * y4[t].w;
-      }
-    const float s = reduce_scatter64(v, lane);
-    const int e = e_base + half * 8 + (lane >> 3), t = lane & 7;
-    if (e < E && t < T) a.lp[((size_t)cs * T + t) * E + e] = s;
+  for (int i = 0; i < 4; ++i) {
+    const float v = add_partner32(acc[i]);
+    const int t = 4 * ((lane >> 4) & 1) + i;
+    if (lane < 32 && e < E && t < T) a.lp[((size_t)cs * T + t) * E + e] = v;
   }
 }
 
@@ -217,7 +324,14 @@ template <int MAXCS>
 DEVI void sum_partials(const SelectArgs& a, int t, float den, float* row) {
   const int tid = threadIdx.x, T = a.T, E = a.E, n_cs = a.n_cs;
   for (int e0 = 0; e0 < E; e0 += 512) {
-    float tmp[2][MAXCS];
+    float tmp[2][MAXCS], bias[2];
+    int ew[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {  // bias and row exponent first: they wait for nothing
+      const int e = min(e0 + tid + 256 * j, E - 1);
+      bias[j] = a.br[e];
+      ew[j] = a.ew[e];
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int e = min(e0 + tid + 256 * j, E - 1);
@@ -232,7 +346,8 @@ DEVI void sum_partials(const SelectArgs& a, int t, float den, float* row) {
       for (int c = 1; c < MAXCS; ++c)
         if (c < n_cs) acc += tmp[j][c];
       if (e < E) {
-        const float l = (a.norm ? acc / den : acc) + a.br[e];
+        const float x = ldexpf(acc, ew[j]);  // router row factor, exact
+        const float l = (a.norm ? x / den : x) + bias[j];
         row[e] = l;
         a.logits[(size_t)t * E + e] = l;
         if (a.out_logits) a.out_logits[(size_t)t * E + e] = l;
@@ -244,6 +359,7 @@ DEVI void sum_partials(const SelectArgs& a, int t, float den, float* row) {
 __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
   extern __shared__ float row[];  // [E]
   __shared__ float den_s;
+  __shared__ uint64_t tk_buf[TOPK_BUF];
   const int t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int T = a.T, k = a.k;
@@ -273,7 +389,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
   else sum_partials<32>(a, t, den, row);
   __syncthreads();
   if (wv == 0) {
-    topk_wave_any(PtrRow{row}, a.E, k, a.idx + t * k, a.w + t * k);
+    topk_wave_any(PtrRow{row}, a.E, k, a.idx + t * k, a.w + t * k, tk_buf);
     if (lane < k) {
       if (a.out_idx) a.out_idx[t * k + lane] = a.idx[t * k + lane];
       if (a.out_w) a.out_w[t * k + lane] = a.w[t * k + lane];

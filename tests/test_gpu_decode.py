@@ -99,7 +99,8 @@ def test_debug_unpack_bitexact(bqe, bits, shape):
             assert np.array_equal(w16.cpu().numpy().view(np.uint16), o16), (e, mat)
 
 
-@pytest.mark.parametrize("E,k,T", [(16, 2, 5), (512, 10, 64), (512, 16, 33), (4096, 8, 9), (3, 3, 7), (1, 1, 4)])
+@pytest.mark.parametrize("E,k,T", [(16, 2, 5), (512, 10, 64), (512, 16, 33), (4096, 8, 9), (3, 3, 7), (1, 1, 4),
+                                   (1000, 12, 6), (2048, 16, 3), (65, 16, 5)])
 def test_route_topk_bitexact(bqe, E, k, T):
     say(f"[topk] E={E} k={k} T={T}")
     g = np.random.default_rng(E * 31 + k)
@@ -108,6 +109,11 @@ def test_route_topk_bitexact(bqe, E, k, T):
              np.where(g.random((T, E)) < 0.5, -0.0, 0.0).astype(np.float32)]
     if E == 512:
         cases.append(mi.direct_logits(mi.WORKLOADS["layer_t1"], T))
+    # experts e with e % 64 < 16 (one wavefront lane in four holds them) all
+    # rank above the rest: more than 64 logits reach the k-th largest of the
+    # per-lane maxima when E is large, which takes the selection's second path
+    cases.append((((np.arange(E) % 64) < 16).astype(np.float32)[None, :]
+                  + g.random((T, E)).astype(np.float32) * 1e-3).astype(np.float32))
     for l in cases:
         lt = torch.from_numpy(l).to(DEV)
         idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
