@@ -59,10 +59,12 @@ DEVI void load_a(const _Float16* frag, const float* sum, size_t b, int lane, hal
 }
 
 // ---------------------------------------------------------------------------
-// Slot list, built in LDS by a workgroup from the routing rows (T*k
-// entries): routed experts are marked in a bitmap, numbered in ascending id
-// order after the shared expert's slot 0, and every (token, rank) entry puts
-// its gate weight in its slot's row.
+// Slot list, built in LDS by one wavefront from the routing rows (T*k <= 128
+// entries, two per lane): routed experts are marked in a bitmap, numbered in
+// ascending id order after the shared expert's slot 0, and every (token,
+// rank) entry puts its gate weight in its slot's row.  Only LDS operations of
+// the one wavefront are involved (they complete in order), so the other
+// wavefronts need a single barrier afterwards.
 // ---------------------------------------------------------------------------
 struct SlotLds {
   uint32_t mark[MOE_MAX_E / 32];
@@ -72,47 +74,53 @@ struct SlotLds {
   int n_routed;
 };
 
-DEVI void build_slots(SlotLds& S, int r_e, float r_w, int tk, int k, int T, int E, bool has_shared) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+DEVI void build_slots_wave(SlotLds& S, const int32_t* idx, const float* w, int tk, int k, int T, int E,
+                           bool has_shared) {
+  const int lane = threadIdx.x & 63;
   const int nwords = (E + 31) >> 5, base = has_shared ? 1 : 0;
-  for (int i = tid; i < nwords; i += blockDim.x) S.mark[i] = 0u;
-  __syncthreads();
-  const bool valid = tid < tk && r_e >= 0 && r_e < E;
-  if (valid) atomicOr(&S.mark[r_e >> 5], 1u << (r_e & 31));
-  __syncthreads();
-  if (wv == 0) {
-    const int c0 = (2 * lane < nwords) ? __popc(S.mark[2 * lane]) : 0;
-    const int c1 = (2 * lane + 1 < nwords) ? __popc(S.mark[2 * lane + 1]) : 0;
-    int incl = c0 + c1;
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += v;
+  int re[2];
+  float rw[2];
+  bool ok[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int j = lane + 64 * h;
+    re[h] = (j < tk) ? idx[j] : -1;
+    rw[h] = (j < tk) ? w[j] : 0.f;
+    ok[h] = re[h] >= 0 && re[h] < E;
+  }
+  for (int i = lane; i < nwords; i += 64) S.mark[i] = 0u;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    if (ok[h]) atomicOr(&S.mark[re[h] >> 5], 1u << (re[h] & 31));
+  // exclusive prefix of the marked counts over the words (lane: words 2l, 2l+1)
+  const uint32_t m0 = (2 * lane < nwords) ? S.mark[2 * lane] : 0u;
+  const uint32_t m1 = (2 * lane + 1 < nwords) ? S.mark[2 * lane + 1] : 0u;
+  const int c0 = __popc(m0), c1 = __popc(m1);
+  int incl = c0 + c1;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  const int excl = incl - c0 - c1;
+  if (2 * lane < nwords) S.wbase[2 * lane] = excl;
+  if (2 * lane + 1 < nwords) S.wbase[2 * lane + 1] = excl + c0;
+  const int n_routed = __shfl(incl, 63, 64);
+  if (lane == 0) S.n_routed = n_routed;
+  {
+    int slot = base + excl;
+    for (uint32_t m = m0; m; m &= m - 1u) S.expert[slot++] = 64 * lane + __builtin_ctz(m);
+    for (uint32_t m = m1; m; m &= m - 1u) S.expert[slot++] = 64 * lane + 32 + __builtin_ctz(m);
+  }
+  if (has_shared && lane == 0) S.expert[0] = E;
+  const int ns = base + n_routed;
+  for (int i = lane; i < ns * 8; i += 64) S.w[i >> 3][i & 7] = (has_shared && i < 8 && i < T) ? 1.0f : 0.f;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    if (ok[h]) {
+      const int word = re[h] >> 5;
+      const int slot = base + S.wbase[word] + __popc(S.mark[word] & ((1u << (re[h] & 31)) - 1u));
+      S.w[slot][(lane + 64 * h) / k] = rw[h];
     }
-    const int excl = incl - c0 - c1;
-    if (2 * lane < nwords) S.wbase[2 * lane] = excl;
-    if (2 * lane + 1 < nwords) S.wbase[2 * lane + 1] = excl + c0;
-    if (lane == 63) S.n_routed = incl;
-  }
-  __syncthreads();
-  for (int i = tid; i < nwords; i += blockDim.x) {
-    uint32_t m = S.mark[i];
-    int slot = base + S.wbase[i];
-    while (m) {
-      const int bit = __builtin_ctz(m);
-      S.expert[slot++] = 32 * i + bit;
-      m &= m - 1u;
-    }
-  }
-  if (has_shared && tid == 0) S.expert[0] = E;
-  const int ns = base + S.n_routed;
-  for (int i = tid; i < ns * 8; i += blockDim.x) S.w[i >> 3][i & 7] = (has_shared && i < 8 && i < T) ? 1.0f : 0.f;
-  __syncthreads();
-  if (valid) {
-    const int word = r_e >> 5;
-    const int slot = base + S.wbase[word] + __popc(S.mark[word] & ((1u << (r_e & 31)) - 1u));
-    S.w[slot][tid / k] = r_w;
-  }
-  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
@@ -134,11 +142,11 @@ DEVI void build_slots(SlotLds& S, int r_e, float r_w, int tk, int k, int T, int 
 constexpr int GU_NW = 8;    // wavefronts per workgroup
 constexpr int GU_WIN = 96;  // activation blocks staged in LDS at once
 
-struct GuLds {
-  unsigned char xs[GU_WIN * 1024];  // A-fragments, [block][lane][8] fp16
-  float cs[GU_WIN * 16];            // accumulator seeds, [block][16]
+struct alignas(16) GuLds {
+  alignas(16) unsigned char xs[GU_WIN * 1024];  // A-fragments, [block][lane][8] fp16
+  alignas(16) float cs[GU_WIN * 16];  // accumulator seeds, [block][16]
   float red[GU_NW][8][64];          // partial sums of the k-parts
-  float rn[8];                      // rms of each token
+  float rn[8];                      // 1 / rms of each token
   SlotLds S;
 };
 
@@ -241,15 +249,10 @@ __global__ __launch_bounds__(64 * GU_NW) void gu_decode_kernel(GuArgs a) {
   const int n_win = (8 * n_kg + GU_WIN - 1) / GU_WIN;
   const int win_kg = (n_kg + n_win - 1) / n_win;  // k-groups per window
 
-  int r_e = -1;
-  float r_w = 0.f;
-  if (tid < tk) {
-    r_e = a.idx[tid];
-    r_w = a.w[tid];
-  }
-  if (tid < 8) L.rn[tid] = tid < T ? a.rnorm[tid] : 1.0f;
+  if (wv == 0) build_slots_wave(L.S, a.idx, a.w, tk, k, T, E, has_shared);
+  if (tid >= 64 && tid < 72) L.rn[tid - 64] = tid - 64 < T ? 1.0f / a.rnorm[tid - 64] : 1.0f;
   if (n_win == 1) stage_window(L, a, 0, 8 * n_kg, tid);
-  build_slots(L.S, r_e, r_w, tk, k, T, E, has_shared);  // its barriers also publish the staging and rms
+  __syncthreads();  // slot list, rms and the staged activations
   if (blockIdx.x == 0) {
     const int ns = base + L.S.n_routed;
     if (tid == 0) *a.n_slots = ns;
@@ -323,10 +326,10 @@ __global__ __launch_bounds__(64 * GU_NW) void gu_decode_kernel(GuArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int tok = tok_e + i;
         const float gw = (u == 0 && has_shared) ? (tok < T ? 1.0f : 0.f) : L.S.w[u][tok];
-        const float rn = L.rn[tok];
-        const float g = add_partner32(accg[i]) / rn;
-        const float uu = add_partner32(accu[i]) / rn;
-        const float hv = g / (1.0f + expf(-g)) * uu;
+        const float rrn = L.rn[tok];  // 1 / rms
+        const float g = add_partner32(accg[i]) * rrn;
+        const float uu = add_partner32(accu[i]) * rrn;
+        const float hv = g * __builtin_amdgcn_rcpf(1.0f + expf(-g)) * uu;
         const float hs = (gw != 0.f) ? gw * hv : 0.f;
         const _Float16 hi = (_Float16)hs;
         const _Float16 val = lo_half ? (_Float16)(hs - (float)hi) : hi;
