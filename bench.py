@@ -150,7 +150,11 @@ def bench_prefill(args):
     def run_pass():
         bqe.moe_layer_forward(L.handle, x, y, ws, rio)
 
+    if args.timing_only:
+        bqe.moe_timing_start(bqe.TIMING_PREFILL_ROUTER, 1)
     run_pass()
+    if args.timing_only:
+        bqe.moe_timing_stop()
     torch.cuda.synchronize()
     idx_np = idx.cpu().numpy()
     kdur = {}
@@ -164,6 +168,10 @@ def bench_prefill(args):
             tot += ms
             n += cnt
         kdur[name] = (tot / n) * 1e-3
+
+    if args.timing_only:
+        print(json.dumps({"timing_only": wl.name, "kernels_avg_us": {n: kdur[n] * 1e6 for n in kdur}}))
+        return
 
     graph = None
     if not args.no_graph:
@@ -360,6 +368,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=3, help="oracle sample size in layers (0 = skip)")
     ap.add_argument("--cpu-tokens", type=int, default=16, help="prefill: oracle sample size in tokens (0 = skip)")
+    ap.add_argument("--timing-only", action="store_true",
+                    help="only the per-kernel timing passes (every launch serialized), for profiler runs")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -415,8 +425,13 @@ def main():
         else:
             bqe.moe_stack_forward(handles, x, y, ws, 1e-6)
 
-    # eager warm-up (also initialises the library before any capture)
+    # eager warm-up (also initialises the library before any capture); with
+    # --timing-only it runs with the launches serialized like the timed passes
+    if args.timing_only:
+        bqe.moe_timing_start(bqe.TIMING_ROUTER, 1)
     run_pass(True)
+    if args.timing_only:
+        bqe.moe_timing_stop()
     torch.cuda.synchronize()
     idx_np = idx_l.cpu().numpy()
 
@@ -432,6 +447,10 @@ def main():
             tot += ms
             n += cnt
         kdur[name] = (tot / n) * 1e-3  # seconds per launch
+
+    if args.timing_only:
+        print(json.dumps({"timing_only": wl.name, "kernels_avg_us": {n: kdur[n] * 1e6 for n in kdur}}))
+        return
 
     graph = None
     if not args.no_graph:

@@ -368,8 +368,18 @@ __global__ __launch_bounds__(512) void down_decode_kernel(DownArgs a) {
   // there is one (split 0 then starts with its k-groups)
   const bool sh_here = a.has_shared && sp == 0;
   const int first_r = sh_here ? S : sp;  // first routed slot of the split
-  const int n_rs = (first_r < ns) ? (ns - first_r + S - 1) / S : 0;
   const int n_sh = sh_here ? a.n_kg_s : 0;
+  // expert ids of this wave's first batch, fetched together with n_slots
+  // (the slot of an item does not depend on n_slots; ids past the list are
+  // clamped to a valid expert and never used)
+  int pre[BATCH];
+#pragma unroll
+  for (int q = 0; q < BATCH; ++q) {
+    const int it = wv + q * nw;
+    const int u = (it < n_sh) ? 0 : first_r + S * ((it - n_sh) / a.n_kg_r);
+    pre[q] = a.slot_expert[min(u, a.max_slots - 1)];
+  }
+  const int n_rs = (first_r < ns) ? (ns - first_r + S - 1) / S : 0;
   const int n_items = n_sh + n_rs * a.n_kg_r;
 
   float4_t acc[RT];
@@ -398,7 +408,9 @@ __global__ __launch_bounds__(512) void down_decode_kernel(DownArgs a) {
         u = first_r + S * (ri / a.n_kg_r);
         kg = ri % a.n_kg_r;
         n_kg = a.n_kg_r;
-        mat = a.X.experts + (int64_t)a.slot_expert[u] * a.X.ex_stride + a.X.off_down;
+        int e = (b0 == wv) ? (ok[q] ? pre[q] : pre[0]) : a.slot_expert[u];
+        e = min(max(e, 0), a.E - 1);
+        mat = a.X.experts + (int64_t)e * a.X.ex_stride + a.X.off_down;
       }
       load_chunk<BITS>(c[q], mat + ((int64_t)rg * n_kg + kg) * CB, lane);
 #pragma unroll
@@ -446,15 +458,15 @@ __global__ __launch_bounds__(512) void down_decode_kernel(DownArgs a) {
 
 template <int BITS, int RT>
 hipError_t launch_down_t(const DownArgs& a, int grid_x, int nw, hipStream_t s) {
-  hipLaunchKernelGGL((down_decode_kernel<BITS, RT>), dim3(grid_x, a.S), dim3(64 * nw), 0, s, a);
+  MOE_LAUNCH((down_decode_kernel<BITS, RT>), dim3(grid_x, a.S), dim3(64 * nw), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gu_decode(const GuArgs& a, int n_wg, hipStream_t s) {
-  if (a.bits == 2) hipLaunchKernelGGL(gu_decode_kernel<2>, dim3(n_wg), dim3(64 * GU_NW), 0, s, a);
-  else hipLaunchKernelGGL(gu_decode_kernel<3>, dim3(n_wg), dim3(64 * GU_NW), 0, s, a);
+  if (a.bits == 2) MOE_LAUNCH(gu_decode_kernel<2>, dim3(n_wg), dim3(64 * GU_NW), 0, s, a);
+  else MOE_LAUNCH(gu_decode_kernel<3>, dim3(n_wg), dim3(64 * GU_NW), 0, s, a);
   return hipGetLastError();
 }
 

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -16,6 +17,8 @@
 #include "../../include/moe.h"
 #include "moe_internal.h"
 #include "moe_launch.h"
+
+thread_local MoeLaunchEvents moe_launch_events;
 
 namespace {
 
@@ -156,8 +159,10 @@ int64_t ctrl_bytes() { return 256; }
 
 int down_splits(const moe_layer* L, int max_slots) {
   const int n_rg = L->ex.down.n_rg;
+  // the down kernel's workgroups (512 threads) fit two per CU: one round of
+  // n_rg * S workgroups when S = 2 CUs / n_rg
   int S = env_int("MOE_DOWN_SPLITS", 0);
-  if (S <= 0) S = (512 + n_rg - 1) / n_rg;
+  if (S <= 0) S = (2 * cu_count()) / n_rg;
   if (S > max_slots) S = max_slots;
   if (S > MOE_MAX_IN_SPLITS) S = MOE_MAX_IN_SPLITS;
   if (S < 1) S = 1;
@@ -248,22 +253,35 @@ PfLayout ws_layout_prefill(const moe_layer* L, int T) {
 // ---------------------------------------------------------------- timing ---
 struct Timing {
   std::mutex mu;
-  int cls = -1;
+  std::atomic<int> cls{-1};
   int max = 0;
   int used = 0;
   std::vector<hipEvent_t> ev;
 } g_timing;
 
+// While per-kernel timing is enabled every launch of the layer functions
+// waits for the stream to drain, so each kernel runs alone (events and
+// profiler time stamps then cover one kernel each).
+void serial_point(hipStream_t s) {
+  if (g_timing.cls >= 0) hipStreamSynchronize(s);
+}
+
+// The timed launch records its own start and stop events (the dispatch's
+// time stamps), so no marker sits between it and the preceding kernel.
 void timed_begin(int cls, hipStream_t s, int* slot) {
+  (void)s;
   *slot = -1;
   if (g_timing.cls != cls) return;
   std::lock_guard<std::mutex> lk(g_timing.mu);
   if (g_timing.cls != cls || g_timing.used >= g_timing.max) return;
   *slot = g_timing.used++;
-  hipEventRecord(g_timing.ev[2 * *slot], s);
+  moe_launch_events.start = g_timing.ev[2 * *slot];
+  moe_launch_events.stop = g_timing.ev[2 * *slot + 1];
 }
 void timed_end(int slot, hipStream_t s) {
-  if (slot >= 0) hipEventRecord(g_timing.ev[2 * slot + 1], s);
+  (void)slot;
+  (void)s;
+  moe_launch_events = MoeLaunchEvents{};
 }
 
 ExpertSet expert_set(const moe_layer* L) {
@@ -315,6 +333,7 @@ int decode_layer(const moe_layer* L, const LayerInput& in, float eps, int T, flo
   ra.xsum = reinterpret_cast<float*>(ws + W.xsum);
   ra.y_out = y_prev_out;
   timed_begin(2, s, &slot);
+  serial_point(s);
   HIPCHK(launch_route(ra, s));
   timed_end(slot, s);
 
@@ -339,6 +358,7 @@ int decode_layer(const moe_layer* L, const LayerInput& in, float eps, int T, flo
   sa.out_logits = (r && !forced) ? r->out_logits : nullptr;
   sa.out_idx = r ? r->out_idx : nullptr;
   sa.out_w = r ? r->out_w : nullptr;
+  serial_point(s);
   HIPCHK(launch_select(sa, s));
 
   const ExpertSet X = expert_set(L);
@@ -372,6 +392,7 @@ int decode_layer(const moe_layer* L, const LayerInput& in, float eps, int T, flo
     if (n_wg > max_items) n_wg = max_items;
     if (n_wg < 1) n_wg = 1;
     timed_begin(0, s, &slot);
+    serial_point(s);
     HIPCHK(launch_gu_decode(ga, n_wg, s));
   }
   timed_end(slot, s);
@@ -393,10 +414,12 @@ int decode_layer(const moe_layer* L, const LayerInput& in, float eps, int T, flo
   da.n_kg_s = L->Is > 0 ? L->sh.down.n_kg : 0;
   da.S = W.S;
   da.has_shared = L->Is > 0;
+  da.max_slots = W.max_slots;
   da.ypart = reinterpret_cast<float*>(ws + W.ypart);
   int dn_nw = env_int("MOE_DOWN_WAVES", 8);
   if (dn_nw <= 0 || dn_nw > 8) dn_nw = 8;
   timed_begin(1, s, &slot);
+  serial_point(s);
   HIPCHK(launch_down_decode(da, L->ex.down.n_rg, dn_nw, s));
   timed_end(slot, s);
   *S_out = W.S;
@@ -421,6 +444,7 @@ int prefill_layer(const moe_layer* L, const float* x, int norm, float eps, int T
   pa.ex = reinterpret_cast<int32_t*>(ws + W.ex);
   pa.xh = reinterpret_cast<_Float16*>(ws + W.xh);
   pa.xl = reinterpret_cast<_Float16*>(ws + W.xl);
+  serial_point(s);
   HIPCHK(launch_pf_prep(pa, s));
 
   const int32_t* idx;
@@ -435,17 +459,20 @@ int prefill_layer(const moe_layer* L, const float* x, int norm, float eps, int T
     ra.ex = pa.ex;
     ra.wh = L->router_wh;
     ra.wl = L->router_wl;
-      ra.bias = L->router_b;
+    ra.ew = L->router_ew;
+    ra.bias = L->router_b;
     ra.T = T;
     ra.d = d;
     ra.E = E;
     ra.E16 = L->E16;
     ra.logits = (r && r->out_logits) ? r->out_logits : reinterpret_cast<float*>(ws + W.logits);
     timed_begin(5, s, &slot);
+    serial_point(s);
     HIPCHK(launch_pf_router(ra, s));
     timed_end(slot, s);
     int32_t* oi = (r && r->out_idx) ? r->out_idx : reinterpret_cast<int32_t*>(ws + W.idx);
     float* ow = (r && r->out_w) ? r->out_w : reinterpret_cast<float*>(ws + W.w);
+    serial_point(s);
     HIPCHK(launch_topk(ra.logits, T, E, k, oi, ow, s));
     idx = oi;
     w = ow;
@@ -476,6 +503,7 @@ int prefill_layer(const moe_layer* L, const float* x, int norm, float eps, int T
   ga.item_row0 = reinterpret_cast<int32_t*>(ws + W.item_row0);
   ga.item_rows = reinterpret_cast<int32_t*>(ws + W.item_rows);
   ga.R_fill = 0;
+  serial_point(s);
   HIPCHK(launch_pf_group(ga, s));
 
   PfGemmArgs ma{};
@@ -500,9 +528,11 @@ int prefill_layer(const moe_layer* L, const float* x, int norm, float eps, int T
   ma.hb = L->hbound;
   ma.ypart = reinterpret_cast<float*>(ws + W.ypart);
   timed_begin(3, s, &slot);
+  serial_point(s);
   HIPCHK(launch_pf_gate_up(ma, L->bits, W.max_items, s));
   timed_end(slot, s);
   timed_begin(4, s, &slot);
+  serial_point(s);
   HIPCHK(launch_pf_down(ma, L->bits, L->ex.down.BK, W.max_items, s));
   timed_end(slot, s);
 
@@ -516,6 +546,7 @@ int prefill_layer(const moe_layer* L, const float* x, int norm, float eps, int T
   ca.E = E;
   ca.has_shared = L->Is > 0;
   ca.y = y;
+  serial_point(s);
   HIPCHK(launch_pf_combine(ca, s));
   return MOE_OK;
 }
@@ -773,6 +804,7 @@ int moe_stack_forward(const moe_layer* const* layers, int n_layers, const float*
     const WsLayout W = ws_layout_decode(layers[l], T);
     in = LayerInput{reinterpret_cast<const float*>(wsb + W.ypart), S, (int64_t)8 * d, 1};
   }
+  serial_point(s);
   HIPCHK(launch_combine(in.p, in.S, in.stride, T, d, y, s));
   if (y_layers)
     HIPCHK(hipMemcpyAsync(y_layers + (size_t)(n_layers - 1) * T * d, y, (size_t)T * d * 4, hipMemcpyDeviceToDevice, s));

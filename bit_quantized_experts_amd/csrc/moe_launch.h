@@ -1,6 +1,7 @@
 // moe_launch.h -- kernel argument blocks and host-side launchers.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 #include "moe_internal.h"
@@ -86,7 +87,7 @@ struct DownArgs {
   const int32_t* slot_expert;
   const _Float16* hfrag;
   const float* hsum;
-  int32_t E, d, T, bits, nbI, BK, RT, n_kg_r, n_kg_s, S, has_shared;
+  int32_t E, d, T, bits, nbI, BK, RT, n_kg_r, n_kg_s, S, has_shared, max_slots;
   float* ypart;  // ws [S][8][d]
 };
 
@@ -191,3 +192,20 @@ hipError_t launch_pf_group(const PfGroupArgs& a, hipStream_t s);
 hipError_t launch_pf_gate_up(const PfGemmArgs& a, int bits, int max_items, hipStream_t s);
 hipError_t launch_pf_down(const PfGemmArgs& a, int bits, int bk, int max_items, hipStream_t s);
 hipError_t launch_pf_combine(const PfCombineArgs& a, hipStream_t s);
+
+// Events that the next launch of the kernel class being timed records itself
+// (start and end of its dispatch, as a profiler sees them); null otherwise.
+// Set by the host code around one launch, never during graph capture.
+struct MoeLaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+extern thread_local MoeLaunchEvents moe_launch_events;
+
+#define MOE_LAUNCH(K, grid, block, shmem, s, ...)                                                        \
+  do {                                                                                                   \
+    if (moe_launch_events.start)                                                                         \
+      hipExtLaunchKernelGGL(K, grid, block, shmem, s, moe_launch_events.start, moe_launch_events.stop, 0, \
+                            __VA_ARGS__);                                                                \
+    else                                                                                                 \
+      hipLaunchKernelGGL(K, grid, block, shmem, s, __VA_ARGS__);                                         \
+  } while (0)

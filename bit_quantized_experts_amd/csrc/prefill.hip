@@ -900,7 +900,7 @@ hipError_t launch_pf_prep(const PfPrepArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_pf_router(const PfRouterArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(pf_router_kernel, dim3((a.T + 127) / 128, (a.E16 + PF_ET - 1) / PF_ET), dim3(256), 0, s, a);
+  MOE_LAUNCH(pf_router_kernel, dim3((a.T + 127) / 128, (a.E16 + PF_ET - 1) / PF_ET), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -917,14 +917,14 @@ hipError_t launch_pf_group(const PfGroupArgs& a, hipStream_t s) {
 
 hipError_t launch_pf_gate_up(const PfGemmArgs& a, int bits, int max_items, hipStream_t s) {
   const dim3 grid((unsigned)((max_items + N_XCD - 1) / N_XCD * N_XCD * a.n_nt));
-  if (bits == 2) hipLaunchKernelGGL(pf_gate_up_kernel<2>, grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(pf_gate_up_kernel<3>, grid, dim3(256), 0, s, a);
+  if (bits == 2) MOE_LAUNCH(pf_gate_up_kernel<2>, grid, dim3(256), 0, s, a);
+  else MOE_LAUNCH(pf_gate_up_kernel<3>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_pf_down(const PfGemmArgs& a, int bits, int bk, int max_items, hipStream_t s) {
   const dim3 grid((unsigned)((max_items + N_XCD - 1) / N_XCD * N_XCD * (a.d / PF_DT)));
-#define PF_DOWN(B, K) hipLaunchKernelGGL((pf_down_kernel<B, K>), grid, dim3(256), 0, s, a)
+#define PF_DOWN(B, K) MOE_LAUNCH((pf_down_kernel<B, K>), grid, dim3(256), 0, s, a)
   if (bits == 2) {
     switch (bk) {
       case 8: PF_DOWN(2, 8); break;

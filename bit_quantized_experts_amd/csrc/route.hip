@@ -442,7 +442,7 @@ __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   const dim3 grid(a.d / MOE_ROUTE_COLS, a.do_logits ? (a.E + MOE_ROUTE_ROWS - 1) / MOE_ROUTE_ROWS : 1);
-  hipLaunchKernelGGL(route_kernel, grid, dim3(256), 0, s, a);
+  MOE_LAUNCH(route_kernel, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

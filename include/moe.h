@@ -205,8 +205,11 @@ int moe_debug_unpack(const moe_layer *layer, int expert, int mat, int8_t *codes,
                      uint16_t *w_f16, void *stream);
 
 /* Per-kernel timing for measurement: while enabled, the library brackets
- * every launch of the chosen kernel class with a pair of HIP events on the
- * launch stream.  class 0 = decode gate/up expert kernel, 1 = decode down
+ * every launch of the chosen kernel class with a pair of HIP events that the
+ * launch records itself (the start and end of its dispatch), and every
+ * kernel of the layer functions waits for the stream to drain on the host
+ * first, so each runs alone (it must not be enabled while a graph is being
+ * captured).  class 0 = decode gate/up expert kernel, 1 = decode down
  * expert kernel, 2 = decode router, 3 = prefill gate/up grouped GEMM, 4 =
  * prefill down grouped GEMM, 5 = prefill router GEMM.  moe_timing_stop waits
  * for the recorded events and returns the summed duration and the number of
