@@ -142,7 +142,7 @@ PackedLayout packed_layout(const moe_layer_desc* D, const moe_expert_layout& ex,
   P.off_rwl = P.off_rwh + moe_align256(E16 * D->d_model * 2);
   P.off_rew = P.off_rwl + moe_align256(E16 * D->d_model * 2);
   P.off_hb = P.off_rew + moe_align256(E16 * 4);
-  P.off_ex = P.off_hb + moe_align256((int64_t)(D->n_experts + 1) * 4);
+  P.off_ex = P.off_hb + moe_align256((int64_t)(D->n_experts + 1) * 8);  // hb then ed
   P.off_sh = P.off_ex + (int64_t)D->n_experts * ex.bytes;
   P.total = P.off_sh + (D->d_ff_shared > 0 ? sh.bytes : 0);
   return P;
@@ -202,7 +202,7 @@ WsLayout ws_layout_decode(const moe_layer* L, int T) {
 // expert (padded to 16).
 struct PfLayout {
   int64_t ctrl, ex, xh, xl, logits, idx, w, tile_bm, tile_cnt, counts, offsets, n_items, item_group, item_row0,
-      item_rows, row_src, row_tok, row_w, slot_pos, hfrag, ypart, total;
+      item_rows, row_src, row_tok, row_w, slot_pos, hfrag, ypart, rowf, total;
   int n_tiles, R, max_items, nbH, n_nt;
 };
 
@@ -245,7 +245,8 @@ PfLayout ws_layout_prefill(const moe_layer* L, int T) {
   W.row_w = take((int64_t)W.R * 4);
   W.slot_pos = take(pairs * 4);
   W.hfrag = take((int64_t)W.R * Imax * 2);
-  W.ypart = take((int64_t)W.R * d * 4);
+  W.ypart = take((int64_t)W.R * d * 2);  // fp16 down rows
+  W.rowf = take((int64_t)W.R * 4);
   W.total = o;
   return W;
 }
@@ -526,7 +527,9 @@ int prefill_layer(const moe_layer* L, const float* x, int norm, float eps, int T
   ma.R = W.R;
   ma.hfrag = reinterpret_cast<_Float16*>(ws + W.hfrag);
   ma.hb = L->hbound;
-  ma.ypart = reinterpret_cast<float*>(ws + W.ypart);
+  ma.ed = L->dbound;
+  ma.yh = reinterpret_cast<_Float16*>(ws + W.ypart);
+  ma.rowf = reinterpret_cast<float*>(ws + W.rowf);
   timed_begin(3, s, &slot);
   serial_point(s);
   HIPCHK(launch_pf_gate_up(ma, L->bits, W.max_items, s));
@@ -537,7 +540,8 @@ int prefill_layer(const moe_layer* L, const float* x, int norm, float eps, int T
   timed_end(slot, s);
 
   PfCombineArgs ca{};
-  ca.ypart = ma.ypart;
+  ca.yh = ma.yh;
+  ca.rowf = ma.rowf;
   ca.slot_pos = ga.slot_pos;
   ca.offsets = ga.offsets;
   ca.T = T;
@@ -619,6 +623,7 @@ int moe_pack_experts(const moe_layer_desc* desc, const void* experts_canon, cons
   L->router_wl = reinterpret_cast<const _Float16*>(base + P.off_rwl);
   L->router_ew = reinterpret_cast<const int32_t*>(base + P.off_rew);
   L->hbound = reinterpret_cast<const int32_t*>(base + P.off_hb);
+  L->dbound = L->hbound + (L->E + 1);
   L->E16 = e16_of(L->E);
   L->experts = base + P.off_ex;
   L->shared = L->Is > 0 ? base + P.off_sh : nullptr;
@@ -641,14 +646,19 @@ int moe_pack_experts(const moe_layer_desc* desc, const void* experts_canon, cons
   const int64_t bb = canon_block_bytes(L->bits);
   {
     int32_t* hb = const_cast<int32_t*>(L->hbound);
+    int32_t* edp = const_cast<int32_t*>(L->dbound);
     const int64_t stride = 3 * (int64_t)L->I * (L->d / 32) * bb;
-    if ((e = launch_pack_hbound(reinterpret_cast<const uint8_t*>(experts_canon), stride, L->E, L->I, L->d, L->bits, hb, s)) != hipSuccess)
+    if ((e = launch_pack_hbound(reinterpret_cast<const uint8_t*>(experts_canon), stride, L->E, L->I, L->d, L->bits, hb,
+                                edp, s)) != hipSuccess)
       return bail(fail(MOE_ERR_HIP, "bound: %s", hipGetErrorString(e)));
     if (L->Is > 0) {
-      if ((e = launch_pack_hbound(reinterpret_cast<const uint8_t*>(shared_canon), 0, 1, L->Is, L->d, L->bits, hb + L->E, s)) != hipSuccess)
+      if ((e = launch_pack_hbound(reinterpret_cast<const uint8_t*>(shared_canon), 0, 1, L->Is, L->d, L->bits, hb + L->E,
+                                  edp + L->E, s)) != hipSuccess)
         return bail(fail(MOE_ERR_HIP, "bound: %s", hipGetErrorString(e)));
-    } else if ((e = launch_fill_u32(reinterpret_cast<uint32_t*>(hb + L->E), 1, 0u, s)) != hipSuccess) {
-      return bail(fail(MOE_ERR_HIP, "bound fill: %s", hipGetErrorString(e)));
+    } else {
+      if ((e = launch_fill_u32(reinterpret_cast<uint32_t*>(hb + L->E), 1, 0u, s)) != hipSuccess ||
+          (e = launch_fill_u32(reinterpret_cast<uint32_t*>(edp + L->E), 1, 0u, s)) != hipSuccess)
+        return bail(fail(MOE_ERR_HIP, "bound fill: %s", hipGetErrorString(e)));
     }
   }
   auto pack_expert = [&](const uint8_t* canon, int I, const moe_expert_layout& X, uint8_t* dst, int n) -> hipError_t {

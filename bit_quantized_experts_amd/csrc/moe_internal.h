@@ -57,6 +57,7 @@ struct moe_layer {
   const _Float16* router_wl;  // same, lo part
   const int32_t* router_ew;   // device [E16] row exponents
   const int32_t* hbound;      // device [E + 1] exponent base of the intermediate rows (E: shared)
+  const int32_t* dbound;      // device [E + 1] exponent of the prefill down rows (E: shared)
   int32_t E16;                // E rounded up to a multiple of 16
   const uint8_t* experts; // device, E * ex.bytes
   const uint8_t* shared;  // device, sh.bytes or null

@@ -170,13 +170,16 @@ struct PfGemmArgs {
   const int32_t* item_row0;
   const int32_t* item_rows;
   const int32_t* hb;  // [E + 1] per-expert exponent base of the intermediate rows (index E: shared)
+  const int32_t* ed;  // [E + 1] per-expert exponent of the down rows (index E: shared)
   int32_t T, d, E, I, Is, nbH, n_nt, R;
   _Float16* hfrag;   // [R/16][nbH][64][8] intermediate rows, fp16(h * 2^-(hb + 2 ex))
-  float* ypart;      // [R][d] down outputs times the gate weight
+  _Float16* yh;      // [R][d] down rows, fp16(sum * 2^-ed)
+  float* rowf;       // [R] factor of each down row: w * 2^(hb + 2 ex + ed)
 };
 
 struct PfCombineArgs {
-  const float* ypart;
+  const _Float16* yh;
+  const float* rowf;
   const int32_t* slot_pos;
   const int32_t* offsets;  // offsets[E] = first shared row
   int32_t T, d, k, E, has_shared;
@@ -185,7 +188,7 @@ struct PfCombineArgs {
 
 hipError_t launch_pack_router(const float* W, int E, int d, _Float16* wh, _Float16* wl, int32_t* ew, hipStream_t s);
 hipError_t launch_pack_hbound(const uint8_t* canon, int64_t canon_stride, int n_experts, int I, int d, int bits,
-                              int32_t* hb, hipStream_t s);
+                              int32_t* hb, int32_t* ed, hipStream_t s);
 hipError_t launch_pf_prep(const PfPrepArgs& a, hipStream_t s);
 hipError_t launch_pf_router(const PfRouterArgs& a, hipStream_t s);
 hipError_t launch_pf_group(const PfGroupArgs& a, hipStream_t s);

@@ -25,11 +25,14 @@
 //             pack time from the row L1 norms of gate and up, so no pass over
 //             the row is needed to choose it;
 //   down      per item and 256 output columns: Y = H W_d^T with H staged into
-//             LDS by direct-to-LDS loads; the epilogue multiplies by the gate
-//             weight times 2^eh and writes one fp32 row per pair;
-//   combine   y[t] = sum of its pairs' rows in rank order + its shared row.
+//             LDS by direct-to-LDS loads; the epilogue writes one fp16 row
+//             per pair, fp16(sum 2^-ed) with ed a per-expert pack-time bound,
+//             and the row's factor w 2^(eh + ed);
+//   combine   y[t] = sum of its pairs' factor times row in rank order + its
+//             shared row.
 // Every product on the matrix cores is exact; the roundings are the fp16
-// activations (x, h), 3-bit weights with a code of +-3, and fp32 accumulation.
+// activations (x, h), 3-bit weights with a code of +-3, the fp16 down rows,
+// and fp32 accumulation.
 #include <type_traits>
 
 #include "kern_common.h"
@@ -147,26 +150,29 @@ __global__ __launch_bounds__(256) void pack_router_kernel(const float* W, int E,
 }
 
 // ---------------------------------------------------------------------------
-// Exponent base of the intermediate rows of one expert, prepared at pack
-// time: Lg = max over gate rows of sum_j |w_ij|, Lu likewise for up.  For an
-// input row scaled to |x_j| < 2^15 (x times 2^-ex), |g| <= Lg 2^(15 + ex),
+// Exponent bases of one expert, prepared at pack time.  Lg = max over gate
+// rows of sum_j |w_ij|, Lu likewise for up, Ld for down.  For an input row
+// scaled to |x_j| < 2^15 (x times 2^-ex), |g| <= Lg 2^(15 + ex),
 // |u| <= Lu 2^(15 + ex) and |silu(g) u| <= |g| |u|, so with 2^e > Lg Lu the
 // value h 2^-(hb + 2 ex) with hb = e + 16 is below 2^14 (2^15 allowing for
 // the fp32 rounding of the sums): the fp16 intermediate needs no pass over
-// the row to choose its exponent.  One workgroup per expert.
+// the row to choose its exponent.  The down sums over such fp16 values are
+// below 2^15 Ld, so with 2^ed > Ld they are stored as fp16(sum 2^-ed), below
+// 2^15.  One workgroup per expert.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void pack_hbound_kernel(const uint8_t* canon, int64_t stride, int I, int d, int bits,
-                                                          int32_t* hb) {
-  __shared__ float red[2][4];
+                                                          int32_t* hb, int32_t* ed) {
+  __shared__ float red[3][4];
   const uint8_t* ex = canon + (int64_t)blockIdx.x * stride;
-  const int nb = d / 32, bb = 2 + 4 * bits, off = 1 << (bits - 1);
-  float lmax[2] = {0.f, 0.f};
-  for (int m = 0; m < 2; ++m) {
+  const int nb = d / 32, nbI = I / 32, bb = 2 + 4 * bits, off = 1 << (bits - 1);
+  float lmax[3] = {0.f, 0.f, 0.f};
+  for (int m = 0; m < 3; ++m) {
     const uint8_t* mat = ex + (int64_t)m * I * nb * bb;
-    for (int i = threadIdx.x; i < I; i += 256) {
+    const int nrow = m < 2 ? I : d, nblk = m < 2 ? nb : nbI;
+    for (int i = threadIdx.x; i < nrow; i += 256) {
       float sum = 0.f;
-      for (int b = 0; b < nb; ++b) {
-        const uint8_t* B = mat + ((int64_t)i * nb + b) * bb;
+      for (int b = 0; b < nblk; ++b) {
+        const uint8_t* B = mat + ((int64_t)i * nblk + b) * bb;
         const float sc = fabsf(half_bits_to_float((uint32_t)B[0] | ((uint32_t)B[1] << 8)));
         int cs = 0;
         for (int j = 0; j < 32; ++j) {
@@ -180,18 +186,21 @@ __global__ __launch_bounds__(256) void pack_hbound_kernel(const uint8_t* canon, 
     }
   }
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int m = 0; m < 2; ++m) {
+  for (int m = 0; m < 3; ++m) {
     const float v = wave_maxf(lmax[m]);
     if (lane == 0) red[m][wv] = v;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    const float lg = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
-    const float lu = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
-    const float p = lg * lu;
+    float l[3];
+    for (int m = 0; m < 3; ++m) l[m] = fmaxf(fmaxf(red[m][0], red[m][1]), fmaxf(red[m][2], red[m][3]));
+    const float p = l[0] * l[1];
     int e = 0;
     if (p > 0.f) frexpf(p, &e);  // p < 2^e
     hb[blockIdx.x] = e + 16;
+    int e2 = 0;
+    if (l[2] > 0.f) frexpf(l[2], &e2);  // Ld < 2^e2
+    ed[blockIdx.x] = e2;
   }
 }
 
@@ -748,8 +757,11 @@ DEVI void down_item(const PfGemmArgs& a, const Stages& S, float* rowf_lds, int g
   const int nrg = rows >> 4;
   if (tid < rows) {
     const int tok = a.row_tok[row0 + tid];
-    rowf_lds[tid] = ldexpf(a.row_w[row0 + tid], a.hb[g] + 2 * a.ex[tok]);
+    const float f = ldexpf(a.row_w[row0 + tid], a.hb[g] + 2 * a.ex[tok] + a.ed[g]);
+    rowf_lds[tid] = f;
+    if (nt == 0) a.rowf[row0 + tid] = f;
   }
+  const int ed = a.ed[g];
 
   float4_t acc[NRG][4];
 #pragma unroll
@@ -829,16 +841,24 @@ DEVI void down_item(const PfGemmArgs& a, const Stages& S, float* rowf_lds, int g
     if (s + 1 < nsteps) step(ic<1>{}, s + 1);
     if (s + 2 < nsteps) step(ic<2>{}, s + 2);
   }
+  // rows stored as fp16(sum 2^-ed) (below 2^15, see the pack-time bound);
+  // the combine multiplies them by rowf = w 2^(hb + 2 ex + ed).  Columns n
+  // and n + 1 (lanes n, n ^ 1) share one dword.
+  (void)rowf_lds;
 #pragma unroll
   for (int rg = 0; rg < NRG; ++rg)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * rg + 4 * q + i;
-      if (r >= rows) continue;
-      const float f = rowf_lds[r];
-      float* yrow = a.ypart + (size_t)(row0 + r) * a.d + r0 + n;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) yrow[16 * t] = acc[rg][t][i] * f;
+      for (int t = 0; t < 4; ++t) {
+        const _Float16 v = (_Float16)ldexpf(acc[rg][t][i], -ed);
+        uint16_t vb;
+        __builtin_memcpy(&vb, &v, 2);
+        const uint32_t nb2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)vb, 0xB1, 0xF, 0xF, true);  // lane n ^ 1
+        if (r < rows && (n & 1) == 0)
+          *reinterpret_cast<uint32_t*>(a.yh + (size_t)(row0 + r) * a.d + r0 + n + 16 * t) = (uint32_t)vb | (nb2 << 16);
+      }
     }
 }
 
@@ -862,19 +882,31 @@ __global__ __launch_bounds__(256) void pf_down_kernel(PfGemmArgs a) {
 // ---------------------------------------------------------------------------
 // combine: y[t] = sum over the token's used pairs in rank order + shared row.
 // ---------------------------------------------------------------------------
+DEVI float4_t half4_to_float4(const _Float16* p) {
+  typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+  const half4_t h = *reinterpret_cast<const half4_t*>(p);
+  return float4_t{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+}
+
 __global__ __launch_bounds__(256) void pf_combine_kernel(PfCombineArgs a) {
   __shared__ int pos[MOE_MAX_K + 1];
   const int t = blockIdx.x;
   if (threadIdx.x < a.k) pos[threadIdx.x] = a.slot_pos[(size_t)t * a.k + threadIdx.x];
   if (threadIdx.x == 0) pos[MOE_MAX_K] = a.has_shared ? a.offsets[a.E] + t : -1;
   __syncthreads();
+  __shared__ float f[MOE_MAX_K + 1];
+  if (threadIdx.x <= MOE_MAX_K) {
+    const int p = threadIdx.x < a.k ? pos[threadIdx.x] : (threadIdx.x == MOE_MAX_K ? pos[MOE_MAX_K] : -1);
+    f[threadIdx.x] = p >= 0 ? a.rowf[p] : 0.f;
+  }
+  __syncthreads();
   for (int c = 4 * threadIdx.x; c < a.d; c += 1024) {
     float4_t acc = float4_t{0.f, 0.f, 0.f, 0.f};
     for (int r = 0; r < a.k; ++r) {
       const int p = pos[r];
-      if (p >= 0) acc += *reinterpret_cast<const float4_t*>(a.ypart + (size_t)p * a.d + c);
+      if (p >= 0) acc += f[r] * half4_to_float4(a.yh + (size_t)p * a.d + c);
     }
-    if (pos[MOE_MAX_K] >= 0) acc += *reinterpret_cast<const float4_t*>(a.ypart + (size_t)pos[MOE_MAX_K] * a.d + c);
+    if (pos[MOE_MAX_K] >= 0) acc += f[MOE_MAX_K] * half4_to_float4(a.yh + (size_t)pos[MOE_MAX_K] * a.d + c);
     *reinterpret_cast<float4_t*>(a.y + (size_t)t * a.d + c) = acc;
   }
 }
@@ -888,9 +920,9 @@ hipError_t launch_pack_router(const float* W, int E, int d, _Float16* wh, _Float
 }
 
 hipError_t launch_pack_hbound(const uint8_t* canon, int64_t canon_stride, int n_experts, int I, int d, int bits,
-                              int32_t* hb, hipStream_t s) {
+                              int32_t* hb, int32_t* ed, hipStream_t s) {
   if (n_experts <= 0) return hipSuccess;
-  hipLaunchKernelGGL(pack_hbound_kernel, dim3(n_experts), dim3(256), 0, s, canon, canon_stride, I, d, bits, hb);
+  hipLaunchKernelGGL(pack_hbound_kernel, dim3(n_experts), dim3(256), 0, s, canon, canon_stride, I, d, bits, hb, ed);
   return hipGetLastError();
 }
 
