@@ -842,24 +842,33 @@ DEVI void down_item(const PfGemmArgs& a, const Stages& S, float* rowf_lds, int g
     if (s + 2 < nsteps) step(ic<2>{}, s + 2);
   }
   // rows stored as fp16(sum 2^-ed) (below 2^15, see the pack-time bound);
-  // the combine multiplies them by rowf = w 2^(hb + 2 ex + ed).  Columns n
-  // and n + 1 (lanes n, n ^ 1) share one dword.
+  // the combine multiplies them by rowf = w 2^(hb + 2 ex + ed).  The tile
+  // (rows x 256 columns, 512 B per row) is assembled in LDS, rows 0..63 in
+  // stage 0 and 64..127 in stage 1, columns n and n + 1 (lanes n, n ^ 1)
+  // sharing one dword, then written out in 16-byte pieces.
   (void)rowf_lds;
+  __syncthreads();  // every wave is past its last read of the stages
 #pragma unroll
   for (int rg = 0; rg < NRG; ++rg)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * rg + 4 * q + i;
+      uint32_t* trow = reinterpret_cast<uint32_t*>((r < 64 ? S.s0 : S.s1) + (r & 63) * 512);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const _Float16 v = (_Float16)ldexpf(acc[rg][t][i], -ed);
         uint16_t vb;
         __builtin_memcpy(&vb, &v, 2);
         const uint32_t nb2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)vb, 0xB1, 0xF, 0xF, true);  // lane n ^ 1
-        if (r < rows && (n & 1) == 0)
-          *reinterpret_cast<uint32_t*>(a.yh + (size_t)(row0 + r) * a.d + r0 + n + 16 * t) = (uint32_t)vb | (nb2 << 16);
+        if ((n & 1) == 0) trow[(64 * wv + 16 * t + n) >> 1] = (uint32_t)vb | (nb2 << 16);
       }
     }
+  __syncthreads();
+  for (int p = tid; p < rows * 32; p += 256) {
+    const int r = p >> 5, c16 = p & 31;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>((r < 64 ? S.s0 : S.s1) + (r & 63) * 512 + 16 * c16);
+    *reinterpret_cast<u32x4_t*>(a.yh + (size_t)(row0 + r) * a.d + nt * PF_DT + 8 * c16) = v;
+  }
 }
 
 template <int BITS, int BK>
