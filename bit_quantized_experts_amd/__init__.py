@@ -227,6 +227,6 @@ class PackedLayer:
 
 def new_workspace(nbytes: int, device="cuda"):
     """A zero-initialised workspace tensor (control words cleared)."""
-    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    ws = torch.empty(max(nbytes, 512), dtype=torch.uint8, device=device)
     moe_workspace_init(ws)
     return ws

@@ -21,6 +21,7 @@
 // LDS (one copy per workgroup), the down kernel's h fragments from L2.
 #include "kern_common.h"
 #include "moe_launch.h"
+#include "topk.h"
 
 namespace {
 
@@ -148,6 +149,9 @@ struct alignas(16) GuLds {
   float red[GU_NW][8][64];          // partial sums of the k-parts
   float rn[8];                      // 1 / rms of each token
   SlotLds S;
+  int32_t tk_idx[MOE_MAX_TOK_DECODE * MOE_MAX_K];  // the selection, [T][k]
+  float tk_w[MOE_MAX_TOK_DECODE * MOE_MAX_K];
+  uint64_t tk_buf[GU_NW][TOPK_BUF];
 };
 
 template <int BITS>
@@ -235,7 +239,7 @@ DEVI void run_tile(const uint8_t* gate, const uint8_t* up, int64_t rowoff, int k
   if (rem == 2) mul_group<BITS>(r1, L, 8 * (kg + step - wkg0), lane, accg, accu);
 }
 
-template <int BITS>
+template <int BITS, int NPER>  // NPER >= ceil(E / 64)
 __global__ __launch_bounds__(64 * GU_NW) void gu_decode_kernel(GuArgs a) {
   constexpr int64_t CB = BITS == 2 ? 1280 : 1792;
   __shared__ GuLds L;
@@ -249,9 +253,34 @@ __global__ __launch_bounds__(64 * GU_NW) void gu_decode_kernel(GuArgs a) {
   const int n_win = (8 * n_kg + GU_WIN - 1) / GU_WIN;
   const int win_kg = (n_kg + n_win - 1) / n_win;  // k-groups per window
 
-  if (wv == 0) build_slots_wave(L.S, a.idx, a.w, tk, k, T, E, has_shared);
-  if (tid >= 64 && tid < 72) L.rn[tid - 64] = tid - 64 < T ? 1.0f / a.rnorm[tid - 64] : 1.0f;
+  // Selection: wavefront t < T takes token t's row of logits.  Its loads,
+  // the divisors' and the activation window's share one round trip.
+  const bool select = a.logits != nullptr;
+  float lv[NPER];
+  if (select) {
+    const float* row = a.logits + (size_t)min(wv, T - 1) * E;
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) lv[i] = row[min(lane + 64 * i, E - 1)];
+  }
+  const float rnv = (tid >= 64 && tid < 64 + T) ? a.rnorm[tid - 64] : 1.0f;
   if (n_win == 1) stage_window(L, a, 0, 8 * n_kg, tid);
+  if (tid >= 64 && tid < 72) L.rn[tid - 64] = 1.0f / rnv;
+  if (select) {
+    if (wv < T) {
+      uint64_t key[NPER];
+#pragma unroll
+      for (int i = 0; i < NPER; ++i) key[i] = (lane + 64 * i < E) ? sel_key(lv[i], lane + 64 * i) : 0ull;
+      topk_keys<NPER>(key, E, k, L.tk_idx + wv * k, L.tk_w + wv * k, L.tk_buf[wv]);
+    }
+    __syncthreads();
+    if (blockIdx.x == 0) {
+      for (int i = tid; i < tk; i += blockDim.x) {
+        if (a.out_idx) a.out_idx[i] = L.tk_idx[i];
+        if (a.out_w) a.out_w[i] = L.tk_w[i];
+      }
+    }
+  }
+  if (wv == 0) build_slots_wave(L.S, select ? L.tk_idx : a.idx, select ? L.tk_w : a.w, tk, k, T, E, has_shared);
   __syncthreads();  // slot list, rms and the staged activations
   if (blockIdx.x == 0) {
     const int ns = base + L.S.n_routed;
@@ -465,8 +494,20 @@ hipError_t launch_down_t(const DownArgs& a, int grid_x, int nw, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gu_decode(const GuArgs& a, int n_wg, hipStream_t s) {
-  if (a.bits == 2) MOE_LAUNCH(gu_decode_kernel<2>, dim3(n_wg), dim3(64 * GU_NW), 0, s, a);
-  else MOE_LAUNCH(gu_decode_kernel<3>, dim3(n_wg), dim3(64 * GU_NW), 0, s, a);
+#define GU_LAUNCH(B, N) MOE_LAUNCH((gu_decode_kernel<B, N>), dim3(n_wg), dim3(64 * GU_NW), 0, s, a)
+  const int np = a.E <= 512 ? 8 : a.E <= 1024 ? 16 : a.E <= 2048 ? 32 : 64;
+  if (a.bits == 2) {
+    if (np == 8) GU_LAUNCH(2, 8);
+    else if (np == 16) GU_LAUNCH(2, 16);
+    else if (np == 32) GU_LAUNCH(2, 32);
+    else GU_LAUNCH(2, 64);
+  } else {
+    if (np == 8) GU_LAUNCH(3, 8);
+    else if (np == 16) GU_LAUNCH(3, 16);
+    else if (np == 32) GU_LAUNCH(3, 32);
+    else GU_LAUNCH(3, 64);
+  }
+#undef GU_LAUNCH
   return hipGetLastError();
 }
 

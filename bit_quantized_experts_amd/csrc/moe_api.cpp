@@ -150,12 +150,11 @@ PackedLayout packed_layout(const moe_layer_desc* D, const moe_expert_layout& ex,
 
 // ------------------------------------------------------------- workspace ---
 struct WsLayout {
-  int64_t ctrl, lp, ss_part, rnorm, logits, idx, w, n_slots, slot_expert, slot_w, xfrag, xsum, hfrag, hsum, ypart,
-      total;
+  int64_t ctrl, lp, ss_part, rnorm, logits, n_slots, slot_expert, slot_w, xfrag, xsum, hfrag, hsum, ypart, total;
   int max_slots, S, nbI, n_cs;
 };
 
-int64_t ctrl_bytes() { return 256; }
+int64_t ctrl_bytes() { return MOE_CTRL_WORDS * 4; }
 
 int down_splits(const moe_layer* L, int max_slots) {
   const int n_rg = L->ex.down.n_rg;
@@ -180,11 +179,9 @@ WsLayout ws_layout_decode(const moe_layer* L, int T) {
   auto take = [&](int64_t bytes) { int64_t r = o; o += moe_align256(bytes); return r; };
   W.ctrl = take(ctrl_bytes());
   W.lp = take((int64_t)W.n_cs * T * E * 4);
-  W.ss_part = take((int64_t)W.n_cs * T * 4);
+  W.ss_part = take((int64_t)((E + MOE_ROUTE_ROWS - 1) / MOE_ROUTE_ROWS) * W.n_cs * T * 4);
   W.rnorm = take(8 * 4);
   W.logits = take((int64_t)T * E * 4);
-  W.idx = take((int64_t)T * k * 4);
-  W.w = take((int64_t)T * k * 4);
   W.n_slots = take(4);
   W.slot_expert = take((int64_t)W.max_slots * 4);
   W.slot_w = take((int64_t)W.max_slots * 8 * 4);
@@ -308,7 +305,8 @@ struct LayerInput {
   int norm;
 };
 
-// One decode layer (T <= 8): route -> select -> gate/up -> down.  The result
+// One decode layer (T <= 8): route (router logits) -> gate/up (with the top-k
+// selection in every workgroup) -> down.  The result
 // is left as split partials in the workspace (ypart, W.S splits).
 int decode_layer(const moe_layer* L, const LayerInput& in, float eps, int T, float* y_prev_out,
                  const moe_route_io* r, uint8_t* ws, hipStream_t s, int* S_out) {
@@ -329,44 +327,37 @@ int decode_layer(const moe_layer* L, const LayerInput& in, float eps, int T, flo
   ra.code_off = 1 << (L->bits - 1);
   ra.do_logits = !forced;
   ra.lp = reinterpret_cast<float*>(ws + W.lp);
-  ra.ss_part = reinterpret_cast<float*>(ws + W.ss_part);
   ra.xfrag = reinterpret_cast<_Float16*>(ws + W.xfrag);
   ra.xsum = reinterpret_cast<float*>(ws + W.xsum);
   ra.y_out = y_prev_out;
+  SelectArgs& sa = ra.sel;
+  sa.ss_part = reinterpret_cast<float*>(ws + W.ss_part);
+  sa.br = L->router_b;
+  sa.ew = L->router_ew;
+  sa.n_cs = W.n_cs;
+  sa.n_rs = forced ? 1 : (E + MOE_ROUTE_ROWS - 1) / MOE_ROUTE_ROWS;
+  sa.T = T;
+  sa.d = d;
+  sa.E = E;
+  sa.norm = in.norm;
+  sa.eps = eps;
+  sa.ctrl = reinterpret_cast<uint32_t*>(ws + W.ctrl);
+  sa.logits = reinterpret_cast<float*>(ws + W.logits);
+  sa.rnorm = reinterpret_cast<float*>(ws + W.rnorm);
+  sa.out_logits = (r && !forced) ? r->out_logits : nullptr;
   timed_begin(2, s, &slot);
   serial_point(s);
   HIPCHK(launch_route(ra, s));
   timed_end(slot, s);
 
-  SelectArgs sa{};
-  sa.lp = ra.lp;
-  sa.ss_part = ra.ss_part;
-  sa.br = L->router_b;
-  sa.ew = L->router_ew;
-  sa.n_cs = W.n_cs;
-  sa.T = T;
-  sa.d = d;
-  sa.E = E;
-  sa.k = L->k;
-  sa.norm = in.norm;
-  sa.eps = eps;
-  sa.fidx = forced ? r->in_idx : nullptr;
-  sa.fw = forced ? r->in_w : nullptr;
-  sa.logits = reinterpret_cast<float*>(ws + W.logits);
-  sa.idx = reinterpret_cast<int32_t*>(ws + W.idx);
-  sa.w = reinterpret_cast<float*>(ws + W.w);
-  sa.rnorm = reinterpret_cast<float*>(ws + W.rnorm);
-  sa.out_logits = (r && !forced) ? r->out_logits : nullptr;
-  sa.out_idx = r ? r->out_idx : nullptr;
-  sa.out_w = r ? r->out_w : nullptr;
-  serial_point(s);
-  HIPCHK(launch_select(sa, s));
-
   const ExpertSet X = expert_set(L);
   GuArgs ga{};
   ga.X = X;
-  ga.idx = sa.idx;
-  ga.w = sa.w;
+  ga.logits = forced ? nullptr : sa.logits;
+  ga.idx = forced ? r->in_idx : nullptr;
+  ga.w = forced ? r->in_w : nullptr;
+  ga.out_idx = r ? r->out_idx : nullptr;
+  ga.out_w = r ? r->out_w : nullptr;
   ga.k = L->k;
   ga.n_slots = reinterpret_cast<int32_t*>(ws + W.n_slots);
   ga.slot_expert = reinterpret_cast<int32_t*>(ws + W.slot_expert);

@@ -17,10 +17,25 @@
 #define MOE_MAX_IN_SPLITS 8
 // Most column slices of the router (d <= 8192).
 #define MOE_MAX_CS 32
+// Control words of the workspace used by the route kernel: one completion
+// counter per row slice (E <= 4096: at most 64).
+#define MOE_CTRL_WORDS 64
 
 // ---------------------------------------------------------------- decode ---
 // Layer input: in = sum over S_in splits of in[s * in_stride + t * d + j]
 // (the previous layer's down partials, or the caller's x with S_in = 1).
+struct SelectArgs {
+  float* ss_part;      // [n_rs][n_cs][T] sums of squares, one copy per row slice
+  const float* br;     // [E]
+  const int32_t* ew;   // [E16] router row exponents (partial logits are unscaled)
+  int32_t n_cs, n_rs, T, d, E, norm;
+  float eps;
+  uint32_t* ctrl;      // completion counters, one per row slice; zero between calls
+  float* logits;       // ws [T][E]
+  float* rnorm;        // ws [8]: per-token divisor (1 when norm == 0)
+  float* out_logits;   // optional copy of the logits
+};
+
 struct RouteArgs {
   const float* in;
   int32_t S_in;
@@ -29,28 +44,10 @@ struct RouteArgs {
   const _Float16* wl;  // same, lo part
   int32_t T, d, E, code_off, do_logits;
   float* lp;        // ws [d/256][T][E] partial logits
-  float* ss_part;   // ws [d/256][T] partial sums of squares
   _Float16* xfrag;  // ws [d/32][64][8]
   float* xsum;      // ws [d/32][16]
   float* y_out;     // optional: the summed input, [T][d]
-};
-
-struct SelectArgs {
-  const float* lp;       // [n_cs][T][E]
-  const float* ss_part;  // [n_cs][T]
-  const float* br;       // [E]
-  const int32_t* ew;     // [E16] router row exponents (partial logits are unscaled)
-  int32_t n_cs, T, d, E, k, norm;
-  float eps;
-  const int32_t* fidx;  // forced routing or null
-  const float* fw;
-  float* logits;  // ws [T][E]
-  int32_t* idx;   // ws [T][k]
-  float* w;       // ws [T][k]
-  float* rnorm;   // ws [8]: per-token divisor (1 when norm == 0)
-  float* out_logits;
-  int32_t* out_idx;
-  float* out_w;
+  SelectArgs sel;   // the logits, finished by the last workgroup of each row slice
 };
 
 struct ExpertSet {
@@ -67,8 +64,11 @@ struct ExpertSet {
 // workgroup from the routing; workgroup 0 publishes it for the down kernel.
 struct GuArgs {
   ExpertSet X;
-  const int32_t* idx;  // [T][k]
-  const float* w;      // [T][k]
+  const float* logits;  // [T][E]: every workgroup selects the top k itself; or null:
+  const int32_t* idx;   // [T][k] forced routing (ids out of range are skipped)
+  const float* w;       // [T][k]
+  int32_t* out_idx;     // optional: the selection ([T][k], written by workgroup 0)
+  float* out_w;
   int32_t k;
   int32_t* n_slots;      // out [1]
   int32_t* slot_expert;  // out [MAX_SLOTS]
@@ -98,7 +98,6 @@ hipError_t launch_debug_unpack(const uint8_t* mat, const moe_mat_layout& L, int 
                                uint16_t* w16, hipStream_t s);
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
-hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 hipError_t launch_gu_decode(const GuArgs& a, int n_wg, hipStream_t s);
 hipError_t launch_down_decode(const DownArgs& a, int grid_x, int nw, hipStream_t s);
 hipError_t launch_combine(const float* part, int S, int64_t stride, int T, int d, float* y, hipStream_t s);

@@ -13,150 +13,9 @@
 // to the accumulators before the SwiGLU nonlinearity.
 #include "kern_common.h"
 #include "moe_launch.h"
+#include "topk.h"
 
 namespace {
-
-// Selection key of (logit v, expert e): larger key = ranks earlier (logit
-// descending, then index ascending).  The float's bits are mapped to an
-// unsigned integer of the same order (-0.0 first folded into +0.0); the low
-// word is the complement of the index.  Key 0 never occurs for a finite
-// logit, so it marks an expert already taken.
-DEVI uint64_t sel_key(float v, int e) {
-  uint32_t b = __float_as_uint(v == 0.f ? 0.f : v);
-  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  return ((uint64_t)b << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
-}
-DEVI float key_value(uint64_t k) {
-  uint32_t b = (uint32_t)(k >> 32);
-  b = (b & 0x80000000u) ? (b & 0x7FFFFFFFu) : ~b;
-  return __uint_as_float(b);
-}
-DEVI int key_index(uint64_t k) { return (int)(0xFFFFFFFFu - (uint32_t)k); }
-
-// Top-k of one row of E logits by one wavefront, then the gate weights.
-// Lane l holds the keys of experts l, l+64, ...; keys are unique.
-//   1. Candidates: theta = the k-th largest of the 64 lane maxima (ranked by
-//      counting larger maxima through LDS).  At least k keys are >= theta
-//      (those k maxima), and every key of the top k is >= theta.
-//   2. If at most 64 keys are >= theta they are compacted to LDS, each is
-//      ranked by counting the larger candidates, and the first k ranks are
-//      the answer.  Otherwise (many equal logits) a radix search on the value
-//      keys finds the k-th largest value (a trial threshold is kept while at
-//      least k values reach it, stopping once exactly k do); the values above
-//      it and the tied ones in ascending expert index are taken, compacted
-//      and ranked the same way.
-// Lane r ends up with rank r (value descending, then index ascending).  Gate
-// weights: m = logit of rank 0, e_r = exp64(l_r - m), S = sum of e_r in rank
-// order, w_r = fp32(e_r / S).  `buf`: this wave's 96 LDS entries.  NPER >=
-// ceil(E / 64).
-DEVI int lanes_below(uint64_t m) {
-  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
-
-DEVI double readlane_f64(double v, int l) {
-  const uint64_t b = __builtin_bit_cast(uint64_t, v);
-  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)b, l);
-  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(b >> 32), l);
-  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
-}
-
-DEVI uint64_t readlane_u64(uint64_t v, int l) {
-  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, l);
-  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), l);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-constexpr int TOPK_BUF = 96;  // LDS entries per wave: 64 candidates + 32
-
-template <int NPER, typename RowT>
-DEVI void topk_wave(RowT row, int E, int k, int32_t* idx_out, float* w_out, uint64_t* buf) {
-  const int lane = threadIdx.x & 63;
-  uint64_t key[NPER];
-  uint64_t lmax = 0;
-#pragma unroll
-  for (int i = 0; i < NPER; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = (e < E) ? sel_key(row(e), e) : 0ull;  // 0: no expert
-    lmax = key[i] > lmax ? key[i] : lmax;
-  }
-  // 1. theta = k-th largest lane maximum
-  buf[lane] = lmax;
-  int rk = 0;
-  for (int j = 0; j < 64; ++j) rk += (buf[j] > lmax) ? 1 : 0;
-  const uint64_t at = __ballot(rk == k - 1 && lmax != 0ull);
-  const uint64_t theta = readlane_u64(lmax, at ? (int)__builtin_ctzll(at) : 0);
-  int c = 0;
-#pragma unroll
-  for (int i = 0; i < NPER; ++i) c += (int)__builtin_popcountll(__ballot(key[i] >= theta));
-
-  // 2. choose the candidate set: keys >= theta, or the exact top k
-  bool exact = true;
-  uint32_t tau = 0;
-  int need = 0;
-  if (c > 64) {
-    uint32_t hv[NPER];
-#pragma unroll
-    for (int i = 0; i < NPER; ++i) hv[i] = (uint32_t)(key[i] >> 32);
-    exact = false;
-    for (int b = 31; b >= 0; --b) {
-      const uint32_t t = tau | (1u << b);
-      int cnt = 0;
-#pragma unroll
-      for (int i = 0; i < NPER; ++i) cnt += (int)__builtin_popcountll(__ballot(hv[i] >= t));
-      if (cnt >= k) {
-        tau = t;
-        if (cnt == k) {
-          exact = true;
-          break;
-        }
-      }
-    }
-    if (!exact) {
-      int c_gt = 0;
-#pragma unroll
-      for (int i = 0; i < NPER; ++i) c_gt += (int)__builtin_popcountll(__ballot(hv[i] > tau));
-      need = k - c_gt;
-    }
-  }
-  const bool radix = c > 64;
-  // compact the candidates to buf[0..n) in (slot, lane) order
-  int n = 0;
-#pragma unroll
-  for (int i = 0; i < NPER; ++i) {
-    const uint32_t hv = (uint32_t)(key[i] >> 32);
-    bool take;
-    if (!radix) {
-      take = key[i] >= theta;
-    } else {
-      const bool tie = !exact && hv == tau;
-      const uint64_t tm = __ballot(tie);
-      take = exact ? (hv >= tau) : (hv > tau || (tie && lanes_below(tm) < need));
-      need -= min(need, (int)__builtin_popcountll(tm));
-    }
-    const uint64_t sm = __ballot(take);
-    const int pos = n + lanes_below(sm);
-    if (take && pos < 64) buf[pos] = key[i];
-    n += (int)__builtin_popcountll(sm);
-  }
-  n = min(n, 64);
-  // rank the candidates; the first k ranks are the result
-  const uint64_t mine = (lane < n) ? buf[lane] : 0ull;
-  int rank = 0;
-  for (int j = 0; j < n; ++j) rank += (buf[j] > mine) ? 1 : 0;
-  if (lane < n && rank < k) buf[64 + rank] = mine;
-  const uint64_t kr = (lane < k) ? buf[64 + lane] : 0ull;
-  const float my_v = key_value(kr);
-  const int my_e = key_index(kr);
-  const double m = (double)__builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(uint32_t, my_v)));
-  double ev = 0.0;
-  if (lane < k) ev = moe_exp64((double)my_v - m);
-  double S = 0.0;
-  for (int r = 0; r < k; ++r) S += readlane_f64(ev, r);  // rank order, same in every lane
-  if (lane < k) {
-    idx_out[lane] = (my_e >= 0 && my_e < E) ? my_e : 0;  // (other only with non-finite logits, out of contract)
-    w_out[lane] = (float)(ev / S);
-  }
-}
 
 template <typename RowT>
 DEVI void topk_wave_any(RowT row, int E, int k, int32_t* idx_out, float* w_out, uint64_t* buf) {
@@ -180,6 +39,94 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 }
 
 // ---------------------------------------------------------------------------
+// Logits, finished inside the route kernel by the workgroup of each row slice
+// that completes last (no workgroup waits for another): every workgroup,
+// once its partial logits and its sums of squares are stored, counts itself
+// on the counter of its row slice rs; the one that completes the count (the
+// last of the n_cs column slices) forms, for the slice's 64 experts and
+// every token, the sum of the partial logits in column-slice order times the
+// router row factor 2^ew (exact), the token's divisor r = sqrt(sum of
+// squares / d + eps) (1 without the norm; the slice's own copies of the sums
+// of squares, added in column-slice order, so every slice gets the same r),
+// and the logit (sum / r) + bias.  It puts the counter back to zero for the
+// next call.  The top-k selection is left to the gate/up kernel.
+//
+// The values handed between workgroups (partial logits, sums of squares)
+// are stored and loaded device-coherently (agent-scope relaxed atomics: sc1
+// accesses that no workgroup's L2 keeps stale), so the count needs no cache
+// write-back or invalidation, only the wait for the stores.
+// ---------------------------------------------------------------------------
+DEVI void st_dev(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+DEVI float ld_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Counts the calling workgroup on *ctr once all its device-coherent stores
+// have completed; true in every thread of the workgroup that completes
+// `total`, which then sees every counted workgroup's stores.
+DEVI bool count_done(uint32_t* ctr, uint32_t total, int* flag) {
+  __builtin_amdgcn_s_waitcnt(0);  // this wavefront's stores are complete
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *flag = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == total - 1u;
+  __syncthreads();
+  return *flag != 0;
+}
+
+// Wavefront wv finishes tokens wv and wv + 4 (pairs p = tid and tid + 256:
+// token p / 64, expert rs * 64 + p % 64); every load is issued before the
+// first add, at clamped addresses.
+template <int MAXCS>
+DEVI void finish_slice(const RouteArgs& a, int rs) {
+  const SelectArgs& c = a.sel;
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int T = a.T, E = a.E, n_cs = c.n_cs;
+  static_assert(MOE_MAX_TOK_DECODE * MOE_ROUTE_ROWS <= 2 * 256, "two (token, expert) pairs per thread");
+  const int er = rs * MOE_ROUTE_ROWS + lane, e = min(er, E - 1);
+  const bool e_ok = er < E;
+  int t[2];
+  float ss[2], tmp[2][MAXCS];
+  const float* ssr = c.ss_part + (size_t)rs * n_cs * T;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    t[j] = min(wv + 4 * j, T - 1);
+    ss[j] = ld_dev(ssr + min(lane, n_cs - 1) * T + t[j]);
+    if (a.do_logits) {
+#pragma unroll
+      for (int q = 0; q < MAXCS; ++q) tmp[j][q] = ld_dev(a.lp + ((size_t)min(q, n_cs - 1) * T + t[j]) * E + e);
+    }
+  }
+  const int ew = a.do_logits ? c.ew[e] : 0;
+  const float bias = a.do_logits ? c.br[e] : 0.f;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int tok = wv + 4 * j;
+    const float r = c.norm ? sqrtf(wave_sum((lane < n_cs) ? ss[j] : 0.f) / (float)c.d + c.eps) : 1.0f;
+    if (tok >= T) continue;
+    if (rs == 0 && lane == 0) c.rnorm[tok] = r;
+    if (!a.do_logits) continue;
+    float acc = tmp[j][0];
+#pragma unroll
+    for (int q = 1; q < MAXCS; ++q)
+      if (q < n_cs) acc += tmp[j][q];
+    const float x = ldexpf(acc, ew);  // router row factor, exact
+    const float l = (c.norm ? x / r : x) + bias;
+    if (e_ok) {
+      c.logits[(size_t)tok * E + er] = l;
+      if (c.out_logits) c.out_logits[(size_t)tok * E + er] = l;
+    }
+  }
+}
+
+DEVI void route_finish(const RouteArgs& a, int rs) {
+  __shared__ int flag;
+  if (!count_done(a.sel.ctrl + rs, (uint32_t)a.sel.n_cs, &flag)) return;
+  if (threadIdx.x == 0) a.sel.ctrl[rs] = 0u;
+  if (a.sel.n_cs <= 16) finish_slice<16>(a, rs);
+  else finish_slice<32>(a, rs);
+}
+
+// ---------------------------------------------------------------------------
 // Route: workgroup (column slice cs of 256 inputs, row slice rs of 64
 // experts).  Sums the input splits for its columns, writes partial logits of
 // its 64 experts over those columns; the rs == 0 workgroups also write the
@@ -193,8 +140,8 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 // experts over the 8 blocks take 16 v_mfma_f32_16x16x32_f16 and the hi and lo
 // rows of a token are added once at the end.  All four products of the
 // ~22-bit operands are formed exactly; the rounding is fp32 accumulation.
-// The power of two 2^ew of each router row is applied by the select kernel
-// to the summed partials (exact).
+// The power of two 2^ew of each router row is applied to the summed
+// partials (exact) when the selection (above) adds them up.
 // ---------------------------------------------------------------------------
 DEVI half8_t x_fragment(const float (*ys)[MOE_ROUTE_COLS], int bl, int lane, int T, float* sum) {
   const int m = lane & 15, q = lane >> 4, tok = m & 7, lo = m >> 3;
@@ -270,12 +217,13 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   }
   __syncthreads();
 
+  // sums of squares of the slice (each row slice keeps its own copy)
+  for (int t = wv; t < T; t += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(&ys[t][4 * lane]);
+    const float ss = wave_sum(v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w);
+    if (lane == 0) st_dev(a.sel.ss_part + ((size_t)rs * gridDim.x + cs) * T + t, ss);
+  }
   if (rs == 0) {
-    for (int t = wv; t < T; t += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(&ys[t][4 * lane]);
-      const float ss = wave_sum(v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w);
-      if (lane == 0) a.ss_part[cs * T + t] = ss;
-    }
     const int m = lane & 15, q = lane >> 4;
     for (int bl = wv; bl < NBL; bl += 4) {
       const int b = cs * NBL + bl;
@@ -288,113 +236,31 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     }
   }
 
-  if (!tile_ok) return;
-  half8_t A[NBL];
+  if (tile_ok) {
+    half8_t A[NBL];
 #pragma unroll
-  for (int j = 0; j < NBL; ++j) {
-    float s;
-    A[j] = x_fragment(ys, j, lane, T, &s);
-  }
-  float4_t acc = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int j = 0; j < NBL; ++j) {
-    acc = mfma16x16x32(A[j], BH[j], acc);
-    acc = mfma16x16x32(A[j], BL[j], acc);
-  }
-  // lane l: expert et*16 + (l & 15), C rows 4(l>>4)+i: token 4((l>>4)&1)+i,
-  // hi part in lanes < 32, lo part in lanes >= 32.  The partial logits are
-  // left without the row factor 2^ew; the select kernel applies it to the sum.
-  const int e = et * 16 + (lane & 15);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float v = add_partner32(acc[i]);
-    const int t = 4 * ((lane >> 4) & 1) + i;
-    if (lane < 32 && e < E && t < T) a.lp[((size_t)cs * T + t) * E + e] = v;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Select: one workgroup per token.  Sums the token's partial logits in
-// column-slice order (every load issued before the first add), applies 1/rms
-// and the bias, and wavefront 0 selects the top-k and the gate weights.  With
-// forced routing it only copies the given row.  The slot list is built by
-// the expert kernels themselves.
-// ---------------------------------------------------------------------------
-template <int MAXCS>
-DEVI void sum_partials(const SelectArgs& a, int t, float den, float* row) {
-  const int tid = threadIdx.x, T = a.T, E = a.E, n_cs = a.n_cs;
-  for (int e0 = 0; e0 < E; e0 += 512) {
-    float tmp[2][MAXCS], bias[2];
-    int ew[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {  // bias and row exponent first: they wait for nothing
-      const int e = min(e0 + tid + 256 * j, E - 1);
-      bias[j] = a.br[e];
-      ew[j] = a.ew[e];
+    for (int j = 0; j < NBL; ++j) {
+      float s;
+      A[j] = x_fragment(ys, j, lane, T, &s);
     }
+    float4_t acc = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int e = min(e0 + tid + 256 * j, E - 1);
-#pragma unroll
-      for (int c = 0; c < MAXCS; ++c) tmp[j][c] = a.lp[((size_t)min(c, n_cs - 1) * T + t) * E + e];
+    for (int j = 0; j < NBL; ++j) {
+      acc = mfma16x16x32(A[j], BH[j], acc);
+      acc = mfma16x16x32(A[j], BL[j], acc);
     }
+    // lane l: expert et*16 + (l & 15), C rows 4(l>>4)+i: token 4((l>>4)&1)+i,
+    // hi part in lanes < 32, lo part in lanes >= 32.  The partial logits are
+    // left without the row factor 2^ew; it is applied to their sum.
+    const int e = et * 16 + (lane & 15);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int e = e0 + tid + 256 * j;
-      float acc = tmp[j][0];
-#pragma unroll
-      for (int c = 1; c < MAXCS; ++c)
-        if (c < n_cs) acc += tmp[j][c];
-      if (e < E) {
-        const float x = ldexpf(acc, ew[j]);  // router row factor, exact
-        const float l = (a.norm ? x / den : x) + bias[j];
-        row[e] = l;
-        a.logits[(size_t)t * E + e] = l;
-        if (a.out_logits) a.out_logits[(size_t)t * E + e] = l;
-      }
+    for (int i = 0; i < 4; ++i) {
+      const float v = add_partner32(acc[i]);
+      const int t = 4 * ((lane >> 4) & 1) + i;
+      if (lane < 32 && e < E && t < T) st_dev(a.lp + ((size_t)cs * T + t) * E + e, v);
     }
   }
-}
-
-__global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
-  extern __shared__ float row[];  // [E]
-  __shared__ float den_s;
-  __shared__ uint64_t tk_buf[TOPK_BUF];
-  const int t = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int T = a.T, k = a.k;
-  if (wv == 0) {
-    float v = (a.norm && lane < a.n_cs) ? a.ss_part[lane * T + t] : 0.f;
-    v = wave_sum(v);
-    if (lane == 0) {
-      const float r = a.norm ? sqrtf(v / (float)a.d + a.eps) : 1.0f;
-      den_s = r;
-      a.rnorm[t] = r;
-    }
-  }
-  if (a.fidx) {
-    if (tid < k) {
-      const int32_t e = a.fidx[t * k + tid];
-      const float w = a.fw[t * k + tid];
-      a.idx[t * k + tid] = e;
-      a.w[t * k + tid] = w;
-      if (a.out_idx) a.out_idx[t * k + tid] = e;
-      if (a.out_w) a.out_w[t * k + tid] = w;
-    }
-    return;
-  }
-  __syncthreads();
-  const float den = den_s;
-  if (a.n_cs <= 16) sum_partials<16>(a, t, den, row);
-  else sum_partials<32>(a, t, den, row);
-  __syncthreads();
-  if (wv == 0) {
-    topk_wave_any(PtrRow{row}, a.E, k, a.idx + t * k, a.w + t * k, tk_buf);
-    if (lane < k) {
-      if (a.out_idx) a.out_idx[t * k + lane] = a.idx[t * k + lane];
-      if (a.out_w) a.out_w[t * k + lane] = a.w[t * k + lane];
-    }
-  }
+  route_finish(a, rs);
 }
 
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part, int S, int64_t stride, int n4,
@@ -442,13 +308,11 @@ __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   const dim3 grid(a.d / MOE_ROUTE_COLS, a.do_logits ? (a.E + MOE_ROUTE_ROWS - 1) / MOE_ROUTE_ROWS : 1);
+  // the completion counts must match the grid, or no workgroup selects
+  if ((int)grid.x != a.sel.n_cs || (int)grid.y != a.sel.n_rs || a.sel.n_rs > MOE_CTRL_WORDS ||
+      a.sel.n_cs > MOE_MAX_CS || a.T < 1 || a.T > MOE_MAX_TOK_DECODE)
+    return hipErrorInvalidValue;
   MOE_LAUNCH(route_kernel, grid, dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
-  const size_t lds = sizeof(float) * (size_t)a.E;
-  hipLaunchKernelGGL(select_kernel, dim3(a.T), dim3(256), lds, s, a);
   return hipGetLastError();
 }
 

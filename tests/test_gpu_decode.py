@@ -189,6 +189,44 @@ def test_forced_routing_and_invalid_entries(bqe):
     assert rel_err_inf(y.cpu().numpy(), oy) <= TOL_LAYER
 
 
+def test_workspace_reuse_control_words(bqe):
+    """The route kernel counts finished workgroups in the workspace's control
+    words; every call must leave them at zero, so one workspace serves calls
+    of any shape in turn with results identical to a fresh workspace's."""
+    wa = mi.small(mi.WORKLOADS["tiny"], Is=64)
+    wb = mi.small(mi.WORKLOADS["layer_t1"], layers=1)
+    La, Lb = packed_layer(wa, 0), packed_layer(wb, 0)
+    nbytes = max(La.workspace_bytes(8), Lb.workspace_bytes(8))
+    shared = bqe.new_workspace(nbytes)
+    g = np.random.default_rng(31)
+
+    def run(L, wl, T, ws, forced):
+        x = activations_device(mi.activations(wl, T=T, stream=100 + T))
+        y = torch.empty((T, wl.d), dtype=torch.float32, device=DEV)
+        idx = torch.empty((T, wl.k), dtype=torch.int32, device=DEV)
+        w = torch.empty((T, wl.k), dtype=torch.float32, device=DEV)
+        if forced:
+            fi = torch.from_numpy(np.stack([g.permutation(wl.E)[:wl.k] for _ in range(T)]).astype(np.int32)).to(DEV)
+            fw = torch.from_numpy(g.random((T, wl.k)).astype(np.float32)).to(DEV)
+            r = bqe.RouteIO(fi.data_ptr(), fw.data_ptr(), None, idx.data_ptr(), w.data_ptr())
+        else:
+            r = bqe.RouteIO(None, None, None, idx.data_ptr(), w.data_ptr())
+        bqe.moe_layer_forward(L.handle, x, y, ws, r)
+        torch.cuda.synchronize()
+        return y.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
+
+    for L, wl, T, forced in [(La, wa, 3, False), (Lb, wb, 8, False), (La, wa, 5, True), (Lb, wb, 1, False),
+                             (La, wa, 8, False), (Lb, wb, 2, True), (Lb, wb, 7, False)]:
+        say(f"[decode] workspace reuse: E={wl.E} d={wl.d} T={T} forced={forced}")
+        state = g.bit_generator.state
+        y1, i1, w1 = run(L, wl, T, shared, forced)
+        assert int(shared[:256].count_nonzero()) == 0, "control words left set"
+        g.bit_generator.state = state
+        y2, i2, w2 = run(L, wl, T, bqe.new_workspace(nbytes), forced)
+        assert np.array_equal(i1, i2) and np.array_equal(w1.view(np.uint32), w2.view(np.uint32))
+        assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
 def test_determinism_and_T8_vs_T1(bqe):
     wl = mi.small(mi.WORKLOADS["layer_t1"], layers=1)
     L = packed_layer(wl, 0)
