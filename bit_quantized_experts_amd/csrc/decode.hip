@@ -60,77 +60,81 @@ DEVI void load_a(const _Float16* frag, const float* sum, size_t b, int lane, hal
 }
 
 // ---------------------------------------------------------------------------
-// Slot list, built in LDS by one wavefront from the routing rows (T*k <= 128
-// entries, two per lane): routed experts are marked in a bitmap, numbered in
-// ascending id order after the shared expert's slot 0, and every (token,
-// rank) entry puts its gate weight in its slot's row.  Only LDS operations of
-// the one wavefront are involved (they complete in order), so the other
-// wavefronts need a single barrier afterwards.
+// Slot list in LDS: routed experts numbered in ascending id order after the
+// shared expert's slot 0, and every (token, rank) entry's gate weight in its
+// slot's row.  The selected experts are first marked in a byte map (each
+// token's wavefront marks its own, right after selecting them; plain byte
+// stores of 1, so no atomics); after a barrier one wavefront numbers them,
+// 64 experts per ballot, and scatters the weights.  The numbering
+// wavefront's LDS operations complete in order, so the other wavefronts need
+// a single barrier afterwards.
 // ---------------------------------------------------------------------------
 struct SlotLds {
-  uint32_t mark[MOE_MAX_E / 32];
-  int wbase[MOE_MAX_E / 32];
+  uint8_t sel[MOE_MAX_E];  // 1 = selected; then the expert's slot (< MOE_MAX_SLOTS <= 255)
   int expert[MOE_MAX_SLOTS];
   float w[MOE_MAX_SLOTS][8];
   int n_routed;
 };
+static_assert(MOE_MAX_SLOTS <= 255, "slot numbers fit the byte map");
 
-DEVI void build_slots_wave(SlotLds& S, const int32_t* idx, const float* w, int tk, int k, int T, int E,
-                           bool has_shared) {
+// Marks this lane's entries (lanes < n of the wavefront: ids out of range
+// are skipped).
+DEVI void mark_selected(SlotLds& S, const int32_t* idx, int n, int E) {
   const int lane = threadIdx.x & 63;
-  const int nwords = (E + 31) >> 5, base = has_shared ? 1 : 0;
+  for (int j = lane; j < n; j += 64) {
+    const int e = idx[j];
+    if (e >= 0 && e < E) S.sel[e] = 1;
+  }
+}
+
+// One wavefront: numbers the marked experts and fills the weight rows from
+// the T*k routing entries (idx, w).
+template <int NPER>
+DEVI void number_slots_wave(SlotLds& S, const int32_t* idx, const float* w, int tk, int k, int T, int E,
+                            bool has_shared) {
+  const int lane = threadIdx.x & 63, base = has_shared ? 1 : 0;
+  // every read first (the numbering overwrites the map)
+  bool mk[NPER];
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) mk[i] = S.sel[min(lane + 64 * i, E - 1)] != 0 && lane + 64 * i < E;
   int re[2];
   float rw[2];
-  bool ok[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int j = lane + 64 * h;
-    re[h] = (j < tk) ? idx[j] : -1;
-    rw[h] = (j < tk) ? w[j] : 0.f;
-    ok[h] = re[h] >= 0 && re[h] < E;
+    const int j = min(lane + 64 * h, tk - 1);
+    re[h] = lane + 64 * h < tk ? idx[j] : -1;
+    rw[h] = w[j];
   }
-  for (int i = lane; i < nwords; i += 64) S.mark[i] = 0u;
+  int n = 0;
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
-    if (ok[h]) atomicOr(&S.mark[re[h] >> 5], 1u << (re[h] & 31));
-  // exclusive prefix of the marked counts over the words (lane: words 2l, 2l+1)
-  const uint32_t m0 = (2 * lane < nwords) ? S.mark[2 * lane] : 0u;
-  const uint32_t m1 = (2 * lane + 1 < nwords) ? S.mark[2 * lane + 1] : 0u;
-  const int c0 = __popc(m0), c1 = __popc(m1);
-  int incl = c0 + c1;
-  for (int o = 1; o < 64; o <<= 1) {
-    const int v = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += v;
+  for (int i = 0; i < NPER; ++i) {
+    const int e = lane + 64 * i;
+    const bool m = mk[i];
+    const uint64_t M = __ballot(m);
+    const int slot = base + n + lanes_below(M);
+    if (m) {
+      S.expert[slot] = e;
+      S.sel[e] = (uint8_t)slot;
+    }
+    n += (int)__builtin_popcountll(M);
   }
-  const int excl = incl - c0 - c1;
-  if (2 * lane < nwords) S.wbase[2 * lane] = excl;
-  if (2 * lane + 1 < nwords) S.wbase[2 * lane + 1] = excl + c0;
-  const int n_routed = __shfl(incl, 63, 64);
-  if (lane == 0) S.n_routed = n_routed;
-  {
-    int slot = base + excl;
-    for (uint32_t m = m0; m; m &= m - 1u) S.expert[slot++] = 64 * lane + __builtin_ctz(m);
-    for (uint32_t m = m1; m; m &= m - 1u) S.expert[slot++] = 64 * lane + 32 + __builtin_ctz(m);
-  }
+  if (lane == 0) S.n_routed = n;
   if (has_shared && lane == 0) S.expert[0] = E;
-  const int ns = base + n_routed;
+  const int ns = base + n;
   for (int i = lane; i < ns * 8; i += 64) S.w[i >> 3][i & 7] = (has_shared && i < 8 && i < T) ? 1.0f : 0.f;
 #pragma unroll
   for (int h = 0; h < 2; ++h)
-    if (ok[h]) {
-      const int word = re[h] >> 5;
-      const int slot = base + S.wbase[word] + __popc(S.mark[word] & ((1u << (re[h] & 31)) - 1u));
-      S.w[slot][(lane + 64 * h) / k] = rw[h];
-    }
+    if (re[h] >= 0 && re[h] < E) S.w[S.sel[re[h]]][(lane + 64 * h) / k] = rw[h];
 }
 
 // ---------------------------------------------------------------------------
 // gate/up: a work item is (slot u, tile t of 16 intermediate rows); slot 0
 // is the shared expert when there is one, and its tiles come first.  One
-// workgroup of 16 wavefronts per CU (the grid is the CU count): it copies the
+// workgroup of 8 wavefronts per CU (the grid is the CU count): it copies the
 // activation fragments and block sums of the input into LDS once (one copy
-// serves all of its items), builds the slot list from the routing rows, and
-// then takes its items in rounds.  In a round, each item has KP wavefronts
+// serves all of its items), selects every token's experts (or takes the
+// given routing rows) and builds the slot list, and then takes its items in
+// rounds.  In a round, each item has KP wavefronts
 // that take every KP-th k-group (256 inputs) of it, KP in {1, 2, 4, 8} being
 // the largest that still gives every wavefront of the grid work.  A wavefront
 // keeps the gate and up chunks of two k-groups in flight ahead of the one it
@@ -265,22 +269,27 @@ __global__ __launch_bounds__(64 * GU_NW) void gu_decode_kernel(GuArgs a) {
   const float rnv = (tid >= 64 && tid < 64 + T) ? a.rnorm[tid - 64] : 1.0f;
   if (n_win == 1) stage_window(L, a, 0, 8 * n_kg, tid);
   if (tid >= 64 && tid < 72) L.rn[tid - 64] = 1.0f / rnv;
+  for (int i = tid; i < (E + 3) / 4; i += blockDim.x) reinterpret_cast<uint32_t*>(L.S.sel)[i] = 0u;
+  __syncthreads();  // byte map cleared before any wavefront marks
   if (select) {
     if (wv < T) {
       uint64_t key[NPER];
 #pragma unroll
       for (int i = 0; i < NPER; ++i) key[i] = (lane + 64 * i < E) ? sel_key(lv[i], lane + 64 * i) : 0ull;
       topk_keys<NPER>(key, E, k, L.tk_idx + wv * k, L.tk_w + wv * k, L.tk_buf[wv]);
+      mark_selected(L.S, L.tk_idx + wv * k, k, E);
     }
-    __syncthreads();
-    if (blockIdx.x == 0) {
-      for (int i = tid; i < tk; i += blockDim.x) {
-        if (a.out_idx) a.out_idx[i] = L.tk_idx[i];
-        if (a.out_w) a.out_w[i] = L.tk_w[i];
-      }
+  } else if (wv == 0) {
+    mark_selected(L.S, a.idx, tk, E);
+  }
+  __syncthreads();  // every token's experts marked
+  if (select && blockIdx.x == 0) {
+    for (int i = tid; i < tk; i += blockDim.x) {
+      if (a.out_idx) a.out_idx[i] = L.tk_idx[i];
+      if (a.out_w) a.out_w[i] = L.tk_w[i];
     }
   }
-  if (wv == 0) build_slots_wave(L.S, select ? L.tk_idx : a.idx, select ? L.tk_w : a.w, tk, k, T, E, has_shared);
+  if (wv == 0) number_slots_wave<NPER>(L.S, select ? L.tk_idx : a.idx, select ? L.tk_w : a.w, tk, k, T, E, has_shared);
   __syncthreads();  // slot list, rms and the staged activations
   if (blockIdx.x == 0) {
     const int ns = base + L.S.n_routed;
