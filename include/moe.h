@@ -144,8 +144,10 @@ int moe_workspace_bytes(const moe_layer *layer, int T, size_t *bytes);
 
 /* Clear the control words of a new workspace (enqueued on `stream`).  Must be
  * called once before a workspace is first used, and again if its memory has
- * been used for anything else in between.  The forward calls leave the
- * control words cleared for the next call. */
+ * been used for anything else in between.  The decode kernels (T <= 8) count
+ * finished workgroups in these words (the first 256 bytes); a workspace whose
+ * words are not zero gives wrong logits and routing.  The forward calls
+ * leave the control words cleared for the next call. */
 int moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
 /* One layer: y[T][d] = MoE(x[T][d]).  T = 0 is a no-op.  T <= 8 runs the
