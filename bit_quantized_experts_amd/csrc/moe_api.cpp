@@ -198,7 +198,7 @@ WsLayout ws_layout_decode(const moe_layer* L, int T) {
 // expert padded to a multiple of 16, then one row per token for the shared
 // expert (padded to 16).
 struct PfLayout {
-  int64_t ctrl, ex, xh, xl, logits, idx, w, tile_bm, tile_cnt, counts, offsets, n_items, item_group, item_row0,
+  int64_t ctrl, ex, xh, xl, logits, rpart, idx, w, tile_bm, tile_cnt, counts, offsets, n_items, item_group, item_row0,
       item_rows, row_src, row_tok, row_w, slot_pos, hfrag, ypart, rowf, total;
   int n_tiles, R, max_items, nbH, n_nt;
 };
@@ -206,6 +206,15 @@ struct PfLayout {
 int64_t routed_rows_max(int64_t T, int k, int E) {
   const int64_t pairs = T * k;
   return pairs + 15 * (pairs < E ? pairs : E);
+}
+
+// The prefill router GEMM has one workgroup per 128 tokens x 128 experts,
+// each over the whole input; with few of them (short chunks) it runs one
+// workgroup per 256-column slice as well and adds the slices in a second
+// kernel (same bits either way).
+bool router_split(const moe_layer* L, int T) {
+  const int n_tt = (T + 127) / 128, n_ey = (L->E16 + PF_ET - 1) / PF_ET;
+  return n_tt * n_ey <= 64;
 }
 
 PfLayout ws_layout_prefill(const moe_layer* L, int T) {
@@ -227,6 +236,7 @@ PfLayout ws_layout_prefill(const moe_layer* L, int T) {
   W.xh = take((int64_t)T * d * 2);
   W.xl = take((int64_t)T * d * 2);
   W.logits = take((int64_t)T * E * 4);
+  W.rpart = take(router_split(L, T) ? (int64_t)(d / 256) * T * E * 4 : 0);
   W.idx = take(pairs * 4);
   W.w = take(pairs * 4);
   W.tile_bm = take((int64_t)W.n_tiles * E * 8);
@@ -458,6 +468,8 @@ int prefill_layer(const moe_layer* L, const float* x, int norm, float eps, int T
     ra.E = E;
     ra.E16 = L->E16;
     ra.logits = (r && r->out_logits) ? r->out_logits : reinterpret_cast<float*>(ws + W.logits);
+    ra.split = router_split(L, T);
+    ra.part = reinterpret_cast<float*>(ws + W.rpart);
     timed_begin(5, s, &slot);
     serial_point(s);
     HIPCHK(launch_pf_router(ra, s));

@@ -137,6 +137,10 @@ struct PfRouterArgs {
   const float* bias;   // [E]
   int32_t T, d, E, E16;
   float* logits;  // [T][E]
+  // split = 1: one workgroup per 256-column slice (blockIdx.z) writes that
+  // slice's unscaled sums to part [d/256][T][E]; a reduce kernel adds them
+  int32_t split;
+  float* part;
 };
 
 struct PfGroupArgs {

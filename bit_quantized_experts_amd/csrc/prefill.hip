@@ -292,17 +292,23 @@ __global__ __launch_bounds__(256) void pf_router_kernel(PfRouterArgs a) {
   const int hl = wv >> 1, dkb = wv & 1;
   const _Float16* asrc = hl ? a.xl : a.xh;
 
-  float4_t acc[8][2];
+  // acc: the current 256-column slice (4 steps) from zero; tot: the slices
+  // added in order, so a split launch (one slice per workgroup, added by the
+  // reduce kernel in the same order) gives the same bits
+  float4_t acc[8][2], tot[8][2];
 #pragma unroll
   for (int rg = 0; rg < 8; ++rg)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[rg][j] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 2; ++j) acc[rg][j] = tot[rg][j] = float4_t{0.f, 0.f, 0.f, 0.f};
 
   constexpr int LOADS = 8 + KS * 2 * 2;
+  static_assert(256 / 32 == 4 * KS, "a slice is four steps");
   u32x4_t bh[3][KS][2], bl[3][KS][2];
-  const int nsteps = nb / KS;
-  auto issue = [&](auto P_, int s) {
+  const int sbase = a.split ? 4 * blockIdx.z : 0;  // first step of this workgroup
+  const int nsteps = a.split ? 4 : nb / KS;
+  auto issue = [&](auto P_, int ls) {
     constexpr int P = decltype(P_)::value;
+    const int s = sbase + ls;
     unsigned char* st = S.get<P>();
 #pragma unroll
     for (int rg = 0; rg < 8; ++rg)
@@ -317,7 +323,7 @@ __global__ __launch_bounds__(256) void pf_router_kernel(PfRouterArgs a) {
         bl[P][kb][j] = ld128(a.wl + off);
       }
   };
-  auto step = [&](auto P_, int s) {
+  auto step = [&](auto P_, int s) {  // s: step of this workgroup
     constexpr int P = decltype(P_)::value;
     if (s + 1 < nsteps) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -344,6 +350,15 @@ __global__ __launch_bounds__(256) void pf_router_kernel(PfRouterArgs a) {
             }
       }
     }
+    if ((s & 3) == 3) {  // end of a slice
+#pragma unroll
+      for (int rg = 0; rg < 8; ++rg)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          tot[rg][j] += acc[rg][j];
+          acc[rg][j] = float4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    }
   };
   issue(ic<0>{}, 0);
   if (nsteps > 1) issue(ic<1>{}, 1);
@@ -358,14 +373,34 @@ __global__ __launch_bounds__(256) void pf_router_kernel(PfRouterArgs a) {
     for (int j = 0; j < 2; ++j) {
       const int e = (et0 + j) * 16 + n;
       if (!(j == 0 ? act0 : act1) || e >= a.E) continue;
+      if (a.split) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = row0 + 16 * rg + 4 * q + i;
+          if (t < a.T) a.part[((size_t)blockIdx.z * a.T + t) * a.E + e] = tot[rg][j][i];
+        }
+        continue;
+      }
       const int ewe = a.ew[e];
       const float b = a.bias[e];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = row0 + 16 * rg + 4 * q + i;
-        if (t < a.T) a.logits[(size_t)t * a.E + e] = ldexpf(acc[rg][j][i], a.ex[t] + ewe) + b;
+        if (t < a.T) a.logits[(size_t)t * a.E + e] = ldexpf(tot[rg][j][i], a.ex[t] + ewe) + b;
       }
     }
+}
+
+// The slices of a split router launch added in slice order from zero (the
+// order the unsplit kernel uses), then scaled and biased.
+__global__ __launch_bounds__(256) void pf_router_reduce_kernel(PfRouterArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)a.T * a.E) return;
+  const int t = (int)(i / a.E), e = (int)(i - (int64_t)t * a.E);
+  const int ns = a.d / 256;
+  float tot = 0.f;
+  for (int z = 0; z < ns; ++z) tot += a.part[((size_t)z * a.T + t) * a.E + e];
+  a.logits[i] = ldexpf(tot, a.ex[t] + a.ew[e]) + a.bias[e];
 }
 
 // ---------------------------------------------------------------------------
@@ -629,7 +664,7 @@ DEVI void gate_up_item(const PfGemmArgs& a, const Stages& S, int* ex_lds, int g,
 #pragma unroll
     for (int m = 0; m < 4; ++m) load_half<BITS>(bw[P][m], cp[m] + (int64_t)(s >> 1) * CB, s & 1, lane);
   };
-  auto step = [&](auto P_, int s) {
+  auto step = [&](auto P_, int s) {  // s: step of this workgroup
     constexpr int P = decltype(P_)::value;
     if (s + 1 < nsteps) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -796,7 +831,7 @@ DEVI void down_item(const PfGemmArgs& a, const Stages& S, float* rowf_lds, int g
       }
     }
   };
-  auto step = [&](auto P_, int s) {
+  auto step = [&](auto P_, int s) {  // s: step of this workgroup
     constexpr int P = decltype(P_)::value;
     if (s + 1 < nsteps) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -941,7 +976,12 @@ hipError_t launch_pf_prep(const PfPrepArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_pf_router(const PfRouterArgs& a, hipStream_t s) {
-  MOE_LAUNCH(pf_router_kernel, dim3((a.T + 127) / 128, (a.E16 + PF_ET - 1) / PF_ET), dim3(256), 0, s, a);
+  MOE_LAUNCH(pf_router_kernel, dim3((a.T + 127) / 128, (a.E16 + PF_ET - 1) / PF_ET, a.split ? a.d / 256 : 1), dim3(256),
+             0, s, a);
+  if (a.split) {
+    const int64_t n = (int64_t)a.T * a.E;
+    hipLaunchKernelGGL(pf_router_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -165,6 +165,27 @@ def test_prefill_chunking_invariance(bqe):
     assert np.array_equal(y2.view(np.uint32), y.view(np.uint32))
 
 
+def test_prefill_router_split_same_bits(bqe):
+    # short chunks run the router GEMM split into 256-column slices (added in
+    # slice order by a second kernel), long ones unsplit with the same slice
+    # order in registers: a token's logits, routing and output do not depend
+    # on which one ran
+    wl = mi.WORKLOADS["prefill"]
+    L = packed_layer(wl, 0)
+    T_long, T_short = 8320, 256  # 65 x 4 router workgroups (unsplit) vs 2 x 4 (split)
+    x = mi.activations(wl, T=T_long, stream=21)
+    y, lg, i, w = _forward(bqe, L, x)
+    ys, lgs, is_, ws_ = _forward(bqe, L, x[:T_short])
+    say(f"[prefill] router split vs unsplit: T={T_short} / {T_long}")
+    assert np.array_equal(lgs.view(np.uint32), lg[:T_short].view(np.uint32))
+    assert np.array_equal(is_, i[:T_short]) and np.array_equal(ws_.view(np.uint32), w[:T_short].view(np.uint32))
+    assert np.array_equal(ys.view(np.uint32), y[:T_short].view(np.uint32))
+    # and the split logits against the fp64 router
+    W, b = mi.router(wl, 0)
+    ol = oracle.router_logits(x[:64], W, b)
+    assert rel_err_inf(lgs[:64], ol) < 1e-5
+
+
 def test_prefill_forced_routing_invalid_and_repeated(bqe):
     wl = mi.small(mi.WORKLOADS["tiny"], Is=64, E=24, k=4)
     L = packed_layer(wl, 0)
