@@ -158,8 +158,11 @@ def bench_prefill(args):
     torch.cuda.synchronize()
     idx_np = idx.cpu().numpy()
     kdur = {}
-    for cls, name in ((bqe.TIMING_PREFILL_GATE_UP, "gate_up"), (bqe.TIMING_PREFILL_DOWN, "down"),
-                      (bqe.TIMING_PREFILL_ROUTER, "router")):
+    # short chunks run the decode kernels (8 tokens at a time): time those
+    classes = ((bqe.TIMING_GATE_UP, "gate_up"), (bqe.TIMING_DOWN, "down"), (bqe.TIMING_ROUTER, "router")) \
+        if T <= bqe.MAX_TOK_DECODE_KERNELS else \
+        ((bqe.TIMING_PREFILL_GATE_UP, "gate_up"), (bqe.TIMING_PREFILL_DOWN, "down"), (bqe.TIMING_PREFILL_ROUTER, "router"))
+    for cls, name in classes:
         tot, n = 0.0, 0
         for _ in range(5):
             bqe.moe_timing_start(cls, 1)

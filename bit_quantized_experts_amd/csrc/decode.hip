@@ -88,10 +88,11 @@ DEVI void mark_selected(SlotLds& S, const int32_t* idx, int n, int E) {
 }
 
 // One wavefront: numbers the marked experts and fills the weight rows from
-// the T*k routing entries (idx, w).
+// the T*k routing entries (idx, w); with dedup (given routing rows) a repeated
+// id in a token's row keeps its first entry's weight (a selection has none).
 template <int NPER>
 DEVI void number_slots_wave(SlotLds& S, const int32_t* idx, const float* w, int tk, int k, int T, int E,
-                            bool has_shared) {
+                            bool has_shared, bool dedup) {
   const int lane = threadIdx.x & 63, base = has_shared ? 1 : 0;
   // every read first (the numbering overwrites the map)
   bool mk[NPER];
@@ -123,8 +124,13 @@ DEVI void number_slots_wave(SlotLds& S, const int32_t* idx, const float* w, int 
   const int ns = base + n;
   for (int i = lane; i < ns * 8; i += 64) S.w[i >> 3][i & 7] = (has_shared && i < 8 && i < T) ? 1.0f : 0.f;
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
-    if (re[h] >= 0 && re[h] < E) S.w[S.sel[re[h]]][(lane + 64 * h) / k] = rw[h];
+  for (int h = 0; h < 2; ++h) {
+    const int j = lane + 64 * h, t = j / k;
+    bool use = re[h] >= 0 && re[h] < E;
+    if (dedup && use)  // a repeated id in a token's row: the first occurrence only
+      for (int r = t * k; r < j; ++r) use = use && idx[r] != re[h];
+    if (use) S.w[S.sel[re[h]]][t] = rw[h];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -283,13 +289,14 @@ __global__ __launch_bounds__(64 * GU_NW) void gu_decode_kernel(GuArgs a) {
     mark_selected(L.S, a.idx, tk, E);
   }
   __syncthreads();  // every token's experts marked
-  if (select && blockIdx.x == 0) {
+  if (blockIdx.x == 0) {  // the routing used (given rows are copied as they are)
     for (int i = tid; i < tk; i += blockDim.x) {
-      if (a.out_idx) a.out_idx[i] = L.tk_idx[i];
-      if (a.out_w) a.out_w[i] = L.tk_w[i];
+      if (a.out_idx) a.out_idx[i] = select ? L.tk_idx[i] : a.idx[i];
+      if (a.out_w) a.out_w[i] = select ? L.tk_w[i] : a.w[i];
     }
   }
-  if (wv == 0) number_slots_wave<NPER>(L.S, select ? L.tk_idx : a.idx, select ? L.tk_w : a.w, tk, k, T, E, has_shared);
+  if (wv == 0)
+    number_slots_wave<NPER>(L.S, select ? L.tk_idx : a.idx, select ? L.tk_w : a.w, tk, k, T, E, has_shared, !select);
   __syncthreads();  // slot list, rms and the staged activations
   if (blockIdx.x == 0) {
     const int ns = base + L.S.n_routed;

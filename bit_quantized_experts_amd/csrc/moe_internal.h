@@ -26,6 +26,9 @@
 
 #define MOE_BLOCK 32
 #define MOE_MAX_TOK_DECODE 8
+// Calls with up to this many tokens run the decode kernels, in chunks of
+// MOE_MAX_TOK_DECODE (faster than the grouped GEMMs at these sizes).
+#define MOE_MAX_TOK_CHUNKED 16
 #define MOE_MAX_TOK_PREFILL 65536
 #define MOE_MAX_K 16
 #define MOE_MAX_E 4096

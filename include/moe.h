@@ -80,9 +80,10 @@ typedef struct moe_layer moe_layer;
 
 /* Optional routing inputs/outputs of moe_layer_forward.
  *   in_idx/in_w   [T][k]: if both non-NULL the router is skipped and this
- *                 routing is used (rank order; expert ids must be in [0,E)
- *                 and distinct within a row; an entry outside [0,E) is
- *                 skipped, i.e. contributes nothing).
+ *                 routing is used (rank order; expert ids should be in
+ *                 [0,E) and distinct within a row; an entry outside [0,E)
+ *                 is skipped, i.e. contributes nothing, and a repeated id
+ *                 uses its first entry only).
  *   out_logits    [T][E]: router logits (ignored when routing is forced).
  *   out_idx/out_w [T][k]: the routing used.
  * Any pointer may be NULL. */
@@ -144,28 +145,30 @@ int moe_workspace_bytes(const moe_layer *layer, int T, size_t *bytes);
 
 /* Clear the control words of a new workspace (enqueued on `stream`).  Must be
  * called once before a workspace is first used, and again if its memory has
- * been used for anything else in between.  The decode kernels (T <= 8) count
+ * been used for anything else in between.  The decode kernels (T <= 16) count
  * finished workgroups in these words (the first 256 bytes); a workspace whose
  * words are not zero gives wrong logits and routing.  The forward calls
  * leave the control words cleared for the next call. */
 int moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
-/* One layer: y[T][d] = MoE(x[T][d]).  T = 0 is a no-op.  T <= 8 runs the
- * decode/verify kernels (experts streamed once per call with 128-bit loads
- * and multiplied from their codes, activations carried as fp16 hi + lo);
- * 8 < T <= 65536 runs the chunked-prefill kernels: the (token, slot) pairs
- * are grouped by expert (as moe_group_tokens) and each expert's rows go
- * through a grouped matrix multiply on the matrix cores with the weights
- * dequantized in registers to fp16 and the activations rounded to fp16
- * after an exact per-row power-of-two scaling (fp32 accumulation).  In the
- * prefill path a token's routing row with a repeated expert id uses the
- * first occurrence only.  x and y must not alias.  `route` may be NULL.
- * ws_bytes >= moe_workspace_bytes(layer, T). */
+/* One layer: y[T][d] = MoE(x[T][d]).  T = 0 is a no-op.  T <= 16 runs the
+ * decode/verify kernels, 8 tokens at a time (experts streamed once per
+ * call with 128-bit loads and multiplied from their codes, activations
+ * carried as fp16 hi + lo); 16 < T <= 65536 runs the chunked-prefill
+ * kernels: the (token, slot) pairs are grouped by expert (as
+ * moe_group_tokens) and each expert's rows go through a grouped matrix
+ * multiply on the matrix cores with the weights dequantized in registers to
+ * fp16 and the activations rounded to fp16 after an exact per-row
+ * power-of-two scaling (fp32 accumulation).  With given routing (in_idx,
+ * in_w) a token's row with a repeated expert id uses the first occurrence
+ * only, and ids outside [0, E) are skipped.  x and y must not alias.
+ * `route` may be NULL.  ws_bytes >= moe_workspace_bytes(layer, T). */
 int moe_layer_forward(const moe_layer *layer, const float *x, int T, float *y, const moe_route_io *route,
                       void *ws, size_t ws_bytes, void *stream);
 
 /* A stack of layers with RMSNorm (unit weight) between consecutive layers
- * (T <= 8: decode kernels; T > 8: prefill kernels, one layer after another):
+ * (T <= 16: decode kernels, the whole stack for 8 tokens at a time; T > 16:
+ * prefill kernels, one layer after another):
  *   h_0 = x,  y_l = MoE_l(h_l),  h_{l+1} = y_l / sqrt(mean(y_l^2) + eps),
  *   y = y_{n-1}.
  * All layers must have equal d_model.  Optional per-layer outputs:

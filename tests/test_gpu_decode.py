@@ -160,30 +160,36 @@ def test_layer_odd_shapes(bqe):
             _check_layer(wl, 0, L, x, bqe, f"odd {kw} T={T}")
 
 
-def test_forced_routing_and_invalid_entries(bqe):
+@pytest.mark.parametrize("T", [6, 12])
+def test_forced_routing_and_invalid_entries(bqe, T):
+    # T = 12: two chunks of the decode kernels (routing rows offset per chunk)
     wl = mi.small(mi.WORKLOADS["tiny"], Is=64)
     L = packed_layer(wl, 0)
-    T = 6
     x_np = mi.activations(wl, T=T, stream=7)
     g = np.random.default_rng(9)
     idx = np.stack([g.permutation(wl.E)[:wl.k] for _ in range(T)]).astype(np.int32)
     w = g.random((T, wl.k)).astype(np.float32)
     idx[2, 1] = wl.E + 5   # out of range: skipped
     idx[4, 0] = -1         # out of range: skipped
+    idx[5, 1] = idx[5, 0]  # repeated: the first occurrence only
+    if T > 8:
+        idx[10, 0] = idx[10, 1]
     x = activations_device(x_np)
     y = torch.empty((T, wl.d), dtype=torch.float32, device=DEV)
     fi = torch.from_numpy(idx).to(DEV)
     fw = torch.from_numpy(w).to(DEV)
+    oi = torch.empty((T, wl.k), dtype=torch.int32, device=DEV)
+    ow = torch.empty((T, wl.k), dtype=torch.float32, device=DEV)
     ws = bqe.new_workspace(L.workspace_bytes(T))
-    r = bqe.RouteIO(fi.data_ptr(), fw.data_ptr(), None, None, None)
+    r = bqe.RouteIO(fi.data_ptr(), fw.data_ptr(), None, oi.data_ptr(), ow.data_ptr())
     bqe.moe_layer_forward(L.handle, x, y, ws, r)
     torch.cuda.synchronize()
+    assert np.array_equal(oi.cpu().numpy(), idx) and np.array_equal(ow.cpu().numpy(), w)
     wz = w.copy()
-    wz[2, 1] = 0.0
-    wz[4, 0] = 0.0
     iz = idx.copy()
-    iz[2, 1] = 0
-    iz[4, 0] = 0
+    for t, rr in [(2, 1), (4, 0), (5, 1)] + ([(10, 1)] if T > 8 else []):
+        wz[t, rr] = 0.0
+        iz[t, rr] = 0
     OL = oracle_layer(wl, 0, iz.reshape(-1))
     oy, _, _, _ = oracle.layer_forward(OL, x_np, force_idx=iz, force_w=wz)
     assert rel_err_inf(y.cpu().numpy(), oy) <= TOL_LAYER
