@@ -933,24 +933,30 @@ DEVI float4_t half4_to_float4(const _Float16* p) {
 }
 
 __global__ __launch_bounds__(256) void pf_combine_kernel(PfCombineArgs a) {
-  __shared__ int pos[MOE_MAX_K + 1];
-  const int t = blockIdx.x;
-  if (threadIdx.x < a.k) pos[threadIdx.x] = a.slot_pos[(size_t)t * a.k + threadIdx.x];
-  if (threadIdx.x == 0) pos[MOE_MAX_K] = a.has_shared ? a.offsets[a.E] + t : -1;
-  __syncthreads();
-  __shared__ float f[MOE_MAX_K + 1];
-  if (threadIdx.x <= MOE_MAX_K) {
-    const int p = threadIdx.x < a.k ? pos[threadIdx.x] : (threadIdx.x == MOE_MAX_K ? pos[MOE_MAX_K] : -1);
-    f[threadIdx.x] = p >= 0 ? a.rowf[p] : 0.f;
+  // every thread reads the token's row positions (one round trip), then all
+  // row factors and row pieces at once (a second one); the sum is formed in
+  // rank order, the shared row last.  Unused ranks (r >= k, skipped entries)
+  // load row 0 and are left out of the sum.
+  constexpr int NR = MOE_MAX_K + 1;
+  const int t = blockIdx.x, k = a.k;
+  int pos[NR];
+#pragma unroll
+  for (int r = 0; r < MOE_MAX_K; ++r) {
+    const int p = a.slot_pos[(size_t)t * k + min(r, k - 1)];
+    pos[r] = r < k ? p : -1;
   }
-  __syncthreads();
+  pos[MOE_MAX_K] = a.has_shared ? a.offsets[a.E] + t : -1;
+  float f[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) f[r] = a.rowf[max(pos[r], 0)];
   for (int c = 4 * threadIdx.x; c < a.d; c += 1024) {
+    float4_t v[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) v[r] = half4_to_float4(a.yh + (size_t)max(pos[r], 0) * a.d + c);
     float4_t acc = float4_t{0.f, 0.f, 0.f, 0.f};
-    for (int r = 0; r < a.k; ++r) {
-      const int p = pos[r];
-      if (p >= 0) acc += f[r] * half4_to_float4(a.yh + (size_t)p * a.d + c);
-    }
-    if (pos[MOE_MAX_K] >= 0) acc += f[MOE_MAX_K] * half4_to_float4(a.yh + (size_t)pos[MOE_MAX_K] * a.d + c);
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+      if (pos[r] >= 0) acc += f[r] * v[r];
     *reinterpret_cast<float4_t*>(a.y + (size_t)t * a.d + c) = acc;
   }
 }
