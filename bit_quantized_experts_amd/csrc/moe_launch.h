@@ -10,13 +10,13 @@
 // routed experts, plus the shared expert.
 #define MOE_MAX_SLOTS (MOE_MAX_TOK_DECODE * MOE_MAX_K + 1)
 // Columns of the layer input handled by one route workgroup.
-#define MOE_ROUTE_COLS 256
+#define MOE_ROUTE_COLS 128
 // Expert rows per route workgroup (4 waves x 16 rows).
 #define MOE_ROUTE_ROWS 64
 // Most down-projection splits (partial sums a consumer adds up).
 #define MOE_MAX_IN_SPLITS 8
 // Most column slices of the router (d <= 8192).
-#define MOE_MAX_CS 32
+#define MOE_MAX_CS 64
 // Control words of the workspace used by the route kernel: one completion
 // counter per row slice (E <= 4096: at most 64).
 #define MOE_CTRL_WORDS 64
@@ -43,7 +43,7 @@ struct RouteArgs {
   const _Float16* wh;  // router rows times 2^-ew, fp16 hi part, B-fragments [E16/16][d/32][64][8]
   const _Float16* wl;  // same, lo part
   int32_t T, d, E, code_off, do_logits;
-  float* lp;        // ws [d/256][T][E] partial logits
+  float* lp;        // ws [d/MOE_ROUTE_COLS][T][E] partial logits
   _Float16* xfrag;  // ws [d/32][64][8]
   float* xsum;      // ws [d/32][16]
   float* y_out;     // optional: the summed input, [T][d]

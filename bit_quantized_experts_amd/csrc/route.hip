@@ -7,7 +7,7 @@
 //
 // Decode (T <= 8) splits the router GEMV over column slices of the input so
 // that no workgroup needs the whole input row: the previous layer's output
-// arrives as split partial sums, and each workgroup adds only the 256 columns
+// arrives as split partial sums, and each workgroup adds only the 128 columns
 // it multiplies.  RMSNorm is a per-token scale, so it is applied after the
 // dot products (logit = (y . w) / rms(y) + bias) and, in the expert kernels,
 // to the accumulators before the SwiGLU nonlinearity.
@@ -123,25 +123,27 @@ DEVI void route_finish(const RouteArgs& a, int rs) {
   if (!count_done(a.sel.ctrl + rs, (uint32_t)a.sel.n_cs, &flag)) return;
   if (threadIdx.x == 0) a.sel.ctrl[rs] = 0u;
   if (a.sel.n_cs <= 16) finish_slice<16>(a, rs);
-  else finish_slice<32>(a, rs);
+  else if (a.sel.n_cs <= 32) finish_slice<32>(a, rs);
+  else finish_slice<64>(a, rs);
 }
 
 // ---------------------------------------------------------------------------
-// Route: workgroup (column slice cs of 256 inputs, row slice rs of 64
+// Route: workgroup (column slice cs of 128 inputs, row slice rs of 64
 // experts).  Sums the input splits for its columns, writes partial logits of
-// its 64 experts over those columns; the rs == 0 workgroups also write the
-// partial sums of squares, the summed input (if asked) and the fp16 hi/lo
-// MFMA A-fragments of the 8 blocks of the slice:
+// its 64 experts over those columns and the slice's sums of squares (every
+// row slice its own copy); the rs == 0 workgroups also write the summed input
+// (if asked) and the fp16 hi/lo MFMA A-fragments of the 4 blocks of the
+// slice:
 //   lane L = m + 16q of block b holds row m (m < 8: token m, hi part; m >= 8:
 //   token m-8, lo part) at inputs 8q..8q+7; xsum[b][m] = -code_off * sum.
 // The partial logits run on the matrix cores: the same A-fragments (built in
 // registers by every workgroup) times the router rows prepared at pack time
 // as 2^ew (wh + wl), fp16 hi and lo B-fragments, so one wavefront's 16
-// experts over the 8 blocks take 16 v_mfma_f32_16x16x32_f16 and the hi and lo
+// experts over the 4 blocks take 8 v_mfma_f32_16x16x32_f16 and the hi and lo
 // rows of a token are added once at the end.  All four products of the
 // ~22-bit operands are formed exactly; the rounding is fp32 accumulation.
 // The power of two 2^ew of each router row is applied to the summed
-// partials (exact) when the selection (above) adds them up.
+// partials (exact) by the workgroup that finishes the row slice (above).
 // ---------------------------------------------------------------------------
 DEVI half8_t x_fragment(const float (*ys)[MOE_ROUTE_COLS], int bl, int lane, int T, float* sum) {
   const int m = lane & 15, q = lane >> 4, tok = m & 7, lo = m >> 3;
@@ -180,11 +182,12 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   // address, so the wait counts before the first add are exact)
   const int et = rs * (MOE_ROUTE_ROWS / 16) + wv;  // 16-expert tile
   const bool tile_ok = a.do_logits && et * 16 < E;
-  constexpr int PER = MOE_MAX_TOK_DECODE * 64 / 256;  // float4 per thread
+  constexpr int RQ = MOE_ROUTE_COLS / 4;                   // float4 per token row of the slice
+  constexpr int PER = (MOE_MAX_TOK_DECODE * RQ + 255) / 256;  // float4 per thread
   float4_t v[PER][MOE_MAX_IN_SPLITS];
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    const int i = tid + 256 * j, t = min(i >> 6, T - 1), c4 = i & 63;
+    const int i = tid + 256 * j, t = min(i / RQ, T - 1), c4 = i % RQ;
     const float* src = a.in + (size_t)t * d + c0 + 4 * c4;
 #pragma unroll
     for (int s = 0; s < MOE_MAX_IN_SPLITS; ++s)
@@ -205,7 +208,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   // summed input slice into LDS (splits added in order)
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    const int i = tid + 256 * j, t = i >> 6, c4 = i & 63;
+    const int i = tid + 256 * j, t = i / RQ, c4 = i % RQ;
     if (t < T) {
       float4_t acc = v[j][0];
 #pragma unroll
@@ -219,7 +222,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
 
   // sums of squares of the slice (each row slice keeps its own copy)
   for (int t = wv; t < T; t += 4) {
-    const float4 v = *reinterpret_cast<const float4*>(&ys[t][4 * lane]);
+    const float4 v = lane < RQ ? *reinterpret_cast<const float4*>(&ys[t][4 * lane]) : float4{0.f, 0.f, 0.f, 0.f};
     const float ss = wave_sum(v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w);
     if (lane == 0) st_dev(a.sel.ss_part + ((size_t)rs * gridDim.x + cs) * T + t, ss);
   }
