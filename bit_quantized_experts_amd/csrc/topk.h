@@ -33,7 +33,8 @@ DEVI int key_index(uint64_t k) { return (int)(0xFFFFFFFFu - (uint32_t)k); }
 //      the 64 lane maxima of the keys' value words (high 32 bits), found bit
 //      by bit from the most significant with ballots.  At least k keys have a
 //      value word >= theta (those k lane maxima), and every key of the top k
-//      does (a smaller one would rank below those k keys).
+//      does (a smaller one would rank below those k keys).  The search takes
+//      two bits per step (three ballots against independent thresholds).
 //   2. If at most 64 keys reach theta they are compacted to LDS, each is
 //      ranked by counting the larger candidates, and the first k ranks are
 //      the answer.  Otherwise (many equal logits) a radix search on the value
@@ -45,8 +46,8 @@ DEVI int key_index(uint64_t k) { return (int)(0xFFFFFFFFu - (uint32_t)k); }
 // weights: m = logit of rank 0, e_r = exp64(l_r - m), S = sum of e_r in rank
 // order, w_r = fp32(e_r / S).  `buf`: this wave's 96 LDS entries.  NPER >=
 // ceil(E / 64).  The work is a single wavefront's dependent chain, so the
-// loops stay short: 32 ballot steps for theta and one step per candidate
-// for the ranks.
+// loops stay short: 16 steps for theta and one step per candidate for the
+// ranks.
 DEVI int lanes_below(uint64_t m) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
@@ -90,10 +91,15 @@ DEVI void topk_keys(const uint64_t (&key)[NPER], int E, int k, int32_t* idx_out,
   uint32_t lhi = 0;
 #pragma unroll
   for (int i = 0; i < NPER; ++i) lhi = max(lhi, (uint32_t)(key[i] >> 32));
+  // two bits per step (the three trial thresholds are independent, so the
+  // dependent chain is 16 steps long; same result as one bit per step)
   uint32_t theta = 0;
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t t = theta | (1u << b);
-    if ((int)__builtin_popcountll(__ballot(lhi >= t)) >= k) theta = t;
+  for (int b = 30; b >= 0; b -= 2) {
+    const uint32_t t1 = theta | (1u << b), t2 = theta | (2u << b), t3 = theta | (3u << b);
+    const int c1 = (int)__builtin_popcountll(__ballot(lhi >= t1));
+    const int c2 = (int)__builtin_popcountll(__ballot(lhi >= t2));
+    const int c3 = (int)__builtin_popcountll(__ballot(lhi >= t3));
+    theta = c3 >= k ? t3 : c2 >= k ? t2 : c1 >= k ? t1 : theta;
   }
   int c = 0;
 #pragma unroll
@@ -153,6 +159,7 @@ DEVI void topk_keys(const uint64_t (&key)[NPER], int E, int k, int32_t* idx_out,
   // first k ranks are the result
   const uint64_t mine = (lane < n) ? buf[lane] : 0ull;
   int rank = 0;
+#pragma unroll 4
   for (int j = 0; j < n; ++j) rank += (readlane_u64(mine, j) > mine) ? 1 : 0;
   if (lane < n && rank < k) buf[64 + rank] = mine;
   const uint64_t kr = (lane < k) ? buf[64 + lane] : 0ull;
