@@ -804,8 +804,7 @@ DEVI void down_item(const PfGemmArgs& a, const Stages& S, float* rowf_lds, int g
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[rg][t] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  constexpr int LOADS = NRG + M::NC * (BITS == 3 ? 3 : 2);
-  WRegs bw[3][M::NC];
+  WRegs bw[2][M::NC];
   auto issue = [&](auto P_, int s) {
     constexpr int P = decltype(P_)::value;
     unsigned char* st = S.get<P>();
@@ -831,50 +830,35 @@ DEVI void down_item(const PfGemmArgs& a, const Stages& S, float* rowf_lds, int g
       }
     }
   };
+  // Two stages, the next step's loads issued one step ahead: two workgroups
+  // share a CU (64 KB of LDS and at most 256 registers per wave each), so
+  // one's loads, epilogue and prologue run under the other's multiplies.
+  // Blocks are multiplied one at a time (one block's A and B fragments live).
   auto step = [&](auto P_, int s) {  // s: step of this workgroup
     constexpr int P = decltype(P_)::value;
-    if (s + 1 < nsteps) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __syncthreads();
-    if (s + 2 < nsteps) issue(ic<(P + 2) % 3>{}, s + 2);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();  // the other stage is free (every wave is past step s - 1)
+    if (s + 1 < nsteps) issue(ic<(P + 1) % 2>{}, s + 1);
     const unsigned char* st = S.get<P>();
     const int nj = min(4, nbK - 4 * s);
-    if (nj == 4) {
-      half8_t A[4][NRG], B[4][4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 4; ++j) {
+      if (j >= nj) break;
+      half8_t B[4];
 #pragma unroll
-        for (int rg = 0; rg < NRG; ++rg) A[j][rg] = *reinterpret_cast<const half8_t*>(st + (rg * 4 + j) * 1024 + 16 * lane);
+      for (int t = 0; t < 4; ++t) B[t] = dequant<BITS>(bw[P][M::chunk(t, j)], M::frag(t, j));
 #pragma unroll
-        for (int t = 0; t < 4; ++t) B[j][t] = dequant<BITS>(bw[P][M::chunk(t, j)], M::frag(t, j));
+      for (int rg = 0; rg < NRG; ++rg) {
+        const half8_t A = *reinterpret_cast<const half8_t*>(st + (rg * 4 + j) * 1024 + 16 * lane);
 #pragma unroll
-        for (int rg = 0; rg < NRG; ++rg)
-#pragma unroll
-          for (int t = 0; t < 4; ++t) acc[rg][t] = mfma16x16x32(A[j][rg], B[j][t], acc[rg][t]);
-      }
-      step_schedule4<NRG, (BITS == 3 ? 20 : 12) * 4 / (4 * NRG) + 1>();
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (j >= nj) break;
-        half8_t B[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) B[t] = dequant<BITS>(bw[P][M::chunk(t, j)], M::frag(t, j));
-#pragma unroll
-        for (int rg = 0; rg < NRG; ++rg) {
-          const half8_t A = *reinterpret_cast<const half8_t*>(st + (rg * 4 + j) * 1024 + 16 * lane);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) acc[rg][t] = mfma16x16x32(A, B[t], acc[rg][t]);
-        }
+        for (int t = 0; t < 4; ++t) acc[rg][t] = mfma16x16x32(A, B[t], acc[rg][t]);
       }
     }
   };
   issue(ic<0>{}, 0);
-  if (nsteps > 1) issue(ic<1>{}, 1);
-  for (int s = 0; s < nsteps; s += 3) {
+  for (int s = 0; s < nsteps; s += 2) {
     step(ic<0>{}, s);
     if (s + 1 < nsteps) step(ic<1>{}, s + 1);
-    if (s + 2 < nsteps) step(ic<2>{}, s + 2);
   }
   // rows stored as fp16(sum 2^-ed) (below 2^15, see the pack-time bound);
   // the combine multiplies them by rowf = w 2^(hb + 2 ex + ed).  The tile
@@ -907,10 +891,10 @@ DEVI void down_item(const PfGemmArgs& a, const Stages& S, float* rowf_lds, int g
 }
 
 template <int BITS, int BK>
-__global__ __launch_bounds__(256) void pf_down_kernel(PfGemmArgs a) {
+__global__ __launch_bounds__(256, 2) void pf_down_kernel(PfGemmArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char st0[GEMM_STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char st1[GEMM_STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char st2[GEMM_STAGE];
+  unsigned char* const st2 = st0;  // (two stages; a third is never used)
   __shared__ float rowf_lds[PF_TM];
   int item, nt;
   if (!xcd_tile(*a.n_items, a.d / PF_DT, &item, &nt)) return;
