@@ -575,38 +575,6 @@ DEVI bool xcd_tile(int n_items, int n_nt, int* item, int* nt) {
   return li < ipx && *item < n_items;
 }
 
-// Scheduling hint for one block of a step: spread NV vector-ALU and ND LDS
-// reads (the next block's operands) between the NM matrix multiplies, so a
-// single wave keeps the matrix core busy while it dequantizes.
-template <int NM, int ND, int NV>
-DEVI void interleave() {
-  constexpr int VPER = (NV + NM - 1) / NM;
-#pragma unroll
-  for (int i = 0; i < NM; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    if (i < ND) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-    __builtin_amdgcn_sched_group_barrier(0x002, VPER, 0);  // VALU
-  }
-}
-
-// Schedule of one four-block step with NRG row groups: the first block's NRG
-// LDS reads and 4 dequantizations, then each block's 4 NRG multiplies, the
-// next block's LDS reads spread one after each of the first NRG multiplies
-// and VPER vector instructions (the next block's dequantization) after each.
-template <int NRG, int VPER>
-DEVI void step_schedule4() {
-  __builtin_amdgcn_sched_group_barrier(0x100, NRG, 0);
-  __builtin_amdgcn_sched_group_barrier(0x002, 48, 0);
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-    for (int i = 0; i < 4 * NRG; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (kb < 3 && i < NRG) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (kb < 3) __builtin_amdgcn_sched_group_barrier(0x002, VPER, 0);
-    }
-}
-
 template <int BITS, int NRG>
 DEVI void gate_up_item(const PfGemmArgs& a, const Stages& S, int* ex_lds, int g, int row0, int rows, int nt) {
   const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, n = lane & 15, q = lane >> 4;
@@ -651,9 +619,7 @@ DEVI void gate_up_item(const PfGemmArgs& a, const Stages& S, int* ex_lds, int g,
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[rg][m] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  // every wave issues the same number of loads per step
-  constexpr int LOADS = NRG + (BITS == 3 ? 12 : 8);
-  WRegs bw[3][4];
+  WRegs bw[2][4];
   const int nsteps = a.d / 128;
   auto issue = [&](auto P_, int s) {
     constexpr int P = decltype(P_)::value;
@@ -664,37 +630,35 @@ DEVI void gate_up_item(const PfGemmArgs& a, const Stages& S, int* ex_lds, int g,
 #pragma unroll
     for (int m = 0; m < 4; ++m) load_half<BITS>(bw[P][m], cp[m] + (int64_t)(s >> 1) * CB, s & 1, lane);
   };
+  // Two stages, the next step's loads issued one step ahead: two workgroups
+  // share a CU (64 KB of LDS and at most 256 registers per wave each), so
+  // one's loads, epilogue and prologue run under the other's multiplies.
+  // Blocks are multiplied one at a time (one block's A and B fragments live).
   auto step = [&](auto P_, int s) {  // s: step of this workgroup
     constexpr int P = decltype(P_)::value;
-    if (s + 1 < nsteps) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __syncthreads();
-    if (s + 2 < nsteps) issue(ic<(P + 2) % 3>{}, s + 2);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();  // the other stage is free (every wave is past step s - 1)
+    if (s + 1 < nsteps) issue(ic<(P + 1) % 2>{}, s + 1);
     if (act) {
       const unsigned char* st = S.get<P>();
-      // the 4 blocks of the step: block kb + 1's LDS reads and dequantized
-      // weights are produced in between block kb's multiplies (schedule below)
-      half8_t A[4][NRG], B[4][4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
+        half8_t B[4];
 #pragma unroll
-        for (int rg = 0; rg < NRG; ++rg) A[kb][rg] = *reinterpret_cast<const half8_t*>(st + rg * 4096 + xs[kb]);
+        for (int m = 0; m < 4; ++m) B[m] = dequant<BITS>(bw[P][m], kb);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) B[kb][m] = dequant<BITS>(bw[P][m], kb);
+        for (int rg = 0; rg < NRG; ++rg) {
+          const half8_t A = *reinterpret_cast<const half8_t*>(st + rg * 4096 + xs[kb]);
 #pragma unroll
-        for (int rg = 0; rg < NRG; ++rg)
-#pragma unroll
-          for (int m = 0; m < 4; ++m) acc[rg][m] = mfma16x16x32(A[kb][rg], B[kb][m], acc[rg][m]);
+          for (int m = 0; m < 4; ++m) acc[rg][m] = mfma16x16x32(A, B[m], acc[rg][m]);
+        }
       }
-      step_schedule4<NRG, (BITS == 3 ? 20 : 12) * 4 / (4 * NRG) + 1>();
     }
   };
   issue(ic<0>{}, 0);
-  if (nsteps > 1) issue(ic<1>{}, 1);
-  for (int s = 0; s < nsteps; s += 3) {
+  for (int s = 0; s < nsteps; s += 2) {
     step(ic<0>{}, s);
     if (s + 1 < nsteps) step(ic<1>{}, s + 1);
-    if (s + 2 < nsteps) step(ic<2>{}, s + 2);
   }
 
   // epilogue: g, u scaled back by 2^ex of the row's token, h = silu(g) u,
@@ -738,10 +702,10 @@ DEVI void gate_up_item(const PfGemmArgs& a, const Stages& S, int* ex_lds, int g,
 }
 
 template <int BITS>
-__global__ __launch_bounds__(256) void pf_gate_up_kernel(PfGemmArgs a) {
+__global__ __launch_bounds__(256, 2) void pf_gate_up_kernel(PfGemmArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char st0[GEMM_STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char st1[GEMM_STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char st2[GEMM_STAGE];
+  unsigned char* const st2 = st0;  // (two stages; a third is never used)
   __shared__ int ex_lds[PF_TM];
   int item, nt;
   if (!xcd_tile(*a.n_items, a.n_nt, &item, &nt)) return;
