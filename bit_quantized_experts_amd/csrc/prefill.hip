@@ -208,19 +208,30 @@ __global__ __launch_bounds__(256) void pack_hbound_kernel(const uint8_t* canon, 
 // prep: one wave per token row.  With norm set the row is first divided by
 // sqrt(mean(x^2) + eps) (the RMSNorm between stacked layers).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void pf_prep_kernel(PfPrepArgs a) {
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + wv;
-  if (t >= a.T) return;
+// One row per wavefront.  Rows up to 4096 wide are loaded once into
+// registers (every load in flight at once); wider rows are read twice.
+template <bool RESIDENT>
+DEVI void prep_row(const PfPrepArgs& a, int t, int lane) {
+  constexpr int NV = 16;  // float4 per lane when resident: 4096 columns
   const float* xr = a.x + (size_t)t * a.d;
+  float4_t v[RESIDENT ? NV : 1];
   float m = 0.f, ss = 0.f;
-  for (int c = 4 * lane; c < a.d; c += 256) {
-    const float4_t v = *reinterpret_cast<const float4_t*>(xr + c);
-    m = fmaxf(m, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
-    ss = fmaf(v[0], v[0], ss);
-    ss = fmaf(v[1], v[1], ss);
-    ss = fmaf(v[2], v[2], ss);
-    ss = fmaf(v[3], v[3], ss);
+  auto acc = [&](const float4_t& u) {
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(u[0]), fabsf(u[1])), fmaxf(fabsf(u[2]), fabsf(u[3]))));
+    ss = fmaf(u[0], u[0], ss);
+    ss = fmaf(u[1], u[1], ss);
+    ss = fmaf(u[2], u[2], ss);
+    ss = fmaf(u[3], u[3], ss);
+  };
+  if constexpr (RESIDENT) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      v[i] = *reinterpret_cast<const float4_t*>(xr + min(4 * lane + 256 * i, a.d - 4));  // clamped; unused past d
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (4 * lane + 256 * i < a.d) acc(v[i]);
+  } else {
+    for (int c = 4 * lane; c < a.d; c += 256) acc(*reinterpret_cast<const float4_t*>(xr + c));
   }
   m = wave_maxf(m);
   float rms = 1.f;
@@ -231,21 +242,33 @@ __global__ __launch_bounds__(256) void pf_prep_kernel(PfPrepArgs a) {
   }
   const int ex = fp16_exponent_for(m);
   if (lane == 0) a.ex[t] = ex;
-  for (int c = 4 * lane; c < a.d; c += 256) {
-    const float4_t v = *reinterpret_cast<const float4_t*>(xr + c);
-    half2_t h01, h23, l01, l23;
+  typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+  auto put = [&](const float4_t& u, int c) {
+    h4_t h, l;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float s = ldexpf(a.norm ? v[i] / rms : v[i], -ex);
-      const _Float16 h = (_Float16)s;
-      const _Float16 l = (_Float16)(s - (float)h);
-      if (i < 2) { h01[i] = h; l01[i] = l; } else { h23[i - 2] = h; l23[i - 2] = l; }
+      const float s = ldexpf(a.norm ? u[i] / rms : u[i], -ex);
+      h[i] = (_Float16)s;
+      l[i] = (_Float16)(s - (float)h[i]);
     }
-    *reinterpret_cast<half2_t*>(a.xh + (size_t)t * a.d + c) = h01;
-    *reinterpret_cast<half2_t*>(a.xh + (size_t)t * a.d + c + 2) = h23;
-    *reinterpret_cast<half2_t*>(a.xl + (size_t)t * a.d + c) = l01;
-    *reinterpret_cast<half2_t*>(a.xl + (size_t)t * a.d + c + 2) = l23;
+    *reinterpret_cast<h4_t*>(a.xh + (size_t)t * a.d + c) = h;
+    *reinterpret_cast<h4_t*>(a.xl + (size_t)t * a.d + c) = l;
+  };
+  if constexpr (RESIDENT) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (4 * lane + 256 * i < a.d) put(v[i], 4 * lane + 256 * i);
+  } else {
+    for (int c = 4 * lane; c < a.d; c += 256) put(*reinterpret_cast<const float4_t*>(xr + c), c);
   }
+}
+
+__global__ __launch_bounds__(256) void pf_prep_kernel(PfPrepArgs a) {
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wv;
+  if (t >= a.T) return;
+  if (a.d <= 4096) prep_row<true>(a, t, lane);
+  else prep_row<false>(a, t, lane);
 }
 
 template <int P>
