@@ -700,10 +700,11 @@ DEVI void gate_up_item(const PfGemmArgs& a, const Stages& S, int* ex_lds, int g,
         const int ex = ex_lds[r];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
+          // h 2^-eh = silu(g) (u 2^-(hb + ex)): the power of two is applied to
+          // u before the product (exact either way), one scaling fewer
           const float gg = ldexpf(acc[rg][j][i], ex);
-          const float uu = ldexpf(acc[rg][2 + j][i], ex);
-          const float h = gg * __builtin_amdgcn_rcpf(1.0f + __expf(-gg)) * uu;
-          const _Float16 v = (_Float16)ldexpf(h, -(hb + 2 * ex));
+          const float us = ldexpf(acc[rg][2 + j][i], -(hb + ex));
+          const _Float16 v = (_Float16)(gg * __builtin_amdgcn_rcpf(1.0f + __expf(-gg)) * us);
           uint16_t vb;
           __builtin_memcpy(&vb, &v, 2);
           // columns c = 16 j + n and c + 1 (lanes n, n + 1) share one dword
