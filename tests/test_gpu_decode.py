@@ -302,3 +302,31 @@ def test_stack_teacher_forced(bqe, which):
         err = rel_err_inf(yl[l], oy)
         say(f"    layer {l}: rel err {err:.3e}")
         assert err <= TOL_LAYER, (l, err)
+
+
+def test_stack_chunks_of_eight(bqe):
+    """9..16 tokens run the decode kernels 8 tokens at a time: a 12-token
+    stack call equals calls on rows 0..7 and 8..11, bit for bit, in the
+    output, the per-layer outputs and the per-layer routing."""
+    wl = mi.small(mi.WORKLOADS["tiny"], Is=64, zipf_s=1.1, layers=3)
+    layers = [packed_layer(wl, l) for l in range(wl.layers)]
+    nL, d, k, T = wl.layers, wl.d, wl.k, 12
+    x_np = mi.activations(wl, T=T, stream=15)
+    ws = bqe.new_workspace(max(L.workspace_bytes(T) for L in layers))
+
+    def run(xs):
+        n = xs.shape[0]
+        y = torch.empty((n, d), dtype=torch.float32, device=DEV)
+        yl = torch.empty((nL, n, d), dtype=torch.float32, device=DEV)
+        il = torch.empty((nL, n, k), dtype=torch.int32, device=DEV)
+        wr = torch.empty((nL, n, k), dtype=torch.float32, device=DEV)
+        bqe.moe_stack_forward([L.handle for L in layers], activations_device(xs), y, ws, 1e-6, yl, il, wr)
+        torch.cuda.synchronize()
+        return [t.cpu().numpy() for t in (y, yl, il, wr)]
+
+    say(f"[stack] chunks of eight: T={T}")
+    full = run(x_np)
+    a, b = run(x_np[:8]), run(x_np[8:])
+    for name, f, pa, pb in zip(("y", "y_layers", "idx_layers", "w_layers"), full, a, b):
+        joined = np.concatenate([pa, pb], axis=0 if name == "y" else 1)
+        assert np.array_equal(f.view(np.uint32), joined.view(np.uint32)), name
