@@ -278,10 +278,12 @@ using ic = std::integral_constant<int, P>;
 // operations of this wave are outstanding; LDS and export counters free.
 constexpr int16_t vmcnt_imm(int n) { return (int16_t)((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8)); }
 
-// Three pipeline stages in three separate LDS arrays, so that the compiler
-// can see that a direct-to-LDS load into one stage does not alias reads of
-// another (with one array it waits for every outstanding load before each
-// LDS read).  Step s uses stage s % 3; its loads are issued two steps ahead.
+// Pipeline stages in separate LDS arrays, so that the compiler can see that
+// a direct-to-LDS load into one stage does not alias reads of another (with
+// one array it waits for every outstanding load before each LDS read).  The
+// router GEMM uses three (step s in stage s % 3, loads two steps ahead), the
+// grouped GEMMs two (step s in stage s % 2, loads one step ahead, two
+// workgroups per CU).
 struct Stages {
   unsigned char* s0;
   unsigned char* s1;
