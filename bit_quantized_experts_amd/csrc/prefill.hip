@@ -40,6 +40,8 @@
 
 namespace {
 
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 DEVI float wave_maxf(float v) {
@@ -706,14 +708,15 @@ DEVI void gate_up_item(const PfGemmArgs& a, const Stages& S, int* ex_lds, int g,
           // u before the product (exact either way), one scaling fewer
           const float gg = ldexpf(acc[rg][j][i], ex);
           const float us = ldexpf(acc[rg][2 + j][i], -(hb + ex));
-          const _Float16 v = (_Float16)(gg * __builtin_amdgcn_rcpf(1.0f + __expf(-gg)) * us);
-          uint16_t vb;
-          __builtin_memcpy(&vb, &v, 2);
-          // columns c = 16 j + n and c + 1 (lanes n, n + 1) share one dword
-          const uint32_t nb = (uint32_t)__builtin_amdgcn_mov_dpp((int)vb, 0xB1, 0xF, 0xF, true);  // lane n ^ 1
+          const float hv = gg * __builtin_amdgcn_rcpf(1.0f + __expf(-gg)) * us;
+          // columns c = 16 j + n and c + 1 (lanes n, n + 1) share one dword:
+          // the neighbour's value by a lane swap, both rounded by one packed
+          // conversion
+          const float hn = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, hv), 0xB1, 0xF, 0xF, true));
           if ((n & 1) == 0) {
             const int c = 16 * j + n;
-            tile[((rg * 4 + wv) * 64 + 4 * q + i + 16 * (c >> 3)) * 4 + ((c & 7) >> 1)] = (uint32_t)vb | (nb << 16);
+            tile[((rg * 4 + wv) * 64 + 4 * q + i + 16 * (c >> 3)) * 4 + ((c & 7) >> 1)] =
+                __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{hv, hn}, half2_t));
           }
         }
       }
@@ -865,11 +868,9 @@ DEVI void down_item(const PfGemmArgs& a, const Stages& S, float* rowf_lds, int g
       uint32_t* trow = reinterpret_cast<uint32_t*>((r < 64 ? S.s0 : S.s1) + (r & 63) * 512);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const _Float16 v = (_Float16)ldexpf(acc[rg][t][i], -ed);
-        uint16_t vb;
-        __builtin_memcpy(&vb, &v, 2);
-        const uint32_t nb2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)vb, 0xB1, 0xF, 0xF, true);  // lane n ^ 1
-        if ((n & 1) == 0) trow[(64 * wv + 16 * t + n) >> 1] = (uint32_t)vb | (nb2 << 16);
+        const float v = ldexpf(acc[rg][t][i], -ed);
+        const float vn = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));  // lane n ^ 1
+        if ((n & 1) == 0) trow[(64 * wv + 16 * t + n) >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{v, vn}, half2_t));
       }
     }
   __syncthreads();
