@@ -299,7 +299,7 @@ struct Stages {
 // experts; x hi/lo fragments staged in LDS by direct loads (2 blocks per
 // step, three stages), weight fragments straight into registers.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void pf_router_kernel(PfRouterArgs a) {
+__global__ __launch_bounds__(512) void pf_router_kernel(PfRouterArgs a) {
   constexpr int KS = 2;
   constexpr int STAGE = 2 * 8 * KS * 1024;  // [hi/lo][row group][block] fragments
   __shared__ __attribute__((aligned(1024))) unsigned char st0[STAGE];
@@ -309,28 +309,30 @@ __global__ __launch_bounds__(256) void pf_router_kernel(PfRouterArgs a) {
   const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, n = lane & 15, q = lane >> 4;
   const int row0 = blockIdx.x * 128;
   const int nb = a.d / 32, n_et = a.E16 / 16;
-  const int et0 = blockIdx.y * 8 + 2 * wv;
-  const bool act0 = et0 < n_et, act1 = et0 + 1 < n_et;
-  const int etl[2] = {act0 ? et0 : 0, act1 ? et0 + 1 : 0};  // idle tiles load (and ignore) tile 0
+  // eight wavefronts (two per SIMD), one 16-expert tile each
+  constexpr int NJ = 1;
+  const int et0 = blockIdx.y * 8 + wv;
+  const bool act0 = et0 < n_et, act1 = false;
+  const int etl[NJ] = {act0 ? et0 : 0};  // an idle wave loads (and ignores) tile 0
   int tok[8];
 #pragma unroll
   for (int rg = 0; rg < 8; ++rg) tok[rg] = min(row0 + 16 * rg + n, a.T - 1);
-  // this wave stages part hl (hi or lo) of block kb of every row group
-  const int hl = wv >> 1, dkb = wv & 1;
+  // this wave stages part hl (hi or lo) of block dkb of row groups 4 rh .. 4 rh + 3
+  const int hl = (wv >> 1) & 1, dkb = wv & 1, rh = wv >> 2;
   const _Float16* asrc = hl ? a.xl : a.xh;
 
   // acc: the current 256-column slice (4 steps) from zero; tot: the slices
   // added in order, so a split launch (one slice per workgroup, added by the
   // reduce kernel in the same order) gives the same bits
-  float4_t acc[8][2], tot[8][2];
+  float4_t acc[8][NJ], tot[8][NJ];
 #pragma unroll
   for (int rg = 0; rg < 8; ++rg)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[rg][j] = tot[rg][j] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NJ; ++j) acc[rg][j] = tot[rg][j] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  constexpr int LOADS = 8 + KS * 2 * 2;
+  constexpr int LOADS = 4 + KS * NJ * 2;
   static_assert(256 / 32 == 4 * KS, "a slice is four steps");
-  u32x4_t bh[3][KS][2], bl[3][KS][2];
+  u32x4_t bh[3][KS][NJ], bl[3][KS][NJ];
   const int sbase = a.split ? 4 * blockIdx.z : 0;  // first step of this workgroup
   const int nsteps = a.split ? 4 : nb / KS;
   auto issue = [&](auto P_, int ls) {
@@ -338,13 +340,15 @@ __global__ __launch_bounds__(256) void pf_router_kernel(PfRouterArgs a) {
     const int s = sbase + ls;
     unsigned char* st = S.get<P>();
 #pragma unroll
-    for (int rg = 0; rg < 8; ++rg)
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int rg = 4 * rh + r4;
       __builtin_amdgcn_global_load_lds(asrc + (size_t)tok[rg] * a.d + (KS * s + dkb) * 32 + 8 * q,
                                        (lds_ptr_t)(st + ((hl * 8 + rg) * KS + dkb) * 1024), 16, 0, 0);
+    }
 #pragma unroll
     for (int kb = 0; kb < KS; ++kb)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < NJ; ++j) {
         const size_t off = (((size_t)etl[j] * nb + KS * s + kb) * 64 + lane) * 8;
         bh[P][kb][j] = ld128(a.wh + off);
         bl[P][kb][j] = ld128(a.wl + off);
@@ -369,7 +373,7 @@ __global__ __launch_bounds__(256) void pf_router_kernel(PfRouterArgs a) {
 #pragma unroll
         for (int term = 0; term < 3; ++term)
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
+          for (int j = 0; j < NJ; ++j)
             if (j == 0 || act1) {
               const half8_t B = __builtin_bit_cast(half8_t, term == 1 ? bl[P][kb][j] : bh[P][kb][j]);
 #pragma unroll
@@ -381,7 +385,7 @@ __global__ __launch_bounds__(256) void pf_router_kernel(PfRouterArgs a) {
 #pragma unroll
       for (int rg = 0; rg < 8; ++rg)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NJ; ++j) {
           tot[rg][j] += acc[rg][j];
           acc[rg][j] = float4_t{0.f, 0.f, 0.f, 0.f};
         }
@@ -397,7 +401,7 @@ __global__ __launch_bounds__(256) void pf_router_kernel(PfRouterArgs a) {
 #pragma unroll
   for (int rg = 0; rg < 8; ++rg)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const int e = (et0 + j) * 16 + n;
       if (!(j == 0 ? act0 : act1) || e >= a.E) continue;
       if (a.split) {
@@ -957,7 +961,7 @@ hipError_t launch_pf_prep(const PfPrepArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_pf_router(const PfRouterArgs& a, hipStream_t s) {
-  MOE_LAUNCH(pf_router_kernel, dim3((a.T + 127) / 128, (a.E16 + PF_ET - 1) / PF_ET, a.split ? a.d / 256 : 1), dim3(256),
+  MOE_LAUNCH(pf_router_kernel, dim3((a.T + 127) / 128, (a.E16 + PF_ET - 1) / PF_ET, a.split ? a.d / 256 : 1), dim3(512),
              0, s, a);
   if (a.split) {
     const int64_t n = (int64_t)a.T * a.E;
