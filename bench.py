@@ -158,7 +158,7 @@ def bench_prefill(args):
     torch.cuda.synchronize()
     idx_np = idx.cpu().numpy()
     kdur = {}
-    # short chunks run the decode kernels (8 tokens at a time): time those
+    # a layer of at most 8 tokens runs the decode kernels: time those
     classes = ((bqe.TIMING_GATE_UP, "gate_up"), (bqe.TIMING_DOWN, "down"), (bqe.TIMING_ROUTER, "router")) \
         if T <= bqe.MAX_TOK_DECODE_KERNELS else \
         ((bqe.TIMING_PREFILL_GATE_UP, "gate_up"), (bqe.TIMING_PREFILL_DOWN, "down"), (bqe.TIMING_PREFILL_ROUTER, "router"))

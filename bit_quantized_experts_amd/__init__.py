@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_DATA = 0, 1, 2, 3, 4, 5
 TIMING_GATE_UP, TIMING_DOWN, TIMING_ROUTER, TIMING_PREFILL_GATE_UP, TIMING_PREFILL_DOWN = 0, 1, 2, 3, 4
 TIMING_PREFILL_ROUTER = 5
-MAX_TOK_DECODE_KERNELS = 16  # calls with at most this many tokens run the decode kernels (8 at a time)
+MAX_TOK_DECODE_KERNELS = 8  # one layer of at most this many tokens runs the decode kernels
 
 EXPORTED = ("moe_last_error", "moe_packed_bytes", "moe_pack_experts", "moe_layer_release", "moe_layer_get_desc",
             "moe_route_topk", "moe_workspace_bytes", "moe_workspace_init", "moe_layer_forward",

@@ -719,7 +719,7 @@ int moe_workspace_bytes(const moe_layer* L, int T, size_t* bytes) {
   if (T > MOE_MAX_TOK_PREFILL) return fail(MOE_ERR_UNSUPPORTED, "T above %d not supported", MOE_MAX_TOK_PREFILL);
   const int Tw = T < 1 ? 1 : T;
   const size_t dec = (size_t)ws_layout_decode(L, Tw < MOE_MAX_TOK_DECODE ? Tw : MOE_MAX_TOK_DECODE).total;
-  *bytes = T > MOE_MAX_TOK_CHUNKED ? std::max(dec, (size_t)ws_layout_prefill(L, T).total) : dec;
+  *bytes = T > MOE_MAX_TOK_DECODE ? std::max(dec, (size_t)ws_layout_prefill(L, T).total) : dec;
   return MOE_OK;
 }
 
@@ -731,17 +731,6 @@ int moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
   if (n > ws_bytes) n = ws_bytes;
   HIPCHK(launch_fill_u32(reinterpret_cast<uint32_t*>(ws), n / 4, 0u, reinterpret_cast<hipStream_t>(stream)));
   return MOE_OK;
-}
-
-// Routing inputs and outputs of the token chunk that starts at row c0.
-moe_route_io chunk_route(const moe_route_io& r, int c0, int k, int E) {
-  moe_route_io c{};
-  c.in_idx = r.in_idx ? r.in_idx + (size_t)c0 * k : nullptr;
-  c.in_w = r.in_w ? r.in_w + (size_t)c0 * k : nullptr;
-  c.out_logits = r.out_logits ? r.out_logits + (size_t)c0 * E : nullptr;
-  c.out_idx = r.out_idx ? r.out_idx + (size_t)c0 * k : nullptr;
-  c.out_w = r.out_w ? r.out_w + (size_t)c0 * k : nullptr;
-  return c;
 }
 
 int moe_layer_forward(const moe_layer* L, const float* x, int T, float* y, const moe_route_io* route, void* ws,
@@ -764,20 +753,12 @@ int moe_layer_forward(const moe_layer* L, const float* x, int T, float* y, const
   if (g_init_err != hipSuccess) return fail(MOE_ERR_HIP, "kernel init: %s", hipGetErrorString(g_init_err));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
-  if (T > MOE_MAX_TOK_CHUNKED) return prefill_layer(L, x, 0, 0.f, T, y, route, wsb, st);
-  // decode kernels, up to 8 tokens at a time (rows are independent)
-  for (int c0 = 0; c0 < T; c0 += MOE_MAX_TOK_DECODE) {
-    const int Tc = T - c0 < MOE_MAX_TOK_DECODE ? T - c0 : MOE_MAX_TOK_DECODE;
-    moe_route_io rc_io{};
-    if (route) rc_io = chunk_route(*route, c0, L->k, L->E);
-    int S = 1;
-    rc = decode_layer(L, LayerInput{x + (size_t)c0 * L->d, 1, 0, 0}, 0.f, Tc, nullptr, route ? &rc_io : nullptr, wsb, st,
-                      &S);
-    if (rc) return rc;
-    const WsLayout W = ws_layout_decode(L, Tc);
-    HIPCHK(launch_combine(reinterpret_cast<const float*>(wsb + W.ypart), S, (int64_t)8 * L->d, Tc, L->d,
-                          y + (size_t)c0 * L->d, st));
-  }
+  if (T > MOE_MAX_TOK_DECODE) return prefill_layer(L, x, 0, 0.f, T, y, route, wsb, st);
+  int S = 1;
+  rc = decode_layer(L, LayerInput{x, 1, 0, 0}, 0.f, T, nullptr, route, wsb, st, &S);
+  if (rc) return rc;
+  const WsLayout W = ws_layout_decode(L, T);
+  HIPCHK(launch_combine(reinterpret_cast<const float*>(wsb + W.ypart), S, (int64_t)8 * L->d, T, L->d, y, st));
   return MOE_OK;
 }
 

@@ -26,8 +26,10 @@
 
 #define MOE_BLOCK 32
 #define MOE_MAX_TOK_DECODE 8
-// Calls with up to this many tokens run the decode kernels, in chunks of
-// MOE_MAX_TOK_DECODE (faster than the grouped GEMMs at these sizes).
+// Stacks of up to this many tokens run the decode kernels, the whole stack
+// for MOE_MAX_TOK_DECODE tokens at a time (faster per layer than the grouped
+// GEMMs at these sizes; a single layer above MOE_MAX_TOK_DECODE tokens is
+// faster on the grouped GEMMs).
 #define MOE_MAX_TOK_CHUNKED 16
 #define MOE_MAX_TOK_PREFILL 65536
 #define MOE_MAX_K 16

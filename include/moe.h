@@ -145,17 +145,16 @@ int moe_workspace_bytes(const moe_layer *layer, int T, size_t *bytes);
 
 /* Clear the control words of a new workspace (enqueued on `stream`).  Must be
  * called once before a workspace is first used, and again if its memory has
- * been used for anything else in between.  The decode kernels (T <= 16) count
+ * been used for anything else in between.  The decode kernels count
  * finished workgroups in these words (the first 256 bytes); a workspace whose
  * words are not zero gives wrong logits and routing.  The forward calls
  * leave the control words cleared for the next call. */
 int moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
-/* One layer: y[T][d] = MoE(x[T][d]).  T = 0 is a no-op.  T <= 16 runs the
- * decode/verify kernels, 8 tokens at a time (experts streamed once per
- * call with 128-bit loads and multiplied from their codes, activations
- * carried as fp16 hi + lo); 16 < T <= 65536 runs the chunked-prefill
- * kernels: the (token, slot) pairs are grouped by expert (as
+/* One layer: y[T][d] = MoE(x[T][d]).  T = 0 is a no-op.  T <= 8 runs the
+ * decode/verify kernels (experts streamed once per call with 128-bit loads
+ * and multiplied from their codes, activations carried as fp16 hi + lo);
+ * 8 < T <= 65536 runs the chunked-prefill kernels: the (token, slot) pairs are grouped by expert (as
  * moe_group_tokens) and each expert's rows go through a grouped matrix
  * multiply on the matrix cores with the weights dequantized in registers to
  * fp16 and the activations rounded to fp16 after an exact per-row

@@ -162,7 +162,7 @@ def test_layer_odd_shapes(bqe):
 
 @pytest.mark.parametrize("T", [6, 12])
 def test_forced_routing_and_invalid_entries(bqe, T):
-    # T = 12: two chunks of the decode kernels (routing rows offset per chunk)
+    # T = 6: the decode kernels; T = 12: the grouped-GEMM kernels
     wl = mi.small(mi.WORKLOADS["tiny"], Is=64)
     L = packed_layer(wl, 0)
     x_np = mi.activations(wl, T=T, stream=7)

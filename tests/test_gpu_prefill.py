@@ -113,7 +113,7 @@ def _check(bqe, wl, L, x_np, tag, sample=None, logit_rows=None):
 def test_prefill_tiny(bqe, bits, Is):
     wl = mi.small(mi.WORKLOADS["tiny"], bits=bits, Is=Is, zipf_s=1.1 if Is else None)
     L = packed_layer(wl, 0)
-    for T in (9, 16, 17, 37, 200):  # up to 16: the decode kernels, 8 tokens at a time
+    for T in (9, 16, 17, 37, 200):  # more than 8 tokens: the grouped-GEMM kernels
         x = mi.activations(wl, T=T, stream=300 + T)
         _check(bqe, wl, L, x, f"tiny bits={bits} Is={Is}")
 
