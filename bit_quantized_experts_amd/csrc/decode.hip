@@ -62,74 +62,68 @@ DEVI void load_a(const _Float16* frag, const float* sum, size_t b, int lane, hal
 // ---------------------------------------------------------------------------
 // Slot list in LDS: routed experts numbered in ascending id order after the
 // shared expert's slot 0, and every (token, rank) entry's gate weight in its
-// slot's row.  The selected experts are first marked in a byte map (each
-// token's wavefront marks its own, right after selecting them; plain byte
-// stores of 1, so no atomics); after a barrier one wavefront numbers them,
-// 64 experts per ballot, and scatters the weights.  The numbering
-// wavefront's LDS operations complete in order, so the other wavefronts need
-// a single barrier afterwards.
+// slot's row.  The weight rows are cleared first (the shared expert's row set
+// to 1 for the tokens present).  Each token's wavefront marks its experts in
+// a byte map (plain byte stores of 1, so no atomics).  After a barrier every
+// token's wavefront reads the whole map, one ballot per 64 ids, which gives
+// the slot of any marked id (the shared slot plus the marked ids below it),
+// and writes its own entries: the slot's expert id and the token's weight.
+// Tokens that share an expert write the same id to its slot.
 // ---------------------------------------------------------------------------
 struct SlotLds {
-  uint8_t sel[MOE_MAX_E];  // 1 = selected; then the expert's slot (< MOE_MAX_SLOTS <= 255)
+  uint8_t sel[MOE_MAX_E];  // 1 = selected
   int expert[MOE_MAX_SLOTS];
   float w[MOE_MAX_SLOTS][8];
   int n_routed;
 };
-static_assert(MOE_MAX_SLOTS <= 255, "slot numbers fit the byte map");
 
-// Marks this lane's entries (lanes < n of the wavefront: ids out of range
-// are skipped).
-DEVI void mark_selected(SlotLds& S, const int32_t* idx, int n, int E) {
-  const int lane = threadIdx.x & 63;
-  for (int j = lane; j < n; j += 64) {
-    const int e = idx[j];
-    if (e >= 0 && e < E) S.sel[e] = 1;
-  }
+// Clears the byte map and the first n_slots weight rows (every thread of the
+// workgroup takes part).
+DEVI void clear_slots(SlotLds& S, int E, int T, int n_slots, bool has_shared) {
+  for (int i = threadIdx.x; i < (E + 3) / 4; i += blockDim.x) reinterpret_cast<uint32_t*>(S.sel)[i] = 0u;
+  for (int i = threadIdx.x; i < n_slots * 8; i += blockDim.x) (&S.w[0][0])[i] = (has_shared && i < T) ? 1.0f : 0.f;
 }
 
-// One wavefront: numbers the marked experts and fills the weight rows from
-// the T*k routing entries (idx, w); with dedup (given routing rows) a repeated
-// id in a token's row keeps its first entry's weight (a selection has none).
+// Marks this lane's expert e (ids out of range are skipped).
+DEVI void mark_lane(SlotLds& S, int e, int E) {
+  if (e >= 0 && e < E) S.sel[e] = 1;
+}
+
+// Token t's wavefront, after every mark: lane r < k holds the token's entry
+// (e, w).  Puts w in row t of e's slot and the id in the slot table.  With
+// dedup (given routing rows) a repeated id in the row keeps its first entry
+// (a selection has no repeats).  With count, lane 0 also writes the number of
+// routed slots and the shared expert's slot entry.
 template <int NPER>
-DEVI void number_slots_wave(SlotLds& S, const int32_t* idx, const float* w, int tk, int k, int T, int E,
-                            bool has_shared, bool dedup) {
-  const int lane = threadIdx.x & 63, base = has_shared ? 1 : 0;
-  // every read first (the numbering overwrites the map)
-  bool mk[NPER];
+DEVI void place_lane(SlotLds& S, int e, float w, int t, int k, int E, int base, bool dedup, bool count) {
+  const int lane = threadIdx.x & 63;
+  uint8_t f[NPER];  // every read first (a guarded read would wait on its own)
 #pragma unroll
-  for (int i = 0; i < NPER; ++i) mk[i] = S.sel[min(lane + 64 * i, E - 1)] != 0 && lane + 64 * i < E;
-  int re[2];
-  float rw[2];
+  for (int i = 0; i < NPER; ++i) f[i] = S.sel[min(lane + 64 * i, E - 1)];
+  uint64_t M[NPER];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int j = min(lane + 64 * h, tk - 1);
-    re[h] = lane + 64 * h < tk ? idx[j] : -1;
-    rw[h] = w[j];
-  }
-  int n = 0;
+  for (int i = 0; i < NPER; ++i) M[i] = __ballot((f[i] != 0) & (lane + 64 * i < E));
+  const bool valid = lane < k && e >= 0 && e < E;
+  bool use = valid;
+  if (dedup)
+    for (int j = 0; j + 1 < k; ++j) use = use && !(j < lane && __builtin_amdgcn_readlane(e, j) == e);
+  const int g = valid ? e >> 6 : 0;
+  const uint64_t below = valid ? (1ull << (e & 63)) - 1ull : 0ull;
+  int slot = base, total = 0;
+  uint64_t m = 0;
 #pragma unroll
   for (int i = 0; i < NPER; ++i) {
-    const int e = lane + 64 * i;
-    const bool m = mk[i];
-    const uint64_t M = __ballot(m);
-    const int slot = base + n + lanes_below(M);
-    if (m) {
-      S.expert[slot] = e;
-      S.sel[e] = (uint8_t)slot;
-    }
-    n += (int)__builtin_popcountll(M);
+    const int c = (int)__builtin_popcountll(M[i]);
+    slot += i < g ? c : 0;
+    m = i == g ? M[i] : m;
+    total += c;
   }
-  if (lane == 0) S.n_routed = n;
-  if (has_shared && lane == 0) S.expert[0] = E;
-  const int ns = base + n;
-  for (int i = lane; i < ns * 8; i += 64) S.w[i >> 3][i & 7] = (has_shared && i < 8 && i < T) ? 1.0f : 0.f;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int j = lane + 64 * h, t = j / k;
-    bool use = re[h] >= 0 && re[h] < E;
-    if (dedup && use)  // a repeated id in a token's row: the first occurrence only
-      for (int r = t * k; r < j; ++r) use = use && idx[r] != re[h];
-    if (use) S.w[S.sel[re[h]]][t] = rw[h];
+  slot += (int)__builtin_popcountll(m & below);
+  if (valid) S.expert[slot] = e;
+  if (use) S.w[slot][t] = w;
+  if (count && lane == 0) {
+    S.n_routed = total;
+    if (base) S.expert[0] = E;
   }
 }
 
@@ -159,8 +153,6 @@ struct alignas(16) GuLds {
   float red[GU_NW][8][64];          // partial sums of the k-parts
   float rn[8];                      // 1 / rms of each token
   SlotLds S;
-  int32_t tk_idx[MOE_MAX_TOK_DECODE * MOE_MAX_K];  // the selection, [T][k]
-  float tk_w[MOE_MAX_TOK_DECODE * MOE_MAX_K];
   uint64_t tk_buf[GU_NW][TOPK_BUF];
 };
 
@@ -275,28 +267,29 @@ __global__ __launch_bounds__(64 * GU_NW) void gu_decode_kernel(GuArgs a) {
   const float rnv = (tid >= 64 && tid < 64 + T) ? a.rnorm[tid - 64] : 1.0f;
   if (n_win == 1) stage_window(L, a, 0, 8 * n_kg, tid);
   if (tid >= 64 && tid < 72) L.rn[tid - 64] = 1.0f / rnv;
-  for (int i = tid; i < (E + 3) / 4; i += blockDim.x) reinterpret_cast<uint32_t*>(L.S.sel)[i] = 0u;
-  __syncthreads();  // byte map cleared before any wavefront marks
-  if (select) {
-    if (wv < T) {
+  clear_slots(L.S, E, T, base + min(tk, E), has_shared);
+  __syncthreads();  // byte map and weight rows cleared before any wavefront marks
+  TopkLane mine{-1, 0.f};
+  if (wv < T) {
+    if (select) {
       uint64_t key[NPER];
 #pragma unroll
       for (int i = 0; i < NPER; ++i) key[i] = (lane + 64 * i < E) ? sel_key(lv[i], lane + 64 * i) : 0ull;
-      topk_keys<NPER>(key, E, k, L.tk_idx + wv * k, L.tk_w + wv * k, L.tk_buf[wv]);
-      mark_selected(L.S, L.tk_idx + wv * k, k, E);
+      mine = topk_keys<NPER>(key, E, k, nullptr, nullptr, L.tk_buf[wv]);
+    } else if (lane < k) {
+      mine.e = a.idx[wv * k + lane];
+      mine.w = a.w[wv * k + lane];
     }
-  } else if (wv == 0) {
-    mark_selected(L.S, a.idx, tk, E);
+    mark_lane(L.S, mine.e, E);
   }
   __syncthreads();  // every token's experts marked
-  if (blockIdx.x == 0) {  // the routing used (given rows are copied as they are)
-    for (int i = tid; i < tk; i += blockDim.x) {
-      if (a.out_idx) a.out_idx[i] = select ? L.tk_idx[i] : a.idx[i];
-      if (a.out_w) a.out_w[i] = select ? L.tk_w[i] : a.w[i];
+  if (wv < T) {
+    place_lane<NPER>(L.S, mine.e, mine.w, wv, k, E, base, !select, wv == 0);
+    if (blockIdx.x == 0 && lane < k) {  // the routing used (given rows are copied as they are)
+      if (a.out_idx) a.out_idx[wv * k + lane] = mine.e;
+      if (a.out_w) a.out_w[wv * k + lane] = mine.w;
     }
   }
-  if (wv == 0)
-    number_slots_wave<NPER>(L.S, select ? L.tk_idx : a.idx, select ? L.tk_w : a.w, tk, k, T, E, has_shared, !select);
   __syncthreads();  // slot list, rms and the staged activations
   if (blockIdx.x == 0) {
     const int ns = base + L.S.n_routed;

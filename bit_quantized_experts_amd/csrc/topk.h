@@ -30,11 +30,14 @@ DEVI int key_index(uint64_t k) { return (int)(0xFFFFFFFFu - (uint32_t)k); }
 // Top-k of one row of E logits by one wavefront, then the gate weights.
 // Lane l holds the keys of experts l, l+64, ...; keys are unique.
 //   1. Candidates: theta = the k-th largest (counted with multiplicity) of
-//      the 64 lane maxima of the keys' value words (high 32 bits), found bit
-//      by bit from the most significant with ballots.  At least k keys have a
-//      value word >= theta (those k lane maxima), and every key of the top k
-//      does (a smaller one would rank below those k keys).  The search takes
-//      two bits per step (three ballots against independent thresholds).
+//      the 64 lane maxima of the keys' value words (high 32 bits), rounded
+//      down to a multiple of 2^16 (sign, exponent and 7 mantissa bits of the
+//      logit), found from the most significant bit with ballots, two bits per
+//      step (three ballots against independent thresholds), 8 steps.  At
+//      least k keys have a value word >= theta (those k lane maxima), so every
+//      key of the top k does too (a smaller one would rank below those k
+//      keys).  The rounding only admits the few keys within 2^-7 relative of
+//      the k-th lane maximum as extra candidates.
 //   2. If at most 64 keys reach theta they are compacted to LDS, each is
 //      ranked by counting the larger candidates, and the first k ranks are
 //      the answer.  Otherwise (many equal logits) a radix search on the value
@@ -46,8 +49,9 @@ DEVI int key_index(uint64_t k) { return (int)(0xFFFFFFFFu - (uint32_t)k); }
 // weights: m = logit of rank 0, e_r = exp64(l_r - m), S = sum of e_r in rank
 // order, w_r = fp32(e_r / S).  `buf`: this wave's 96 LDS entries.  NPER >=
 // ceil(E / 64).  The work is a single wavefront's dependent chain, so the
-// loops stay short: 16 steps for theta and one step per candidate for the
-// ranks.
+// loops stay short: 8 steps for theta and one step per candidate for the
+// ranks.  Returns lane r's (expert, weight) for r < k ({-1, 0} above) and
+// also stores them to idx_out / w_out unless those are null.
 DEVI int lanes_below(uint64_t m) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
@@ -67,8 +71,13 @@ DEVI uint64_t readlane_u64(uint64_t v, int l) {
 
 constexpr int TOPK_BUF = 96;  // LDS entries per wave: 64 candidates + 32
 
+struct TopkLane {
+  int e;
+  float w;
+};
+
 template <int NPER>
-DEVI void topk_keys(const uint64_t (&key)[NPER], int E, int k, int32_t* idx_out, float* w_out, uint64_t* buf);
+DEVI TopkLane topk_keys(const uint64_t (&key)[NPER], int E, int k, int32_t* idx_out, float* w_out, uint64_t* buf);
 
 template <int NPER, typename RowT>
 DEVI void topk_wave(RowT row, int E, int k, int32_t* idx_out, float* w_out, uint64_t* buf) {
@@ -84,17 +93,18 @@ DEVI void topk_wave(RowT row, int E, int k, int32_t* idx_out, float* w_out, uint
 
 // The same from the keys (lane l: experts l, l+64, ...; 0 = no expert).
 template <int NPER>
-DEVI void topk_keys(const uint64_t (&key)[NPER], int E, int k, int32_t* idx_out, float* w_out, uint64_t* buf) {
+DEVI TopkLane topk_keys(const uint64_t (&key)[NPER], int E, int k, int32_t* idx_out, float* w_out, uint64_t* buf) {
   const int lane = threadIdx.x & 63;
-  // 1. theta = the k-th largest (with multiplicity) of the 64 lane maxima of
-  // the value words, by a most-significant-bit-first search over ballots
+  // 1. theta = the largest multiple of 2^16 that at least k of the 64 lane
+  // maxima of the value words reach, by a most-significant-bit-first search
+  // over ballots
   uint32_t lhi = 0;
 #pragma unroll
   for (int i = 0; i < NPER; ++i) lhi = max(lhi, (uint32_t)(key[i] >> 32));
-  // two bits per step (the three trial thresholds are independent, so the
-  // dependent chain is 16 steps long; same result as one bit per step)
+  // two bits per step over the high 16 bits (the three trial thresholds are
+  // independent, so the dependent chain is 8 steps long)
   uint32_t theta = 0;
-  for (int b = 30; b >= 0; b -= 2) {
+  for (int b = 30; b >= 16; b -= 2) {
     const uint32_t t1 = theta | (1u << b), t2 = theta | (2u << b), t3 = theta | (3u << b);
     const int c1 = (int)__builtin_popcountll(__ballot(lhi >= t1));
     const int c2 = (int)__builtin_popcountll(__ballot(lhi >= t2));
@@ -170,10 +180,14 @@ DEVI void topk_keys(const uint64_t (&key)[NPER], int E, int k, int32_t* idx_out,
   if (lane < k) ev = moe_exp64((double)my_v - m);
   double S = 0.0;
   for (int r = 0; r < k; ++r) S += readlane_f64(ev, r);  // rank order, same in every lane
+  TopkLane r{-1, 0.f};
   if (lane < k) {
-    idx_out[lane] = (my_e >= 0 && my_e < E) ? my_e : 0;  // (other only with non-finite logits, out of contract)
-    w_out[lane] = (float)(ev / S);
+    r.e = (my_e >= 0 && my_e < E) ? my_e : 0;  // (other only with non-finite logits, out of contract)
+    r.w = (float)(ev / S);
+    if (idx_out) idx_out[lane] = r.e;
+    if (w_out) w_out[lane] = r.w;
   }
+  return r;
 }
 
 }  // namespace
