@@ -5,7 +5,11 @@ Default workload: the 48-layer MoE stack (d 2560, 512 experts of intermediate
 per pass (one real token plus seven drafts, as in a verify pass), RMSNorm
 between layers.  One step = one pass of the whole stack over one batch of 8
 synthetic tokens, replayed from a HIP graph; all weights (about 38 GB) are
-resident in HBM before timing starts.
+resident in HBM before timing starts.  Consecutive steps take the next of 16
+input batches (so the routing changes from pass to pass), each step
+bracketed by its own events; the same is also reported with the Infinity
+Cache emptied before every pass, and for the same input replayed back to
+back.
 
 Prints one JSON line: tokens/s, plus achieved HBM bandwidth from the
 algorithmic bytes of the actual routing, the roofline of the dominant kernel
@@ -192,6 +196,18 @@ def bench_prefill(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # each timed step after a 512 MB write (the Infinity Cache then holds
+    # none of the layer's weights), bracketed by its own events
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        flush.fill_(float(i))
+        ev[i][0].record()
+        step()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    times = np.array([a.elapsed_time(b) * 1e-3 for a, b in ev])
+    sec_per_step = float(times.mean())
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -199,7 +215,7 @@ def bench_prefill(args):
         step()
     e1.record()
     torch.cuda.synchronize()
-    sec_per_step = e0.elapsed_time(e1) * 1e-3 / args.steps
+    sec_b2b = e0.elapsed_time(e1) * 1e-3 / args.steps
 
     # algorithmic matrix-core work from the routing taken: 2 flops per
     # multiply-add, gate+up (2 d I) and down (d I) per routed pair, the
@@ -239,6 +255,10 @@ def bench_prefill(args):
         "config": {"workload": wl.name, "layers": 1, "T": T, "d": wl.d, "experts": wl.E, "d_ff": wl.I,
                    "shared_d_ff": wl.Is, "top_k": wl.k, "bits": wl.bits, "graph": graph is not None,
                    "parallelism": "none (1 GPU)"},
+        "step_ms": {"p10": float(np.percentile(times, 10)) * 1e3, "median": float(np.median(times)) * 1e3,
+                    "p90": float(np.percentile(times, 90)) * 1e3,
+                    "note": "512 MB written before each step (Infinity Cache emptied)"},
+        "back_to_back": {"ms_per_step": sec_b2b * 1e3, "value": T / sec_b2b},
         "grouped_gemm_mfma_util": gemm_util,
         "tokens_per_expert": {"max": int(counts.max()), "empty_experts": int((counts == 0).sum())},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS,
@@ -414,8 +434,14 @@ def main():
     log(f"built {wl.layers} packed layers in {time.time() - t0:.1f}s "
         f"({sum(L.buffer.numel() for L in layers) / 1e9:.2f} GB resident)")
 
-    x_np = mi.activations(wl, T=T, stream=1)
-    x = activations_device(x_np, dev)
+    # a ring of input batches: consecutive passes route differently, as in
+    # decoding, instead of re-reading the same experts every pass
+    RING = 16
+    ring_np = [mi.activations(wl, T=T, stream=1 + i) for i in range(RING)]
+    ring = [activations_device(r, dev) for r in ring_np]
+    x_np = ring_np[0]
+    x = torch.empty_like(ring[0])
+    x.copy_(ring[0])
     y = torch.empty((T, wl.d), dtype=torch.float32, device=dev)
     ws = bqe.new_workspace(max(L.workspace_bytes(T) for L in layers), dev)
     handles = [L.handle for L in layers]
@@ -469,9 +495,30 @@ def main():
         torch.cuda.synchronize()
 
     step = graph.replay if graph is not None else run_pass
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+
+    def timed_ring(n, with_flush):
+        """n passes over the ring, each bracketed by its own events (the
+        input copy, and the 512 MB write that empties the Infinity Cache,
+        stay outside); seconds per pass."""
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for i in range(n):
+            if with_flush:
+                flush.fill_(float(i))
+            x.copy_(ring[i % RING])
+            ev[i][0].record()
+            step()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) * 1e-3 for a, b in ev])
+
+    timed_ring(args.warmup, False)
+    times = timed_ring(args.steps, False)
+    sec_per_step = float(times.mean())
+    times_fl = timed_ring(max(10, args.steps // 2), True)
+    # the same input every pass, back to back (the experts of the previous pass
+    # partly still in the Infinity Cache)
+    x.copy_(ring[0])
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -479,16 +526,25 @@ def main():
         step()
     e1.record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1)
-    sec_per_step = ms * 1e-3 / args.steps
+    sec_same = e0.elapsed_time(e1) * 1e-3 / args.steps
 
-    # the graph replays the same routing as the eager pass (same input)
+    # the graph replays the eager pass's routing (same input), and the
+    # algorithmic bytes of every ring input from its own routing
     run_pass(True)
     torch.cuda.synchronize()
     assert np.array_equal(idx_l.cpu().numpy(), idx_np), "routing changed between passes"
-    total_bytes, gu_bytes, dn_bytes = algorithmic_bytes_decode(wl, idx_np, T)
+    ring_bytes = []
+    distinct = []
+    for i in range(RING):
+        x.copy_(ring[i])
+        run_pass(True)
+        torch.cuda.synchronize()
+        ir = idx_l.cpu().numpy()
+        ring_bytes.append(algorithmic_bytes_decode(wl, ir, T)[0])
+        distinct += [int(len(np.unique(ir[l]))) for l in range(wl.layers)]
+    total_bytes = float(np.mean(ring_bytes))
+    _, gu_bytes, dn_bytes = algorithmic_bytes_decode(wl, idx_np, T)
     gbs = total_bytes / sec_per_step / 1e9
-    distinct = [int(len(np.unique(idx_np[l]))) for l in range(wl.layers)]
 
     # roofline of the dominant kernel (largest share of the pass)
     per_class_bytes = {"gate_up": gu_bytes.mean(), "down": dn_bytes.mean(),
@@ -521,7 +577,14 @@ def main():
         "data": "synthetic (counter-hash codes/scales, N(0,1) activations, N(0,0.02) router + Zipf(1.1) log bias)",
         "config": {"workload": wl.name, "layers": wl.layers, "T": T, "d": wl.d, "experts": wl.E, "d_ff": wl.I,
                    "shared_d_ff": wl.Is, "top_k": wl.k, "bits": wl.bits, "graph": graph is not None,
-                   "parallelism": "none (1 GPU)"},
+                   "inputs": f"ring of {RING} batches of {T} rows", "parallelism": "none (1 GPU)"},
+        "step_ms": {"p10": float(np.percentile(times, 10)) * 1e3, "median": float(np.median(times)) * 1e3,
+                    "p90": float(np.percentile(times, 90)) * 1e3},
+        "flushed": {"note": "512 MB written before each pass (Infinity Cache emptied)",
+                    "ms_per_step": float(times_fl.mean()) * 1e3, "value": T / float(times_fl.mean()),
+                    "p10_ms": float(np.percentile(times_fl, 10)) * 1e3,
+                    "p90_ms": float(np.percentile(times_fl, 90)) * 1e3},
+        "same_input_back_to_back": {"ms_per_step": sec_same * 1e3, "value": T / sec_same},
         "hbm_GBps": gbs,
         "bytes_per_step": total_bytes,
         "distinct_experts_per_layer": {"min": min(distinct), "mean": float(np.mean(distinct)), "max": max(distinct)},

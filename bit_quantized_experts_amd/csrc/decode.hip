@@ -162,16 +162,21 @@ struct GroupRegs {
 };
 
 // Activation blocks [b0, b0 + nblk) into LDS (plain loads and LDS stores).
+// Entry p of a block is lane p % 64 of its A-fragment, which holds token
+// (p % 64) & 7; the rows of tokens >= T are zeros (as the route kernel writes
+// them), so they are stored without being read.
 DEVI void stage_window(GuLds& L, const GuArgs& a, int b0, int nblk, int tid) {
   constexpr int PER = GU_WIN * 64 / (64 * GU_NW);
   const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.xfrag + (size_t)b0 * 512);
   u32x4_t* dst = reinterpret_cast<u32x4_t*>(L.xs);
   const int n = nblk * 64, nc = nblk * 4;
+  const bool live = (tid & 7) < a.T;  // (64 * GU_NW is a multiple of 64: same lane for every i)
   u32x4_t v[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int p = tid + 64 * GU_NW * i;
-    if (p < n) v[i] = src[p];
+    v[i] = u32x4_t{0u, 0u, 0u, 0u};
+    if (p < n && live) v[i] = src[p];
   }
   float4_t c{};
   if (tid < nc) c = reinterpret_cast<const float4_t*>(a.xsum + (size_t)b0 * 16)[tid];
