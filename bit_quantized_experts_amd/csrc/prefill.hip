@@ -861,7 +861,10 @@ DEVI void down_item(const PfGemmArgs& a, const Stages& S, float* rowf_lds, int g
   // the combine multiplies them by rowf = w 2^(hb + 2 ex + ed).  The tile
   // (rows x 256 columns, 512 B per row) is assembled in LDS, rows 0..63 in
   // stage 0 and 64..127 in stage 1, columns n and n + 1 (lanes n, n ^ 1)
-  // sharing one dword, then written out in 16-byte pieces.
+  // sharing one dword, then written out in 16-byte pieces.  Dword c of row r
+  // sits at c ^ 8 ((r >> 2) & 3): the four lane groups of a store (rows 4
+  // apart, 512 B apart, so the same banks unswizzled) then take distinct
+  // banks, and 16-byte pieces stay whole.
   (void)rowf_lds;
   __syncthreads();  // every wave is past its last read of the stages
 #pragma unroll
@@ -874,13 +877,16 @@ DEVI void down_item(const PfGemmArgs& a, const Stages& S, float* rowf_lds, int g
       for (int t = 0; t < 4; ++t) {
         const float v = ldexpf(acc[rg][t][i], -ed);
         const float vn = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));  // lane n ^ 1
-        if ((n & 1) == 0) trow[(64 * wv + 16 * t + n) >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{v, vn}, half2_t));
+        if ((n & 1) == 0)
+          trow[((64 * wv + 16 * t + n) >> 1) ^ (8 * ((r >> 2) & 3))] =
+              __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{v, vn}, half2_t));
       }
     }
   __syncthreads();
   for (int p = tid; p < rows * 32; p += 256) {
     const int r = p >> 5, c16 = p & 31;
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>((r < 64 ? S.s0 : S.s1) + (r & 63) * 512 + 16 * c16);
+    const u32x4_t v =
+        *reinterpret_cast<const u32x4_t*>((r < 64 ? S.s0 : S.s1) + (r & 63) * 512 + 16 * (c16 ^ (2 * ((r >> 2) & 3))));
     *reinterpret_cast<u32x4_t*>(a.yh + (size_t)(row0 + r) * a.d + nt * PF_DT + 8 * c16) = v;
   }
 }
