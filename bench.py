@@ -270,6 +270,121 @@ def bench_prefill(args):
     print(json.dumps(out))
 
 
+def bench_stack_prefill(args):
+    """Chunked prefill through the 48-layer 2-bit stack (RMSNorm between
+    layers): one step = one chunk of T tokens (default 8192) through every
+    layer, replayed from a HIP graph, each step after a 512 MB write and
+    bracketed by its own events."""
+    import torch
+
+    import bit_quantized_experts_amd as bqe
+    import moe_inputs as mi
+    from moe_inputs.device import activations_device, packed_layer
+
+    wl = mi.WORKLOADS["stack_prefill"]
+    if args.layers:
+        wl = mi.small(wl, layers=args.layers)
+    T = args.T or wl.T
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    layers = [packed_layer(wl, l, dev) for l in range(wl.layers)]
+    handles = [L.handle for L in layers]
+    x = activations_device(mi.activations(wl, T=T, stream=1), dev)
+    y = torch.empty((T, wl.d), dtype=torch.float32, device=dev)
+    ws = bqe.new_workspace(max(L.workspace_bytes(T) for L in layers), dev)
+    idx_l = torch.empty((wl.layers, T, wl.k), dtype=torch.int32, device=dev)
+    w_l = torch.empty((wl.layers, T, wl.k), dtype=torch.float32, device=dev)
+
+    def run_pass(record_routing=False):
+        if record_routing:
+            bqe.moe_stack_forward(handles, x, y, ws, 1e-6, None, idx_l, w_l)
+        else:
+            bqe.moe_stack_forward(handles, x, y, ws, 1e-6)
+
+    run_pass(True)
+    torch.cuda.synchronize()
+    idx_np = idx_l.cpu().numpy()
+    kdur = {}
+    for cls, name in ((bqe.TIMING_PREFILL_GATE_UP, "gate_up"), (bqe.TIMING_PREFILL_DOWN, "down"),
+                      (bqe.TIMING_PREFILL_ROUTER, "router")):
+        bqe.moe_timing_start(cls, wl.layers)
+        run_pass()
+        ms, cnt = bqe.moe_timing_stop()
+        kdur[name] = (ms / cnt) * 1e-3
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run_pass()
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run_pass()
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        graph.replay()
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        flush.fill_(float(i))
+        ev[i][0].record()
+        graph.replay()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    times = np.array([a.elapsed_time(b) * 1e-3 for a, b in ev])
+    sec_per_step = float(times.mean())
+
+    # algorithmic matrix-core work from the routing of every layer (as for
+    # one layer: gate+up 2 d I and down d I multiply-adds per routed pair,
+    # the shared expert once per token)
+    pairs = (idx_np >= 0).sum(axis=(1, 2)).astype(np.float64)
+    gu_flops = 2.0 * pairs * 2 * wl.d * wl.I + 2.0 * T * 2 * wl.d * wl.Is
+    dn_flops = 2.0 * pairs * wl.d * wl.I + 2.0 * T * wl.d * wl.Is
+    flops = {"gate_up": float(gu_flops.mean()), "down": float(dn_flops.mean()), "router": 2.0 * T * wl.E * wl.d}
+    kernels = {n: {"avg_us": kdur[n] * 1e6, "flops_per_launch": flops[n],
+                   "TFLOPs": flops[n] / kdur[n] / 1e12} for n in kdur}
+    dom = max(("gate_up", "down"), key=lambda n: kdur[n])
+    achieved = flops[dom] / kdur[dom] / 1e12
+    total_flops = float(gu_flops.sum() + dn_flops.sum())
+    cpu = None
+    if args.cpu_tokens > 0 and args.cpu_layers > 0:
+        n_tok, n_l = args.cpu_tokens, min(args.cpu_layers, wl.layers)
+        log(f"timing the CPU oracle on {n_tok} tokens through {n_l} layers ...")
+        tps, per_layer = cpu_baseline_stack(wl, n_tok, mi.activations(wl, T=T, stream=1)[:n_tok], n_l)
+        cpu = {"value": tps, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"first {n_tok} of {T} tokens through the first {n_l} of {wl.layers} layers "
+                         f"({per_layer:.2f} s/layer), scaled to the full stack; single thread; expert generation untimed"}
+    out = {
+        "metric": "MoE-stack prefill tokens/s (48 layers, chunk of T tokens)",
+        "value": T / sec_per_step,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": sec_per_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16 MFMA operands (weights s*c, activations scaled per row), fp32 accumulate",
+        "data": "synthetic (counter-hash codes/scales, N(0,1) activations, N(0,0.02) router + Zipf(1.1) log bias)",
+        "config": {"workload": wl.name, "layers": wl.layers, "T": T, "d": wl.d, "experts": wl.E, "d_ff": wl.I,
+                   "shared_d_ff": wl.Is, "top_k": wl.k, "bits": wl.bits, "graph": True,
+                   "parallelism": "none (1 GPU)"},
+        "step_ms": {"p10": float(np.percentile(times, 10)) * 1e3, "median": float(np.median(times)) * 1e3,
+                    "p90": float(np.percentile(times, 90)) * 1e3,
+                    "note": "512 MB written before each step (Infinity Cache emptied)"},
+        "expert_gemm_TFLOPs_per_step": total_flops / sec_per_step / 1e12,
+        "distinct_experts_per_layer": [int(len(np.unique(idx_np[l]))) for l in range(wl.layers)],
+        "max_tokens_per_expert_per_layer": [int(np.bincount(idx_np[l].reshape(-1), minlength=wl.E).max())
+                                            for l in range(wl.layers)],
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / MFMA_F16_PEAK_TFLOPS, "traffic": None},
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
 def bench_layer_t1(args):
     """One full-size layer, decode T = 1, over a ring of 16 input rows (the
     routing changes from row to row).  Before each timed forward a 512 MB
@@ -385,7 +500,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="stack_t8_2bit", choices=["stack_t8_2bit", "stack_3bit", "prefill", "layer_t1"])
+    ap.add_argument("--workload", default="stack_t8_2bit",
+                    choices=["stack_t8_2bit", "stack_3bit", "prefill", "layer_t1", "stack_prefill"])
     ap.add_argument("--T", type=int, default=None, help="tokens per pass (default: the workload's)")
     ap.add_argument("--layers", type=int, default=None, help="override the number of layers (testing only)")
     ap.add_argument("--no-graph", action="store_true")
@@ -411,6 +527,9 @@ def main():
         return
     if args.workload == "layer_t1":
         bench_layer_t1(args)
+        return
+    if args.workload == "stack_prefill":
+        bench_stack_prefill(args)
         return
 
     import torch

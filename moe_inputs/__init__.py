@@ -79,6 +79,9 @@ WORKLOADS = {
     # chunked prefill through one layer
     "prefill": Workload("prefill", d=2560, E=512, I=640, Is=640, k=10, bits=2, T=8192,
                         layers=1, scale_lo=0.01, scale_hi=0.05),
+    # chunked prefill through the 48-layer 2-bit stack (the same layers as stack_t8_2bit)
+    "stack_prefill": Workload("stack_prefill", d=2560, E=512, I=640, Is=640, k=10, bits=2, T=8192,
+                              layers=48, scale_lo=0.01, scale_hi=0.05),
 }
 
 # stream ids inside one (seed, layer)
