@@ -505,6 +505,8 @@ def main():
     ap.add_argument("--T", type=int, default=None, help="tokens per pass (default: the workload's)")
     ap.add_argument("--layers", type=int, default=None, help="override the number of layers (testing only)")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--f16act", action="store_true",
+                    help="stacks: the fp16-activation decode entry point (up to 16 tokens per pass)")
     ap.add_argument("--cpu-layers", type=int, default=3, help="oracle sample size in layers (0 = skip)")
     ap.add_argument("--cpu-tokens", type=int, default=16, help="prefill: oracle sample size in tokens (0 = skip)")
     ap.add_argument("--timing-only", action="store_true",
@@ -567,11 +569,13 @@ def main():
     idx_l = torch.empty((wl.layers, T, wl.k), dtype=torch.int32, device=dev)
     w_l = torch.empty((wl.layers, T, wl.k), dtype=torch.float32, device=dev)
 
+    fwd = bqe.moe_stack_forward_f16act if args.f16act else bqe.moe_stack_forward
+
     def run_pass(record_routing=False):
         if record_routing:
-            bqe.moe_stack_forward(handles, x, y, ws, 1e-6, None, idx_l, w_l)
+            fwd(handles, x, y, ws, 1e-6, None, idx_l, w_l)
         else:
-            bqe.moe_stack_forward(handles, x, y, ws, 1e-6)
+            fwd(handles, x, y, ws, 1e-6)
 
     # eager warm-up (also initialises the library before any capture); with
     # --timing-only it runs with the launches serialized like the timed passes
@@ -692,9 +696,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp16 MFMA operands (codes exact, activations as fp16 hi+lo), fp32 accumulate",
+        "dtype": ("fp16 MFMA operands (codes exact, activations rounded to fp16), fp32 accumulate" if args.f16act
+                  else "fp16 MFMA operands (codes exact, activations as fp16 hi+lo), fp32 accumulate"),
         "data": "synthetic (counter-hash codes/scales, N(0,1) activations, N(0,0.02) router + Zipf(1.1) log bias)",
-        "config": {"workload": wl.name, "layers": wl.layers, "T": T, "d": wl.d, "experts": wl.E, "d_ff": wl.I,
+        "config": {"workload": wl.name, "layers": wl.layers, "T": T, "f16act": bool(args.f16act), "d": wl.d, "experts": wl.E, "d_ff": wl.I,
                    "shared_d_ff": wl.Is, "top_k": wl.k, "bits": wl.bits, "graph": graph is not None,
                    "inputs": f"ring of {RING} batches of {T} rows", "parallelism": "none (1 GPU)"},
         "step_ms": {"p10": float(np.percentile(times, 10)) * 1e3, "median": float(np.median(times)) * 1e3,

@@ -20,11 +20,13 @@ MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ER
 TIMING_GATE_UP, TIMING_DOWN, TIMING_ROUTER, TIMING_PREFILL_GATE_UP, TIMING_PREFILL_DOWN = 0, 1, 2, 3, 4
 TIMING_PREFILL_ROUTER = 5
 MAX_TOK_DECODE_KERNELS = 8  # one layer of at most this many tokens runs the decode kernels
+MAX_TOK_F16ACT = 16  # tokens per call of the fp16-activation decode entry points
 
 EXPORTED = ("moe_last_error", "moe_packed_bytes", "moe_pack_experts", "moe_layer_release", "moe_layer_get_desc",
             "moe_route_topk", "moe_workspace_bytes", "moe_workspace_init", "moe_layer_forward",
             "moe_stack_forward", "moe_rmsnorm", "moe_debug_unpack", "moe_timing_start", "moe_timing_stop",
-            "moe_group_workspace_bytes", "moe_group_tokens")
+            "moe_group_workspace_bytes", "moe_group_tokens", "moe_layer_forward_f16act",
+            "moe_stack_forward_f16act")
 
 
 class MoeError(RuntimeError):
@@ -66,6 +68,8 @@ def lib() -> ctypes.CDLL:
         L.moe_workspace_init.argtypes = [P, S, P]
         L.moe_layer_forward.argtypes = [P, P, I, P, P, P, S, P]
         L.moe_stack_forward.argtypes = [P, I, P, I, ctypes.c_float, P, P, P, P, P, S, P]
+        L.moe_layer_forward_f16act.argtypes = [P, P, I, P, P, P, S, P]
+        L.moe_stack_forward_f16act.argtypes = [P, I, P, I, ctypes.c_float, P, P, P, P, P, S, P]
         L.moe_rmsnorm.argtypes = [P, I, I, ctypes.c_float, P, P]
         L.moe_debug_unpack.argtypes = [P, I, I, P, P, P, P]
         L.moe_timing_start.argtypes = [I, I]
@@ -155,6 +159,23 @@ def moe_layer_forward(handle: int, x, y, ws, route: RouteIO | None = None, strea
     T = x.shape[0]
     _check(lib().moe_layer_forward(handle, _ptr(x), T, _ptr(y), ctypes.byref(route) if route is not None else None,
                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "moe_layer_forward")
+
+
+def moe_layer_forward_f16act(handle: int, x, y, ws, route: RouteIO | None = None, stream=None):
+    T = x.shape[0]
+    _check(lib().moe_layer_forward_f16act(handle, _ptr(x), T, _ptr(y),
+                                          ctypes.byref(route) if route is not None else None, _ptr(ws),
+                                          ws.numel() * ws.element_size(), _stream(stream)), "moe_layer_forward_f16act")
+
+
+def moe_stack_forward_f16act(handles, x, y, ws, eps: float = 1e-6, y_layers=None, idx_layers=None, w_layers=None,
+                             stream=None):
+    arr = (ctypes.c_void_p * len(handles))(*handles)
+    T = x.shape[0]
+    _check(lib().moe_stack_forward_f16act(arr, len(handles), _ptr(x), T, eps, _ptr(y), _ptr(y_layers),
+                                          _ptr(idx_layers), _ptr(w_layers), _ptr(ws),
+                                          ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_stack_forward_f16act")
 
 
 def moe_stack_forward(handles, x, y, ws, eps: float = 1e-6, y_layers=None, idx_layers=None, w_layers=None,

@@ -73,7 +73,7 @@ DEVI void load_a(const _Float16* frag, const float* sum, size_t b, int lane, hal
 struct SlotLds {
   uint8_t sel[MOE_MAX_E];  // 1 = selected
   int expert[MOE_MAX_SLOTS];
-  float w[MOE_MAX_SLOTS][8];
+  float w[MOE_MAX_SLOTS][16];  // [slot][token]
   int n_routed;
 };
 
@@ -81,7 +81,7 @@ struct SlotLds {
 // workgroup takes part).
 DEVI void clear_slots(SlotLds& S, int E, int T, int n_slots, bool has_shared) {
   for (int i = threadIdx.x; i < (E + 3) / 4; i += blockDim.x) reinterpret_cast<uint32_t*>(S.sel)[i] = 0u;
-  for (int i = threadIdx.x; i < n_slots * 8; i += blockDim.x) (&S.w[0][0])[i] = (has_shared && i < T) ? 1.0f : 0.f;
+  for (int i = threadIdx.x; i < n_slots * 16; i += blockDim.x) (&S.w[0][0])[i] = (has_shared && i < T) ? 1.0f : 0.f;
 }
 
 // Marks this lane's expert e (ids out of range are skipped).
@@ -151,7 +151,7 @@ struct alignas(16) GuLds {
   alignas(16) unsigned char xs[GU_WIN * 1024];  // A-fragments, [block][lane][8] fp16
   alignas(16) float cs[GU_WIN * 16];  // accumulator seeds, [block][16]
   float red[GU_NW][8][64];          // partial sums of the k-parts
-  float rn[8];                      // 1 / rms of each token
+  float rn[16];                     // 1 / rms of each token
   SlotLds S;
   uint64_t tk_buf[GU_NW][TOPK_BUF];
 };
@@ -163,14 +163,15 @@ struct GroupRegs {
 
 // Activation blocks [b0, b0 + nblk) into LDS (plain loads and LDS stores).
 // Entry p of a block is lane p % 64 of its A-fragment, which holds token
-// (p % 64) & 7; the rows of tokens >= T are zeros (as the route kernel writes
-// them), so they are stored without being read.
+// (p % 64) & 7 (fp16 activations: (p % 64) & 15); the rows of tokens >= T are
+// zeros (as the route kernel writes them), so they are stored without being
+// read.
 DEVI void stage_window(GuLds& L, const GuArgs& a, int b0, int nblk, int tid) {
   constexpr int PER = GU_WIN * 64 / (64 * GU_NW);
   const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.xfrag + (size_t)b0 * 512);
   u32x4_t* dst = reinterpret_cast<u32x4_t*>(L.xs);
   const int n = nblk * 64, nc = nblk * 4;
-  const bool live = (tid & 7) < a.T;  // (64 * GU_NW is a multiple of 64: same lane for every i)
+  const bool live = (tid & (a.act16 ? 15 : 7)) < a.T;  // (64 * GU_NW is a multiple of 64: same lane for every i)
   u32x4_t v[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -260,39 +261,59 @@ __global__ __launch_bounds__(64 * GU_NW) void gu_decode_kernel(GuArgs a) {
   const int n_win = (8 * n_kg + GU_WIN - 1) / GU_WIN;
   const int win_kg = (n_kg + n_win - 1) / n_win;  // k-groups per window
 
-  // Selection: wavefront t < T takes token t's row of logits.  Its loads,
-  // the divisors' and the activation window's share one round trip.
+  // Selection: wavefront w takes the rows of tokens w and w + 8 (below T) of
+  // the logits.  The loads of its first row (both rows, for rows of up to
+  // 1024 experts), the divisors' and the activation window's share one round
+  // trip.
+  constexpr bool PRE2 = NPER <= 16;
   const bool select = a.logits != nullptr;
-  float lv[NPER];
+  float lv[2][NPER];
   if (select) {
-    const float* row = a.logits + (size_t)min(wv, T - 1) * E;
 #pragma unroll
-    for (int i = 0; i < NPER; ++i) lv[i] = row[min(lane + 64 * i, E - 1)];
+    for (int h = 0; h < (PRE2 ? 2 : 1); ++h) {
+      const float* row = a.logits + (size_t)min(wv + GU_NW * h, T - 1) * E;
+#pragma unroll
+      for (int i = 0; i < NPER; ++i) lv[h][i] = row[min(lane + 64 * i, E - 1)];
+    }
   }
   const float rnv = (tid >= 64 && tid < 64 + T) ? a.rnorm[tid - 64] : 1.0f;
   if (n_win == 1) stage_window(L, a, 0, 8 * n_kg, tid);
-  if (tid >= 64 && tid < 72) L.rn[tid - 64] = 1.0f / rnv;
+  if (tid >= 64 && tid < 80) L.rn[tid - 64] = 1.0f / rnv;
   clear_slots(L.S, E, T, base + min(tk, E), has_shared);
   __syncthreads();  // byte map and weight rows cleared before any wavefront marks
-  TopkLane mine{-1, 0.f};
-  if (wv < T) {
-    if (select) {
-      uint64_t key[NPER];
+  static_assert(2 * GU_NW >= MOE_MAX_TOK_F16ACT, "two tokens per wavefront");
+  TopkLane mine[2] = {{-1, 0.f}, {-1, 0.f}};
 #pragma unroll
-      for (int i = 0; i < NPER; ++i) key[i] = (lane + 64 * i < E) ? sel_key(lv[i], lane + 64 * i) : 0ull;
-      mine = topk_keys<NPER>(key, E, k, nullptr, nullptr, L.tk_buf[wv]);
-    } else if (lane < k) {
-      mine.e = a.idx[wv * k + lane];
-      mine.w = a.w[wv * k + lane];
+  for (int h = 0; h < 2; ++h) {
+    const int t = wv + GU_NW * h;
+    if (t < T) {
+      if (select) {
+        if (!PRE2 && h == 1) {
+          const float* row = a.logits + (size_t)t * E;
+#pragma unroll
+          for (int i = 0; i < NPER; ++i) lv[1][i] = row[min(lane + 64 * i, E - 1)];
+        }
+        uint64_t key[NPER];
+#pragma unroll
+        for (int i = 0; i < NPER; ++i) key[i] = (lane + 64 * i < E) ? sel_key(lv[h][i], lane + 64 * i) : 0ull;
+        mine[h] = topk_keys<NPER>(key, E, k, nullptr, nullptr, L.tk_buf[wv]);
+      } else if (lane < k) {
+        mine[h].e = a.idx[t * k + lane];
+        mine[h].w = a.w[t * k + lane];
+      }
+      mark_lane(L.S, mine[h].e, E);
     }
-    mark_lane(L.S, mine.e, E);
   }
   __syncthreads();  // every token's experts marked
-  if (wv < T) {
-    place_lane<NPER>(L.S, mine.e, mine.w, wv, k, E, base, !select, wv == 0);
-    if (blockIdx.x == 0 && lane < k) {  // the routing used (given rows are copied as they are)
-      if (a.out_idx) a.out_idx[wv * k + lane] = mine.e;
-      if (a.out_w) a.out_w[wv * k + lane] = mine.w;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int t = wv + GU_NW * h;
+    if (t < T) {
+      place_lane<NPER>(L.S, mine[h].e, mine[h].w, t, k, E, base, !select, t == 0);
+      if (blockIdx.x == 0 && lane < k) {  // the routing used (given rows are copied as they are)
+        if (a.out_idx) a.out_idx[t * k + lane] = mine[h].e;
+        if (a.out_w) a.out_w[t * k + lane] = mine[h].w;
+      }
     }
   }
   __syncthreads();  // slot list, rms and the staged activations
@@ -300,7 +321,7 @@ __global__ __launch_bounds__(64 * GU_NW) void gu_decode_kernel(GuArgs a) {
     const int ns = base + L.S.n_routed;
     if (tid == 0) *a.n_slots = ns;
     for (int i = tid; i < ns; i += blockDim.x) a.slot_expert[i] = L.S.expert[i];
-    for (int i = tid; i < ns * 8; i += blockDim.x) a.slot_w[i] = L.S.w[i >> 3][i & 7];
+    for (int i = tid; i < ns * 16; i += blockDim.x) a.slot_w[i] = L.S.w[i >> 4][i & 15];
   }
   const int n_items = tiles_s + L.S.n_routed * tiles_r;
   int KP = 8;
@@ -361,22 +382,24 @@ __global__ __launch_bounds__(64 * GU_NW) void gu_decode_kernel(GuArgs a) {
     }
     if (valid && kp == 0) {
       // lane l: intermediate row n = l & 15 of the tile, C rows 4(l>>4)+i:
-      // tokens tok_e + i, hi part in lanes < 32, lo part in lanes >= 32
+      // tokens tok_e + i, hi part in lanes < 32, lo part in lanes >= 32 (fp16
+      // activations: token 4(l>>4)+i, no lo part)
       const int n = lane & 15;
-      const bool lo_half = lane >= 32;
+      const bool a16 = a.act16 != 0;
+      const bool lo_half = !a16 && lane >= 32;
       const int pblk = t >> 1, kk = 16 * (t & 1) + n;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int tok = tok_e + i;
+        const int tok = a16 ? 4 * (lane >> 4) + i : tok_e + i;
         const float gw = (u == 0 && has_shared) ? (tok < T ? 1.0f : 0.f) : L.S.w[u][tok];
         const float rrn = L.rn[tok];  // 1 / rms
-        const float g = add_partner32(accg[i]) * rrn;
-        const float uu = add_partner32(accu[i]) * rrn;
+        const float g = (a16 ? accg[i] : add_partner32(accg[i])) * rrn;
+        const float uu = (a16 ? accu[i] : add_partner32(accu[i])) * rrn;
         const float hv = g * __builtin_amdgcn_rcpf(1.0f + expf(-g)) * uu;
         const float hs = (gw != 0.f) ? gw * hv : 0.f;
         const _Float16 hi = (_Float16)hs;
         const _Float16 val = lo_half ? (_Float16)(hs - (float)hi) : hi;
-        const int mrow = tok + (lo_half ? 8 : 0);
+        const int mrow = a16 ? tok : tok + (lo_half ? 8 : 0);
         a.hfrag[(((size_t)u * a.nbI + pblk) * 64 + mrow + 16 * (kk >> 3)) * 8 + (kk & 7)] = val;
         const float sm = row16_sum((float)val);
         if (n == 0) a.hsum[((size_t)u * 2 * a.nbI + t) * 16 + mrow] = -(float)a.code_off * sm;
@@ -492,10 +515,11 @@ __global__ __launch_bounds__(512) void down_decode_kernel(DownArgs a) {
 #pragma unroll
       for (int w = 1; w < 8; ++w)
         if (w < nw) s += part[w];
-      s = add_partner32(s);
-      const int tok = 4 * (lane >> 4) + i;  // lanes < 32 hold tokens 0..7
+      const bool a16 = a.act16 != 0;  // fp16 activations: C row = token, 16 tokens
+      if (!a16) s = add_partner32(s);
+      const int tok = 4 * (lane >> 4) + i;  // (hi/lo: lanes < 32 hold tokens 0..7)
       const int o = rg * 16 * RT + 16 * t + n;
-      if (lane < 32 && tok < T) a.ypart[((size_t)sp * 8 + tok) * d + o] = s;
+      if ((a16 || lane < 32) && tok < T) a.ypart[((size_t)sp * (a16 ? 16 : 8) + tok) * d + o] = s;
     }
 }
 

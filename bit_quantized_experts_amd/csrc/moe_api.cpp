@@ -168,8 +168,11 @@ int down_splits(const moe_layer* L, int max_slots) {
   return S;
 }
 
-WsLayout ws_layout_decode(const moe_layer* L, int T) {
+// Decode pass of T tokens; act16: fp16 activations (16 token rows per pass,
+// else 8).
+WsLayout ws_layout_decode(const moe_layer* L, int T, bool act16 = false) {
   WsLayout W{};
+  const int R = act16 ? MOE_MAX_TOK_F16ACT : MOE_MAX_TOK_DECODE;
   const int k = L->k, E = L->E, d = L->d;
   W.max_slots = (T * k < E ? T * k : E) + (L->Is > 0 ? 1 : 0);
   W.nbI = (L->I > L->Is ? L->I : L->Is) / 32;
@@ -180,16 +183,16 @@ WsLayout ws_layout_decode(const moe_layer* L, int T) {
   W.ctrl = take(ctrl_bytes());
   W.lp = take((int64_t)W.n_cs * T * E * 4);
   W.ss_part = take((int64_t)((E + MOE_ROUTE_ROWS - 1) / MOE_ROUTE_ROWS) * W.n_cs * T * 4);
-  W.rnorm = take(8 * 4);
+  W.rnorm = take(16 * 4);
   W.logits = take((int64_t)T * E * 4);
   W.n_slots = take(4);
   W.slot_expert = take((int64_t)W.max_slots * 4);
-  W.slot_w = take((int64_t)W.max_slots * 8 * 4);
+  W.slot_w = take((int64_t)W.max_slots * 16 * 4);
   W.xfrag = take((int64_t)(d / 32) * 64 * 8 * 2);
   W.xsum = take((int64_t)(d / 32) * 16 * 4);
   W.hfrag = take((int64_t)W.max_slots * W.nbI * 64 * 8 * 2);
   W.hsum = take((int64_t)W.max_slots * W.nbI * 2 * 16 * 4);
-  W.ypart = take((int64_t)W.S * 8 * d * 4);
+  W.ypart = take((int64_t)W.S * R * d * 4);
   W.total = o;
   return W;
 }
@@ -319,8 +322,8 @@ struct LayerInput {
 // selection in every workgroup) -> down.  The result
 // is left as split partials in the workspace (ypart, W.S splits).
 int decode_layer(const moe_layer* L, const LayerInput& in, float eps, int T, float* y_prev_out,
-                 const moe_route_io* r, uint8_t* ws, hipStream_t s, int* S_out) {
-  const WsLayout W = ws_layout_decode(L, T);
+                 const moe_route_io* r, uint8_t* ws, hipStream_t s, int* S_out, bool act16 = false) {
+  const WsLayout W = ws_layout_decode(L, T, act16);
   const int d = L->d, E = L->E;
   const bool forced = r && r->in_idx && r->in_w;
   int slot;
@@ -336,6 +339,7 @@ int decode_layer(const moe_layer* L, const LayerInput& in, float eps, int T, flo
   ra.E = E;
   ra.code_off = 1 << (L->bits - 1);
   ra.do_logits = !forced;
+  ra.act16 = act16;
   ra.lp = reinterpret_cast<float*>(ws + W.lp);
   ra.xfrag = reinterpret_cast<_Float16*>(ws + W.xfrag);
   ra.xsum = reinterpret_cast<float*>(ws + W.xsum);
@@ -386,6 +390,7 @@ int decode_layer(const moe_layer* L, const LayerInput& in, float eps, int T, flo
   ga.nbI = W.nbI;
   ga.code_off = ra.code_off;
   ga.has_shared = L->Is > 0;
+  ga.act16 = act16;
   {
     // one workgroup per CU (the kernel's LDS allows no more), never more
     // workgroups than 16-row tiles
@@ -417,6 +422,7 @@ int decode_layer(const moe_layer* L, const LayerInput& in, float eps, int T, flo
   da.S = W.S;
   da.has_shared = L->Is > 0;
   da.max_slots = W.max_slots;
+  da.act16 = act16;
   da.ypart = reinterpret_cast<float*>(ws + W.ypart);
   int dn_nw = env_int("MOE_DOWN_WAVES", 8);
   if (dn_nw <= 0 || dn_nw > 8) dn_nw = 8;
@@ -718,7 +724,10 @@ int moe_workspace_bytes(const moe_layer* L, int T, size_t* bytes) {
   if (T < 0) return fail(MOE_ERR_ARG, "T must be >= 0");
   if (T > MOE_MAX_TOK_PREFILL) return fail(MOE_ERR_UNSUPPORTED, "T above %d not supported", MOE_MAX_TOK_PREFILL);
   const int Tw = T < 1 ? 1 : T;
-  const size_t dec = (size_t)ws_layout_decode(L, Tw < MOE_MAX_TOK_DECODE ? Tw : MOE_MAX_TOK_DECODE).total;
+  // the decode layouts (8 tokens with fp16 hi + lo activations, 16 with fp16
+  // activations) and, above 8 tokens, the prefill layout
+  const size_t dec = std::max((size_t)ws_layout_decode(L, Tw < MOE_MAX_TOK_DECODE ? Tw : MOE_MAX_TOK_DECODE).total,
+                              (size_t)ws_layout_decode(L, Tw < MOE_MAX_TOK_F16ACT ? Tw : MOE_MAX_TOK_F16ACT, true).total);
   *bytes = T > MOE_MAX_TOK_DECODE ? std::max(dec, (size_t)ws_layout_prefill(L, T).total) : dec;
   return MOE_OK;
 }
@@ -733,8 +742,9 @@ int moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
   return MOE_OK;
 }
 
-int moe_layer_forward(const moe_layer* L, const float* x, int T, float* y, const moe_route_io* route, void* ws,
-                      size_t ws_bytes, void* stream) {
+// Argument checks shared by the layer entry points.
+static int layer_args(const moe_layer* L, const float* x, int T, float* y, const moe_route_io* route, void* ws,
+                      size_t ws_bytes) {
   if (!L) return fail(MOE_ERR_ARG, "layer is NULL");
   if (T < 0) return fail(MOE_ERR_ARG, "T must be >= 0");
   if (T == 0) return MOE_OK;
@@ -751,20 +761,43 @@ int moe_layer_forward(const moe_layer* L, const float* x, int T, float* y, const
   if (rc) return rc;
   init_kernels();
   if (g_init_err != hipSuccess) return fail(MOE_ERR_HIP, "kernel init: %s", hipGetErrorString(g_init_err));
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
-  if (T > MOE_MAX_TOK_DECODE) return prefill_layer(L, x, 0, 0.f, T, y, route, wsb, st);
-  int S = 1;
-  rc = decode_layer(L, LayerInput{x, 1, 0, 0}, 0.f, T, nullptr, route, wsb, st, &S);
-  if (rc) return rc;
-  const WsLayout W = ws_layout_decode(L, T);
-  HIPCHK(launch_combine(reinterpret_cast<const float*>(wsb + W.ypart), S, (int64_t)8 * L->d, T, L->d, y, st));
   return MOE_OK;
 }
 
-int moe_stack_forward(const moe_layer* const* layers, int n_layers, const float* x, int T, float eps, float* y,
-                      float* y_layers, int32_t* idx_layers, float* w_layers, void* ws, size_t ws_bytes,
-                      void* stream) {
+// One decode pass of T tokens and the combine of the down splits into y.
+static int decode_layer_out(const moe_layer* L, const float* x, int T, float* y, const moe_route_io* route,
+                            uint8_t* wsb, hipStream_t st, bool act16) {
+  int S = 1;
+  int rc = decode_layer(L, LayerInput{x, 1, 0, 0}, 0.f, T, nullptr, route, wsb, st, &S, act16);
+  if (rc) return rc;
+  const WsLayout W = ws_layout_decode(L, T, act16);
+  const int64_t R = act16 ? MOE_MAX_TOK_F16ACT : MOE_MAX_TOK_DECODE;
+  HIPCHK(launch_combine(reinterpret_cast<const float*>(wsb + W.ypart), S, R * L->d, T, L->d, y, st));
+  return MOE_OK;
+}
+
+int moe_layer_forward(const moe_layer* L, const float* x, int T, float* y, const moe_route_io* route, void* ws,
+                      size_t ws_bytes, void* stream) {
+  int rc = layer_args(L, x, T, y, route, ws, ws_bytes);
+  if (rc || T == 0) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
+  if (T > MOE_MAX_TOK_DECODE) return prefill_layer(L, x, 0, 0.f, T, y, route, wsb, st);
+  return decode_layer_out(L, x, T, y, route, wsb, st, false);
+}
+
+int moe_layer_forward_f16act(const moe_layer* L, const float* x, int T, float* y, const moe_route_io* route,
+                             void* ws, size_t ws_bytes, void* stream) {
+  if (T > MOE_MAX_TOK_F16ACT) return fail(MOE_ERR_UNSUPPORTED, "T above %d not supported with fp16 activations", MOE_MAX_TOK_F16ACT);
+  int rc = layer_args(L, x, T, y, route, ws, ws_bytes);
+  if (rc || T == 0) return rc;
+  return decode_layer_out(L, x, T, y, route, reinterpret_cast<uint8_t*>(ws), reinterpret_cast<hipStream_t>(stream),
+                          true);
+}
+
+// Argument checks shared by the stack entry points.
+static int stack_args(const moe_layer* const* layers, int n_layers, const float* x, int T, float* y,
+                      float* y_layers, int32_t* idx_layers, float* w_layers, void* ws, size_t ws_bytes) {
   if (!layers || n_layers < 1) return fail(MOE_ERR_ARG, "need at least one layer");
   if (T < 0) return fail(MOE_ERR_ARG, "T must be >= 0");
   if (T == 0) return MOE_OK;
@@ -782,6 +815,48 @@ int moe_stack_forward(const moe_layer* const* layers, int n_layers, const float*
   }
   init_kernels();
   if (g_init_err != hipSuccess) return fail(MOE_ERR_HIP, "kernel init: %s", hipGetErrorString(g_init_err));
+  return MOE_OK;
+}
+
+// The decode kernels, the whole stack for up to `chunk` tokens at a time
+// (rows are independent); chunk rows sit at row c0 of x, y, y_layers[l] and
+// the routing outputs.
+static int decode_stack(const moe_layer* const* layers, int n_layers, const float* x, int T, float eps, float* y,
+                        float* y_layers, int32_t* idx_layers, float* w_layers, uint8_t* wsb, hipStream_t s,
+                        bool act16) {
+  const int d = layers[0]->d;
+  const int chunk = act16 ? MOE_MAX_TOK_F16ACT : MOE_MAX_TOK_DECODE;
+  for (int c0 = 0; c0 < T; c0 += chunk) {
+    const int Tc = T - c0 < chunk ? T - c0 : chunk;
+    LayerInput in{x + (size_t)c0 * d, 1, 0, 0};
+    for (int l = 0; l < n_layers; ++l) {
+      moe_route_io r{};
+      if (idx_layers) {
+        r.out_idx = idx_layers + ((size_t)l * T + c0) * layers[l]->k;
+        r.out_w = w_layers + ((size_t)l * T + c0) * layers[l]->k;
+      }
+      float* prev_out = (l > 0 && y_layers) ? y_layers + ((size_t)(l - 1) * T + c0) * d : nullptr;
+      int S = 1;
+      int rc = decode_layer(layers[l], in, eps, Tc, prev_out, &r, wsb, s, &S, act16);
+      if (rc) return rc;
+      const WsLayout W = ws_layout_decode(layers[l], Tc, act16);
+      in = LayerInput{reinterpret_cast<const float*>(wsb + W.ypart), S, (int64_t)chunk * d, 1};
+    }
+    serial_point(s);
+    HIPCHK(launch_combine(in.p, in.S, in.stride, Tc, d, y + (size_t)c0 * d, s));
+    if (y_layers)
+      HIPCHK(hipMemcpyAsync(y_layers + ((size_t)(n_layers - 1) * T + c0) * d, y + (size_t)c0 * d, (size_t)Tc * d * 4,
+                            hipMemcpyDeviceToDevice, s));
+  }
+  return MOE_OK;
+}
+
+int moe_stack_forward(const moe_layer* const* layers, int n_layers, const float* x, int T, float eps, float* y,
+                      float* y_layers, int32_t* idx_layers, float* w_layers, void* ws, size_t ws_bytes,
+                      void* stream) {
+  int rc = stack_args(layers, n_layers, x, T, y, y_layers, idx_layers, w_layers, ws, ws_bytes);
+  if (rc || T == 0) return rc;
+  const int d = layers[0]->d;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
   if (T > MOE_MAX_TOK_CHUNKED) {
@@ -797,38 +872,23 @@ int moe_stack_forward(const moe_layer* const* layers, int n_layers, const float*
       }
       const float* in = l == 0 ? x : (y_layers ? y_layers + (size_t)(l - 1) * T * d : y);
       float* out = y_layers ? y_layers + (size_t)l * T * d : y;
-      int rc = prefill_layer(layers[l], in, l > 0, eps, T, out, &r, wsb, s);
+      rc = prefill_layer(layers[l], in, l > 0, eps, T, out, &r, wsb, s);
       if (rc) return rc;
     }
     if (y_layers) HIPCHK(hipMemcpyAsync(y, y_layers + (size_t)(n_layers - 1) * T * d, (size_t)T * d * 4, hipMemcpyDeviceToDevice, s));
     return MOE_OK;
   }
-  // decode kernels, the whole stack for up to 8 tokens at a time (rows are
-  // independent); chunk rows sit at row c0 of x, y, y_layers[l] and the
-  // routing outputs
-  for (int c0 = 0; c0 < T; c0 += MOE_MAX_TOK_DECODE) {
-    const int Tc = T - c0 < MOE_MAX_TOK_DECODE ? T - c0 : MOE_MAX_TOK_DECODE;
-    LayerInput in{x + (size_t)c0 * d, 1, 0, 0};
-    for (int l = 0; l < n_layers; ++l) {
-      moe_route_io r{};
-      if (idx_layers) {
-        r.out_idx = idx_layers + ((size_t)l * T + c0) * layers[l]->k;
-        r.out_w = w_layers + ((size_t)l * T + c0) * layers[l]->k;
-      }
-      float* prev_out = (l > 0 && y_layers) ? y_layers + ((size_t)(l - 1) * T + c0) * d : nullptr;
-      int S = 1;
-      int rc = decode_layer(layers[l], in, eps, Tc, prev_out, &r, wsb, s, &S);
-      if (rc) return rc;
-      const WsLayout W = ws_layout_decode(layers[l], Tc);
-      in = LayerInput{reinterpret_cast<const float*>(wsb + W.ypart), S, (int64_t)8 * d, 1};
-    }
-    serial_point(s);
-    HIPCHK(launch_combine(in.p, in.S, in.stride, Tc, d, y + (size_t)c0 * d, s));
-    if (y_layers)
-      HIPCHK(hipMemcpyAsync(y_layers + ((size_t)(n_layers - 1) * T + c0) * d, y + (size_t)c0 * d, (size_t)Tc * d * 4,
-                            hipMemcpyDeviceToDevice, s));
-  }
-  return MOE_OK;
+  return decode_stack(layers, n_layers, x, T, eps, y, y_layers, idx_layers, w_layers, wsb, s, false);
+}
+
+int moe_stack_forward_f16act(const moe_layer* const* layers, int n_layers, const float* x, int T, float eps,
+                             float* y, float* y_layers, int32_t* idx_layers, float* w_layers, void* ws,
+                             size_t ws_bytes, void* stream) {
+  if (T > MOE_MAX_TOK_F16ACT) return fail(MOE_ERR_UNSUPPORTED, "T above %d not supported with fp16 activations", MOE_MAX_TOK_F16ACT);
+  int rc = stack_args(layers, n_layers, x, T, y, y_layers, idx_layers, w_layers, ws, ws_bytes);
+  if (rc || T == 0) return rc;
+  return decode_stack(layers, n_layers, x, T, eps, y, y_layers, idx_layers, w_layers, reinterpret_cast<uint8_t*>(ws),
+                      reinterpret_cast<hipStream_t>(stream), true);
 }
 
 int moe_group_workspace_bytes(int T, int E, int k, size_t* bytes) {

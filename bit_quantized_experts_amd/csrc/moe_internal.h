@@ -26,6 +26,9 @@
 
 #define MOE_BLOCK 32
 #define MOE_MAX_TOK_DECODE 8
+// Tokens per decode pass with fp16 activations (one MFMA row per token
+// instead of an fp16 hi and lo row).
+#define MOE_MAX_TOK_F16ACT 16
 // Stacks of up to this many tokens run the decode kernels, the whole stack
 // for MOE_MAX_TOK_DECODE tokens at a time (faster per layer than the grouped
 // GEMMs at these sizes; a single layer above MOE_MAX_TOK_DECODE tokens is

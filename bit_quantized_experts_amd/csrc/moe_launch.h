@@ -6,9 +6,9 @@
 
 #include "moe_internal.h"
 
-// Largest number of expert slots a decode call can touch: up to 8 tokens x 16
-// routed experts, plus the shared expert.
-#define MOE_MAX_SLOTS (MOE_MAX_TOK_DECODE * MOE_MAX_K + 1)
+// Largest number of expert slots a decode pass can touch: up to 16 tokens
+// (fp16 activations) x 16 routed experts, plus the shared expert.
+#define MOE_MAX_SLOTS (MOE_MAX_TOK_F16ACT * MOE_MAX_K + 1)
 // Columns of the layer input handled by one route workgroup.
 #define MOE_ROUTE_COLS 128
 // Expert rows per route workgroup (4 waves x 16 rows).
@@ -32,7 +32,7 @@ struct SelectArgs {
   float eps;
   uint32_t* ctrl;      // completion counters, one per row slice; zero between calls
   float* logits;       // ws [T][E]
-  float* rnorm;        // ws [8]: per-token divisor (1 when norm == 0)
+  float* rnorm;        // ws [16]: per-token divisor (1 when norm == 0)
   float* out_logits;   // optional copy of the logits
 };
 
@@ -43,6 +43,7 @@ struct RouteArgs {
   const _Float16* wh;  // router rows times 2^-ew, fp16 hi part, B-fragments [E16/16][d/32][64][8]
   const _Float16* wl;  // same, lo part
   int32_t T, d, E, code_off, do_logits;
+  int32_t act16;    // 1: gate/up A-fragments hold 16 tokens in fp16 (else 8 tokens as fp16 hi + lo)
   float* lp;        // ws [d/MOE_ROUTE_COLS][T][E] partial logits
   _Float16* xfrag;  // ws [d/32][64][8]
   float* xsum;      // ws [d/32][16]
@@ -72,13 +73,14 @@ struct GuArgs {
   int32_t k;
   int32_t* n_slots;      // out [1]
   int32_t* slot_expert;  // out [MAX_SLOTS]
-  float* slot_w;         // out [MAX_SLOTS][8]
+  float* slot_w;         // out [MAX_SLOTS][16]
   const float* rnorm;
   const _Float16* xfrag;
   const float* xsum;
   _Float16* hfrag;  // ws [MAX_SLOTS][nbI][64][8]
   float* hsum;      // ws [MAX_SLOTS][2 nbI][16], one row of sums per 16-row tile
   int32_t E, I, Is, T, n_kg, bits, nbI, code_off, has_shared;
+  int32_t act16;  // 1: A rows are 16 tokens in fp16 (else 8 tokens as fp16 hi + lo)
 };
 
 struct DownArgs {
@@ -88,7 +90,8 @@ struct DownArgs {
   const _Float16* hfrag;
   const float* hsum;
   int32_t E, d, T, bits, nbI, BK, RT, n_kg_r, n_kg_s, S, has_shared, max_slots;
-  float* ypart;  // ws [S][8][d]
+  int32_t act16;  // 1: A rows are 16 tokens in fp16 (else 8 tokens as fp16 hi + lo)
+  float* ypart;   // ws [S][R][d], R = 16 with act16, else 8
 };
 
 hipError_t launch_pack_matrix(const uint8_t* canon, int64_t canon_stride, uint8_t* out, int64_t out_stride,

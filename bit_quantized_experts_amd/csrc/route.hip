@@ -73,47 +73,50 @@ DEVI bool count_done(uint32_t* ctr, uint32_t total, int* flag) {
   return *flag != 0;
 }
 
-// Wavefront wv finishes tokens wv and wv + 4 (pairs p = tid and tid + 256:
-// token p / 64, expert rs * 64 + p % 64); every load is issued before the
-// first add, at clamped addresses.
+// Wavefront wv finishes tokens wv + 4j (below T), two at a time (pairs p =
+// tid and tid + 256 of a pass: token 8h + p / 64, expert rs * 64 + p % 64);
+// every load of a pass is issued before its first add, at clamped
+// addresses.
 template <int MAXCS>
 DEVI void finish_slice(const RouteArgs& a, int rs) {
   const SelectArgs& c = a.sel;
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int T = a.T, E = a.E, n_cs = c.n_cs;
-  static_assert(MOE_MAX_TOK_DECODE * MOE_ROUTE_ROWS <= 2 * 256, "two (token, expert) pairs per thread");
+  static_assert(MOE_MAX_TOK_F16ACT <= 16, "two passes of 8 tokens");
   const int er = rs * MOE_ROUTE_ROWS + lane, e = min(er, E - 1);
   const bool e_ok = er < E;
-  int t[2];
-  float ss[2], tmp[2][MAXCS];
-  const float* ssr = c.ss_part + (size_t)rs * n_cs * T;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    t[j] = min(wv + 4 * j, T - 1);
-    ss[j] = ld_dev(ssr + min(lane, n_cs - 1) * T + t[j]);
-    if (a.do_logits) {
-#pragma unroll
-      for (int q = 0; q < MAXCS; ++q) tmp[j][q] = ld_dev(a.lp + ((size_t)min(q, n_cs - 1) * T + t[j]) * E + e);
-    }
-  }
   const int ew = a.do_logits ? c.ew[e] : 0;
   const float bias = a.do_logits ? c.br[e] : 0.f;
+  const float* ssr = c.ss_part + (size_t)rs * n_cs * T;
+  for (int h = 0; 8 * h < T; ++h) {
+    int t[2];
+    float ss[2], tmp[2][MAXCS];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int tok = wv + 4 * j;
-    const float r = c.norm ? sqrtf(wave_sum((lane < n_cs) ? ss[j] : 0.f) / (float)c.d + c.eps) : 1.0f;
-    if (tok >= T) continue;
-    if (rs == 0 && lane == 0) c.rnorm[tok] = r;
-    if (!a.do_logits) continue;
-    float acc = tmp[j][0];
+    for (int j = 0; j < 2; ++j) {
+      t[j] = min(8 * h + wv + 4 * j, T - 1);
+      ss[j] = ld_dev(ssr + min(lane, n_cs - 1) * T + t[j]);
+      if (a.do_logits) {
 #pragma unroll
-    for (int q = 1; q < MAXCS; ++q)
-      if (q < n_cs) acc += tmp[j][q];
-    const float x = ldexpf(acc, ew);  // router row factor, exact
-    const float l = (c.norm ? x / r : x) + bias;
-    if (e_ok) {
-      c.logits[(size_t)tok * E + er] = l;
-      if (c.out_logits) c.out_logits[(size_t)tok * E + er] = l;
+        for (int q = 0; q < MAXCS; ++q) tmp[j][q] = ld_dev(a.lp + ((size_t)min(q, n_cs - 1) * T + t[j]) * E + e);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int tok = 8 * h + wv + 4 * j;
+      const float r = c.norm ? sqrtf(wave_sum((lane < n_cs) ? ss[j] : 0.f) / (float)c.d + c.eps) : 1.0f;
+      if (tok >= T) continue;
+      if (rs == 0 && lane == 0) c.rnorm[tok] = r;
+      if (!a.do_logits) continue;
+      float acc = tmp[j][0];
+#pragma unroll
+      for (int q = 1; q < MAXCS; ++q)
+        if (q < n_cs) acc += tmp[j][q];
+      const float x = ldexpf(acc, ew);  // router row factor, exact
+      const float l = (c.norm ? x / r : x) + bias;
+      if (e_ok) {
+        c.logits[(size_t)tok * E + er] = l;
+        if (c.out_logits) c.out_logits[(size_t)tok * E + er] = l;
+      }
     }
   }
 }
@@ -135,9 +138,11 @@ DEVI void route_finish(const RouteArgs& a, int rs) {
 // (if asked) and the fp16 hi/lo MFMA A-fragments of the 4 blocks of the
 // slice:
 //   lane L = m + 16q of block b holds row m (m < 8: token m, hi part; m >= 8:
-//   token m-8, lo part) at inputs 8q..8q+7; xsum[b][m] = -code_off * sum.
-// The partial logits run on the matrix cores: the same A-fragments (built in
-// registers by every workgroup) times the router rows prepared at pack time
+//   token m-8, lo part) at inputs 8q..8q+7; xsum[b][m] = -code_off * sum;
+//   with fp16 activations (act16) row m is token m rounded to fp16.
+// The partial logits run on the matrix cores: hi/lo A-fragments of 8 tokens
+// (built in registers by every workgroup; a second row tile for tokens 8..15)
+// times the router rows prepared at pack time
 // as 2^ew (wh + wl), fp16 hi and lo B-fragments, so one wavefront's 16
 // experts over the 4 blocks take 8 v_mfma_f32_16x16x32_f16 and the hi and lo
 // rows of a token are added once at the end.  All four products of the
@@ -146,7 +151,7 @@ DEVI void route_finish(const RouteArgs& a, int rs) {
 // partials (exact) by the workgroup that finishes the row slice (above).
 // ---------------------------------------------------------------------------
 DEVI half8_t x_fragment(const float (*ys)[MOE_ROUTE_COLS], int bl, int lane, int T, float* sum) {
-  const int m = lane & 15, q = lane >> 4, tok = m & 7, lo = m >> 3;
+  const int m = lane & 15, q = lane >> 4, tok = m & 7, lo = m >> 3;  // (ys, T: from the tile's first token)
   float4_t v0 = float4_t{0.f, 0.f, 0.f, 0.f}, v1 = v0;
   if (tok < T) {
     v0 = *reinterpret_cast<const float4_t*>(&ys[tok][32 * bl + 8 * q]);
@@ -166,8 +171,27 @@ DEVI half8_t x_fragment(const float (*ys)[MOE_ROUTE_COLS], int bl, int lane, int
   return h;
 }
 
+// The same block with one fp16 row per token (16 tokens).
+DEVI half8_t x_fragment16(const float (*ys)[MOE_ROUTE_COLS], int bl, int lane, int T, float* sum) {
+  const int m = lane & 15, q = lane >> 4;
+  float4_t v0 = float4_t{0.f, 0.f, 0.f, 0.f}, v1 = v0;
+  if (m < T) {
+    v0 = *reinterpret_cast<const float4_t*>(&ys[m][32 * bl + 8 * q]);
+    v1 = *reinterpret_cast<const float4_t*>(&ys[m][32 * bl + 8 * q + 4]);
+  }
+  half8_t h;
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    h[c] = (_Float16)(c < 4 ? v0[c] : v1[c - 4]);
+    s += (float)h[c];
+  }
+  *sum = s;
+  return h;
+}
+
 __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
-  __shared__ float ys[MOE_MAX_TOK_DECODE][MOE_ROUTE_COLS];
+  __shared__ float ys[MOE_MAX_TOK_F16ACT][MOE_ROUTE_COLS];
   const int cs = blockIdx.x, rs = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -183,11 +207,11 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   const int et = rs * (MOE_ROUTE_ROWS / 16) + wv;  // 16-expert tile
   const bool tile_ok = a.do_logits && et * 16 < E;
   constexpr int RQ = MOE_ROUTE_COLS / 4;                   // float4 per token row of the slice
-  constexpr int PER = (MOE_MAX_TOK_DECODE * RQ + 255) / 256;  // float4 per thread
+  constexpr int PER = (MOE_MAX_TOK_F16ACT * RQ + 255) / 256;  // float4 per thread
   float4_t v[PER][MOE_MAX_IN_SPLITS];
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    const int i = tid + 256 * j, t = min(i / RQ, T - 1), c4 = i % RQ;
+    const int i = tid + 256 * j, t = min(i / RQ, T - 1), c4 = i % RQ;  // (rows past T re-read row T - 1)
     const float* src = a.in + (size_t)t * d + c0 + 4 * c4;
 #pragma unroll
     for (int s = 0; s < MOE_MAX_IN_SPLITS; ++s)
@@ -231,7 +255,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     for (int bl = wv; bl < NBL; bl += 4) {
       const int b = cs * NBL + bl;
       float s;
-      const half8_t h = x_fragment(ys, bl, lane, T, &s);
+      const half8_t h = a.act16 ? x_fragment16(ys, bl, lane, T, &s) : x_fragment(ys, bl, lane, T, &s);
       *reinterpret_cast<half8_t*>(a.xfrag + ((size_t)b * 64 + lane) * 8) = h;
       s += __shfl_xor(s, 16, 64);
       s += __shfl_xor(s, 32, 64);
@@ -240,27 +264,31 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   }
 
   if (tile_ok) {
-    half8_t A[NBL];
+    // row tiles of 8 tokens: tokens 8 tb .. 8 tb + 7
+    for (int tb = 0; 8 * tb < T; ++tb) {
+      half8_t A[NBL];
 #pragma unroll
-    for (int j = 0; j < NBL; ++j) {
-      float s;
-      A[j] = x_fragment(ys, j, lane, T, &s);
-    }
-    float4_t acc = float4_t{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < NBL; ++j) {
+        float s;
+        A[j] = x_fragment(ys + 8 * tb, j, lane, T - 8 * tb, &s);
+      }
+      float4_t acc = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < NBL; ++j) {
-      acc = mfma16x16x32(A[j], BH[j], acc);
-      acc = mfma16x16x32(A[j], BL[j], acc);
-    }
-    // lane l: expert et*16 + (l & 15), C rows 4(l>>4)+i: token 4((l>>4)&1)+i,
-    // hi part in lanes < 32, lo part in lanes >= 32.  The partial logits are
-    // left without the row factor 2^ew; it is applied to their sum.
-    const int e = et * 16 + (lane & 15);
+      for (int j = 0; j < NBL; ++j) {
+        acc = mfma16x16x32(A[j], BH[j], acc);
+        acc = mfma16x16x32(A[j], BL[j], acc);
+      }
+      // lane l: expert et*16 + (l & 15), C rows 4(l>>4)+i: token 8 tb +
+      // 4((l>>4)&1)+i, hi part in lanes < 32, lo part in lanes >= 32.  The
+      // partial logits are left without the row factor 2^ew; it is applied
+      // to their sum.
+      const int e = et * 16 + (lane & 15);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float v = add_partner32(acc[i]);
-      const int t = 4 * ((lane >> 4) & 1) + i;
-      if (lane < 32 && e < E && t < T) st_dev(a.lp + ((size_t)cs * T + t) * E + e, v);
+      for (int i = 0; i < 4; ++i) {
+        const float v = add_partner32(acc[i]);
+        const int t = 8 * tb + 4 * ((lane >> 4) & 1) + i;
+        if (lane < 32 && e < E && t < T) st_dev(a.lp + ((size_t)cs * T + t) * E + e, v);
+      }
     }
   }
   route_finish(a, rs);
@@ -313,7 +341,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   const dim3 grid(a.d / MOE_ROUTE_COLS, a.do_logits ? (a.E + MOE_ROUTE_ROWS - 1) / MOE_ROUTE_ROWS : 1);
   // the completion counts must match the grid, or no workgroup selects
   if ((int)grid.x != a.sel.n_cs || (int)grid.y != a.sel.n_rs || a.sel.n_rs > MOE_CTRL_WORDS ||
-      a.sel.n_cs > MOE_MAX_CS || a.T < 1 || a.T > MOE_MAX_TOK_DECODE)
+      a.sel.n_cs > MOE_MAX_CS || a.T < 1 || a.T > (a.act16 ? MOE_MAX_TOK_F16ACT : MOE_MAX_TOK_DECODE))
     return hipErrorInvalidValue;
   MOE_LAUNCH(route_kernel, grid, dim3(256), 0, s, a);
   return hipGetLastError();

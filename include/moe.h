@@ -165,6 +165,21 @@ int moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
 int moe_layer_forward(const moe_layer *layer, const float *x, int T, float *y, const moe_route_io *route,
                       void *ws, size_t ws_bytes, void *stream);
 
+/* The same layer through the decode kernels with fp16 activations, for
+ * 1 <= T <= 16 tokens in one pass: speed for accuracy, the trade the
+ * strata-mlx engine offers between its 16-bit default and its slower,
+ * exact float32 mode [strata-mlx wiki, "Measured"].  The expert FFN's
+ * activations, x (normalised, for stacked layers)
+ * and h = silu(g) u times the gate weight, are rounded to fp16 once instead
+ * of being carried as fp16 hi + lo, so one matrix-core pass carries 16
+ * tokens instead of 8 and every dequantized weight fragment serves twice as
+ * many tokens; the router logits, the selection and the accumulation are
+ * as in moe_layer_forward (the logits keep the hi + lo activations).
+ * Arguments, routing input/output and errors as moe_layer_forward; T > 16 is
+ * MOE_ERR_UNSUPPORTED.  ws_bytes >= moe_workspace_bytes(layer, T). */
+int moe_layer_forward_f16act(const moe_layer *layer, const float *x, int T, float *y, const moe_route_io *route,
+                             void *ws, size_t ws_bytes, void *stream);
+
 /* A stack of layers with RMSNorm (unit weight) between consecutive layers
  * (T <= 16: decode kernels, the whole stack for 8 tokens at a time; T > 16:
  * prefill kernels, one layer after another):
@@ -177,6 +192,14 @@ int moe_layer_forward(const moe_layer *layer, const float *x, int T, float *y, c
 int moe_stack_forward(const moe_layer *const *layers, int n_layers, const float *x, int T, float eps,
                       float *y, float *y_layers, int32_t *idx_layers, float *w_layers, void *ws,
                       size_t ws_bytes, void *stream);
+
+/* The stack through the decode kernels with fp16 activations (as
+ * moe_layer_forward_f16act), 1 <= T <= 16 tokens per call, the whole stack
+ * in one pass.  Arguments and outputs as moe_stack_forward; T > 16 is
+ * MOE_ERR_UNSUPPORTED. */
+int moe_stack_forward_f16act(const moe_layer *const *layers, int n_layers, const float *x, int T, float eps,
+                             float *y, float *y_layers, int32_t *idx_layers, float *w_layers, void *ws,
+                             size_t ws_bytes, void *stream);
 
 /* Token-to-expert grouping (counting sort) of a routing idx device int32
  * [T][k].  Pair (t, r) names expert idx[t][r]; it is used unless that id is

@@ -79,6 +79,13 @@ def test_host_checks_without_gpu(bqe):
     assert L.moe_workspace_init(None, 1024, None) == bqe.MOE_ERR_ARG
     assert L.moe_layer_forward(None, None, 1, None, None, None, 0, None) == bqe.MOE_ERR_ARG
     assert L.moe_stack_forward(None, 0, None, 1, ctypes.c_float(1e-6), None, None, None, None, None, 0, None) == bqe.MOE_ERR_ARG
+    # fp16-activation entry points: at most 16 tokens, then the usual checks
+    assert L.moe_layer_forward_f16act(None, None, 17, None, None, None, 0, None) == bqe.MOE_ERR_UNSUPPORTED
+    assert L.moe_layer_forward_f16act(None, None, 1, None, None, None, 0, None) == bqe.MOE_ERR_ARG
+    assert L.moe_stack_forward_f16act(None, 1, None, 17, ctypes.c_float(1e-6), None, None, None, None, None, 0,
+                                      None) == bqe.MOE_ERR_UNSUPPORTED
+    assert L.moe_stack_forward_f16act(None, 0, None, 1, ctypes.c_float(1e-6), None, None, None, None, None, 0,
+                                      None) == bqe.MOE_ERR_ARG
     assert L.moe_timing_start(9, 1) == bqe.MOE_ERR_ARG
     assert L.moe_group_workspace_bytes(-1, 8, 2, ctypes.byref(ctypes.c_size_t())) == bqe.MOE_ERR_ARG
     assert L.moe_group_tokens(None, 4, 8, 2, None, None, None, None, 0, None) == bqe.MOE_ERR_ARG
