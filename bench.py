@@ -151,8 +151,12 @@ def bench_prefill(args):
     w = torch.empty((T, wl.k), dtype=torch.float32, device=dev)
     rio = bqe.RouteIO(None, None, None, idx.data_ptr(), w.data_ptr())
 
+    if args.f16act and T > bqe.MAX_TOK_F16ACT:
+        raise SystemExit(f"--f16act takes at most {bqe.MAX_TOK_F16ACT} tokens")
+    fwd = bqe.moe_layer_forward_f16act if args.f16act else bqe.moe_layer_forward
+
     def run_pass():
-        bqe.moe_layer_forward(L.handle, x, y, ws, rio)
+        fwd(L.handle, x, y, ws, rio)
 
     if args.timing_only:
         bqe.moe_timing_start(bqe.TIMING_PREFILL_ROUTER, 1)
@@ -164,7 +168,7 @@ def bench_prefill(args):
     kdur = {}
     # a layer of at most 8 tokens runs the decode kernels: time those
     classes = ((bqe.TIMING_GATE_UP, "gate_up"), (bqe.TIMING_DOWN, "down"), (bqe.TIMING_ROUTER, "router")) \
-        if T <= bqe.MAX_TOK_DECODE_KERNELS else \
+        if T <= bqe.MAX_TOK_DECODE_KERNELS or args.f16act else \
         ((bqe.TIMING_PREFILL_GATE_UP, "gate_up"), (bqe.TIMING_PREFILL_DOWN, "down"), (bqe.TIMING_PREFILL_ROUTER, "router"))
     for cls, name in classes:
         tot, n = 0.0, 0
@@ -252,7 +256,8 @@ def bench_prefill(args):
         "vs_baseline": None,
         "dtype": "fp16 MFMA operands (weights s*c, activations scaled per row), fp32 accumulate",
         "data": "synthetic (counter-hash codes/scales, N(0,1) activations, N(0,0.02) router + Zipf(1.1) log bias)",
-        "config": {"workload": wl.name, "layers": 1, "T": T, "d": wl.d, "experts": wl.E, "d_ff": wl.I,
+        "config": {"workload": wl.name, "layers": 1, "T": T, "f16act": bool(args.f16act), "d": wl.d, "experts": wl.E,
+                   "d_ff": wl.I,
                    "shared_d_ff": wl.Is, "top_k": wl.k, "bits": wl.bits, "graph": graph is not None,
                    "parallelism": "none (1 GPU)"},
         "step_ms": {"p10": float(np.percentile(times, 10)) * 1e3, "median": float(np.median(times)) * 1e3,
