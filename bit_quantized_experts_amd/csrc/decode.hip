@@ -438,12 +438,16 @@ __global__ __launch_bounds__(512) void down_decode_kernel(DownArgs a) {
   // expert ids of this wave's first batch, fetched together with n_slots
   // (the slot of an item does not depend on n_slots; ids past the list are
   // clamped to a valid expert and never used)
-  int pre[BATCH];
-#pragma unroll
-  for (int q = 0; q < BATCH; ++q) {
-    const int it = wv + q * nw;
-    const int u = (it < n_sh) ? 0 : first_r + S * ((it - n_sh) / a.n_kg_r);
-    pre[q] = a.slot_expert[min(u, a.max_slots - 1)];
+  // (two named registers: an array here was kept in scratch memory, and its
+  // store waited for the loads)
+  static_assert(BATCH == 2, "two prefetched ids");
+  int pre0, pre1;
+  {
+    const int it0 = wv, it1 = wv + nw;
+    const int u0 = (it0 < n_sh) ? 0 : first_r + S * ((it0 - n_sh) / a.n_kg_r);
+    const int u1 = (it1 < n_sh) ? 0 : first_r + S * ((it1 - n_sh) / a.n_kg_r);
+    pre0 = a.slot_expert[min(u0, a.max_slots - 1)];
+    pre1 = a.slot_expert[min(u1, a.max_slots - 1)];
   }
   const int n_rs = (first_r < ns) ? (ns - first_r + S - 1) / S : 0;
   const int n_items = n_sh + n_rs * a.n_kg_r;
@@ -474,7 +478,7 @@ __global__ __launch_bounds__(512) void down_decode_kernel(DownArgs a) {
         u = first_r + S * (ri / a.n_kg_r);
         kg = ri % a.n_kg_r;
         n_kg = a.n_kg_r;
-        int e = (b0 == wv) ? (ok[q] ? pre[q] : pre[0]) : a.slot_expert[u];
+        int e = (b0 == wv) ? ((ok[q] && q == 1) ? pre1 : pre0) : a.slot_expert[u];
         e = min(max(e, 0), a.E - 1);
         mat = a.X.experts + (int64_t)e * a.X.ex_stride + a.X.off_down;
       }
