@@ -126,6 +126,7 @@ DEVI void route_finish(const RouteArgs& a, int rs) {
   if (!count_done(a.sel.ctrl + rs, (uint32_t)a.sel.n_cs, &flag)) return;
   if (threadIdx.x == 0) a.sel.ctrl[rs] = 0u;
   if (a.sel.n_cs <= 16) finish_slice<16>(a, rs);
+  else if (a.sel.n_cs <= 20) finish_slice<20>(a, rs);  // d = 2560
   else if (a.sel.n_cs <= 32) finish_slice<32>(a, rs);
   else finish_slice<64>(a, rs);
 }
