@@ -161,32 +161,47 @@ struct GroupRegs {
   ChunkRegs<BITS> g, u;
 };
 
-// Activation blocks [b0, b0 + nblk) into LDS (plain loads and LDS stores).
+// Activation blocks [b0, b0 + nblk) into LDS (plain loads and LDS stores),
+// in two halves so that other work can run while the loads are in flight.
 // Entry p of a block is lane p % 64 of its A-fragment, which holds token
 // (p % 64) & 7 (fp16 activations: (p % 64) & 15); the rows of tokens >= T are
 // zeros (as the route kernel writes them), so they are stored without being
 // read.
-DEVI void stage_window(GuLds& L, const GuArgs& a, int b0, int nblk, int tid) {
-  constexpr int PER = GU_WIN * 64 / (64 * GU_NW);
+struct WindowRegs {
+  static constexpr int PER = GU_WIN * 64 / (64 * GU_NW);
+  u32x4_t v[PER];
+  float4_t c;
+};
+
+DEVI void window_load(WindowRegs& W, const GuArgs& a, int b0, int nblk, int tid) {
   const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.xfrag + (size_t)b0 * 512);
-  u32x4_t* dst = reinterpret_cast<u32x4_t*>(L.xs);
   const int n = nblk * 64, nc = nblk * 4;
   const bool live = (tid & (a.act16 ? 15 : 7)) < a.T;  // (64 * GU_NW is a multiple of 64: same lane for every i)
-  u32x4_t v[PER];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
+  for (int i = 0; i < WindowRegs::PER; ++i) {
     const int p = tid + 64 * GU_NW * i;
-    v[i] = u32x4_t{0u, 0u, 0u, 0u};
-    if (p < n && live) v[i] = src[p];
+    W.v[i] = u32x4_t{0u, 0u, 0u, 0u};
+    if (p < n && live) W.v[i] = src[p];
   }
-  float4_t c{};
-  if (tid < nc) c = reinterpret_cast<const float4_t*>(a.xsum + (size_t)b0 * 16)[tid];
+  W.c = float4_t{0.f, 0.f, 0.f, 0.f};
+  if (tid < nc) W.c = reinterpret_cast<const float4_t*>(a.xsum + (size_t)b0 * 16)[tid];
+}
+
+DEVI void window_store(const WindowRegs& W, GuLds& L, int nblk, int tid) {
+  u32x4_t* dst = reinterpret_cast<u32x4_t*>(L.xs);
+  const int n = nblk * 64, nc = nblk * 4;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
+  for (int i = 0; i < WindowRegs::PER; ++i) {
     const int p = tid + 64 * GU_NW * i;
-    if (p < n) dst[p] = v[i];
+    if (p < n) dst[p] = W.v[i];
   }
-  if (tid < nc) reinterpret_cast<float4_t*>(L.cs)[tid] = c;
+  if (tid < nc) reinterpret_cast<float4_t*>(L.cs)[tid] = W.c;
+}
+
+DEVI void stage_window(GuLds& L, const GuArgs& a, int b0, int nblk, int tid) {
+  WindowRegs W;
+  window_load(W, a, b0, nblk, tid);
+  window_store(W, L, nblk, tid);
 }
 
 template <int BITS>
@@ -277,8 +292,12 @@ __global__ __launch_bounds__(64 * GU_NW) void gu_decode_kernel(GuArgs a) {
     }
   }
   const float rnv = (tid >= 64 && tid < 64 + T) ? a.rnorm[tid - 64] : 1.0f;
-  if (n_win == 1) stage_window(L, a, 0, 8 * n_kg, tid);
-  if (tid >= 64 && tid < 80) L.rn[tid - 64] = 1.0f / rnv;
+  // the activation window (one window for inputs of up to GU_WIN blocks)
+  // stays in registers through the selection and is stored to LDS before the
+  // barrier that ends it: the selection starts as soon as its logits are in,
+  // while the larger window is still arriving
+  WindowRegs win;
+  if (n_win == 1) window_load(win, a, 0, 8 * n_kg, tid);
   clear_slots(L.S, E, T, base + min(tk, E), has_shared);
   __syncthreads();  // byte map and weight rows cleared before any wavefront marks
   static_assert(2 * GU_NW >= MOE_MAX_TOK_F16ACT, "two tokens per wavefront");
@@ -304,7 +323,10 @@ __global__ __launch_bounds__(64 * GU_NW) void gu_decode_kernel(GuArgs a) {
       mark_lane(L.S, mine[h].e, E);
     }
   }
-  __syncthreads();  // every token's experts marked
+  __builtin_amdgcn_sched_barrier(0);  // (the window's stores stay after the selection)
+  if (n_win == 1) window_store(win, L, 8 * n_kg, tid);
+  if (tid >= 64 && tid < 80) L.rn[tid - 64] = 1.0f / rnv;
+  __syncthreads();  // every token's experts marked, the window staged
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int t = wv + GU_NW * h;
