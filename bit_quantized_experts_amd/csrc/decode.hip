@@ -299,7 +299,7 @@ __global__ __launch_bounds__(64 * GU_NW) void gu_decode_kernel(GuArgs a) {
   WindowRegs win;
   if (n_win == 1) window_load(win, a, 0, 8 * n_kg, tid);
   clear_slots(L.S, E, T, base + min(tk, E), has_shared);
-  __syncthreads();  // byte map and weight rows cleared before any wavefront marks
+  lds_barrier();  // byte map and weight rows cleared before any wavefront marks (the loads stay in flight)
   static_assert(2 * GU_NW >= MOE_MAX_TOK_F16ACT, "two tokens per wavefront");
   TopkLane mine[2] = {{-1, 0.f}, {-1, 0.f}};
 #pragma unroll
@@ -326,7 +326,7 @@ __global__ __launch_bounds__(64 * GU_NW) void gu_decode_kernel(GuArgs a) {
   __builtin_amdgcn_sched_barrier(0);  // (the window's stores stay after the selection)
   if (n_win == 1) window_store(win, L, 8 * n_kg, tid);
   if (tid >= 64 && tid < 80) L.rn[tid - 64] = 1.0f / rnv;
-  __syncthreads();  // every token's experts marked, the window staged
+  lds_barrier();  // every token's experts marked, the window staged
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int t = wv + GU_NW * h;
@@ -338,7 +338,7 @@ __global__ __launch_bounds__(64 * GU_NW) void gu_decode_kernel(GuArgs a) {
       }
     }
   }
-  __syncthreads();  // slot list, rms and the staged activations
+  lds_barrier();  // slot list, rms and the staged activations
   if (blockIdx.x == 0) {
     const int ns = base + L.S.n_routed;
     if (tid == 0) *a.n_slots = ns;
