@@ -231,6 +231,16 @@ int moe_rmsnorm(const float *x, int T, int d, float eps, float *y, void *stream)
 int moe_debug_unpack(const moe_layer *layer, int expert, int mat, int8_t *codes, float *w_f32,
                      uint16_t *w_f16, void *stream);
 
+/* Tuning overrides read from the environment at each call (set them before
+ * the first call and leave them unchanged: the split count also sets the
+ * workspace layout, so moe_workspace_bytes and the forward calls must see
+ * the same value).  Defaults in brackets.
+ *   MOE_GU_WGS       decode gate/up workgroups [the CU count, at most the
+ *                    number of 16-row tiles]
+ *   MOE_DOWN_SPLITS  decode down-projection splits [2 x CUs / row groups,
+ *                    clamped to 1..8 and to the slot count]
+ *   MOE_DOWN_WAVES   wavefronts per decode down workgroup [8; 1..8] */
+
 /* Per-kernel timing for measurement: while enabled, the library brackets
  * every launch of the chosen kernel class with a pair of HIP events that the
  * launch records itself (the start and end of its dispatch), and every
