@@ -353,7 +353,7 @@ def bench_stack_prefill(args):
     total_flops = float(gu_flops.sum() + dn_flops.sum())
     cpu = None
     if args.cpu_tokens > 0 and args.cpu_layers > 0:
-        n_tok, n_l = args.cpu_tokens, min(args.cpu_layers, wl.layers)
+        n_tok, n_l = min(args.cpu_tokens, 16), min(args.cpu_layers, 2, wl.layers)  # (a few seconds)
         log(f"timing the CPU oracle on {n_tok} tokens through {n_l} layers ...")
         tps, per_layer = cpu_baseline_stack(wl, n_tok, mi.activations(wl, T=T, stream=1)[:n_tok], n_l)
         cpu = {"value": tps, "unit": "tokens/s", "cores": 1, "kind": "oracle",
@@ -451,9 +451,10 @@ def bench_layer_t1(args):
     achieved = per[dom] / kdur[dom] / 1e9
     cpu = None
     if args.cpu_layers > 0:
-        tps, per_layer = cpu_baseline_stack(wl, 1, mi.activations(wl, T=1, stream=500), 1)
+        rows = np.concatenate([mi.activations(wl, T=1, stream=500 + i) for i in range(ring)], axis=0)
+        tps, per_layer = cpu_baseline_stack(wl, ring, rows, 1)
         cpu = {"value": tps, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-               "sample": f"the layer on the first row of the ring ({per_layer:.2f} s), single thread; "
+               "sample": f"the layer on the {ring} rows of the ring ({per_layer:.2f} s), single thread; "
                          f"expert generation untimed"}
     out = {
         "metric": "MoE layer forwards/s (decode T=1, one full-size layer)",
@@ -512,8 +513,10 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--f16act", action="store_true",
                     help="stacks: the fp16-activation decode entry point (up to 16 tokens per pass)")
-    ap.add_argument("--cpu-layers", type=int, default=3, help="oracle sample size in layers (0 = skip)")
-    ap.add_argument("--cpu-tokens", type=int, default=16, help="prefill: oracle sample size in tokens (0 = skip)")
+    ap.add_argument("--cpu-layers", type=int, default=12,
+                    help="oracle sample size in layers (0 = skip; about 10 s of CPU time at T = 8)")
+    ap.add_argument("--cpu-tokens", type=int, default=96,
+                    help="prefill: oracle sample size in tokens (0 = skip; about 10 s of CPU time)")
     ap.add_argument("--timing-only", action="store_true",
                     help="only the per-kernel timing passes (every launch serialized), for profiler runs")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
