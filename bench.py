@@ -1,15 +1,21 @@
 """Benchmark of the low-bit sparse-MoE hot path on one MI355X.
 
-Default workload: the 48-layer MoE stack (d 2560, 512 experts of intermediate
-640 per layer, top-10 plus a shared expert of 640, 2-bit blocks), eight tokens
-per pass (one real token plus seven drafts, as in a verify pass), RMSNorm
-between layers.  One step = one pass of the whole stack over one batch of 8
-synthetic tokens, replayed from a HIP graph; all weights (about 38 GB) are
-resident in HBM before timing starts.  Consecutive steps take the next of 16
-input batches (so the routing changes from pass to pass), each step
-bracketed by its own events; the same is also reported with the Infinity
-Cache emptied before every pass, and for the same input replayed back to
-back.
+Headline (the line's value): the 48-layer MoE stack (d 2560, 512 experts of
+intermediate 640 per layer, top-10 plus a shared expert of 640, 2-bit blocks),
+eight tokens per pass (one real token plus seven drafts, as in a verify
+pass), RMSNorm between layers.  One step = one pass of the whole stack over
+one batch of 8 synthetic tokens, replayed from a HIP graph; all weights
+(about 38 GB) are resident in HBM before timing starts.  Consecutive steps
+take the next of 16 input batches (so the routing changes from pass to
+pass), each step bracketed by its own events; the same is also reported with
+the Infinity Cache emptied before every pass, and for the same input
+replayed back to back.
+
+The default run also measures, under "configs", the other configurations of
+the workload set, each with its own roofline and oracle baseline: one
+full-size layer at T = 1 (Infinity Cache emptied before each forward), the
+48-layer 3-bit stack at T = 8 and T = 1, and one layer over an 8192-token
+prefill chunk.  --workload picks a single one.
 
 Prints one JSON line: tokens/s, plus achieved HBM bandwidth from the
 algorithmic bytes of the actual routing, the roofline of the dominant kernel
@@ -36,6 +42,25 @@ MFMA_F16_PEAK_TFLOPS = 2500.0
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def host_cpu():
+    """The host CPU the oracle baseline runs on: model name and the number of
+    logical CPUs this process may use (the oracle itself uses one thread)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 0
+    return {"host_cpu": model, "host_nproc": n, "threads_used": 1}
 
 
 def algorithmic_bytes_decode(wl, idx_layers: np.ndarray, T: int):
@@ -181,8 +206,7 @@ def bench_prefill(args):
         kdur[name] = (tot / n) * 1e-3
 
     if args.timing_only:
-        print(json.dumps({"timing_only": wl.name, "kernels_avg_us": {n: kdur[n] * 1e6 for n in kdur}}))
-        return
+        return {"timing_only": wl.name, "kernels_avg_us": {n: kdur[n] * 1e6 for n in kdur}}
 
     graph = None
     if not args.no_graph:
@@ -240,7 +264,7 @@ def bench_prefill(args):
     if args.cpu_tokens > 0:
         log(f"timing the CPU oracle on {args.cpu_tokens} tokens ...")
         tps, tsec = cpu_baseline_prefill(wl, x_np, args.cpu_tokens)
-        cpu = {"value": tps, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        cpu = {"value": tps, "unit": "tokens/s", "cores": 1, "kind": "oracle", **host_cpu(),
                "sample": f"first {args.cpu_tokens} of {T} tokens of the chunk ({tsec:.1f} s: router, top-k, "
                          f"layer), single thread; expert generation untimed"}
     out = {
@@ -272,7 +296,7 @@ def bench_prefill(args):
         "kernels": kernels,
         "cpu_baseline": cpu,
     }
-    print(json.dumps(out))
+    return out
 
 
 def bench_stack_prefill(args):
@@ -356,7 +380,7 @@ def bench_stack_prefill(args):
         n_tok, n_l = min(args.cpu_tokens, 16), min(args.cpu_layers, 2, wl.layers)  # (a few seconds)
         log(f"timing the CPU oracle on {n_tok} tokens through {n_l} layers ...")
         tps, per_layer = cpu_baseline_stack(wl, n_tok, mi.activations(wl, T=T, stream=1)[:n_tok], n_l)
-        cpu = {"value": tps, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        cpu = {"value": tps, "unit": "tokens/s", "cores": 1, "kind": "oracle", **host_cpu(),
                "sample": f"first {n_tok} of {T} tokens through the first {n_l} of {wl.layers} layers "
                          f"({per_layer:.2f} s/layer), scaled to the full stack; single thread; expert generation untimed"}
     out = {
@@ -387,7 +411,7 @@ def bench_stack_prefill(args):
         "kernels": kernels,
         "cpu_baseline": cpu,
     }
-    print(json.dumps(out))
+    return out
 
 
 def bench_layer_t1(args):
@@ -453,7 +477,7 @@ def bench_layer_t1(args):
     if args.cpu_layers > 0:
         rows = np.concatenate([mi.activations(wl, T=1, stream=500 + i) for i in range(ring)], axis=0)
         tps, per_layer = cpu_baseline_stack(wl, ring, rows, 1)
-        cpu = {"value": tps, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        cpu = {"value": tps, "unit": "tokens/s", "cores": 1, "kind": "oracle", **host_cpu(),
                "sample": f"the layer on the {ring} rows of the ring ({per_layer:.2f} s), single thread; "
                          f"expert generation untimed"}
     out = {
@@ -480,7 +504,7 @@ def bench_layer_t1(args):
         "kernels": kernels,
         "cpu_baseline": cpu,
     }
-    print(json.dumps(out))
+    return out
 
 
 def copy_calibration(n_mib: int, reps: int):
@@ -501,67 +525,30 @@ def copy_calibration(n_mib: int, reps: int):
     print(json.dumps({"copy_calibration": {"bytes_read": n * 4, "bytes_written": n * 4, "launches": reps}}))
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="stack_t8_2bit",
-                    choices=["stack_t8_2bit", "stack_3bit", "prefill", "layer_t1", "stack_prefill"])
-    ap.add_argument("--T", type=int, default=None, help="tokens per pass (default: the workload's)")
-    ap.add_argument("--layers", type=int, default=None, help="override the number of layers (testing only)")
-    ap.add_argument("--no-graph", action="store_true")
-    ap.add_argument("--f16act", action="store_true",
-                    help="stacks: the fp16-activation decode entry point (up to 16 tokens per pass)")
-    ap.add_argument("--cpu-layers", type=int, default=12,
-                    help="oracle sample size in layers (0 = skip; about 10 s of CPU time at T = 8)")
-    ap.add_argument("--cpu-tokens", type=int, default=96,
-                    help="prefill: oracle sample size in tokens (0 = skip; about 10 s of CPU time)")
-    ap.add_argument("--timing-only", action="store_true",
-                    help="only the per-kernel timing passes (every launch serialized), for profiler runs")
-    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
-                    help="only run a plain device copy of MIB MiB (counter calibration) and exit")
-    args = ap.parse_args()
+def build_stack(wl):
+    """Generate and pack every layer of a stack on the GPU (untimed)."""
+    import torch
 
-    if args.copy_calib:
-        copy_calibration(args.copy_calib, 5)
-        return
+    from moe_inputs.device import packed_layer
 
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no multi-GPU path. "
-              "Run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
+    t0 = time.time()
+    layers = [packed_layer(wl, l, "cuda") for l in range(wl.layers)]
+    torch.cuda.synchronize()
+    log(f"built {wl.layers} packed layers of {wl.name} in {time.time() - t0:.1f}s "
+        f"({sum(L.buffer.numel() for L in layers) / 1e9:.2f} GB resident)")
+    return layers
 
-    if args.workload == "prefill":
-        bench_prefill(args)
-        return
-    if args.workload == "layer_t1":
-        bench_layer_t1(args)
-        return
-    if args.workload == "stack_prefill":
-        bench_stack_prefill(args)
-        return
 
+def bench_stack(args, wl, T, layers):
+    """The stack over T tokens per pass: one step = one pass of every layer
+    over one batch of T synthetic tokens, replayed from a HIP graph."""
     import torch
 
     import bit_quantized_experts_amd as bqe
     import moe_inputs as mi
-    from moe_inputs.device import activations_device, packed_layer
+    from moe_inputs.device import activations_device
 
-    wl = mi.WORKLOADS[args.workload]
-    if args.layers:
-        wl = mi.small(wl, layers=args.layers)
-    T = args.T or wl.T
     dev = "cuda"
-    torch.cuda.set_device(0)
-
-    t0 = time.time()
-    layers = []
-    for l in range(wl.layers):
-        layers.append(packed_layer(wl, l, dev))
-    torch.cuda.synchronize()
-    log(f"built {wl.layers} packed layers in {time.time() - t0:.1f}s "
-        f"({sum(L.buffer.numel() for L in layers) / 1e9:.2f} GB resident)")
 
     # a ring of input batches: consecutive passes route differently, as in
     # decoding, instead of re-reading the same experts every pass
@@ -609,8 +596,7 @@ def main():
         kdur[name] = (tot / n) * 1e-3  # seconds per launch
 
     if args.timing_only:
-        print(json.dumps({"timing_only": wl.name, "kernels_avg_us": {n: kdur[n] * 1e6 for n in kdur}}))
-        return
+        return {"timing_only": wl.name, "T": T, "kernels_avg_us": {n: kdur[n] * 1e6 for n in kdur}}
 
     graph = None
     if not args.no_graph:
@@ -689,7 +675,7 @@ def main():
     if args.cpu_layers > 0:
         log(f"timing the CPU oracle on {args.cpu_layers} layers ...")
         tps, per_layer = cpu_baseline_stack(wl, T, x_np, args.cpu_layers)
-        cpu = {"value": tps, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        cpu = {"value": tps, "unit": "tokens/s", "cores": 1, "kind": "oracle", **host_cpu(),
                "sample": f"first {args.cpu_layers} of {wl.layers} layers at T={T}, "
                          f"{per_layer:.2f} s/layer, scaled to the full stack; expert generation untimed"}
 
@@ -726,6 +712,90 @@ def main():
         "kernels": kernels,
         "cpu_baseline": cpu,
     }
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="all",
+                    choices=["all", "stack_t8_2bit", "stack_3bit", "prefill", "layer_t1", "stack_prefill"],
+                    help="all (default): the 2-bit stack at T = 8 as the value, with the one-layer T = 1 "
+                         "decode, the 3-bit stack at T = 8 and T = 1 and the 8192-token prefill under configs")
+    ap.add_argument("--T", type=int, default=None, help="tokens per pass (default: the workload's)")
+    ap.add_argument("--layers", type=int, default=None, help="override the number of layers (testing only)")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--f16act", action="store_true",
+                    help="stacks: the fp16-activation decode entry point (up to 16 tokens per pass)")
+    ap.add_argument("--cpu-layers", type=int, default=12,
+                    help="oracle sample size in layers (0 = skip; about 10 s of CPU time at T = 8)")
+    ap.add_argument("--cpu-tokens", type=int, default=96,
+                    help="prefill: oracle sample size in tokens (0 = skip; about 10 s of CPU time)")
+    ap.add_argument("--timing-only", action="store_true",
+                    help="only the per-kernel timing passes (every launch serialized), for profiler runs")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration) and exit")
+    args = ap.parse_args()
+
+    if args.copy_calib:
+        copy_calibration(args.copy_calib, 5)
+        return
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no multi-GPU path. "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    if args.workload == "prefill":
+        print(json.dumps(bench_prefill(args)))
+        return
+    if args.workload == "layer_t1":
+        print(json.dumps(bench_layer_t1(args)))
+        return
+    if args.workload == "stack_prefill":
+        print(json.dumps(bench_stack_prefill(args)))
+        return
+
+    import torch
+
+    import moe_inputs as mi
+
+    torch.cuda.set_device(0)
+    if args.workload != "all":
+        wl = mi.WORKLOADS[args.workload]
+        if args.layers:
+            wl = mi.small(wl, layers=args.layers)
+        print(json.dumps(bench_stack(args, wl, args.T or wl.T, build_stack(wl))))
+        return
+
+    # Default: the headline configuration (the 48-layer 2-bit stack at T = 8)
+    # is the line's value; the other configurations of the workload set are
+    # measured in the same run and reported under "configs", each with its
+    # own roofline and oracle baseline.
+    wl = mi.WORKLOADS["stack_t8_2bit"]
+    layers = build_stack(wl)
+    out = bench_stack(args, wl, wl.T, layers)
+    del layers
+    torch.cuda.empty_cache()
+    if args.timing_only:
+        print(json.dumps(out))
+        return
+    configs = {}
+    log("layer_t1 ...")
+    configs["layer_t1"] = bench_layer_t1(args)
+    torch.cuda.empty_cache()
+    wl3 = mi.WORKLOADS["stack_3bit"]
+    layers = build_stack(wl3)
+    for T in (wl3.T,) + tuple(wl3.extra_T):
+        log(f"stack_3bit T={T} ...")
+        configs[f"stack_3bit_T{T}"] = bench_stack(args, wl3, T, layers)
+    del layers
+    torch.cuda.empty_cache()
+    log("prefill ...")
+    configs["prefill_T8192"] = bench_prefill(args)
+    out["configs"] = configs
     print(json.dumps(out))
 
 

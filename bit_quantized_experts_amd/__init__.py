@@ -26,7 +26,7 @@ EXPORTED = ("moe_last_error", "moe_packed_bytes", "moe_pack_experts", "moe_layer
             "moe_route_topk", "moe_workspace_bytes", "moe_workspace_init", "moe_layer_forward",
             "moe_stack_forward", "moe_rmsnorm", "moe_debug_unpack", "moe_timing_start", "moe_timing_stop",
             "moe_group_workspace_bytes", "moe_group_tokens", "moe_layer_forward_f16act",
-            "moe_stack_forward_f16act")
+            "moe_stack_forward_f16act", "moe_debug_unpack_path")
 
 
 class MoeError(RuntimeError):
@@ -72,6 +72,7 @@ def lib() -> ctypes.CDLL:
         L.moe_stack_forward_f16act.argtypes = [P, I, P, I, ctypes.c_float, P, P, P, P, P, S, P]
         L.moe_rmsnorm.argtypes = [P, I, I, ctypes.c_float, P, P]
         L.moe_debug_unpack.argtypes = [P, I, I, P, P, P, P]
+        L.moe_debug_unpack_path.argtypes = [P, I, I, I, P, P, P, P]
         L.moe_timing_start.argtypes = [I, I]
         L.moe_timing_stop.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
         L.moe_group_workspace_bytes.argtypes = [I, I, I, ctypes.POINTER(S)]
@@ -207,6 +208,12 @@ def moe_rmsnorm(x, y, eps: float = 1e-6, stream=None):
 def moe_debug_unpack(handle: int, expert: int, mat: int, codes=None, w_f32=None, w_f16=None, stream=None):
     _check(lib().moe_debug_unpack(handle, expert, mat, _ptr(codes), _ptr(w_f32), _ptr(w_f16), _stream(stream)),
            "moe_debug_unpack")
+
+
+def moe_debug_unpack_path(handle: int, expert: int, mat: int, path: int, codes=None, w_f32=None, w_f16=None,
+                          stream=None):
+    _check(lib().moe_debug_unpack_path(handle, expert, mat, path, _ptr(codes), _ptr(w_f32), _ptr(w_f16),
+                                       _stream(stream)), "moe_debug_unpack_path")
 
 
 def moe_timing_start(kernel_class: int, max_launches: int):

@@ -549,6 +549,41 @@ __global__ __launch_bounds__(512) void down_decode_kernel(DownArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Test export of one packed matrix through this file's own decoders: one
+// wavefront per chunk loads it with load_chunk and, for each of its 8
+// fragments, takes the unsigned codes from chunk_frag (the matrix-core B
+// operand) and the block scale from chunk_scale (the epilogue factor).  Lane
+// l = n + 16 q writes row 16 (RT rg + t) + n, inputs 32 (BK kg + j) + 8 q + c
+// of fragment f = BK t + j: code q_c - 2^(b-1) and scale times code (exact in
+// fp32).
+// ---------------------------------------------------------------------------
+template <int BITS>
+__global__ __launch_bounds__(256) void debug_decode_path_kernel(DebugPathArgs a) {
+  const int chunk = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (chunk >= a.n_rg * a.n_kg) return;
+  const int rg = chunk / a.n_kg, kg = chunk - rg * a.n_kg;
+  const int n = lane & 15, q = lane >> 4;
+  ChunkRegs<BITS> c;
+  load_chunk<BITS>(c, a.mat + (int64_t)chunk * a.chunk_bytes, lane);
+  const int off = 1 << (BITS - 1);
+#pragma unroll
+  for (int f = 0; f < 8; ++f) {
+    const int t = f / a.BK, j = f - t * a.BK;
+    const int row = (rg * a.RT + t) * 16 + n;
+    const int col = 32 * (kg * a.BK + j) + 8 * q;
+    const half8_t qv = chunk_frag<BITS>(c, f);
+    const float s = chunk_scale(c.scales, f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int code = (int)(float)qv[e] - off;
+      const size_t o = (size_t)row * a.cols + col + e;
+      if (a.codes) a.codes[o] = (int8_t)code;
+      if (a.w32) a.w32[o] = s * (float)code;
+    }
+  }
+}
+
 template <int BITS, int RT>
 hipError_t launch_down_t(const DownArgs& a, int grid_x, int nw, hipStream_t s) {
   MOE_LAUNCH((down_decode_kernel<BITS, RT>), dim3(grid_x, a.S), dim3(64 * nw), 0, s, a);
@@ -572,6 +607,14 @@ hipError_t launch_gu_decode(const GuArgs& a, int n_wg, hipStream_t s) {
     else GU_LAUNCH(3, 64);
   }
 #undef GU_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_decode_path(const DebugPathArgs& a, int bits, hipStream_t s) {
+  const int n = a.n_rg * a.n_kg;
+  if (n == 0) return hipSuccess;
+  if (bits == 2) hipLaunchKernelGGL(debug_decode_path_kernel<2>, dim3((n + 3) / 4), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(debug_decode_path_kernel<3>, dim3((n + 3) / 4), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -172,7 +172,6 @@ int down_splits(const moe_layer* L, int max_slots) {
 // else 8).
 WsLayout ws_layout_decode(const moe_layer* L, int T, bool act16 = false) {
   WsLayout W{};
-  const int R = act16 ? MOE_MAX_TOK_F16ACT : MOE_MAX_TOK_DECODE;
   const int k = L->k, E = L->E, d = L->d;
   W.max_slots = (T * k < E ? T * k : E) + (L->Is > 0 ? 1 : 0);
   W.nbI = (L->I > L->Is ? L->I : L->Is) / 32;
@@ -181,6 +180,11 @@ WsLayout ws_layout_decode(const moe_layer* L, int T, bool act16 = false) {
   int64_t o = 0;
   auto take = [&](int64_t bytes) { int64_t r = o; o += moe_align256(bytes); return r; };
   W.ctrl = take(ctrl_bytes());
+  // The down partials come right after the control words, sized for the
+  // most splits and rows whatever the layer's shapes: in a stack, layer l+1
+  // reads layer l's partials while it writes the rest of this layout for its
+  // own shapes, so their place must not depend on E, k or the expert sizes.
+  W.ypart = take((int64_t)MOE_MAX_IN_SPLITS * MOE_MAX_TOK_F16ACT * d * 4);
   W.lp = take((int64_t)W.n_cs * T * E * 4);
   W.ss_part = take((int64_t)((E + MOE_ROUTE_ROWS - 1) / MOE_ROUTE_ROWS) * W.n_cs * T * 4);
   W.rnorm = take(16 * 4);
@@ -192,7 +196,6 @@ WsLayout ws_layout_decode(const moe_layer* L, int T, bool act16 = false) {
   W.xsum = take((int64_t)(d / 32) * 16 * 4);
   W.hfrag = take((int64_t)W.max_slots * W.nbI * 64 * 8 * 2);
   W.hsum = take((int64_t)W.max_slots * W.nbI * 2 * 16 * 4);
-  W.ypart = take((int64_t)W.S * R * d * 4);
   W.total = o;
   return W;
 }
@@ -959,6 +962,38 @@ int moe_debug_unpack(const moe_layer* L, int expert, int mat, int8_t* codes, flo
   const moe_mat_layout& M = mat == 0 ? X.gate : mat == 1 ? X.up : X.down;
   const int64_t off = mat == 0 ? X.off_gate : mat == 1 ? X.off_up : X.off_down;
   HIPCHK(launch_debug_unpack(base + off, M, L->bits, codes, w_f32, w_f16, reinterpret_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
+int moe_debug_unpack_path(const moe_layer* L, int expert, int mat, int path, int8_t* codes, float* w_f32,
+                          uint16_t* w_f16, void* stream) {
+  if (!L) return fail(MOE_ERR_ARG, "layer is NULL");
+  if (expert < -1 || expert >= L->E) return fail(MOE_ERR_ARG, "expert out of range");
+  if (expert == -1 && L->Is == 0) return fail(MOE_ERR_ARG, "layer has no shared expert");
+  if (mat < 0 || mat > 2) return fail(MOE_ERR_ARG, "mat must be 0, 1 or 2");
+  if (path < 0 || path > 2) return fail(MOE_ERR_ARG, "path must be 0, 1 or 2");
+  if (path == 0 && w_f16) return fail(MOE_ERR_ARG, "path 0 exports codes and w_f32 only");
+  if (path > 0 && (codes || w_f32)) return fail(MOE_ERR_ARG, "paths 1 and 2 export w_f16 only");
+  if (!codes && !w_f32 && !w_f16) return MOE_OK;
+  const moe_expert_layout& X = expert < 0 ? L->sh : L->ex;
+  const uint8_t* base = expert < 0 ? L->shared : L->experts + (int64_t)expert * L->ex.bytes;
+  const moe_mat_layout& M = mat == 0 ? X.gate : mat == 1 ? X.up : X.down;
+  const int64_t off = mat == 0 ? X.off_gate : mat == 1 ? X.off_up : X.off_down;
+  DebugPathArgs a{};
+  a.mat = base + off;
+  a.cols = M.cols;
+  a.BK = M.BK;
+  a.RT = M.RT;
+  a.n_rg = M.n_rg;
+  a.n_kg = M.n_kg;
+  a.chunk_bytes = M.chunk_bytes;
+  a.full = path == 2;
+  a.codes = codes;
+  a.w32 = w_f32;
+  a.w16 = w_f16;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (path == 0) HIPCHK(launch_debug_decode_path(a, L->bits, s));
+  else HIPCHK(launch_debug_prefill_path(a, L->bits, s));
   return MOE_OK;
 }
 

@@ -100,6 +100,18 @@ hipError_t launch_pack_matrix(const uint8_t* canon, int64_t canon_stride, uint8_
 hipError_t launch_debug_unpack(const uint8_t* mat, const moe_mat_layout& L, int bits, int8_t* codes, float* w32,
                                uint16_t* w16, hipStream_t s);
 
+// Test export of one packed matrix through an expert kernel's own decoder.
+struct DebugPathArgs {
+  const uint8_t* mat;  // packed matrix
+  int32_t cols, BK, RT, n_rg, n_kg, chunk_bytes;
+  int32_t full;        // prefill: 1 = whole chunks (load_full), 0 = half chunks (load_half)
+  int8_t* codes;       // decode: signed codes [rows][cols], or null
+  float* w32;          // decode: scale * code [rows][cols], or null
+  uint16_t* w16;       // prefill: fp16 bits of the dequantized weight [rows][cols]
+};
+hipError_t launch_debug_decode_path(const DebugPathArgs& a, int bits, hipStream_t s);
+hipError_t launch_debug_prefill_path(const DebugPathArgs& a, int bits, hipStream_t s);
+
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 hipError_t launch_gu_decode(const GuArgs& a, int n_wg, hipStream_t s);
 hipError_t launch_down_decode(const DownArgs& a, int grid_x, int nw, hipStream_t s);

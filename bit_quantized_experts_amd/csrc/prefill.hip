@@ -946,7 +946,52 @@ __global__ __launch_bounds__(256) void pf_combine_kernel(PfCombineArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Test export of one packed matrix through the grouped GEMMs' own register
+// dequantization: one wavefront per chunk, loaded as two half chunks
+// (load_half, as the gate/up kernel and the down kernel with 8 or 1 blocks
+// per chunk do) or as one full chunk (load_full, as the down kernel with 4
+// or 2 blocks per chunk does), each fragment through dequant.  Lane
+// l = n + 16 q writes the fp16 bits of row 16 (RT rg + t) + n, inputs
+// 32 (BK kg + j) + 8 q + c of fragment f = BK t + j.
+// ---------------------------------------------------------------------------
+template <int BITS>
+__global__ __launch_bounds__(256) void debug_prefill_path_kernel(DebugPathArgs a) {
+  const int chunk = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (chunk >= a.n_rg * a.n_kg) return;
+  const int rg = chunk / a.n_kg, kg = chunk - rg * a.n_kg;
+  const int n = lane & 15, q = lane >> 4;
+  const uint8_t* ch = a.mat + (int64_t)chunk * a.chunk_bytes;
+  auto put = [&](int f, const half8_t& w) {
+    const int t = f / a.BK, j = f - t * a.BK;
+    const size_t o = (size_t)((rg * a.RT + t) * 16 + n) * a.cols + 32 * (kg * a.BK + j) + 8 * q;
+    *reinterpret_cast<half8_t*>(a.w16 + o) = w;  // (o is a multiple of 8: 16-byte aligned)
+  };
+  if (a.full) {
+    WRegs w;
+    load_full<BITS>(w, ch, lane);
+#pragma unroll
+    for (int f = 0; f < 8; ++f) put(f, dequant<BITS>(w, f));
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      WRegs w;
+      load_half<BITS>(w, ch, h, lane);
+#pragma unroll
+      for (int f = 0; f < 4; ++f) put(4 * h + f, dequant<BITS>(w, f));
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_debug_prefill_path(const DebugPathArgs& a, int bits, hipStream_t s) {
+  const int n = a.n_rg * a.n_kg;
+  if (n == 0) return hipSuccess;
+  if (bits == 2) hipLaunchKernelGGL(debug_prefill_path_kernel<2>, dim3((n + 3) / 4), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(debug_prefill_path_kernel<3>, dim3((n + 3) / 4), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_pack_router(const float* W, int E, int d, _Float16* wh, _Float16* wl, int32_t* ew, hipStream_t s) {
   const int E16 = (E + 15) / 16 * 16;

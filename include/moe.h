@@ -231,6 +231,23 @@ int moe_rmsnorm(const float *x, int T, int d, float eps, float *y, void *stream)
 int moe_debug_unpack(const moe_layer *layer, int expert, int mat, int8_t *codes, float *w_f32,
                      uint16_t *w_f16, void *stream);
 
+/* Test export of the same matrix through the decoders the expert kernels run
+ * (moe_debug_unpack above has a decoder of its own), so that the weights the
+ * multiplications actually see can be compared bit for bit:
+ *   path 0  the decode kernels' fragment decode: codes come out of the packed
+ *           chunk as exact fp16 integers (the matrix-core B operand) and the
+ *           fp16 block scale as the epilogue factor; exports codes (int8,
+ *           q - 2^(b-1)) and/or w_f32 = scale * code; w_f16 must be NULL;
+ *   path 1  the grouped GEMMs' register dequantization from half chunks (the
+ *           gate/up kernel's loads): exports w_f16, the fp16 bits of
+ *           scale * code rounded once to nearest even; codes and w_f32 must
+ *           be NULL;
+ *   path 2  the same dequantization from whole chunks (the down kernel's
+ *           loads when a chunk holds 4 or 2 blocks of a row).
+ * Layouts and errors as moe_debug_unpack; a bad path is MOE_ERR_ARG. */
+int moe_debug_unpack_path(const moe_layer *layer, int expert, int mat, int path, int8_t *codes, float *w_f32,
+                          uint16_t *w_f16, void *stream);
+
 /* Tuning overrides read from the environment at each call (set them before
  * the first call and leave them unchanged: the split count also sets the
  * workspace layout, so moe_workspace_bytes and the forward calls must see

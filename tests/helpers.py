@@ -34,3 +34,19 @@ def oracle_layer(wl: mi.Workload, layer: int, experts) -> oracle.Layer:
 
 # layer-output tolerance: global infinity-norm relative error max|y - ref| / max|ref|
 TOL_LAYER = 2e-3
+
+# Regression envelope of the decode path with fp16 hi + lo activations (not
+# the tolerance of the method, which is TOL_LAYER): its products are exact and
+# its roundings are fp32 accumulation and the ~22-bit activation split, so
+# observed errors are 2e-7 (median) to 5e-6 (largest); a single wrongly
+# decoded weight or a dropped block would exceed this long before TOL_LAYER.
+TOL_DECODE_PATH = 1e-5
+
+
+def row_rel_err(y, ref) -> float:
+    """Largest per-row relative error max_t ||y_t - ref_t|| / ||ref_t|| (2-norms)."""
+    y = np.asarray(y, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    num = np.linalg.norm(y - ref, axis=-1)
+    den = np.linalg.norm(ref, axis=-1)
+    return float(np.max(num / np.where(den > 0, den, 1.0)))

@@ -12,7 +12,7 @@ import torch
 import moe_inputs as mi
 import oracle
 from moe_inputs.device import packed_layer, activations_device
-from tests.helpers import TOL_LAYER, oracle_layer, rel_err_inf, say
+from tests.helpers import TOL_DECODE_PATH, TOL_LAYER, oracle_layer, rel_err_inf, row_rel_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -56,8 +56,10 @@ def _check_layer(wl, layer, L, x_np, bqe, tag):
     OL = oracle_layer(wl, layer, idx.reshape(-1))
     oy, _, _, _ = oracle.layer_forward(OL, x_np, force_idx=idx, force_w=w)
     err = rel_err_inf(y, oy)
-    say(f"    rel err {err:.3e}")
+    rerr = row_rel_err(y, oy)
+    say(f"    rel err {err:.3e} (largest per-row {rerr:.3e})")
     assert err <= TOL_LAYER, (tag, err)
+    assert err <= TOL_DECODE_PATH and rerr <= TOL_DECODE_PATH, (tag, err, rerr)
     assert np.all(np.isfinite(y))
     return y, idx, w, err
 
@@ -97,6 +99,43 @@ def test_debug_unpack_bitexact(bqe, bits, shape):
             assert np.array_equal(w32.cpu().numpy().astype(np.float64), ow), (e, mat)
             o16 = oracle.double_to_half_array(ow)
             assert np.array_equal(w16.cpu().numpy().view(np.uint16), o16), (e, mat)
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+@pytest.mark.parametrize("shape", ["tiny", "full"])
+def test_debug_unpack_path_bitexact(bqe, bits, shape):
+    """The weights as the expert kernels' own decoders see them: the decode
+    kernels' fragment decode (codes and fp32 scale x code) and the grouped
+    GEMMs' fp16 register dequantization from half and whole chunks, bit for
+    bit against the oracle's unpack and dequant."""
+    if shape == "tiny":
+        wl = mi.small(mi.WORKLOADS["tiny"], bits=bits, Is=96)
+        experts = list(range(wl.E)) + [-1]
+    else:
+        base = mi.WORKLOADS["layer_t1"] if bits == 2 else mi.WORKLOADS["stack_3bit"]
+        wl = mi.small(base, E=12, layers=1)
+        experts = [0, 7, 11, -1]
+    say(f"[unpack path] {shape} bits={bits}")
+    L = packed_layer(wl, 0)
+    for e in experts:
+        canon = mi.expert_canon(wl, 0, e).numpy()
+        I = wl.Is if e < 0 else wl.I
+        parts = oracle.split_expert(canon, wl.d, I, bits)
+        for mat, (rows, cols) in enumerate(((I, wl.d), (I, wl.d), (wl.d, I))):
+            oc, _ = oracle.unpack_matrix(parts[mat], rows, cols, bits)
+            ow = oracle.dequant_matrix(parts[mat], rows, cols, bits)
+            o16 = oracle.double_to_half_array(ow)
+            codes = torch.full((rows, cols), 99, dtype=torch.int8, device=DEV)
+            w32 = torch.full((rows, cols), float("nan"), dtype=torch.float32, device=DEV)
+            bqe.moe_debug_unpack_path(L.handle, e, mat, 0, codes, w32, None)
+            torch.cuda.synchronize()
+            assert np.array_equal(codes.cpu().numpy(), oc), (e, mat, "decode codes")
+            assert np.array_equal(w32.cpu().numpy().astype(np.float64), ow), (e, mat, "decode weights")
+            for path in (1, 2):
+                w16 = torch.full((rows, cols), -1, dtype=torch.int16, device=DEV)
+                bqe.moe_debug_unpack_path(L.handle, e, mat, path, None, None, w16)
+                torch.cuda.synchronize()
+                assert np.array_equal(w16.cpu().numpy().view(np.uint16), o16), (e, mat, path)
 
 
 @pytest.mark.parametrize("E,k,T", [(16, 2, 5), (512, 10, 64), (512, 16, 33), (4096, 8, 9), (3, 3, 7), (1, 1, 4),
@@ -271,14 +310,18 @@ def test_unused_experts_do_not_change_output(bqe):
     assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
 
 
-@pytest.mark.parametrize("which", ["tiny", "full"])
+@pytest.mark.parametrize("which", ["tiny", "full", "full_3bit_T8", "full_3bit_T1"])
 def test_stack_teacher_forced(bqe, which):
     if which == "tiny":
         wl = mi.small(mi.WORKLOADS["tiny"], Is=64, zipf_s=1.1, layers=5)
         T = 7
-    else:
+    elif which == "full":
         wl = mi.small(mi.WORKLOADS["stack_t8_2bit"], layers=3)
         T = 8
+    else:
+        # the first layers of the 3-bit stack, at both of its decode sizes
+        wl = mi.small(mi.WORKLOADS["stack_3bit"], layers=3)
+        T = 8 if which.endswith("T8") else 1
     layers = [packed_layer(wl, l) for l in range(wl.layers)]
     x_np = mi.activations(wl, T=T, stream=5)
     nL, d, k = wl.layers, wl.d, wl.k
@@ -300,8 +343,42 @@ def test_stack_teacher_forced(bqe, which):
         OL = oracle_layer(wl, l, il[l].reshape(-1))
         oy, ologits, _, _ = oracle.layer_forward(OL, h, force_idx=il[l], force_w=wlr[l])
         err = rel_err_inf(yl[l], oy)
-        say(f"    layer {l}: rel err {err:.3e}")
+        rerr = row_rel_err(yl[l], oy)
+        say(f"    layer {l}: rel err {err:.3e} (largest per-row {rerr:.3e})")
         assert err <= TOL_LAYER, (l, err)
+
+
+def test_stack_mixed_layer_shapes(bqe):
+    """Consecutive stacked layers with different expert counts and expert
+    sizes (same d and k): each layer's workspace layout differs, and every
+    layer must still read its input from the previous layer's output."""
+    wls = [mi.small(mi.WORKLOADS["tiny"], E=16, k=4, I=64, Is=0, zipf_s=None, layers=4),
+           mi.small(mi.WORKLOADS["tiny"], E=512, k=4, I=96, Is=64, zipf_s=1.1, layers=4),
+           mi.small(mi.WORKLOADS["tiny"], E=40, k=4, I=32, Is=160, zipf_s=None, layers=4),
+           mi.small(mi.WORKLOADS["tiny"], E=16, k=4, I=64, Is=0, zipf_s=None, layers=4)]
+    layers = [packed_layer(wl, l) for l, wl in enumerate(wls)]
+    T, d, k, nL = 8, wls[0].d, 4, len(wls)
+    x_np = mi.activations(wls[0], T=T, stream=44)
+    x = activations_device(x_np)
+    y = torch.empty((T, d), dtype=torch.float32, device=DEV)
+    yl = torch.empty((nL, T, d), dtype=torch.float32, device=DEV)
+    il = torch.empty((nL, T, k), dtype=torch.int32, device=DEV)
+    wlr = torch.empty((nL, T, k), dtype=torch.float32, device=DEV)
+    ws = bqe.new_workspace(max(L.workspace_bytes(T) for L in layers))
+    say(f"[stack] mixed shapes: E={[w.E for w in wls]} I={[w.I for w in wls]} Is={[w.Is for w in wls]} T={T}")
+    bqe.moe_stack_forward([L.handle for L in layers], x, y, ws, 1e-6, yl, il, wlr)
+    torch.cuda.synchronize()
+    yl, il, wlr = yl.cpu().numpy(), il.cpu().numpy(), wlr.cpu().numpy()
+    assert np.array_equal(y.cpu().numpy(), yl[-1])
+    h = x_np
+    for l, wl in enumerate(wls):
+        if l > 0:
+            h = oracle.rmsnorm(yl[l - 1], 1e-6)
+        OL = oracle_layer(wl, l, il[l].reshape(-1))
+        oy, _, _, _ = oracle.layer_forward(OL, h, force_idx=il[l], force_w=wlr[l])
+        err = rel_err_inf(yl[l], oy)
+        say(f"    layer {l}: rel err {err:.3e}")
+        assert err <= TOL_DECODE_PATH, (l, err)
 
 
 def test_stack_chunks_of_eight(bqe):

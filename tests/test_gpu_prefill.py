@@ -14,7 +14,7 @@ import torch
 import moe_inputs as mi
 import oracle
 from moe_inputs.device import packed_layer, activations_device
-from tests.helpers import TOL_LAYER, oracle_layer, rel_err_inf, say
+from tests.helpers import TOL_LAYER, oracle_layer, rel_err_inf, row_rel_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -139,16 +139,46 @@ def test_prefill_full_size_mid_T(bqe, bits):
 
 
 def test_prefill_full_size_8192(bqe):
+    """The full 8192-token chunk: routing bit-exact on every token, logits of
+    every 32nd token against the fp64 router, and the outputs of every token
+    in the work items most likely to hide a fault, against the oracle: the
+    busiest expert's first and last 128-row items (the last one partial, so
+    its last 16-row subtile is partly padding) and the last item of shared
+    rows.  The grouped GEMMs take an expert's (token, slot) pairs in token
+    order, 128 rows per item, and the shared expert's rows one per token."""
     wl = mi.WORKLOADS["prefill"]
     L = packed_layer(wl, 0)
     T = wl.T
     x = mi.activations(wl, T=T, stream=0)
-    sample = np.array([0, 1, 2, 1000, 4095, 4096, 6000, 8190, 8191])
-    y, idx, w = _check(bqe, wl, L, x, "prefill 8192", sample=sample, logit_rows=np.arange(0, T, 32))
+    say(f"[prefill] full 8192: T={T}")
+    y, logits, idx, w = _forward(bqe, L, x)
+    assert np.all(np.isfinite(y))
+    oi, ow = oracle.topk(logits, wl.k)
+    assert np.array_equal(idx, oi)
+    assert np.array_equal(w.view(np.uint32), ow.view(np.uint32))
+    W, b = mi.router(wl, 0)
+    rows = np.arange(0, T, 32)
+    lerr = rel_err_inf(logits[rows], oracle.router_logits(x[rows], W, b))
+    assert lerr < 1e-5, lerr
     # the routing is Zipf-skewed: several thousand tokens on the busiest expert
     counts = np.bincount(idx.reshape(-1), minlength=wl.E)
     say(f"    max tokens per expert {counts.max()}, empty experts {(counts == 0).sum()}")
     assert counts.max() > 2000
+    e1 = int(np.argmax(counts))
+    toks = np.nonzero((idx == e1).any(axis=1))[0]  # ascending: the order of the expert's rows
+    n_items = (len(toks) + 127) // 128
+    first_item, last_item = toks[:128], toks[128 * (n_items - 1):]
+    assert len(last_item) % 16 != 0  # a padded last subtile
+    shared_last = np.arange(128 * ((T - 1) // 128), T)
+    sample = np.unique(np.concatenate([first_item, last_item, shared_last]))
+    say(f"    expert {e1}: {len(toks)} rows in {n_items} items, last item {len(last_item)} rows; "
+        f"checking {len(sample)} tokens")
+    assert len(sample) >= 256
+    OL = oracle_layer(wl, 0, idx[sample].reshape(-1))
+    oy, _, _, _ = oracle.layer_forward(OL, x[sample], force_idx=idx[sample], force_w=w[sample])
+    err = rel_err_inf(y[sample], oy)
+    say(f"    logits rel err {lerr:.3e}, layer rel err {err:.3e} (largest per-row {row_rel_err(y[sample], oy):.3e})")
+    assert err <= TOL_LAYER, err
 
 
 def test_prefill_chunking_invariance(bqe):
