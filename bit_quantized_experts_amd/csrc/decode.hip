@@ -50,15 +50,6 @@ DEVI float chunk_scale(const u32x4_t& s, int f) {
   return half_bits_to_float((f & 1) ? (dw >> 16) : (dw & 0xffffu));
 }
 
-// A-fragment and accumulator seed of block b of the h fragments: the seed is
-// the sum of the two 16-row tile sums the gate/up kernel wrote for the block.
-DEVI void load_a(const _Float16* frag, const float* sum, size_t b, int lane, half8_t& A, float4_t& cin) {
-  A = *reinterpret_cast<const half8_t*>(frag + (b * 64 + lane) * 8);
-  const float4_t c0 = *reinterpret_cast<const float4_t*>(sum + (2 * b) * 16 + 4 * (lane >> 4));
-  const float4_t c1 = *reinterpret_cast<const float4_t*>(sum + (2 * b + 1) * 16 + 4 * (lane >> 4));
-  cin = c0 + c1;
-}
-
 // ---------------------------------------------------------------------------
 // Slot list in LDS: routed experts numbered in ascending id order after the
 // shared expert's slot 0, and every (token, rank) entry's gate weight in its
@@ -152,6 +143,7 @@ struct alignas(16) GuLds {
   alignas(16) float cs[GU_WIN * 16];  // accumulator seeds, [block][16]
   float red[GU_NW][8][64];          // partial sums of the k-parts
   float rn[16];                     // 1 / rms of each token
+  int rx[16];                       // exponent ex of each token's activation scaling
   SlotLds S;
   uint64_t tk_buf[GU_NW][TOPK_BUF];
 };
@@ -161,47 +153,79 @@ struct GroupRegs {
   ChunkRegs<BITS> g, u;
 };
 
-// Activation blocks [b0, b0 + nblk) into LDS (plain loads and LDS stores),
-// in two halves so that other work can run while the loads are in flight.
-// Entry p of a block is lane p % 64 of its A-fragment, which holds token
-// (p % 64) & 7 (fp16 activations: (p % 64) & 15); the rows of tokens >= T are
-// zeros (as the route kernel writes them), so they are stored without being
-// read.
+// Activation blocks [b0, b0 + nblk) of the layer input into LDS as
+// matrix-core A-fragments, with their accumulator seeds.  Thread p takes the
+// entries e = p + 512 i: block b = e / 4R, token row t = (e / 4) % R (the same
+// t for every i), quarter q = e % 4, i.e. inputs 32 (b0 + b) + 8q .. +8 of
+// token t.  They are loaded from xin, and after the selection scaled by 2^-ex
+// of the token (exact: the row's largest magnitude then lies in [2^14, 2^15))
+// and split into an fp16 hi part (A row t) and lo part (row t + 8), or, with
+// fp16 activations (R = 16 tokens), rounded to fp16 (row t).  The four
+// threads of a quad (q = 0..3, one block and token) add up their block sums.
+// Rows of tokens >= T are zeros.
+template <bool A16>
 struct WindowRegs {
-  static constexpr int PER = GU_WIN * 64 / (64 * GU_NW);
-  u32x4_t v[PER];
-  float4_t c;
+  static constexpr int R = A16 ? MOE_MAX_TOK_F16ACT : MOE_MAX_TOK_DECODE;
+  static constexpr int PER = GU_WIN * 4 * R / (64 * GU_NW);
+  float4_t v[PER][2];
+  int ex;  // exponent of this thread's token (the values are scaled by 2^-ex)
 };
 
-DEVI void window_load(WindowRegs& W, const GuArgs& a, int b0, int nblk, int tid) {
-  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.xfrag + (size_t)b0 * 512);
-  const int n = nblk * 64, nc = nblk * 4;
-  const bool live = (tid & (a.act16 ? 15 : 7)) < a.T;  // (64 * GU_NW is a multiple of 64: same lane for every i)
+template <bool A16>
+DEVI void window_load(WindowRegs<A16>& W, const GuArgs& a, int b0, int nblk, int tid) {
+  constexpr int R = WindowRegs<A16>::R;
+  const int t = (tid >> 2) % R, q = tid & 3;
+  const bool live = t < a.T;
+  W.ex = live ? a.xexp[t] : 0;
+  const float* src = a.xin + (size_t)(live ? t : 0) * a.d + 32 * b0 + 8 * q;
 #pragma unroll
-  for (int i = 0; i < WindowRegs::PER; ++i) {
-    const int p = tid + 64 * GU_NW * i;
-    W.v[i] = u32x4_t{0u, 0u, 0u, 0u};
-    if (p < n && live) W.v[i] = src[p];
+  for (int i = 0; i < WindowRegs<A16>::PER; ++i) {
+    const int b = (tid + 64 * GU_NW * i) / (4 * R);
+    W.v[i][0] = W.v[i][1] = float4_t{0.f, 0.f, 0.f, 0.f};
+    if (b < nblk && live) {
+      W.v[i][0] = *reinterpret_cast<const float4_t*>(src + 32 * b);
+      W.v[i][1] = *reinterpret_cast<const float4_t*>(src + 32 * b + 4);
+    }
   }
-  W.c = float4_t{0.f, 0.f, 0.f, 0.f};
-  if (tid < nc) W.c = reinterpret_cast<const float4_t*>(a.xsum + (size_t)b0 * 16)[tid];
 }
 
-DEVI void window_store(const WindowRegs& W, GuLds& L, int nblk, int tid) {
-  u32x4_t* dst = reinterpret_cast<u32x4_t*>(L.xs);
-  const int n = nblk * 64, nc = nblk * 4;
+template <bool A16>
+DEVI void window_store(const WindowRegs<A16>& W, GuLds& L, int nblk, int code_off, int tid) {
+  constexpr int R = WindowRegs<A16>::R;
+  const int t = (tid >> 2) % R, q = tid & 3;
+  const float off = -(float)code_off;
 #pragma unroll
-  for (int i = 0; i < WindowRegs::PER; ++i) {
-    const int p = tid + 64 * GU_NW * i;
-    if (p < n) dst[p] = W.v[i];
+  for (int i = 0; i < WindowRegs<A16>::PER; ++i) {
+    const int b = (tid + 64 * GU_NW * i) / (4 * R);
+    if (b >= nblk) continue;  // (the four threads of a quad share b)
+    half8_t h, l;
+    float sh = 0.f, sl = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float v = ldexpf(W.v[i][c >> 2][c & 3], -W.ex);  // exact (2^-ex itself may exceed the fp32 range)
+      h[c] = (_Float16)v;
+      sh += (float)h[c];
+      if (!A16) {
+        l[c] = (_Float16)(v - (float)h[c]);
+        sl += (float)l[c];
+      }
+    }
+    sh = quad_sum(sh);
+    *reinterpret_cast<half8_t*>(L.xs + ((size_t)b * 64 + t + 16 * q) * 16) = h;
+    if (q == 0) L.cs[b * 16 + t] = off * sh;
+    if (!A16) {
+      sl = quad_sum(sl);
+      *reinterpret_cast<half8_t*>(L.xs + ((size_t)b * 64 + t + 8 + 16 * q) * 16) = l;
+      if (q == 0) L.cs[b * 16 + t + 8] = off * sl;
+    }
   }
-  if (tid < nc) reinterpret_cast<float4_t*>(L.cs)[tid] = W.c;
 }
 
+template <bool A16>
 DEVI void stage_window(GuLds& L, const GuArgs& a, int b0, int nblk, int tid) {
-  WindowRegs W;
-  window_load(W, a, b0, nblk, tid);
-  window_store(W, L, nblk, tid);
+  WindowRegs<A16> W;
+  window_load<A16>(W, a, b0, nblk, tid);
+  window_store<A16>(W, L, nblk, a.code_off, tid);
 }
 
 template <int BITS>
@@ -262,7 +286,7 @@ DEVI void run_tile(const uint8_t* gate, const uint8_t* up, int64_t rowoff, int k
   if (rem == 2) mul_group<BITS>(r1, L, 8 * (kg + step - wkg0), lane, accg, accu);
 }
 
-template <int BITS, int NPER>  // NPER >= ceil(E / 64)
+template <int BITS, int NPER, bool A16>  // NPER >= ceil(E / 64)
 __global__ __launch_bounds__(64 * GU_NW) void gu_decode_kernel(GuArgs a) {
   constexpr int64_t CB = BITS == 2 ? 1280 : 1792;
   __shared__ GuLds L;
@@ -292,12 +316,13 @@ __global__ __launch_bounds__(64 * GU_NW) void gu_decode_kernel(GuArgs a) {
     }
   }
   const float rnv = (tid >= 64 && tid < 64 + T) ? a.rnorm[tid - 64] : 1.0f;
+  const int xev = (tid >= 64 && tid < 64 + T) ? a.xexp[tid - 64] : 0;
   // the activation window (one window for inputs of up to GU_WIN blocks)
   // stays in registers through the selection and is stored to LDS before the
   // barrier that ends it: the selection starts as soon as its logits are in,
   // while the larger window is still arriving
-  WindowRegs win;
-  if (n_win == 1) window_load(win, a, 0, 8 * n_kg, tid);
+  WindowRegs<A16> win;
+  if (n_win == 1) window_load<A16>(win, a, 0, 8 * n_kg, tid);
   clear_slots(L.S, E, T, base + min(tk, E), has_shared);
   lds_barrier();  // byte map and weight rows cleared before any wavefront marks (the loads stay in flight)
   static_assert(2 * GU_NW >= MOE_MAX_TOK_F16ACT, "two tokens per wavefront");
@@ -324,8 +349,11 @@ __global__ __launch_bounds__(64 * GU_NW) void gu_decode_kernel(GuArgs a) {
     }
   }
   __builtin_amdgcn_sched_barrier(0);  // (the window's stores stay after the selection)
-  if (n_win == 1) window_store(win, L, 8 * n_kg, tid);
-  if (tid >= 64 && tid < 80) L.rn[tid - 64] = 1.0f / rnv;
+  if (n_win == 1) window_store<A16>(win, L, 8 * n_kg, a.code_off, tid);
+  if (tid >= 64 && tid < 80) {
+    L.rn[tid - 64] = 1.0f / rnv;
+    L.rx[tid - 64] = xev;
+  }
   lds_barrier();  // every token's experts marked, the window staged
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -381,7 +409,7 @@ __global__ __launch_bounds__(64 * GU_NW) void gu_decode_kernel(GuArgs a) {
       const int kg0 = w * win_kg, kg1 = min(n_kg, kg0 + win_kg);
       if (n_win > 1) {
         __syncthreads();
-        stage_window(L, a, 8 * kg0, 8 * (kg1 - kg0), tid);
+        stage_window<A16>(L, a, 8 * kg0, 8 * (kg1 - kg0), tid);
         __syncthreads();
       }
       if (valid) run_tile<BITS>(gate, up, (int64_t)t * n_kg * CB, kg0 + kp, kg1, KP, kg0, L, lane, accg, accu);
@@ -405,26 +433,30 @@ __global__ __launch_bounds__(64 * GU_NW) void gu_decode_kernel(GuArgs a) {
     if (valid && kp == 0) {
       // lane l: intermediate row n = l & 15 of the tile, C rows 4(l>>4)+i:
       // tokens tok_e + i, hi part in lanes < 32, lo part in lanes >= 32 (fp16
-      // activations: token 4(l>>4)+i, no lo part)
+      // activations: token 4(l>>4)+i, no lo part).  h is kept in fp32 rows
+      // [slot][token][row] with the largest |h| of each (slot, token) (the
+      // down kernel scales by it before rounding to fp16); maxima of
+      // non-negative floats order like their bit patterns.
       const int n = lane & 15;
-      const bool a16 = a.act16 != 0;
-      const bool lo_half = !a16 && lane >= 32;
-      const int pblk = t >> 1, kk = 16 * (t & 1) + n;
+      const bool writer = A16 || lane < 32;
+      constexpr int R = A16 ? MOE_MAX_TOK_F16ACT : MOE_MAX_TOK_DECODE;
+      float* hrow = a.hbuf + (size_t)u * R * a.hI + 16 * t + n;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int tok = a16 ? 4 * (lane >> 4) + i : tok_e + i;
+        const int tok = A16 ? 4 * (lane >> 4) + i : tok_e + i;
         const float gw = (u == 0 && has_shared) ? (tok < T ? 1.0f : 0.f) : L.S.w[u][tok];
-        const float rrn = L.rn[tok];  // 1 / rms
-        const float g = (a16 ? accg[i] : add_partner32(accg[i])) * rrn;
-        const float uu = (a16 ? accu[i] : add_partner32(accu[i])) * rrn;
+        // the norm's 1 / rms, then 2^ex undoes the activations' scaling (exact)
+        const float rrn = L.rn[tok];
+        const int rx = L.rx[tok];
+        const float g = ldexpf((A16 ? accg[i] : add_partner32(accg[i])) * rrn, rx);
+        const float uu = ldexpf((A16 ? accu[i] : add_partner32(accu[i])) * rrn, rx);
         const float hv = g * __builtin_amdgcn_rcpf(1.0f + expf(-g)) * uu;
         const float hs = (gw != 0.f) ? gw * hv : 0.f;
-        const _Float16 hi = (_Float16)hs;
-        const _Float16 val = lo_half ? (_Float16)(hs - (float)hi) : hi;
-        const int mrow = a16 ? tok : tok + (lo_half ? 8 : 0);
-        a.hfrag[(((size_t)u * a.nbI + pblk) * 64 + mrow + 16 * (kk >> 3)) * 8 + (kk & 7)] = val;
-        const float sm = row16_sum((float)val);
-        if (n == 0) a.hsum[((size_t)u * 2 * a.nbI + t) * 16 + mrow] = -(float)a.code_off * sm;
+        if (writer) hrow[(size_t)tok * a.hI] = hs;
+        const float m = row16_max(fabsf(hs));
+        if (writer && n == 0)
+          __hip_atomic_fetch_max(a.hmax + u * 16 + tok, __float_as_uint(m), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     if (KP > 1) __syncthreads();  // red is rewritten in the next round
@@ -442,11 +474,30 @@ __global__ __launch_bounds__(64 * GU_NW) void gu_decode_kernel(GuArgs a) {
 // ypart[s]; the consumer adds the S splits in split order, so the output does
 // not depend on timing.
 // ---------------------------------------------------------------------------
-template <int BITS, int RT>
+// A-fragment of one block of slot u's intermediate h (fp32 rows
+// [slot][token][row]): lane L = m + 16q holds inputs 8q..8q+7 of row m, i.e.
+// token m & 7, its fp16 hi part for m < 8 and lo part for m >= 8 (fp16
+// activations: token m, rounded to fp16), after scaling by the power of two
+// 2^-eh that puts the largest |h| of the (slot, token) in [2^14, 2^15).
+template <bool A16>
+DEVI half8_t h_fragment(const float4_t (&v)[2], int eh, int lane) {
+  const bool lo = !A16 && (lane & 8);
+  half8_t h;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const float x = ldexpf(v[c >> 2][c & 3], -eh);  // exact (2^-eh itself may exceed the fp32 range)
+    const _Float16 hi = (_Float16)x;
+    h[c] = lo ? (_Float16)(x - (float)hi) : hi;
+  }
+  return h;
+}
+
+template <int BITS, int RT, bool A16>
 __global__ __launch_bounds__(512) void down_decode_kernel(DownArgs a) {
   constexpr int CB = BITS == 2 ? 1280 : 1792;
   constexpr int BK = 8 / RT;
   constexpr int BATCH = 2;
+  constexpr int R = A16 ? MOE_MAX_TOK_F16ACT : MOE_MAX_TOK_DECODE;
   __shared__ float red[8][RT * 4][64];
   const int rg = blockIdx.x, sp = blockIdx.y;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
@@ -478,10 +529,18 @@ __global__ __launch_bounds__(512) void down_decode_kernel(DownArgs a) {
 #pragma unroll
   for (int t = 0; t < RT; ++t) acc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
 
+  // this lane's A-fragment token, and the token of its accumulator rows
+  // 4 (lane >> 4) + i (hi/lo: the lo rows 8..15 are tokens 0..7 again)
+  const int tok_a = A16 ? (lane & 15) : (lane & 7);
+  const int tok_c = A16 ? 4 * (lane >> 4) : (4 * (lane >> 4)) & 7;
+  const float off = -(float)(1 << (BITS - 1));
+  const half8_t ones = half8_t{1, 1, 1, 1, 1, 1, 1, 1};
+
   for (int b0 = wv; b0 < n_items; b0 += nw * BATCH) {
     ChunkRegs<BITS> c[BATCH];
-    half8_t A[BATCH][BK];
-    float4_t cin[BATCH][BK];
+    float4_t hv[BATCH][BK][2];
+    uint32_t hm_a[BATCH];
+    u32x4_t hm_c[BATCH];
     bool ok[BATCH];
 #pragma unroll
     for (int q = 0; q < BATCH; ++q) {
@@ -505,21 +564,42 @@ __global__ __launch_bounds__(512) void down_decode_kernel(DownArgs a) {
         mat = a.X.experts + (int64_t)e * a.X.ex_stride + a.X.off_down;
       }
       load_chunk<BITS>(c[q], mat + ((int64_t)rg * n_kg + kg) * CB, lane);
+      const float* hr = a.hbuf + ((size_t)u * R + tok_a) * a.hI + 32 * (kg * BK) + 8 * (lane >> 4);
 #pragma unroll
-      for (int j = 0; j < BK; ++j)
-        load_a(a.hfrag, a.hsum, (size_t)u * a.nbI + kg * BK + j, lane, A[q][j], cin[q][j]);
+      for (int j = 0; j < BK; ++j) {
+        hv[q][j][0] = *reinterpret_cast<const float4_t*>(hr + 32 * j);
+        hv[q][j][1] = *reinterpret_cast<const float4_t*>(hr + 32 * j + 4);
+      }
+      hm_a[q] = a.hmax[u * 16 + tok_a];
+      hm_c[q] = *reinterpret_cast<const u32x4_t*>(a.hmax + u * 16 + tok_c);
     }
 #pragma unroll
     for (int q = 0; q < BATCH; ++q) {
       if (!ok[q]) continue;
+      const int eh_a = fp16_exponent_for(__uint_as_float(hm_a[q]));
+      float4_t part[RT];
 #pragma unroll
-      for (int j = 0; j < BK; ++j)
+      for (int t = 0; t < RT; ++t) part[t] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < BK; ++j) {
+        const half8_t A = h_fragment<A16>(hv[q][j], eh_a, lane);
+        // the accumulator seed -2^(b-1) sum_k A[m][k], with the row sums laid
+        // out as the accumulators by a product with an all-ones B operand
+        const float4_t cin = off * mfma16x16x32(A, ones, float4_t{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
           const int f = t * BK + j;
-          const float4_t C = mfma16x16x32(A[q][j], chunk_frag<BITS>(c[q], f), cin[q][j]);
-          acc[t] += chunk_scale(c[q].scales, f) * C;
+          const float4_t C = mfma16x16x32(A, chunk_frag<BITS>(c[q], f), cin);
+          part[t] += chunk_scale(c[q].scales, f) * C;
         }
+      }
+      // undo the (slot, token) scaling of this item's rows: 2^eh, exact
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int eh = fp16_exponent_for(__uint_as_float(hm_c[q][i]));
+#pragma unroll
+        for (int t = 0; t < RT; ++t) acc[t][i] += ldexpf(part[t][i], eh);
+      }
     }
   }
 
@@ -541,11 +621,10 @@ __global__ __launch_bounds__(512) void down_decode_kernel(DownArgs a) {
 #pragma unroll
       for (int w = 1; w < 8; ++w)
         if (w < nw) s += part[w];
-      const bool a16 = a.act16 != 0;  // fp16 activations: C row = token, 16 tokens
-      if (!a16) s = add_partner32(s);
+      if (!A16) s = add_partner32(s);  // (fp16 activations: C row = token, 16 tokens)
       const int tok = 4 * (lane >> 4) + i;  // (hi/lo: lanes < 32 hold tokens 0..7)
       const int o = rg * 16 * RT + 16 * t + n;
-      if ((a16 || lane < 32) && tok < T) a.ypart[((size_t)sp * (a16 ? 16 : 8) + tok) * d + o] = s;
+      if ((A16 || lane < 32) && tok < T) a.ypart[((size_t)sp * R + tok) * d + o] = s;
     }
 }
 
@@ -586,14 +665,19 @@ __global__ __launch_bounds__(256) void debug_decode_path_kernel(DebugPathArgs a)
 
 template <int BITS, int RT>
 hipError_t launch_down_t(const DownArgs& a, int grid_x, int nw, hipStream_t s) {
-  MOE_LAUNCH((down_decode_kernel<BITS, RT>), dim3(grid_x, a.S), dim3(64 * nw), 0, s, a);
+  if (a.act16) MOE_LAUNCH((down_decode_kernel<BITS, RT, true>), dim3(grid_x, a.S), dim3(64 * nw), 0, s, a);
+  else MOE_LAUNCH((down_decode_kernel<BITS, RT, false>), dim3(grid_x, a.S), dim3(64 * nw), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gu_decode(const GuArgs& a, int n_wg, hipStream_t s) {
-#define GU_LAUNCH(B, N) MOE_LAUNCH((gu_decode_kernel<B, N>), dim3(n_wg), dim3(64 * GU_NW), 0, s, a)
+#define GU_LAUNCH(B, N)                                                                     \
+  do {                                                                                      \
+    if (a.act16) MOE_LAUNCH((gu_decode_kernel<B, N, true>), dim3(n_wg), dim3(64 * GU_NW), 0, s, a);  \
+    else MOE_LAUNCH((gu_decode_kernel<B, N, false>), dim3(n_wg), dim3(64 * GU_NW), 0, s, a);         \
+  } while (0)
   const int np = a.E <= 512 ? 8 : a.E <= 1024 ? 16 : a.E <= 2048 ? 32 : 64;
   if (a.bits == 2) {
     if (np == 8) GU_LAUNCH(2, 8);

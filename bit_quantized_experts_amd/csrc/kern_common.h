@@ -98,6 +98,11 @@ DEVI float wave_sum(float v) {
   return v;
 }
 
+DEVI float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
 // ---------------------------------------------------------------------------
 // Cross-lane moves that stay in the vector ALU (DPP and the gfx950 permlane
 // swaps), for reductions whose operator is commutative: every step pairs
@@ -115,6 +120,23 @@ DEVI uint32_t dpp_perm(uint32_t v, int step) {
     case 2: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, true);
     default: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, true);
   }
+}
+
+// Sum over the 4 lanes of a quad (lanes 4j..4j+3), in every lane of the quad.
+DEVI float quad_sum(float v) {
+  v += __uint_as_float(dpp_perm(__float_as_uint(v), 0));
+  return v + __uint_as_float(dpp_perm(__float_as_uint(v), 1));
+}
+
+// Exponent e with 2^14 <= m * 2^-e < 2^15 (0 when m is 0 or not a number):
+// scaling a vector by 2^-e (exact) puts its largest magnitude m at the top of
+// the fp16 range, so an fp16 hi + lo split of it neither overflows nor loses
+// its low part to subnormals.
+DEVI int fp16_exponent_for(float m) {
+  if (!(m > 0.f)) return 0;
+  int e;
+  frexpf(m, &e);  // m = f * 2^e, 0.5 <= f < 1
+  return e - 15;
 }
 
 DEVI uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
@@ -141,6 +163,13 @@ DEVI uint64_t wave_max_u64(uint64_t k) {
 DEVI float row16_sum(float v) {
 #pragma unroll
   for (int st = 0; st < 4; ++st) v += __uint_as_float(dpp_perm(__float_as_uint(v), st));
+  return v;
+}
+
+// Largest value over the 16 lanes of a row, in every lane of the row.
+DEVI float row16_max(float v) {
+#pragma unroll
+  for (int st = 0; st < 4; ++st) v = fmaxf(v, __uint_as_float(dpp_perm(__float_as_uint(v), st)));
   return v;
 }
 

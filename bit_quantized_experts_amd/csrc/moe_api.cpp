@@ -150,7 +150,8 @@ PackedLayout packed_layout(const moe_layer_desc* D, const moe_expert_layout& ex,
 
 // ------------------------------------------------------------- workspace ---
 struct WsLayout {
-  int64_t ctrl, lp, ss_part, rnorm, logits, n_slots, slot_expert, slot_w, xfrag, xsum, hfrag, hsum, ypart, total;
+  int64_t ctrl, lp, ss_part, mx_part, rnorm, xexp, logits, n_slots, slot_expert, slot_w, xin, hbuf, hmax, ypart,
+      total;
   int max_slots, S, nbI, n_cs;
 };
 
@@ -187,15 +188,17 @@ WsLayout ws_layout_decode(const moe_layer* L, int T, bool act16 = false) {
   W.ypart = take((int64_t)MOE_MAX_IN_SPLITS * MOE_MAX_TOK_F16ACT * d * 4);
   W.lp = take((int64_t)W.n_cs * T * E * 4);
   W.ss_part = take((int64_t)((E + MOE_ROUTE_ROWS - 1) / MOE_ROUTE_ROWS) * W.n_cs * T * 4);
+  W.mx_part = take((int64_t)W.n_cs * 16 * 4);
   W.rnorm = take(16 * 4);
+  W.xexp = take(16 * 4);
   W.logits = take((int64_t)T * E * 4);
   W.n_slots = take(4);
   W.slot_expert = take((int64_t)W.max_slots * 4);
   W.slot_w = take((int64_t)W.max_slots * 16 * 4);
-  W.xfrag = take((int64_t)(d / 32) * 64 * 8 * 2);
-  W.xsum = take((int64_t)(d / 32) * 16 * 4);
-  W.hfrag = take((int64_t)W.max_slots * W.nbI * 64 * 8 * 2);
-  W.hsum = take((int64_t)W.max_slots * W.nbI * 2 * 16 * 4);
+  W.xin = take((int64_t)MOE_MAX_TOK_F16ACT * d * 4);
+  const int R = act16 ? MOE_MAX_TOK_F16ACT : MOE_MAX_TOK_DECODE;
+  W.hbuf = take((int64_t)W.max_slots * R * W.nbI * 32 * 4);
+  W.hmax = take((int64_t)W.max_slots * 16 * 4);
   W.total = o;
   return W;
 }
@@ -344,11 +347,14 @@ int decode_layer(const moe_layer* L, const LayerInput& in, float eps, int T, flo
   ra.do_logits = !forced;
   ra.act16 = act16;
   ra.lp = reinterpret_cast<float*>(ws + W.lp);
-  ra.xfrag = reinterpret_cast<_Float16*>(ws + W.xfrag);
-  ra.xsum = reinterpret_cast<float*>(ws + W.xsum);
+  ra.xin = reinterpret_cast<float*>(ws + W.xin);
+  ra.hmax = reinterpret_cast<uint32_t*>(ws + W.hmax);
+  ra.hmax_n = W.max_slots * 16;
   ra.y_out = y_prev_out;
   SelectArgs& sa = ra.sel;
   sa.ss_part = reinterpret_cast<float*>(ws + W.ss_part);
+  sa.mx_part = reinterpret_cast<float*>(ws + W.mx_part);
+  sa.xexp = reinterpret_cast<int32_t*>(ws + W.xexp);
   sa.br = L->router_b;
   sa.ew = L->router_ew;
   sa.n_cs = W.n_cs;
@@ -380,17 +386,18 @@ int decode_layer(const moe_layer* L, const LayerInput& in, float eps, int T, flo
   ga.slot_expert = reinterpret_cast<int32_t*>(ws + W.slot_expert);
   ga.slot_w = reinterpret_cast<float*>(ws + W.slot_w);
   ga.rnorm = sa.rnorm;
-  ga.xfrag = ra.xfrag;
-  ga.xsum = ra.xsum;
-  ga.hfrag = reinterpret_cast<_Float16*>(ws + W.hfrag);
-  ga.hsum = reinterpret_cast<float*>(ws + W.hsum);
+  ga.xin = ra.xin;
+  ga.xexp = sa.xexp;
+  ga.hbuf = reinterpret_cast<float*>(ws + W.hbuf);
+  ga.hmax = ra.hmax;
   ga.E = E;
   ga.I = L->I;
   ga.Is = L->Is;
   ga.T = T;
+  ga.d = d;
   ga.n_kg = d / 256;
   ga.bits = L->bits;
-  ga.nbI = W.nbI;
+  ga.hI = W.nbI * 32;
   ga.code_off = ra.code_off;
   ga.has_shared = L->Is > 0;
   ga.act16 = act16;
@@ -411,13 +418,13 @@ int decode_layer(const moe_layer* L, const LayerInput& in, float eps, int T, flo
   da.X = X;
   da.n_slots = ga.n_slots;
   da.slot_expert = ga.slot_expert;
-  da.hfrag = ga.hfrag;
-  da.hsum = ga.hsum;
+  da.hbuf = ga.hbuf;
+  da.hmax = ga.hmax;
   da.E = E;
   da.d = d;
   da.T = T;
   da.bits = L->bits;
-  da.nbI = W.nbI;
+  da.hI = ga.hI;
   da.BK = L->ex.down.BK;
   da.RT = L->ex.down.RT;
   da.n_kg_r = L->ex.down.n_kg;

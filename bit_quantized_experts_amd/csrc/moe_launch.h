@@ -26,6 +26,8 @@
 // (the previous layer's down partials, or the caller's x with S_in = 1).
 struct SelectArgs {
   float* ss_part;      // [n_rs][n_cs][T] sums of squares, one copy per row slice
+  float* mx_part;      // [n_cs][16] largest |input| of each column slice (row slice 0)
+  int32_t* xexp;       // ws [16]: exponent ex of each token row: 2^14 <= max|x| 2^-ex < 2^15
   const float* br;     // [E]
   const int32_t* ew;   // [E16] router row exponents (partial logits are unscaled)
   int32_t n_cs, n_rs, T, d, E, norm;
@@ -45,8 +47,9 @@ struct RouteArgs {
   int32_t T, d, E, code_off, do_logits;
   int32_t act16;    // 1: gate/up A-fragments hold 16 tokens in fp16 (else 8 tokens as fp16 hi + lo)
   float* lp;        // ws [d/MOE_ROUTE_COLS][T][E] partial logits
-  _Float16* xfrag;  // ws [d/32][64][8]
-  float* xsum;      // ws [d/32][16]
+  float* xin;       // ws [16][d]: the summed layer input (row slice 0 writes it)
+  uint32_t* hmax;   // ws [hmax_n]: cleared here for the gate/up kernel's maxima
+  int32_t hmax_n;
   float* y_out;     // optional: the summed input, [T][d]
   SelectArgs sel;   // the logits, finished by the last workgroup of each row slice
 };
@@ -75,11 +78,11 @@ struct GuArgs {
   int32_t* slot_expert;  // out [MAX_SLOTS]
   float* slot_w;         // out [MAX_SLOTS][16]
   const float* rnorm;
-  const _Float16* xfrag;
-  const float* xsum;
-  _Float16* hfrag;  // ws [MAX_SLOTS][nbI][64][8]
-  float* hsum;      // ws [MAX_SLOTS][2 nbI][16], one row of sums per 16-row tile
-  int32_t E, I, Is, T, n_kg, bits, nbI, code_off, has_shared;
+  const float* xin;      // [16][d] layer input rows (before the RMSNorm of stacked layers)
+  const int32_t* xexp;   // [16] row exponents (the fragments hold x 2^-ex)
+  float* hbuf;      // ws [MAX_SLOTS][R][hI] fp32 h = w silu(g) u, R = 16 (act16) or 8
+  uint32_t* hmax;   // ws [MAX_SLOTS][16] largest |h| of each (slot, token), as float bits
+  int32_t E, I, Is, T, d, n_kg, bits, hI, code_off, has_shared;
   int32_t act16;  // 1: A rows are 16 tokens in fp16 (else 8 tokens as fp16 hi + lo)
 };
 
@@ -87,9 +90,9 @@ struct DownArgs {
   ExpertSet X;
   const int32_t* n_slots;
   const int32_t* slot_expert;
-  const _Float16* hfrag;
-  const float* hsum;
-  int32_t E, d, T, bits, nbI, BK, RT, n_kg_r, n_kg_s, S, has_shared, max_slots;
+  const float* hbuf;       // [MAX_SLOTS][R][hI] fp32
+  const uint32_t* hmax;    // [MAX_SLOTS][16]
+  int32_t E, d, T, bits, hI, BK, RT, n_kg_r, n_kg_s, S, has_shared, max_slots;
   int32_t act16;  // 1: A rows are 16 tokens in fp16 (else 8 tokens as fp16 hi + lo)
   float* ypart;   // ws [S][R][d], R = 16 with act16, else 8
 };

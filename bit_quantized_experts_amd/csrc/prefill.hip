@@ -44,25 +44,6 @@ typedef float float2_t __attribute__((ext_vector_type(2)));
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-DEVI float wave_maxf(float v) {
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-
-DEVI float row16_max(float v) {
-#pragma unroll
-  for (int st = 0; st < 4; ++st) v = fmaxf(v, __uint_as_float(dpp_perm(__float_as_uint(v), st)));
-  return v;
-}
-
-// Exponent e with 2^14 <= m * 2^-e < 2^15 (0 when m is 0 or not a number).
-DEVI int fp16_exponent_for(float m) {
-  if (!(m > 0.f)) return 0;
-  int e;
-  frexpf(m, &e);  // m = f * 2^e, 0.5 <= f < 1
-  return e - 15;
-}
-
 DEVI _Float16 half_of_bits(uint32_t b) {
   _Float16 h;
   const uint16_t v = (uint16_t)b;
@@ -132,7 +113,7 @@ __global__ __launch_bounds__(256) void pack_router_kernel(const float* W, int E,
       const float4_t v = *reinterpret_cast<const float4_t*>(row + c);
       m = fmaxf(m, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
     }
-  m = wave_maxf(m);
+  m = wave_max(m);
   const int x = fp16_exponent_for(m);
   if (lane == 0) ew[e] = x;
   const int nb = d / 32;
@@ -189,7 +170,7 @@ __global__ __launch_bounds__(256) void pack_hbound_kernel(const uint8_t* canon, 
   }
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   for (int m = 0; m < 3; ++m) {
-    const float v = wave_maxf(lmax[m]);
+    const float v = wave_max(lmax[m]);
     if (lane == 0) red[m][wv] = v;
   }
   __syncthreads();
@@ -235,7 +216,7 @@ DEVI void prep_row(const PfPrepArgs& a, int t, int lane) {
   } else {
     for (int c = 4 * lane; c < a.d; c += 256) acc(*reinterpret_cast<const float4_t*>(xr + c));
   }
-  m = wave_maxf(m);
+  m = wave_max(m);
   float rms = 1.f;
   if (a.norm) {
     ss = wave_sum(ss);

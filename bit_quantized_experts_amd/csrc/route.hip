@@ -90,11 +90,12 @@ DEVI void finish_slice(const RouteArgs& a, int rs) {
   const float* ssr = c.ss_part + (size_t)rs * n_cs * T;
   for (int h = 0; 8 * h < T; ++h) {
     int t[2];
-    float ss[2], tmp[2][MAXCS];
+    float ss[2], mx[2], tmp[2][MAXCS];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       t[j] = min(8 * h + wv + 4 * j, T - 1);
       ss[j] = ld_dev(ssr + min(lane, n_cs - 1) * T + t[j]);
+      mx[j] = rs == 0 ? ld_dev(c.mx_part + min(lane, n_cs - 1) * 16 + t[j]) : 0.f;
       if (a.do_logits) {
 #pragma unroll
         for (int q = 0; q < MAXCS; ++q) tmp[j][q] = ld_dev(a.lp + ((size_t)min(q, n_cs - 1) * T + t[j]) * E + e);
@@ -104,8 +105,12 @@ DEVI void finish_slice(const RouteArgs& a, int rs) {
     for (int j = 0; j < 2; ++j) {
       const int tok = 8 * h + wv + 4 * j;
       const float r = c.norm ? sqrtf(wave_sum((lane < n_cs) ? ss[j] : 0.f) / (float)c.d + c.eps) : 1.0f;
+      const float m = wave_max((lane < n_cs) ? mx[j] : 0.f);
       if (tok >= T) continue;
-      if (rs == 0 && lane == 0) c.rnorm[tok] = r;
+      if (rs == 0 && lane == 0) {
+        c.rnorm[tok] = r;
+        c.xexp[tok] = fp16_exponent_for(m);
+      }
       if (!a.do_logits) continue;
       float acc = tmp[j][0];
 #pragma unroll
@@ -136,22 +141,25 @@ DEVI void route_finish(const RouteArgs& a, int rs) {
 // experts).  Sums the input splits for its columns, writes partial logits of
 // its 64 experts over those columns and the slice's sums of squares (every
 // row slice its own copy); the rs == 0 workgroups also write the summed input
-// (if asked) and the fp16 hi/lo MFMA A-fragments of the 4 blocks of the
-// slice:
-//   lane L = m + 16q of block b holds row m (m < 8: token m, hi part; m >= 8:
-//   token m-8, lo part) at inputs 8q..8q+7; xsum[b][m] = -code_off * sum;
-//   with fp16 activations (act16) row m is token m rounded to fp16.
-// The partial logits run on the matrix cores: hi/lo A-fragments of 8 tokens
-// (built in registers by every workgroup; a second row tile for tokens 8..15)
-// times the router rows prepared at pack time
-// as 2^ew (wh + wl), fp16 hi and lo B-fragments, so one wavefront's 16
+// slice (xin, for the gate/up kernel, and the caller's copy if asked) and its
+// largest magnitude per token (the finishing workgroup turns those into the
+// row exponents the gate/up kernel scales the activations by).
+// The partial logits run on the matrix cores: fp16 hi/lo A-fragments of 8
+// tokens of the slice scaled by 2^-e (e per token and slice, from the
+// slice's largest magnitude, so the split neither overflows nor underflows;
+// a second row tile for tokens 8..15) times the router rows prepared at pack
+// time as 2^ew (wh + wl), fp16 hi and lo B-fragments, so one wavefront's 16
 // experts over the 4 blocks take 8 v_mfma_f32_16x16x32_f16 and the hi and lo
-// rows of a token are added once at the end.  All four products of the
-// ~22-bit operands are formed exactly; the rounding is fp32 accumulation.
-// The power of two 2^ew of each router row is applied to the summed
-// partials (exact) by the workgroup that finishes the row slice (above).
+// rows of a token are added once at the end, then scaled back by 2^e.  All
+// four products of the ~22-bit operands are formed exactly; the rounding is
+// fp32 accumulation.  The power of two 2^ew of each router row is applied to
+// the summed partials (exact) by the workgroup that finishes the row slice
+// (above).
 // ---------------------------------------------------------------------------
-DEVI half8_t x_fragment(const float (*ys)[MOE_ROUTE_COLS], int bl, int lane, int T, float* sum) {
+// A-fragment of block bl of the slice: lane L = m + 16q holds row m (m < 8:
+// token m, hi part; m >= 8: token m-8, lo part) at inputs 8q..8q+7, scaled by
+// 2^-e of its token.
+DEVI half8_t x_fragment(const float (*ys)[MOE_ROUTE_COLS], int bl, int lane, int T, int e) {
   const int m = lane & 15, q = lane >> 4, tok = m & 7, lo = m >> 3;  // (ys, T: from the tile's first token)
   float4_t v0 = float4_t{0.f, 0.f, 0.f, 0.f}, v1 = v0;
   if (tok < T) {
@@ -159,40 +167,18 @@ DEVI half8_t x_fragment(const float (*ys)[MOE_ROUTE_COLS], int bl, int lane, int
     v1 = *reinterpret_cast<const float4_t*>(&ys[tok][32 * bl + 8 * q + 4]);
   }
   half8_t h;
-  float s = 0.f;
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    const float v = c < 4 ? v0[c] : v1[c - 4];
+    const float v = ldexpf(c < 4 ? v0[c] : v1[c - 4], -e);  // exact (2^-e itself may exceed the fp32 range)
     const _Float16 hi = (_Float16)v;
-    const _Float16 out = lo ? (_Float16)(v - (float)hi) : hi;
-    h[c] = out;
-    s += (float)out;
+    h[c] = lo ? (_Float16)(v - (float)hi) : hi;
   }
-  *sum = s;
-  return h;
-}
-
-// The same block with one fp16 row per token (16 tokens).
-DEVI half8_t x_fragment16(const float (*ys)[MOE_ROUTE_COLS], int bl, int lane, int T, float* sum) {
-  const int m = lane & 15, q = lane >> 4;
-  float4_t v0 = float4_t{0.f, 0.f, 0.f, 0.f}, v1 = v0;
-  if (m < T) {
-    v0 = *reinterpret_cast<const float4_t*>(&ys[m][32 * bl + 8 * q]);
-    v1 = *reinterpret_cast<const float4_t*>(&ys[m][32 * bl + 8 * q + 4]);
-  }
-  half8_t h;
-  float s = 0.f;
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    h[c] = (_Float16)(c < 4 ? v0[c] : v1[c - 4]);
-    s += (float)h[c];
-  }
-  *sum = s;
   return h;
 }
 
 __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   __shared__ float ys[MOE_MAX_TOK_F16ACT][MOE_ROUTE_COLS];
+  __shared__ int xe[MOE_MAX_TOK_F16ACT];  // slice exponent of each token
   const int cs = blockIdx.x, rs = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -240,39 +226,38 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
       for (int s = 1; s < MOE_MAX_IN_SPLITS; ++s)
         if (s < a.S_in) acc += v[j][s];
       *reinterpret_cast<float4_t*>(&ys[t][4 * c4]) = acc;
-      if (rs == 0 && a.y_out) *reinterpret_cast<float4_t*>(a.y_out + (size_t)t * d + c0 + 4 * c4) = acc;
+      if (rs == 0) {
+        *reinterpret_cast<float4_t*>(a.xin + (size_t)t * d + c0 + 4 * c4) = acc;
+        if (a.y_out) *reinterpret_cast<float4_t*>(a.y_out + (size_t)t * d + c0 + 4 * c4) = acc;
+      }
     }
   }
+  // the gate/up kernel's per-(slot, token) maxima start from zero
+  if (cs == 0 && rs == 0)
+    for (int i = tid; i < a.hmax_n; i += 256) a.hmax[i] = 0u;
   __syncthreads();
 
-  // sums of squares of the slice (each row slice keeps its own copy)
+  // sums of squares of the slice (each row slice keeps its own copy) and its
+  // largest magnitude per token
   for (int t = wv; t < T; t += 4) {
     const float4 v = lane < RQ ? *reinterpret_cast<const float4*>(&ys[t][4 * lane]) : float4{0.f, 0.f, 0.f, 0.f};
     const float ss = wave_sum(v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w);
-    if (lane == 0) st_dev(a.sel.ss_part + ((size_t)rs * gridDim.x + cs) * T + t, ss);
-  }
-  if (rs == 0) {
-    const int m = lane & 15, q = lane >> 4;
-    for (int bl = wv; bl < NBL; bl += 4) {
-      const int b = cs * NBL + bl;
-      float s;
-      const half8_t h = a.act16 ? x_fragment16(ys, bl, lane, T, &s) : x_fragment(ys, bl, lane, T, &s);
-      *reinterpret_cast<half8_t*>(a.xfrag + ((size_t)b * 64 + lane) * 8) = h;
-      s += __shfl_xor(s, 16, 64);
-      s += __shfl_xor(s, 32, 64);
-      if (q == 0) a.xsum[b * 16 + m] = -(float)a.code_off * s;
+    const float mx = wave_max(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    if (lane == 0) {
+      st_dev(a.sel.ss_part + ((size_t)rs * gridDim.x + cs) * T + t, ss);
+      if (rs == 0) st_dev(a.sel.mx_part + cs * 16 + t, mx);
+      xe[t] = fp16_exponent_for(mx);
     }
   }
+  __syncthreads();
 
   if (tile_ok) {
     // row tiles of 8 tokens: tokens 8 tb .. 8 tb + 7
     for (int tb = 0; 8 * tb < T; ++tb) {
       half8_t A[NBL];
+      const int tl = min(8 * tb + (lane & 7), T - 1);  // this lane's token (clamped past T: its rows are zero)
 #pragma unroll
-      for (int j = 0; j < NBL; ++j) {
-        float s;
-        A[j] = x_fragment(ys + 8 * tb, j, lane, T - 8 * tb, &s);
-      }
+      for (int j = 0; j < NBL; ++j) A[j] = x_fragment(ys + 8 * tb, j, lane, T - 8 * tb, xe[tl]);
       float4_t acc = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < NBL; ++j) {
@@ -288,7 +273,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
       for (int i = 0; i < 4; ++i) {
         const float v = add_partner32(acc[i]);
         const int t = 8 * tb + 4 * ((lane >> 4) & 1) + i;
-        if (lane < 32 && e < E && t < T) st_dev(a.lp + ((size_t)cs * T + t) * E + e, v);
+        if (lane < 32 && e < E && t < T) st_dev(a.lp + ((size_t)cs * T + t) * E + e, ldexpf(v, xe[t]));
       }
     }
   }

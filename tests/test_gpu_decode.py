@@ -184,6 +184,21 @@ def test_layer_full_size(bqe, bits):
         _check_layer(wl, 0, L, x, bqe, f"full bits={bits} T={T}")
 
 
+@pytest.mark.parametrize("shape", ["tiny", "full"])
+def test_layer_extreme_scales(bqe, shape):
+    """Inputs far from unit scale (x times 2^20 and 2^-20) and block scales
+    near the largest the packer accepts: every row keeps the decode path's
+    precision relative to its own norm (the activations and the intermediate
+    h are scaled by powers of two before they are split into fp16 parts)."""
+    base = mi.WORKLOADS["tiny"] if shape == "tiny" else mi.small(mi.WORKLOADS["layer_t1"], E=24, layers=1)
+    for scale_lo, scale_hi in ((0.01, 0.05), (6.0, 7.9)):
+        wl = mi.small(base, Is=64 if shape == "tiny" else base.Is, zipf_s=1.1, scale_lo=scale_lo, scale_hi=scale_hi)
+        L = packed_layer(wl, 0)
+        for T, p in ((3, 20), (8, -20), (1, -60)):
+            x = (mi.activations(wl, T=T, stream=90 + T) * np.float32(2.0 ** p)).astype(np.float32)
+            _check_layer(wl, 0, L, x, bqe, f"{shape} scales U({scale_lo},{scale_hi}) x*2^{p} T={T}")
+
+
 def test_layer_odd_shapes(bqe):
     # E not a multiple of 16, intermediate sizes not multiples of 64, k = E,
     # a shared expert wider than the routed ones, and inputs wider than one
@@ -346,6 +361,7 @@ def test_stack_teacher_forced(bqe, which):
         rerr = row_rel_err(yl[l], oy)
         say(f"    layer {l}: rel err {err:.3e} (largest per-row {rerr:.3e})")
         assert err <= TOL_LAYER, (l, err)
+        assert err <= TOL_DECODE_PATH and rerr <= TOL_DECODE_PATH, (l, err, rerr)
 
 
 def test_stack_mixed_layer_shapes(bqe):

@@ -16,7 +16,7 @@ import torch
 import moe_inputs as mi
 import oracle
 from moe_inputs.device import packed_layer, activations_device
-from tests.helpers import TOL_LAYER, oracle_layer, rel_err_inf, say
+from tests.helpers import TOL_LAYER, oracle_layer, rel_err_inf, row_rel_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -62,10 +62,22 @@ def _check(bqe, wl, L, x_np, tag, layer=0):
     OL = oracle_layer(wl, layer, idx.reshape(-1))
     oy, _, _, _ = oracle.layer_forward(OL, x_np, force_idx=idx, force_w=w)
     err = rel_err_inf(y, oy)
-    say(f"    rel err {err:.3e}")
+    rerr = row_rel_err(y, oy)
+    say(f"    rel err {err:.3e} (largest per-row {rerr:.3e})")
     assert np.all(np.isfinite(y))
-    assert err <= TOL_LAYER, (tag, err)
+    assert err <= TOL_LAYER and rerr <= TOL_LAYER, (tag, err, rerr)
     return err
+
+
+def test_f16act_extreme_scales(bqe):
+    """Inputs far from unit scale and block scales near the largest the
+    packer accepts: every row within the bar relative to its own norm."""
+    for scale_lo, scale_hi in ((0.01, 0.05), (6.0, 7.9)):
+        wl = mi.small(mi.WORKLOADS["tiny"], Is=64, zipf_s=1.1, scale_lo=scale_lo, scale_hi=scale_hi)
+        L = packed_layer(wl, 0)
+        for T, p in ((5, 20), (16, -20), (9, -60)):
+            x = (mi.activations(wl, T=T, stream=80 + T) * np.float32(2.0 ** p)).astype(np.float32)
+            _check(bqe, wl, L, x, f"scales U({scale_lo},{scale_hi}) x*2^{p}")
 
 
 @pytest.mark.parametrize("bits", [2, 3])
@@ -155,8 +167,9 @@ def test_f16act_stack_teacher_forced(bqe, which):
         OL = oracle_layer(wl, l, il[l].reshape(-1))
         oy, _, _, _ = oracle.layer_forward(OL, h, force_idx=il[l], force_w=wr[l])
         err = rel_err_inf(yl[l], oy)
-        say(f"    layer {l}: rel err {err:.3e}")
-        assert err <= TOL_LAYER, (l, err)
+        rerr = row_rel_err(yl[l], oy)
+        say(f"    layer {l}: rel err {err:.3e} (largest per-row {rerr:.3e})")
+        assert err <= TOL_LAYER and rerr <= TOL_LAYER, (l, err, rerr)
 
 
 def test_f16act_rows_independent(bqe):
