@@ -26,7 +26,7 @@ EXPORTED = ("moe_last_error", "moe_packed_bytes", "moe_pack_experts", "moe_layer
             "moe_route_topk", "moe_workspace_bytes", "moe_workspace_init", "moe_layer_forward",
             "moe_stack_forward", "moe_rmsnorm", "moe_debug_unpack", "moe_timing_start", "moe_timing_stop",
             "moe_group_workspace_bytes", "moe_group_tokens", "moe_layer_forward_f16act",
-            "moe_stack_forward_f16act", "moe_debug_unpack_path")
+            "moe_stack_forward_f16act", "moe_debug_unpack_path", "moe_layer_forward_noalloc")
 
 
 class MoeError(RuntimeError):
@@ -69,6 +69,7 @@ def lib() -> ctypes.CDLL:
         L.moe_layer_forward.argtypes = [P, P, I, P, P, P, S, P]
         L.moe_stack_forward.argtypes = [P, I, P, I, ctypes.c_float, P, P, P, P, P, S, P]
         L.moe_layer_forward_f16act.argtypes = [P, P, I, P, P, P, S, P]
+        L.moe_layer_forward_noalloc.argtypes = [P, P, I, P, P, P]
         L.moe_stack_forward_f16act.argtypes = [P, I, P, I, ctypes.c_float, P, P, P, P, P, S, P]
         L.moe_rmsnorm.argtypes = [P, I, I, ctypes.c_float, P, P]
         L.moe_debug_unpack.argtypes = [P, I, I, P, P, P, P]
@@ -160,6 +161,16 @@ def moe_layer_forward(handle: int, x, y, ws, route: RouteIO | None = None, strea
     T = x.shape[0]
     _check(lib().moe_layer_forward(handle, _ptr(x), T, _ptr(y), ctypes.byref(route) if route is not None else None,
                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "moe_layer_forward")
+
+
+def moe_layer_forward_noalloc(handle: int, x, y, route: RouteIO | None = None, stream=None):
+    T = x.shape[0]
+    _check(lib().moe_layer_forward_noalloc(handle, _ptr(x), T, _ptr(y),
+                                           ctypes.byref(route) if route is not None else None, _stream(stream)),
+           "moe_layer_forward_noalloc")
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 def moe_layer_forward_f16act(handle: int, x, y, ws, route: RouteIO | None = None, stream=None):

@@ -584,6 +584,37 @@ int check_ws(const moe_layer* L, int T, void* ws, size_t ws_bytes, size_t* need)
 
 }  // namespace
 
+// ------------------------------------------------------ allocation-free ---
+// Device scratch of moe_layer_forward_noalloc: a file-scope device array that
+// every such call on a GPU shares (each GPU holds its own copy until the
+// process ends).  Its name is a host-side stand-in in host code, not a device
+// address: the address comes from hipGetSymbolAddress, once per device with
+// that device current, and only that address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+// Device address of this device's scratch (looked up on the first call on
+// each device).
+int scratch_ptr(void** out) {
+  int dev = 0;
+  HIPCHK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) return fail(MOE_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    HIPCHK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* moe_last_error(void) { return g_err.c_str(); }
@@ -792,6 +823,22 @@ int moe_layer_forward(const moe_layer* L, const float* x, int T, float* y, const
   if (rc || T == 0) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
+  if (T > MOE_MAX_TOK_DECODE) return prefill_layer(L, x, 0, 0.f, T, y, route, wsb, st);
+  return decode_layer_out(L, x, T, y, route, wsb, st, false);
+}
+
+int moe_layer_forward_noalloc(const moe_layer* L, const float* x, int T, float* y, const moe_route_io* route,
+                              void* stream) {
+  void* ws = nullptr;
+  int rc = scratch_ptr(&ws);
+  if (rc) return rc;
+  rc = layer_args(L, x, T, y, route, ws, MOE_NOALLOC_SCRATCH_BYTES);
+  if (rc || T == 0) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
+  // the scratch keeps the previous call's contents: clear the control words
+  // the kernels count in (a fill kernel, so the call stays capturable)
+  HIPCHK(launch_fill_u32(reinterpret_cast<uint32_t*>(wsb), (size_t)ctrl_bytes() / 4, 0u, st));
   if (T > MOE_MAX_TOK_DECODE) return prefill_layer(L, x, 0, 0.f, T, y, route, wsb, st);
   return decode_layer_out(L, x, T, y, route, wsb, st, false);
 }

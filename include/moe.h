@@ -37,7 +37,9 @@
  *     moe_last_error() returns a message for the calling thread.  Nothing is
  *     launched when an argument check fails.  No call aborts the process.
  *   - Device pointers are caller-owned HIP device memory, 16-byte aligned
- *     (checked).  The library never allocates or frees device memory.
+ *     (checked).  The library never allocates or frees device memory (its one
+ *     static device array, the scratch of moe_layer_forward_noalloc, is part
+ *     of its code object).
  *   - `stream` is a hipStream_t (NULL = the default stream).  All GPU work is
  *     enqueued asynchronously on it; apart from moe_pack_experts no call waits
  *     for the GPU, and the forward calls may be captured into a HIP graph.
@@ -164,6 +166,23 @@ int moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
  * `route` may be NULL.  ws_bytes >= moe_workspace_bytes(layer, T). */
 int moe_layer_forward(const moe_layer *layer, const float *x, int T, float *y, const moe_route_io *route,
                       void *ws, size_t ws_bytes, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * moe_layer_forward with the library's own device scratch instead of a
+ * caller's workspace.  The scratch is a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds until the
+ * process ends; this call allocates nothing and frees nothing.  Arguments,
+ * routing input/output and results as moe_layer_forward (the same kernels).
+ * A call whose workspace (moe_workspace_bytes) exceeds the scratch returns
+ * MOE_ERR_WORKSPACE before launching anything (a full-size layer of 2560 x
+ * 512 experts fits up to 8 tokens; long prefill chunks do not).  Every call
+ * on one GPU shares that GPU's scratch: calls that can overlap on one GPU
+ * (different streams, or several host threads) race and must be serialised
+ * by the caller. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int moe_layer_forward_noalloc(const moe_layer *layer, const float *x, int T, float *y, const moe_route_io *route,
+                              void *stream);
 
 /* The same layer through the decode kernels with fp16 activations, for
  * 1 <= T <= 16 tokens in one pass: speed for accuracy, the trade the
