@@ -108,6 +108,33 @@ def measured_traffic(workload: str, kernel: str):
     return 1024.0 * (ent["fetch_kib"] * tab["fetch_scale"] + ent["write_kib"] * tab["write_scale"])
 
 
+def time_classes(bqe, run_pass, classes, reps, max_launches, before=None):
+    """Average duration (seconds per launch) of each kernel class the pass
+    launches, from the events its launches record themselves (launches
+    serialized); classes the pass does not launch are left out."""
+    kdur = {}
+    for cls, name in classes:
+        tot, n = 0.0, 0
+        for i in range(reps):
+            if before is not None:
+                before(i)
+            bqe.moe_timing_start(cls, max_launches)
+            run_pass(i)
+            ms, cnt = bqe.moe_timing_stop()
+            tot += ms
+            n += cnt
+        if n:
+            kdur[name] = (tot / n) * 1e-3
+    return kdur
+
+
+def decode_classes(bqe):
+    # the persistent decode pass (one launch per pass) where it applies, else
+    # the three kernels per layer
+    return ((bqe.TIMING_PERSIST, "decode_pass"), (bqe.TIMING_GATE_UP, "gate_up"), (bqe.TIMING_DOWN, "down"),
+            (bqe.TIMING_ROUTER, "router"))
+
+
 def cpu_baseline_stack(wl, T, x_np, n_layers_sample):
     """Time the oracle (single-threaded fp64 C) on the first layers of the
     stack; expert generation is excluded from the timed parts."""
@@ -456,20 +483,11 @@ def bench_layer_t1(args):
     # algorithmic bytes: router + bias, the 10 routed experts and the shared
     # expert, x and y
     nbytes = wl.E * wl.d * 4 + wl.E * 4 + wl.k * wl.expert_bytes() + wl.expert_bytes(wl.Is) + 2 * wl.d * 4
-    kdur = {}
-    for cls, name in ((bqe.TIMING_GATE_UP, "gate_up"), (bqe.TIMING_DOWN, "down"), (bqe.TIMING_ROUTER, "router")):
-        tot, n = 0.0, 0
-        for i in range(ring):
-            flush.fill_(float(i))
-            bqe.moe_timing_start(cls, 1)
-            bqe.moe_layer_forward(L.handle, xs[i], y, ws, rio)
-            ms, cnt = bqe.moe_timing_stop()
-            tot += ms
-            n += cnt
-        kdur[name] = (tot / n) * 1e-3
+    kdur = time_classes(bqe, lambda i: bqe.moe_layer_forward(L.handle, xs[i], y, ws, rio), decode_classes(bqe),
+                        ring, 1, before=lambda i: flush.fill_(float(i)))
     gu_bytes = (wl.k + 1) * 2 * wl.I * (wl.d // 32) * wl.block_bytes()
     dn_bytes = (wl.k + 1) * wl.d * (wl.I // 32) * wl.block_bytes()
-    per = {"gate_up": gu_bytes, "down": dn_bytes, "router": wl.E * wl.d * 4 + wl.E * 4}
+    per = {"gate_up": gu_bytes, "down": dn_bytes, "router": wl.E * wl.d * 4 + wl.E * 4, "decode_pass": nbytes}
     kernels = {n: {"avg_us": kdur[n] * 1e6, "bytes_per_launch": per[n], "GBps": per[n] / kdur[n] / 1e9} for n in kdur}
     dom = max(kdur, key=lambda n: kdur[n])
     achieved = per[dom] / kdur[dom] / 1e9
@@ -584,16 +602,7 @@ def bench_stack(args, wl, T, layers):
 
     # per-kernel durations, measured with HIP events bracketing each launch on
     # the launch stream (eager passes, one kernel class at a time)
-    kdur = {}
-    for cls, name in ((bqe.TIMING_GATE_UP, "gate_up"), (bqe.TIMING_DOWN, "down"), (bqe.TIMING_ROUTER, "router")):
-        tot, n = 0.0, 0
-        for _ in range(3):
-            bqe.moe_timing_start(cls, wl.layers)
-            run_pass()
-            ms, cnt = bqe.moe_timing_stop()
-            tot += ms
-            n += cnt
-        kdur[name] = (tot / n) * 1e-3  # seconds per launch
+    kdur = time_classes(bqe, lambda i: run_pass(), decode_classes(bqe), 3, wl.layers)
 
     if args.timing_only:
         return {"timing_only": wl.name, "T": T, "kernels_avg_us": {n: kdur[n] * 1e6 for n in kdur}}
@@ -664,8 +673,11 @@ def bench_stack(args, wl, T, layers):
     gbs = total_bytes / sec_per_step / 1e9
 
     # roofline of the dominant kernel (largest share of the pass)
+    # (the persistent pass moves the whole pass's bytes in one launch of up
+    # to 64 layers)
     per_class_bytes = {"gate_up": gu_bytes.mean(), "down": dn_bytes.mean(),
-                       "router": float(wl.E * wl.d * 4 + wl.E * 4)}
+                       "router": float(wl.E * wl.d * 4 + wl.E * 4),
+                       "decode_pass": algorithmic_bytes_decode(wl, idx_np, T)[0] / ((wl.layers + 63) // 64)}
     dom = max(kdur, key=lambda n: kdur[n])
     achieved = per_class_bytes[dom] / kdur[dom] / 1e9
     kernels = {n: {"avg_us": kdur[n] * 1e6, "bytes_per_launch": per_class_bytes[n],

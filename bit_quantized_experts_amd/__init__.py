@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_DATA = 0, 1, 2, 3, 4, 5
 TIMING_GATE_UP, TIMING_DOWN, TIMING_ROUTER, TIMING_PREFILL_GATE_UP, TIMING_PREFILL_DOWN = 0, 1, 2, 3, 4
 TIMING_PREFILL_ROUTER = 5
+TIMING_PERSIST = 6
 MAX_TOK_DECODE_KERNELS = 8  # one layer of at most this many tokens runs the decode kernels
 MAX_TOK_F16ACT = 16  # tokens per call of the fp16-activation decode entry points
 
@@ -26,7 +27,8 @@ EXPORTED = ("moe_last_error", "moe_packed_bytes", "moe_pack_experts", "moe_layer
             "moe_route_topk", "moe_workspace_bytes", "moe_workspace_init", "moe_layer_forward",
             "moe_stack_forward", "moe_rmsnorm", "moe_debug_unpack", "moe_timing_start", "moe_timing_stop",
             "moe_group_workspace_bytes", "moe_group_tokens", "moe_layer_forward_f16act",
-            "moe_stack_forward_f16act", "moe_debug_unpack_path", "moe_layer_forward_noalloc")
+            "moe_stack_forward_f16act", "moe_debug_unpack_path", "moe_layer_forward_noalloc",
+            "moe_workspace_status", "moe_layer_workspace_bytes")
 
 
 class MoeError(RuntimeError):
@@ -65,11 +67,13 @@ def lib() -> ctypes.CDLL:
         L.moe_layer_get_desc.argtypes = [P, P]
         L.moe_route_topk.argtypes = [P, I, I, I, P, P, P]
         L.moe_workspace_bytes.argtypes = [P, I, ctypes.POINTER(S)]
+        L.moe_layer_workspace_bytes.argtypes = [P, I, ctypes.POINTER(S)]
         L.moe_workspace_init.argtypes = [P, S, P]
         L.moe_layer_forward.argtypes = [P, P, I, P, P, P, S, P]
         L.moe_stack_forward.argtypes = [P, I, P, I, ctypes.c_float, P, P, P, P, P, S, P]
         L.moe_layer_forward_f16act.argtypes = [P, P, I, P, P, P, S, P]
         L.moe_layer_forward_noalloc.argtypes = [P, P, I, P, P, P]
+        L.moe_workspace_status.argtypes = [P, S, ctypes.POINTER(I), P]
         L.moe_stack_forward_f16act.argtypes = [P, I, P, I, ctypes.c_float, P, P, P, P, P, S, P]
         L.moe_rmsnorm.argtypes = [P, I, I, ctypes.c_float, P, P]
         L.moe_debug_unpack.argtypes = [P, I, I, P, P, P, P]
@@ -153,6 +157,12 @@ def moe_workspace_bytes(handle: int, T: int) -> int:
     return n.value
 
 
+def moe_layer_workspace_bytes(handle: int, T: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().moe_layer_workspace_bytes(handle, T, ctypes.byref(n)), "moe_layer_workspace_bytes")
+    return n.value
+
+
 def moe_workspace_init(ws, stream=None):
     _check(lib().moe_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "moe_workspace_init")
 
@@ -227,6 +237,13 @@ def moe_debug_unpack_path(handle: int, expert: int, mat: int, path: int, codes=N
                                        _stream(stream)), "moe_debug_unpack_path")
 
 
+def moe_workspace_status(ws, stream=None) -> int:
+    st = ctypes.c_int()
+    _check(lib().moe_workspace_status(_ptr(ws), ws.numel() * ws.element_size(), ctypes.byref(st), _stream(stream)),
+           "moe_workspace_status")
+    return st.value
+
+
 def moe_timing_start(kernel_class: int, max_launches: int):
     _check(lib().moe_timing_start(kernel_class, max_launches), "moe_timing_start")
 
@@ -252,6 +269,9 @@ class PackedLayer:
 
     def workspace_bytes(self, T: int) -> int:
         return moe_workspace_bytes(self.handle, T)
+
+    def layer_workspace_bytes(self, T: int) -> int:
+        return moe_layer_workspace_bytes(self.handle, T)
 
     def close(self):
         if getattr(self, "handle", None):

@@ -1,631 +1,26 @@
-// decode.hip -- expert kernels for decode and draft verification (T <= 8).
-//
-// Experts are multiplied straight from their low-bit blocks [strata-mlx wiki,
-// opening feature list, first item]; one pass checks up to eight tokens (one
-// real token and seven drafts) [devlabs blog "32GB Mac mini 6 跑 125B 大模型",
-// section 核心技术特点, MTP item].
-//
-// Arithmetic on the matrix cores (v_mfma_f32_16x16x32_f16), transposed so the
-// tokens are the M dimension and weight rows the N dimension:
-//   A[m][k]  = activation fp16, m < 8: hi part of token m, m >= 8: lo part
-//              of token m-8 (x = hi + lo to ~22 bits),
-//   B[k][n]  = unsigned code q of weight row n, input k (exact fp16 integer),
-//   C_in[m]  = -2^(b-1) * sum_k A[m][k]  (the block sum, fp32),
-// so one MFMA per 32-weight block gives sum_k A (q - 2^(b-1)) = sum_k A c for
-// 16 rows; the lane holding column n then applies the fp16 block scale of row
-// n with one fused multiply-add per output.  Every product and the offset are
-// exact; the rounding is the fp32 accumulation.
-//
-// Memory: weight chunks stream from HBM into registers, several k-groups
-// ahead of the multiplies; the gate/up activation fragments are read from
-// LDS (one copy per workgroup), the down kernel's h fragments from L2.
-#include "kern_common.h"
-#include "moe_launch.h"
-#include "topk.h"
+// decode.hip -- the decode path as three kernels per layer (route.hip's
+// router, then gate/up and down here), for stacks whose layers differ in
+// shape; the persistent stack kernel (persist.hip) runs the same device code
+// (decode_dev.h) as phases of one launch.
+#include "decode_dev.h"
 
 namespace {
 
-template <int BITS>
-struct ChunkRegs {
-  u32x4_t codes;
-  u32x4_t scales;  // 8 fp16
-  u32x2_t hbits;   // 3-bit only
-};
-
-template <int BITS>
-DEVI void load_chunk(ChunkRegs<BITS>& c, const uint8_t* chunk, int lane) {
-  c.codes = ld128_nt(chunk + 16 * lane);
-  c.scales = ld128_nt(chunk + 1024 + 16 * (lane & 15));
-  if constexpr (BITS == 3) c.hbits = ld64_nt(chunk + 1280 + 8 * lane);
-}
-
-template <int BITS>
-DEVI half8_t chunk_frag(const ChunkRegs<BITS>& c, int f) {
-  if constexpr (BITS == 2) return frag_q2(c.codes, f);
-  else return frag_q3(c.codes, c.hbits, f);
-}
-
-DEVI float chunk_scale(const u32x4_t& s, int f) {
-  const uint32_t dw = s[f >> 1];
-  return half_bits_to_float((f & 1) ? (dw >> 16) : (dw & 0xffffu));
-}
-
-// ---------------------------------------------------------------------------
-// Slot list in LDS: routed experts numbered in ascending id order after the
-// shared expert's slot 0, and every (token, rank) entry's gate weight in its
-// slot's row.  The weight rows are cleared first (the shared expert's row set
-// to 1 for the tokens present).  Each token's wavefront marks its experts in
-// a byte map (plain byte stores of 1, so no atomics).  After a barrier every
-// token's wavefront reads the whole map, one ballot per 64 ids, which gives
-// the slot of any marked id (the shared slot plus the marked ids below it),
-// and writes its own entries: the slot's expert id and the token's weight.
-// Tokens that share an expert write the same id to its slot.
-// ---------------------------------------------------------------------------
-struct SlotLds {
-  uint8_t sel[MOE_MAX_E];  // 1 = selected
-  int expert[MOE_MAX_SLOTS];
-  float w[MOE_MAX_SLOTS][16];  // [slot][token]
-  int n_routed;
-};
-
-// Clears the byte map and the first n_slots weight rows (every thread of the
-// workgroup takes part).
-DEVI void clear_slots(SlotLds& S, int E, int T, int n_slots, bool has_shared) {
-  for (int i = threadIdx.x; i < (E + 3) / 4; i += blockDim.x) reinterpret_cast<uint32_t*>(S.sel)[i] = 0u;
-  for (int i = threadIdx.x; i < n_slots * 16; i += blockDim.x) (&S.w[0][0])[i] = (has_shared && i < T) ? 1.0f : 0.f;
-}
-
-// Marks this lane's expert e (ids out of range are skipped).
-DEVI void mark_lane(SlotLds& S, int e, int E) {
-  if (e >= 0 && e < E) S.sel[e] = 1;
-}
-
-// Token t's wavefront, after every mark: lane r < k holds the token's entry
-// (e, w).  Puts w in row t of e's slot and the id in the slot table.  With
-// dedup (given routing rows) a repeated id in the row keeps its first entry
-// (a selection has no repeats).  With count, lane 0 also writes the number of
-// routed slots and the shared expert's slot entry.
-template <int NPER>
-DEVI void place_lane(SlotLds& S, int e, float w, int t, int k, int E, int base, bool dedup, bool count) {
-  const int lane = threadIdx.x & 63;
-  uint8_t f[NPER];  // every read first (a guarded read would wait on its own)
-#pragma unroll
-  for (int i = 0; i < NPER; ++i) f[i] = S.sel[min(lane + 64 * i, E - 1)];
-  uint64_t M[NPER];
-#pragma unroll
-  for (int i = 0; i < NPER; ++i) M[i] = __ballot((f[i] != 0) & (lane + 64 * i < E));
-  const bool valid = lane < k && e >= 0 && e < E;
-  bool use = valid;
-  if (dedup)
-    for (int j = 0; j + 1 < k; ++j) use = use && !(j < lane && __builtin_amdgcn_readlane(e, j) == e);
-  const int g = valid ? e >> 6 : 0;
-  const uint64_t below = valid ? (1ull << (e & 63)) - 1ull : 0ull;
-  int slot = base, total = 0;
-  uint64_t m = 0;
-#pragma unroll
-  for (int i = 0; i < NPER; ++i) {
-    const int c = (int)__builtin_popcountll(M[i]);
-    slot += i < g ? c : 0;
-    m = i == g ? M[i] : m;
-    total += c;
-  }
-  slot += (int)__builtin_popcountll(m & below);
-  if (valid) S.expert[slot] = e;
-  if (use) S.w[slot][t] = w;
-  if (count && lane == 0) {
-    S.n_routed = total;
-    if (base) S.expert[0] = E;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// gate/up: a work item is (slot u, tile t of 16 intermediate rows); slot 0
-// is the shared expert when there is one, and its tiles come first.  One
-// workgroup of 8 wavefronts per CU (the grid is the CU count): it copies the
-// activation fragments and block sums of the input into LDS once (one copy
-// serves all of its items), selects every token's experts (or takes the
-// given routing rows) and builds the slot list, and then takes its items in
-// rounds.  In a round, each item has KP wavefronts
-// that take every KP-th k-group (256 inputs) of it, KP in {1, 2, 4, 8} being
-// the largest that still gives every wavefront of the grid work.  A wavefront
-// keeps the gate and up chunks of two k-groups in flight ahead of the one it
-// multiplies.  The KP partial sums are added in k-part order through LDS; the
-// epilogue divides by the token's rms (stacked layers), forms h = silu(g) * u
-// times the token's gate weight and writes it as fp16 hi/lo A-fragments of
-// the down projection, with the sums of each 16-row tile.
-// Inputs wider than GU_WIN blocks are staged in windows, one after another.
-// ---------------------------------------------------------------------------
-constexpr int GU_NW = 8;    // wavefronts per workgroup
-constexpr int GU_WIN = 96;  // activation blocks staged in LDS at once
-
-struct alignas(16) GuLds {
-  alignas(16) unsigned char xs[GU_WIN * 1024];  // A-fragments, [block][lane][8] fp16
-  alignas(16) float cs[GU_WIN * 16];  // accumulator seeds, [block][16]
-  float red[GU_NW][8][64];          // partial sums of the k-parts
-  float rn[16];                     // 1 / rms of each token
-  int rx[16];                       // exponent ex of each token's activation scaling
-  SlotLds S;
-  uint64_t tk_buf[GU_NW][TOPK_BUF];
-};
-
-template <int BITS>
-struct GroupRegs {
-  ChunkRegs<BITS> g, u;
-};
-
-// Activation blocks [b0, b0 + nblk) of the layer input into LDS as
-// matrix-core A-fragments, with their accumulator seeds.  Thread p takes the
-// entries e = p + 512 i: block b = e / 4R, token row t = (e / 4) % R (the same
-// t for every i), quarter q = e % 4, i.e. inputs 32 (b0 + b) + 8q .. +8 of
-// token t.  They are loaded from xin, and after the selection scaled by 2^-ex
-// of the token (exact: the row's largest magnitude then lies in [2^14, 2^15))
-// and split into an fp16 hi part (A row t) and lo part (row t + 8), or, with
-// fp16 activations (R = 16 tokens), rounded to fp16 (row t).  The four
-// threads of a quad (q = 0..3, one block and token) add up their block sums.
-// Rows of tokens >= T are zeros.
-template <bool A16>
-struct WindowRegs {
-  static constexpr int R = A16 ? MOE_MAX_TOK_F16ACT : MOE_MAX_TOK_DECODE;
-  static constexpr int PER = GU_WIN * 4 * R / (64 * GU_NW);
-  float4_t v[PER][2];
-  int ex;  // exponent of this thread's token (the values are scaled by 2^-ex)
-};
-
-template <bool A16>
-DEVI void window_load(WindowRegs<A16>& W, const GuArgs& a, int b0, int nblk, int tid) {
-  constexpr int R = WindowRegs<A16>::R;
-  const int t = (tid >> 2) % R, q = tid & 3;
-  const bool live = t < a.T;
-  W.ex = live ? a.xexp[t] : 0;
-  const float* src = a.xin + (size_t)(live ? t : 0) * a.d + 32 * b0 + 8 * q;
-#pragma unroll
-  for (int i = 0; i < WindowRegs<A16>::PER; ++i) {
-    const int b = (tid + 64 * GU_NW * i) / (4 * R);
-    W.v[i][0] = W.v[i][1] = float4_t{0.f, 0.f, 0.f, 0.f};
-    if (b < nblk && live) {
-      W.v[i][0] = *reinterpret_cast<const float4_t*>(src + 32 * b);
-      W.v[i][1] = *reinterpret_cast<const float4_t*>(src + 32 * b + 4);
-    }
-  }
-}
-
-template <bool A16>
-DEVI void window_store(const WindowRegs<A16>& W, GuLds& L, int nblk, int code_off, int tid) {
-  constexpr int R = WindowRegs<A16>::R;
-  const int t = (tid >> 2) % R, q = tid & 3;
-  const float off = -(float)code_off;
-#pragma unroll
-  for (int i = 0; i < WindowRegs<A16>::PER; ++i) {
-    const int b = (tid + 64 * GU_NW * i) / (4 * R);
-    if (b >= nblk) continue;  // (the four threads of a quad share b)
-    half8_t h, l;
-    float sh = 0.f, sl = 0.f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const float v = ldexpf(W.v[i][c >> 2][c & 3], -W.ex);  // exact (2^-ex itself may exceed the fp32 range)
-      h[c] = (_Float16)v;
-      sh += (float)h[c];
-      if (!A16) {
-        l[c] = (_Float16)(v - (float)h[c]);
-        sl += (float)l[c];
-      }
-    }
-    sh = quad_sum(sh);
-    *reinterpret_cast<half8_t*>(L.xs + ((size_t)b * 64 + t + 16 * q) * 16) = h;
-    if (q == 0) L.cs[b * 16 + t] = off * sh;
-    if (!A16) {
-      sl = quad_sum(sl);
-      *reinterpret_cast<half8_t*>(L.xs + ((size_t)b * 64 + t + 8 + 16 * q) * 16) = l;
-      if (q == 0) L.cs[b * 16 + t + 8] = off * sl;
-    }
-  }
-}
-
-template <bool A16>
-DEVI void stage_window(GuLds& L, const GuArgs& a, int b0, int nblk, int tid) {
-  WindowRegs<A16> W;
-  window_load<A16>(W, a, b0, nblk, tid);
-  window_store<A16>(W, L, nblk, a.code_off, tid);
-}
-
-template <int BITS>
-DEVI void issue_group(GroupRegs<BITS>& r, const uint8_t* gate, const uint8_t* up, int64_t off, int lane) {
-  load_chunk<BITS>(r.g, gate + off, lane);
-  load_chunk<BITS>(r.u, up + off, lane);
-}
-
-// Eight blocks (one k-group) of gate and up; lb = first block in the window.
-template <int BITS>
-DEVI void mul_group(const GroupRegs<BITS>& r, const GuLds& L, int lb, int lane, float4_t& accg, float4_t& accu) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const half8_t A = *reinterpret_cast<const half8_t*>(L.xs + (size_t)(lb + j) * 1024 + 16 * lane);
-    const float4_t cin = *reinterpret_cast<const float4_t*>(L.cs + (lb + j) * 16 + 4 * (lane >> 4));
-    const float4_t Cg = mfma16x16x32(A, chunk_frag<BITS>(r.g, j), cin);
-    const float4_t Cu = mfma16x16x32(A, chunk_frag<BITS>(r.u, j), cin);
-    accg += chunk_scale(r.g.scales, j) * Cg;
-    accu += chunk_scale(r.u.scales, j) * Cu;
-  }
-}
-
-// k-groups kg0, kg0 + step, ... below kg1 of one 16-row tile (chunk row
-// offset rowoff); the window starts at k-group wkg0.  A three-slot register
-// ring: each step of the main loop issues the k-group two steps ahead (the
-// last k-group again once past the end) and multiplies the oldest one; the
-// main loop has no early exit, so the loads in flight at every multiply are
-// the same and the compiler's wait counts stay exact; a tail of up to two
-// steps multiplies what is already in flight.
-template <int BITS>
-DEVI void run_tile(const uint8_t* gate, const uint8_t* up, int64_t rowoff, int kg0, int kg1, int step, int wkg0,
-                   const GuLds& L, int lane, float4_t& accg, float4_t& accu) {
-  constexpr int64_t CB = BITS == 2 ? 1280 : 1792;
-  if (kg0 >= kg1) return;
-  const int nsteps = (kg1 - 1 - kg0) / step + 1;
-  const int last = kg0 + (nsteps - 1) * step;
-  GroupRegs<BITS> r0, r1, r2;
-  int kg = kg0;
-  issue_group<BITS>(r0, gate, up, rowoff + kg * CB, lane);
-  issue_group<BITS>(r1, gate, up, rowoff + min(kg + step, last) * CB, lane);
-  __builtin_amdgcn_sched_barrier(0);
-  for (int it = nsteps / 3; it > 0; --it) {
-    issue_group<BITS>(r2, gate, up, rowoff + min(kg + 2 * step, last) * CB, lane);
-    __builtin_amdgcn_sched_barrier(0);
-    mul_group<BITS>(r0, L, 8 * (kg - wkg0), lane, accg, accu);
-    kg += step;
-    issue_group<BITS>(r0, gate, up, rowoff + min(kg + 2 * step, last) * CB, lane);
-    __builtin_amdgcn_sched_barrier(0);
-    mul_group<BITS>(r1, L, 8 * (kg - wkg0), lane, accg, accu);
-    kg += step;
-    issue_group<BITS>(r1, gate, up, rowoff + min(kg + 2 * step, last) * CB, lane);
-    __builtin_amdgcn_sched_barrier(0);
-    mul_group<BITS>(r2, L, 8 * (kg - wkg0), lane, accg, accu);
-    kg += step;
-  }
-  const int rem = nsteps % 3;
-  if (rem >= 1) mul_group<BITS>(r0, L, 8 * (kg - wkg0), lane, accg, accu);
-  if (rem == 2) mul_group<BITS>(r1, L, 8 * (kg + step - wkg0), lane, accg, accu);
-}
-
-template <int BITS, int NPER, bool A16>  // NPER >= ceil(E / 64)
+// gate/up: one workgroup of 8 wavefronts per CU (the grid is the CU count);
+// every workgroup selects the experts of every token itself and builds the
+// slot list, workgroup 0 publishes the routing and the slot list.
+template <int BITS, int NPER, bool A16>
 __global__ __launch_bounds__(64 * GU_NW) void gu_decode_kernel(GuArgs a) {
-  constexpr int64_t CB = BITS == 2 ? 1280 : 1792;
   __shared__ GuLds L;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: loop bounds stay scalar
-  const int T = a.T, k = a.k, E = a.E, tk = a.T * a.k;
-  const bool has_shared = a.has_shared != 0;
-  const int base = has_shared ? 1 : 0;
-  const int tiles_r = a.I / 16, tiles_s = has_shared ? a.Is / 16 : 0;
-  const int n_kg = a.n_kg;
-  const int n_win = (8 * n_kg + GU_WIN - 1) / GU_WIN;
-  const int win_kg = (n_kg + n_win - 1) / n_win;  // k-groups per window
-
-  // Selection: wavefront w takes the rows of tokens w and w + 8 (below T) of
-  // the logits.  The loads of its first row (both rows, for rows of up to
-  // 1024 experts), the divisors' and the activation window's share one round
-  // trip.
-  constexpr bool PRE2 = NPER <= 16;
-  const bool select = a.logits != nullptr;
-  float lv[2][NPER];
-  if (select) {
-#pragma unroll
-    for (int h = 0; h < (PRE2 ? 2 : 1); ++h) {
-      const float* row = a.logits + (size_t)min(wv + GU_NW * h, T - 1) * E;
-#pragma unroll
-      for (int i = 0; i < NPER; ++i) lv[h][i] = row[min(lane + 64 * i, E - 1)];
-    }
-  }
-  const float rnv = (tid >= 64 && tid < 64 + T) ? a.rnorm[tid - 64] : 1.0f;
-  const int xev = (tid >= 64 && tid < 64 + T) ? a.xexp[tid - 64] : 0;
-  // the activation window (one window for inputs of up to GU_WIN blocks)
-  // stays in registers through the selection and is stored to LDS before the
-  // barrier that ends it: the selection starts as soon as its logits are in,
-  // while the larger window is still arriving
-  WindowRegs<A16> win;
-  if (n_win == 1) window_load<A16>(win, a, 0, 8 * n_kg, tid);
-  clear_slots(L.S, E, T, base + min(tk, E), has_shared);
-  lds_barrier();  // byte map and weight rows cleared before any wavefront marks (the loads stay in flight)
-  static_assert(2 * GU_NW >= MOE_MAX_TOK_F16ACT, "two tokens per wavefront");
-  TopkLane mine[2] = {{-1, 0.f}, {-1, 0.f}};
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int t = wv + GU_NW * h;
-    if (t < T) {
-      if (select) {
-        if (!PRE2 && h == 1) {
-          const float* row = a.logits + (size_t)t * E;
-#pragma unroll
-          for (int i = 0; i < NPER; ++i) lv[1][i] = row[min(lane + 64 * i, E - 1)];
-        }
-        uint64_t key[NPER];
-#pragma unroll
-        for (int i = 0; i < NPER; ++i) key[i] = (lane + 64 * i < E) ? sel_key(lv[h][i], lane + 64 * i) : 0ull;
-        mine[h] = topk_keys<NPER>(key, E, k, nullptr, nullptr, L.tk_buf[wv]);
-      } else if (lane < k) {
-        mine[h].e = a.idx[t * k + lane];
-        mine[h].w = a.w[t * k + lane];
-      }
-      mark_lane(L.S, mine[h].e, E);
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);  // (the window's stores stay after the selection)
-  if (n_win == 1) window_store<A16>(win, L, 8 * n_kg, a.code_off, tid);
-  if (tid >= 64 && tid < 80) {
-    L.rn[tid - 64] = 1.0f / rnv;
-    L.rx[tid - 64] = xev;
-  }
-  lds_barrier();  // every token's experts marked, the window staged
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int t = wv + GU_NW * h;
-    if (t < T) {
-      place_lane<NPER>(L.S, mine[h].e, mine[h].w, t, k, E, base, !select, t == 0);
-      if (blockIdx.x == 0 && lane < k) {  // the routing used (given rows are copied as they are)
-        if (a.out_idx) a.out_idx[t * k + lane] = mine[h].e;
-        if (a.out_w) a.out_w[t * k + lane] = mine[h].w;
-      }
-    }
-  }
-  lds_barrier();  // slot list, rms and the staged activations
-  if (blockIdx.x == 0) {
-    const int ns = base + L.S.n_routed;
-    if (tid == 0) *a.n_slots = ns;
-    for (int i = tid; i < ns; i += blockDim.x) a.slot_expert[i] = L.S.expert[i];
-    for (int i = tid; i < ns * 16; i += blockDim.x) a.slot_w[i] = L.S.w[i >> 4][i & 15];
-  }
-  const int n_items = tiles_s + L.S.n_routed * tiles_r;
-  int KP = 8;
-  while (KP > 1 && (KP > n_kg || n_items * KP > (int)gridDim.x * GU_NW)) KP >>= 1;
-  const int G = GU_NW / KP, jw = wv / KP, kp = wv - jw * KP;
-  const int tok_e = 4 * ((lane >> 4) & 1);
-
-  for (int grp = blockIdx.x; grp * G < n_items; grp += gridDim.x) {
-    const int item = grp * G + jw;
-    const bool valid = item < n_items;
-    int u = 0, t = 0;
-    const uint8_t* gate = nullptr;
-    const uint8_t* up = nullptr;
-    if (valid) {
-      const uint8_t* ebase;
-      int64_t og, ou;
-      if (item < tiles_s) {
-        t = item;
-        ebase = a.X.shared;
-        og = a.X.sh_off_gate;
-        ou = a.X.sh_off_up;
-      } else {
-        const int ri = item - tiles_s;
-        u = base + ri / tiles_r;
-        t = ri - (ri / tiles_r) * tiles_r;
-        ebase = a.X.experts + (int64_t)L.S.expert[u] * a.X.ex_stride;
-        og = a.X.off_gate;
-        ou = a.X.off_up;
-      }
-      gate = ebase + og;
-      up = ebase + ou;
-    }
-    float4_t accg = float4_t{0.f, 0.f, 0.f, 0.f}, accu = accg;
-    for (int w = 0; w < n_win; ++w) {
-      const int kg0 = w * win_kg, kg1 = min(n_kg, kg0 + win_kg);
-      if (n_win > 1) {
-        __syncthreads();
-        stage_window<A16>(L, a, 8 * kg0, 8 * (kg1 - kg0), tid);
-        __syncthreads();
-      }
-      if (valid) run_tile<BITS>(gate, up, (int64_t)t * n_kg * CB, kg0 + kp, kg1, KP, kg0, L, lane, accg, accu);
-    }
-    if (KP > 1) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        L.red[wv][i][lane] = accg[i];
-        L.red[wv][4 + i][lane] = accu[i];
-      }
-      __syncthreads();
-      if (kp == 0) {
-        for (int p = 1; p < KP; ++p)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            accg[i] += L.red[wv + p][i][lane];
-            accu[i] += L.red[wv + p][4 + i][lane];
-          }
-      }
-    }
-    if (valid && kp == 0) {
-      // lane l: intermediate row n = l & 15 of the tile, C rows 4(l>>4)+i:
-      // tokens tok_e + i, hi part in lanes < 32, lo part in lanes >= 32 (fp16
-      // activations: token 4(l>>4)+i, no lo part).  h is kept in fp32 rows
-      // [slot][token][row] with the largest |h| of each (slot, token) (the
-      // down kernel scales by it before rounding to fp16); maxima of
-      // non-negative floats order like their bit patterns.
-      const int n = lane & 15;
-      const bool writer = A16 || lane < 32;
-      constexpr int R = A16 ? MOE_MAX_TOK_F16ACT : MOE_MAX_TOK_DECODE;
-      float* hrow = a.hbuf + (size_t)u * R * a.hI + 16 * t + n;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = A16 ? 4 * (lane >> 4) + i : tok_e + i;
-        const float gw = (u == 0 && has_shared) ? (tok < T ? 1.0f : 0.f) : L.S.w[u][tok];
-        // the norm's 1 / rms, then 2^ex undoes the activations' scaling (exact)
-        const float rrn = L.rn[tok];
-        const int rx = L.rx[tok];
-        const float g = ldexpf((A16 ? accg[i] : add_partner32(accg[i])) * rrn, rx);
-        const float uu = ldexpf((A16 ? accu[i] : add_partner32(accu[i])) * rrn, rx);
-        const float hv = g * __builtin_amdgcn_rcpf(1.0f + expf(-g)) * uu;
-        const float hs = (gw != 0.f) ? gw * hv : 0.f;
-        if (writer) hrow[(size_t)tok * a.hI] = hs;
-        const float m = row16_max(fabsf(hs));
-        if (writer && n == 0)
-          __hip_atomic_fetch_max(a.hmax + u * 16 + tok, __float_as_uint(m), __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-    if (KP > 1) __syncthreads();  // red is rewritten in the next round
-  }
+  gu_select<BITS, NPER, A16>(a, L, blockIdx.x == 0, blockIdx.x == 0);
+  gu_items<BITS, A16>(a, L, blockIdx.x, gridDim.x, nullptr);
 }
 
-// ---------------------------------------------------------------------------
-// down: workgroup = (row group rg of 16*RT output rows, split s).  It sums,
-// for every slot u = s, s+S, ... of the slot list, the down projection of the
-// gate-weighted h, so the
-// combine across experts happens in the accumulators.  Items (slot, k-group)
-// go to the waves in batches of two; a batch's weight chunks and activation
-// fragments are all loaded before its first multiply.  Waves reduce through
-// LDS in a fixed order and the split's partial result is written to
-// ypart[s]; the consumer adds the S splits in split order, so the output does
-// not depend on timing.
-// ---------------------------------------------------------------------------
-// A-fragment of one block of slot u's intermediate h (fp32 rows
-// [slot][token][row]): lane L = m + 16q holds inputs 8q..8q+7 of row m, i.e.
-// token m & 7, its fp16 hi part for m < 8 and lo part for m >= 8 (fp16
-// activations: token m, rounded to fp16), after scaling by the power of two
-// 2^-eh that puts the largest |h| of the (slot, token) in [2^14, 2^15).
-template <bool A16>
-DEVI half8_t h_fragment(const float4_t (&v)[2], int eh, int lane) {
-  const bool lo = !A16 && (lane & 8);
-  half8_t h;
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const float x = ldexpf(v[c >> 2][c & 3], -eh);  // exact (2^-eh itself may exceed the fp32 range)
-    const _Float16 hi = (_Float16)x;
-    h[c] = lo ? (_Float16)(x - (float)hi) : hi;
-  }
-  return h;
-}
-
+// down: workgroup = (row group, split), the slot list from the workspace.
 template <int BITS, int RT, bool A16>
 __global__ __launch_bounds__(512) void down_decode_kernel(DownArgs a) {
-  constexpr int CB = BITS == 2 ? 1280 : 1792;
-  constexpr int BK = 8 / RT;
-  constexpr int BATCH = 2;
-  constexpr int R = A16 ? MOE_MAX_TOK_F16ACT : MOE_MAX_TOK_DECODE;
-  __shared__ float red[8][RT * 4][64];
-  const int rg = blockIdx.x, sp = blockIdx.y;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  const int ns = *a.n_slots;
-  const int S = a.S;
-  // slots of this split: sp, sp + S, ...; slot 0 is the shared expert when
-  // there is one (split 0 then starts with its k-groups)
-  const bool sh_here = a.has_shared && sp == 0;
-  const int first_r = sh_here ? S : sp;  // first routed slot of the split
-  const int n_sh = sh_here ? a.n_kg_s : 0;
-  // expert ids of this wave's first batch, fetched together with n_slots
-  // (the slot of an item does not depend on n_slots; ids past the list are
-  // clamped to a valid expert and never used)
-  // (two named registers: an array here was kept in scratch memory, and its
-  // store waited for the loads)
-  static_assert(BATCH == 2, "two prefetched ids");
-  int pre0, pre1;
-  {
-    const int it0 = wv, it1 = wv + nw;
-    const int u0 = (it0 < n_sh) ? 0 : first_r + S * ((it0 - n_sh) / a.n_kg_r);
-    const int u1 = (it1 < n_sh) ? 0 : first_r + S * ((it1 - n_sh) / a.n_kg_r);
-    pre0 = a.slot_expert[min(u0, a.max_slots - 1)];
-    pre1 = a.slot_expert[min(u1, a.max_slots - 1)];
-  }
-  const int n_rs = (first_r < ns) ? (ns - first_r + S - 1) / S : 0;
-  const int n_items = n_sh + n_rs * a.n_kg_r;
-
-  float4_t acc[RT];
-#pragma unroll
-  for (int t = 0; t < RT; ++t) acc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-  // this lane's A-fragment token, and the token of its accumulator rows
-  // 4 (lane >> 4) + i (hi/lo: the lo rows 8..15 are tokens 0..7 again)
-  const int tok_a = A16 ? (lane & 15) : (lane & 7);
-  const int tok_c = A16 ? 4 * (lane >> 4) : (4 * (lane >> 4)) & 7;
-  const float off = -(float)(1 << (BITS - 1));
-  const half8_t ones = half8_t{1, 1, 1, 1, 1, 1, 1, 1};
-
-  for (int b0 = wv; b0 < n_items; b0 += nw * BATCH) {
-    ChunkRegs<BITS> c[BATCH];
-    float4_t hv[BATCH][BK][2];
-    uint32_t hm_a[BATCH];
-    u32x4_t hm_c[BATCH];
-    bool ok[BATCH];
-#pragma unroll
-    for (int q = 0; q < BATCH; ++q) {
-      const int it = b0 + q * nw;
-      ok[q] = it < n_items;
-      const int itc = ok[q] ? it : b0;  // keep every address valid
-      int u, kg, n_kg;
-      const uint8_t* mat;
-      if (itc < n_sh) {
-        u = 0;
-        kg = itc;
-        n_kg = a.n_kg_s;
-        mat = a.X.shared + a.X.sh_off_down;
-      } else {
-        const int ri = itc - n_sh;
-        u = first_r + S * (ri / a.n_kg_r);
-        kg = ri % a.n_kg_r;
-        n_kg = a.n_kg_r;
-        int e = (b0 == wv) ? ((ok[q] && q == 1) ? pre1 : pre0) : a.slot_expert[u];
-        e = min(max(e, 0), a.E - 1);
-        mat = a.X.experts + (int64_t)e * a.X.ex_stride + a.X.off_down;
-      }
-      load_chunk<BITS>(c[q], mat + ((int64_t)rg * n_kg + kg) * CB, lane);
-      const float* hr = a.hbuf + ((size_t)u * R + tok_a) * a.hI + 32 * (kg * BK) + 8 * (lane >> 4);
-#pragma unroll
-      for (int j = 0; j < BK; ++j) {
-        hv[q][j][0] = *reinterpret_cast<const float4_t*>(hr + 32 * j);
-        hv[q][j][1] = *reinterpret_cast<const float4_t*>(hr + 32 * j + 4);
-      }
-      hm_a[q] = a.hmax[u * 16 + tok_a];
-      hm_c[q] = *reinterpret_cast<const u32x4_t*>(a.hmax + u * 16 + tok_c);
-    }
-#pragma unroll
-    for (int q = 0; q < BATCH; ++q) {
-      if (!ok[q]) continue;
-      const int eh_a = fp16_exponent_for(__uint_as_float(hm_a[q]));
-      float4_t part[RT];
-#pragma unroll
-      for (int t = 0; t < RT; ++t) part[t] = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < BK; ++j) {
-        const half8_t A = h_fragment<A16>(hv[q][j], eh_a, lane);
-        // the accumulator seed -2^(b-1) sum_k A[m][k], with the row sums laid
-        // out as the accumulators by a product with an all-ones B operand
-        const float4_t cin = off * mfma16x16x32(A, ones, float4_t{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-        for (int t = 0; t < RT; ++t) {
-          const int f = t * BK + j;
-          const float4_t C = mfma16x16x32(A, chunk_frag<BITS>(c[q], f), cin);
-          part[t] += chunk_scale(c[q].scales, f) * C;
-        }
-      }
-      // undo the (slot, token) scaling of this item's rows: 2^eh, exact
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int eh = fp16_exponent_for(__uint_as_float(hm_c[q][i]));
-#pragma unroll
-        for (int t = 0; t < RT; ++t) acc[t][i] += ldexpf(part[t][i], eh);
-      }
-    }
-  }
-
-#pragma unroll
-  for (int t = 0; t < RT; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) red[wv][t * 4 + i][lane] = acc[t][i];
-  __syncthreads();
-  if (wv != 0) return;
-  const int T = a.T, d = a.d, n = lane & 15;
-#pragma unroll
-  for (int t = 0; t < RT; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float part[8];
-#pragma unroll
-      for (int w = 0; w < 8; ++w) part[w] = red[w < nw ? w : 0][t * 4 + i][lane];
-      float s = part[0];
-#pragma unroll
-      for (int w = 1; w < 8; ++w)
-        if (w < nw) s += part[w];
-      if (!A16) s = add_partner32(s);  // (fp16 activations: C row = token, 16 tokens)
-      const int tok = 4 * (lane >> 4) + i;  // (hi/lo: lanes < 32 hold tokens 0..7)
-      const int o = rg * 16 * RT + 16 * t + n;
-      if ((A16 || lane < 32) && tok < T) a.ypart[((size_t)sp * R + tok) * d + o] = s;
-    }
+  __shared__ float red[8 * RT * 4 * 64];
+  down_role<BITS, RT, A16>(a, blockIdx.x, blockIdx.y, *a.n_slots, a.slot_expert, red);
 }
 
 // ---------------------------------------------------------------------------

@@ -13,6 +13,17 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 #define DEVI __device__ __forceinline__
 
+// The work-item index as a value the optimiser cannot see through.  Phase
+// functions derive their per-lane addresses from it, so in a kernel that runs
+// the phases in a loop (the persistent decode pass) those addresses are
+// recomputed inside each phase instead of being hoisted out of the loop and
+// kept live (or spilled) across every other phase.
+DEVI int opaque_tid() {
+  int t = (int)threadIdx.x;
+  __asm__ volatile("" : "+v"(t));
+  return t;
+}
+
 // ---------------------------------------------------------------------------
 // Fragment decode.
 //
@@ -64,6 +75,81 @@ DEVI u32x4_t ld128_nt(const void* p) {
 }
 DEVI u32x2_t ld64_nt(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+}
+
+// ---------------------------------------------------------------------------
+// Device-coherent accesses: values that workgroups hand to each other inside
+// one kernel (or that another XCD's workgroup wrote) are stored and loaded
+// with the sc1 cache policy, as agent-scope atomics are, so no XCD's L2 serves
+// a stale copy and no cache write-back or invalidation is needed.  The
+// 16-byte forms go through a raw buffer resource (offsets in bytes; an access
+// past 2^31 - 1 bytes of the base reads zero instead of faulting).
+// ---------------------------------------------------------------------------
+DEVI void st_dev(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+DEVI float ld_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+DEVI void st_dev_i(int32_t* p, int32_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+DEVI int32_t ld_dev_i(const int32_t* p) {
+  return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+DEVI void st_dev_u(uint32_t* p, uint32_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+DEVI uint32_t ld_dev_u(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+DEVI __amdgpu_buffer_rsrc_t coh_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+}
+constexpr int kCohSc1 = 16;  // cache-policy operand of the buffer intrinsics: sc1
+DEVI float4_t coh_ld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCohSc1));
+}
+DEVI u32x4_t coh_ld4u(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCohSc1));
+}
+DEVI void coh_st4(__amdgpu_buffer_rsrc_t r, uint32_t off, const float4_t& v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off, 0, kCohSc1);
+}
+
+// Adds one to a counter other workgroups wait on (after the caller has made
+// its own stores complete).
+DEVI void signal_add(uint32_t* ctr, uint32_t n = 1u) {
+  __hip_atomic_fetch_add(ctr, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Workgroup-wide bounded wait until *ctr >= target: thread 0 polls, the
+// others wait at the barrier.  Gives up (false in every thread) once the
+// kernel's abort word is set by another workgroup, or after kSpinLimit polls
+// (then it sets the abort word itself), so every wait ends and a pass whose
+// workgroups cannot all make progress finishes early instead of hanging.
+// `flag` is a workgroup-shared int.
+constexpr uint32_t kSpinLimit = 1u << 21;
+DEVI bool wg_wait(const uint32_t* ctr, uint32_t target, uint32_t* abort_w, int* flag) {
+  if (threadIdx.x == 0) {
+    int ok = 1;
+    uint32_t n = 0;
+    while (ld_dev_u(ctr) < target) {
+      ++n;
+      if ((n & 31u) == 0u && ld_dev_u(abort_w) != 0u) {
+        ok = 0;
+        break;
+      }
+      if (n > kSpinLimit) {
+        st_dev_u(abort_w, 1u);
+        ok = 0;
+        break;
+      }
+      // a short pause between polls: many workgroups poll one line
+      if (n < 8) __builtin_amdgcn_s_sleep(2);
+      else __builtin_amdgcn_s_sleep(8);
+    }
+    *flag = ok;
+  }
+  __syncthreads();
+  const bool ok = *flag != 0;
+  __syncthreads();  // every thread has read the flag before it is reused
+  return ok;
 }
 
 DEVI float half_bits_to_float(uint32_t h16) {

@@ -62,6 +62,19 @@ int cu_count() {
   return cached[dev];
 }
 
+// Workgroups of a persistent pass: one per CU, all resident at once (the
+// kernel's waits need every workgroup running); 0 if the kernel cannot hold
+// one workgroup per CU on this device.
+int persist_grid() {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  std::lock_guard<std::mutex> lk(mu);
+  if (cached[dev] == 0) cached[dev] = persist_blocks_per_cu() >= 1 ? cu_count() : -1;
+  return cached[dev] > 0 ? cached[dev] : 0;
+}
+
 std::once_flag g_init_once;
 hipError_t g_init_err = hipSuccess;
 void init_kernels() {
@@ -155,7 +168,14 @@ struct WsLayout {
   int max_slots, S, nbI, n_cs;
 };
 
-int64_t ctrl_bytes() { return MOE_CTRL_WORDS * 4; }
+// control region: the per-phase route kernel's counters (MOE_CTRL_WORDS
+// words), then the persistent pass's abort word at byte 256
+int64_t ctrl_bytes() { return 512; }
+
+// Row stride of the workspace logits: E rounded up to 64, so the 64 logits a
+// row slice finishes fill cache lines no other workgroup writes.
+int logits_row(int E) { return (E + 63) / 64 * 64; }
+constexpr int64_t kStatusOffset = 256;
 
 int down_splits(const moe_layer* L, int max_slots) {
   const int n_rg = L->ex.down.n_rg;
@@ -191,7 +211,7 @@ WsLayout ws_layout_decode(const moe_layer* L, int T, bool act16 = false) {
   W.mx_part = take((int64_t)W.n_cs * 16 * 4);
   W.rnorm = take(16 * 4);
   W.xexp = take(16 * 4);
-  W.logits = take((int64_t)T * E * 4);
+  W.logits = take((int64_t)T * logits_row(E) * 4);
   W.n_slots = take(4);
   W.slot_expert = take((int64_t)W.max_slots * 4);
   W.slot_w = take((int64_t)W.max_slots * 16 * 4);
@@ -200,6 +220,64 @@ WsLayout ws_layout_decode(const moe_layer* L, int T, bool act16 = false) {
   W.hbuf = take((int64_t)W.max_slots * R * W.nbI * 32 * 4);
   W.hmax = take((int64_t)W.max_slots * 16 * 4);
   W.total = o;
+  return W;
+}
+
+// Persistent decode pass of T tokens over up to n layers per launch
+// (persist.hip): the router's partial results, each layer's own copies of the
+// buffers the router step hands to the gate/up step and of h, and per-layer
+// maxima and counters (cleared together before each launch).  The down
+// partials sit where the per-phase layout has them.
+struct PsLayout {
+  int64_t ctrl, ypart, lp, ss_part, mx_part, rnorm, xexp, logits, xin, hbuf, hmax, ctl, total;
+  int64_t logits_stride, xin_stride, hbuf_stride;  // floats per layer
+  int max_slots, S, n_rs, n_cs, cpl, hI;
+  size_t clear_words;  // hmax and ctl
+};
+
+int persist_grid();  // workgroups of a persistent pass (0: not available)
+
+int persist_splits(const moe_layer* L, int max_slots) {
+  int S = persist_grid() / L->ex.down.n_rg;
+  if (S > max_slots) S = max_slots;
+  if (S > MOE_MAX_IN_SPLITS) S = MOE_MAX_IN_SPLITS;
+  if (S < 1) S = 1;
+  return S;
+}
+
+PsLayout ws_layout_persist(const moe_layer* L, int T, bool act16, int n_layers) {
+  PsLayout W{};
+  const int n = n_layers < MOE_PERSIST_MAX_LAYERS ? (n_layers < 1 ? 1 : n_layers) : MOE_PERSIST_MAX_LAYERS;
+  const int R = act16 ? MOE_MAX_TOK_F16ACT : MOE_MAX_TOK_DECODE;
+  const int k = L->k, E = L->E, d = L->d;
+  W.max_slots = (T * k < E ? T * k : E) + (L->Is > 0 ? 1 : 0);
+  W.hI = ((L->I > L->Is ? L->I : L->Is) / 32) * 32;
+  W.S = persist_splits(L, W.max_slots);
+  W.n_cs = d / MOE_ROUTE_COLS;
+  W.n_rs = (E + MOE_ROUTE_ROWS - 1) / MOE_ROUTE_ROWS;
+  W.cpl = (W.n_rs + 1 + W.n_cs + W.max_slots) * MOE_CTR_STRIDE;
+  W.logits_stride = moe_align256((int64_t)T * logits_row(E) * 4) / 4;
+  W.xin_stride = moe_align256((int64_t)MOE_MAX_TOK_F16ACT * d * 4) / 4;
+  W.hbuf_stride = moe_align256((int64_t)W.max_slots * R * W.hI * 4) / 4;
+  int64_t o = 0;
+  auto take = [&](int64_t bytes) { int64_t r = o; o += moe_align256(bytes); return r; };
+  W.ctrl = take(ctrl_bytes());
+  W.ypart = take((int64_t)MOE_MAX_IN_SPLITS * MOE_MAX_TOK_F16ACT * d * 4);
+  W.lp = take((int64_t)W.n_cs * T * E * 4);
+  W.ss_part = take((int64_t)W.n_rs * W.n_cs * T * 4);
+  W.mx_part = take((int64_t)W.n_cs * 16 * 4);
+  W.rnorm = take((int64_t)n * MOE_PERSIST_TOK_STRIDE * 4);
+  W.xexp = take((int64_t)n * MOE_PERSIST_TOK_STRIDE * 4);
+  W.logits = take((int64_t)n * W.logits_stride * 4);
+  W.xin = take((int64_t)n * W.xin_stride * 4);
+  W.hbuf = take((int64_t)n * W.hbuf_stride * 4);
+  const int64_t hmax_bytes = (int64_t)n * W.max_slots * 16 * 4;
+  const int64_t ctl_bytes = (int64_t)n * W.cpl * 4;
+  W.hmax = o;
+  W.ctl = o + hmax_bytes;
+  o += moe_align256(hmax_bytes + ctl_bytes);
+  W.total = o;
+  W.clear_words = (size_t)(hmax_bytes + ctl_bytes) / 4;
   return W;
 }
 
@@ -365,7 +443,9 @@ int decode_layer(const moe_layer* L, const LayerInput& in, float eps, int T, flo
   sa.norm = in.norm;
   sa.eps = eps;
   sa.ctrl = reinterpret_cast<uint32_t*>(ws + W.ctrl);
+  sa.ctrl_stride = 1;
   sa.logits = reinterpret_cast<float*>(ws + W.logits);
+  sa.logits_stride = logits_row(E);
   sa.rnorm = reinterpret_cast<float*>(ws + W.rnorm);
   sa.out_logits = (r && !forced) ? r->out_logits : nullptr;
   timed_begin(2, s, &slot);
@@ -377,6 +457,7 @@ int decode_layer(const moe_layer* L, const LayerInput& in, float eps, int T, flo
   GuArgs ga{};
   ga.X = X;
   ga.logits = forced ? nullptr : sa.logits;
+  ga.logits_stride = sa.logits_stride;
   ga.idx = forced ? r->in_idx : nullptr;
   ga.w = forced ? r->in_w : nullptr;
   ga.out_idx = r ? r->out_idx : nullptr;
@@ -574,8 +655,22 @@ int prefill_layer(const moe_layer* L, const float* x, int norm, float eps, int T
   return MOE_OK;
 }
 
-int check_ws(const moe_layer* L, int T, void* ws, size_t ws_bytes, size_t* need) {
-  if (moe_workspace_bytes(L, T, need) != MOE_OK) return MOE_ERR_ARG;
+// Workspace for calls of up to T tokens through n layers at a time (the
+// persistent pass keeps per-layer buffers for up to MOE_PERSIST_MAX_LAYERS).
+size_t ws_need(const moe_layer* L, int T, int n_layers) {
+  const int Tw = T < 1 ? 1 : T;
+  // the decode layouts (8 tokens with fp16 hi + lo activations, 16 with fp16
+  // activations) and, above 8 tokens, the prefill layout
+  const int t8 = Tw < MOE_MAX_TOK_DECODE ? Tw : MOE_MAX_TOK_DECODE, t16 = Tw < MOE_MAX_TOK_F16ACT ? Tw : MOE_MAX_TOK_F16ACT;
+  size_t dec = std::max((size_t)ws_layout_decode(L, t8).total, (size_t)ws_layout_decode(L, t16, true).total);
+  dec = std::max(dec, (size_t)std::max(ws_layout_persist(L, t8, false, n_layers).total,
+                                       ws_layout_persist(L, t16, true, n_layers).total));
+  return T > MOE_MAX_TOK_DECODE ? std::max(dec, (size_t)ws_layout_prefill(L, T).total) : dec;
+}
+
+int check_ws(const moe_layer* L, int T, int n_layers, void* ws, size_t ws_bytes, size_t* need) {
+  if (T > MOE_MAX_TOK_PREFILL) return fail(MOE_ERR_UNSUPPORTED, "T above %d not supported", MOE_MAX_TOK_PREFILL);
+  *need = ws_need(L, T, n_layers);
   if (!ws) return fail(MOE_ERR_ARG, "workspace is NULL");
   if (!aligned(ws, 256)) return fail(MOE_ERR_ARG, "workspace must be 256-byte aligned");
   if (ws_bytes < *need) return fail(MOE_ERR_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes, *need);
@@ -764,12 +859,15 @@ int moe_workspace_bytes(const moe_layer* L, int T, size_t* bytes) {
   if (!L || !bytes) return fail(MOE_ERR_ARG, "NULL argument");
   if (T < 0) return fail(MOE_ERR_ARG, "T must be >= 0");
   if (T > MOE_MAX_TOK_PREFILL) return fail(MOE_ERR_UNSUPPORTED, "T above %d not supported", MOE_MAX_TOK_PREFILL);
-  const int Tw = T < 1 ? 1 : T;
-  // the decode layouts (8 tokens with fp16 hi + lo activations, 16 with fp16
-  // activations) and, above 8 tokens, the prefill layout
-  const size_t dec = std::max((size_t)ws_layout_decode(L, Tw < MOE_MAX_TOK_DECODE ? Tw : MOE_MAX_TOK_DECODE).total,
-                              (size_t)ws_layout_decode(L, Tw < MOE_MAX_TOK_F16ACT ? Tw : MOE_MAX_TOK_F16ACT, true).total);
-  *bytes = T > MOE_MAX_TOK_DECODE ? std::max(dec, (size_t)ws_layout_prefill(L, T).total) : dec;
+  *bytes = ws_need(L, T, MOE_PERSIST_MAX_LAYERS);
+  return MOE_OK;
+}
+
+int moe_layer_workspace_bytes(const moe_layer* L, int T, size_t* bytes) {
+  if (!L || !bytes) return fail(MOE_ERR_ARG, "NULL argument");
+  if (T < 0) return fail(MOE_ERR_ARG, "T must be >= 0");
+  if (T > MOE_MAX_TOK_PREFILL) return fail(MOE_ERR_UNSUPPORTED, "T above %d not supported", MOE_MAX_TOK_PREFILL);
+  *bytes = ws_need(L, T, 1);
   return MOE_OK;
 }
 
@@ -798,7 +896,7 @@ static int layer_args(const moe_layer* L, const float* x, int T, float* y, const
   if (route && ((route->in_idx == nullptr) != (route->in_w == nullptr)))
     return fail(MOE_ERR_ARG, "in_idx and in_w must be given together");
   size_t need;
-  int rc = check_ws(L, T, ws, ws_bytes, &need);
+  int rc = check_ws(L, T, 1, ws, ws_bytes, &need);
   if (rc) return rc;
   init_kernels();
   if (g_init_err != hipSuccess) return fail(MOE_ERR_HIP, "kernel init: %s", hipGetErrorString(g_init_err));
@@ -806,8 +904,120 @@ static int layer_args(const moe_layer* L, const float* x, int T, float* y, const
 }
 
 // One decode pass of T tokens and the combine of the down splits into y.
+// The persistent pass applies to layers of one shape with at most 1024
+// experts; it runs where MOE_PERSIST=1 is set in the environment (the
+// per-phase kernels are the default: they measure faster on the 48-layer,
+// 8-token stack).
+static bool persist_usable(const moe_layer* const* layers, int n_layers) {
+  if (env_int("MOE_PERSIST", 0) == 0 || persist_grid() <= 0) return false;
+  const moe_layer* L = layers[0];
+  if (!persist_supported(L->E, L->bits)) return false;
+  for (int l = 1; l < n_layers; ++l) {
+    const moe_layer* M = layers[l];
+    if (M->d != L->d || M->E != L->E || M->I != L->I || M->Is != L->Is || M->k != L->k || M->bits != L->bits)
+      return false;
+  }
+  return true;
+}
+
+// One decode pass of T tokens through layers[0..n) by the persistent kernel,
+// in launches of up to MOE_PERSIST_MAX_LAYERS layers (a later launch takes the
+// previous one's split partials as its input).  x, y point at the pass's first
+// row; layer l's output goes to y_layers + l * yl_stride, its routing to
+// idx_layers / w_layers + l * route_stride.  r: one-layer routing input and
+// outputs (n_layers == 1), or null.
+static int persist_pass(const moe_layer* const* layers, int n_layers, const float* x, int T, float eps, float* y,
+                        float* y_layers, int64_t yl_stride, int32_t* idx_layers, float* w_layers, int64_t route_stride,
+                        const moe_route_io* r, uint8_t* ws, hipStream_t s, bool act16) {
+  const moe_layer* L = layers[0];
+  const PsLayout W = ws_layout_persist(L, T, act16, n_layers);
+  const int R = act16 ? MOE_MAX_TOK_F16ACT : MOE_MAX_TOK_DECODE;
+  const int d = L->d;
+  PersistArgs P{};
+  P.off_wh = reinterpret_cast<const uint8_t*>(L->router_wh) - L->packed;
+  P.off_wl = reinterpret_cast<const uint8_t*>(L->router_wl) - L->packed;
+  P.off_ew = reinterpret_cast<const uint8_t*>(L->router_ew) - L->packed;
+  P.off_br = reinterpret_cast<const uint8_t*>(L->router_b) - L->packed;
+  P.off_ex = L->experts - L->packed;
+  P.off_sh = L->Is > 0 ? L->shared - L->packed : 0;
+  P.ex_stride = L->ex.bytes;
+  P.off_gate = L->ex.off_gate;
+  P.off_up = L->ex.off_up;
+  P.off_down = L->ex.off_down;
+  P.sh_off_gate = L->sh.off_gate;
+  P.sh_off_up = L->sh.off_up;
+  P.sh_off_down = L->sh.off_down;
+  P.T = T;
+  P.d = d;
+  P.E = L->E;
+  P.k = L->k;
+  P.I = L->I;
+  P.Is = L->Is;
+  P.bits = L->bits;
+  P.has_shared = L->Is > 0;
+  P.code_off = 1 << (L->bits - 1);
+  P.n_cs = W.n_cs;
+  P.n_rs = W.n_rs;
+  P.S = W.S;
+  P.n_rg = L->ex.down.n_rg;
+  P.n_kg_r = L->ex.down.n_kg;
+  P.n_kg_s = L->Is > 0 ? L->sh.down.n_kg : 0;
+  P.max_slots = W.max_slots;
+  P.hI = W.hI;
+  P.cpl = W.cpl;
+  P.eps = eps;
+  P.yl_stride = yl_stride;
+  P.route_stride = route_stride;
+  const bool forced = r && r->in_idx && r->in_w;
+  P.out_logits = (r && !forced) ? r->out_logits : nullptr;
+  P.in_idx = forced ? r->in_idx : nullptr;
+  P.in_w = forced ? r->in_w : nullptr;
+  P.lp = reinterpret_cast<float*>(ws + W.lp);
+  P.ss_part = reinterpret_cast<float*>(ws + W.ss_part);
+  P.mx_part = reinterpret_cast<float*>(ws + W.mx_part);
+  P.rnorm = reinterpret_cast<float*>(ws + W.rnorm);
+  P.xexp = reinterpret_cast<int32_t*>(ws + W.xexp);
+  P.logits = reinterpret_cast<float*>(ws + W.logits);
+  P.xin = reinterpret_cast<float*>(ws + W.xin);
+  P.hbuf = reinterpret_cast<float*>(ws + W.hbuf);
+  P.logits_stride = W.logits_stride;
+  P.logits_row = logits_row(L->E);
+  P.xin_stride = W.xin_stride;
+  P.hbuf_stride = W.hbuf_stride;
+  P.hmax = reinterpret_cast<uint32_t*>(ws + W.hmax);
+  P.ctl = reinterpret_cast<uint32_t*>(ws + W.ctl);
+  P.ypart = reinterpret_cast<float*>(ws + W.ypart);
+  P.status = reinterpret_cast<uint32_t*>(ws + W.ctrl + kStatusOffset);
+  const size_t clear_words = W.clear_words;
+  for (int l0 = 0; l0 < n_layers; l0 += MOE_PERSIST_MAX_LAYERS) {
+    const int nl = n_layers - l0 < MOE_PERSIST_MAX_LAYERS ? n_layers - l0 : MOE_PERSIST_MAX_LAYERS;
+    P.n_layers = nl;
+    for (int i = 0; i < nl; ++i) P.base[i] = layers[l0 + i]->packed;
+    P.in = l0 == 0 ? x : P.ypart;
+    P.S_in = l0 == 0 ? 1 : W.S;
+    P.in_stride = l0 == 0 ? 0 : (int64_t)R * d;
+    P.norm0 = l0 > 0;
+    P.y = l0 + nl == n_layers ? y : nullptr;
+    P.y_prev_out = (l0 > 0 && y_layers) ? y_layers + (size_t)(l0 - 1) * yl_stride : nullptr;
+    P.y_layers = y_layers ? y_layers + (size_t)l0 * yl_stride : nullptr;
+    P.idx_layers = idx_layers ? idx_layers + (size_t)l0 * route_stride : nullptr;
+    P.w_layers = w_layers ? w_layers + (size_t)l0 * route_stride : nullptr;
+    int slot;
+    timed_begin(6, s, &slot);
+    serial_point(s);
+    HIPCHK(launch_persist(P, L->ex.down.RT, persist_grid(), act16, clear_words, s));
+    timed_end(slot, s);
+  }
+  return MOE_OK;
+}
+
 static int decode_layer_out(const moe_layer* L, const float* x, int T, float* y, const moe_route_io* route,
                             uint8_t* wsb, hipStream_t st, bool act16) {
+  if (persist_usable(&L, 1)) {
+    int32_t* oi = route ? route->out_idx : nullptr;
+    float* ow = route ? route->out_w : nullptr;
+    return persist_pass(&L, 1, x, T, 0.f, y, nullptr, 0, oi, ow, 0, route, wsb, st, act16);
+  }
   int S = 1;
   int rc = decode_layer(L, LayerInput{x, 1, 0, 0}, 0.f, T, nullptr, route, wsb, st, &S, act16);
   if (rc) return rc;
@@ -867,7 +1077,7 @@ static int stack_args(const moe_layer* const* layers, int n_layers, const float*
     if (!layers[l]) return fail(MOE_ERR_ARG, "layer %d is NULL", l);
     if (layers[l]->d != d) return fail(MOE_ERR_ARG, "layer %d has d_model %d, expected %d", l, layers[l]->d, d);
     size_t need;
-    int rc = check_ws(layers[l], T, ws, ws_bytes, &need);
+    int rc = check_ws(layers[l], T, n_layers, ws, ws_bytes, &need);
     if (rc) return rc;
   }
   init_kernels();
@@ -883,6 +1093,18 @@ static int decode_stack(const moe_layer* const* layers, int n_layers, const floa
                         bool act16) {
   const int d = layers[0]->d;
   const int chunk = act16 ? MOE_MAX_TOK_F16ACT : MOE_MAX_TOK_DECODE;
+  if (persist_usable(layers, n_layers)) {
+    const int k = layers[0]->k;
+    for (int c0 = 0; c0 < T; c0 += chunk) {
+      const int Tc = T - c0 < chunk ? T - c0 : chunk;
+      int rc = persist_pass(layers, n_layers, x + (size_t)c0 * d, Tc, eps, y + (size_t)c0 * d,
+                            y_layers ? y_layers + (size_t)c0 * d : nullptr, (int64_t)T * d,
+                            idx_layers ? idx_layers + (size_t)c0 * k : nullptr,
+                            w_layers ? w_layers + (size_t)c0 * k : nullptr, (int64_t)T * k, nullptr, wsb, s, act16);
+      if (rc) return rc;
+    }
+    return MOE_OK;
+  }
   for (int c0 = 0; c0 < T; c0 += chunk) {
     const int Tc = T - c0 < chunk ? T - c0 : chunk;
     LayerInput in{x + (size_t)c0 * d, 1, 0, 0};
@@ -1051,8 +1273,19 @@ int moe_debug_unpack_path(const moe_layer* L, int expert, int mat, int path, int
   return MOE_OK;
 }
 
+int moe_workspace_status(const void* ws, size_t ws_bytes, int* status, void* stream) {
+  if (!ws || !status || !aligned(ws, 256)) return fail(MOE_ERR_ARG, "workspace and status must be non-NULL (workspace 256-byte aligned)");
+  if (ws_bytes < (size_t)ctrl_bytes()) return fail(MOE_ERR_WORKSPACE, "workspace too small");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint32_t v = 0;
+  HIPCHK(hipMemcpyAsync(&v, reinterpret_cast<const uint8_t*>(ws) + kStatusOffset, 4, hipMemcpyDeviceToHost, s));
+  HIPCHK(hipStreamSynchronize(s));
+  *status = v ? 1 : 0;
+  return MOE_OK;
+}
+
 int moe_timing_start(int kernel_class, int max_launches) {
-  if (kernel_class < 0 || kernel_class > 5 || max_launches < 1) return fail(MOE_ERR_ARG, "bad timing arguments");
+  if (kernel_class < 0 || kernel_class > 6 || max_launches < 1) return fail(MOE_ERR_ARG, "bad timing arguments");
   std::lock_guard<std::mutex> lk(g_timing.mu);
   for (hipEvent_t e : g_timing.ev) hipEventDestroy(e);
   g_timing.ev.assign(2 * (size_t)max_launches, nullptr);

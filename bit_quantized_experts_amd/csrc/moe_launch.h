@@ -33,7 +33,10 @@ struct SelectArgs {
   int32_t n_cs, n_rs, T, d, E, norm;
   float eps;
   uint32_t* ctrl;      // completion counters, one per row slice; zero between calls
-  float* logits;       // ws [T][E]
+  int32_t ctrl_stride; // words between two of them
+  float* logits;       // ws [T][logits_stride]
+  int32_t logits_stride;  // floats per token row: E rounded up to a multiple of 64 (a row
+                          // slice's 64 logits fill whole lines of their own)
   float* rnorm;        // ws [16]: per-token divisor (1 when norm == 0)
   float* out_logits;   // optional copy of the logits
 };
@@ -68,7 +71,8 @@ struct ExpertSet {
 // workgroup from the routing; workgroup 0 publishes it for the down kernel.
 struct GuArgs {
   ExpertSet X;
-  const float* logits;  // [T][E]: every workgroup selects the top k itself; or null:
+  const float* logits;  // [T][logits_stride]: every workgroup selects the top k itself; or null:
+  int32_t logits_stride;
   const int32_t* idx;   // [T][k] forced routing (ids out of range are skipped)
   const float* w;       // [T][k]
   int32_t* out_idx;     // optional: the selection ([T][k], written by workgroup 0)
@@ -80,7 +84,7 @@ struct GuArgs {
   const float* rnorm;
   const float* xin;      // [16][d] layer input rows (before the RMSNorm of stacked layers)
   const int32_t* xexp;   // [16] row exponents (the fragments hold x 2^-ex)
-  float* hbuf;      // ws [MAX_SLOTS][R][hI] fp32 h = w silu(g) u, R = 16 (act16) or 8
+  float* hbuf;      // ws [MAX_SLOTS][hI/16][R][16] fp32 h = w silu(g) u, R = 16 (act16) or 8
   uint32_t* hmax;   // ws [MAX_SLOTS][16] largest |h| of each (slot, token), as float bits
   int32_t E, I, Is, T, d, n_kg, bits, hI, code_off, has_shared;
   int32_t act16;  // 1: A rows are 16 tokens in fp16 (else 8 tokens as fp16 hi + lo)
@@ -96,6 +100,62 @@ struct DownArgs {
   int32_t act16;  // 1: A rows are 16 tokens in fp16 (else 8 tokens as fp16 hi + lo)
   float* ypart;   // ws [S][R][d], R = 16 with act16, else 8
 };
+
+// Persistent decode pass over up to MOE_PERSIST_MAX_LAYERS layers of one
+// shape (persist.hip).  Every layer's packed buffer has the same layout, so a
+// layer is its base pointer plus these offsets.
+#define MOE_PERSIST_MAX_LAYERS 16
+// Words between two counters of the persistent pass (each its own 128-byte
+// line, so workgroups polling one counter do not slow the others).
+#define MOE_CTR_STRIDE 32
+// Words between two layers' per-token words (divisors, exponents): each
+// layer's copy has 256-byte lines of its own.  L2-cached reads of a line
+// another layer writes later would otherwise return the earlier contents.
+#define MOE_PERSIST_TOK_STRIDE 64
+struct PersistArgs {
+  const uint8_t* base[MOE_PERSIST_MAX_LAYERS];
+  int64_t off_wh, off_wl, off_ew, off_br, off_ex, off_sh;
+  int64_t ex_stride, off_gate, off_up, off_down, sh_off_gate, sh_off_up, sh_off_down;
+  int32_t n_layers, T, d, E, k, I, Is, bits, has_shared, code_off;
+  int32_t n_cs, n_rs, S, n_rg, n_kg_r, n_kg_s, max_slots, hI, cpl;
+  float eps;
+  // input of the first layer: S_in splits at in_stride floats; norm0: the
+  // first layer's input is RMS-normalised (it is a previous layer's output)
+  const float* in;
+  int32_t S_in, norm0;
+  int64_t in_stride;
+  float* y;           // [T][d] output, or null: the last layer's partials stay in ypart
+  float* y_prev_out;  // optional: where the first layer's (summed) input is copied
+  float* y_layers;    // optional: layer l's output at y_layers + l * yl_stride
+  int64_t yl_stride;
+  int32_t* idx_layers;  // optional routing outputs at + l * route_stride
+  float* w_layers;
+  int64_t route_stride;
+  float* out_logits;        // optional logits of the first layer
+  const int32_t* in_idx;    // forced routing of a one-layer pass, or null
+  const float* in_w;
+  // workspace
+  float* lp;
+  float* ss_part;
+  float* mx_part;
+  // per layer (a layer's copy is written once per pass, by one workgroup
+  // per cache line, and no line holds two layers' words, so its readers may
+  // use L2-cached loads): layer l's buffer at base + l * stride
+  float* rnorm;      // [n][MOE_PERSIST_TOK_STRIDE]
+  int32_t* xexp;     // [n][MOE_PERSIST_TOK_STRIDE]
+  float* logits;     // [n][T][logits_row]
+  float* xin;        // [n][16][d]
+  float* hbuf;       // [n][max_slots][hI/16][R][16]
+  int64_t logits_stride, xin_stride, hbuf_stride;
+  int32_t logits_row;  // floats per token row of the logits
+  uint32_t* hmax;    // [n_layers][max_slots][16], then the counters (cleared together)
+  uint32_t* ctl;     // [n_layers][cpl], counters MOE_CTR_STRIDE words apart
+  float* ypart;      // [S][R][d]
+  uint32_t* status;  // abort word: non-zero once a wait gave up
+};
+bool persist_supported(int E, int bits);
+int persist_blocks_per_cu();
+hipError_t launch_persist(const PersistArgs& a, int rt, int grid, bool act16, size_t clear_words, hipStream_t s);
 
 hipError_t launch_pack_matrix(const uint8_t* canon, int64_t canon_stride, uint8_t* out, int64_t out_stride,
                               int n_experts, const moe_mat_layout& L, int bits, uint32_t* bad_scale,

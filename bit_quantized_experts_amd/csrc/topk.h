@@ -81,7 +81,7 @@ DEVI TopkLane topk_keys(const uint64_t (&key)[NPER], int E, int k, int32_t* idx_
 
 template <int NPER, typename RowT>
 DEVI void topk_wave(RowT row, int E, int k, int32_t* idx_out, float* w_out, uint64_t* buf) {
-  const int lane = threadIdx.x & 63;
+  const int lane = opaque_tid() & 63;
   uint64_t key[NPER];
 #pragma unroll
   for (int i = 0; i < NPER; ++i) {
@@ -94,7 +94,7 @@ DEVI void topk_wave(RowT row, int E, int k, int32_t* idx_out, float* w_out, uint
 // The same from the keys (lane l: experts l, l+64, ...; 0 = no expert).
 template <int NPER>
 DEVI TopkLane topk_keys(const uint64_t (&key)[NPER], int E, int k, int32_t* idx_out, float* w_out, uint64_t* buf) {
-  const int lane = threadIdx.x & 63;
+  const int lane = opaque_tid() & 63;
   // 1. theta = the largest multiple of 2^16 that at least k of the 64 lane
   // maxima of the value words reach, by a most-significant-bit-first search
   // over ballots

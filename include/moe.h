@@ -142,8 +142,12 @@ int moe_layer_get_desc(const moe_layer *layer, moe_layer_desc *out);
 int moe_route_topk(const float *logits, int T, int E, int k, int32_t *idx, float *w, void *stream);
 
 /* Device scratch needed by moe_layer_forward / moe_stack_forward for up to T
- * tokens per call with this layer's shapes. */
+ * tokens per call with this layer's shapes (any number of stacked layers). */
 int moe_workspace_bytes(const moe_layer *layer, int T, size_t *bytes);
+
+/* The (smaller) device scratch a one-layer call (moe_layer_forward and its
+ * variants) of up to T tokens needs; at most moe_workspace_bytes. */
+int moe_layer_workspace_bytes(const moe_layer *layer, int T, size_t *bytes);
 
 /* Clear the control words of a new workspace (enqueued on `stream`).  Must be
  * called once before a workspace is first used, and again if its memory has
@@ -174,7 +178,7 @@ int moe_layer_forward(const moe_layer *layer, const float *x, int T, float *y, c
  * MOE_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds until the
  * process ends; this call allocates nothing and frees nothing.  Arguments,
  * routing input/output and results as moe_layer_forward (the same kernels).
- * A call whose workspace (moe_workspace_bytes) exceeds the scratch returns
+ * A call whose workspace (moe_layer_workspace_bytes) exceeds the scratch returns
  * MOE_ERR_WORKSPACE before launching anything (a full-size layer of 2560 x
  * 512 experts fits up to 8 tokens; long prefill chunks do not).  Every call
  * on one GPU shares that GPU's scratch: calls that can overlap on one GPU
@@ -267,6 +271,17 @@ int moe_debug_unpack(const moe_layer *layer, int expert, int mat, int8_t *codes,
 int moe_debug_unpack_path(const moe_layer *layer, int expert, int mat, int path, int8_t *codes, float *w_f32,
                           uint16_t *w_f16, void *stream);
 
+/* Status of the last persistent decode pass that used this workspace: 0 = it
+ * ran to completion; 1 = it gave up.  The decode kernels of a layer or stack
+ * of layers of one shape (at most 1024 experts) run as one persistent kernel
+ * whose workgroups (one per compute unit) hand results to each other; every
+ * wait in it is bounded, and a pass that cannot make progress (its
+ * workgroups are not all resident at once, e.g. because other work occupies
+ * the device) ends early with unspecified outputs and this status set.  The
+ * status stays until the next pass on the workspace.  This call waits for
+ * `stream`. */
+int moe_workspace_status(const void *ws, size_t ws_bytes, int *status, void *stream);
+
 /* Tuning overrides read from the environment at each call (set them before
  * the first call and leave them unchanged: the split count also sets the
  * workspace layout, so moe_workspace_bytes and the forward calls must see
@@ -275,7 +290,10 @@ int moe_debug_unpack_path(const moe_layer *layer, int expert, int mat, int path,
  *                    number of 16-row tiles]
  *   MOE_DOWN_SPLITS  decode down-projection splits [2 x CUs / row groups,
  *                    clamped to 1..8 and to the slot count]
- *   MOE_DOWN_WAVES   wavefronts per decode down workgroup [8; 1..8] */
+ *   MOE_DOWN_WAVES   wavefronts per decode down workgroup [8; 1..8]
+ *   MOE_PERSIST      1 = run a stack of layers of one shape (at most 1024
+ *                    experts) as one persistent launch per 16 layers; 0 =
+ *                    separate kernels per layer (route, gate/up, down) [0] */
 
 /* Per-kernel timing for measurement: while enabled, the library brackets
  * every launch of the chosen kernel class with a pair of HIP events that the
@@ -284,7 +302,8 @@ int moe_debug_unpack_path(const moe_layer *layer, int expert, int mat, int path,
  * first, so each runs alone (it must not be enabled while a graph is being
  * captured).  class 0 = decode gate/up expert kernel, 1 = decode down
  * expert kernel, 2 = decode router, 3 = prefill gate/up grouped GEMM, 4 =
- * prefill down grouped GEMM, 5 = prefill router GEMM.  moe_timing_stop waits
+ * prefill down grouped GEMM, 5 = prefill router GEMM, 6 = persistent decode
+ * pass (one launch per pass of up to 64 layers).  moe_timing_stop waits
  * for the recorded events and returns the summed duration and the number of
  * launches. */
 int moe_timing_start(int kernel_class, int max_launches);

@@ -325,8 +325,13 @@ def test_unused_experts_do_not_change_output(bqe):
     assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
 
 
+@pytest.mark.parametrize("path", ["phases", "persist"])
 @pytest.mark.parametrize("which", ["tiny", "full", "full_3bit_T8", "full_3bit_T1"])
-def test_stack_teacher_forced(bqe, which):
+def test_stack_teacher_forced(bqe, which, path, monkeypatch):
+    """Every layer of a stack against the oracle under the stack's own
+    routing, on both decode paths: the per-phase kernels, and the persistent
+    pass (one launch for the stack, which must leave its abort word clear)."""
+    monkeypatch.setenv("MOE_PERSIST", "1" if path == "persist" else "0")
     if which == "tiny":
         wl = mi.small(mi.WORKLOADS["tiny"], Is=64, zipf_s=1.1, layers=5)
         T = 7
@@ -346,9 +351,10 @@ def test_stack_teacher_forced(bqe, which):
     il = torch.empty((nL, T, k), dtype=torch.int32, device=DEV)
     wlr = torch.empty((nL, T, k), dtype=torch.float32, device=DEV)
     ws = bqe.new_workspace(max(L.workspace_bytes(T) for L in layers))
-    say(f"[stack] {which} layers={nL} T={T}")
+    say(f"[stack] {which} layers={nL} T={T} path={path}")
     bqe.moe_stack_forward([L.handle for L in layers], x, y, ws, 1e-6, yl, il, wlr)
     torch.cuda.synchronize()
+    assert bqe.moe_workspace_status(ws) == 0
     yl, il, wlr = yl.cpu().numpy(), il.cpu().numpy(), wlr.cpu().numpy()
     assert np.array_equal(y.cpu().numpy(), yl[-1])
     h = x_np

@@ -139,8 +139,10 @@ def test_f16act_forced_routing(bqe):
     assert err <= TOL_LAYER
 
 
+@pytest.mark.parametrize("path", ["phases", "persist"])
 @pytest.mark.parametrize("which", ["tiny", "full"])
-def test_f16act_stack_teacher_forced(bqe, which):
+def test_f16act_stack_teacher_forced(bqe, which, path, monkeypatch):
+    monkeypatch.setenv("MOE_PERSIST", "1" if path == "persist" else "0")
     if which == "tiny":
         wl = mi.small(mi.WORKLOADS["tiny"], Is=64, zipf_s=1.1, layers=4)
         T = 13
@@ -155,9 +157,10 @@ def test_f16act_stack_teacher_forced(bqe, which):
     il = torch.empty((nL, T, k), dtype=torch.int32, device=DEV)
     wr = torch.empty((nL, T, k), dtype=torch.float32, device=DEV)
     ws = bqe.new_workspace(max(L.workspace_bytes(T) for L in layers))
-    say(f"[f16act stack] {which} layers={nL} T={T}")
+    say(f"[f16act stack] {which} layers={nL} T={T} path={path}")
     bqe.moe_stack_forward_f16act([L.handle for L in layers], activations_device(x_np), y, ws, 1e-6, yl, il, wr)
     torch.cuda.synchronize()
+    assert bqe.moe_workspace_status(ws) == 0
     yl, il, wr = yl.cpu().numpy(), il.cpu().numpy(), wr.cpu().numpy()
     assert np.array_equal(y.cpu().numpy(), yl[-1])
     h = x_np

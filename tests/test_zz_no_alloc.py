@@ -35,7 +35,7 @@ def _run(bqe, L, x_np, noalloc):
     if noalloc:
         bqe.moe_layer_forward_noalloc(L.handle, x, y, r)
     else:
-        bqe.moe_layer_forward(L.handle, x, y, bqe.new_workspace(L.workspace_bytes(T)), r)
+        bqe.moe_layer_forward(L.handle, x, y, bqe.new_workspace(L.layer_workspace_bytes(T)), r)
     torch.cuda.synchronize()
     return [t.cpu().numpy() for t in (y, logits, idx, w)]
 
@@ -51,7 +51,7 @@ def test_noalloc_equals_workspace_entry(bqe, which):
     L = packed_layer(wl, 0)
     for T in sizes:
         say(f"[noalloc] {which}: T={T}")
-        assert L.workspace_bytes(T) <= bqe.NOALLOC_SCRATCH_BYTES
+        assert L.layer_workspace_bytes(T) <= bqe.NOALLOC_SCRATCH_BYTES
         x = mi.activations(wl, T=T, stream=700 + T)
         ref = _run(bqe, L, x, noalloc=False)
         got = _run(bqe, L, x, noalloc=True)
@@ -63,7 +63,7 @@ def test_noalloc_rejects_oversized_call(bqe):
     wl = mi.small(mi.WORKLOADS["layer_t1"], layers=1)
     L = packed_layer(wl, 0)
     T = 4096  # a long prefill chunk: its workspace is far above the scratch
-    assert L.workspace_bytes(T) > bqe.NOALLOC_SCRATCH_BYTES
+    assert L.layer_workspace_bytes(T) > bqe.NOALLOC_SCRATCH_BYTES
     x = torch.zeros((T, wl.d), dtype=torch.float32, device=DEV)
     y = torch.zeros((T, wl.d), dtype=torch.float32, device=DEV)
     with pytest.raises(bqe.MoeError) as e:
