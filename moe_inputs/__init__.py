@@ -51,9 +51,10 @@ class Workload:
     zipf_s: float | None = 1.1   # None = no router bias
     seed: int = 0
     extra_T: tuple = field(default_factory=tuple)
+    codebook: bool = False       # codebook blocks (15 bytes per 32 weights) instead of b-bit codes
 
     def block_bytes(self) -> int:
-        return 2 + 4 * self.bits
+        return CB_BLOCK_BYTES if self.codebook else 2 + 4 * self.bits
 
     def expert_blocks(self, I: int | None = None) -> int:
         I = self.I if I is None else I
@@ -83,6 +84,17 @@ WORKLOADS = {
     "stack_prefill": Workload("stack_prefill", d=2560, E=512, I=640, Is=640, k=10, bits=2, T=8192,
                               layers=48, scale_lo=0.01, scale_hi=0.05),
 }
+
+# codebook-block variants (a synthetic grid stands in for the real tables)
+WORKLOADS["layer_t1_cb3"] = replace(WORKLOADS["layer_t1"], name="layer_t1_cb3", bits=3, codebook=True,
+                                    scale_lo=0.002, scale_hi=0.008)
+WORKLOADS["stack_cb3"] = replace(WORKLOADS["stack_t8_2bit"], name="stack_cb3", bits=3, codebook=True,
+                                 scale_lo=0.002, scale_hi=0.008)
+
+# codebook blocks: fp16 scale + 13 payload bytes (index bytes, index high
+# bits, sign bits); grid of 512 entries of 4 magnitudes
+CB_BLOCK_BYTES = 15
+CB_ENTRIES = 512
 
 # stream ids inside one (seed, layer)
 STREAM_ROUTED = 1
@@ -128,43 +140,60 @@ def hash_words(k0: int, k1: int, ctr: torch.Tensor) -> torch.Tensor:
 
 
 def canon_blocks(seed: int, layer: int, stream: int, first: int, count: int, bits: int,
-                 scale_lo: float, scale_hi: float, device="cpu", chunk: int = 1 << 22) -> torch.Tensor:
-    """Canonical blocks [first, first+count) of one stream, as uint8 [count, 2+4*bits].
+                 scale_lo: float, scale_hi: float, device="cpu", chunk: int = 1 << 22,
+                 codebook: bool = False) -> torch.Tensor:
+    """Canonical blocks [first, first+count) of one stream, as uint8 [count, bytes].
 
-    Block n uses counters 4n .. 4n+bits: word 4n gives the scale
-    (u = word / 2^32, s = fp16(fp32(lo + (hi-lo) u))), words 4n+1.. give the
-    4*bits code bytes, little endian.
+    b-bit blocks (2 + 4*bits bytes): block n uses counters 4n .. 4n+bits; word
+    4n gives the scale (u = word / 2^32, s = fp16(fp32(lo + (hi-lo) u))),
+    words 4n+1.. give the 4*bits code bytes, little endian.
+
+    Codebook blocks (15 bytes): block n uses counters 8n .. 8n+4; word 8n gives
+    the scale as above, words 8n+1..8n+4 give the 13 payload bytes (the first
+    13 of their 16 little-endian bytes), so grid indices and signs are uniform.
     """
     assert bits in (2, 3)
-    assert 4 * (first + count) < (1 << 32), "counter space of one stream exceeded"
+    per = 8 if codebook else 4
+    assert per * (first + count) < (1 << 32), "counter space of one stream exceeded"
     k0, k1 = stream_keys(seed, layer, stream)
-    bb = 2 + 4 * bits
+    bb = CB_BLOCK_BYTES if codebook else 2 + 4 * bits
+    n_words = 4 if codebook else bits
     out = torch.empty((count, bb), dtype=torch.uint8, device=device)
     for c0 in range(0, count, chunk):
         n = min(chunk, count - c0)
-        base = torch.arange(first + c0, first + c0 + n, dtype=torch.int64, device=device) * 4
+        base = torch.arange(first + c0, first + c0 + n, dtype=torch.int64, device=device) * per
         w0 = hash_words(k0, k1, base)
         u = w0.to(torch.float64) * (2.0 ** -32)
         s = (u * (scale_hi - scale_lo) + scale_lo).to(torch.float32).to(torch.float16)
         sb = s.view(torch.int16).to(torch.int64) & 0xFFFF
         cols = [sb & 0xFF, sb >> 8]
-        for j in range(bits):
+        for j in range(n_words):
             wj = hash_words(k0, k1, base + (1 + j))
             cols += [wj & 0xFF, (wj >> 8) & 0xFF, (wj >> 16) & 0xFF, wj >> 24]
-        out[c0:c0 + n] = torch.stack(cols, dim=1).to(torch.uint8)
+        out[c0:c0 + n] = torch.stack(cols[:bb], dim=1).to(torch.uint8)
         del base, w0, u, s, sb, cols
     return out
+
+
+def codebook_grid(seed: int = 0) -> np.ndarray:
+    """Synthetic codebook [512, 4] uint8: 512 distinct 4-vectors of odd
+    magnitudes 1..15 (a seeded choice among the 8^4 = 4096 such vectors)."""
+    g = _rng(seed, 404)
+    pick = g.permutation(8 ** 4)[:CB_ENTRIES]
+    digits = np.stack([(pick >> (3 * c)) & 7 for c in range(4)], axis=1)
+    return (2 * digits + 1).astype(np.uint8)
 
 
 def expert_canon(wl: Workload, layer: int, expert: int, device="cpu") -> torch.Tensor:
     """Canonical bytes of one expert (expert = -1: the shared expert), flat uint8."""
     if expert < 0:
         nb = wl.expert_blocks(wl.Is)
-        blk = canon_blocks(wl.seed, layer, STREAM_SHARED, 0, nb, wl.bits, wl.scale_lo, wl.scale_hi, device)
+        blk = canon_blocks(wl.seed, layer, STREAM_SHARED, 0, nb, wl.bits, wl.scale_lo, wl.scale_hi, device,
+                           codebook=wl.codebook)
     else:
         nb = wl.expert_blocks()
         blk = canon_blocks(wl.seed, layer, STREAM_ROUTED, expert * nb, nb, wl.bits,
-                           wl.scale_lo, wl.scale_hi, device)
+                           wl.scale_lo, wl.scale_hi, device, codebook=wl.codebook)
     return blk.reshape(-1)
 
 
@@ -172,7 +201,7 @@ def layer_experts_canon(wl: Workload, layer: int, device="cpu") -> torch.Tensor:
     """Canonical bytes of all routed experts of one layer, [E * expert_bytes] uint8."""
     nb = wl.expert_blocks()
     blk = canon_blocks(wl.seed, layer, STREAM_ROUTED, 0, wl.E * nb, wl.bits,
-                       wl.scale_lo, wl.scale_hi, device)
+                       wl.scale_lo, wl.scale_hi, device, codebook=wl.codebook)
     return blk.reshape(-1)
 
 

@@ -81,11 +81,19 @@ def _declare(L):
     L.orc_group_tokens.argtypes = [_P, _I, _I, _I, _P, _P, _P]
     L.orc_group_tokens.restype = None
     L.orc_rmsnorm.restype = None
+    L.orc_cb_block_bytes.argtypes = []
+    L.orc_cb_unpack_block.argtypes = [_P, _P, _P, _P]
+    L.orc_cb_unpack_block.restype = None
+    L.orc_cb_unpack_matrix.argtypes = [_P, _I, _I, _P, _P, _P]
+    L.orc_cb_dequant_matrix.argtypes = [_P, _I, _I, _P, _P]
+    L.orc_cb_expert_bytes.argtypes = [_I, _I]
+    L.orc_cb_expert_bytes.restype = ctypes.c_size_t
+    L.orc_expert_ffn_any.argtypes = [_P, _I, _I, _I, _P, _P, _P]
 
 
 class _Layer(ctypes.Structure):
     _fields_ = [("d", _I), ("E", _I), ("I", _I), ("Is", _I), ("k", _I), ("bits", _I),
-                ("router_w", _P), ("router_bias", _P), ("experts", _P), ("shared", _P)]
+                ("router_w", _P), ("router_bias", _P), ("experts", _P), ("shared", _P), ("grid", _P)]
 
 
 def _ptr(a):
@@ -142,8 +150,10 @@ def exp64_ln2_parts():
     return L.orc_exp64_ln2(0), L.orc_exp64_ln2(1), L.orc_exp64_ln2(2)
 
 
-def block_bytes(bits: int) -> int:
-    return 2 + 4 * bits
+def block_bytes(bits: int, grid=None) -> int:
+    """Bytes of one canonical block: b-bit codes, or a codebook block when a
+    grid is given."""
+    return int(lib().orc_cb_block_bytes()) if grid is not None else 2 + 4 * bits
 
 
 def expert_bytes(d: int, I: int, bits: int) -> int:
@@ -179,9 +189,48 @@ def dequant_matrix(canon, rows: int, cols: int, bits: int):
     return w
 
 
-def split_expert(canon, d: int, I: int, bits: int):
+# ---------------------------------------------------------------------------
+# codebook blocks (grid [512, 4] uint8 of magnitudes)
+# ---------------------------------------------------------------------------
+def cb_unpack_block(blk: bytes, grid):
+    """Return (codes[32] int8, scale float) of one canonical codebook block."""
+    b = _c(np.frombuffer(bytes(blk), dtype=np.uint8), np.uint8)
+    g = _c(grid, np.uint8)
+    codes = np.empty(32, dtype=np.int8)
+    s = ctypes.c_double()
+    lib().orc_cb_unpack_block(_ptr(b), _ptr(g), _ptr(codes), ctypes.byref(s))
+    return codes, s.value
+
+
+def cb_unpack_matrix(canon, rows: int, cols: int, grid):
+    c = _c(canon, np.uint8)
+    g = _c(grid, np.uint8)
+    codes = np.empty((rows, cols), dtype=np.int8)
+    scales = np.empty((rows, cols // 32), dtype=np.float64)
+    _check(lib().orc_cb_unpack_matrix(_ptr(c), rows, cols, _ptr(g), _ptr(codes), _ptr(scales)),
+           "cb_unpack_matrix")
+    return codes, scales
+
+
+def cb_dequant_matrix(canon, rows: int, cols: int, grid):
+    c = _c(canon, np.uint8)
+    g = _c(grid, np.uint8)
+    w = np.empty((rows, cols), dtype=np.float64)
+    _check(lib().orc_cb_dequant_matrix(_ptr(c), rows, cols, _ptr(g), _ptr(w)), "cb_dequant_matrix")
+    return w
+
+
+def unpack_any(canon, rows: int, cols: int, bits: int, grid=None):
+    return cb_unpack_matrix(canon, rows, cols, grid) if grid is not None else unpack_matrix(canon, rows, cols, bits)
+
+
+def dequant_any(canon, rows: int, cols: int, bits: int, grid=None):
+    return cb_dequant_matrix(canon, rows, cols, grid) if grid is not None else dequant_matrix(canon, rows, cols, bits)
+
+
+def split_expert(canon, d: int, I: int, bits: int, grid=None):
     """Byte ranges of gate [I][d], up [I][d], down [d][I] inside one expert."""
-    bb = block_bytes(bits)
+    bb = block_bytes(bits, grid)
     g = I * (d // 32) * bb
     dn = d * (I // 32) * bb
     c = np.asarray(canon, dtype=np.uint8)
@@ -212,11 +261,15 @@ def topk(logits, k: int):
     return idx, w
 
 
-def expert_ffn(canon, d: int, I: int, bits: int, x):
+def expert_ffn(canon, d: int, I: int, bits: int, x, grid=None):
     c = _c(canon, np.uint8)
     xv = _c(x, np.float64)
     y = np.empty(d, dtype=np.float64)
-    _check(lib().orc_expert_ffn(_ptr(c), d, I, bits, _ptr(xv), _ptr(y)), "expert_ffn")
+    if grid is None:
+        _check(lib().orc_expert_ffn(_ptr(c), d, I, bits, _ptr(xv), _ptr(y)), "expert_ffn")
+    else:
+        g = _c(grid, np.uint8)
+        _check(lib().orc_expert_ffn_any(_ptr(c), d, I, bits, _ptr(g), _ptr(xv), _ptr(y)), "expert_ffn")
     return y
 
 
@@ -227,8 +280,9 @@ class Layer:
     the routing never selects may be left out.
     """
 
-    def __init__(self, d, E, I, Is, k, bits, router_w, router_bias, experts, shared=None):
+    def __init__(self, d, E, I, Is, k, bits, router_w, router_bias, experts, shared=None, grid=None):
         self.d, self.E, self.I, self.Is, self.k, self.bits = d, E, I, Is, k, bits
+        self.grid = None if grid is None else _c(grid, np.uint8)
         self.router_w = _c(router_w, np.float32)
         self.router_bias = None if router_bias is None else _c(router_bias, np.float32)
         self.experts = {int(e): _c(v, np.uint8) for e, v in dict(experts).items()}
@@ -240,7 +294,7 @@ class Layer:
             ptrs[e] = v.ctypes.data
         s = _Layer(self.d, self.E, self.I, self.Is, self.k, self.bits,
                    _ptr(self.router_w), _ptr(self.router_bias),
-                   ctypes.cast(ptrs, _P), _ptr(self.shared))
+                   ctypes.cast(ptrs, _P), _ptr(self.shared), _ptr(self.grid))
         return s, ptrs
 
 

@@ -30,6 +30,17 @@
  *      deterministic exp64 below.
  *   R5 shared expert has weight 1 and no gate.
  *   R6 stack glue = RMSNorm with unit weight and eps 1e-6 between layers.
+ *   R7 codebook blocks (the codebook block types the same credits list
+ *      names, whose tables ship with the model file and are absent here, so
+ *      a synthetic table of the same shape stands in): 32 weights per block,
+ *      15 bytes: [0,2) fp16 scale; [2,10) the low 8 bits of eight 9-bit
+ *      grid indices, index i covering weights 4i..4i+3; byte 10, bit i = bit
+ *      8 of index i; [11,15) 32 sign bits, bit j of the little-endian word
+ *      set = weight j negative.  Weight j = scale * (+-1) * G[index][j % 4]
+ *      for a grid G of 512 entries of 4 unsigned magnitudes (0..127).
+ *   R8 a forced routing row names each expert at most once: an entry
+ *      outside [0, E) or repeating an expert of an earlier rank of the same
+ *      token contributes nothing (the same rule as the token grouping).
  *
  * Every function here is pinned by a CPU test (values fixed by the
  * mathematics, brute force, closed forms and invariants).
@@ -161,6 +172,70 @@ int orc_dequant_matrix(const uint8_t *canon, int rows, int cols, int bits, doubl
 }
 
 /* ------------------------------------------------------------------ */
+/* Codebook block (reading R7): 15 bytes, 32 weights.                    */
+/* ------------------------------------------------------------------ */
+#define ORC_CB_BLOCK_BYTES 15
+#define ORC_CB_ENTRIES 512
+int orc_cb_block_bytes(void) { return ORC_CB_BLOCK_BYTES; }
+
+/* Unpack one codebook block: 32 signed codes (the looked-up magnitude with
+ * the block's sign bit applied) and the scale as fp64.  grid is [512][4]. */
+void orc_cb_unpack_block(const uint8_t *blk, const uint8_t *grid, int8_t *codes, double *scale)
+{
+    uint16_t sbits = (uint16_t)(blk[0] | (blk[1] << 8));
+    uint32_t signs = (uint32_t)blk[11] | ((uint32_t)blk[12] << 8) |
+                     ((uint32_t)blk[13] << 16) | ((uint32_t)blk[14] << 24);
+    for (int i = 0; i < 8; ++i) {
+        int index = blk[2 + i] | (((blk[10] >> i) & 1) << 8);
+        for (int c = 0; c < 4; ++c) {
+            int j = 4 * i + c;
+            int m = grid[4 * index + c];
+            codes[j] = (int8_t)(((signs >> j) & 1) ? -m : m);
+        }
+    }
+    *scale = orc_half_to_double(sbits);
+}
+
+static int grid_ok(const uint8_t *grid)
+{
+    if (!grid) return 0;
+    for (int i = 0; i < 4 * ORC_CB_ENTRIES; ++i)
+        if (grid[i] > 127) return 0;
+    return 1;
+}
+
+/* Whole canonical codebook matrix [rows][cols]: codes[rows*cols],
+ * scales[rows*(cols/32)]. */
+int orc_cb_unpack_matrix(const uint8_t *canon, int rows, int cols, const uint8_t *grid,
+                         int8_t *codes, double *scales)
+{
+    if (cols % 32 || rows < 0 || !grid_ok(grid)) return ORC_ERR_ARG;
+    int nb = cols / 32;
+    for (int r = 0; r < rows; ++r)
+        for (int b = 0; b < nb; ++b)
+            orc_cb_unpack_block(canon + ((size_t)r * nb + b) * ORC_CB_BLOCK_BYTES, grid,
+                                codes + (size_t)r * cols + 32 * b, scales + (size_t)r * nb + b);
+    return ORC_OK;
+}
+
+/* w = scale * code in fp64 (exact: 11 significant bits times a magnitude
+ * below 128, at most 18 bits, so exact in fp32 too). */
+int orc_cb_dequant_matrix(const uint8_t *canon, int rows, int cols, const uint8_t *grid, double *w)
+{
+    if (cols % 32 || rows < 0 || !grid_ok(grid)) return ORC_ERR_ARG;
+    int nb = cols / 32;
+    int8_t c[32];
+    double s;
+    for (int r = 0; r < rows; ++r)
+        for (int b = 0; b < nb; ++b) {
+            orc_cb_unpack_block(canon + ((size_t)r * nb + b) * ORC_CB_BLOCK_BYTES, grid, c, &s);
+            for (int j = 0; j < 32; ++j)
+                w[(size_t)r * cols + 32 * b + j] = s * (double)c[j];
+        }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ */
 /* exp64: deterministic fp64 exponential, written from the mathematics   */
 /* so that any implementation following the same steps in IEEE fp64     */
 /* reproduces it bit for bit:                                            */
@@ -277,13 +352,21 @@ int orc_topk(const float *logits, int T, int E, int k, int32_t *idx, float *w)
 /* Expert canonical bytes: gate [I][d/32 blocks], up [I][d/32], down      */
 /* [d][I/32], consecutive.                                                */
 /* ------------------------------------------------------------------ */
-static double matvec_row(const uint8_t *row_blocks, int cols, int bits, const double *v)
+/* A block of either format: plain b-bit codes, or codebook blocks when a
+ * grid is given. */
+static int any_block_bytes(int bits, const uint8_t *grid)
 {
-    int bb = orc_block_bytes(bits);
+    return grid ? ORC_CB_BLOCK_BYTES : orc_block_bytes(bits);
+}
+
+static double matvec_row(const uint8_t *row_blocks, int cols, int bits, const uint8_t *grid, const double *v)
+{
+    int bb = any_block_bytes(bits, grid);
     int8_t c[32];
     double s, acc = 0.0;
     for (int b = 0; b < cols / 32; ++b) {
-        orc_unpack_block(row_blocks + (size_t)b * bb, bits, c, &s);
+        if (grid) orc_cb_unpack_block(row_blocks + (size_t)b * bb, grid, c, &s);
+        else orc_unpack_block(row_blocks + (size_t)b * bb, bits, c, &s);
         for (int j = 0; j < 32; ++j) acc += (s * (double)c[j]) * v[32 * b + j];
     }
     return acc;
@@ -294,22 +377,35 @@ size_t orc_expert_bytes(int d, int I, int bits)
     return (size_t)3 * (size_t)I * (size_t)(d / 32) * (size_t)orc_block_bytes(bits);
 }
 
-int orc_expert_ffn(const uint8_t *ex, int d, int I, int bits, const double *x, double *y)
+size_t orc_cb_expert_bytes(int d, int I)
 {
-    if (d % 32 || I % 32 || (bits != 2 && bits != 3)) return ORC_ERR_ARG;
-    int bb = orc_block_bytes(bits);
+    return (size_t)3 * (size_t)I * (size_t)(d / 32) * (size_t)ORC_CB_BLOCK_BYTES;
+}
+
+/* The expert FFN from blocks of either format (grid NULL: b-bit blocks). */
+int orc_expert_ffn_any(const uint8_t *ex, int d, int I, int bits, const uint8_t *grid,
+                       const double *x, double *y)
+{
+    if (d % 32 || I % 32) return ORC_ERR_ARG;
+    if (grid ? !grid_ok(grid) : (bits != 2 && bits != 3)) return ORC_ERR_ARG;
+    int bb = any_block_bytes(bits, grid);
     size_t gate_row = (size_t)(d / 32) * bb, down_row = (size_t)(I / 32) * bb;
     const uint8_t *Wg = ex, *Wu = ex + (size_t)I * gate_row, *Wd = ex + 2 * (size_t)I * gate_row;
     double *h = (double *)malloc(sizeof(double) * (size_t)I);
     if (!h) return ORC_ERR_ARG;
     for (int i = 0; i < I; ++i) {
-        double g = matvec_row(Wg + (size_t)i * gate_row, d, bits, x);
-        double u = matvec_row(Wu + (size_t)i * gate_row, d, bits, x);
+        double g = matvec_row(Wg + (size_t)i * gate_row, d, bits, grid, x);
+        double u = matvec_row(Wu + (size_t)i * gate_row, d, bits, grid, x);
         h[i] = g / (1.0 + exp(-g)) * u;
     }
-    for (int o = 0; o < d; ++o) y[o] = matvec_row(Wd + (size_t)o * down_row, I, bits, h);
+    for (int o = 0; o < d; ++o) y[o] = matvec_row(Wd + (size_t)o * down_row, I, bits, grid, h);
     free(h);
     return ORC_OK;
+}
+
+int orc_expert_ffn(const uint8_t *ex, int d, int I, int bits, const double *x, double *y)
+{
+    return orc_expert_ffn_any(ex, d, I, bits, NULL, x, y);
 }
 
 /* ------------------------------------------------------------------ */
@@ -321,6 +417,7 @@ typedef struct {
     const float *router_bias;   /* [E] or NULL (= 0) */
     const uint8_t *const *experts; /* E pointers; NULL for experts never selected */
     const uint8_t *shared;      /* shared expert canonical bytes, NULL if Is == 0 */
+    const uint8_t *grid;        /* codebook [512][4] for codebook blocks, NULL for b-bit blocks */
 } orc_layer;
 
 /* y[t] = fp32( sum_{r in rank order} w[t][r] * FFN_{idx[t][r]}(x[t])
@@ -357,9 +454,12 @@ int orc_layer_forward(const orc_layer *L, const float *x, int T,
         for (int j = 0; j < d; ++j) { xv[j] = (double)x[(size_t)t * d + j]; acc[j] = 0.0; }
         for (int r = 0; r < k; ++r) {
             int e = idx[(size_t)t * k + r];
-            if (e < 0 || e >= E) { rc = ORC_ERR_ARG; break; }
+            if (e < 0 || e >= E) continue;  /* reading R8 */
+            int earlier = 0;
+            for (int q = 0; q < r; ++q) earlier |= idx[(size_t)t * k + q] == e;
+            if (earlier) continue;
             if (!L->experts || !L->experts[e]) { rc = ORC_ERR_MISSING_EXPERT; break; }
-            rc = orc_expert_ffn(L->experts[e], d, L->I, L->bits, xv, ye);
+            rc = orc_expert_ffn_any(L->experts[e], d, L->I, L->bits, L->grid, xv, ye);
             if (rc != ORC_OK) break;
             double g = (double)w[(size_t)t * k + r];
             for (int o = 0; o < d; ++o) acc[o] += g * ye[o];
@@ -367,7 +467,7 @@ int orc_layer_forward(const orc_layer *L, const float *x, int T,
         if (rc != ORC_OK) break;
         if (L->Is > 0) {
             if (!L->shared) { rc = ORC_ERR_MISSING_EXPERT; break; }
-            rc = orc_expert_ffn(L->shared, d, L->Is, L->bits, xv, ye);
+            rc = orc_expert_ffn_any(L->shared, d, L->Is, L->bits, L->grid, xv, ye);
             if (rc != ORC_OK) break;
             for (int o = 0; o < d; ++o) acc[o] += ye[o];
         }

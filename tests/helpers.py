@@ -29,7 +29,8 @@ def oracle_layer(wl: mi.Workload, layer: int, experts) -> oracle.Layer:
     W, b = mi.router(wl, layer)
     ex = {int(e): mi.expert_canon(wl, layer, int(e)).numpy() for e in set(int(v) for v in experts)}
     sh = mi.expert_canon(wl, layer, -1).numpy() if wl.Is else None
-    return oracle.Layer(wl.d, wl.E, wl.I, wl.Is, wl.k, wl.bits, W, b, ex, sh)
+    grid = mi.codebook_grid(wl.seed) if wl.codebook else None
+    return oracle.Layer(wl.d, wl.E, wl.I, wl.Is, wl.k, wl.bits, W, b, ex, sh, grid=grid)
 
 
 # layer-output tolerance: global infinity-norm relative error max|y - ref| / max|ref|

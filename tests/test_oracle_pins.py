@@ -442,3 +442,172 @@ def test_group_tokens_closed_form(orc):
         assert counts[e] == len(toks)
         got = perm[offsets[e]:offsets[e + 1]]
         assert got.tolist() == [t * k + (e - t) % E for t in toks]
+
+
+# ---------------------------------------------------------------------------
+# codebook blocks (reading R7) and the forced-routing rule (reading R8)
+# ---------------------------------------------------------------------------
+def np_cb_decode(canon, rows, cols, grid):
+    """Independent numpy decoder of codebook blocks: fields by slicing, sign
+    bits by unpackbits, magnitudes by fancy indexing into the grid."""
+    blk = np.asarray(canon, dtype=np.uint8).reshape(rows, cols // 32, 15)
+    scale = np.ascontiguousarray(blk[..., :2]).view(np.float16)[..., 0].astype(np.float64)
+    hi = np.unpackbits(blk[..., 10:11], axis=-1, bitorder="little").astype(np.int64)  # [.., 8]
+    index = blk[..., 2:10].astype(np.int64) + 256 * hi                                    # [.., 8]
+    mag = np.asarray(grid, dtype=np.int64)[index]                                        # [.., 8, 4]
+    sign = np.unpackbits(blk[..., 11:15], axis=-1, bitorder="little").astype(np.int64)  # [.., 32]
+    c = mag.reshape(rows, cols // 32, 32) * (1 - 2 * sign)
+    return (scale[..., None] * c).reshape(rows, cols), c.reshape(rows, cols)
+
+
+def np_cb_expert(canon, d, I, grid):
+    g = I * (d // 32) * 15
+    dn = d * (I // 32) * 15
+    c = np.asarray(canon, dtype=np.uint8)
+    return (np_cb_decode(c[:g], I, d, grid)[0], np_cb_decode(c[g:2 * g], I, d, grid)[0],
+            np_cb_decode(c[2 * g:2 * g + dn], d, I, grid)[0])
+
+
+def test_cb_golden_blocks(orc):
+    with open(os.path.join(GOLDEN, "cb_blocks.json")) as f:
+        cases = json.load(f)["cases"]
+    for case in cases:
+        grid = np.zeros((512, 4), np.uint8)
+        for i, v in case["grid"].items():
+            grid[int(i)] = v
+        blk = bytes.fromhex(case["bytes"].replace(" ", ""))
+        assert len(blk) == 15 == orc.block_bytes(3, grid)
+        codes, scale = orc.cb_unpack_block(blk, grid)
+        assert scale == case["scale"], case["note"]
+        assert codes.tolist() == case["codes"], case["note"]
+
+
+def test_cb_every_index_and_sign_byte(orc):
+    """Each of the 512 indices at each of the 8 positions, and each sign byte
+    value at each of the 4 sign bytes, against a direct table walk of the
+    field values the block was built from."""
+    g = np.random.default_rng(11)
+    grid = g.integers(0, 128, (512, 4)).astype(np.uint8)
+    for pos in range(8):
+        for index in range(512):
+            blk = bytearray(15)
+            blk[0:2] = b"\x00\x3c"
+            blk[2 + pos] = index & 0xFF
+            blk[10] = (index >> 8) << pos
+            codes, _ = orc.cb_unpack_block(bytes(blk), grid)
+            expect = np.tile(grid[0], 8).astype(np.int64)      # other positions: index 0
+            expect[4 * pos:4 * pos + 4] = grid[index]
+            assert codes.tolist() == expect.tolist(), (pos, index)
+    for sb in range(4):
+        for v in range(256):
+            blk = bytearray(15)
+            blk[0:2] = b"\x00\x3c"
+            blk[11 + sb] = v
+            codes, _ = orc.cb_unpack_block(bytes(blk), grid)
+            expect = np.tile(grid[0], 8).astype(np.int64)
+            for bit in range(8):
+                if (v >> bit) & 1:
+                    expect[8 * sb + bit] *= -1
+            assert codes.tolist() == expect.tolist(), (sb, v)
+
+
+def test_cb_generated_matrices_vs_numpy(orc):
+    wl = mi.small(mi.WORKLOADS["tiny"], bits=3, codebook=True, scale_lo=0.002, scale_hi=0.008)
+    grid = mi.codebook_grid()
+    ex = mi.expert_canon(wl, 0, 3).numpy()
+    n = wl.I * (wl.d // 32) * 15
+    w, c = np_cb_decode(ex[:n], wl.I, wl.d, grid)
+    codes, scales = orc.cb_unpack_matrix(ex[:n], wl.I, wl.d, grid)
+    assert np.array_equal(codes.astype(np.int64), c)
+    assert np.array_equal(orc.cb_dequant_matrix(ex[:n], wl.I, wl.d, grid), w)
+    assert np.array_equal(np.repeat(scales, 32, axis=1) * codes, w)
+
+
+def test_cb_reduces_to_plain_2bit(orc):
+    """With grid entry i (i < 256) = the base-4 digits of i, a 2-bit block
+    rewritten as a codebook block (index = sum |c| 4^m, sign = c < 0) must
+    dequantise to the same weights as the plain 2-bit decoder."""
+    grid = np.zeros((512, 4), np.uint8)
+    for i in range(256):
+        grid[i] = [(i >> (2 * m)) & 3 for m in range(4)]
+    wl = mi.small(mi.WORKLOADS["tiny"], bits=2)
+    canon = mi.expert_canon(wl, 0, 1).numpy()[: 64 * 8 * 10]          # 64 rows x 256 inputs
+    codes, scales = orc.unpack_matrix(canon, 64, 256, 2)
+    cb = np.zeros((64, 8, 15), np.uint8)
+    blk = canon.reshape(64, 8, 10)
+    cb[..., 0:2] = blk[..., 0:2]
+    c = codes.reshape(64, 8, 8, 4).astype(np.int64)
+    index = (np.abs(c) * (4 ** np.arange(4))).sum(-1)                  # [64, 8, 8] < 256
+    cb[..., 2:10] = index.astype(np.uint8)
+    sign = (codes.reshape(64, 8, 32) < 0).astype(np.uint8)
+    cb[..., 11:15] = np.packbits(sign, axis=-1, bitorder="little")
+    w_cb = orc.cb_dequant_matrix(cb.reshape(-1), 64, 256, grid)
+    assert np.array_equal(w_cb, orc.dequant_matrix(canon, 64, 256, 2))
+
+
+def test_cb_dequant_exact_all_scales(orc):
+    """Every positive finite fp16 scale times magnitudes up to 127 with both
+    signs: the fp64 product is exact and also exact in fp32."""
+    grid = np.zeros((512, 4), np.uint8)
+    grid[0] = [127, 1, 77, 0]
+    grid[1] = [3, 101, 126, 15]
+    scales = np.arange(1, 0x7C00, dtype=np.uint16)
+    rows = scales.size
+    canon = np.zeros((rows, 15), np.uint8)
+    canon[:, 0] = scales & 0xFF
+    canon[:, 1] = scales >> 8
+    canon[:, 2:10] = [0, 1, 0, 1, 0, 1, 0, 1]
+    canon[:, 11:15] = [0x5A, 0xC3, 0x0F, 0xF0]
+    w = orc.cb_dequant_matrix(canon.reshape(-1), rows, 32, grid)
+    s = scales.view(np.float16).astype(np.float64)
+    _, c = np_cb_decode(canon.reshape(-1), rows, 32, grid)
+    from fractions import Fraction as F
+    for r in range(0, rows, 97):
+        for j in range(32):
+            assert F(w[r, j]) == F(s[r]) * int(c[r, j])
+    assert np.array_equal(w.astype(np.float32).astype(np.float64), w)
+
+
+def test_cb_expert_ffn_and_layer_vs_dense(orc):
+    grid = mi.codebook_grid()
+    wl = mi.small(mi.WORKLOADS["tiny"], bits=3, codebook=True, Is=64, k=3, zipf_s=1.1, T=5,
+                  scale_lo=0.002, scale_hi=0.008)
+    ex = mi.expert_canon(wl, 0, 2).numpy()
+    x = mi.activations(wl, T=1)[0].astype(np.float64)
+    got = orc.expert_ffn(ex, wl.d, wl.I, 3, x, grid=grid)
+    ref = np_ffn(*np_cb_expert(ex, wl.d, wl.I, grid), x)
+    assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+    W, bias = mi.router(wl, 0)
+    allx = mi.layer_experts_canon(wl, 0).numpy()
+    eb = wl.expert_bytes()
+    assert eb == 3 * wl.I * (wl.d // 32) * 15
+    experts = {e: allx[e * eb:(e + 1) * eb] for e in range(wl.E)}
+    sh = mi.expert_canon(wl, 0, -1).numpy()
+    L = orc.Layer(wl.d, wl.E, wl.I, wl.Is, wl.k, wl.bits, W, bias, experts, sh, grid=grid)
+    xs = mi.activations(wl)
+    y, _, idx, w = orc.layer_forward(L, xs)
+    dense = [np_cb_expert(experts[e], wl.d, wl.I, grid) for e in range(wl.E)]
+    dsh = np_cb_expert(sh, wl.d, wl.Is, grid)
+    for t in range(xs.shape[0]):
+        gate = np.zeros(wl.E)
+        gate[idx[t]] = w[t]
+        xt = xs[t].astype(np.float64)
+        r = sum(gate[e] * np_ffn(*dense[e], xt) for e in range(wl.E)) + np_ffn(*dsh, xt)
+        assert np.max(np.abs(y[t] - r)) <= 4 * np.spacing(np.float32(np.max(np.abs(r))))
+
+
+def test_forced_routing_invalid_and_repeated_ids(orc):
+    """Reading R8: an id outside [0, E) contributes nothing and a repeated id
+    counts once, at its first rank: the output equals the closed form
+    w_first * FFN_e(x) (+ the other valid experts)."""
+    wl = mi.small(mi.WORKLOADS["tiny"], k=3)
+    L = _tiny_layer(orc, wl)
+    x = mi.activations(wl, T=2)
+    fi = np.array([[5, 5, 99], [-1, 7, 7]], np.int32)
+    fw = np.array([[0.75, 0.25, 0.5], [0.5, 0.375, 0.125]], np.float32)
+    y, _, _, _ = orc.layer_forward(L, x, force_idx=fi, force_w=fw)
+    r0 = 0.75 * orc.expert_ffn(L.experts[5], wl.d, wl.I, wl.bits, x[0].astype(np.float64))
+    r1 = 0.375 * orc.expert_ffn(L.experts[7], wl.d, wl.I, wl.bits, x[1].astype(np.float64))
+    assert np.array_equal(y[0], r0.astype(np.float32))
+    assert np.array_equal(y[1], r1.astype(np.float32))
