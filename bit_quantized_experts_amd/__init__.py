@@ -28,7 +28,7 @@ EXPORTED = ("moe_last_error", "moe_packed_bytes", "moe_pack_experts", "moe_layer
             "moe_stack_forward", "moe_rmsnorm", "moe_debug_unpack", "moe_timing_start", "moe_timing_stop",
             "moe_group_workspace_bytes", "moe_group_tokens", "moe_layer_forward_f16act",
             "moe_stack_forward_f16act", "moe_debug_unpack_path", "moe_layer_forward_noalloc",
-            "moe_workspace_status", "moe_layer_workspace_bytes")
+            "moe_workspace_status", "moe_layer_workspace_bytes", "moe_pack_experts_cb")
 
 
 class MoeError(RuntimeError):
@@ -40,7 +40,7 @@ class MoeError(RuntimeError):
 class LayerDesc(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("d_ff_shared", ctypes.c_int32), ("top_k", ctypes.c_int32), ("bits", ctypes.c_int32),
-                ("block", ctypes.c_int32)]
+                ("block", ctypes.c_int32), ("codebook", ctypes.c_int32)]
 
 
 class RouteIO(ctypes.Structure):
@@ -63,6 +63,7 @@ def lib() -> ctypes.CDLL:
         L.moe_last_error.argtypes = []
         L.moe_packed_bytes.argtypes = [P, ctypes.POINTER(S)]
         L.moe_pack_experts.argtypes = [P, P, P, P, P, P, S, ctypes.POINTER(P), P]
+        L.moe_pack_experts_cb.argtypes = [P, P, P, P, P, P, P, S, ctypes.POINTER(P), P]
         L.moe_layer_release.argtypes = [P]
         L.moe_layer_get_desc.argtypes = [P, P]
         L.moe_route_topk.argtypes = [P, I, I, I, P, P, P]
@@ -110,8 +111,8 @@ def _stream(stream=None):
     return stream.cuda_stream
 
 
-def make_desc(d_model, n_experts, d_ff, d_ff_shared, top_k, bits, block=32) -> LayerDesc:
-    return LayerDesc(d_model, n_experts, d_ff, d_ff_shared, top_k, bits, block)
+def make_desc(d_model, n_experts, d_ff, d_ff_shared, top_k, bits, block=32, codebook=False) -> LayerDesc:
+    return LayerDesc(d_model, n_experts, d_ff, d_ff_shared, top_k, bits, block, int(bool(codebook)))
 
 
 # ---------------------------------------------------------------------------
@@ -133,6 +134,17 @@ def moe_pack_experts(desc: LayerDesc, experts_canon, shared_canon, router_w, rou
     _check(lib().moe_pack_experts(ctypes.byref(desc), _ptr(experts_canon), _ptr(shared_canon), _ptr(router_w),
                                   _ptr(router_bias), _ptr(packed), packed.numel() * packed.element_size(),
                                   ctypes.byref(h), _stream(stream)), "moe_pack_experts")
+    return h.value
+
+
+def moe_pack_experts_cb(desc: LayerDesc, experts_canon, shared_canon, grid, router_w, router_bias, packed,
+                        stream=None) -> int:
+    """Codebook blocks: as moe_pack_experts plus the grid (uint8 [512, 4] on the device)."""
+    h = ctypes.c_void_p()
+    _check(lib().moe_pack_experts_cb(ctypes.byref(desc), _ptr(experts_canon), _ptr(shared_canon), _ptr(grid),
+                                     _ptr(router_w), _ptr(router_bias), _ptr(packed),
+                                     packed.numel() * packed.element_size(), ctypes.byref(h), _stream(stream)),
+           "moe_pack_experts_cb")
     return h.value
 
 
@@ -261,11 +273,16 @@ def moe_timing_stop():
 class PackedLayer:
     """A packed layer: owns its device buffer (torch uint8) and host handle."""
 
-    def __init__(self, desc: LayerDesc, experts_canon, shared_canon, router_w, router_bias, device="cuda"):
+    def __init__(self, desc: LayerDesc, experts_canon, shared_canon, router_w, router_bias, device="cuda",
+                 grid=None):
         self.desc = desc
         n = moe_packed_bytes(desc)
         self.buffer = torch.empty(n, dtype=torch.uint8, device=device)
-        self.handle = moe_pack_experts(desc, experts_canon, shared_canon, router_w, router_bias, self.buffer)
+        if desc.codebook:
+            self.handle = moe_pack_experts_cb(desc, experts_canon, shared_canon, grid, router_w, router_bias,
+                                              self.buffer)
+        else:
+            self.handle = moe_pack_experts(desc, experts_canon, shared_canon, router_w, router_bias, self.buffer)
 
     def workspace_bytes(self, T: int) -> int:
         return moe_workspace_bytes(self.handle, T)

@@ -12,6 +12,7 @@ namespace {
 template <int BITS, int NPER, bool A16>
 __global__ __launch_bounds__(64 * GU_NW) void gu_decode_kernel(GuArgs a) {
   __shared__ GuLds L;
+  load_grid<BITS>(a.X.grid16, threadIdx.x, 64 * GU_NW);  // (the selection's barriers publish it)
   gu_select<BITS, NPER, A16>(a, L, blockIdx.x == 0, blockIdx.x == 0);
   gu_items<BITS, A16>(a, L, blockIdx.x, gridDim.x, nullptr);
 }
@@ -20,27 +21,36 @@ __global__ __launch_bounds__(64 * GU_NW) void gu_decode_kernel(GuArgs a) {
 template <int BITS, int RT, bool A16>
 __global__ __launch_bounds__(512) void down_decode_kernel(DownArgs a) {
   __shared__ float red[8 * RT * 4 * 64];
+  if constexpr (BITS == MOE_KIND_CB) {
+    load_grid<BITS>(a.X.grid16, threadIdx.x, blockDim.x);
+    __syncthreads();
+  }
   down_role<BITS, RT, A16>(a, blockIdx.x, blockIdx.y, *a.n_slots, a.slot_expert, red);
 }
 
 // ---------------------------------------------------------------------------
 // Test export of one packed matrix through this file's own decoders: one
 // wavefront per chunk loads it with load_chunk and, for each of its 8
-// fragments, takes the unsigned codes from chunk_frag (the matrix-core B
-// operand) and the block scale from chunk_scale (the epilogue factor).  Lane
-// l = n + 16 q writes row 16 (RT rg + t) + n, inputs 32 (BK kg + j) + 8 q + c
-// of fragment f = BK t + j: code q_c - 2^(b-1) and scale times code (exact in
-// fp32).
+// fragments, takes the codes from chunk_frag (the matrix-core B operand:
+// unsigned for b-bit blocks, signed for codebook blocks) and the block scale
+// from chunk_scale (the epilogue factor).  Lane l = n + 16 q writes row
+// 16 (RT rg + t) + n, inputs 32 (BK kg + j) + 8 q + c of fragment f = BK t + j:
+// the signed code (q_c - 2^(b-1), or the codebook's) and scale times code
+// (exact in fp32).
 // ---------------------------------------------------------------------------
 template <int BITS>
 __global__ __launch_bounds__(256) void debug_decode_path_kernel(DebugPathArgs a) {
   const int chunk = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if constexpr (BITS == MOE_KIND_CB) {
+    load_grid<BITS>(a.grid16, threadIdx.x, blockDim.x);
+    __syncthreads();
+  }
   if (chunk >= a.n_rg * a.n_kg) return;
   const int rg = chunk / a.n_kg, kg = chunk - rg * a.n_kg;
   const int n = lane & 15, q = lane >> 4;
   ChunkRegs<BITS> c;
   load_chunk<BITS>(c, a.mat + (int64_t)chunk * a.chunk_bytes, lane);
-  const int off = 1 << (BITS - 1);
+  const int off = moe_code_offset(BITS);
 #pragma unroll
   for (int f = 0; f < 8; ++f) {
     const int t = f / a.BK, j = f - t * a.BK;
@@ -79,6 +89,11 @@ hipError_t launch_gu_decode(const GuArgs& a, int n_wg, hipStream_t s) {
     else if (np == 16) GU_LAUNCH(2, 16);
     else if (np == 32) GU_LAUNCH(2, 32);
     else GU_LAUNCH(2, 64);
+  } else if (a.bits == MOE_KIND_CB) {
+    if (np == 8) GU_LAUNCH(MOE_KIND_CB, 8);
+    else if (np == 16) GU_LAUNCH(MOE_KIND_CB, 16);
+    else if (np == 32) GU_LAUNCH(MOE_KIND_CB, 32);
+    else GU_LAUNCH(MOE_KIND_CB, 64);
   } else {
     if (np == 8) GU_LAUNCH(3, 8);
     else if (np == 16) GU_LAUNCH(3, 16);
@@ -93,7 +108,8 @@ hipError_t launch_debug_decode_path(const DebugPathArgs& a, int bits, hipStream_
   const int n = a.n_rg * a.n_kg;
   if (n == 0) return hipSuccess;
   if (bits == 2) hipLaunchKernelGGL(debug_decode_path_kernel<2>, dim3((n + 3) / 4), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(debug_decode_path_kernel<3>, dim3((n + 3) / 4), dim3(256), 0, s, a);
+  else if (bits == 3) hipLaunchKernelGGL(debug_decode_path_kernel<3>, dim3((n + 3) / 4), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(debug_decode_path_kernel<MOE_KIND_CB>, dim3((n + 3) / 4), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -107,6 +123,10 @@ hipError_t launch_down_decode(const DownArgs& a, int grid_x, int nw, hipStream_t
     case 23: return launch_down_t<3, 2>(a, grid_x, nw, s);
     case 43: return launch_down_t<3, 4>(a, grid_x, nw, s);
     case 83: return launch_down_t<3, 8>(a, grid_x, nw, s);
+    case 10 + MOE_KIND_CB: return launch_down_t<MOE_KIND_CB, 1>(a, grid_x, nw, s);
+    case 20 + MOE_KIND_CB: return launch_down_t<MOE_KIND_CB, 2>(a, grid_x, nw, s);
+    case 40 + MOE_KIND_CB: return launch_down_t<MOE_KIND_CB, 4>(a, grid_x, nw, s);
+    case 80 + MOE_KIND_CB: return launch_down_t<MOE_KIND_CB, 8>(a, grid_x, nw, s);
   }
   return hipErrorInvalidValue;
 }

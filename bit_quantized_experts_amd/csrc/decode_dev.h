@@ -41,24 +41,44 @@
 
 namespace {
 
+// The codebook grid of the layer being multiplied (codebook blocks only):
+// 512 entries of 4 fp16 magnitudes, staged by load_grid at kernel start.
+// Kernels of the b-bit kinds never touch it, so it takes no LDS there.
+__shared__ uint2 cb_grid_lds[512];
+
+// Stage the grid (all threads of the workgroup; a barrier must follow
+// before the first chunk_frag).
+template <int BITS>
+DEVI void load_grid(const uint32_t* grid16, int tid, int nthreads) {
+  if constexpr (BITS == MOE_KIND_CB)
+    for (int i = tid; i < 512; i += nthreads) cb_grid_lds[i] = reinterpret_cast<const uint2*>(grid16)[i];
+}
+
+// A lane's share of one chunk.  b-bit kinds: codes (16 B), the 8 fp16
+// scales of its row, and for 3 bits the high bits (8 B).  Codebook: index
+// bytes (in codes), scales, sign bits (in hbits) and index high bits (hi).
 template <int BITS>
 struct ChunkRegs {
   u32x4_t codes;
   u32x4_t scales;  // 8 fp16
-  u32x2_t hbits;   // 3-bit only
+  u32x2_t hbits;   // 3-bit: high code bits; codebook: sign bits
+  uint32_t hi;     // codebook: index high bits
 };
 
 template <int BITS>
 DEVI void load_chunk(ChunkRegs<BITS>& c, const uint8_t* chunk, int lane) {
   c.codes = ld128_nt(chunk + 16 * lane);
   c.scales = ld128_nt(chunk + 1024 + 16 * (lane & 15));
-  if constexpr (BITS == 3) c.hbits = ld64_nt(chunk + 1280 + 8 * lane);
+  if constexpr (BITS != 2) c.hbits = ld64_nt(chunk + 1280 + 8 * lane);
+  if constexpr (BITS == MOE_KIND_CB)
+    c.hi = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(chunk + 1792 + 2 * lane));
 }
 
 template <int BITS>
 DEVI half8_t chunk_frag(const ChunkRegs<BITS>& c, int f) {
   if constexpr (BITS == 2) return frag_q2(c.codes, f);
-  else return frag_q3(c.codes, c.hbits, f);
+  else if constexpr (BITS == 3) return frag_q3(c.codes, c.hbits, f);
+  else return frag_cb(c.codes, c.hi, c.hbits, f, cb_grid_lds);
 }
 
 DEVI float chunk_scale(const u32x4_t& s, int f) {
@@ -276,7 +296,7 @@ DEVI void mul_group(const GroupRegs<BITS>& r, const GuLds& L, int lb, int lane, 
 template <int BITS>
 DEVI void run_tile(const uint8_t* gate, const uint8_t* up, int64_t rowoff, int kg0, int kg1, int step, int wkg0,
                    const GuLds& L, int lane, float4_t& accg, float4_t& accu) {
-  constexpr int64_t CB = BITS == 2 ? 1280 : 1792;
+  constexpr int64_t CB = moe_chunk_bytes(BITS);
   if (kg0 >= kg1) return;
   const int nsteps = (kg1 - 1 - kg0) / step + 1;
   const int last = kg0 + (nsteps - 1) * step;
@@ -401,7 +421,7 @@ DEVI void gu_select(const GuArgs& a, GuLds& L, bool publish_routing, bool publis
 // them).
 template <int BITS, bool A16>
 DEVI void gu_items(const GuArgs& a, GuLds& L, int wg, int n_wg, uint32_t* h_ready) {
-  constexpr int64_t CB = BITS == 2 ? 1280 : 1792;
+  constexpr int64_t CB = moe_chunk_bytes(BITS);
   const int tid = opaque_tid(), lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int T = a.T;
@@ -540,7 +560,7 @@ DEVI half8_t h_fragment(const float4_t (&v)[2], int eh, int lane) {
 // 8 x RT*4 x 64 floats of LDS.  Ends with a barrier (red is free again).
 template <int BITS, int RT, bool A16>
 DEVI void down_role(const DownArgs& a, int rg, int sp, int ns, const int* slots, float* red) {
-  constexpr int CB = BITS == 2 ? 1280 : 1792;
+  constexpr int CB = moe_chunk_bytes(BITS);
   constexpr int BK = 8 / RT;
   constexpr int BATCH = 2;
   constexpr int R = A16 ? MOE_MAX_TOK_F16ACT : MOE_MAX_TOK_DECODE;
@@ -577,7 +597,7 @@ DEVI void down_role(const DownArgs& a, int rg, int sp, int ns, const int* slots,
   // 4 (lane >> 4) + i (hi/lo: the lo rows 8..15 are tokens 0..7 again)
   const int tok_a = A16 ? (lane & 15) : (lane & 7);
   const int tok_c = A16 ? 4 * (lane >> 4) : (4 * (lane >> 4)) & 7;
-  const float off = -(float)(1 << (BITS - 1));
+  const float off = -(float)moe_code_offset(BITS);
   const half8_t ones = half8_t{1, 1, 1, 1, 1, 1, 1, 1};
   const __amdgpu_buffer_rsrc_t mr = coh_rsrc(a.hmax);
 
@@ -634,7 +654,8 @@ DEVI void down_role(const DownArgs& a, int rg, int sp, int ns, const int* slots,
         const half8_t A = h_fragment<A16>(hv[q][j], eh_a, lane);
         // the accumulator seed -2^(b-1) sum_k A[m][k], with the row sums laid
         // out as the accumulators by a product with an all-ones B operand
-        const float4_t cin = off * mfma16x16x32(A, ones, float4_t{0.f, 0.f, 0.f, 0.f});
+        float4_t cin = float4_t{0.f, 0.f, 0.f, 0.f};
+        if constexpr (moe_code_offset(BITS) != 0) cin = off * mfma16x16x32(A, ones, cin);
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
           const int f = t * BK + j;

@@ -66,6 +66,28 @@ DEVI half8_t frag_q3(const u32x4_t& w, const u32x2_t& hbits, int f) {
 }
 
 // ---------------------------------------------------------------------------
+// Codebook fragments.  The lane's chunk data: 16 index bytes (bytes 2f and
+// 2f+1: the low 8 bits of the two grid indices of fragment f, inputs 8q..8q+3
+// and 8q+4..8q+7), 16 index high bits (bits 2f, 2f+1) and 64 sign bits (bits
+// 8f..8f+7: inputs 8q..8q+7 of fragment f, set = negative).  The grid sits in
+// LDS as 4 fp16 magnitudes per entry (two words), so one 64-bit LDS read
+// gives 4 exact codes; the sign bits go into the fp16 sign bits by XOR.
+// ---------------------------------------------------------------------------
+DEVI half8_t frag_cb(const u32x4_t& idx, uint32_t hi, const u32x2_t& sg, int f, const uint2* grid) {
+  const uint32_t w = idx[f >> 1] >> (16 * (f & 1));
+  const uint32_t i0 = (w & 0xffu) | (((hi >> (2 * f)) & 1u) << 8);
+  const uint32_t i1 = ((w >> 8) & 0xffu) | (((hi >> (2 * f + 1)) & 1u) << 8);
+  const uint2 m0 = grid[i0], m1 = grid[i1];
+  const uint32_t s = (sg[f >> 2] >> (8 * (f & 3))) & 0xffu;
+  u32x4_t r;
+  r[0] = m0.x ^ (((s & 1u) << 15) | ((s & 2u) << 30));
+  r[1] = m0.y ^ (((s & 4u) << 13) | ((s & 8u) << 28));
+  r[2] = m1.x ^ (((s & 16u) << 11) | ((s & 32u) << 26));
+  r[3] = m1.y ^ (((s & 64u) << 9) | ((s & 128u) << 24));
+  return __builtin_bit_cast(half8_t, r);
+}
+
+// ---------------------------------------------------------------------------
 // Buffer loads that bypass nothing special: plain 128/64-bit global loads.
 // ---------------------------------------------------------------------------
 DEVI u32x4_t ld128(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }

@@ -97,7 +97,7 @@ bool make_mat(int rows, int cols, int bits, moe_mat_layout* L, int bk = 0) {
   if (rows % (16 * L->RT) != 0) return false;
   L->n_rg = rows / (16 * L->RT);
   L->n_kg = L->nb / L->BK;
-  L->chunk_bytes = bits == 2 ? 1280 : 1792;
+  L->chunk_bytes = moe_chunk_bytes(bits);
   L->bytes = (int64_t)L->n_rg * L->n_kg * L->chunk_bytes;
   return true;
 }
@@ -121,12 +121,19 @@ bool make_expert(int d, int I, int bits, moe_expert_layout* X, int bk_down) {
   return true;
 }
 
-int64_t canon_block_bytes(int bits) { return 2 + 4 * bits; }
+// Canonical bytes of one block of a kind (2, 3: b-bit codes; codebook: 15).
+int64_t canon_block_bytes(int kind) { return kind == MOE_KIND_CB ? 15 : 2 + 4 * kind; }
+
+// The kernels' block kind of a descriptor (the layer keeps it in `bits`).
+int desc_kind(const moe_layer_desc* D) { return D->codebook ? MOE_KIND_CB : D->bits; }
 
 int check_desc(const moe_layer_desc* D) {
   if (!D) return fail(MOE_ERR_ARG, "desc is NULL");
   if (D->block != 32) return fail(MOE_ERR_UNSUPPORTED, "block must be 32 (got %d)", D->block);
   if (D->bits != 2 && D->bits != 3) return fail(MOE_ERR_UNSUPPORTED, "bits must be 2 or 3 (got %d)", D->bits);
+  if (D->codebook != 0 && D->codebook != 1) return fail(MOE_ERR_ARG, "codebook must be 0 or 1 (got %d)", D->codebook);
+  if (D->codebook && D->bits != 3)
+    return fail(MOE_ERR_UNSUPPORTED, "codebook blocks are of the 3-bit class: bits must be 3 (got %d)", D->bits);
   if (D->d_model <= 0 || D->d_model % 256) return fail(MOE_ERR_UNSUPPORTED, "d_model must be a positive multiple of 256 (got %d)", D->d_model);
   if (D->d_model > 8192) return fail(MOE_ERR_UNSUPPORTED, "d_model above 8192 not supported (got %d)", D->d_model);
   if (D->n_experts < 1 || D->n_experts > MOE_MAX_E) return fail(MOE_ERR_UNSUPPORTED, "n_experts must be in [1, %d] (got %d)", MOE_MAX_E, D->n_experts);
@@ -138,9 +145,9 @@ int check_desc(const moe_layer_desc* D) {
 }
 
 // packed buffer: [status 256 B][router_w][router_b][router hi][router lo]
-// [router exponents][E experts][shared]
+// [router exponents][bounds][codebook grid (codebook blocks)][E experts][shared]
 struct PackedLayout {
-  int64_t off_status, off_rw, off_rb, off_rwh, off_rwl, off_rew, off_hb, off_ex, off_sh, total;
+  int64_t off_status, off_rw, off_rb, off_rwh, off_rwl, off_rew, off_hb, off_grid, off_ex, off_sh, total;
 };
 
 int e16_of(int E) { return (E + 15) / 16 * 16; }
@@ -155,7 +162,8 @@ PackedLayout packed_layout(const moe_layer_desc* D, const moe_expert_layout& ex,
   P.off_rwl = P.off_rwh + moe_align256(E16 * D->d_model * 2);
   P.off_rew = P.off_rwl + moe_align256(E16 * D->d_model * 2);
   P.off_hb = P.off_rew + moe_align256(E16 * 4);
-  P.off_ex = P.off_hb + moe_align256((int64_t)(D->n_experts + 1) * 8);  // hb then ed
+  P.off_grid = P.off_hb + moe_align256((int64_t)(D->n_experts + 1) * 8);  // hb then ed
+  P.off_ex = P.off_grid + (D->codebook ? 512 * 4 * 2 : 0);
   P.off_sh = P.off_ex + (int64_t)D->n_experts * ex.bytes;
   P.total = P.off_sh + (D->d_ff_shared > 0 ? sh.bytes : 0);
   return P;
@@ -390,6 +398,7 @@ ExpertSet expert_set(const moe_layer* L) {
   X.sh_off_gate = L->sh.off_gate;
   X.sh_off_up = L->sh.off_up;
   X.sh_off_down = L->sh.off_down;
+  X.grid16 = L->grid16;
   return X;
 }
 
@@ -421,7 +430,7 @@ int decode_layer(const moe_layer* L, const LayerInput& in, float eps, int T, flo
   ra.T = T;
   ra.d = d;
   ra.E = E;
-  ra.code_off = 1 << (L->bits - 1);
+  ra.code_off = moe_code_offset(L->bits);
   ra.do_logits = !forced;
   ra.act16 = act16;
   ra.lp = reinterpret_cast<float*>(ws + W.lp);
@@ -720,22 +729,23 @@ int moe_packed_bytes(const moe_layer_desc* desc, size_t* bytes) {
   if (!bytes) return fail(MOE_ERR_ARG, "bytes is NULL");
   moe_expert_layout ex{}, sh{};
   const int bkd = down_bk(desc->d_ff, desc->d_ff_shared);
-  if (!make_expert(desc->d_model, desc->d_ff, desc->bits, &ex, bkd))
+  if (!make_expert(desc->d_model, desc->d_ff, desc_kind(desc), &ex, bkd))
     return fail(MOE_ERR_UNSUPPORTED, "expert shape not tileable");
-  if (desc->d_ff_shared > 0 && !make_expert(desc->d_model, desc->d_ff_shared, desc->bits, &sh, bkd))
+  if (desc->d_ff_shared > 0 && !make_expert(desc->d_model, desc->d_ff_shared, desc_kind(desc), &sh, bkd))
     return fail(MOE_ERR_UNSUPPORTED, "shared expert shape not tileable");
   *bytes = (size_t)packed_layout(desc, ex, sh).total;
   return MOE_OK;
 }
 
-int moe_pack_experts(const moe_layer_desc* desc, const void* experts_canon, const void* shared_canon,
-                     const float* router_w, const float* router_bias, void* packed, size_t packed_bytes,
-                     moe_layer** out, void* stream) {
+static int pack_layer(const moe_layer_desc* desc, const void* experts_canon, const void* shared_canon,
+                      const uint8_t* grid, const float* router_w, const float* router_bias, void* packed,
+                      size_t packed_bytes, moe_layer** out, void* stream) {
   size_t need = 0;
   int rc = moe_packed_bytes(desc, &need);
   if (rc) return rc;
   if (!out) return fail(MOE_ERR_ARG, "out is NULL");
   *out = nullptr;
+  if (desc->codebook && !grid) return fail(MOE_ERR_ARG, "codebook blocks need a grid (moe_pack_experts_cb)");
   if (!experts_canon || !router_w || !packed) return fail(MOE_ERR_ARG, "experts_canon, router_w and packed must be non-NULL");
   if ((desc->d_ff_shared > 0) != (shared_canon != nullptr))
     return fail(MOE_ERR_ARG, "shared_canon must be given exactly when d_ff_shared > 0");
@@ -754,7 +764,7 @@ int moe_pack_experts(const moe_layer_desc* desc, const void* experts_canon, cons
   L->I = desc->d_ff;
   L->Is = desc->d_ff_shared;
   L->k = desc->top_k;
-  L->bits = desc->bits;
+  L->bits = desc_kind(desc);
   const int bkd = down_bk(L->I, L->Is);
   make_expert(L->d, L->I, L->bits, &L->ex, bkd);
   if (L->Is > 0) make_expert(L->d, L->Is, L->bits, &L->sh, bkd);
@@ -772,6 +782,7 @@ int moe_pack_experts(const moe_layer_desc* desc, const void* experts_canon, cons
   L->E16 = e16_of(L->E);
   L->experts = base + P.off_ex;
   L->shared = L->Is > 0 ? base + P.off_sh : nullptr;
+  L->grid16 = desc->codebook ? reinterpret_cast<const uint32_t*>(base + P.off_grid) : nullptr;
 
   auto bail = [&](int code) { delete L; return code; };
   uint32_t* status = reinterpret_cast<uint32_t*>(base + P.off_status);
@@ -789,7 +800,16 @@ int moe_pack_experts(const moe_layer_desc* desc, const void* experts_canon, cons
                               const_cast<_Float16*>(L->router_wl), const_cast<int32_t*>(L->router_ew), s)) != hipSuccess)
     return bail(fail(MOE_ERR_HIP, "router split: %s", hipGetErrorString(e)));
   const int64_t bb = canon_block_bytes(L->bits);
-  {
+  if (L->grid16 &&
+      (e = launch_pack_grid(grid, reinterpret_cast<uint16_t*>(const_cast<uint32_t*>(L->grid16)), status, s)) != hipSuccess)
+    return bail(fail(MOE_ERR_HIP, "grid: %s", hipGetErrorString(e)));
+  if (L->bits == MOE_KIND_CB) {
+    // the exponent bounds serve the prefill kernels only, which codebook
+    // blocks do not run
+    if ((e = launch_fill_u32(reinterpret_cast<uint32_t*>(const_cast<int32_t*>(L->hbound)), 2 * (size_t)(L->E + 1), 0u,
+                             s)) != hipSuccess)
+      return bail(fail(MOE_ERR_HIP, "bound fill: %s", hipGetErrorString(e)));
+  } else {
     int32_t* hb = const_cast<int32_t*>(L->hbound);
     int32_t* edp = const_cast<int32_t*>(L->dbound);
     const int64_t stride = 3 * (int64_t)L->I * (L->d / 32) * bb;
@@ -822,9 +842,25 @@ int moe_pack_experts(const moe_layer_desc* desc, const void* experts_canon, cons
   if ((e = hipMemcpyAsync(&flag, status, 4, hipMemcpyDeviceToHost, s)) != hipSuccess)
     return bail(fail(MOE_ERR_HIP, "status copy: %s", hipGetErrorString(e)));
   if ((e = hipStreamSynchronize(s)) != hipSuccess) return bail(fail(MOE_ERR_HIP, "sync: %s", hipGetErrorString(e)));
-  if (flag) return bail(fail(MOE_ERR_DATA, "a block scale is inf/nan or has magnitude >= 8192"));
+  if (flag & 1u) return bail(fail(MOE_ERR_DATA, "a block scale is inf/nan or has magnitude >= 8192"));
+  if (flag & 2u) return bail(fail(MOE_ERR_DATA, "a codebook magnitude is above 127"));
   *out = L;
   return MOE_OK;
+}
+
+int moe_pack_experts(const moe_layer_desc* desc, const void* experts_canon, const void* shared_canon,
+                     const float* router_w, const float* router_bias, void* packed, size_t packed_bytes,
+                     moe_layer** out, void* stream) {
+  return pack_layer(desc, experts_canon, shared_canon, nullptr, router_w, router_bias, packed, packed_bytes, out,
+                    stream);
+}
+
+int moe_pack_experts_cb(const moe_layer_desc* desc, const void* experts_canon, const void* shared_canon,
+                        const uint8_t* grid, const float* router_w, const float* router_bias, void* packed,
+                        size_t packed_bytes, moe_layer** out, void* stream) {
+  if (desc && !desc->codebook) return fail(MOE_ERR_ARG, "moe_pack_experts_cb needs desc->codebook = 1");
+  if (!grid || !aligned(grid, 16)) return fail(MOE_ERR_ARG, "grid must be non-NULL and 16-byte aligned");
+  return pack_layer(desc, experts_canon, shared_canon, grid, router_w, router_bias, packed, packed_bytes, out, stream);
 }
 
 int moe_layer_release(moe_layer* layer) {
@@ -839,8 +875,9 @@ int moe_layer_get_desc(const moe_layer* L, moe_layer_desc* out) {
   out->d_ff = L->I;
   out->d_ff_shared = L->Is;
   out->top_k = L->k;
-  out->bits = L->bits;
+  out->bits = L->bits == MOE_KIND_CB ? 3 : L->bits;
   out->block = 32;
+  out->codebook = L->bits == MOE_KIND_CB;
   return MOE_OK;
 }
 
@@ -883,7 +920,7 @@ int moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
 
 // Argument checks shared by the layer entry points.
 static int layer_args(const moe_layer* L, const float* x, int T, float* y, const moe_route_io* route, void* ws,
-                      size_t ws_bytes) {
+                      size_t ws_bytes, int max_tok = MOE_MAX_TOK_DECODE) {
   if (!L) return fail(MOE_ERR_ARG, "layer is NULL");
   if (T < 0) return fail(MOE_ERR_ARG, "T must be >= 0");
   if (T == 0) return MOE_OK;
@@ -895,6 +932,8 @@ static int layer_args(const moe_layer* L, const float* x, int T, float* y, const
   if (xb < yb + nbytes && yb < xb + nbytes) return fail(MOE_ERR_ARG, "x and y must not alias");
   if (route && ((route->in_idx == nullptr) != (route->in_w == nullptr)))
     return fail(MOE_ERR_ARG, "in_idx and in_w must be given together");
+  if (L->bits == MOE_KIND_CB && T > max_tok)
+    return fail(MOE_ERR_UNSUPPORTED, "codebook blocks run the decode path only: T <= %d (got %d)", max_tok, T);
   size_t need;
   int rc = check_ws(L, T, 1, ws, ws_bytes, &need);
   if (rc) return rc;
@@ -955,7 +994,7 @@ static int persist_pass(const moe_layer* const* layers, int n_layers, const floa
   P.Is = L->Is;
   P.bits = L->bits;
   P.has_shared = L->Is > 0;
-  P.code_off = 1 << (L->bits - 1);
+  P.code_off = moe_code_offset(L->bits);
   P.n_cs = W.n_cs;
   P.n_rs = W.n_rs;
   P.S = W.S;
@@ -1056,7 +1095,7 @@ int moe_layer_forward_noalloc(const moe_layer* L, const float* x, int T, float* 
 int moe_layer_forward_f16act(const moe_layer* L, const float* x, int T, float* y, const moe_route_io* route,
                              void* ws, size_t ws_bytes, void* stream) {
   if (T > MOE_MAX_TOK_F16ACT) return fail(MOE_ERR_UNSUPPORTED, "T above %d not supported with fp16 activations", MOE_MAX_TOK_F16ACT);
-  int rc = layer_args(L, x, T, y, route, ws, ws_bytes);
+  int rc = layer_args(L, x, T, y, route, ws, ws_bytes, MOE_MAX_TOK_F16ACT);
   if (rc || T == 0) return rc;
   return decode_layer_out(L, x, T, y, route, reinterpret_cast<uint8_t*>(ws), reinterpret_cast<hipStream_t>(stream),
                           true);
@@ -1076,6 +1115,9 @@ static int stack_args(const moe_layer* const* layers, int n_layers, const float*
   for (int l = 0; l < n_layers; ++l) {
     if (!layers[l]) return fail(MOE_ERR_ARG, "layer %d is NULL", l);
     if (layers[l]->d != d) return fail(MOE_ERR_ARG, "layer %d has d_model %d, expected %d", l, layers[l]->d, d);
+    if (layers[l]->bits == MOE_KIND_CB && T > 2 * MOE_MAX_TOK_DECODE)
+      return fail(MOE_ERR_UNSUPPORTED, "codebook blocks run the decode path only: T <= %d (got %d)",
+                  2 * MOE_MAX_TOK_DECODE, T);
     size_t need;
     int rc = check_ws(layers[l], T, n_layers, ws, ws_bytes, &need);
     if (rc) return rc;
@@ -1237,7 +1279,8 @@ int moe_debug_unpack(const moe_layer* L, int expert, int mat, int8_t* codes, flo
   const uint8_t* base = expert < 0 ? L->shared : L->experts + (int64_t)expert * L->ex.bytes;
   const moe_mat_layout& M = mat == 0 ? X.gate : mat == 1 ? X.up : X.down;
   const int64_t off = mat == 0 ? X.off_gate : mat == 1 ? X.off_up : X.off_down;
-  HIPCHK(launch_debug_unpack(base + off, M, L->bits, codes, w_f32, w_f16, reinterpret_cast<hipStream_t>(stream)));
+  HIPCHK(launch_debug_unpack(base + off, reinterpret_cast<const uint16_t*>(L->grid16), M, L->bits, codes, w_f32, w_f16,
+                             reinterpret_cast<hipStream_t>(stream)));
   return MOE_OK;
 }
 
@@ -1250,6 +1293,7 @@ int moe_debug_unpack_path(const moe_layer* L, int expert, int mat, int path, int
   if (path < 0 || path > 2) return fail(MOE_ERR_ARG, "path must be 0, 1 or 2");
   if (path == 0 && w_f16) return fail(MOE_ERR_ARG, "path 0 exports codes and w_f32 only");
   if (path > 0 && (codes || w_f32)) return fail(MOE_ERR_ARG, "paths 1 and 2 export w_f16 only");
+  if (path > 0 && L->bits == MOE_KIND_CB) return fail(MOE_ERR_UNSUPPORTED, "codebook blocks have no prefill path");
   if (!codes && !w_f32 && !w_f16) return MOE_OK;
   const moe_expert_layout& X = expert < 0 ? L->sh : L->ex;
   const uint8_t* base = expert < 0 ? L->shared : L->experts + (int64_t)expert * L->ex.bytes;
@@ -1257,6 +1301,7 @@ int moe_debug_unpack_path(const moe_layer* L, int expert, int mat, int path, int
   const int64_t off = mat == 0 ? X.off_gate : mat == 1 ? X.off_up : X.off_down;
   DebugPathArgs a{};
   a.mat = base + off;
+  a.grid16 = L->grid16;
   a.cols = M.cols;
   a.BK = M.BK;
   a.RT = M.RT;

@@ -55,7 +55,9 @@ struct moe_expert_layout {
 
 // Host-side handle (opaque to callers).
 struct moe_layer {
-  int32_t d, E, I, Is, k, bits;
+  int32_t d, E, I, Is, k;
+  int32_t bits;             // block kind: 2, 3 (b-bit codes) or MOE_KIND_CB (codebook blocks)
+  const uint32_t* grid16;   // codebook blocks: device [512][4] fp16 magnitudes (else null)
   moe_expert_layout ex;   // routed experts
   moe_expert_layout sh;   // shared expert (valid if Is > 0)
   const uint8_t* packed;  // device base

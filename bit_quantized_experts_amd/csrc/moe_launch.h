@@ -63,6 +63,7 @@ struct ExpertSet {
   const uint8_t* shared;   // shared expert or null
   int64_t off_gate, off_up, off_down;           // routed
   int64_t sh_off_gate, sh_off_up, sh_off_down;  // shared
+  const uint32_t* grid16;  // codebook blocks: [512][2] words, 4 fp16 magnitudes per entry (else null)
 };
 
 // Slot list of a decode layer: slot 0 is the shared expert (if any), then the
@@ -100,6 +101,16 @@ struct DownArgs {
   int32_t act16;  // 1: A rows are 16 tokens in fp16 (else 8 tokens as fp16 hi + lo)
   float* ypart;   // ws [S][R][d], R = 16 with act16, else 8
 };
+
+// Block kinds as the kernels' template tag: 2 and 3 are b-bit code blocks,
+// MOE_KIND_CB codebook blocks (32 weights: fp16 scale, eight 9-bit indices
+// into a grid of 512 entries of 4 magnitudes, 32 sign bits).  A packed chunk
+// holds 8 fragments of 16 rows x 32 inputs (4096 weights) in every kind:
+// 1280, 1792 and 1920 bytes.
+#define MOE_KIND_CB 4
+constexpr int moe_chunk_bytes(int kind) { return kind == 2 ? 1280 : kind == 3 ? 1792 : 1920; }
+// The unsigned-code offset the accumulator seed removes (0: signed codes).
+constexpr int moe_code_offset(int kind) { return kind == MOE_KIND_CB ? 0 : 1 << (kind - 1); }
 
 // Persistent decode pass over up to MOE_PERSIST_MAX_LAYERS layers of one
 // shape (persist.hip).  Every layer's packed buffer has the same layout, so a
@@ -160,12 +171,14 @@ hipError_t launch_persist(const PersistArgs& a, int rt, int grid, bool act16, si
 hipError_t launch_pack_matrix(const uint8_t* canon, int64_t canon_stride, uint8_t* out, int64_t out_stride,
                               int n_experts, const moe_mat_layout& L, int bits, uint32_t* bad_scale,
                               hipStream_t s);
-hipError_t launch_debug_unpack(const uint8_t* mat, const moe_mat_layout& L, int bits, int8_t* codes, float* w32,
-                               uint16_t* w16, hipStream_t s);
+hipError_t launch_debug_unpack(const uint8_t* mat, const uint16_t* grid16, const moe_mat_layout& L, int bits,
+                               int8_t* codes, float* w32, uint16_t* w16, hipStream_t s);
+hipError_t launch_pack_grid(const uint8_t* grid, uint16_t* out, uint32_t* bad, hipStream_t s);
 
 // Test export of one packed matrix through an expert kernel's own decoder.
 struct DebugPathArgs {
   const uint8_t* mat;  // packed matrix
+  const uint32_t* grid16;  // codebook blocks: the layer's fp16 grid (else null)
   int32_t cols, BK, RT, n_rg, n_kg, chunk_bytes;
   int32_t full;        // prefill: 1 = whole chunks (load_full), 0 = half chunks (load_half)
   int8_t* codes;       // decode: signed codes [rows][cols], or null

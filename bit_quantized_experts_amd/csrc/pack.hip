@@ -5,7 +5,11 @@
 //
 // Canonical block (input): fp16 scale (little endian) then 4b code bytes;
 // code j = bits [b*j, b*j+b) of the code bytes' little-endian bitstream,
-// value q_j - 2^(b-1).  Keeping experts in their low-bit blocks and
+// value q_j - 2^(b-1).  Codebook blocks (kind MOE_KIND_CB, 15 bytes): fp16
+// scale, the low bytes of eight 9-bit grid indices (index i: inputs
+// 4i..4i+3), a byte of index high bits (bit i), then 32 sign bits (bit j of
+// the little-endian word: input j negative); the packed chunk keeps the same
+// fields, regrouped per lane.  Keeping experts in their low-bit blocks and
 // multiplying from them is the method of the strata-mlx wiki (opening
 // feature list, first item); the block structure follows the ggml block types
 // named in that wiki's credits list.
@@ -33,13 +37,15 @@ __global__ __launch_bounds__(256) void pack_matrix_kernel(PackArgs a) {
   const int64_t chunk = r >> 6;
   const int rg = (int)(chunk / a.n_kg), kg = (int)(chunk - (int64_t)rg * a.n_kg);
   const int n = lane & 15, q = lane >> 4;
-  const int bb = 2 + 4 * a.bits, nb = a.cols / 32;
+  const bool cbk = a.bits == MOE_KIND_CB;
+  const int bb = cbk ? 15 : 2 + 4 * a.bits, nb = a.cols / 32;
   const uint8_t* cb = a.canon + (int64_t)e * a.canon_stride;
   uint8_t* ob = a.out + (int64_t)e * a.out_stride + chunk * a.chunk_bytes;
 
   uint32_t dw[4] = {0u, 0u, 0u, 0u};
   uint32_t hw[2] = {0u, 0u};
   uint32_t sc[4] = {0u, 0u, 0u, 0u};
+  uint32_t ih = 0u;
   bool bad = false;
   for (int f = 0; f < 8; ++f) {
     const int t = f / a.BK, j = f - t * a.BK;
@@ -49,6 +55,13 @@ __global__ __launch_bounds__(256) void pack_matrix_kernel(PackArgs a) {
     const uint32_t s = (uint32_t)B[0] | ((uint32_t)B[1] << 8);
     bad |= (s & 0x7fffu) >= 0x7000u;  // exponent field 28..31: |s| >= 8192, inf or nan
     sc[f >> 1] |= s << (16 * (f & 1));
+    if (cbk) {
+      // indices 2q, 2q+1 (inputs 8q..8q+7), their high bits, sign byte q
+      dw[f >> 1] |= ((uint32_t)B[2 + 2 * q] | ((uint32_t)B[3 + 2 * q] << 8)) << (16 * (f & 1));
+      ih |= ((uint32_t)(B[10] >> (2 * q)) & 3u) << (2 * f);
+      hw[f >> 2] |= (uint32_t)B[11 + q] << (8 * (f & 3));
+      continue;
+    }
     uint32_t v;
     if (a.bits == 2) {
       v = (uint32_t)B[2 + 2 * q] | ((uint32_t)B[3 + 2 * q] << 8);
@@ -63,12 +76,27 @@ __global__ __launch_bounds__(256) void pack_matrix_kernel(PackArgs a) {
   }
   *reinterpret_cast<u32x4_t*>(ob + 16 * lane) = u32x4_t{dw[0], dw[1], dw[2], dw[3]};
   if (q == 0) *reinterpret_cast<u32x4_t*>(ob + 1024 + 16 * n) = u32x4_t{sc[0], sc[1], sc[2], sc[3]};
-  if (a.bits == 3) *reinterpret_cast<u32x2_t*>(ob + 1280 + 8 * lane) = u32x2_t{hw[0], hw[1]};
+  if (a.bits != 2) *reinterpret_cast<u32x2_t*>(ob + 1280 + 8 * lane) = u32x2_t{hw[0], hw[1]};
+  if (cbk) *reinterpret_cast<uint16_t*>(ob + 1792 + 2 * lane) = (uint16_t)ih;
   if (bad) atomicOr(a.bad_scale, 1u);
+}
+
+// The codebook grid of a layer: 512 x 4 unsigned magnitudes (bytes) to fp16
+// (exact), rejecting magnitudes above 127 through the status word.
+__global__ __launch_bounds__(256) void pack_grid_kernel(const uint8_t* grid, uint16_t* out, uint32_t* bad) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= 512 * 4) return;
+  const uint32_t m = grid[i];
+  const _Float16 h = (_Float16)(float)m;
+  uint16_t hb;
+  __builtin_memcpy(&hb, &h, 2);
+  out[i] = hb;
+  if (m > 127u) atomicOr(bad, 2u);
 }
 
 struct UnpackArgs {
   const uint8_t* mat;  // packed matrix
+  const uint16_t* grid16;  // codebook blocks: fp16 grid [512][4]
   int32_t rows, cols, bits, BK, RT, n_kg, chunk_bytes;
   int8_t* codes;
   float* w32;
@@ -85,15 +113,26 @@ __global__ __launch_bounds__(256) void debug_unpack_kernel(UnpackArgs a) {
   const int kg = blk / a.BK, j = blk - kg * a.BK, f = t * a.BK + j;
   const int lane = n + 16 * q;
   const uint8_t* ch = a.mat + ((int64_t)rg * a.n_kg + kg) * a.chunk_bytes;
-  const uint32_t dw = *reinterpret_cast<const uint32_t*>(ch + 16 * lane + 4 * (f >> 1));
-  uint32_t qv = (dw >> (4 * c + 2 * (f & 1))) & 3u;
-  if (a.bits == 3) {
-    const uint32_t hw = *reinterpret_cast<const uint32_t*>(ch + 1280 + 8 * lane + 4 * (f >> 2));
-    qv += 4u * ((hw >> (4 * c + (f & 3))) & 1u);
+  int code;
+  if (a.bits == MOE_KIND_CB) {
+    const int i = c >> 2;  // first or second index of the fragment
+    const uint32_t lo = ch[16 * lane + 2 * f + i];
+    const uint32_t hb = *reinterpret_cast<const uint16_t*>(ch + 1792 + 2 * lane);
+    const uint32_t index = lo | (((hb >> (2 * f + i)) & 1u) << 8);
+    const int m = (int)half_bits_to_float(a.grid16[4 * index + (c & 3)]);
+    const uint32_t sg = ch[1280 + 8 * lane + f];
+    code = ((sg >> c) & 1u) ? -m : m;
+  } else {
+    const uint32_t dw = *reinterpret_cast<const uint32_t*>(ch + 16 * lane + 4 * (f >> 1));
+    uint32_t qv = (dw >> (4 * c + 2 * (f & 1))) & 3u;
+    if (a.bits == 3) {
+      const uint32_t hw = *reinterpret_cast<const uint32_t*>(ch + 1280 + 8 * lane + 4 * (f >> 2));
+      qv += 4u * ((hw >> (4 * c + (f & 3))) & 1u);
+    }
+    code = (int)qv - (1 << (a.bits - 1));
   }
-  const int code = (int)qv - (1 << (a.bits - 1));
   const uint32_t sb = *reinterpret_cast<const uint16_t*>(ch + 1024 + 16 * n + 2 * f);
-  const float w = half_bits_to_float(sb) * (float)code;  // exact: <= 14 significant bits
+  const float w = half_bits_to_float(sb) * (float)code;  // exact: <= 18 significant bits
   if (a.codes) a.codes[gid] = (int8_t)code;
   if (a.w32) a.w32[gid] = w;
   if (a.w16) {
@@ -118,9 +157,14 @@ hipError_t launch_pack_matrix(const uint8_t* canon, int64_t canon_stride, uint8_
   return hipGetLastError();
 }
 
-hipError_t launch_debug_unpack(const uint8_t* mat, const moe_mat_layout& L, int bits, int8_t* codes, float* w32,
-                               uint16_t* w16, hipStream_t s) {
-  UnpackArgs a{mat, L.rows, L.cols, bits, L.BK, L.RT, L.n_kg, L.chunk_bytes, codes, w32, w16};
+hipError_t launch_pack_grid(const uint8_t* grid, uint16_t* out, uint32_t* bad, hipStream_t s) {
+  hipLaunchKernelGGL(pack_grid_kernel, dim3(8), dim3(256), 0, s, grid, out, bad);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_unpack(const uint8_t* mat, const uint16_t* grid16, const moe_mat_layout& L, int bits,
+                               int8_t* codes, float* w32, uint16_t* w16, hipStream_t s) {
+  UnpackArgs a{mat, grid16, L.rows, L.cols, bits, L.BK, L.RT, L.n_kg, L.chunk_bytes, codes, w32, w16};
   const int64_t n = (int64_t)L.rows * L.cols;
   const int64_t blocks = (n + 255) / 256;
   if (blocks == 0) return hipSuccess;

@@ -37,7 +37,7 @@ namespace {
 // then), so the down roles find them there instead of waiting for HBM.
 template <int BITS, int RT>
 DEVI void warm_down_weights(const PersistArgs& P, const ExpertSet& X, GuLds& L, int b, int G) {
-  constexpr int CB = BITS == 2 ? 1280 : 1792, LPC = CB / 128;
+  constexpr int CB = moe_chunk_bytes(BITS), LPC = CB / 128;
   const int tid = opaque_tid(), lane = tid & 63, wv = tid >> 6;
   const int S = P.S, n_rg = P.n_rg, base = P.has_shared ? 1 : 0;
   const int ns = base + L.S.n_routed;

@@ -32,6 +32,18 @@
  * stored back to back; the shared expert is a separate buffer of the same
  * layout with its own intermediate size.
  *
+ * Codebook blocks (desc.codebook = 1, packed by moe_pack_experts_cb).  The
+ * codebook block types that the model files also use multiply magnitudes
+ * looked up in a table that ships with the file [strata-mlx wiki, opening
+ * feature list, first item ("nine block types"), and credits list (codebook
+ * tables)]; this library takes the table as an input.  A block holds 32
+ * weights in 15 bytes: [0,2) fp16 scale; [2,10) the low 8 bits of eight 9-bit
+ * grid indices, index i covering weights 4i..4i+3; byte 10, bit i = bit 8 of
+ * index i; [11,15) 32 sign bits, bit j of the little-endian word set = weight
+ * j negative.  Weight j = scale * (+-1) * grid[index][j % 4], grid = 512
+ * entries of 4 unsigned magnitudes (bytes, at most 127).  Same expert layout
+ * as above with 15-byte blocks.
+ *
  * Conventions for every entry point:
  *   - Return value: MOE_OK (0) or a positive MOE_ERR_* code.  On error,
  *     moe_last_error() returns a message for the calling thread.  Nothing is
@@ -72,8 +84,9 @@ typedef struct moe_layer_desc {
     int32_t d_ff;         /* I: routed-expert intermediate size; multiple of 32 */
     int32_t d_ff_shared;  /* shared-expert intermediate size, multiple of 32, or 0 = none */
     int32_t top_k;        /* k: 1..min(E, 16) */
-    int32_t bits;         /* code width b: 2 or 3 */
+    int32_t bits;         /* code width b: 2 or 3 (3 with codebook blocks) */
     int32_t block;        /* weights per block: must be 32 */
+    int32_t codebook;     /* 0: b-bit code blocks; 1: codebook blocks (see above) */
 } moe_layer_desc;
 
 /* Opaque host handle of one packed layer: shapes plus device pointers into
@@ -103,12 +116,14 @@ const char *moe_last_error(void);
 /* Bytes of device memory moe_pack_experts needs for one layer.
  * Rejects (MOE_ERR_ARG / MOE_ERR_UNSUPPORTED) d % 256 != 0, d_ff % 32 != 0,
  * d_ff_shared % 32 != 0, k < 1, k > E, k > 16, E > 4096, bits not in {2,3},
- * block != 32. */
+ * block != 32, codebook not in {0,1}, codebook with bits != 3. */
 int moe_packed_bytes(const moe_layer_desc *desc, size_t *bytes);
 
 /* Re-tile one layer's canonical blocks into the device layout the kernels
  * stream (lossless integer shuffling: codes stay b-bit, scales stay fp16; no
- * weight is expanded to full precision) and copy the router.
+ * weight is expanded to full precision) and copy the router.  Experts stay
+ * in the file's own blocks and the kernels multiply from them [strata-mlx
+ * wiki, opening feature list, first item].
  *   experts_canon  device, E * expert_bytes canonical bytes
  *   shared_canon   device, canonical bytes of the shared expert, or NULL when
  *                  d_ff_shared == 0
@@ -124,13 +139,27 @@ int moe_pack_experts(const moe_layer_desc *desc, const void *experts_canon, cons
                      const float *router_w, const float *router_bias, void *packed, size_t packed_bytes,
                      moe_layer **out, void *stream);
 
+/* moe_pack_experts for codebook blocks (desc->codebook = 1): the same
+ * arguments plus `grid`, device uint8 [512][4] (16-byte aligned), the table
+ * of magnitudes the blocks index [strata-mlx wiki, credits list: the
+ * codebook tables come with the model files].  The grid is copied into the
+ * packed buffer (as exact fp16 values); a magnitude above 127 gives
+ * MOE_ERR_DATA.  Codebook layers run the decode path only: a forward call
+ * with more tokens than the decode kernels take (8 per layer call, 16 with
+ * fp16 activations or in a stack) returns MOE_ERR_UNSUPPORTED. */
+int moe_pack_experts_cb(const moe_layer_desc *desc, const void *experts_canon, const void *shared_canon,
+                        const uint8_t *grid, const float *router_w, const float *router_bias, void *packed,
+                        size_t packed_bytes, moe_layer **out, void *stream);
+
 /* Free the host handle (the packed device buffer stays the caller's). */
 int moe_layer_release(moe_layer *layer);
 
 /* Copy the layer's shape description. */
 int moe_layer_get_desc(const moe_layer *layer, moe_layer_desc *out);
 
-/* Top-k selection and gate weights on given logits (the routing step alone):
+/* Top-k selection and gate weights on given logits (the routing step alone;
+ * a router that sends each token to about ten of 512 experts [cnyes profile
+ * of Strata, section "Strata 到底是什麼？"]):
  *   logits device fp32 [T][E], idx device int32 [T][k], w device fp32 [T][k].
  * Order: logit descending, ties to the lower expert index (-0.0 == +0.0).
  * Gate weights: m = largest selected logit, e_r = exp(l_r - m) computed in
@@ -157,7 +186,12 @@ int moe_layer_workspace_bytes(const moe_layer *layer, int T, size_t *bytes);
  * leave the control words cleared for the next call. */
 int moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
-/* One layer: y[T][d] = MoE(x[T][d]).  T = 0 is a no-op.  T <= 8 runs the
+/* One layer: y[T][d] = MoE(x[T][d]) [cnyes profile of Strata, sections
+ * "Strata 到底是什麼？" (routed experts) and "三層記憶體" part 1 (shared
+ * expert); devlabs blog, section 核心技术特点, MTP item (eight tokens per
+ * verify pass); agentlenshq article, section "Strata 如何让 125 B 模型适配
+ * 12-24 GB 显存", last item (8192-token prompt chunks)].  T = 0 is a no-op.
+ * T <= 8 runs the
  * decode/verify kernels (experts streamed once per call with 128-bit loads
  * and multiplied from their codes, activations carried as fp16 hi + lo);
  * 8 < T <= 65536 runs the chunked-prefill kernels: the (token, slot) pairs are grouped by expert (as

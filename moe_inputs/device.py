@@ -10,7 +10,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import Workload, expert_canon, layer_experts_canon, router
+from . import Workload, codebook_grid, expert_canon, layer_experts_canon, router
 
 
 def packed_layer(wl: Workload, layer: int, device="cuda", canon_hook=None):
@@ -28,9 +28,10 @@ def packed_layer(wl: Workload, layer: int, device="cuda", canon_hook=None):
     W, b = router(wl, layer)
     Wd = torch.from_numpy(W).to(device)
     bd = torch.from_numpy(b).to(device) if b is not None else None
-    desc = bqe.make_desc(wl.d, wl.E, wl.I, wl.Is, wl.k, wl.bits)
-    L = bqe.PackedLayer(desc, canon, shared, Wd, bd, device)
-    del canon, shared, Wd, bd
+    desc = bqe.make_desc(wl.d, wl.E, wl.I, wl.Is, wl.k, wl.bits, codebook=wl.codebook)
+    grid = torch.from_numpy(codebook_grid(wl.seed)).to(device) if wl.codebook else None
+    L = bqe.PackedLayer(desc, canon, shared, Wd, bd, device, grid=grid)
+    del canon, shared, Wd, bd, grid
     return L
 
 
