@@ -135,6 +135,12 @@ def decode_classes(bqe):
             (bqe.TIMING_ROUTER, "router"))
 
 
+def data_note(wl):
+    blocks = ("counter-hash codebook blocks (uniform indices, signs; fp16 scales) over a seeded 512x4 grid of odd "
+              "magnitudes" if wl.codebook else "counter-hash codes/scales")
+    return f"synthetic ({blocks}, N(0,1) activations, N(0,0.02) router + Zipf(1.1) log bias)"
+
+
 def cpu_baseline_stack(wl, T, x_np, n_layers_sample):
     """Time the oracle (single-threaded fp64 C) on the first layers of the
     stack; expert generation is excluded from the timed parts."""
@@ -153,7 +159,8 @@ def cpu_baseline_stack(wl, T, x_np, n_layers_sample):
         t_total += time.perf_counter() - t0
         ex = {int(e): mi.expert_canon(wl, l, int(e)).numpy() for e in np.unique(idx)}
         sh = mi.expert_canon(wl, l, -1).numpy() if wl.Is else None
-        OL = oracle.Layer(wl.d, wl.E, wl.I, wl.Is, wl.k, wl.bits, W, b, ex, sh)
+        grid = mi.codebook_grid(wl.seed) if wl.codebook else None
+        OL = oracle.Layer(wl.d, wl.E, wl.I, wl.Is, wl.k, wl.bits, W, b, ex, sh, grid=grid)
         t0 = time.perf_counter()
         h, _, _, _ = oracle.layer_forward(OL, h, force_idx=idx, force_w=w)
         t_total += time.perf_counter() - t0
@@ -306,7 +313,7 @@ def bench_prefill(args):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp16 MFMA operands (weights s*c, activations scaled per row), fp32 accumulate",
-        "data": "synthetic (counter-hash codes/scales, N(0,1) activations, N(0,0.02) router + Zipf(1.1) log bias)",
+        "data": data_note(wl),
         "config": {"workload": wl.name, "layers": 1, "T": T, "f16act": bool(args.f16act), "d": wl.d, "experts": wl.E,
                    "d_ff": wl.I,
                    "shared_d_ff": wl.Is, "top_k": wl.k, "bits": wl.bits, "graph": graph is not None,
@@ -422,7 +429,7 @@ def bench_stack_prefill(args):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp16 MFMA operands (weights s*c, activations scaled per row), fp32 accumulate",
-        "data": "synthetic (counter-hash codes/scales, N(0,1) activations, N(0,0.02) router + Zipf(1.1) log bias)",
+        "data": data_note(wl),
         "config": {"workload": wl.name, "layers": wl.layers, "T": T, "d": wl.d, "experts": wl.E, "d_ff": wl.I,
                    "shared_d_ff": wl.Is, "top_k": wl.k, "bits": wl.bits, "graph": True,
                    "parallelism": "none (1 GPU)"},
@@ -441,7 +448,7 @@ def bench_stack_prefill(args):
     return out
 
 
-def bench_layer_t1(args):
+def bench_layer_t1(args, name="layer_t1"):
     """One full-size layer, decode T = 1, over a ring of 16 input rows (the
     routing changes from row to row).  Before each timed forward a 512 MB
     buffer is written, so the layer's weights are not served from the 256 MB
@@ -452,7 +459,7 @@ def bench_layer_t1(args):
     import moe_inputs as mi
     from moe_inputs.device import activations_device, packed_layer
 
-    wl = mi.WORKLOADS["layer_t1"]
+    wl = mi.WORKLOADS[name]
     dev = "cuda"
     torch.cuda.set_device(0)
     L = packed_layer(wl, 0, dev)
@@ -510,7 +517,7 @@ def bench_layer_t1(args):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp16 MFMA operands (codes exact, activations as fp16 hi+lo), fp32 accumulate",
-        "data": "synthetic (counter-hash codes/scales, N(0,1) activations, N(0,0.02) router + Zipf(1.1) log bias)",
+        "data": data_note(wl),
         "config": {"workload": wl.name, "layers": 1, "T": 1, "d": wl.d, "experts": wl.E, "d_ff": wl.I,
                    "shared_d_ff": wl.Is, "top_k": wl.k, "bits": wl.bits, "ring": ring,
                    "infinity_cache": "flushed before each forward", "parallelism": "none (1 GPU)"},
@@ -704,7 +711,7 @@ def bench_stack(args, wl, T, layers):
         "vs_baseline": None,
         "dtype": ("fp16 MFMA operands (codes exact, activations rounded to fp16), fp32 accumulate" if args.f16act
                   else "fp16 MFMA operands (codes exact, activations as fp16 hi+lo), fp32 accumulate"),
-        "data": "synthetic (counter-hash codes/scales, N(0,1) activations, N(0,0.02) router + Zipf(1.1) log bias)",
+        "data": data_note(wl),
         "config": {"workload": wl.name, "layers": wl.layers, "T": T, "f16act": bool(args.f16act), "d": wl.d, "experts": wl.E, "d_ff": wl.I,
                    "shared_d_ff": wl.Is, "top_k": wl.k, "bits": wl.bits, "graph": graph is not None,
                    "inputs": f"ring of {RING} batches of {T} rows", "parallelism": "none (1 GPU)"},
@@ -733,9 +740,11 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="all",
-                    choices=["all", "stack_t8_2bit", "stack_3bit", "prefill", "layer_t1", "stack_prefill"],
+                    choices=["all", "stack_t8_2bit", "stack_3bit", "prefill", "layer_t1", "stack_prefill",
+                             "layer_t1_cb3", "stack_cb3"],
                     help="all (default): the 2-bit stack at T = 8 as the value, with the one-layer T = 1 "
-                         "decode, the 3-bit stack at T = 8 and T = 1 and the 8192-token prefill under configs")
+                         "decode, the 3-bit stack at T = 8 and T = 1, the 8192-token prefill and the "
+                         "codebook-block layer and stack under configs")
     ap.add_argument("--T", type=int, default=None, help="tokens per pass (default: the workload's)")
     ap.add_argument("--layers", type=int, default=None, help="override the number of layers (testing only)")
     ap.add_argument("--no-graph", action="store_true")
@@ -763,8 +772,8 @@ def main():
     if args.workload == "prefill":
         print(json.dumps(bench_prefill(args)))
         return
-    if args.workload == "layer_t1":
-        print(json.dumps(bench_layer_t1(args)))
+    if args.workload in ("layer_t1", "layer_t1_cb3"):
+        print(json.dumps(bench_layer_t1(args, args.workload)))
         return
     if args.workload == "stack_prefill":
         print(json.dumps(bench_stack_prefill(args)))
@@ -807,6 +816,15 @@ def main():
     torch.cuda.empty_cache()
     log("prefill ...")
     configs["prefill_T8192"] = bench_prefill(args)
+    torch.cuda.empty_cache()
+    log("layer_t1_cb3 ...")
+    configs["layer_t1_cb3"] = bench_layer_t1(args, "layer_t1_cb3")
+    torch.cuda.empty_cache()
+    wlc = mi.WORKLOADS["stack_cb3"]
+    layers = build_stack(wlc)
+    log(f"stack_cb3 T={wlc.T} ...")
+    configs[f"stack_cb3_T{wlc.T}"] = bench_stack(args, wlc, wlc.T, layers)
+    del layers
     out["configs"] = configs
     print(json.dumps(out))
 

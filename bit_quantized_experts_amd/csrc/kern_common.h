@@ -88,6 +88,25 @@ DEVI half8_t frag_cb(const u32x4_t& idx, uint32_t hi, const u32x2_t& sg, int f, 
 }
 
 // ---------------------------------------------------------------------------
+// Read-ahead: lines rank, rank + n, ... of the ranges in w (128-byte lines),
+// one 4-byte load each into a 1 KB scratch LDS area (no registers, nothing
+// written to memory), waited for before the workgroup's LDS is released.
+// Every such load fetches its whole line into the memory-side cache.
+// ---------------------------------------------------------------------------
+template <typename WarmT>
+DEVI void warm_lines(const WarmT& w, int rank, int n, void* lds_scratch) {
+  typedef __attribute__((address_space(3))) void* lds_ptr_t;
+  const int wv = threadIdx.x >> 6;
+  char* sink = reinterpret_cast<char*>(lds_scratch) + 256 * (wv & 3);
+  for (int r = 0; r < w.n; ++r) {
+    const int64_t lines = w.bytes[r] >> 7;
+    for (int64_t i = (int64_t)rank * blockDim.x + threadIdx.x; i < lines; i += (int64_t)n * blockDim.x)
+      __builtin_amdgcn_global_load_lds(w.p[r] + 128 * i, (lds_ptr_t)sink, 4, 0, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
+// ---------------------------------------------------------------------------
 // Buffer loads that bypass nothing special: plain 128/64-bit global loads.
 // ---------------------------------------------------------------------------
 DEVI u32x4_t ld128(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }

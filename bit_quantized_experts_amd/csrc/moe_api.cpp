@@ -534,10 +534,27 @@ int decode_layer(const moe_layer* L, const LayerInput& in, float eps, int T, flo
   return MOE_OK;
 }
 
+// The next layer's routing-independent weights: router rows (fp16 hi and
+// lo, the form the prefill router reads) and the shared expert.
+static WarmArgs next_layer_lines(const moe_layer* L) {
+  WarmArgs a{};
+  const int64_t rb = (int64_t)L->E16 * L->d * 2;
+  a.p[0] = reinterpret_cast<const uint8_t*>(L->router_wh);
+  a.bytes[0] = rb;
+  a.p[1] = reinterpret_cast<const uint8_t*>(L->router_wl);
+  a.bytes[1] = rb;
+  a.p[2] = L->shared;
+  a.bytes[2] = L->Is > 0 ? L->sh.bytes : 0;
+  a.n = L->Is > 0 ? 3 : 2;
+  return a;
+}
+
 // One prefill layer (T > 8): prep -> router -> top-k -> group -> gate/up ->
-// down -> combine into y.
+// down -> combine into y.  next: the layer after this one in a stack, whose
+// routing-independent weights the gate/up kernel's idle workgroups read
+// ahead, or null.
 int prefill_layer(const moe_layer* L, const float* x, int norm, float eps, int T, float* y, const moe_route_io* r,
-                  uint8_t* ws, hipStream_t s) {
+                  uint8_t* ws, hipStream_t s, const moe_layer* next = nullptr) {
   const PfLayout W = ws_layout_prefill(L, T);
   const int d = L->d, E = L->E, k = L->k;
   const bool forced = r && r->in_idx && r->in_w;
@@ -639,6 +656,7 @@ int prefill_layer(const moe_layer* L, const float* x, int norm, float eps, int T
   ma.ed = L->dbound;
   ma.yh = reinterpret_cast<_Float16*>(ws + W.ypart);
   ma.rowf = reinterpret_cast<float*>(ws + W.rowf);
+  if (next) ma.warm = next_layer_lines(next);
   timed_begin(3, s, &slot);
   serial_point(s);
   HIPCHK(launch_pf_gate_up(ma, L->bits, W.max_items, s));
@@ -1185,6 +1203,10 @@ int moe_stack_forward(const moe_layer* const* layers, int n_layers, const float*
     // or y; the RMSNorm of the input is fused into the layer's prep step.
     // Reading and writing y in one layer is safe: the prep step consumes its
     // input before the combine step writes the output.
+    // While layer l computes, its gate/up kernel's workgroups without a work
+    // item read layer l + 1's router rows and shared expert into the
+    // Infinity Cache (MOE_PREFETCH=0 in the environment turns this off).
+    const bool ahead = env_int("MOE_PREFETCH", 1) != 0;
     for (int l = 0; l < n_layers; ++l) {
       moe_route_io r{};
       if (idx_layers) {
@@ -1193,7 +1215,8 @@ int moe_stack_forward(const moe_layer* const* layers, int n_layers, const float*
       }
       const float* in = l == 0 ? x : (y_layers ? y_layers + (size_t)(l - 1) * T * d : y);
       float* out = y_layers ? y_layers + (size_t)l * T * d : y;
-      rc = prefill_layer(layers[l], in, l > 0, eps, T, out, &r, wsb, s);
+      rc = prefill_layer(layers[l], in, l > 0, eps, T, out, &r, wsb, s,
+                         ahead && l + 1 < n_layers ? layers[l + 1] : nullptr);
       if (rc) return rc;
     }
     if (y_layers) HIPCHK(hipMemcpyAsync(y, y_layers + (size_t)(n_layers - 1) * T * d, (size_t)T * d * 4, hipMemcpyDeviceToDevice, s));

@@ -175,6 +175,8 @@ hipError_t launch_debug_unpack(const uint8_t* mat, const uint16_t* grid16, const
                                int8_t* codes, float* w32, uint16_t* w16, hipStream_t s);
 hipError_t launch_pack_grid(const uint8_t* grid, uint16_t* out, uint32_t* bad, hipStream_t s);
 
+
+
 // Test export of one packed matrix through an expert kernel's own decoder.
 struct DebugPathArgs {
   const uint8_t* mat;  // packed matrix
@@ -253,8 +255,17 @@ struct PfGroupArgs {
   int32_t R_fill;      // rows of row_src to fill with -1 beyond the routed rows (export)
 };
 
+// Byte ranges (128-byte aligned starts; a tail below 128 bytes is skipped)
+// whose cache lines are loaded once, results discarded (warm_lines).
+struct WarmArgs {
+  const uint8_t* p[4];
+  int64_t bytes[4];
+  int32_t n;
+};
+
 struct PfGemmArgs {
   ExpertSet X;
+  WarmArgs warm;          // gate/up: lines its workgroups without a work item read ahead (n = 0: none)
   const _Float16* xh;     // gate/up: activation rows
   const int32_t* ex;      // gate/up: row exponents of x
   const int32_t* row_tok;

@@ -722,10 +722,18 @@ __global__ __launch_bounds__(256, 2) void pf_gate_up_kernel(PfGemmArgs a) {
   unsigned char* const st2 = st0;  // (two stages; a third is never used)
   __shared__ int ex_lds[PF_TM];
   int item, nt;
-  if (!xcd_tile(*a.n_items, a.n_nt, &item, &nt)) return;
+  // a workgroup without a work item reads the next layer's lines ahead
+  // (its share of them: rank blockIdx.x of the grid)
+  if (!xcd_tile(*a.n_items, a.n_nt, &item, &nt)) {
+    warm_lines(a.warm, blockIdx.x, gridDim.x, st0);
+    return;
+  }
   const int g = a.item_group[item], row0 = a.item_row0[item], rows = a.item_rows[item];
   const int Ig = g == a.E ? a.Is : a.I;
-  if (nt * PF_HT >= Ig) return;
+  if (nt * PF_HT >= Ig) {
+    warm_lines(a.warm, blockIdx.x, gridDim.x, st0);
+    return;
+  }
   const int nrg = rows >> 4;
   const Stages S{st0, st1, st2};
   if (nrg > 4) gate_up_item<BITS, 8>(a, S, ex_lds, g, row0, rows, nt);

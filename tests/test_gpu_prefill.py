@@ -229,11 +229,9 @@ def test_prefill_forced_routing_invalid_and_repeated(bqe):
     idx[9, 3] = idx[9, 1]     # repeat: the first occurrence is used
     y, _, oi, ow = _forward(bqe, L, x, forced=(idx, w))
     assert np.array_equal(oi, idx) and np.array_equal(ow, w)
-    iz, wz = idx.copy(), w.copy()
-    for t, r in ((3, 2), (7, 0), (9, 3)):
-        iz[t, r], wz[t, r] = 0, 0.0
-    OL = oracle_layer(wl, 0, iz.reshape(-1))
-    oy, _, _, _ = oracle.layer_forward(OL, x, force_idx=iz, force_w=wz)
+    # the oracle applies the same rule to the raw rows
+    OL = oracle_layer(wl, 0, idx[(idx >= 0) & (idx < wl.E)])
+    oy, _, _, _ = oracle.layer_forward(OL, x, force_idx=idx, force_w=w)
     assert rel_err_inf(y, oy) <= TOL_LAYER
 
 
@@ -291,3 +289,47 @@ def test_prefill_stack_teacher_forced(bqe):
     bqe.moe_stack_forward([L.handle for L in layers], x, y2, ws, 1e-6)
     torch.cuda.synchronize()
     assert np.array_equal(y2.cpu().numpy(), y.cpu().numpy())
+
+
+def test_prefill_stack_read_ahead_and_graph(bqe, monkeypatch):
+    """The next-layer read-ahead (loads issued by the gate/up kernel's
+    workgroups without a work item) changes nothing: the chunked-prefill
+    stack gives the same bits with it and without it, eagerly and replayed
+    from a captured graph (four replays with eager work in between)."""
+    wl = mi.small(mi.WORKLOADS["stack_prefill"], layers=4)
+    layers = [packed_layer(wl, l) for l in range(wl.layers)]
+    handles = [L.handle for L in layers]
+    T = 256
+    x = activations_device(mi.activations(wl, T=T, stream=31))
+    ws = bqe.new_workspace(max(L.workspace_bytes(T) for L in layers))
+    say(f"[prefill stack read-ahead] layers={wl.layers} T={T}")
+
+    def run(flag):
+        monkeypatch.setenv("MOE_PREFETCH", flag)
+        y = torch.full((T, wl.d), float("nan"), dtype=torch.float32, device=DEV)
+        bqe.moe_stack_forward(handles, x, y, ws, 1e-6)
+        torch.cuda.synchronize()
+        return y
+
+    y_off = run("0").cpu()
+    y_on = run("1")
+    assert torch.equal(y_on.cpu(), y_off)
+    # captured with the read-ahead on
+    monkeypatch.setenv("MOE_PREFETCH", "1")
+    yg = torch.full((T, wl.d), float("nan"), dtype=torch.float32, device=DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        bqe.moe_stack_forward(handles, x, yg, ws, 1e-6)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        bqe.moe_stack_forward(handles, x, yg, ws, 1e-6)
+    torch.cuda.synchronize()
+    for i in range(4):
+        yg.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(yg.cpu(), y_off), i
+        run("0")  # eager work between replays
