@@ -22,7 +22,7 @@
 // Memory: weight chunks stream from HBM into registers, several k-groups
 // ahead of the multiplies; the gate/up activation fragments are read from
 // LDS (one copy per workgroup).  Everything one workgroup hands to another
-// (the layer input, logits, h and its maxima, the down partials) is stored
+// (the layer input, logits, h, the down partials) is stored
 // device-coherently (kern_common.h: written through to memory), so the same
 // code serves kernels separated by launches and phases of one persistent
 // kernel.  The bulk of it (layer input, logits, divisors, exponents, h) is
@@ -32,7 +32,7 @@
 // them (a kernel starts with its L2 invalidated); the many workgroups that
 // read the same line then share one fetch per XCD instead of each going to
 // memory.  Values that are rewritten within a kernel and read by few
-// workgroups (split partials, maxima, partial logits, counters) are loaded
+// workgroups (split partials, partial logits, counters) are loaded
 // device-coherently.
 #pragma once
 #include "kern_common.h"
@@ -206,24 +206,25 @@ struct WindowRegs {
   static constexpr int R = A16 ? MOE_MAX_TOK_F16ACT : MOE_MAX_TOK_DECODE;
   static constexpr int PER = GU_WIN * 4 * R / (64 * GU_NW);
   float4_t v[PER][2];
-  int ex;  // exponent of this thread's token (the values are scaled by 2^-ex)
+  int ex;     // exponent of this thread's token (the values are scaled by 2^-ex)
+  bool live;  // this thread's token is below T (else its rows are zeros)
 };
 
+// Every load is issued unconditionally (blocks past the window and tokens
+// past T re-read a valid address; window_store drops them), so the loads of
+// a thread stay in flight together instead of each waiting behind a branch.
 template <bool A16>
 DEVI void window_load(WindowRegs<A16>& W, const GuArgs& a, int b0, int nblk, int tid) {
   constexpr int R = WindowRegs<A16>::R;
   const int t = (tid >> 2) % R, q = tid & 3;
-  const bool live = t < a.T;
-  W.ex = live ? a.xexp[t] : 0;
-  const float* src = a.xin + (size_t)(live ? t : 0) * a.d + 32 * b0 + 8 * q;
+  W.live = t < a.T;
+  W.ex = W.live ? a.xexp[t] : 0;
+  const float* src = a.xin + (size_t)(W.live ? t : 0) * a.d + 32 * b0 + 8 * q;
 #pragma unroll
   for (int i = 0; i < WindowRegs<A16>::PER; ++i) {
-    const int b = (tid + 64 * GU_NW * i) / (4 * R);
-    W.v[i][0] = W.v[i][1] = float4_t{0.f, 0.f, 0.f, 0.f};
-    if (b < nblk && live) {
-      W.v[i][0] = *reinterpret_cast<const float4_t*>(src + 32 * b);
-      W.v[i][1] = *reinterpret_cast<const float4_t*>(src + 32 * b + 4);
-    }
+    const int b = min((tid + 64 * GU_NW * i) / (4 * R), nblk - 1);
+    W.v[i][0] = *reinterpret_cast<const float4_t*>(src + 32 * b);
+    W.v[i][1] = *reinterpret_cast<const float4_t*>(src + 32 * b + 4);
   }
 }
 
@@ -240,7 +241,8 @@ DEVI void window_store(const WindowRegs<A16>& W, GuLds& L, int nblk, int code_of
     float sh = 0.f, sl = 0.f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const float v = ldexpf(W.v[i][c >> 2][c & 3], -W.ex);  // exact (2^-ex itself may exceed the fp32 range)
+      // exact (2^-ex itself may exceed the fp32 range); rows past T are zeros
+      const float v = W.live ? ldexpf(W.v[i][c >> 2][c & 3], -W.ex) : 0.f;
       h[c] = (_Float16)v;
       sh += (float)h[c];
       if (!A16) {
@@ -417,8 +419,7 @@ DEVI void gu_select(const GuArgs& a, GuLds& L, bool publish_routing, bool publis
 // The gate/up work items of one workgroup (wg of n_wg): a work item is
 // (slot u, tile t of 16 intermediate rows).  With h_ready, each finished
 // item adds one to its slot's counter (h_ready + u * MOE_CTR_STRIDE) once its
-// h values and maxima are stored (a consumer inside the same kernel waits on
-// them).
+// h values are stored (a consumer inside the same kernel waits on them).
 template <int BITS, bool A16>
 DEVI void gu_items(const GuArgs& a, GuLds& L, int wg, int n_wg, uint32_t* h_ready) {
   constexpr int64_t CB = moe_chunk_bytes(BITS);
@@ -479,50 +480,49 @@ DEVI void gu_items(const GuArgs& a, GuLds& L, int wg, int n_wg, uint32_t* h_read
         L.red[wv][4 + i][lane] = accu[i];
       }
       __syncthreads();
-      if (kp == 0) {
-        for (int p = 1; p < KP; ++p)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            accg[i] += L.red[wv + p][i][lane];
-            accu[i] += L.red[wv + p][4 + i][lane];
-          }
-      }
     }
-    if (valid && kp == 0) {
+    if (valid) {
       // lane l: intermediate row n = l & 15 of the tile, C rows 4(l>>4)+i:
       // tokens tok_e + i, hi part in lanes < 32, lo part in lanes >= 32 (fp16
       // activations: token 4(l>>4)+i, no lo part).  h is kept in fp32 as
       // [slot][16-row tile][token][16] (an item writes whole 128-byte lines,
-      // none shared with another item) with the largest |h| of each (slot,
-      // token) (the down kernel scales by it before rounding to fp16); maxima
-      // of non-negative floats order like their bit patterns.
+      // none shared with another item, zeros for tokens without this slot);
+      // the down kernel scales it before rounding to fp16.
       const int n = lane & 15;
       const bool writer = A16 || lane < 32;
       constexpr int R = A16 ? MOE_MAX_TOK_F16ACT : MOE_MAX_TOK_DECODE;
       float* hrow = a.hbuf + ((size_t)u * (a.hI / 16) + t) * R * 16 + n;
+      // The item's KP waves share the epilogue: wave kp finishes the
+      // accumulator rows i with i % KP == kp, summing the k-parts in wave
+      // order (KP is a power of two, so the choice is wave-uniform).
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        if ((i & (KP - 1)) != kp) continue;
+        float sg = accg[i], su = accu[i];
+        if (KP > 1) {
+          const int w0 = jw * KP;
+          sg = L.red[w0][i][lane];
+          su = L.red[w0][4 + i][lane];
+          for (int p = 1; p < KP; ++p) {
+            sg += L.red[w0 + p][i][lane];
+            su += L.red[w0 + p][4 + i][lane];
+          }
+        }
         const int tok = A16 ? 4 * (lane >> 4) + i : tok_e + i;
         const float gw = (u == 0 && has_shared) ? (tok < T ? 1.0f : 0.f) : L.S.w[u][tok];
         // the norm's 1 / rms, then 2^ex undoes the activations' scaling (exact)
         const float rrn = L.rn[tok];
         const int rx = L.rx[tok];
-        const float g = ldexpf((A16 ? accg[i] : add_partner32(accg[i])) * rrn, rx);
-        const float uu = ldexpf((A16 ? accu[i] : add_partner32(accu[i])) * rrn, rx);
+        const float g = ldexpf((A16 ? sg : add_partner32(sg)) * rrn, rx);
+        const float uu = ldexpf((A16 ? su : add_partner32(su)) * rrn, rx);
         const float hv = g * __builtin_amdgcn_rcpf(1.0f + expf(-g)) * uu;
         const float hs = (gw != 0.f) ? gw * hv : 0.f;
         if (writer) st_dev(hrow + tok * 16, hs);
-        const float m = row16_max(fabsf(hs));
-        if (writer && n == 0)
-          __hip_atomic_fetch_max(a.hmax + u * 16 + tok, __float_as_uint(m), __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
       }
-      if (h_ready) {
-        __builtin_amdgcn_s_waitcnt(0);  // this item's h values and maxima are stored
-        if (lane == 0) signal_add(h_ready + (size_t)u * MOE_CTR_STRIDE);
-      }
+      if (h_ready) __builtin_amdgcn_s_waitcnt(0);  // this wave's h values are stored
     }
-    if (KP > 1) __syncthreads();  // red is rewritten in the next round
+    if (KP > 1) __syncthreads();  // red is rewritten in the next round; every wave's stores waited for
+    if (h_ready && valid && kp == 0 && lane == 0) signal_add(h_ready + (size_t)u * MOE_CTR_STRIDE);
   }
 }
 
@@ -541,7 +541,8 @@ DEVI void gu_items(const GuArgs& a, GuLds& L, int wg, int n_wg, uint32_t* h_read
 // [slot][token][row]): lane L = m + 16q holds inputs 8q..8q+7 of row m, i.e.
 // token m & 7, its fp16 hi part for m < 8 and lo part for m >= 8 (fp16
 // activations: token m, rounded to fp16), after scaling by the power of two
-// 2^-eh that puts the largest |h| of the (slot, token) in [2^14, 2^15).
+// 2^-eh that puts the token's largest |h| over the down item's inputs in
+// [2^14, 2^15).
 template <bool A16>
 DEVI half8_t h_fragment(const float4_t (&v)[2], int eh, int lane) {
   const bool lo = !A16 && (lane & 8);
@@ -599,13 +600,10 @@ DEVI void down_role(const DownArgs& a, int rg, int sp, int ns, const int* slots,
   const int tok_c = A16 ? 4 * (lane >> 4) : (4 * (lane >> 4)) & 7;
   const float off = -(float)moe_code_offset(BITS);
   const half8_t ones = half8_t{1, 1, 1, 1, 1, 1, 1, 1};
-  const __amdgpu_buffer_rsrc_t mr = coh_rsrc(a.hmax);
 
   for (int b0 = wv; b0 < n_items; b0 += nw * BATCH) {
     ChunkRegs<BITS> c[BATCH];
     float4_t hv[BATCH][BK][2];
-    uint32_t hm_a[BATCH];
-    u32x4_t hm_c[BATCH];
     bool ok[BATCH];
 #pragma unroll
     for (int q = 0; q < BATCH; ++q) {
@@ -639,13 +637,22 @@ DEVI void down_role(const DownArgs& a, int rg, int sp, int ns, const int* slots,
         hv[q][j][0] = *reinterpret_cast<const float4_t*>(hr + 2 * j * R * 16);
         hv[q][j][1] = *reinterpret_cast<const float4_t*>(hr + 2 * j * R * 16 + 4);
       }
-      hm_a[q] = ld_dev_u(a.hmax + u * 16 + tok_a);
-      hm_c[q] = coh_ld4u(mr, (uint32_t)(u * 16 + tok_c) * 4);
     }
 #pragma unroll
     for (int q = 0; q < BATCH; ++q) {
       if (!ok[q]) continue;
-      const int eh_a = fp16_exponent_for(__uint_as_float(hm_a[q]));
+      // the item's scale for each token: the largest |h| of the token over
+      // the item's inputs (this lane's values, then the other lanes holding
+      // the same token: 8 apart, or 16 apart with fp16 activations)
+      float m = 0.f;
+#pragma unroll
+      for (int j = 0; j < BK; ++j)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) m = fmaxf(m, fabsf(hv[q][j][c >> 2][c & 3]));
+      if (!A16) m = fmaxf(m, __shfl_xor(m, 8, 64));
+      m = fmaxf(m, __shfl_xor(m, 16, 64));
+      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      const int eh_a = fp16_exponent_for(m);
       float4_t part[RT];
 #pragma unroll
       for (int t = 0; t < RT; ++t) part[t] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -663,10 +670,11 @@ DEVI void down_role(const DownArgs& a, int rg, int sp, int ns, const int* slots,
           part[t] += chunk_scale(c[q].scales, f) * C;
         }
       }
-      // undo the (slot, token) scaling of this item's rows: 2^eh, exact
+      // undo the item's scaling of the accumulator rows' tokens: 2^eh, exact
+      // (lane t < 8, or < 16 with fp16 activations, holds token t's exponent)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int eh = fp16_exponent_for(__uint_as_float(hm_c[q][i]));
+        const int eh = __shfl(eh_a, tok_c + i, 64);
 #pragma unroll
         for (int t = 0; t < RT; ++t) acc[t][i] += ldexpf(part[t][i], eh);
       }
@@ -678,25 +686,26 @@ DEVI void down_role(const DownArgs& a, int rg, int sp, int ns, const int* slots,
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[(wv * RT * 4 + t * 4 + i) * 64 + lane] = acc[t][i];
   __syncthreads();
-  if (wv == 0) {
+  {
+    // the RT x 4 accumulator rows are shared out over the waves; each adds
+    // the waves' partial sums in wave order
     const int T = a.T, d = a.d, n = lane & 15;
+    for (int pi = wv; pi < RT * 4; pi += nw) {
+      const int t = pi >> 2, i = pi & 3;
+      float part[8];
 #pragma unroll
-    for (int t = 0; t < RT; ++t)
+      for (int w = 0; w < 8; ++w) part[w] = red[((w < nw ? w : 0) * RT * 4 + pi) * 64 + lane];
+      float s = part[0];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float part[8];
-#pragma unroll
-        for (int w = 0; w < 8; ++w) part[w] = red[((w < nw ? w : 0) * RT * 4 + t * 4 + i) * 64 + lane];
-        float s = part[0];
-#pragma unroll
-        for (int w = 1; w < 8; ++w)
-          if (w < nw) s += part[w];
-        if (!A16) s = add_partner32(s);  // (fp16 activations: C row = token, 16 tokens)
-        const int tok = 4 * (lane >> 4) + i;  // (hi/lo: lanes < 32 hold tokens 0..7)
-        const int o = rg * 16 * RT + 16 * t + n;
-        if ((A16 || lane < 32) && tok < T) st_dev(a.ypart + ((size_t)sp * R + tok) * d + o, s);
-      }
+      for (int w = 1; w < 8; ++w)
+        if (w < nw) s += part[w];
+      if (!A16) s = add_partner32(s);  // (fp16 activations: C row = token, 16 tokens)
+      const int tok = 4 * (lane >> 4) + i;  // (hi/lo: lanes < 32 hold tokens 0..7)
+      const int o = rg * 16 * RT + 16 * t + n;
+      if ((A16 || lane < 32) && tok < T) st_dev(a.ypart + ((size_t)sp * R + tok) * d + o, s);
+    }
   }
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's partial sums are stored (a signal may follow the barrier)
   __syncthreads();  // red is free again
 }
 

@@ -293,13 +293,6 @@ DEVI float row16_sum(float v) {
   return v;
 }
 
-// Largest value over the 16 lanes of a row, in every lane of the row.
-DEVI float row16_max(float v) {
-#pragma unroll
-  for (int st = 0; st < 4; ++st) v = fmaxf(v, __uint_as_float(dpp_perm(__float_as_uint(v), st)));
-  return v;
-}
-
 // ---------------------------------------------------------------------------
 // Deterministic fp64 exponential for the gate weights.  Steps: n = rint(z /
 // ln2); r = z - n*ln2 as two fused steps with ln2 split into a high part (the

@@ -171,7 +171,7 @@ PackedLayout packed_layout(const moe_layer_desc* D, const moe_expert_layout& ex,
 
 // ------------------------------------------------------------- workspace ---
 struct WsLayout {
-  int64_t ctrl, lp, ss_part, mx_part, rnorm, xexp, logits, n_slots, slot_expert, slot_w, xin, hbuf, hmax, ypart,
+  int64_t ctrl, lp, ss_part, mx_part, rnorm, xexp, logits, n_slots, slot_expert, slot_w, xin, hbuf, ypart,
       total;
   int max_slots, S, nbI, n_cs;
 };
@@ -226,7 +226,6 @@ WsLayout ws_layout_decode(const moe_layer* L, int T, bool act16 = false) {
   W.xin = take((int64_t)MOE_MAX_TOK_F16ACT * d * 4);
   const int R = act16 ? MOE_MAX_TOK_F16ACT : MOE_MAX_TOK_DECODE;
   W.hbuf = take((int64_t)W.max_slots * R * W.nbI * 32 * 4);
-  W.hmax = take((int64_t)W.max_slots * 16 * 4);
   W.total = o;
   return W;
 }
@@ -237,10 +236,10 @@ WsLayout ws_layout_decode(const moe_layer* L, int T, bool act16 = false) {
 // maxima and counters (cleared together before each launch).  The down
 // partials sit where the per-phase layout has them.
 struct PsLayout {
-  int64_t ctrl, ypart, lp, ss_part, mx_part, rnorm, xexp, logits, xin, hbuf, hmax, ctl, total;
+  int64_t ctrl, ypart, lp, ss_part, mx_part, rnorm, xexp, logits, xin, hbuf, ctl, total;
   int64_t logits_stride, xin_stride, hbuf_stride;  // floats per layer
   int max_slots, S, n_rs, n_cs, cpl, hI;
-  size_t clear_words;  // hmax and ctl
+  size_t clear_words;  // ctl
 };
 
 int persist_grid();  // workgroups of a persistent pass (0: not available)
@@ -279,13 +278,10 @@ PsLayout ws_layout_persist(const moe_layer* L, int T, bool act16, int n_layers) 
   W.logits = take((int64_t)n * W.logits_stride * 4);
   W.xin = take((int64_t)n * W.xin_stride * 4);
   W.hbuf = take((int64_t)n * W.hbuf_stride * 4);
-  const int64_t hmax_bytes = (int64_t)n * W.max_slots * 16 * 4;
   const int64_t ctl_bytes = (int64_t)n * W.cpl * 4;
-  W.hmax = o;
-  W.ctl = o + hmax_bytes;
-  o += moe_align256(hmax_bytes + ctl_bytes);
+  W.ctl = take(ctl_bytes);
   W.total = o;
-  W.clear_words = (size_t)(hmax_bytes + ctl_bytes) / 4;
+  W.clear_words = (size_t)ctl_bytes / 4;
   return W;
 }
 
@@ -435,8 +431,6 @@ int decode_layer(const moe_layer* L, const LayerInput& in, float eps, int T, flo
   ra.act16 = act16;
   ra.lp = reinterpret_cast<float*>(ws + W.lp);
   ra.xin = reinterpret_cast<float*>(ws + W.xin);
-  ra.hmax = reinterpret_cast<uint32_t*>(ws + W.hmax);
-  ra.hmax_n = W.max_slots * 16;
   ra.y_out = y_prev_out;
   SelectArgs& sa = ra.sel;
   sa.ss_part = reinterpret_cast<float*>(ws + W.ss_part);
@@ -479,7 +473,6 @@ int decode_layer(const moe_layer* L, const LayerInput& in, float eps, int T, flo
   ga.xin = ra.xin;
   ga.xexp = sa.xexp;
   ga.hbuf = reinterpret_cast<float*>(ws + W.hbuf);
-  ga.hmax = ra.hmax;
   ga.E = E;
   ga.I = L->I;
   ga.Is = L->Is;
@@ -509,7 +502,6 @@ int decode_layer(const moe_layer* L, const LayerInput& in, float eps, int T, flo
   da.n_slots = ga.n_slots;
   da.slot_expert = ga.slot_expert;
   da.hbuf = ga.hbuf;
-  da.hmax = ga.hmax;
   da.E = E;
   da.d = d;
   da.T = T;
@@ -1041,7 +1033,6 @@ static int persist_pass(const moe_layer* const* layers, int n_layers, const floa
   P.logits_row = logits_row(L->E);
   P.xin_stride = W.xin_stride;
   P.hbuf_stride = W.hbuf_stride;
-  P.hmax = reinterpret_cast<uint32_t*>(ws + W.hmax);
   P.ctl = reinterpret_cast<uint32_t*>(ws + W.ctl);
   P.ypart = reinterpret_cast<float*>(ws + W.ypart);
   P.status = reinterpret_cast<uint32_t*>(ws + W.ctrl + kStatusOffset);

@@ -51,8 +51,6 @@ struct RouteArgs {
   int32_t act16;    // 1: gate/up A-fragments hold 16 tokens in fp16 (else 8 tokens as fp16 hi + lo)
   float* lp;        // ws [d/MOE_ROUTE_COLS][T][E] partial logits
   float* xin;       // ws [16][d]: the summed layer input (row slice 0 writes it)
-  uint32_t* hmax;   // ws [hmax_n]: cleared here for the gate/up kernel's maxima
-  int32_t hmax_n;
   float* y_out;     // optional: the summed input, [T][d]
   SelectArgs sel;   // the logits, finished by the last workgroup of each row slice
 };
@@ -86,7 +84,6 @@ struct GuArgs {
   const float* xin;      // [16][d] layer input rows (before the RMSNorm of stacked layers)
   const int32_t* xexp;   // [16] row exponents (the fragments hold x 2^-ex)
   float* hbuf;      // ws [MAX_SLOTS][hI/16][R][16] fp32 h = w silu(g) u, R = 16 (act16) or 8
-  uint32_t* hmax;   // ws [MAX_SLOTS][16] largest |h| of each (slot, token), as float bits
   int32_t E, I, Is, T, d, n_kg, bits, hI, code_off, has_shared;
   int32_t act16;  // 1: A rows are 16 tokens in fp16 (else 8 tokens as fp16 hi + lo)
 };
@@ -96,7 +93,6 @@ struct DownArgs {
   const int32_t* n_slots;
   const int32_t* slot_expert;
   const float* hbuf;       // [MAX_SLOTS][R][hI] fp32
-  const uint32_t* hmax;    // [MAX_SLOTS][16]
   int32_t E, d, T, bits, hI, BK, RT, n_kg_r, n_kg_s, S, has_shared, max_slots;
   int32_t act16;  // 1: A rows are 16 tokens in fp16 (else 8 tokens as fp16 hi + lo)
   float* ypart;   // ws [S][R][d], R = 16 with act16, else 8
@@ -159,7 +155,6 @@ struct PersistArgs {
   float* hbuf;       // [n][max_slots][hI/16][R][16]
   int64_t logits_stride, xin_stride, hbuf_stride;
   int32_t logits_row;  // floats per token row of the logits
-  uint32_t* hmax;    // [n_layers][max_slots][16], then the counters (cleared together)
   uint32_t* ctl;     // [n_layers][cpl], counters MOE_CTR_STRIDE words apart
   float* ypart;      // [S][R][d]
   uint32_t* status;  // abort word: non-zero once a wait gave up

@@ -86,7 +86,6 @@ __global__ __launch_bounds__(512) void decode_persist_kernel(PersistArgs P) {
     uint32_t* y_ready = ctl + (n_rs + 1) * CS;
     uint32_t* h_ready = y_ready + n_cs * CS;
     const uint32_t* y_prev = l > 0 ? P.ctl + (size_t)(l - 1) * P.cpl + (n_rs + 1) * CS : nullptr;
-    uint32_t* hmax = P.hmax + (size_t)l * P.max_slots * 16;
     float* logits = P.logits + (size_t)l * P.logits_stride;
     float* xin = P.xin + (size_t)l * P.xin_stride;
     float* rnorm = P.rnorm + (size_t)l * MOE_PERSIST_TOK_STRIDE;
@@ -108,8 +107,6 @@ __global__ __launch_bounds__(512) void decode_persist_kernel(PersistArgs P) {
     ra.act16 = A16;
     ra.lp = P.lp;
     ra.xin = xin;
-    ra.hmax = nullptr;
-    ra.hmax_n = 0;
     ra.y_out = l == 0 ? P.y_prev_out : (P.y_layers ? P.y_layers + (size_t)(l - 1) * P.yl_stride : nullptr);
     SelectArgs& sa = ra.sel;
     sa.ss_part = P.ss_part;
@@ -160,7 +157,6 @@ __global__ __launch_bounds__(512) void decode_persist_kernel(PersistArgs P) {
     ga.xin = xin;
     ga.xexp = xexp;
     ga.hbuf = hbuf;
-    ga.hmax = hmax;
     ga.E = P.E;
     ga.I = P.I;
     ga.Is = P.Is;
@@ -181,7 +177,6 @@ __global__ __launch_bounds__(512) void decode_persist_kernel(PersistArgs P) {
     DownArgs da{};
     da.X = ga.X;
     da.hbuf = hbuf;
-    da.hmax = hmax;
     da.E = P.E;
     da.d = d;
     da.T = T;
@@ -206,7 +201,8 @@ __global__ __launch_bounds__(512) void decode_persist_kernel(PersistArgs P) {
       }
       down_role<BITS, RT, A16>(da, rg, sp, ns, L.S.expert, reinterpret_cast<float*>(L.xs));
       if (threadIdx.x == 0) {
-        __builtin_amdgcn_s_waitcnt(0);  // wavefront 0's partial sums are stored
+        // every wavefront's partial sums are stored (each waited before the
+        // role's last barrier)
         signal_add(y_ready + (size_t)((rg * 16 * RT) / MOE_ROUTE_COLS) * CS);
       }
     }
@@ -237,7 +233,7 @@ __global__ __launch_bounds__(512) void decode_persist_kernel(PersistArgs P) {
   }
 }
 
-// Clears the per-layer counters and maxima of a pass, and the abort word.
+// Clears the per-layer counters of a pass, and the abort word.
 __global__ void persist_clear_kernel(uint32_t* region, size_t n, uint32_t* status) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) region[i] = 0u;
@@ -285,7 +281,7 @@ int persist_blocks_per_cu() {
 
 hipError_t launch_persist(const PersistArgs& a, int rt, int grid, bool act16, size_t clear_words, hipStream_t s) {
   if (clear_words) {
-    hipLaunchKernelGGL(persist_clear_kernel, dim3((unsigned)((clear_words + 255) / 256)), dim3(256), 0, s, a.hmax,
+    hipLaunchKernelGGL(persist_clear_kernel, dim3((unsigned)((clear_words + 255) / 256)), dim3(256), 0, s, a.ctl,
                        clear_words, a.status);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -242,9 +242,6 @@ DEVI bool route_role(const RouteArgs& a, int cs, int rs, float (*ys)[MOE_ROUTE_C
       }
     }
   }
-  // the gate/up kernel's per-(slot, token) maxima start from zero
-  if (cs == 0 && rs == 0)
-    for (int i = tid; i < a.hmax_n; i += blockDim.x) a.hmax[i] = 0u;
   __syncthreads();
 
   // sums of squares of the slice (each row slice keeps its own copy) and its
