@@ -179,7 +179,7 @@ struct alignas(16) GuLds {
   alignas(16) float cs[GU_WIN * 16];  // accumulator seeds, [block][16]
   float red[GU_NW][8][64];          // partial sums of the k-parts
   float rn[16];                     // 1 / rms of each token
-  int rx[16];                       // exponent ex of each token's activation scaling
+  int sx[MOE_MAX_CS][16];           // exponent e of each (column slice, token) scaling of the fragments
   SlotLds S;
   uint64_t tk_buf[GU_NW][TOPK_BUF];
   int flag;                         // workgroup-wide result of a wait or a count
@@ -191,81 +191,42 @@ struct GroupRegs {
   ChunkRegs<BITS> g, u;
 };
 
-// Activation blocks [b0, b0 + nblk) of the layer input into LDS as
-// matrix-core A-fragments, with their accumulator seeds.  Thread p takes the
-// entries e = p + 512 i: block b = e / 4R, token row t = (e / 4) % R (the same
-// t for every i), quarter q = e % 4, i.e. inputs 32 (b0 + b) + 8q .. +8 of
-// token t.  They are loaded from xin, and after the selection scaled by 2^-ex
-// of the token (exact: the row's largest magnitude then lies in [2^14, 2^15))
-// and split into an fp16 hi part (A row t) and lo part (row t + 8), or, with
-// fp16 activations (R = 16 tokens), rounded to fp16 (row t).  The four
-// threads of a quad (q = 0..3, one block and token) add up their block sums.
-// Rows of tokens >= T are zeros.
+// Activation blocks [b0, b0 + nblk) of the layer input into LDS: the
+// A-fragments (1 KB per block) and accumulator seeds (16 floats per block)
+// the router wrote (XFrag), copied as 16-byte pieces (thread p takes pieces
+// p, p + 512, ...).  Every load is issued unconditionally (pieces past the
+// window re-read a valid address and are not stored), so a thread's loads
+// stay in flight together.
 template <bool A16>
 struct WindowRegs {
-  static constexpr int R = A16 ? MOE_MAX_TOK_F16ACT : MOE_MAX_TOK_DECODE;
-  static constexpr int PER = GU_WIN * 4 * R / (64 * GU_NW);
-  float4_t v[PER][2];
-  int ex;     // exponent of this thread's token (the values are scaled by 2^-ex)
-  bool live;  // this thread's token is below T (else its rows are zeros)
+  static constexpr int PER = GU_WIN * 64 / (64 * GU_NW);  // fragment pieces per thread
+  u32x4_t v[PER];
+  float4_t c;  // a piece of the seeds (threads below 4 nblk)
 };
 
-// Every load is issued unconditionally (blocks past the window and tokens
-// past T re-read a valid address; window_store drops them), so the loads of
-// a thread stay in flight together instead of each waiting behind a branch.
 template <bool A16>
 DEVI void window_load(WindowRegs<A16>& W, const GuArgs& a, int b0, int nblk, int tid) {
-  constexpr int R = WindowRegs<A16>::R;
-  const int t = (tid >> 2) % R, q = tid & 3;
-  W.live = t < a.T;
-  W.ex = W.live ? a.xexp[t] : 0;
-  const float* src = a.xin + (size_t)(W.live ? t : 0) * a.d + 32 * b0 + 8 * q;
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.x.frag) + (size_t)b0 * 64;
 #pragma unroll
-  for (int i = 0; i < WindowRegs<A16>::PER; ++i) {
-    const int b = min((tid + 64 * GU_NW * i) / (4 * R), nblk - 1);
-    W.v[i][0] = *reinterpret_cast<const float4_t*>(src + 32 * b);
-    W.v[i][1] = *reinterpret_cast<const float4_t*>(src + 32 * b + 4);
-  }
+  for (int i = 0; i < WindowRegs<A16>::PER; ++i) W.v[i] = src[min(tid + 64 * GU_NW * i, 64 * nblk - 1)];
+  W.c = reinterpret_cast<const float4_t*>(a.x.cs + (size_t)b0 * 16)[min(tid, 4 * nblk - 1)];
 }
 
 template <bool A16>
-DEVI void window_store(const WindowRegs<A16>& W, GuLds& L, int nblk, int code_off, int tid) {
-  constexpr int R = WindowRegs<A16>::R;
-  const int t = (tid >> 2) % R, q = tid & 3;
-  const float off = -(float)code_off;
+DEVI void window_store(const WindowRegs<A16>& W, GuLds& L, int nblk, int tid) {
 #pragma unroll
   for (int i = 0; i < WindowRegs<A16>::PER; ++i) {
-    const int b = (tid + 64 * GU_NW * i) / (4 * R);
-    if (b >= nblk) continue;  // (the four threads of a quad share b)
-    half8_t h, l;
-    float sh = 0.f, sl = 0.f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      // exact (2^-ex itself may exceed the fp32 range); rows past T are zeros
-      const float v = W.live ? ldexpf(W.v[i][c >> 2][c & 3], -W.ex) : 0.f;
-      h[c] = (_Float16)v;
-      sh += (float)h[c];
-      if (!A16) {
-        l[c] = (_Float16)(v - (float)h[c]);
-        sl += (float)l[c];
-      }
-    }
-    sh = quad_sum(sh);
-    *reinterpret_cast<half8_t*>(L.xs + ((size_t)b * 64 + t + 16 * q) * 16) = h;
-    if (q == 0) L.cs[b * 16 + t] = off * sh;
-    if (!A16) {
-      sl = quad_sum(sl);
-      *reinterpret_cast<half8_t*>(L.xs + ((size_t)b * 64 + t + 8 + 16 * q) * 16) = l;
-      if (q == 0) L.cs[b * 16 + t + 8] = off * sl;
-    }
+    const int p = tid + 64 * GU_NW * i;
+    if (p < 64 * nblk) *reinterpret_cast<u32x4_t*>(L.xs + (size_t)p * 16) = W.v[i];
   }
+  if (tid < 4 * nblk) *reinterpret_cast<float4_t*>(L.cs + 4 * tid) = W.c;
 }
 
 template <bool A16>
 DEVI void stage_window(GuLds& L, const GuArgs& a, int b0, int nblk, int tid) {
   WindowRegs<A16> W;
   window_load<A16>(W, a, b0, nblk, tid);
-  window_store<A16>(W, L, nblk, a.code_off, tid);
+  window_store<A16>(W, L, nblk, tid);
 }
 
 template <int BITS>
@@ -274,17 +235,37 @@ DEVI void issue_group(GroupRegs<BITS>& r, const uint8_t* gate, const uint8_t* up
   load_chunk<BITS>(r.u, up + off, lane);
 }
 
-// Eight blocks (one k-group) of gate and up; lb = first block in the window.
-template <int BITS>
-DEVI void mul_group(const GroupRegs<BITS>& r, const GuLds& L, int lb, int lane, float4_t& accg, float4_t& accu) {
+// Eight blocks (k-group kg) of gate and up; lb = its first block in the
+// window.  A k-group spans two column slices of the router (4 blocks each):
+// each slice's sum is scaled back by 2^e of its (slice, token) (exact) before
+// it joins the accumulators; this lane's C rows are tokens tok4 .. tok4 + 3.
+template <int BITS, bool A16>
+DEVI void mul_group(const GroupRegs<BITS>& r, const GuLds& L, int lb, int kg, int lane, float4_t& accg,
+                    float4_t& accu) {
+  static_assert(MOE_ROUTE_COLS == 128, "two column slices per k-group");
+  const int tok4 = A16 ? 4 * (lane >> 4) : 4 * ((lane >> 4) & 1);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const half8_t A = *reinterpret_cast<const half8_t*>(L.xs + (size_t)(lb + j) * 1024 + 16 * lane);
-    const float4_t cin = *reinterpret_cast<const float4_t*>(L.cs + (lb + j) * 16 + 4 * (lane >> 4));
-    const float4_t Cg = mfma16x16x32(A, chunk_frag<BITS>(r.g, j), cin);
-    const float4_t Cu = mfma16x16x32(A, chunk_frag<BITS>(r.u, j), cin);
-    accg += chunk_scale(r.g.scales, j) * Cg;
-    accu += chunk_scale(r.u.scales, j) * Cu;
+  for (int hs = 0; hs < 2; ++hs) {
+    float4_t pg = float4_t{0.f, 0.f, 0.f, 0.f}, pu = pg;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int j = 4 * hs + jj;
+      const half8_t A = *reinterpret_cast<const half8_t*>(L.xs + (size_t)(lb + j) * 1024 + 16 * lane);
+      const float4_t cin = *reinterpret_cast<const float4_t*>(L.cs + (lb + j) * 16 + 4 * (lane >> 4));
+      const float4_t Cg = mfma16x16x32(A, chunk_frag<BITS>(r.g, j), cin);
+      const float4_t Cu = mfma16x16x32(A, chunk_frag<BITS>(r.u, j), cin);
+      pg += chunk_scale(r.g.scales, j) * Cg;
+      pu += chunk_scale(r.u.scales, j) * Cu;
+    }
+    const int4 e = *reinterpret_cast<const int4*>(&L.sx[2 * kg + hs][tok4]);
+    accg[0] += ldexpf(pg[0], e.x);
+    accg[1] += ldexpf(pg[1], e.y);
+    accg[2] += ldexpf(pg[2], e.z);
+    accg[3] += ldexpf(pg[3], e.w);
+    accu[0] += ldexpf(pu[0], e.x);
+    accu[1] += ldexpf(pu[1], e.y);
+    accu[2] += ldexpf(pu[2], e.z);
+    accu[3] += ldexpf(pu[3], e.w);
   }
 }
 
@@ -295,7 +276,7 @@ DEVI void mul_group(const GroupRegs<BITS>& r, const GuLds& L, int lb, int lane, 
 // main loop has no early exit, so the loads in flight at every multiply are
 // the same and the compiler's wait counts stay exact; a tail of up to two
 // steps multiplies what is already in flight.
-template <int BITS>
+template <int BITS, bool A16>
 DEVI void run_tile(const uint8_t* gate, const uint8_t* up, int64_t rowoff, int kg0, int kg1, int step, int wkg0,
                    const GuLds& L, int lane, float4_t& accg, float4_t& accu) {
   constexpr int64_t CB = moe_chunk_bytes(BITS);
@@ -310,20 +291,20 @@ DEVI void run_tile(const uint8_t* gate, const uint8_t* up, int64_t rowoff, int k
   for (int it = nsteps / 3; it > 0; --it) {
     issue_group<BITS>(r2, gate, up, rowoff + min(kg + 2 * step, last) * CB, lane);
     __builtin_amdgcn_sched_barrier(0);
-    mul_group<BITS>(r0, L, 8 * (kg - wkg0), lane, accg, accu);
+    mul_group<BITS, A16>(r0, L, 8 * (kg - wkg0), kg, lane, accg, accu);
     kg += step;
     issue_group<BITS>(r0, gate, up, rowoff + min(kg + 2 * step, last) * CB, lane);
     __builtin_amdgcn_sched_barrier(0);
-    mul_group<BITS>(r1, L, 8 * (kg - wkg0), lane, accg, accu);
+    mul_group<BITS, A16>(r1, L, 8 * (kg - wkg0), kg, lane, accg, accu);
     kg += step;
     issue_group<BITS>(r1, gate, up, rowoff + min(kg + 2 * step, last) * CB, lane);
     __builtin_amdgcn_sched_barrier(0);
-    mul_group<BITS>(r2, L, 8 * (kg - wkg0), lane, accg, accu);
+    mul_group<BITS, A16>(r2, L, 8 * (kg - wkg0), kg, lane, accg, accu);
     kg += step;
   }
   const int rem = nsteps % 3;
-  if (rem >= 1) mul_group<BITS>(r0, L, 8 * (kg - wkg0), lane, accg, accu);
-  if (rem == 2) mul_group<BITS>(r1, L, 8 * (kg + step - wkg0), lane, accg, accu);
+  if (rem >= 1) mul_group<BITS, A16>(r0, L, 8 * (kg - wkg0), kg, lane, accg, accu);
+  if (rem == 2) mul_group<BITS, A16>(r1, L, 8 * (kg + step - wkg0), kg + step, lane, accg, accu);
 }
 
 // Selection and slot list of a gate/up workgroup (every workgroup runs it):
@@ -357,7 +338,14 @@ DEVI void gu_select(const GuArgs& a, GuLds& L, bool publish_routing, bool publis
     }
   }
   const float rnv = (tid >= 64 && tid < 64 + T) ? a.rnorm[tid - 64] : 1.0f;
-  const int xev = (tid >= 64 && tid < 64 + T) ? a.xexp[tid - 64] : 0;
+  // the fragments' exponents of every (column slice, token)
+  const int n_sx = 16 * (a.d / MOE_ROUTE_COLS);
+  int sxv[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = min(tid + 512 * h, n_sx - 1);
+    sxv[h] = a.x.sx[(size_t)(i >> 4) * MOE_XSX_STRIDE + (i & 15)];
+  }
   // the activation window (one window for inputs of up to GU_WIN blocks)
   // stays in registers through the selection and is stored to LDS before the
   // barrier that ends it: the selection starts as soon as its logits are in,
@@ -390,11 +378,11 @@ DEVI void gu_select(const GuArgs& a, GuLds& L, bool publish_routing, bool publis
     }
   }
   __builtin_amdgcn_sched_barrier(0);  // (the window's stores stay after the selection)
-  if (n_win == 1) window_store<A16>(win, L, 8 * n_kg, a.code_off, tid);
-  if (tid >= 64 && tid < 80) {
-    L.rn[tid - 64] = 1.0f / rnv;
-    L.rx[tid - 64] = xev;
-  }
+  if (n_win == 1) window_store<A16>(win, L, 8 * n_kg, tid);
+  if (tid >= 64 && tid < 80) L.rn[tid - 64] = 1.0f / rnv;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    if (tid + 512 * h < n_sx) (&L.sx[0][0])[tid + 512 * h] = sxv[h];
   lds_barrier();  // every token's experts marked, the window staged
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -471,7 +459,7 @@ DEVI void gu_items(const GuArgs& a, GuLds& L, int wg, int n_wg, uint32_t* h_read
         stage_window<A16>(L, a, 8 * kg0, 8 * (kg1 - kg0), tid);
         __syncthreads();
       }
-      if (valid) run_tile<BITS>(gate, up, (int64_t)t * n_kg * CB, kg0 + kp, kg1, KP, kg0, L, lane, accg, accu);
+      if (valid) run_tile<BITS, A16>(gate, up, (int64_t)t * n_kg * CB, kg0 + kp, kg1, KP, kg0, L, lane, accg, accu);
     }
     if (KP > 1) {
 #pragma unroll
@@ -510,11 +498,10 @@ DEVI void gu_items(const GuArgs& a, GuLds& L, int wg, int n_wg, uint32_t* h_read
         }
         const int tok = A16 ? 4 * (lane >> 4) + i : tok_e + i;
         const float gw = (u == 0 && has_shared) ? (tok < T ? 1.0f : 0.f) : L.S.w[u][tok];
-        // the norm's 1 / rms, then 2^ex undoes the activations' scaling (exact)
+        // the norm's 1 / rms (the fragments' scaling was undone per slice)
         const float rrn = L.rn[tok];
-        const int rx = L.rx[tok];
-        const float g = ldexpf((A16 ? sg : add_partner32(sg)) * rrn, rx);
-        const float uu = ldexpf((A16 ? su : add_partner32(su)) * rrn, rx);
+        const float g = (A16 ? sg : add_partner32(sg)) * rrn;
+        const float uu = (A16 ? su : add_partner32(su)) * rrn;
         const float hv = g * __builtin_amdgcn_rcpf(1.0f + expf(-g)) * uu;
         const float hs = (gw != 0.f) ? gw * hv : 0.f;
         if (writer) st_dev(hrow + tok * 16, hs);

@@ -171,7 +171,7 @@ PackedLayout packed_layout(const moe_layer_desc* D, const moe_expert_layout& ex,
 
 // ------------------------------------------------------------- workspace ---
 struct WsLayout {
-  int64_t ctrl, lp, ss_part, mx_part, rnorm, xexp, logits, n_slots, slot_expert, slot_w, xin, hbuf, ypart,
+  int64_t ctrl, lp, ss_part, rnorm, logits, n_slots, slot_expert, slot_w, xfrag, xcs, xsx, hbuf, ypart,
       total;
   int max_slots, S, nbI, n_cs;
 };
@@ -216,14 +216,14 @@ WsLayout ws_layout_decode(const moe_layer* L, int T, bool act16 = false) {
   W.ypart = take((int64_t)MOE_MAX_IN_SPLITS * MOE_MAX_TOK_F16ACT * d * 4);
   W.lp = take((int64_t)W.n_cs * T * E * 4);
   W.ss_part = take((int64_t)((E + MOE_ROUTE_ROWS - 1) / MOE_ROUTE_ROWS) * W.n_cs * T * 4);
-  W.mx_part = take((int64_t)W.n_cs * 16 * 4);
   W.rnorm = take(16 * 4);
-  W.xexp = take(16 * 4);
   W.logits = take((int64_t)T * logits_row(E) * 4);
   W.n_slots = take(4);
   W.slot_expert = take((int64_t)W.max_slots * 4);
   W.slot_w = take((int64_t)W.max_slots * 16 * 4);
-  W.xin = take((int64_t)MOE_MAX_TOK_F16ACT * d * 4);
+  W.xfrag = take((int64_t)(d / 32) * 1024);
+  W.xcs = take((int64_t)(d / 32) * 16 * 4);
+  W.xsx = take((int64_t)W.n_cs * MOE_XSX_STRIDE * 4);
   const int R = act16 ? MOE_MAX_TOK_F16ACT : MOE_MAX_TOK_DECODE;
   W.hbuf = take((int64_t)W.max_slots * R * W.nbI * 32 * 4);
   W.total = o;
@@ -233,11 +233,12 @@ WsLayout ws_layout_decode(const moe_layer* L, int T, bool act16 = false) {
 // Persistent decode pass of T tokens over up to n layers per launch
 // (persist.hip): the router's partial results, each layer's own copies of the
 // buffers the router step hands to the gate/up step and of h, and per-layer
-// maxima and counters (cleared together before each launch).  The down
-// partials sit where the per-phase layout has them.
+// counters (cleared before each launch).  The down partials sit where the
+// per-phase layout has them.
 struct PsLayout {
-  int64_t ctrl, ypart, lp, ss_part, mx_part, rnorm, xexp, logits, xin, hbuf, ctl, total;
-  int64_t logits_stride, xin_stride, hbuf_stride;  // floats per layer
+  int64_t ctrl, ypart, lp, ss_part, rnorm, logits, xfrag, xcs, xsx, hbuf, ctl, total;
+  int64_t logits_stride, hbuf_stride, xcs_stride, xsx_stride;  // elements per layer
+  int64_t xfrag_stride;                                        // fp16 elements per layer
   int max_slots, S, n_rs, n_cs, cpl, hI;
   size_t clear_words;  // ctl
 };
@@ -264,19 +265,21 @@ PsLayout ws_layout_persist(const moe_layer* L, int T, bool act16, int n_layers) 
   W.n_rs = (E + MOE_ROUTE_ROWS - 1) / MOE_ROUTE_ROWS;
   W.cpl = (W.n_rs + 1 + W.n_cs + W.max_slots) * MOE_CTR_STRIDE;
   W.logits_stride = moe_align256((int64_t)T * logits_row(E) * 4) / 4;
-  W.xin_stride = moe_align256((int64_t)MOE_MAX_TOK_F16ACT * d * 4) / 4;
   W.hbuf_stride = moe_align256((int64_t)W.max_slots * R * W.hI * 4) / 4;
+  W.xfrag_stride = moe_align256((int64_t)(d / 32) * 1024) / 2;
+  W.xcs_stride = moe_align256((int64_t)(d / 32) * 16 * 4) / 4;
+  W.xsx_stride = moe_align256((int64_t)W.n_cs * MOE_XSX_STRIDE * 4) / 4;
   int64_t o = 0;
   auto take = [&](int64_t bytes) { int64_t r = o; o += moe_align256(bytes); return r; };
   W.ctrl = take(ctrl_bytes());
   W.ypart = take((int64_t)MOE_MAX_IN_SPLITS * MOE_MAX_TOK_F16ACT * d * 4);
   W.lp = take((int64_t)W.n_cs * T * E * 4);
   W.ss_part = take((int64_t)W.n_rs * W.n_cs * T * 4);
-  W.mx_part = take((int64_t)W.n_cs * 16 * 4);
   W.rnorm = take((int64_t)n * MOE_PERSIST_TOK_STRIDE * 4);
-  W.xexp = take((int64_t)n * MOE_PERSIST_TOK_STRIDE * 4);
   W.logits = take((int64_t)n * W.logits_stride * 4);
-  W.xin = take((int64_t)n * W.xin_stride * 4);
+  W.xfrag = take((int64_t)n * W.xfrag_stride * 2);
+  W.xcs = take((int64_t)n * W.xcs_stride * 4);
+  W.xsx = take((int64_t)n * W.xsx_stride * 4);
   W.hbuf = take((int64_t)n * W.hbuf_stride * 4);
   const int64_t ctl_bytes = (int64_t)n * W.cpl * 4;
   W.ctl = take(ctl_bytes);
@@ -430,12 +433,12 @@ int decode_layer(const moe_layer* L, const LayerInput& in, float eps, int T, flo
   ra.do_logits = !forced;
   ra.act16 = act16;
   ra.lp = reinterpret_cast<float*>(ws + W.lp);
-  ra.xin = reinterpret_cast<float*>(ws + W.xin);
+  ra.x.frag = reinterpret_cast<_Float16*>(ws + W.xfrag);
+  ra.x.cs = reinterpret_cast<float*>(ws + W.xcs);
+  ra.x.sx = reinterpret_cast<int32_t*>(ws + W.xsx);
   ra.y_out = y_prev_out;
   SelectArgs& sa = ra.sel;
   sa.ss_part = reinterpret_cast<float*>(ws + W.ss_part);
-  sa.mx_part = reinterpret_cast<float*>(ws + W.mx_part);
-  sa.xexp = reinterpret_cast<int32_t*>(ws + W.xexp);
   sa.br = L->router_b;
   sa.ew = L->router_ew;
   sa.n_cs = W.n_cs;
@@ -470,8 +473,7 @@ int decode_layer(const moe_layer* L, const LayerInput& in, float eps, int T, flo
   ga.slot_expert = reinterpret_cast<int32_t*>(ws + W.slot_expert);
   ga.slot_w = reinterpret_cast<float*>(ws + W.slot_w);
   ga.rnorm = sa.rnorm;
-  ga.xin = ra.xin;
-  ga.xexp = sa.xexp;
+  ga.x = ra.x;
   ga.hbuf = reinterpret_cast<float*>(ws + W.hbuf);
   ga.E = E;
   ga.I = L->I;
@@ -1023,15 +1025,17 @@ static int persist_pass(const moe_layer* const* layers, int n_layers, const floa
   P.in_w = forced ? r->in_w : nullptr;
   P.lp = reinterpret_cast<float*>(ws + W.lp);
   P.ss_part = reinterpret_cast<float*>(ws + W.ss_part);
-  P.mx_part = reinterpret_cast<float*>(ws + W.mx_part);
   P.rnorm = reinterpret_cast<float*>(ws + W.rnorm);
-  P.xexp = reinterpret_cast<int32_t*>(ws + W.xexp);
   P.logits = reinterpret_cast<float*>(ws + W.logits);
-  P.xin = reinterpret_cast<float*>(ws + W.xin);
+  P.x.frag = reinterpret_cast<_Float16*>(ws + W.xfrag);
+  P.x.cs = reinterpret_cast<float*>(ws + W.xcs);
+  P.x.sx = reinterpret_cast<int32_t*>(ws + W.xsx);
   P.hbuf = reinterpret_cast<float*>(ws + W.hbuf);
   P.logits_stride = W.logits_stride;
   P.logits_row = logits_row(L->E);
-  P.xin_stride = W.xin_stride;
+  P.xfrag_stride = W.xfrag_stride;
+  P.xcs_stride = W.xcs_stride;
+  P.xsx_stride = W.xsx_stride;
   P.hbuf_stride = W.hbuf_stride;
   P.ctl = reinterpret_cast<uint32_t*>(ws + W.ctl);
   P.ypart = reinterpret_cast<float*>(ws + W.ypart);

@@ -22,12 +22,26 @@
 #define MOE_CTRL_WORDS 64
 
 // ---------------------------------------------------------------- decode ---
+// The layer input as the gate/up kernel's matrix-core A operand, written by
+// the router's row-slice-0 workgroups (one per column slice of
+// MOE_ROUTE_COLS inputs): every 32-input block as [64 lanes][8] fp16 (lane
+// m + 16q holds inputs 8q..8q+7 of row m: the fp16 hi part of token m for
+// m < 8 and the lo part of token m - 8 for m >= 8, or token m rounded to fp16
+// with 16 tokens), the block's accumulator seeds (-2^(b-1) times the row sums
+// of the block), and the power of two 2^-e every (column slice, token) was
+// scaled by before the split (e from the slice's largest magnitude of the
+// token: 2^14 <= max 2^-e < 2^15).
+#define MOE_XSX_STRIDE 64  // words between two slices' exponents (a 256-byte line each)
+struct XFrag {
+  _Float16* frag;  // [d/32][64][8]
+  float* cs;       // [d/32][16]
+  int32_t* sx;     // [d/MOE_ROUTE_COLS][MOE_XSX_STRIDE], token t at t
+};
+
 // Layer input: in = sum over S_in splits of in[s * in_stride + t * d + j]
 // (the previous layer's down partials, or the caller's x with S_in = 1).
 struct SelectArgs {
   float* ss_part;      // [n_rs][n_cs][T] sums of squares, one copy per row slice
-  float* mx_part;      // [n_cs][16] largest |input| of each column slice (row slice 0)
-  int32_t* xexp;       // ws [16]: exponent ex of each token row: 2^14 <= max|x| 2^-ex < 2^15
   const float* br;     // [E]
   const int32_t* ew;   // [E16] router row exponents (partial logits are unscaled)
   int32_t n_cs, n_rs, T, d, E, norm;
@@ -50,7 +64,7 @@ struct RouteArgs {
   int32_t T, d, E, code_off, do_logits;
   int32_t act16;    // 1: gate/up A-fragments hold 16 tokens in fp16 (else 8 tokens as fp16 hi + lo)
   float* lp;        // ws [d/MOE_ROUTE_COLS][T][E] partial logits
-  float* xin;       // ws [16][d]: the summed layer input (row slice 0 writes it)
+  XFrag x;          // the gate/up kernel's A operand (row slice 0 writes it)
   float* y_out;     // optional: the summed input, [T][d]
   SelectArgs sel;   // the logits, finished by the last workgroup of each row slice
 };
@@ -81,8 +95,7 @@ struct GuArgs {
   int32_t* slot_expert;  // out [MAX_SLOTS]
   float* slot_w;         // out [MAX_SLOTS][16]
   const float* rnorm;
-  const float* xin;      // [16][d] layer input rows (before the RMSNorm of stacked layers)
-  const int32_t* xexp;   // [16] row exponents (the fragments hold x 2^-ex)
+  XFrag x;               // the layer input as A-fragments (before the RMSNorm of stacked layers)
   float* hbuf;      // ws [MAX_SLOTS][hI/16][R][16] fp32 h = w silu(g) u, R = 16 (act16) or 8
   int32_t E, I, Is, T, d, n_kg, bits, hI, code_off, has_shared;
   int32_t act16;  // 1: A rows are 16 tokens in fp16 (else 8 tokens as fp16 hi + lo)
@@ -144,16 +157,14 @@ struct PersistArgs {
   // workspace
   float* lp;
   float* ss_part;
-  float* mx_part;
   // per layer (a layer's copy is written once per pass, by one workgroup
   // per cache line, and no line holds two layers' words, so its readers may
   // use L2-cached loads): layer l's buffer at base + l * stride
   float* rnorm;      // [n][MOE_PERSIST_TOK_STRIDE]
-  int32_t* xexp;     // [n][MOE_PERSIST_TOK_STRIDE]
   float* logits;     // [n][T][logits_row]
-  float* xin;        // [n][16][d]
+  XFrag x;           // layer 0's; layer l's at + l * the strides below
   float* hbuf;       // [n][max_slots][hI/16][R][16]
-  int64_t logits_stride, xin_stride, hbuf_stride;
+  int64_t logits_stride, hbuf_stride, xfrag_stride, xcs_stride, xsx_stride;
   int32_t logits_row;  // floats per token row of the logits
   uint32_t* ctl;     // [n_layers][cpl], counters MOE_CTR_STRIDE words apart
   float* ypart;      // [S][R][d]

@@ -87,9 +87,11 @@ __global__ __launch_bounds__(512) void decode_persist_kernel(PersistArgs P) {
     uint32_t* h_ready = y_ready + n_cs * CS;
     const uint32_t* y_prev = l > 0 ? P.ctl + (size_t)(l - 1) * P.cpl + (n_rs + 1) * CS : nullptr;
     float* logits = P.logits + (size_t)l * P.logits_stride;
-    float* xin = P.xin + (size_t)l * P.xin_stride;
     float* rnorm = P.rnorm + (size_t)l * MOE_PERSIST_TOK_STRIDE;
-    int32_t* xexp = P.xexp + (size_t)l * MOE_PERSIST_TOK_STRIDE;
+    XFrag xf;
+    xf.frag = P.x.frag + (size_t)l * P.xfrag_stride;
+    xf.cs = P.x.cs + (size_t)l * P.xcs_stride;
+    xf.sx = P.x.sx + (size_t)l * P.xsx_stride;
     float* hbuf = P.hbuf + (size_t)l * P.hbuf_stride;
 
     // ---------------------------------------------------------- router ---
@@ -106,12 +108,10 @@ __global__ __launch_bounds__(512) void decode_persist_kernel(PersistArgs P) {
     ra.do_logits = !forced;
     ra.act16 = A16;
     ra.lp = P.lp;
-    ra.xin = xin;
+    ra.x = xf;
     ra.y_out = l == 0 ? P.y_prev_out : (P.y_layers ? P.y_layers + (size_t)(l - 1) * P.yl_stride : nullptr);
     SelectArgs& sa = ra.sel;
     sa.ss_part = P.ss_part;
-    sa.mx_part = P.mx_part;
-    sa.xexp = xexp;
     sa.br = reinterpret_cast<const float*>(pb + P.off_br);
     sa.ew = reinterpret_cast<const int32_t*>(pb + P.off_ew);
     sa.n_cs = n_cs;
@@ -154,8 +154,7 @@ __global__ __launch_bounds__(512) void decode_persist_kernel(PersistArgs P) {
     ga.out_w = P.w_layers ? P.w_layers + (size_t)l * P.route_stride : nullptr;
     ga.k = P.k;
     ga.rnorm = rnorm;
-    ga.xin = xin;
-    ga.xexp = xexp;
+    ga.x = xf;
     ga.hbuf = hbuf;
     ga.E = P.E;
     ga.I = P.I;

@@ -68,12 +68,11 @@ DEVI void finish_slice(const RouteArgs& a, int rs) {
   const float* ssr = c.ss_part + (size_t)rs * n_cs * T;
   for (int h = 0; 8 * h < T; ++h) {
     int t[2];
-    float ss[2], mx[2], tmp[2][MAXCS];
+    float ss[2], tmp[2][MAXCS];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       t[j] = min(8 * h + wv + 4 * j, T - 1);
       ss[j] = ld_dev(ssr + min(lane, n_cs - 1) * T + t[j]);
-      mx[j] = rs == 0 ? ld_dev(c.mx_part + min(lane, n_cs - 1) * 16 + t[j]) : 0.f;
       if (a.do_logits) {
 #pragma unroll
         for (int q = 0; q < MAXCS; ++q) tmp[j][q] = ld_dev(a.lp + ((size_t)min(q, n_cs - 1) * T + t[j]) * E + e);
@@ -83,12 +82,8 @@ DEVI void finish_slice(const RouteArgs& a, int rs) {
     for (int j = 0; j < 2; ++j) {
       const int tok = 8 * h + wv + 4 * j;
       const float r = c.norm ? sqrtf(wave_sum((lane < n_cs) ? ss[j] : 0.f) / (float)c.d + c.eps) : 1.0f;
-      const float m = wave_max((lane < n_cs) ? mx[j] : 0.f);
       if (tok >= T) continue;
-      if (rs == 0 && lane == 0) {
-        st_dev(c.rnorm + tok, r);
-        st_dev_i(c.xexp + tok, fp16_exponent_for(m));
-      }
+      if (rs == 0 && lane == 0) st_dev(c.rnorm + tok, r);
       if (!a.do_logits) continue;
       float acc = tmp[j][0];
 #pragma unroll
@@ -106,8 +101,8 @@ DEVI void finish_slice(const RouteArgs& a, int rs) {
 
 // reset: put the counter back to zero for the next launch (the persistent
 // kernel's counters are per layer and cleared before each pass instead).
-// With done, the finishing workgroup adds one to it once its logits, divisors
-// and exponents are stored.
+// With done, the finishing workgroup adds one to it once its logits and
+// divisors are stored.
 DEVI void route_finish(const RouteArgs& a, int rs, int* flag, bool reset, uint32_t* done) {
   uint32_t* ctr = a.sel.ctrl + (size_t)rs * a.sel.ctrl_stride;
   if (!count_done(ctr, (uint32_t)a.sel.n_cs, flag)) return;
@@ -127,10 +122,10 @@ DEVI void route_finish(const RouteArgs& a, int rs, int* flag, bool reset, uint32
 // Route: workgroup (column slice cs of 128 inputs, row slice rs of 64
 // experts).  Sums the input splits for its columns, writes partial logits of
 // its 64 experts over those columns and the slice's sums of squares (every
-// row slice its own copy); the rs == 0 workgroups also write the summed input
-// slice (xin, for the gate/up kernel, and the caller's copy if asked) and its
-// largest magnitude per token (the finishing workgroup turns those into the
-// row exponents the gate/up kernel scales the activations by).
+// row slice its own copy); the rs == 0 workgroups also write the slice's
+// blocks of the gate/up kernel's A operand (XFrag: the fragments, their
+// accumulator seeds and the slice's token exponents) and the caller's copy
+// of the summed input if asked.
 // The partial logits run on the matrix cores: fp16 hi/lo A-fragments of 8
 // tokens of the slice scaled by 2^-e (e per token and slice, from the
 // slice's largest magnitude, so the split neither overflows nor underflows;
@@ -161,6 +156,40 @@ DEVI half8_t x_fragment(const float (*ys)[MOE_ROUTE_COLS], int bl, int lane, int
     h[c] = lo ? (_Float16)(v - (float)hi) : hi;
   }
   return h;
+}
+
+// The same for 16 tokens in fp16 (fp16 activations): lane L = m + 16q holds
+// token m at inputs 8q..8q+7, scaled by 2^-e of the token, rounded to fp16.
+DEVI half8_t x_fragment16(const float (*ys)[MOE_ROUTE_COLS], int bl, int lane, int T, int e) {
+  const int m = lane & 15, q = lane >> 4;
+  float4_t v0 = float4_t{0.f, 0.f, 0.f, 0.f}, v1 = v0;
+  if (m < T) {
+    v0 = *reinterpret_cast<const float4_t*>(&ys[m][32 * bl + 8 * q]);
+    v1 = *reinterpret_cast<const float4_t*>(&ys[m][32 * bl + 8 * q + 4]);
+  }
+  half8_t h;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) h[c] = (_Float16)ldexpf(c < 4 ? v0[c] : v1[c - 4], -e);
+  return h;
+}
+
+// Row slice 0 only: block bl of this column slice as the gate/up kernel's
+// A-fragment (device-coherent 16-byte stores) and its accumulator seeds
+// (-2^(b-1) times each row's sum of the block's 32 fp16 values, four lanes
+// per row added), one wavefront per block.
+DEVI void write_xfrag(const RouteArgs& a, int cs, const float (*ys)[MOE_ROUTE_COLS], const int* xe, int bl,
+                      int lane) {
+  const int T = a.T;
+  const half8_t A = a.act16 ? x_fragment16(ys, bl, lane, T, xe[min(lane & 15, T - 1)])
+                            : x_fragment(ys, bl, lane, T, xe[min(lane & 7, T - 1)]);
+  const int b = cs * (MOE_ROUTE_COLS / 32) + bl;
+  coh_st4(coh_rsrc(a.x.frag), (uint32_t)(((size_t)b * 64 + lane) * 16), __builtin_bit_cast(float4_t, A));
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) s += (float)A[c];
+  s += __shfl_xor(s, 16, 64);
+  s += __shfl_xor(s, 32, 64);
+  if (lane < 16) st_dev(a.x.cs + (size_t)b * 16 + lane, -(float)a.code_off * s);
 }
 
 // One route role (column slice cs, row slice rs) run by the first 256
@@ -226,7 +255,6 @@ DEVI bool route_role(const RouteArgs& a, int cs, int rs, float (*ys)[MOE_ROUTE_C
     load_router();
   }
   // summed input slice into LDS (splits added in order)
-  const __amdgpu_buffer_rsrc_t xr = coh_rsrc(a.xin);
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const int i = tid + 256 * j, t = i / RQ, c4 = i % RQ;
@@ -236,10 +264,7 @@ DEVI bool route_role(const RouteArgs& a, int cs, int rs, float (*ys)[MOE_ROUTE_C
       for (int s = 1; s < MOE_MAX_IN_SPLITS; ++s)
         if (s < a.S_in) acc += v[j][s];
       *reinterpret_cast<float4_t*>(&ys[t][4 * c4]) = acc;
-      if (rs == 0) {
-        coh_st4(xr, (uint32_t)((size_t)t * d + c0 + 4 * c4) * 4, acc);
-        if (a.y_out) *reinterpret_cast<float4_t*>(a.y_out + (size_t)t * d + c0 + 4 * c4) = acc;
-      }
+      if (rs == 0 && a.y_out) *reinterpret_cast<float4_t*>(a.y_out + (size_t)t * d + c0 + 4 * c4) = acc;
     }
   }
   __syncthreads();
@@ -252,11 +277,15 @@ DEVI bool route_role(const RouteArgs& a, int cs, int rs, float (*ys)[MOE_ROUTE_C
     const float mx = wave_max(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
     if (lane == 0) {
       st_dev(a.sel.ss_part + ((size_t)rs * a.sel.n_cs + cs) * T + t, ss);
-      if (rs == 0) st_dev(a.sel.mx_part + cs * 16 + t, mx);
       xe[t] = fp16_exponent_for(mx);
     }
   }
   __syncthreads();
+  if (rs == 0) {
+    static_assert(MOE_ROUTE_COLS == 128, "one wavefront per block of the slice");
+    if (active) write_xfrag(a, cs, ys, xe, wv, lane);
+    if (tid < 16) st_dev_i(a.x.sx + (size_t)cs * MOE_XSX_STRIDE + tid, tid < T ? xe[tid] : 0);
+  }
 
   if (tile_ok) {
     // row tiles of 8 tokens: tokens 8 tb .. 8 tb + 7
