@@ -41,19 +41,6 @@
 
 namespace {
 
-// The codebook grid of the layer being multiplied (codebook blocks only):
-// 512 entries of 4 fp16 magnitudes, staged by load_grid at kernel start.
-// Kernels of the b-bit kinds never touch it, so it takes no LDS there.
-__shared__ uint2 cb_grid_lds[512];
-
-// Stage the grid (all threads of the workgroup; a barrier must follow
-// before the first chunk_frag).
-template <int BITS>
-DEVI void load_grid(const uint32_t* grid16, int tid, int nthreads) {
-  if constexpr (BITS == MOE_KIND_CB)
-    for (int i = tid; i < 512; i += nthreads) cb_grid_lds[i] = reinterpret_cast<const uint2*>(grid16)[i];
-}
-
 // A lane's share of one chunk.  b-bit kinds: codes (16 B), the 8 fp16
 // scales of its row, and for 3 bits the high bits (8 B).  Codebook: index
 // bytes (in codes), scales, sign bits (in hbits) and index high bits (hi).

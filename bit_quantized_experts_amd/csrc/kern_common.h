@@ -66,6 +66,22 @@ DEVI half8_t frag_q3(const u32x4_t& w, const u32x2_t& hbits, int f) {
 }
 
 // ---------------------------------------------------------------------------
+// The codebook grid of the layer being multiplied (codebook blocks only):
+// 512 entries of 4 fp16 magnitudes, staged by load_grid at kernel start.
+// Kernels of the b-bit kinds never touch it, so it takes no LDS there.
+// ---------------------------------------------------------------------------
+__shared__ uint2 cb_grid_lds[512];
+
+// Stage the grid (all threads of the workgroup; a barrier must follow
+// before the first fragment decode).  The block kinds are those of
+// moe_launch.h: MOE_KIND_CB = 4.
+template <int BITS>
+DEVI void load_grid(const uint32_t* grid16, int tid, int nthreads) {
+  if constexpr (BITS == 4)
+    for (int i = tid; i < 512; i += nthreads) cb_grid_lds[i] = reinterpret_cast<const uint2*>(grid16)[i];
+}
+
+// ---------------------------------------------------------------------------
 // Codebook fragments.  The lane's chunk data: 16 index bytes (bytes 2f and
 // 2f+1: the low 8 bits of the two grid indices of fragment f, inputs 8q..8q+3
 // and 8q+4..8q+7), 16 index high bits (bits 2f, 2f+1) and 64 sign bits (bits

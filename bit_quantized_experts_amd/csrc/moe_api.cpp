@@ -815,22 +815,16 @@ static int pack_layer(const moe_layer_desc* desc, const void* experts_canon, con
   if (L->grid16 &&
       (e = launch_pack_grid(grid, reinterpret_cast<uint16_t*>(const_cast<uint32_t*>(L->grid16)), status, s)) != hipSuccess)
     return bail(fail(MOE_ERR_HIP, "grid: %s", hipGetErrorString(e)));
-  if (L->bits == MOE_KIND_CB) {
-    // the exponent bounds serve the prefill kernels only, which codebook
-    // blocks do not run
-    if ((e = launch_fill_u32(reinterpret_cast<uint32_t*>(const_cast<int32_t*>(L->hbound)), 2 * (size_t)(L->E + 1), 0u,
-                             s)) != hipSuccess)
-      return bail(fail(MOE_ERR_HIP, "bound fill: %s", hipGetErrorString(e)));
-  } else {
+  {
     int32_t* hb = const_cast<int32_t*>(L->hbound);
     int32_t* edp = const_cast<int32_t*>(L->dbound);
     const int64_t stride = 3 * (int64_t)L->I * (L->d / 32) * bb;
-    if ((e = launch_pack_hbound(reinterpret_cast<const uint8_t*>(experts_canon), stride, L->E, L->I, L->d, L->bits, hb,
-                                edp, s)) != hipSuccess)
+    if ((e = launch_pack_hbound(reinterpret_cast<const uint8_t*>(experts_canon), stride, L->E, L->I, L->d, L->bits, grid,
+                                hb, edp, s)) != hipSuccess)
       return bail(fail(MOE_ERR_HIP, "bound: %s", hipGetErrorString(e)));
     if (L->Is > 0) {
-      if ((e = launch_pack_hbound(reinterpret_cast<const uint8_t*>(shared_canon), 0, 1, L->Is, L->d, L->bits, hb + L->E,
-                                  edp + L->E, s)) != hipSuccess)
+      if ((e = launch_pack_hbound(reinterpret_cast<const uint8_t*>(shared_canon), 0, 1, L->Is, L->d, L->bits, grid,
+                                  hb + L->E, edp + L->E, s)) != hipSuccess)
         return bail(fail(MOE_ERR_HIP, "bound: %s", hipGetErrorString(e)));
     } else {
       if ((e = launch_fill_u32(reinterpret_cast<uint32_t*>(hb + L->E), 1, 0u, s)) != hipSuccess ||
@@ -854,7 +848,8 @@ static int pack_layer(const moe_layer_desc* desc, const void* experts_canon, con
   if ((e = hipMemcpyAsync(&flag, status, 4, hipMemcpyDeviceToHost, s)) != hipSuccess)
     return bail(fail(MOE_ERR_HIP, "status copy: %s", hipGetErrorString(e)));
   if ((e = hipStreamSynchronize(s)) != hipSuccess) return bail(fail(MOE_ERR_HIP, "sync: %s", hipGetErrorString(e)));
-  if (flag & 1u) return bail(fail(MOE_ERR_DATA, "a block scale is inf/nan or has magnitude >= 8192"));
+  if (flag & 1u)
+    return bail(fail(MOE_ERR_DATA, "a block scale is inf/nan or has magnitude >= %d", L->bits == MOE_KIND_CB ? 256 : 8192));
   if (flag & 2u) return bail(fail(MOE_ERR_DATA, "a codebook magnitude is above 127"));
   *out = L;
   return MOE_OK;
@@ -932,7 +927,7 @@ int moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
 
 // Argument checks shared by the layer entry points.
 static int layer_args(const moe_layer* L, const float* x, int T, float* y, const moe_route_io* route, void* ws,
-                      size_t ws_bytes, int max_tok = MOE_MAX_TOK_DECODE) {
+                      size_t ws_bytes) {
   if (!L) return fail(MOE_ERR_ARG, "layer is NULL");
   if (T < 0) return fail(MOE_ERR_ARG, "T must be >= 0");
   if (T == 0) return MOE_OK;
@@ -944,8 +939,6 @@ static int layer_args(const moe_layer* L, const float* x, int T, float* y, const
   if (xb < yb + nbytes && yb < xb + nbytes) return fail(MOE_ERR_ARG, "x and y must not alias");
   if (route && ((route->in_idx == nullptr) != (route->in_w == nullptr)))
     return fail(MOE_ERR_ARG, "in_idx and in_w must be given together");
-  if (L->bits == MOE_KIND_CB && T > max_tok)
-    return fail(MOE_ERR_UNSUPPORTED, "codebook blocks run the decode path only: T <= %d (got %d)", max_tok, T);
   size_t need;
   int rc = check_ws(L, T, 1, ws, ws_bytes, &need);
   if (rc) return rc;
@@ -1108,7 +1101,7 @@ int moe_layer_forward_noalloc(const moe_layer* L, const float* x, int T, float* 
 int moe_layer_forward_f16act(const moe_layer* L, const float* x, int T, float* y, const moe_route_io* route,
                              void* ws, size_t ws_bytes, void* stream) {
   if (T > MOE_MAX_TOK_F16ACT) return fail(MOE_ERR_UNSUPPORTED, "T above %d not supported with fp16 activations", MOE_MAX_TOK_F16ACT);
-  int rc = layer_args(L, x, T, y, route, ws, ws_bytes, MOE_MAX_TOK_F16ACT);
+  int rc = layer_args(L, x, T, y, route, ws, ws_bytes);
   if (rc || T == 0) return rc;
   return decode_layer_out(L, x, T, y, route, reinterpret_cast<uint8_t*>(ws), reinterpret_cast<hipStream_t>(stream),
                           true);
@@ -1128,9 +1121,6 @@ static int stack_args(const moe_layer* const* layers, int n_layers, const float*
   for (int l = 0; l < n_layers; ++l) {
     if (!layers[l]) return fail(MOE_ERR_ARG, "layer %d is NULL", l);
     if (layers[l]->d != d) return fail(MOE_ERR_ARG, "layer %d has d_model %d, expected %d", l, layers[l]->d, d);
-    if (layers[l]->bits == MOE_KIND_CB && T > 2 * MOE_MAX_TOK_DECODE)
-      return fail(MOE_ERR_UNSUPPORTED, "codebook blocks run the decode path only: T <= %d (got %d)",
-                  2 * MOE_MAX_TOK_DECODE, T);
     size_t need;
     int rc = check_ws(layers[l], T, n_layers, ws, ws_bytes, &need);
     if (rc) return rc;
@@ -1311,7 +1301,6 @@ int moe_debug_unpack_path(const moe_layer* L, int expert, int mat, int path, int
   if (path < 0 || path > 2) return fail(MOE_ERR_ARG, "path must be 0, 1 or 2");
   if (path == 0 && w_f16) return fail(MOE_ERR_ARG, "path 0 exports codes and w_f32 only");
   if (path > 0 && (codes || w_f32)) return fail(MOE_ERR_ARG, "paths 1 and 2 export w_f16 only");
-  if (path > 0 && L->bits == MOE_KIND_CB) return fail(MOE_ERR_UNSUPPORTED, "codebook blocks have no prefill path");
   if (!codes && !w_f32 && !w_f16) return MOE_OK;
   const moe_expert_layout& X = expert < 0 ? L->sh : L->ex;
   const uint8_t* base = expert < 0 ? L->shared : L->experts + (int64_t)expert * L->ex.bytes;

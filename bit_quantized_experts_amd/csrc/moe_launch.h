@@ -299,7 +299,7 @@ struct PfCombineArgs {
 
 hipError_t launch_pack_router(const float* W, int E, int d, _Float16* wh, _Float16* wl, int32_t* ew, hipStream_t s);
 hipError_t launch_pack_hbound(const uint8_t* canon, int64_t canon_stride, int n_experts, int I, int d, int bits,
-                              int32_t* hb, int32_t* ed, hipStream_t s);
+                              const uint8_t* grid, int32_t* hb, int32_t* ed, hipStream_t s);
 hipError_t launch_pf_prep(const PfPrepArgs& a, hipStream_t s);
 hipError_t launch_pf_router(const PfRouterArgs& a, hipStream_t s);
 hipError_t launch_pf_group(const PfGroupArgs& a, hipStream_t s);

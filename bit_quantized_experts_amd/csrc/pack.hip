@@ -53,7 +53,10 @@ __global__ __launch_bounds__(256) void pack_matrix_kernel(PackArgs a) {
     const int blk = kg * a.BK + j;
     const uint8_t* B = cb + (row * nb + blk) * bb;
     const uint32_t s = (uint32_t)B[0] | ((uint32_t)B[1] << 8);
-    bad |= (s & 0x7fffu) >= 0x7000u;  // exponent field 28..31: |s| >= 8192, inf or nan
+    // b-bit codes: exponent field 28..31 (|s| >= 8192, inf or nan); codebook
+    // magnitudes reach 127, so there |s| >= 256 (0x5C00) is refused: s * c
+    // then stays below 2^15 in fp16, as for the b-bit codes
+    bad |= (s & 0x7fffu) >= (cbk ? 0x5C00u : 0x7000u);
     sc[f >> 1] |= s << (16 * (f & 1));
     if (cbk) {
       // indices 2q, 2q+1 (inputs 8q..8q+7), their high bits, sign byte q

@@ -55,19 +55,24 @@ DEVI _Float16 half_of_bits(uint32_t b) {
 // Weight registers of one 16-row tile for up to 8 fragments (a full chunk) or
 // 4 fragments (half a chunk: codes and scales in elements [0..1], high bits
 // in hi[0]).  Fragment f: codes dword f/2 at shift 2(f%2), fp16 scale half f,
-// high bits dword f/4 at bit f%4.
+// high bits dword f/4 at bit f%4.  Codebook blocks (MOE_KIND_CB): codes hold
+// the index low bytes (bytes 2f, 2f+1), hi the sign bits (byte f), ih the
+// index high bits (bits 2f, 2f+1), all renumbered from the half's first
+// fragment for a half chunk.
 // ---------------------------------------------------------------------------
 struct WRegs {
   u32x4_t codes;
   u32x4_t scales;
   u32x2_t hi;
+  uint32_t ih;
 };
 
 template <int BITS>
 DEVI void load_full(WRegs& w, const uint8_t* chunk, int lane) {
   w.codes = ld128(chunk + 16 * lane);
   w.scales = ld128(chunk + 1024 + 16 * (lane & 15));
-  if constexpr (BITS == 3) w.hi = ld64(chunk + 1280 + 8 * lane);
+  if constexpr (BITS != 2) w.hi = ld64(chunk + 1280 + 8 * lane);
+  if constexpr (BITS == MOE_KIND_CB) w.ih = *reinterpret_cast<const uint16_t*>(chunk + 1792 + 2 * lane);
 }
 
 // fragments 4h..4h+3 of a chunk
@@ -77,21 +82,28 @@ DEVI void load_half(WRegs& w, const uint8_t* chunk, int h, int lane) {
   const u32x2_t s = ld64(chunk + 1024 + 16 * (lane & 15) + 8 * h);
   w.codes = u32x4_t{c[0], c[1], 0u, 0u};
   w.scales = u32x4_t{s[0], s[1], 0u, 0u};
-  if constexpr (BITS == 3) w.hi = u32x2_t{*reinterpret_cast<const uint32_t*>(chunk + 1280 + 8 * lane + 4 * h), 0u};
+  if constexpr (BITS != 2) w.hi = u32x2_t{*reinterpret_cast<const uint32_t*>(chunk + 1280 + 8 * lane + 4 * h), 0u};
+  if constexpr (BITS == MOE_KIND_CB) w.ih = (uint32_t)chunk[1792 + 2 * lane + h];
 }
 
 // w = s * (q - 2^(b-1)) for the lane's 8 codes of fragment f, in fp16: q is
 // exact from the fp4 conversion, the fused multiply-add rounds once.
+// Codebook blocks: w = s * c with c the signed code from the LDS grid, one
+// rounding.
 template <int BITS>
 DEVI half8_t dequant(const WRegs& w, int f) {
-  const uint32_t dw = w.codes[f >> 1];
-  half8_t q = nibbles_to_half8(((f & 1) ? (dw >> 2) : dw) & 0x33333333u, 2.0f);
-  if constexpr (BITS == 3) q += nibbles_to_half8((w.hi[f >> 2] >> (f & 3)) & 0x11111111u, 8.0f);
   const uint32_t sd = w.scales[f >> 1];
   const _Float16 s = half_of_bits((f & 1) ? (sd >> 16) : sd);
   const half8_t sv = s;
-  const half8_t ov = sv * (_Float16)(-(float)(1 << (BITS - 1)));
-  return __builtin_elementwise_fma(q, sv, ov);
+  if constexpr (BITS == MOE_KIND_CB) {
+    return frag_cb(w.codes, w.ih, w.hi, f, cb_grid_lds) * sv;
+  } else {
+    const uint32_t dw = w.codes[f >> 1];
+    half8_t q = nibbles_to_half8(((f & 1) ? (dw >> 2) : dw) & 0x33333333u, 2.0f);
+    if constexpr (BITS == 3) q += nibbles_to_half8((w.hi[f >> 2] >> (f & 3)) & 0x11111111u, 8.0f);
+    const half8_t ov = sv * (_Float16)(-(float)(1 << (BITS - 1)));
+    return __builtin_elementwise_fma(q, sv, ov);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -144,10 +156,11 @@ __global__ __launch_bounds__(256) void pack_router_kernel(const float* W, int E,
 // 2^15.  One workgroup per expert.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void pack_hbound_kernel(const uint8_t* canon, int64_t stride, int I, int d, int bits,
-                                                          int32_t* hb, int32_t* ed) {
+                                                          const uint8_t* grid, int32_t* hb, int32_t* ed) {
   __shared__ float red[3][4];
   const uint8_t* ex = canon + (int64_t)blockIdx.x * stride;
-  const int nb = d / 32, nbI = I / 32, bb = 2 + 4 * bits, off = 1 << (bits - 1);
+  const bool cbk = bits == MOE_KIND_CB;
+  const int nb = d / 32, nbI = I / 32, bb = cbk ? 15 : 2 + 4 * bits, off = cbk ? 0 : 1 << (bits - 1);
   float lmax[3] = {0.f, 0.f, 0.f};
   for (int m = 0; m < 3; ++m) {
     const uint8_t* mat = ex + (int64_t)m * I * nb * bb;
@@ -158,10 +171,18 @@ __global__ __launch_bounds__(256) void pack_hbound_kernel(const uint8_t* canon, 
         const uint8_t* B = mat + ((int64_t)i * nblk + b) * bb;
         const float sc = fabsf(half_bits_to_float((uint32_t)B[0] | ((uint32_t)B[1] << 8)));
         int cs = 0;
-        for (int j = 0; j < 32; ++j) {
-          const int bit = bits * j, by = bit >> 3;
-          const uint32_t v = (uint32_t)B[2 + by] | (by + 1 < 4 * bits ? (uint32_t)B[3 + by] << 8 : 0u);
-          cs += abs((int)((v >> (bit & 7)) & ((1u << bits) - 1u)) - off);
+        if (cbk) {
+          // the magnitudes of the block's eight grid entries (signs do not count)
+          for (int i = 0; i < 8; ++i) {
+            const int index = B[2 + i] | (((B[10] >> i) & 1) << 8);
+            for (int c = 0; c < 4; ++c) cs += grid[4 * index + c];
+          }
+        } else {
+          for (int j = 0; j < 32; ++j) {
+            const int bit = bits * j, by = bit >> 3;
+            const uint32_t v = (uint32_t)B[2 + by] | (by + 1 < 4 * bits ? (uint32_t)B[3 + by] << 8 : 0u);
+            cs += abs((int)((v >> (bit & 7)) & ((1u << bits) - 1u)) - off);
+          }
         }
         sum += sc * (float)cs;
       }
@@ -596,7 +617,7 @@ DEVI void gate_up_item(const PfGemmArgs& a, const Stages& S, int* ex_lds, int g,
   const int h0 = nt * PF_HT + 32 * wv;
   const bool act = h0 < Ig;
   const int nkg = a.d / 256;
-  constexpr int CB = BITS == 2 ? 1280 : 1792;
+  constexpr int CB = moe_chunk_bytes(BITS);
   const uint8_t* cp[4];
   {
     const uint8_t* gate = eb + (shared ? a.X.sh_off_gate : a.X.off_gate);
@@ -721,6 +742,7 @@ __global__ __launch_bounds__(256, 2) void pf_gate_up_kernel(PfGemmArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char st1[GEMM_STAGE];
   unsigned char* const st2 = st0;  // (two stages; a third is never used)
   __shared__ int ex_lds[PF_TM];
+  load_grid<BITS>(a.X.grid16, threadIdx.x, 256);  // (the first step's barrier publishes it)
   int item, nt;
   // a workgroup without a work item reads the next layer's lines ahead
   // (its share of them: rank blockIdx.x of the grid)
@@ -767,7 +789,7 @@ DEVI void down_item(const PfGemmArgs& a, const Stages& S, float* rowf_lds, int g
   using M = DownMap<BK>;
   constexpr int RT = 8 / BK;
   static_assert(RT * BK == 8, "chunk shape");
-  constexpr int CB = BITS == 2 ? 1280 : 1792;
+  constexpr int CB = moe_chunk_bytes(BITS);
   const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, n = lane & 15, q = lane >> 4;
   const bool shared = g == a.E;
   const int Ig = shared ? a.Is : a.I;
@@ -886,6 +908,7 @@ __global__ __launch_bounds__(256, 2) void pf_down_kernel(PfGemmArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char st1[GEMM_STAGE];
   unsigned char* const st2 = st0;  // (two stages; a third is never used)
   __shared__ float rowf_lds[PF_TM];
+  load_grid<BITS>(a.X.grid16, threadIdx.x, 256);  // (the first step's barrier publishes it)
   int item, nt;
   if (!xcd_tile(*a.n_items, a.d / PF_DT, &item, &nt)) return;
   const int g = a.item_group[item], row0 = a.item_row0[item], rows = a.item_rows[item];
@@ -947,6 +970,10 @@ __global__ __launch_bounds__(256) void pf_combine_kernel(PfCombineArgs a) {
 template <int BITS>
 __global__ __launch_bounds__(256) void debug_prefill_path_kernel(DebugPathArgs a) {
   const int chunk = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if constexpr (BITS == MOE_KIND_CB) {
+    load_grid<BITS>(a.grid16, threadIdx.x, blockDim.x);
+    __syncthreads();
+  }
   if (chunk >= a.n_rg * a.n_kg) return;
   const int rg = chunk / a.n_kg, kg = chunk - rg * a.n_kg;
   const int n = lane & 15, q = lane >> 4;
@@ -978,7 +1005,8 @@ hipError_t launch_debug_prefill_path(const DebugPathArgs& a, int bits, hipStream
   const int n = a.n_rg * a.n_kg;
   if (n == 0) return hipSuccess;
   if (bits == 2) hipLaunchKernelGGL(debug_prefill_path_kernel<2>, dim3((n + 3) / 4), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(debug_prefill_path_kernel<3>, dim3((n + 3) / 4), dim3(256), 0, s, a);
+  else if (bits == 3) hipLaunchKernelGGL(debug_prefill_path_kernel<3>, dim3((n + 3) / 4), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(debug_prefill_path_kernel<MOE_KIND_CB>, dim3((n + 3) / 4), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -989,9 +1017,11 @@ hipError_t launch_pack_router(const float* W, int E, int d, _Float16* wh, _Float
 }
 
 hipError_t launch_pack_hbound(const uint8_t* canon, int64_t canon_stride, int n_experts, int I, int d, int bits,
-                              int32_t* hb, int32_t* ed, hipStream_t s) {
+                              const uint8_t* grid, int32_t* hb, int32_t* ed, hipStream_t s) {
   if (n_experts <= 0) return hipSuccess;
-  hipLaunchKernelGGL(pack_hbound_kernel, dim3(n_experts), dim3(256), 0, s, canon, canon_stride, I, d, bits, hb, ed);
+  if (bits == MOE_KIND_CB && !grid) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pack_hbound_kernel, dim3(n_experts), dim3(256), 0, s, canon, canon_stride, I, d, bits, grid, hb,
+                     ed);
   return hipGetLastError();
 }
 
@@ -1024,28 +1054,29 @@ hipError_t launch_pf_group(const PfGroupArgs& a, hipStream_t s) {
 hipError_t launch_pf_gate_up(const PfGemmArgs& a, int bits, int max_items, hipStream_t s) {
   const dim3 grid((unsigned)((max_items + N_XCD - 1) / N_XCD * N_XCD * a.n_nt));
   if (bits == 2) MOE_LAUNCH(pf_gate_up_kernel<2>, grid, dim3(256), 0, s, a);
-  else MOE_LAUNCH(pf_gate_up_kernel<3>, grid, dim3(256), 0, s, a);
+  else if (bits == 3) MOE_LAUNCH(pf_gate_up_kernel<3>, grid, dim3(256), 0, s, a);
+  else MOE_LAUNCH(pf_gate_up_kernel<MOE_KIND_CB>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_pf_down(const PfGemmArgs& a, int bits, int bk, int max_items, hipStream_t s) {
   const dim3 grid((unsigned)((max_items + N_XCD - 1) / N_XCD * N_XCD * (a.d / PF_DT)));
 #define PF_DOWN(B, K) MOE_LAUNCH((pf_down_kernel<B, K>), grid, dim3(256), 0, s, a)
-  if (bits == 2) {
-    switch (bk) {
-      case 8: PF_DOWN(2, 8); break;
-      case 4: PF_DOWN(2, 4); break;
-      case 2: PF_DOWN(2, 2); break;
-      default: PF_DOWN(2, 1); break;
-    }
-  } else {
-    switch (bk) {
-      case 8: PF_DOWN(3, 8); break;
-      case 4: PF_DOWN(3, 4); break;
-      case 2: PF_DOWN(3, 2); break;
-      default: PF_DOWN(3, 1); break;
-    }
+#define PF_DOWN_BK(B)         \
+  switch (bk) {               \
+    case 8: PF_DOWN(B, 8); break; \
+    case 4: PF_DOWN(B, 4); break; \
+    case 2: PF_DOWN(B, 2); break; \
+    default: PF_DOWN(B, 1); break; \
   }
+  if (bits == 2) {
+    PF_DOWN_BK(2)
+  } else if (bits == 3) {
+    PF_DOWN_BK(3)
+  } else {
+    PF_DOWN_BK(MOE_KIND_CB)
+  }
+#undef PF_DOWN_BK
 #undef PF_DOWN
   return hipGetLastError();
 }

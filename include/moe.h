@@ -143,10 +143,10 @@ int moe_pack_experts(const moe_layer_desc *desc, const void *experts_canon, cons
  * arguments plus `grid`, device uint8 [512][4] (16-byte aligned), the table
  * of magnitudes the blocks index [strata-mlx wiki, credits list: the
  * codebook tables come with the model files].  The grid is copied into the
- * packed buffer (as exact fp16 values); a magnitude above 127 gives
- * MOE_ERR_DATA.  Codebook layers run the decode path only: a forward call
- * with more tokens than the decode kernels take (8 per layer call, 16 with
- * fp16 activations or in a stack) returns MOE_ERR_UNSUPPORTED. */
+ * packed buffer (as exact fp16 values); a magnitude above 127, or a block
+ * scale of magnitude 256 or more (so that scale * code stays below 2^15 in
+ * fp16, as for b-bit codes), gives MOE_ERR_DATA.  Every forward entry point
+ * takes codebook layers (decode and chunked prefill). */
 int moe_pack_experts_cb(const moe_layer_desc *desc, const void *experts_canon, const void *shared_canon,
                         const uint8_t *grid, const float *router_w, const float *router_bias, void *packed,
                         size_t packed_bytes, moe_layer **out, void *stream);

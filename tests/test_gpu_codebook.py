@@ -3,9 +3,11 @@
 oracle, with the synthetic grid of the input generator.
 
 Bars as for b-bit blocks: codes and dequantised weights bit-exact through the
-scalar export and through the decode kernels' own fragment decoder; routing
-bit-exact given the logits; layer outputs within the decode path's envelope
-(and the 2e-3 bar) with the oracle fed the GPU's routing.
+scalar export and through the expert kernels' own decoders (the decode
+fragment decoder, and the grouped GEMMs' fp16 dequantization, one rounding of
+scale times code); routing bit-exact given the logits; layer outputs within
+the decode path's envelope (and the 2e-3 bar) on the decode kernels, within
+2e-3 on the grouped GEMMs, with the oracle fed the GPU's routing.
 """
 import numpy as np
 import pytest
@@ -75,6 +77,12 @@ def test_cb_unpack_bitexact(bqe, shape):
             torch.cuda.synchronize()
             assert np.array_equal(codes.cpu().numpy(), oc), (e, mat, "decode-path codes")
             assert np.array_equal(w32.cpu().numpy().astype(np.float64), ow), (e, mat, "decode-path weights")
+            o16 = oracle.double_to_half_array(ow)
+            for path in (1, 2):  # the grouped GEMMs' dequantization from half and whole chunks
+                w16.fill_(-1)
+                bqe.moe_debug_unpack_path(L.handle, e, mat, path, None, None, w16)
+                torch.cuda.synchronize()
+                assert np.array_equal(w16.cpu().numpy().view(np.uint16), o16), (e, mat, path)
 
 
 def test_cb_pack_checks(bqe):
@@ -96,6 +104,11 @@ def test_cb_pack_checks(bqe):
     with pytest.raises(bqe.MoeError) as ei:  # the 3-bit class only
         bqe.moe_packed_bytes(bqe.make_desc(wl.d, wl.E, wl.I, 0, wl.k, 2, codebook=True))
     assert ei.value.code == bqe.MOE_ERR_UNSUPPORTED
+    big = canon.clone()
+    big[15 * 7: 15 * 7 + 2] = torch.tensor([0x00, 0x5C], dtype=torch.uint8)  # block 7's scale = 256.0
+    with pytest.raises(bqe.MoeError) as ei:  # scale * code must stay below 2^15 in fp16
+        bqe.moe_pack_experts_cb(desc, big, None, grid, Wd, None, buf)
+    assert ei.value.code == bqe.MOE_ERR_DATA
     h = bqe.moe_pack_experts_cb(desc, canon, None, grid, Wd, None, buf)
     got = bqe.moe_layer_get_desc(h)
     assert (got.bits, got.codebook, got.block) == (3, 1, 32)
@@ -170,17 +183,47 @@ def test_cb_stack_teacher_forced(bqe, T):
         assert err <= TOL_DECODE_PATH and rerr <= TOL_DECODE_PATH, (l, err, rerr)
 
 
-def test_cb_more_tokens_rejected(bqe):
-    """Codebook layers run the decode kernels only: 9 tokens in one layer call
-    (17 in a stack) is refused before anything is launched."""
-    wl = _cb("tiny")
+@pytest.mark.parametrize("shape,T", [("tiny", 9), ("tiny", 37), ("tiny", 200), ("full", 300)])
+def test_cb_prefill_layer(bqe, shape, T):
+    """Chunks of more than 8 tokens through the grouped GEMMs (codebook
+    weights dequantized in registers from the LDS grid), teacher-forced."""
+    wl = _cb("tiny", Is=64, zipf_s=1.1) if shape == "tiny" else _cb("layer_t1")
     L = packed_layer(wl, 0)
-    x = activations_device(mi.activations(wl, T=17))
-    y = torch.empty((17, wl.d), dtype=torch.float32, device=DEV)
-    ws = bqe.new_workspace(L.workspace_bytes(17))
-    with pytest.raises(bqe.MoeError) as ei:
-        bqe.moe_layer_forward(L.handle, x[:9], y[:9], ws)
-    assert ei.value.code == bqe.MOE_ERR_UNSUPPORTED
-    with pytest.raises(bqe.MoeError) as ei:
-        bqe.moe_stack_forward([L.handle], x, y, ws, 1e-6)
-    assert ei.value.code == bqe.MOE_ERR_UNSUPPORTED
+    x_np = mi.activations(wl, T=T, stream=24)
+    say(f"[cb prefill] {shape} T={T}")
+    y, logits, idx, w = _forward(bqe, L, x_np)
+    oi, ow = oracle.topk(logits, wl.k)
+    assert np.array_equal(idx, oi) and np.array_equal(w.view(np.uint32), ow.view(np.uint32))
+    rows = np.arange(T) if shape == "tiny" else np.unique(np.linspace(0, T - 1, 24).astype(int))
+    OL = oracle_layer(wl, 0, idx[rows].reshape(-1))
+    oy, _, _, _ = oracle.layer_forward(OL, x_np[rows], force_idx=idx[rows], force_w=w[rows])
+    err = rel_err_inf(y[rows], oy)
+    say(f"    rel err {err:.3e} on {len(rows)} rows")
+    assert err <= TOL_LAYER
+
+
+def test_cb_prefill_stack(bqe):
+    """Three stacked tiny codebook layers over 50 tokens (the chunked-prefill
+    stack), each against the oracle under the stack's routing."""
+    wl = _cb("tiny", Is=64, zipf_s=1.1, layers=3)
+    layers = [packed_layer(wl, l) for l in range(wl.layers)]
+    T, nL, d, k = 50, wl.layers, wl.d, wl.k
+    x_np = mi.activations(wl, T=T, stream=25)
+    y = torch.empty((T, d), dtype=torch.float32, device=DEV)
+    yl = torch.empty((nL, T, d), dtype=torch.float32, device=DEV)
+    il = torch.empty((nL, T, k), dtype=torch.int32, device=DEV)
+    wr = torch.empty((nL, T, k), dtype=torch.float32, device=DEV)
+    ws = bqe.new_workspace(max(L.workspace_bytes(T) for L in layers))
+    say(f"[cb prefill stack] layers={nL} T={T}")
+    bqe.moe_stack_forward([L.handle for L in layers], activations_device(x_np), y, ws, 1e-6, yl, il, wr)
+    torch.cuda.synchronize()
+    yl, il, wr = yl.cpu().numpy(), il.cpu().numpy(), wr.cpu().numpy()
+    h = x_np
+    for l in range(nL):
+        if l > 0:
+            h = oracle.rmsnorm(yl[l - 1], 1e-6)
+        OL = oracle_layer(wl, l, il[l].reshape(-1))
+        oy, _, _, _ = oracle.layer_forward(OL, h, force_idx=il[l], force_w=wr[l])
+        err = rel_err_inf(yl[l], oy)
+        say(f"    layer {l}: rel err {err:.3e}")
+        assert err <= TOL_LAYER, (l, err)
