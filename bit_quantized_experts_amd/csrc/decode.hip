@@ -9,23 +9,23 @@ namespace {
 // gate/up: one workgroup of 8 wavefronts per CU (the grid is the CU count);
 // every workgroup selects the experts of every token itself and builds the
 // slot list, workgroup 0 publishes the routing and the slot list.
-template <int BITS, int NPER, bool A16>
+template <int BITS, int NPER, int AM>
 __global__ __launch_bounds__(64 * GU_NW) void gu_decode_kernel(GuArgs a) {
   __shared__ GuLds L;
   load_grid<BITS>(a.X.grid16, threadIdx.x, 64 * GU_NW);  // (the selection's barriers publish it)
-  gu_select<BITS, NPER, A16>(a, L, blockIdx.x == 0, blockIdx.x == 0);
-  gu_items<BITS, A16>(a, L, blockIdx.x, gridDim.x, nullptr);
+  gu_select<BITS, NPER, AM>(a, L, blockIdx.x == 0, blockIdx.x == 0);
+  gu_items<BITS, AM>(a, L, blockIdx.x, gridDim.x, nullptr);
 }
 
 // down: workgroup = (row group, split), the slot list from the workspace.
-template <int BITS, int RT, bool A16>
+template <int BITS, int RT, int AM>
 __global__ __launch_bounds__(512) void down_decode_kernel(DownArgs a) {
   __shared__ float red[8 * RT * 4 * 64];
   if constexpr (BITS == MOE_KIND_CB) {
     load_grid<BITS>(a.X.grid16, threadIdx.x, blockDim.x);
     __syncthreads();
   }
-  down_role<BITS, RT, A16>(a, blockIdx.x, blockIdx.y, *a.n_slots, a.slot_expert, red);
+  down_role<BITS, RT, AM>(a, blockIdx.x, blockIdx.y, *a.n_slots, a.slot_expert, red);
 }
 
 // ---------------------------------------------------------------------------
@@ -70,8 +70,9 @@ __global__ __launch_bounds__(256) void debug_decode_path_kernel(DebugPathArgs a)
 
 template <int BITS, int RT>
 hipError_t launch_down_t(const DownArgs& a, int grid_x, int nw, hipStream_t s) {
-  if (a.act16) MOE_LAUNCH((down_decode_kernel<BITS, RT, true>), dim3(grid_x, a.S), dim3(64 * nw), 0, s, a);
-  else MOE_LAUNCH((down_decode_kernel<BITS, RT, false>), dim3(grid_x, a.S), dim3(64 * nw), 0, s, a);
+  if (a.am == MOE_AM_HL16) MOE_LAUNCH((down_decode_kernel<BITS, RT, MOE_AM_HL16>), dim3(grid_x, a.S), dim3(64 * nw), 0, s, a);
+  else if (a.am == MOE_AM_F16) MOE_LAUNCH((down_decode_kernel<BITS, RT, MOE_AM_F16>), dim3(grid_x, a.S), dim3(64 * nw), 0, s, a);
+  else MOE_LAUNCH((down_decode_kernel<BITS, RT, MOE_AM_HL8>), dim3(grid_x, a.S), dim3(64 * nw), 0, s, a);
   return hipGetLastError();
 }
 
@@ -80,8 +81,9 @@ hipError_t launch_down_t(const DownArgs& a, int grid_x, int nw, hipStream_t s) {
 hipError_t launch_gu_decode(const GuArgs& a, int n_wg, hipStream_t s) {
 #define GU_LAUNCH(B, N)                                                                     \
   do {                                                                                      \
-    if (a.act16) MOE_LAUNCH((gu_decode_kernel<B, N, true>), dim3(n_wg), dim3(64 * GU_NW), 0, s, a);  \
-    else MOE_LAUNCH((gu_decode_kernel<B, N, false>), dim3(n_wg), dim3(64 * GU_NW), 0, s, a);         \
+    if (a.am == MOE_AM_HL16) MOE_LAUNCH((gu_decode_kernel<B, N, MOE_AM_HL16>), dim3(n_wg), dim3(64 * GU_NW), 0, s, a); \
+    else if (a.am == MOE_AM_F16) MOE_LAUNCH((gu_decode_kernel<B, N, MOE_AM_F16>), dim3(n_wg), dim3(64 * GU_NW), 0, s, a); \
+    else MOE_LAUNCH((gu_decode_kernel<B, N, MOE_AM_HL8>), dim3(n_wg), dim3(64 * GU_NW), 0, s, a);                      \
   } while (0)
   const int np = a.E <= 512 ? 8 : a.E <= 1024 ? 16 : a.E <= 2048 ? 32 : 64;
   if (a.bits == 2) {

@@ -1,6 +1,6 @@
-// decode_dev.h -- device code of the decode path (T <= 8 tokens per pass,
-// 16 with fp16 activations), shared by the per-phase kernels (decode.hip)
-// and the persistent stack kernel (persist.hip).
+// decode_dev.h -- device code of the decode path (up to 16 tokens per
+// pass), shared by the per-phase kernels (decode.hip) and the persistent
+// stack kernel (persist.hip).
 //
 // Experts are multiplied straight from their low-bit blocks [strata-mlx wiki,
 // opening feature list, first item]; one pass checks up to eight tokens (one
@@ -18,6 +18,11 @@
 // 16 rows; the lane holding column n then applies the fp16 block scale of row
 // n with one fused multiply-add per output.  Every product and the offset are
 // exact; the rounding is the fp32 accumulation.
+// With 9..16 tokens (MOE_AM_HL16) the rows are the 16 tokens: a first MFMA
+// with their fp16 hi parts and a second one, chained on the same
+// accumulators, with their lo parts, so every weight fragment serves 16
+// tokens at full precision; the seed then holds the sums of hi and lo.  With
+// fp16 activations (MOE_AM_F16) only the first of the two runs.
 //
 // Memory: weight chunks stream from HBM into registers, several k-groups
 // ahead of the multiplies; the gate/up activation fragments are read from
@@ -156,7 +161,9 @@ DEVI void place_lane(SlotLds& S, int e, float w, int t, int k, int E, int base, 
 // epilogue divides by the token's rms (stacked layers), forms h = silu(g) * u
 // times the token's gate weight and writes it as fp16 hi/lo A-fragments of
 // the down projection, with the sums of each 16-row tile.
-// Inputs wider than GU_WIN blocks are staged in windows, one after another.
+// Inputs wider than GU_WIN blocks (GU_WIN / 2 with the two tiles of 16 hi +
+// lo token rows, so d = 2560 takes two) are staged in windows, one after
+// another.
 // ---------------------------------------------------------------------------
 constexpr int GU_NW = 8;    // wavefronts per workgroup
 constexpr int GU_WIN = 96;  // activation blocks staged in LDS at once
@@ -178,42 +185,52 @@ struct GroupRegs {
   ChunkRegs<BITS> g, u;
 };
 
+// C rows are the 16 tokens themselves (no hi/lo row pairs to add).
+constexpr bool am_tok16(int am) { return am != MOE_AM_HL8; }
+// Activation windows of the gate/up kernel: a block takes NT KB of LDS.
+constexpr int gu_win_blocks(int am) { return GU_WIN / moe_am_tiles(am); }
+template <int AM>
+DEVI int gu_windows(int n_kg) {
+  return (8 * n_kg + gu_win_blocks(AM) - 1) / gu_win_blocks(AM);
+}
+
 // Activation blocks [b0, b0 + nblk) of the layer input into LDS: the
-// A-fragments (1 KB per block) and accumulator seeds (16 floats per block)
-// the router wrote (XFrag), copied as 16-byte pieces (thread p takes pieces
-// p, p + 512, ...).  Every load is issued unconditionally (pieces past the
+// A-fragments (1 KB per tile, NT tiles per block) and accumulator seeds (16
+// floats per block) the router wrote (XFrag), copied as 16-byte pieces
+// (thread p takes pieces p, p + 512, ...).  Every load is issued unconditionally (pieces past the
 // window re-read a valid address and are not stored), so a thread's loads
 // stay in flight together.
-template <bool A16>
 struct WindowRegs {
   static constexpr int PER = GU_WIN * 64 / (64 * GU_NW);  // fragment pieces per thread
   u32x4_t v[PER];
   float4_t c;  // a piece of the seeds (threads below 4 nblk)
 };
 
-template <bool A16>
-DEVI void window_load(WindowRegs<A16>& W, const GuArgs& a, int b0, int nblk, int tid) {
-  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.x.frag) + (size_t)b0 * 64;
+template <int AM>
+DEVI void window_load(WindowRegs& W, const GuArgs& a, int b0, int nblk, int tid) {
+  constexpr int NT = moe_am_tiles(AM);
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.x.frag) + (size_t)b0 * NT * 64;
 #pragma unroll
-  for (int i = 0; i < WindowRegs<A16>::PER; ++i) W.v[i] = src[min(tid + 64 * GU_NW * i, 64 * nblk - 1)];
+  for (int i = 0; i < WindowRegs::PER; ++i) W.v[i] = src[min(tid + 64 * GU_NW * i, 64 * NT * nblk - 1)];
   W.c = reinterpret_cast<const float4_t*>(a.x.cs + (size_t)b0 * 16)[min(tid, 4 * nblk - 1)];
 }
 
-template <bool A16>
-DEVI void window_store(const WindowRegs<A16>& W, GuLds& L, int nblk, int tid) {
+template <int AM>
+DEVI void window_store(const WindowRegs& W, GuLds& L, int nblk, int tid) {
+  constexpr int NT = moe_am_tiles(AM);
 #pragma unroll
-  for (int i = 0; i < WindowRegs<A16>::PER; ++i) {
+  for (int i = 0; i < WindowRegs::PER; ++i) {
     const int p = tid + 64 * GU_NW * i;
-    if (p < 64 * nblk) *reinterpret_cast<u32x4_t*>(L.xs + (size_t)p * 16) = W.v[i];
+    if (p < 64 * NT * nblk) *reinterpret_cast<u32x4_t*>(L.xs + (size_t)p * 16) = W.v[i];
   }
   if (tid < 4 * nblk) *reinterpret_cast<float4_t*>(L.cs + 4 * tid) = W.c;
 }
 
-template <bool A16>
+template <int AM>
 DEVI void stage_window(GuLds& L, const GuArgs& a, int b0, int nblk, int tid) {
-  WindowRegs<A16> W;
-  window_load<A16>(W, a, b0, nblk, tid);
-  window_store<A16>(W, L, nblk, tid);
+  WindowRegs W;
+  window_load<AM>(W, a, b0, nblk, tid);
+  window_store<AM>(W, L, nblk, tid);
 }
 
 template <int BITS>
@@ -226,21 +243,31 @@ DEVI void issue_group(GroupRegs<BITS>& r, const uint8_t* gate, const uint8_t* up
 // window.  A k-group spans two column slices of the router (4 blocks each):
 // each slice's sum is scaled back by 2^e of its (slice, token) (exact) before
 // it joins the accumulators; this lane's C rows are tokens tok4 .. tok4 + 3.
-template <int BITS, bool A16>
+// (MOE_AM_HL16: the block's lo tile follows its hi tile in LDS, and its
+// MFMAs continue the hi tile's accumulators.)
+template <int BITS, int AM>
 DEVI void mul_group(const GroupRegs<BITS>& r, const GuLds& L, int lb, int kg, int lane, float4_t& accg,
                     float4_t& accu) {
   static_assert(MOE_ROUTE_COLS == 128, "two column slices per k-group");
-  const int tok4 = A16 ? 4 * (lane >> 4) : 4 * ((lane >> 4) & 1);
+  constexpr int NT = moe_am_tiles(AM);
+  const int tok4 = am_tok16(AM) ? 4 * (lane >> 4) : 4 * ((lane >> 4) & 1);
 #pragma unroll
   for (int hs = 0; hs < 2; ++hs) {
     float4_t pg = float4_t{0.f, 0.f, 0.f, 0.f}, pu = pg;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int j = 4 * hs + jj;
-      const half8_t A = *reinterpret_cast<const half8_t*>(L.xs + (size_t)(lb + j) * 1024 + 16 * lane);
+      const unsigned char* ap = L.xs + (size_t)(lb + j) * NT * 1024 + 16 * lane;
+      const half8_t A = *reinterpret_cast<const half8_t*>(ap);
       const float4_t cin = *reinterpret_cast<const float4_t*>(L.cs + (lb + j) * 16 + 4 * (lane >> 4));
-      const float4_t Cg = mfma16x16x32(A, chunk_frag<BITS>(r.g, j), cin);
-      const float4_t Cu = mfma16x16x32(A, chunk_frag<BITS>(r.u, j), cin);
+      const half8_t Bg = chunk_frag<BITS>(r.g, j), Bu = chunk_frag<BITS>(r.u, j);
+      float4_t Cg = mfma16x16x32(A, Bg, cin);
+      float4_t Cu = mfma16x16x32(A, Bu, cin);
+      if constexpr (AM == MOE_AM_HL16) {
+        const half8_t Al = *reinterpret_cast<const half8_t*>(ap + 1024);
+        Cg = mfma16x16x32(Al, Bg, Cg);
+        Cu = mfma16x16x32(Al, Bu, Cu);
+      }
       pg += chunk_scale(r.g.scales, j) * Cg;
       pu += chunk_scale(r.u.scales, j) * Cu;
     }
@@ -263,7 +290,7 @@ DEVI void mul_group(const GroupRegs<BITS>& r, const GuLds& L, int lb, int kg, in
 // main loop has no early exit, so the loads in flight at every multiply are
 // the same and the compiler's wait counts stay exact; a tail of up to two
 // steps multiplies what is already in flight.
-template <int BITS, bool A16>
+template <int BITS, int AM>
 DEVI void run_tile(const uint8_t* gate, const uint8_t* up, int64_t rowoff, int kg0, int kg1, int step, int wkg0,
                    const GuLds& L, int lane, float4_t& accg, float4_t& accu) {
   constexpr int64_t CB = moe_chunk_bytes(BITS);
@@ -278,20 +305,20 @@ DEVI void run_tile(const uint8_t* gate, const uint8_t* up, int64_t rowoff, int k
   for (int it = nsteps / 3; it > 0; --it) {
     issue_group<BITS>(r2, gate, up, rowoff + min(kg + 2 * step, last) * CB, lane);
     __builtin_amdgcn_sched_barrier(0);
-    mul_group<BITS, A16>(r0, L, 8 * (kg - wkg0), kg, lane, accg, accu);
+    mul_group<BITS, AM>(r0, L, 8 * (kg - wkg0), kg, lane, accg, accu);
     kg += step;
     issue_group<BITS>(r0, gate, up, rowoff + min(kg + 2 * step, last) * CB, lane);
     __builtin_amdgcn_sched_barrier(0);
-    mul_group<BITS, A16>(r1, L, 8 * (kg - wkg0), kg, lane, accg, accu);
+    mul_group<BITS, AM>(r1, L, 8 * (kg - wkg0), kg, lane, accg, accu);
     kg += step;
     issue_group<BITS>(r1, gate, up, rowoff + min(kg + 2 * step, last) * CB, lane);
     __builtin_amdgcn_sched_barrier(0);
-    mul_group<BITS, A16>(r2, L, 8 * (kg - wkg0), kg, lane, accg, accu);
+    mul_group<BITS, AM>(r2, L, 8 * (kg - wkg0), kg, lane, accg, accu);
     kg += step;
   }
   const int rem = nsteps % 3;
-  if (rem >= 1) mul_group<BITS, A16>(r0, L, 8 * (kg - wkg0), kg, lane, accg, accu);
-  if (rem == 2) mul_group<BITS, A16>(r1, L, 8 * (kg + step - wkg0), kg + step, lane, accg, accu);
+  if (rem >= 1) mul_group<BITS, AM>(r0, L, 8 * (kg - wkg0), kg, lane, accg, accu);
+  if (rem == 2) mul_group<BITS, AM>(r1, L, 8 * (kg + step - wkg0), kg + step, lane, accg, accu);
 }
 
 // Selection and slot list of a gate/up workgroup (every workgroup runs it):
@@ -299,7 +326,7 @@ DEVI void run_tile(const uint8_t* gate, const uint8_t* up, int64_t rowoff, int k
 // activation window staged.  publish_routing: write the routing used to the
 // caller's outputs; publish_slots: write the slot list to the workspace (for
 // a separate down kernel).
-template <int BITS, int NPER, bool A16>  // NPER >= ceil(E / 64)
+template <int BITS, int NPER, int AM>  // NPER >= ceil(E / 64)
 DEVI void gu_select(const GuArgs& a, GuLds& L, bool publish_routing, bool publish_slots) {
   const int tid = opaque_tid(), lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: loop bounds stay scalar
@@ -307,7 +334,7 @@ DEVI void gu_select(const GuArgs& a, GuLds& L, bool publish_routing, bool publis
   const bool has_shared = a.has_shared != 0;
   const int base = has_shared ? 1 : 0;
   const int n_kg = a.n_kg;
-  const int n_win = (8 * n_kg + GU_WIN - 1) / GU_WIN;
+  const int n_win = gu_windows<AM>(n_kg);
 
   // Selection: wavefront w takes the rows of tokens w and w + 8 (below T) of
   // the logits.  The loads of its first row (both rows, for rows of up to
@@ -333,12 +360,12 @@ DEVI void gu_select(const GuArgs& a, GuLds& L, bool publish_routing, bool publis
     const int i = min(tid + 512 * h, n_sx - 1);
     sxv[h] = a.x.sx[(size_t)(i >> 4) * MOE_XSX_STRIDE + (i & 15)];
   }
-  // the activation window (one window for inputs of up to GU_WIN blocks)
-  // stays in registers through the selection and is stored to LDS before the
-  // barrier that ends it: the selection starts as soon as its logits are in,
-  // while the larger window is still arriving
-  WindowRegs<A16> win;
-  if (n_win == 1) window_load<A16>(win, a, 0, 8 * n_kg, tid);
+  // the activation window (one window for inputs of up to
+  // gu_win_blocks(AM) blocks) stays in registers through the selection and
+  // is stored to LDS before the barrier that ends it: the selection starts as
+  // soon as its logits are in, while the larger window is still arriving
+  WindowRegs win;
+  if (n_win == 1) window_load<AM>(win, a, 0, 8 * n_kg, tid);
   clear_slots(L.S, E, T, base + min(tk, E), has_shared);
   lds_barrier();  // byte map and weight rows cleared before any wavefront marks (the loads stay in flight)
   static_assert(2 * GU_NW >= MOE_MAX_TOK_F16ACT, "two tokens per wavefront");
@@ -365,7 +392,7 @@ DEVI void gu_select(const GuArgs& a, GuLds& L, bool publish_routing, bool publis
     }
   }
   __builtin_amdgcn_sched_barrier(0);  // (the window's stores stay after the selection)
-  if (n_win == 1) window_store<A16>(win, L, 8 * n_kg, tid);
+  if (n_win == 1) window_store<AM>(win, L, 8 * n_kg, tid);
   if (tid >= 64 && tid < 80) L.rn[tid - 64] = 1.0f / rnv;
 #pragma unroll
   for (int h = 0; h < 2; ++h)
@@ -395,7 +422,7 @@ DEVI void gu_select(const GuArgs& a, GuLds& L, bool publish_routing, bool publis
 // (slot u, tile t of 16 intermediate rows).  With h_ready, each finished
 // item adds one to its slot's counter (h_ready + u * MOE_CTR_STRIDE) once its
 // h values are stored (a consumer inside the same kernel waits on them).
-template <int BITS, bool A16>
+template <int BITS, int AM>
 DEVI void gu_items(const GuArgs& a, GuLds& L, int wg, int n_wg, uint32_t* h_ready) {
   constexpr int64_t CB = moe_chunk_bytes(BITS);
   const int tid = opaque_tid(), lane = tid & 63;
@@ -405,7 +432,7 @@ DEVI void gu_items(const GuArgs& a, GuLds& L, int wg, int n_wg, uint32_t* h_read
   const int base = has_shared ? 1 : 0;
   const int tiles_r = a.I / 16, tiles_s = has_shared ? a.Is / 16 : 0;
   const int n_kg = a.n_kg;
-  const int n_win = (8 * n_kg + GU_WIN - 1) / GU_WIN;
+  const int n_win = gu_windows<AM>(n_kg);
   const int win_kg = (n_kg + n_win - 1) / n_win;  // k-groups per window
   const int n_items = tiles_s + L.S.n_routed * tiles_r;
   int KP = 8;
@@ -443,10 +470,10 @@ DEVI void gu_items(const GuArgs& a, GuLds& L, int wg, int n_wg, uint32_t* h_read
       const int kg0 = w * win_kg, kg1 = min(n_kg, kg0 + win_kg);
       if (n_win > 1) {
         __syncthreads();
-        stage_window<A16>(L, a, 8 * kg0, 8 * (kg1 - kg0), tid);
+        stage_window<AM>(L, a, 8 * kg0, 8 * (kg1 - kg0), tid);
         __syncthreads();
       }
-      if (valid) run_tile<BITS, A16>(gate, up, (int64_t)t * n_kg * CB, kg0 + kp, kg1, KP, kg0, L, lane, accg, accu);
+      if (valid) run_tile<BITS, AM>(gate, up, (int64_t)t * n_kg * CB, kg0 + kp, kg1, KP, kg0, L, lane, accg, accu);
     }
     if (KP > 1) {
 #pragma unroll
@@ -458,14 +485,15 @@ DEVI void gu_items(const GuArgs& a, GuLds& L, int wg, int n_wg, uint32_t* h_read
     }
     if (valid) {
       // lane l: intermediate row n = l & 15 of the tile, C rows 4(l>>4)+i:
-      // tokens tok_e + i, hi part in lanes < 32, lo part in lanes >= 32 (fp16
-      // activations: token 4(l>>4)+i, no lo part).  h is kept in fp32 as
+      // tokens tok_e + i, hi part in lanes < 32, lo part in lanes >= 32 (16
+      // token rows: token 4(l>>4)+i, hi and lo already summed).  h is kept in fp32 as
       // [slot][16-row tile][token][16] (an item writes whole 128-byte lines,
       // none shared with another item, zeros for tokens without this slot);
       // the down kernel scales it before rounding to fp16.
       const int n = lane & 15;
-      const bool writer = A16 || lane < 32;
-      constexpr int R = A16 ? MOE_MAX_TOK_F16ACT : MOE_MAX_TOK_DECODE;
+      constexpr bool T16 = am_tok16(AM);
+      const bool writer = T16 || lane < 32;
+      constexpr int R = moe_am_tokens(AM);
       float* hrow = a.hbuf + ((size_t)u * (a.hI / 16) + t) * R * 16 + n;
       // The item's KP waves share the epilogue: wave kp finishes the
       // accumulator rows i with i % KP == kp, summing the k-parts in wave
@@ -483,12 +511,12 @@ DEVI void gu_items(const GuArgs& a, GuLds& L, int wg, int n_wg, uint32_t* h_read
             su += L.red[w0 + p][4 + i][lane];
           }
         }
-        const int tok = A16 ? 4 * (lane >> 4) + i : tok_e + i;
+        const int tok = T16 ? 4 * (lane >> 4) + i : tok_e + i;
         const float gw = (u == 0 && has_shared) ? (tok < T ? 1.0f : 0.f) : L.S.w[u][tok];
         // the norm's 1 / rms (the fragments' scaling was undone per slice)
         const float rrn = L.rn[tok];
-        const float g = (A16 ? sg : add_partner32(sg)) * rrn;
-        const float uu = (A16 ? su : add_partner32(su)) * rrn;
+        const float g = (T16 ? sg : add_partner32(sg)) * rrn;
+        const float uu = (T16 ? su : add_partner32(su)) * rrn;
         const float hv = g * __builtin_amdgcn_rcpf(1.0f + expf(-g)) * uu;
         const float hs = (gw != 0.f) ? gw * hv : 0.f;
         if (writer) st_dev(hrow + tok * 16, hs);
@@ -513,32 +541,33 @@ DEVI void gu_items(const GuArgs& a, GuLds& L, int wg, int n_wg, uint32_t* h_read
 // ---------------------------------------------------------------------------
 // A-fragment of one block of slot u's intermediate h (fp32 rows
 // [slot][token][row]): lane L = m + 16q holds inputs 8q..8q+7 of row m, i.e.
-// token m & 7, its fp16 hi part for m < 8 and lo part for m >= 8 (fp16
-// activations: token m, rounded to fp16), after scaling by the power of two
-// 2^-eh that puts the token's largest |h| over the down item's inputs in
-// [2^14, 2^15).
-template <bool A16>
-DEVI half8_t h_fragment(const float4_t (&v)[2], int eh, int lane) {
-  const bool lo = !A16 && (lane & 8);
-  half8_t h;
+// token m & 7, its fp16 hi part for m < 8 and lo part for m >= 8 (16 token
+// rows: token m, its fp16 hi part in h and, for MOE_AM_HL16, its lo part in
+// hl), after scaling by the power of two 2^-eh that puts the token's largest
+// |h| over the down item's inputs in [2^14, 2^15).
+template <int AM>
+DEVI void h_fragment(const float4_t (&v)[2], int eh, int lane, half8_t& h, half8_t& hl) {
+  const bool lo = AM == MOE_AM_HL8 && (lane & 8);
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     const float x = ldexpf(v[c >> 2][c & 3], -eh);  // exact (2^-eh itself may exceed the fp32 range)
     const _Float16 hi = (_Float16)x;
-    h[c] = lo ? (_Float16)(x - (float)hi) : hi;
+    const _Float16 rest = (_Float16)(x - (float)hi);
+    h[c] = lo ? rest : hi;
+    hl[c] = rest;
   }
-  return h;
 }
 
 // One down role (row group rg, split sp): ns slots, their expert ids in
 // `slots` (the workspace or the workgroup's own LDS slot list); `red` is
 // 8 x RT*4 x 64 floats of LDS.  Ends with a barrier (red is free again).
-template <int BITS, int RT, bool A16>
+template <int BITS, int RT, int AM>
 DEVI void down_role(const DownArgs& a, int rg, int sp, int ns, const int* slots, float* red) {
   constexpr int CB = moe_chunk_bytes(BITS);
   constexpr int BK = 8 / RT;
   constexpr int BATCH = 2;
-  constexpr int R = A16 ? MOE_MAX_TOK_F16ACT : MOE_MAX_TOK_DECODE;
+  constexpr int R = moe_am_tokens(AM);
+  constexpr bool T16 = am_tok16(AM);
   const int tid = opaque_tid();
   const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6), nw = blockDim.x >> 6;
   const int S = a.S;
@@ -570,8 +599,8 @@ DEVI void down_role(const DownArgs& a, int rg, int sp, int ns, const int* slots,
 
   // this lane's A-fragment token, and the token of its accumulator rows
   // 4 (lane >> 4) + i (hi/lo: the lo rows 8..15 are tokens 0..7 again)
-  const int tok_a = A16 ? (lane & 15) : (lane & 7);
-  const int tok_c = A16 ? 4 * (lane >> 4) : (4 * (lane >> 4)) & 7;
+  const int tok_a = T16 ? (lane & 15) : (lane & 7);
+  const int tok_c = T16 ? 4 * (lane >> 4) : (4 * (lane >> 4)) & 7;
   const float off = -(float)moe_code_offset(BITS);
   const half8_t ones = half8_t{1, 1, 1, 1, 1, 1, 1, 1};
 
@@ -617,13 +646,13 @@ DEVI void down_role(const DownArgs& a, int rg, int sp, int ns, const int* slots,
       if (!ok[q]) continue;
       // the item's scale for each token: the largest |h| of the token over
       // the item's inputs (this lane's values, then the other lanes holding
-      // the same token: 8 apart, or 16 apart with fp16 activations)
+      // the same token: 8 apart, or 16 apart with 16 token rows)
       float m = 0.f;
 #pragma unroll
       for (int j = 0; j < BK; ++j)
 #pragma unroll
         for (int c = 0; c < 8; ++c) m = fmaxf(m, fabsf(hv[q][j][c >> 2][c & 3]));
-      if (!A16) m = fmaxf(m, __shfl_xor(m, 8, 64));
+      if (!T16) m = fmaxf(m, __shfl_xor(m, 8, 64));
       m = fmaxf(m, __shfl_xor(m, 16, 64));
       m = fmaxf(m, __shfl_xor(m, 32, 64));
       const int eh_a = fp16_exponent_for(m);
@@ -632,20 +661,27 @@ DEVI void down_role(const DownArgs& a, int rg, int sp, int ns, const int* slots,
       for (int t = 0; t < RT; ++t) part[t] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < BK; ++j) {
-        const half8_t A = h_fragment<A16>(hv[q][j], eh_a, lane);
+        half8_t A, Al;
+        h_fragment<AM>(hv[q][j], eh_a, lane, A, Al);
         // the accumulator seed -2^(b-1) sum_k A[m][k], with the row sums laid
         // out as the accumulators by a product with an all-ones B operand
         float4_t cin = float4_t{0.f, 0.f, 0.f, 0.f};
-        if constexpr (moe_code_offset(BITS) != 0) cin = off * mfma16x16x32(A, ones, cin);
+        if constexpr (moe_code_offset(BITS) != 0) {
+          cin = mfma16x16x32(A, ones, cin);
+          if constexpr (AM == MOE_AM_HL16) cin = mfma16x16x32(Al, ones, cin);
+          cin = off * cin;
+        }
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
           const int f = t * BK + j;
-          const float4_t C = mfma16x16x32(A, chunk_frag<BITS>(c[q], f), cin);
+          const half8_t B = chunk_frag<BITS>(c[q], f);
+          float4_t C = mfma16x16x32(A, B, cin);
+          if constexpr (AM == MOE_AM_HL16) C = mfma16x16x32(Al, B, C);
           part[t] += chunk_scale(c[q].scales, f) * C;
         }
       }
       // undo the item's scaling of the accumulator rows' tokens: 2^eh, exact
-      // (lane t < 8, or < 16 with fp16 activations, holds token t's exponent)
+      // (lane t < 8, or < 16 with 16 token rows, holds token t's exponent)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int eh = __shfl(eh_a, tok_c + i, 64);
@@ -673,10 +709,10 @@ DEVI void down_role(const DownArgs& a, int rg, int sp, int ns, const int* slots,
 #pragma unroll
       for (int w = 1; w < 8; ++w)
         if (w < nw) s += part[w];
-      if (!A16) s = add_partner32(s);  // (fp16 activations: C row = token, 16 tokens)
+      if (!T16) s = add_partner32(s);  // (16 token rows: C row = token)
       const int tok = 4 * (lane >> 4) + i;  // (hi/lo: lanes < 32 hold tokens 0..7)
       const int o = rg * 16 * RT + 16 * t + n;
-      if ((A16 || lane < 32) && tok < T) st_dev(a.ypart + ((size_t)sp * R + tok) * d + o, s);
+      if ((T16 || lane < 32) && tok < T) st_dev(a.ypart + ((size_t)sp * R + tok) * d + o, s);
     }
   }
   __builtin_amdgcn_s_waitcnt(0);  // this wave's partial sums are stored (a signal may follow the barrier)

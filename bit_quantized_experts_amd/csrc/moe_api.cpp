@@ -197,9 +197,9 @@ int down_splits(const moe_layer* L, int max_slots) {
   return S;
 }
 
-// Decode pass of T tokens; act16: fp16 activations (16 token rows per pass,
-// else 8).
-WsLayout ws_layout_decode(const moe_layer* L, int T, bool act16 = false) {
+// Decode pass of T tokens; am: the activation rows (MOE_AM_*: 8 tokens hi +
+// lo, 16 in fp16, 16 hi + lo).
+WsLayout ws_layout_decode(const moe_layer* L, int T, int am = MOE_AM_HL8) {
   WsLayout W{};
   const int k = L->k, E = L->E, d = L->d;
   W.max_slots = (T * k < E ? T * k : E) + (L->Is > 0 ? 1 : 0);
@@ -221,10 +221,10 @@ WsLayout ws_layout_decode(const moe_layer* L, int T, bool act16 = false) {
   W.n_slots = take(4);
   W.slot_expert = take((int64_t)W.max_slots * 4);
   W.slot_w = take((int64_t)W.max_slots * 16 * 4);
-  W.xfrag = take((int64_t)(d / 32) * 1024);
+  W.xfrag = take((int64_t)(d / 32) * moe_am_tiles(am) * 1024);
   W.xcs = take((int64_t)(d / 32) * 16 * 4);
   W.xsx = take((int64_t)W.n_cs * MOE_XSX_STRIDE * 4);
-  const int R = act16 ? MOE_MAX_TOK_F16ACT : MOE_MAX_TOK_DECODE;
+  const int R = moe_am_tokens(am);
   W.hbuf = take((int64_t)W.max_slots * R * W.nbI * 32 * 4);
   W.total = o;
   return W;
@@ -410,12 +410,12 @@ struct LayerInput {
   int norm;
 };
 
-// One decode layer (T <= 8): route (router logits) -> gate/up (with the top-k
-// selection in every workgroup) -> down.  The result
+// One decode layer (T <= moe_am_tokens(am)): route (router logits) -> gate/up
+// (with the top-k selection in every workgroup) -> down.  The result
 // is left as split partials in the workspace (ypart, W.S splits).
 int decode_layer(const moe_layer* L, const LayerInput& in, float eps, int T, float* y_prev_out,
-                 const moe_route_io* r, uint8_t* ws, hipStream_t s, int* S_out, bool act16 = false) {
-  const WsLayout W = ws_layout_decode(L, T, act16);
+                 const moe_route_io* r, uint8_t* ws, hipStream_t s, int* S_out, int am = MOE_AM_HL8) {
+  const WsLayout W = ws_layout_decode(L, T, am);
   const int d = L->d, E = L->E;
   const bool forced = r && r->in_idx && r->in_w;
   int slot;
@@ -431,7 +431,7 @@ int decode_layer(const moe_layer* L, const LayerInput& in, float eps, int T, flo
   ra.E = E;
   ra.code_off = moe_code_offset(L->bits);
   ra.do_logits = !forced;
-  ra.act16 = act16;
+  ra.am = am;
   ra.lp = reinterpret_cast<float*>(ws + W.lp);
   ra.x.frag = reinterpret_cast<_Float16*>(ws + W.xfrag);
   ra.x.cs = reinterpret_cast<float*>(ws + W.xcs);
@@ -485,7 +485,7 @@ int decode_layer(const moe_layer* L, const LayerInput& in, float eps, int T, flo
   ga.hI = W.nbI * 32;
   ga.code_off = ra.code_off;
   ga.has_shared = L->Is > 0;
-  ga.act16 = act16;
+  ga.am = am;
   {
     // one workgroup per CU (the kernel's LDS allows no more), never more
     // workgroups than 16-row tiles
@@ -516,7 +516,7 @@ int decode_layer(const moe_layer* L, const LayerInput& in, float eps, int T, flo
   da.S = W.S;
   da.has_shared = L->Is > 0;
   da.max_slots = W.max_slots;
-  da.act16 = act16;
+  da.am = am;
   da.ypart = reinterpret_cast<float*>(ws + W.ypart);
   int dn_nw = env_int("MOE_DOWN_WAVES", 8);
   if (dn_nw <= 0 || dn_nw > 8) dn_nw = 8;
@@ -681,9 +681,10 @@ int prefill_layer(const moe_layer* L, const float* x, int norm, float eps, int T
 size_t ws_need(const moe_layer* L, int T, int n_layers) {
   const int Tw = T < 1 ? 1 : T;
   // the decode layouts (8 tokens with fp16 hi + lo activations, 16 with fp16
-  // activations) and, above 8 tokens, the prefill layout
+  // or with fp16 hi + lo activations) and, above 8 tokens, the prefill layout
   const int t8 = Tw < MOE_MAX_TOK_DECODE ? Tw : MOE_MAX_TOK_DECODE, t16 = Tw < MOE_MAX_TOK_F16ACT ? Tw : MOE_MAX_TOK_F16ACT;
-  size_t dec = std::max((size_t)ws_layout_decode(L, t8).total, (size_t)ws_layout_decode(L, t16, true).total);
+  size_t dec = std::max((size_t)ws_layout_decode(L, t8).total, (size_t)ws_layout_decode(L, t16, MOE_AM_F16).total);
+  dec = std::max(dec, (size_t)ws_layout_decode(L, t16, MOE_AM_HL16).total);
   dec = std::max(dec, (size_t)std::max(ws_layout_persist(L, t8, false, n_layers).total,
                                        ws_layout_persist(L, t16, true, n_layers).total));
   return T > MOE_MAX_TOK_DECODE ? std::max(dec, (size_t)ws_layout_prefill(L, T).total) : dec;
@@ -1056,18 +1057,23 @@ static int persist_pass(const moe_layer* const* layers, int n_layers, const floa
   return MOE_OK;
 }
 
+// Tokens 9..16 of a full-precision call take one decode pass with 16 hi + lo
+// token rows (MOE_MID_T=0 in the environment: the grouped GEMMs for a layer,
+// passes of 8 tokens for a stack, as before the 16-row pass existed).
+static bool mid_t_decode() { return env_int("MOE_MID_T", 1) != 0; }
+
 static int decode_layer_out(const moe_layer* L, const float* x, int T, float* y, const moe_route_io* route,
-                            uint8_t* wsb, hipStream_t st, bool act16) {
-  if (persist_usable(&L, 1)) {
+                            uint8_t* wsb, hipStream_t st, int am) {
+  if (am != MOE_AM_HL16 && persist_usable(&L, 1)) {
     int32_t* oi = route ? route->out_idx : nullptr;
     float* ow = route ? route->out_w : nullptr;
-    return persist_pass(&L, 1, x, T, 0.f, y, nullptr, 0, oi, ow, 0, route, wsb, st, act16);
+    return persist_pass(&L, 1, x, T, 0.f, y, nullptr, 0, oi, ow, 0, route, wsb, st, am == MOE_AM_F16);
   }
   int S = 1;
-  int rc = decode_layer(L, LayerInput{x, 1, 0, 0}, 0.f, T, nullptr, route, wsb, st, &S, act16);
+  int rc = decode_layer(L, LayerInput{x, 1, 0, 0}, 0.f, T, nullptr, route, wsb, st, &S, am);
   if (rc) return rc;
-  const WsLayout W = ws_layout_decode(L, T, act16);
-  const int64_t R = act16 ? MOE_MAX_TOK_F16ACT : MOE_MAX_TOK_DECODE;
+  const WsLayout W = ws_layout_decode(L, T, am);
+  const int64_t R = moe_am_tokens(am);
   HIPCHK(launch_combine(reinterpret_cast<const float*>(wsb + W.ypart), S, R * L->d, T, L->d, y, st));
   return MOE_OK;
 }
@@ -1078,8 +1084,10 @@ int moe_layer_forward(const moe_layer* L, const float* x, int T, float* y, const
   if (rc || T == 0) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
+  if (T > MOE_MAX_TOK_DECODE && T <= MOE_MAX_TOK_F16ACT && mid_t_decode())
+    return decode_layer_out(L, x, T, y, route, wsb, st, MOE_AM_HL16);
   if (T > MOE_MAX_TOK_DECODE) return prefill_layer(L, x, 0, 0.f, T, y, route, wsb, st);
-  return decode_layer_out(L, x, T, y, route, wsb, st, false);
+  return decode_layer_out(L, x, T, y, route, wsb, st, MOE_AM_HL8);
 }
 
 int moe_layer_forward_noalloc(const moe_layer* L, const float* x, int T, float* y, const moe_route_io* route,
@@ -1094,8 +1102,10 @@ int moe_layer_forward_noalloc(const moe_layer* L, const float* x, int T, float* 
   // the scratch keeps the previous call's contents: clear the control words
   // the kernels count in (a fill kernel, so the call stays capturable)
   HIPCHK(launch_fill_u32(reinterpret_cast<uint32_t*>(wsb), (size_t)ctrl_bytes() / 4, 0u, st));
+  if (T > MOE_MAX_TOK_DECODE && T <= MOE_MAX_TOK_F16ACT && mid_t_decode())
+    return decode_layer_out(L, x, T, y, route, wsb, st, MOE_AM_HL16);
   if (T > MOE_MAX_TOK_DECODE) return prefill_layer(L, x, 0, 0.f, T, y, route, wsb, st);
-  return decode_layer_out(L, x, T, y, route, wsb, st, false);
+  return decode_layer_out(L, x, T, y, route, wsb, st, MOE_AM_HL8);
 }
 
 int moe_layer_forward_f16act(const moe_layer* L, const float* x, int T, float* y, const moe_route_io* route,
@@ -1104,7 +1114,7 @@ int moe_layer_forward_f16act(const moe_layer* L, const float* x, int T, float* y
   int rc = layer_args(L, x, T, y, route, ws, ws_bytes);
   if (rc || T == 0) return rc;
   return decode_layer_out(L, x, T, y, route, reinterpret_cast<uint8_t*>(ws), reinterpret_cast<hipStream_t>(stream),
-                          true);
+                          MOE_AM_F16);
 }
 
 // Argument checks shared by the stack entry points.
@@ -1135,10 +1145,11 @@ static int stack_args(const moe_layer* const* layers, int n_layers, const float*
 // the routing outputs.
 static int decode_stack(const moe_layer* const* layers, int n_layers, const float* x, int T, float eps, float* y,
                         float* y_layers, int32_t* idx_layers, float* w_layers, uint8_t* wsb, hipStream_t s,
-                        bool act16) {
+                        int am) {
   const int d = layers[0]->d;
-  const int chunk = act16 ? MOE_MAX_TOK_F16ACT : MOE_MAX_TOK_DECODE;
-  if (persist_usable(layers, n_layers)) {
+  const int chunk = moe_am_tokens(am);
+  const bool act16 = am == MOE_AM_F16;
+  if (am != MOE_AM_HL16 && persist_usable(layers, n_layers)) {
     const int k = layers[0]->k;
     for (int c0 = 0; c0 < T; c0 += chunk) {
       const int Tc = T - c0 < chunk ? T - c0 : chunk;
@@ -1161,9 +1172,9 @@ static int decode_stack(const moe_layer* const* layers, int n_layers, const floa
       }
       float* prev_out = (l > 0 && y_layers) ? y_layers + ((size_t)(l - 1) * T + c0) * d : nullptr;
       int S = 1;
-      int rc = decode_layer(layers[l], in, eps, Tc, prev_out, &r, wsb, s, &S, act16);
+      int rc = decode_layer(layers[l], in, eps, Tc, prev_out, &r, wsb, s, &S, am);
       if (rc) return rc;
-      const WsLayout W = ws_layout_decode(layers[l], Tc, act16);
+      const WsLayout W = ws_layout_decode(layers[l], Tc, am);
       in = LayerInput{reinterpret_cast<const float*>(wsb + W.ypart), S, (int64_t)chunk * d, 1};
     }
     serial_point(s);
@@ -1207,7 +1218,8 @@ int moe_stack_forward(const moe_layer* const* layers, int n_layers, const float*
     if (y_layers) HIPCHK(hipMemcpyAsync(y, y_layers + (size_t)(n_layers - 1) * T * d, (size_t)T * d * 4, hipMemcpyDeviceToDevice, s));
     return MOE_OK;
   }
-  return decode_stack(layers, n_layers, x, T, eps, y, y_layers, idx_layers, w_layers, wsb, s, false);
+  const int am = T > MOE_MAX_TOK_DECODE && mid_t_decode() ? MOE_AM_HL16 : MOE_AM_HL8;
+  return decode_stack(layers, n_layers, x, T, eps, y, y_layers, idx_layers, w_layers, wsb, s, am);
 }
 
 int moe_stack_forward_f16act(const moe_layer* const* layers, int n_layers, const float* x, int T, float eps,
@@ -1217,7 +1229,7 @@ int moe_stack_forward_f16act(const moe_layer* const* layers, int n_layers, const
   int rc = stack_args(layers, n_layers, x, T, y, y_layers, idx_layers, w_layers, ws, ws_bytes);
   if (rc || T == 0) return rc;
   return decode_stack(layers, n_layers, x, T, eps, y, y_layers, idx_layers, w_layers, reinterpret_cast<uint8_t*>(ws),
-                      reinterpret_cast<hipStream_t>(stream), true);
+                      reinterpret_cast<hipStream_t>(stream), MOE_AM_F16);
 }
 
 int moe_group_workspace_bytes(int T, int E, int k, size_t* bytes) {

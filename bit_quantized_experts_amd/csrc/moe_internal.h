@@ -25,14 +25,13 @@
 #include <stdint.h>
 
 #define MOE_BLOCK 32
+// Tokens per decode pass with one 16-row tile of fp16 hi and lo rows.
 #define MOE_MAX_TOK_DECODE 8
-// Tokens per decode pass with fp16 activations (one MFMA row per token
-// instead of an fp16 hi and lo row).
+// Tokens per decode pass with 16 token rows: fp16 activations (one row per
+// token), or a tile of hi parts followed by a tile of lo parts.
 #define MOE_MAX_TOK_F16ACT 16
-// Stacks of up to this many tokens run the decode kernels, the whole stack
-// for MOE_MAX_TOK_DECODE tokens at a time (faster per layer than the grouped
-// GEMMs at these sizes; a single layer above MOE_MAX_TOK_DECODE tokens is
-// faster on the grouped GEMMs).
+// Layers and stacks of up to this many tokens run the decode kernels (faster
+// than the grouped GEMMs at these sizes).
 #define MOE_MAX_TOK_CHUNKED 16
 #define MOE_MAX_TOK_PREFILL 65536
 #define MOE_MAX_K 16

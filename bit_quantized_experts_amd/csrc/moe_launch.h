@@ -22,19 +22,31 @@
 #define MOE_CTRL_WORDS 64
 
 // ---------------------------------------------------------------- decode ---
+// Activation rows of the decode kernels' matrix-core A operand (the `am`
+// argument fields): 8 tokens as fp16 hi + lo rows (one 16-row tile per
+// 32-input block), 16 tokens rounded to fp16 (one tile), or 16 tokens as fp16
+// hi + lo rows (two tiles per block: tokens 0..7 and 8..15, each weight
+// fragment multiplied by both).
+#define MOE_AM_HL8 0
+#define MOE_AM_F16 1
+#define MOE_AM_HL16 2
+constexpr int moe_am_tokens(int am) { return am == MOE_AM_HL8 ? 8 : 16; }
+constexpr int moe_am_tiles(int am) { return am == MOE_AM_HL16 ? 2 : 1; }
+
 // The layer input as the gate/up kernel's matrix-core A operand, written by
 // the router's row-slice-0 workgroups (one per column slice of
-// MOE_ROUTE_COLS inputs): every 32-input block as [64 lanes][8] fp16 (lane
-// m + 16q holds inputs 8q..8q+7 of row m: the fp16 hi part of token m for
-// m < 8 and the lo part of token m - 8 for m >= 8, or token m rounded to fp16
-// with 16 tokens), the block's accumulator seeds (-2^(b-1) times the row sums
-// of the block), and the power of two 2^-e every (column slice, token) was
-// scaled by before the split (e from the slice's largest magnitude of the
-// token: 2^14 <= max 2^-e < 2^15).
+// MOE_ROUTE_COLS inputs): every 32-input block as NT tiles of [64 lanes][8]
+// fp16 (NT = moe_am_tiles(am); in tile tt lane m + 16q holds inputs
+// 8q..8q+7 of row m: the fp16 hi part of token 8tt + m for m < 8 and the lo
+// part of token 8tt + m - 8 for m >= 8, or token m rounded to fp16 with fp16
+// rows), the tiles' accumulator seeds (-2^(b-1) times the row sums of the
+// block), and the power of two 2^-e every (column slice, token) was scaled
+// by before the split (e from the slice's largest magnitude of the token:
+// 2^14 <= max 2^-e < 2^15).
 #define MOE_XSX_STRIDE 64  // words between two slices' exponents (a 256-byte line each)
 struct XFrag {
-  _Float16* frag;  // [d/32][64][8]
-  float* cs;       // [d/32][16]
+  _Float16* frag;  // [d/32][NT][64][8]
+  float* cs;       // [d/32][NT][16]
   int32_t* sx;     // [d/MOE_ROUTE_COLS][MOE_XSX_STRIDE], token t at t
 };
 
@@ -62,7 +74,7 @@ struct RouteArgs {
   const _Float16* wh;  // router rows times 2^-ew, fp16 hi part, B-fragments [E16/16][d/32][64][8]
   const _Float16* wl;  // same, lo part
   int32_t T, d, E, code_off, do_logits;
-  int32_t act16;    // 1: gate/up A-fragments hold 16 tokens in fp16 (else 8 tokens as fp16 hi + lo)
+  int32_t am;       // activation rows of the gate/up A operand (MOE_AM_*)
   float* lp;        // ws [d/MOE_ROUTE_COLS][T][E] partial logits
   XFrag x;          // the gate/up kernel's A operand (row slice 0 writes it)
   float* y_out;     // optional: the summed input, [T][d]
@@ -96,9 +108,9 @@ struct GuArgs {
   float* slot_w;         // out [MAX_SLOTS][16]
   const float* rnorm;
   XFrag x;               // the layer input as A-fragments (before the RMSNorm of stacked layers)
-  float* hbuf;      // ws [MAX_SLOTS][hI/16][R][16] fp32 h = w silu(g) u, R = 16 (act16) or 8
+  float* hbuf;      // ws [MAX_SLOTS][hI/16][R][16] fp32 h = w silu(g) u, R = moe_am_tokens(am)
   int32_t E, I, Is, T, d, n_kg, bits, hI, code_off, has_shared;
-  int32_t act16;  // 1: A rows are 16 tokens in fp16 (else 8 tokens as fp16 hi + lo)
+  int32_t am;  // activation rows (MOE_AM_*)
 };
 
 struct DownArgs {
@@ -107,8 +119,8 @@ struct DownArgs {
   const int32_t* slot_expert;
   const float* hbuf;       // [MAX_SLOTS][R][hI] fp32
   int32_t E, d, T, bits, hI, BK, RT, n_kg_r, n_kg_s, S, has_shared, max_slots;
-  int32_t act16;  // 1: A rows are 16 tokens in fp16 (else 8 tokens as fp16 hi + lo)
-  float* ypart;   // ws [S][R][d], R = 16 with act16, else 8
+  int32_t am;     // activation rows (MOE_AM_*)
+  float* ypart;   // ws [S][R][d], R = moe_am_tokens(am)
 };
 
 // Block kinds as the kernels' template tag: 2 and 3 are b-bit code blocks,

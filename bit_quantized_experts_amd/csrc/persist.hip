@@ -69,7 +69,8 @@ DEVI void warm_down_weights(const PersistArgs& P, const ExpertSet& X, GuLds& L, 
 template <int BITS, int NPER, int RT, bool A16>
 __global__ __launch_bounds__(512) void decode_persist_kernel(PersistArgs P) {
   __shared__ GuLds L;
-  constexpr int R = A16 ? MOE_MAX_TOK_F16ACT : MOE_MAX_TOK_DECODE;
+  constexpr int AM = A16 ? MOE_AM_F16 : MOE_AM_HL8;  // (16 hi/lo token rows run as per-phase kernels)
+  constexpr int R = moe_am_tokens(AM);
   const int b = blockIdx.x, G = gridDim.x;
   const int T = P.T, d = P.d, n_cs = P.n_cs, n_rs = P.n_rs, S = P.S, n_rg = P.n_rg;
   const bool forced = P.in_idx != nullptr;
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(512) void decode_persist_kernel(PersistArgs P) {
     ra.E = P.E;
     ra.code_off = P.code_off;
     ra.do_logits = !forced;
-    ra.act16 = A16;
+    ra.am = AM;
     ra.lp = P.lp;
     ra.x = xf;
     ra.y_out = l == 0 ? P.y_prev_out : (P.y_layers ? P.y_layers + (size_t)(l - 1) * P.yl_stride : nullptr);
@@ -166,10 +167,10 @@ __global__ __launch_bounds__(512) void decode_persist_kernel(PersistArgs P) {
     ga.hI = P.hI;
     ga.code_off = P.code_off;
     ga.has_shared = P.has_shared;
-    ga.act16 = A16;
-    gu_select<BITS, NPER, A16>(ga, L, b == 0, false);
+    ga.am = AM;
+    gu_select<BITS, NPER, AM>(ga, L, b == 0, false);
     warm_down_weights<BITS, RT>(P, ga.X, L, b, G);
-    gu_items<BITS, A16>(ga, L, b, G, h_ready);
+    gu_items<BITS, AM>(ga, L, b, G, h_ready);
     __syncthreads();
 
     // ------------------------------------------------------------ down ---
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(512) void decode_persist_kernel(PersistArgs P) {
     da.S = S;
     da.has_shared = P.has_shared;
     da.max_slots = MOE_MAX_SLOTS;
-    da.act16 = A16;
+    da.am = AM;
     da.ypart = P.ypart;
     const int base = P.has_shared ? 1 : 0;
     const int ns = base + L.S.n_routed;
@@ -198,7 +199,7 @@ __global__ __launch_bounds__(512) void decode_persist_kernel(PersistArgs P) {
         const uint32_t tiles = (uint32_t)((u == 0 && base) ? P.Is / 16 : P.I / 16);
         if (!wg_wait(h_ready + (size_t)u * CS, tiles, P.status, &L.flag)) return;
       }
-      down_role<BITS, RT, A16>(da, rg, sp, ns, L.S.expert, reinterpret_cast<float*>(L.xs));
+      down_role<BITS, RT, AM>(da, rg, sp, ns, L.S.expert, reinterpret_cast<float*>(L.xs));
       if (threadIdx.x == 0) {
         // every wavefront's partial sums are stored (each waited before the
         // role's last barrier)

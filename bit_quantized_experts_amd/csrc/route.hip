@@ -81,7 +81,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   const dim3 grid(a.d / MOE_ROUTE_COLS, a.do_logits ? (a.E + MOE_ROUTE_ROWS - 1) / MOE_ROUTE_ROWS : 1);
   // the completion counts must match the grid, or no workgroup selects
   if ((int)grid.x != a.sel.n_cs || (int)grid.y != a.sel.n_rs || a.sel.n_rs > MOE_CTRL_WORDS ||
-      a.sel.n_cs > MOE_MAX_CS || a.T < 1 || a.T > (a.act16 ? MOE_MAX_TOK_F16ACT : MOE_MAX_TOK_DECODE))
+      a.sel.n_cs > MOE_MAX_CS || a.T < 1 || a.T > moe_am_tokens(a.am) || a.am < MOE_AM_HL8 || a.am > MOE_AM_HL16)
     return hipErrorInvalidValue;
   MOE_LAUNCH(route_kernel, grid, dim3(256), 0, s, a);
   return hipGetLastError();

@@ -158,35 +158,53 @@ DEVI half8_t x_fragment(const float (*ys)[MOE_ROUTE_COLS], int bl, int lane, int
   return h;
 }
 
-// The same for 16 tokens in fp16 (fp16 activations): lane L = m + 16q holds
-// token m at inputs 8q..8q+7, scaled by 2^-e of the token, rounded to fp16.
-DEVI half8_t x_fragment16(const float (*ys)[MOE_ROUTE_COLS], int bl, int lane, int T, int e) {
+// The same for 16 token rows: lane L = m + 16q holds token m at inputs
+// 8q..8q+7, scaled by 2^-e of the token, as its fp16 hi part (in h) and the
+// fp16 rest (in lo).
+DEVI void x_fragment16(const float (*ys)[MOE_ROUTE_COLS], int bl, int lane, int T, int e, half8_t& h, half8_t& lo) {
   const int m = lane & 15, q = lane >> 4;
   float4_t v0 = float4_t{0.f, 0.f, 0.f, 0.f}, v1 = v0;
   if (m < T) {
     v0 = *reinterpret_cast<const float4_t*>(&ys[m][32 * bl + 8 * q]);
     v1 = *reinterpret_cast<const float4_t*>(&ys[m][32 * bl + 8 * q + 4]);
   }
-  half8_t h;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) h[c] = (_Float16)ldexpf(c < 4 ? v0[c] : v1[c - 4], -e);
-  return h;
+  for (int c = 0; c < 8; ++c) {
+    const float v = ldexpf(c < 4 ? v0[c] : v1[c - 4], -e);
+    h[c] = (_Float16)v;
+    lo[c] = (_Float16)(v - (float)h[c]);
+  }
 }
 
 // Row slice 0 only: block bl of this column slice as the gate/up kernel's
-// A-fragment (device-coherent 16-byte stores) and its accumulator seeds
-// (-2^(b-1) times each row's sum of the block's 32 fp16 values, four lanes
-// per row added), one wavefront per block.
+// A-fragments (device-coherent 16-byte stores: one tile, or the hi and lo
+// tiles of 16 tokens) and its accumulator seeds (-2^(b-1) times each row's
+// sum of the block's 32 fp16 values, of both tiles with two; four lanes per
+// row added), one wavefront per block.
 DEVI void write_xfrag(const RouteArgs& a, int cs, const float (*ys)[MOE_ROUTE_COLS], const int* xe, int bl,
                       int lane) {
   const int T = a.T;
-  const half8_t A = a.act16 ? x_fragment16(ys, bl, lane, T, xe[min(lane & 15, T - 1)])
-                            : x_fragment(ys, bl, lane, T, xe[min(lane & 7, T - 1)]);
   const int b = cs * (MOE_ROUTE_COLS / 32) + bl;
-  coh_st4(coh_rsrc(a.x.frag), (uint32_t)(((size_t)b * 64 + lane) * 16), __builtin_bit_cast(float4_t, A));
+  const __amdgpu_buffer_rsrc_t fr = coh_rsrc(a.x.frag);
   float s = 0.f;
+  if (a.am == MOE_AM_HL8) {
+    const half8_t A = x_fragment(ys, bl, lane, T, xe[min(lane & 7, T - 1)]);
+    coh_st4(fr, (uint32_t)(((size_t)b * 64 + lane) * 16), __builtin_bit_cast(float4_t, A));
 #pragma unroll
-  for (int c = 0; c < 8; ++c) s += (float)A[c];
+    for (int c = 0; c < 8; ++c) s += (float)A[c];
+  } else {
+    half8_t A, Al;
+    x_fragment16(ys, bl, lane, T, xe[min(lane & 15, T - 1)], A, Al);
+    const int NT = a.am == MOE_AM_HL16 ? 2 : 1;
+    coh_st4(fr, (uint32_t)(((size_t)b * NT * 64 + lane) * 16), __builtin_bit_cast(float4_t, A));
+    if (NT == 2) coh_st4(fr, (uint32_t)(((size_t)b * NT * 64 + 64 + lane) * 16), __builtin_bit_cast(float4_t, Al));
+#pragma unroll
+    for (int c = 0; c < 8; ++c) s += (float)A[c];
+    if (NT == 2) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) s += (float)Al[c];
+    }
+  }
   s += __shfl_xor(s, 16, 64);
   s += __shfl_xor(s, 32, 64);
   if (lane < 16) st_dev(a.x.cs + (size_t)b * 16 + lane, -(float)a.code_off * s);

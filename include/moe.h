@@ -191,10 +191,13 @@ int moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
  * expert); devlabs blog, section 核心技术特点, MTP item (eight tokens per
  * verify pass); agentlenshq article, section "Strata 如何让 125 B 模型适配
  * 12-24 GB 显存", last item (8192-token prompt chunks)].  T = 0 is a no-op.
- * T <= 8 runs the
+ * T <= 16 runs the
  * decode/verify kernels (experts streamed once per call with 128-bit loads
- * and multiplied from their codes, activations carried as fp16 hi + lo);
- * 8 < T <= 65536 runs the chunked-prefill kernels: the (token, slot) pairs are grouped by expert (as
+ * and multiplied from their codes, activations carried as fp16 hi + lo: up
+ * to 8 tokens as hi and lo rows of one matrix-core tile, 9..16 tokens as a
+ * tile of their hi parts whose products the tile of their lo parts
+ * continues, so each weight fragment is decoded once for all 16);
+ * 16 < T <= 65536 runs the chunked-prefill kernels: the (token, slot) pairs are grouped by expert (as
  * moe_group_tokens) and each expert's rows go through a grouped matrix
  * multiply on the matrix cores with the weights dequantized in registers to
  * fp16 and the activations rounded to fp16 after an exact per-row
@@ -238,8 +241,8 @@ int moe_layer_forward_f16act(const moe_layer *layer, const float *x, int T, floa
                              void *ws, size_t ws_bytes, void *stream);
 
 /* A stack of layers with RMSNorm (unit weight) between consecutive layers
- * (T <= 16: decode kernels, the whole stack for 8 tokens at a time; T > 16:
- * prefill kernels, one layer after another):
+ * (T <= 16: decode kernels as in moe_layer_forward, the whole stack in one
+ * pass; T > 16: prefill kernels, one layer after another):
  *   h_0 = x,  y_l = MoE_l(h_l),  h_{l+1} = y_l / sqrt(mean(y_l^2) + eps),
  *   y = y_{n-1}.
  * All layers must have equal d_model.  Optional per-layer outputs:
@@ -327,7 +330,11 @@ int moe_workspace_status(const void *ws, size_t ws_bytes, int *status, void *str
  *   MOE_DOWN_WAVES   wavefronts per decode down workgroup [8; 1..8]
  *   MOE_PERSIST      1 = run a stack of layers of one shape (at most 1024
  *                    experts) as one persistent launch per 16 layers; 0 =
- *                    separate kernels per layer (route, gate/up, down) [0] */
+ *                    separate kernels per layer (route, gate/up, down) [0]
+ *                    (up to 8 tokens and the fp16-activation calls only)
+ *   MOE_MID_T        1 = 9..16 tokens through one decode pass of 16 hi + lo
+ *                    token rows; 0 = a layer through the chunked-prefill
+ *                    kernels, a stack in decode passes of 8 tokens [1] */
 
 /* Per-kernel timing for measurement: while enabled, the library brackets
  * every launch of the chosen kernel class with a pair of HIP events that the

@@ -184,9 +184,11 @@ def test_cb_stack_teacher_forced(bqe, T):
 
 
 @pytest.mark.parametrize("shape,T", [("tiny", 9), ("tiny", 37), ("tiny", 200), ("full", 300)])
-def test_cb_prefill_layer(bqe, shape, T):
+def test_cb_prefill_layer(bqe, shape, T, monkeypatch):
     """Chunks of more than 8 tokens through the grouped GEMMs (codebook
-    weights dequantized in registers from the LDS grid), teacher-forced."""
+    weights dequantized in registers from the LDS grid), teacher-forced
+    (MOE_MID_T=0: T = 9 too)."""
+    monkeypatch.setenv("MOE_MID_T", "0")
     wl = _cb("tiny", Is=64, zipf_s=1.1) if shape == "tiny" else _cb("layer_t1")
     L = packed_layer(wl, 0)
     x_np = mi.activations(wl, T=T, stream=24)

@@ -214,9 +214,11 @@ def test_layer_odd_shapes(bqe):
             _check_layer(wl, 0, L, x, bqe, f"odd {kw} T={T}")
 
 
-@pytest.mark.parametrize("T", [6, 12])
-def test_forced_routing_and_invalid_entries(bqe, T):
-    # T = 6: the decode kernels; T = 12: the grouped-GEMM kernels
+@pytest.mark.parametrize("T,mid", [(6, "1"), (12, "1"), (12, "0")])
+def test_forced_routing_and_invalid_entries(bqe, T, mid, monkeypatch):
+    # T = 6: the 8-row decode pass; T = 12: the 16-row decode pass, or with
+    # MOE_MID_T=0 the grouped-GEMM kernels
+    monkeypatch.setenv("MOE_MID_T", mid)
     wl = mi.small(mi.WORKLOADS["tiny"], Is=64)
     L = packed_layer(wl, 0)
     x_np = mi.activations(wl, T=T, stream=7)
@@ -400,10 +402,11 @@ def test_stack_mixed_layer_shapes(bqe):
         assert err <= TOL_DECODE_PATH, (l, err)
 
 
-def test_stack_chunks_of_eight(bqe):
-    """9..16 tokens run the decode kernels 8 tokens at a time: a 12-token
-    stack call equals calls on rows 0..7 and 8..11, bit for bit, in the
-    output, the per-layer outputs and the per-layer routing."""
+def test_stack_chunks_of_eight(bqe, monkeypatch):
+    """With MOE_MID_T=0, 9..16 tokens run the decode kernels 8 tokens at a
+    time: a 12-token stack call equals calls on rows 0..7 and 8..11, bit for
+    bit, in the output, the per-layer outputs and the per-layer routing."""
+    monkeypatch.setenv("MOE_MID_T", "0")
     wl = mi.small(mi.WORKLOADS["tiny"], Is=64, zipf_s=1.1, layers=3)
     layers = [packed_layer(wl, l) for l in range(wl.layers)]
     nL, d, k, T = wl.layers, wl.d, wl.k, 12

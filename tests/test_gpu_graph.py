@@ -51,11 +51,11 @@ def _replays_match(run, outs, other, n_replay=3):
     say(f"    {n_replay} replays equal the eager result")
 
 
-@pytest.mark.parametrize("mode", ["decode", "f16act", "prefill_T200"])
+@pytest.mark.parametrize("mode", ["decode", "decode_T12", "f16act", "prefill_T200"])
 def test_stack_graph_replays(bqe, mode):
     wl = mi.small(mi.WORKLOADS["stack_t8_2bit"], layers=2) if mode != "prefill_T200" else \
         mi.small(mi.WORKLOADS["tiny"], Is=64, zipf_s=1.1, layers=3)
-    T = {"decode": 8, "f16act": 16, "prefill_T200": 200}[mode]
+    T = {"decode": 8, "decode_T12": 12, "f16act": 16, "prefill_T200": 200}[mode]
     layers = [packed_layer(wl, l) for l in range(wl.layers)]
     handles = [L.handle for L in layers]
     nL, d, k = wl.layers, wl.d, wl.k
@@ -72,7 +72,7 @@ def test_stack_graph_replays(bqe, mode):
                    lambda: fwd(handles, x2, y2, ws, 1e-6))
 
 
-@pytest.mark.parametrize("T", [1, 8, 40])
+@pytest.mark.parametrize("T", [1, 8, 12, 40])
 def test_layer_graph_replays(bqe, T):
     wl = mi.small(mi.WORKLOADS["layer_t1"], layers=1)
     L = packed_layer(wl, 0)

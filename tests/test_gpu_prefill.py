@@ -110,7 +110,10 @@ def _check(bqe, wl, L, x_np, tag, sample=None, logit_rows=None):
 
 @pytest.mark.parametrize("bits", [2, 3])
 @pytest.mark.parametrize("Is", [0, 64, 96])
-def test_prefill_tiny(bqe, bits, Is):
+def test_prefill_tiny(bqe, bits, Is, monkeypatch):
+    # (MOE_MID_T=0: 9..16 tokens through the grouped GEMMs too, not the
+    # 16-row decode pass)
+    monkeypatch.setenv("MOE_MID_T", "0")
     wl = mi.small(mi.WORKLOADS["tiny"], bits=bits, Is=Is, zipf_s=1.1 if Is else None)
     L = packed_layer(wl, 0)
     for T in (9, 16, 17, 37, 200):  # more than 8 tokens: the grouped-GEMM kernels
