@@ -674,6 +674,9 @@ DEVI void gate_up_item(const PfGemmArgs& a, const Stages& S, int* ex_lds, int g,
     if (s + 1 < nsteps) issue(ic<(P + 1) % 2>{}, s + 1);
     if (act) {
       const unsigned char* st = S.get<P>();
+      // the A fragment of the next row group is read before the current
+      // one's multiplies, so LDS latency hides under them
+      half8_t A = *reinterpret_cast<const half8_t*>(st + xs[0]);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         half8_t B[4];
@@ -681,9 +684,13 @@ DEVI void gate_up_item(const PfGemmArgs& a, const Stages& S, int* ex_lds, int g,
         for (int m = 0; m < 4; ++m) B[m] = dequant<BITS>(bw[P][m], kb);
 #pragma unroll
         for (int rg = 0; rg < NRG; ++rg) {
-          const half8_t A = *reinterpret_cast<const half8_t*>(st + rg * 4096 + xs[kb]);
+          const bool last = kb == 3 && rg == NRG - 1;
+          const int nkb = rg == NRG - 1 ? kb + 1 : kb, nrg = rg == NRG - 1 ? 0 : rg + 1;
+          const half8_t An = last ? A : *reinterpret_cast<const half8_t*>(st + nrg * 4096 + xs[nkb & 3]);
+          __builtin_amdgcn_sched_barrier(0);  // (the read stays ahead of the multiplies)
 #pragma unroll
           for (int m = 0; m < 4; ++m) acc[rg][m] = mfma16x16x32(A, B[m], acc[rg][m]);
+          A = An;
         }
       }
     }
@@ -849,6 +856,9 @@ DEVI void down_item(const PfGemmArgs& a, const Stages& S, float* rowf_lds, int g
     if (s + 1 < nsteps) issue(ic<(P + 1) % 2>{}, s + 1);
     const unsigned char* st = S.get<P>();
     const int nj = min(4, nbK - 4 * s);
+    // the A fragment of the next row group is read before the current
+    // one's multiplies, so LDS latency hides under them
+    half8_t A = *reinterpret_cast<const half8_t*>(st + 16 * lane);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (j >= nj) break;
@@ -857,9 +867,13 @@ DEVI void down_item(const PfGemmArgs& a, const Stages& S, float* rowf_lds, int g
       for (int t = 0; t < 4; ++t) B[t] = dequant<BITS>(bw[P][M::chunk(t, j)], M::frag(t, j));
 #pragma unroll
       for (int rg = 0; rg < NRG; ++rg) {
-        const half8_t A = *reinterpret_cast<const half8_t*>(st + (rg * 4 + j) * 1024 + 16 * lane);
+        const bool last = j == 3 && rg == NRG - 1;
+        const int nj2 = rg == NRG - 1 ? j + 1 : j, nrg = rg == NRG - 1 ? 0 : rg + 1;
+        const half8_t An = last ? A : *reinterpret_cast<const half8_t*>(st + (nrg * 4 + (nj2 & 3)) * 1024 + 16 * lane);
+        __builtin_amdgcn_sched_barrier(0);  // (the read stays ahead of the multiplies)
 #pragma unroll
         for (int t = 0; t < 4; ++t) acc[rg][t] = mfma16x16x32(A, B[t], acc[rg][t]);
+        A = An;
       }
     }
   };
