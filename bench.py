@@ -12,10 +12,12 @@ the Infinity Cache emptied before every pass, and for the same input
 replayed back to back.
 
 The default run also measures, under "configs", the other configurations of
-the workload set, each with its own roofline and oracle baseline: one
-full-size layer at T = 1 (Infinity Cache emptied before each forward), the
-48-layer 3-bit stack at T = 8 and T = 1, and one layer over an 8192-token
-prefill chunk.  --workload picks a single one.
+the workload set, each with its own roofline and oracle baseline: the same
+2-bit stack at 16 tokens per pass (one pass of 16 hi + lo token rows per
+layer), one full-size layer at T = 1 (Infinity Cache emptied before each
+forward), the 48-layer 3-bit stack at T = 8 and T = 1, one layer over an
+8192-token prefill chunk, and the codebook-block layer and stack.
+--workload picks a single one.
 
 Prints one JSON line: tokens/s, plus achieved HBM bandwidth from the
 algorithmic bytes of the actual routing, the roofline of the dominant kernel
@@ -798,12 +800,19 @@ def main():
     wl = mi.WORKLOADS["stack_t8_2bit"]
     layers = build_stack(wl)
     out = bench_stack(args, wl, wl.T, layers)
-    del layers
-    torch.cuda.empty_cache()
     if args.timing_only:
         print(json.dumps(out))
         return
     configs = {}
+    # the same stack at 16 tokens per pass: one decode pass of 16 hi + lo
+    # token rows per layer (the oracle sample halved: each layer costs twice
+    # the CPU time)
+    log("stack_t8_2bit T=16 ...")
+    args16 = argparse.Namespace(**vars(args))
+    args16.cpu_layers = max(1, args.cpu_layers // 2) if args.cpu_layers > 0 else 0
+    configs["stack_t8_2bit_T16"] = bench_stack(args16, wl, 16, layers)
+    del layers
+    torch.cuda.empty_cache()
     log("layer_t1 ...")
     configs["layer_t1"] = bench_layer_t1(args)
     torch.cuda.empty_cache()
