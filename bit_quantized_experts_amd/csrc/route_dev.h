@@ -49,53 +49,65 @@ DEVI bool count_done(uint32_t* ctr, uint32_t total, int* flag) {
   return *flag != 0;
 }
 
-// Wavefront wv finishes tokens wv + 4j (below T), two at a time (pairs p =
-// tid and tid + 256 of a pass: token 8h + p / 64, expert rs * 64 + p % 64);
-// every load of a pass is issued before its first add, at clamped
-// addresses.
-template <int MAXCS>
-DEVI void finish_slice(const RouteArgs& a, int rs) {
+// Wavefront wv finishes tokens wv + 4j (below T), in passes of NP: every
+// load of a pass is issued before its first add, at clamped addresses.  A
+// wavefront has at most two tokens up to T = 8 and four up to 16; up to 32
+// column slices one pass takes all of them (one round trip whatever T),
+// wider inputs take two per pass (the partials of four tokens would not fit
+// in registers).
+template <int MAXCS, int NP>
+DEVI void finish_pass(const RouteArgs& a, int rs, int j0, int nj, int wv, int lane) {
   const SelectArgs& c = a.sel;
-  const int tid = opaque_tid();
-  const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (wv >= 4) return;  // (four wavefronts finish a slice; no barrier follows here)
   const int T = a.T, E = a.E, n_cs = c.n_cs;
-  static_assert(MOE_MAX_TOK_F16ACT <= 16, "two passes of 8 tokens");
   const int er = rs * MOE_ROUTE_ROWS + lane, e = min(er, E - 1);
   const bool e_ok = er < E;
   const int ew = a.do_logits ? c.ew[e] : 0;
   const float bias = a.do_logits ? c.br[e] : 0.f;
   const float* ssr = c.ss_part + (size_t)rs * n_cs * T;
-  for (int h = 0; 8 * h < T; ++h) {
-    int t[2];
-    float ss[2], tmp[2][MAXCS];
+  float ss[NP], tmp[NP][MAXCS];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      t[j] = min(8 * h + wv + 4 * j, T - 1);
-      ss[j] = ld_dev(ssr + min(lane, n_cs - 1) * T + t[j]);
-      if (a.do_logits) {
+  for (int j = 0; j < NP; ++j) {
+    const int t = min(wv + 4 * min(j0 + j, nj - 1), T - 1);
+    ss[j] = ld_dev(ssr + min(lane, n_cs - 1) * T + t);
+    if (a.do_logits) {
 #pragma unroll
-        for (int q = 0; q < MAXCS; ++q) tmp[j][q] = ld_dev(a.lp + ((size_t)min(q, n_cs - 1) * T + t[j]) * E + e);
-      }
+      for (int q = 0; q < MAXCS; ++q) tmp[j][q] = ld_dev(a.lp + ((size_t)min(q, n_cs - 1) * T + t) * E + e);
     }
+  }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int tok = 8 * h + wv + 4 * j;
-      const float r = c.norm ? sqrtf(wave_sum((lane < n_cs) ? ss[j] : 0.f) / (float)c.d + c.eps) : 1.0f;
-      if (tok >= T) continue;
-      if (rs == 0 && lane == 0) st_dev(c.rnorm + tok, r);
-      if (!a.do_logits) continue;
-      float acc = tmp[j][0];
+  for (int j = 0; j < NP; ++j) {
+    if (j0 + j >= nj) break;
+    const int tok = wv + 4 * (j0 + j);
+    const float r = c.norm ? sqrtf(wave_sum((lane < n_cs) ? ss[j] : 0.f) / (float)c.d + c.eps) : 1.0f;
+    if (rs == 0 && lane == 0) st_dev(c.rnorm + tok, r);
+    if (!a.do_logits) continue;
+    float acc = tmp[j][0];
 #pragma unroll
-      for (int q = 1; q < MAXCS; ++q)
-        if (q < n_cs) acc += tmp[j][q];
-      const float x = ldexpf(acc, ew);  // router row factor, exact
-      const float l = (c.norm ? x / r : x) + bias;
-      if (e_ok) {
-        st_dev(c.logits + (size_t)tok * c.logits_stride + er, l);
-        if (c.out_logits) c.out_logits[(size_t)tok * E + er] = l;
-      }
+    for (int q = 1; q < MAXCS; ++q)
+      if (q < n_cs) acc += tmp[j][q];
+    const float x = ldexpf(acc, ew);  // router row factor, exact
+    const float l = (c.norm ? x / r : x) + bias;
+    if (e_ok) {
+      st_dev(c.logits + (size_t)tok * c.logits_stride + er, l);
+      if (c.out_logits) c.out_logits[(size_t)tok * E + er] = l;
     }
+  }
+}
+
+template <int MAXCS>
+DEVI void finish_slice(const RouteArgs& a, int rs) {
+  const int tid = opaque_tid();
+  const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (wv >= 4) return;  // (four wavefronts finish a slice; no barrier follows here)
+  static_assert(MOE_MAX_TOK_F16ACT <= 16, "at most four tokens per wavefront");
+  const int nj = (a.T - wv + 3) / 4;  // this wavefront's tokens (wave-uniform)
+  if (nj <= 2) {
+    if (nj > 0) finish_pass<MAXCS, 2>(a, rs, 0, nj, wv, lane);
+  } else if constexpr (MAXCS <= 32) {
+    finish_pass<MAXCS, 4>(a, rs, 0, nj, wv, lane);
+  } else {
+    finish_pass<MAXCS, 2>(a, rs, 0, nj, wv, lane);
+    finish_pass<MAXCS, 2>(a, rs, 2, nj, wv, lane);
   }
 }
 
