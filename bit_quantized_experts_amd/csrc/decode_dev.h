@@ -323,7 +323,7 @@ DEVI void run_tile(const uint8_t* gate, const uint8_t* up, int64_t rowoff, int k
 
 // Selection and slot list of a gate/up workgroup (every workgroup runs it):
 // each token's top k (or the given routing rows), the slot list in LDS, the
-// activation window staged.  publish_routing: write the routing used to the
+// first activation window staged.  publish_routing: write the routing used to the
 // caller's outputs; publish_slots: write the slot list to the workspace (for
 // a separate down kernel).
 template <int BITS, int NPER, int AM>  // NPER >= ceil(E / 64)
@@ -360,12 +360,13 @@ DEVI void gu_select(const GuArgs& a, GuLds& L, bool publish_routing, bool publis
     const int i = min(tid + 512 * h, n_sx - 1);
     sxv[h] = a.x.sx[(size_t)(i >> 4) * MOE_XSX_STRIDE + (i & 15)];
   }
-  // the activation window (one window for inputs of up to
+  // the first activation window (the whole input for inputs of up to
   // gu_win_blocks(AM) blocks) stays in registers through the selection and
   // is stored to LDS before the barrier that ends it: the selection starts as
   // soon as its logits are in, while the larger window is still arriving
+  const int win_kg = (n_kg + n_win - 1) / n_win;
   WindowRegs win;
-  if (n_win == 1) window_load<AM>(win, a, 0, 8 * n_kg, tid);
+  window_load<AM>(win, a, 0, 8 * win_kg, tid);
   clear_slots(L.S, E, T, base + min(tk, E), has_shared);
   lds_barrier();  // byte map and weight rows cleared before any wavefront marks (the loads stay in flight)
   static_assert(2 * GU_NW >= MOE_MAX_TOK_F16ACT, "two tokens per wavefront");
@@ -392,7 +393,7 @@ DEVI void gu_select(const GuArgs& a, GuLds& L, bool publish_routing, bool publis
     }
   }
   __builtin_amdgcn_sched_barrier(0);  // (the window's stores stay after the selection)
-  if (n_win == 1) window_store<AM>(win, L, 8 * n_kg, tid);
+  window_store<AM>(win, L, 8 * win_kg, tid);
   if (tid >= 64 && tid < 80) L.rn[tid - 64] = 1.0f / rnv;
 #pragma unroll
   for (int h = 0; h < 2; ++h)
@@ -439,6 +440,7 @@ DEVI void gu_items(const GuArgs& a, GuLds& L, int wg, int n_wg, uint32_t* h_read
   while (KP > 1 && (KP > n_kg || n_items * KP > n_wg * GU_NW)) KP >>= 1;
   const int G = GU_NW / KP, jw = wv / KP, kp = wv - jw * KP;
   const int tok_e = 4 * ((lane >> 4) & 1);
+  int staged = 0;  // the window in LDS (gu_select stages the first)
 
   for (int grp = wg; grp * G < n_items; grp += n_wg) {
     const int item = grp * G + jw;
@@ -466,12 +468,18 @@ DEVI void gu_items(const GuArgs& a, GuLds& L, int wg, int n_wg, uint32_t* h_read
       up = ebase + ou;
     }
     float4_t accg = float4_t{0.f, 0.f, 0.f, 0.f}, accu = accg;
-    for (int w = 0; w < n_win; ++w) {
+    // (several windows: every other round takes them in reverse order, so
+    // a round starts with the window the previous round ended with, which
+    // is still staged)
+    const bool rev = (((grp - wg) / n_wg) & 1) != 0;
+    for (int wi = 0; wi < n_win; ++wi) {
+      const int w = rev ? n_win - 1 - wi : wi;
       const int kg0 = w * win_kg, kg1 = min(n_kg, kg0 + win_kg);
-      if (n_win > 1) {
+      if (w != staged) {
         __syncthreads();
         stage_window<AM>(L, a, 8 * kg0, 8 * (kg1 - kg0), tid);
         __syncthreads();
+        staged = w;
       }
       if (valid) run_tile<BITS, AM>(gate, up, (int64_t)t * n_kg * CB, kg0 + kp, kg1, KP, kg0, L, lane, accg, accu);
     }
