@@ -675,13 +675,25 @@ DEVI void gate_up_item(const PfGemmArgs& a, const Stages& S, int* ex_lds, int g,
     if (act) {
       const unsigned char* st = S.get<P>();
       // the A fragment of the next row group is read before the current
-      // one's multiplies, so LDS latency hides under them
+      // one's multiplies, so LDS latency hides under them; with 2-bit blocks
+      // and at least four row groups the next block's weight fragments are
+      // also dequantized between this block's multiplies (one fragment per
+      // NRG / 4 row groups) instead of in a burst before them (3-bit and
+      // codebook blocks have no registers to spare for the second set)
+      constexpr bool SPREAD = BITS == 2 && NRG >= 4;
       half8_t A = *reinterpret_cast<const half8_t*>(st + xs[0]);
+      half8_t B[4];
+      if constexpr (SPREAD) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) B[m] = dequant<BITS>(bw[P][m], 0);
+      }
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        half8_t B[4];
+        half8_t Bn[4];
+        if constexpr (!SPREAD) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) B[m] = dequant<BITS>(bw[P][m], kb);
+          for (int m = 0; m < 4; ++m) B[m] = dequant<BITS>(bw[P][m], kb);
+        }
 #pragma unroll
         for (int rg = 0; rg < NRG; ++rg) {
           const bool last = kb == 3 && rg == NRG - 1;
@@ -690,7 +702,16 @@ DEVI void gate_up_item(const PfGemmArgs& a, const Stages& S, int* ex_lds, int g,
           __builtin_amdgcn_sched_barrier(0);  // (the read stays ahead of the multiplies)
 #pragma unroll
           for (int m = 0; m < 4; ++m) acc[rg][m] = mfma16x16x32(A, B[m], acc[rg][m]);
+          if constexpr (SPREAD) {
+            if (kb < 3 && (rg * 4) % NRG == 0) Bn[rg * 4 / NRG] = dequant<BITS>(bw[P][rg * 4 / NRG], kb + 1);
+          }
           A = An;
+        }
+        if constexpr (SPREAD) {
+          if (kb < 3) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) B[m] = Bn[m];
+          }
         }
       }
     }
@@ -857,14 +878,24 @@ DEVI void down_item(const PfGemmArgs& a, const Stages& S, float* rowf_lds, int g
     const unsigned char* st = S.get<P>();
     const int nj = min(4, nbK - 4 * s);
     // the A fragment of the next row group is read before the current
-    // one's multiplies, so LDS latency hides under them
+    // one's multiplies, so LDS latency hides under them; with 2-bit blocks
+    // and at least four row groups the next block's weight fragments are
+    // dequantized between this block's multiplies (as in gate/up)
+    constexpr bool SPREAD = BITS == 2 && NRG >= 4;
     half8_t A = *reinterpret_cast<const half8_t*>(st + 16 * lane);
+    half8_t B[4];
+    if constexpr (SPREAD) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) B[t] = dequant<BITS>(bw[P][M::chunk(t, 0)], M::frag(t, 0));
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (j >= nj) break;
-      half8_t B[4];
+      half8_t Bn[4];
+      if constexpr (!SPREAD) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) B[t] = dequant<BITS>(bw[P][M::chunk(t, j)], M::frag(t, j));
+        for (int t = 0; t < 4; ++t) B[t] = dequant<BITS>(bw[P][M::chunk(t, j)], M::frag(t, j));
+      }
 #pragma unroll
       for (int rg = 0; rg < NRG; ++rg) {
         const bool last = j == 3 && rg == NRG - 1;
@@ -873,7 +904,19 @@ DEVI void down_item(const PfGemmArgs& a, const Stages& S, float* rowf_lds, int g
         __builtin_amdgcn_sched_barrier(0);  // (the read stays ahead of the multiplies)
 #pragma unroll
         for (int t = 0; t < 4; ++t) acc[rg][t] = mfma16x16x32(A, B[t], acc[rg][t]);
+        if constexpr (SPREAD) {
+          if (j < 3 && (rg * 4) % NRG == 0) {
+            const int t = rg * 4 / NRG;
+            Bn[t] = dequant<BITS>(bw[P][M::chunk(t, j + 1)], M::frag(t, j + 1));
+          }
+        }
         A = An;
+      }
+      if constexpr (SPREAD) {
+        if (j < 3) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) B[t] = Bn[t];
+        }
       }
     }
   };
