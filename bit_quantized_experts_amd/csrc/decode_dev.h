@@ -481,7 +481,10 @@ DEVI void gu_items(const GuArgs& a, GuLds& L, int wg, int n_wg, uint32_t* h_read
         __syncthreads();
         staged = w;
       }
-      if (valid) run_tile<BITS, AM>(gate, up, (int64_t)t * n_kg * CB, kg0 + kp, kg1, KP, kg0, L, lane, accg, accu);
+      // k-group g goes to k-part g % KP in every window, so the parts stay
+      // within one k-group of each other however the windows split
+      const int first = kg0 + (kp - kg0 % KP + KP) % KP;
+      if (valid) run_tile<BITS, AM>(gate, up, (int64_t)t * n_kg * CB, first, kg1, KP, kg0, L, lane, accg, accu);
     }
     if (KP > 1) {
 #pragma unroll
