@@ -167,10 +167,12 @@ DEVI TopkLane topk_keys(const uint64_t (&key)[NPER], int E, int k, int32_t* idx_
   n = min(n, 64);
   // rank the candidates (lanes >= n hold 0, which is never larger); the
   // first k ranks are the result
+  // (each candidate read by every lane from LDS at once, a broadcast; the
+  // wavefront's own compaction stores are in order before these reads)
   const uint64_t mine = (lane < n) ? buf[lane] : 0ull;
   int rank = 0;
-#pragma unroll 4
-  for (int j = 0; j < n; ++j) rank += (readlane_u64(mine, j) > mine) ? 1 : 0;
+#pragma unroll 8
+  for (int j = 0; j < n; ++j) rank += (buf[j] > mine) ? 1 : 0;
   if (lane < n && rank < k) buf[64 + rank] = mine;
   const uint64_t kr = (lane < k) ? buf[64 + lane] : 0ull;
   const float my_v = key_value(kr);
