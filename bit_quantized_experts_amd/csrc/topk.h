@@ -56,13 +56,6 @@ DEVI int lanes_below(uint64_t m) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-DEVI double readlane_f64(double v, int l) {
-  const uint64_t b = __builtin_bit_cast(uint64_t, v);
-  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)b, l);
-  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(b >> 32), l);
-  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
-}
-
 DEVI uint64_t readlane_u64(uint64_t v, int l) {
   const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, l);
   const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), l);
@@ -180,8 +173,12 @@ DEVI TopkLane topk_keys(const uint64_t (&key)[NPER], int E, int k, int32_t* idx_
   const double m = (double)__builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(uint32_t, my_v)));
   double ev = 0.0;
   if (lane < k) ev = moe_exp64((double)my_v - m);
+  // S in rank order, the same in every lane: each lane puts its e_r in
+  // buf[r] (the candidates are no longer needed) and every lane adds them
+  // back from broadcast reads
+  if (lane < k) buf[lane] = __builtin_bit_cast(uint64_t, ev);
   double S = 0.0;
-  for (int r = 0; r < k; ++r) S += readlane_f64(ev, r);  // rank order, same in every lane
+  for (int r = 0; r < k; ++r) S += __builtin_bit_cast(double, buf[r]);
   TopkLane r{-1, 0.f};
   if (lane < k) {
     r.e = (my_e >= 0 && my_e < E) ? my_e : 0;  // (other only with non-finite logits, out of contract)
