@@ -980,38 +980,49 @@ __global__ __launch_bounds__(256, 2) void pf_down_kernel(PfGemmArgs a) {
 // ---------------------------------------------------------------------------
 // combine: y[t] = sum over the token's used pairs in rank order + shared row.
 // ---------------------------------------------------------------------------
-DEVI float4_t half4_to_float4(const _Float16* p) {
-  typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
-  const half4_t h = *reinterpret_cast<const half4_t*>(p);
-  return float4_t{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
-}
-
+// One wavefront per token (four per workgroup): lane l takes the 8 columns
+// 8 l + 512 j of chunk j.  The token's row positions and factors are
+// wave-uniform (scalar loads); the K + 1 rows of two chunks (16-byte loads)
+// are all issued before the first add.  The sum is formed in rank order, the
+// shared row last; skipped entries (position -1) are left out.
+template <int K>
 __global__ __launch_bounds__(256) void pf_combine_kernel(PfCombineArgs a) {
-  // every thread reads the token's row positions (one round trip), then all
-  // row factors and row pieces at once (a second one); the sum is formed in
-  // rank order, the shared row last.  Unused ranks (r >= k, skipped entries)
-  // load row 0 and are left out of the sum.
-  constexpr int NR = MOE_MAX_K + 1;
-  const int t = blockIdx.x, k = a.k;
+  constexpr int NR = K + 1;
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6)), lane = threadIdx.x & 63;
+  if (t >= a.T) return;
+  const int d = a.d;
   int pos[NR];
 #pragma unroll
-  for (int r = 0; r < MOE_MAX_K; ++r) {
-    const int p = a.slot_pos[(size_t)t * k + min(r, k - 1)];
-    pos[r] = r < k ? p : -1;
-  }
-  pos[MOE_MAX_K] = a.has_shared ? a.offsets[a.E] + t : -1;
+  for (int r = 0; r < K; ++r) pos[r] = a.slot_pos[(size_t)t * K + r];
+  pos[K] = a.has_shared ? a.offsets[a.E] + t : -1;
   float f[NR];
 #pragma unroll
   for (int r = 0; r < NR; ++r) f[r] = a.rowf[max(pos[r], 0)];
-  for (int c = 4 * threadIdx.x; c < a.d; c += 1024) {
-    float4_t v[NR];
+  for (int c0 = 8 * lane; c0 < d; c0 += 1024) {
+    const int c1 = min(c0 + 512, d - 8);  // (a second chunk past d re-reads the last columns, not stored)
+    half8_t v[2][NR];
 #pragma unroll
-    for (int r = 0; r < NR; ++r) v[r] = half4_to_float4(a.yh + (size_t)max(pos[r], 0) * a.d + c);
-    float4_t acc = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < NR; ++r) {
+      const _Float16* row = a.yh + (size_t)max(pos[r], 0) * d;
+      v[0][r] = *reinterpret_cast<const half8_t*>(row + c0);
+      v[1][r] = *reinterpret_cast<const half8_t*>(row + c1);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // (every load issued before the first add)
 #pragma unroll
-    for (int r = 0; r < NR; ++r)
-      if (pos[r] >= 0) acc += f[r] * v[r];
-    *reinterpret_cast<float4_t*>(a.y + (size_t)t * a.d + c) = acc;
+    for (int h = 0; h < 2; ++h) {
+      if (h == 1 && c0 + 512 >= d) break;
+      float4_t acc0 = float4_t{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+        if (pos[r] >= 0) {
+          const half8_t& x = v[h][r];
+          acc0 += f[r] * float4_t{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+          acc1 += f[r] * float4_t{(float)x[4], (float)x[5], (float)x[6], (float)x[7]};
+        }
+      float* yo = a.y + (size_t)t * d + (h ? c1 : c0);
+      *reinterpret_cast<float4_t*>(yo) = acc0;
+      *reinterpret_cast<float4_t*>(yo + 4) = acc1;
+    }
   }
 }
 
@@ -1139,6 +1150,17 @@ hipError_t launch_pf_down(const PfGemmArgs& a, int bits, int bk, int max_items, 
 }
 
 hipError_t launch_pf_combine(const PfCombineArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(pf_combine_kernel, dim3(a.T), dim3(256), 0, s, a);
+  if (a.T == 0) return hipSuccess;
+  if (a.d % 8 != 0 || a.k < 1 || a.k > MOE_MAX_K) return hipErrorInvalidValue;
+  const dim3 grid((a.T + 3) / 4), block(256);
+  switch (a.k) {
+#define MOE_COMBINE_CASE(K) \
+  case K: hipLaunchKernelGGL(pf_combine_kernel<K>, grid, block, 0, s, a); break;
+    MOE_COMBINE_CASE(1) MOE_COMBINE_CASE(2) MOE_COMBINE_CASE(3) MOE_COMBINE_CASE(4)
+    MOE_COMBINE_CASE(5) MOE_COMBINE_CASE(6) MOE_COMBINE_CASE(7) MOE_COMBINE_CASE(8)
+    MOE_COMBINE_CASE(9) MOE_COMBINE_CASE(10) MOE_COMBINE_CASE(11) MOE_COMBINE_CASE(12)
+    MOE_COMBINE_CASE(13) MOE_COMBINE_CASE(14) MOE_COMBINE_CASE(15) MOE_COMBINE_CASE(16)
+#undef MOE_COMBINE_CASE
+  }
   return hipGetLastError();
 }
