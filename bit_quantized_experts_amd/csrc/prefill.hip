@@ -582,6 +582,119 @@ __global__ __launch_bounds__(256) void pf_permute_kernel(PfGroupArgs a) {
   if (a.slot_pos) a.slot_pos[i] = p;
 }
 
+// Short chunks (at most PF_SMALL_T tokens and PF_SMALL_E experts): the work
+// of the three kernels above in one workgroup of 1024 threads, with the same
+// results (short chunks pay mostly the fixed costs of the layer's kernels).
+// The token bitmaps of every expert per 64-token tile stay in LDS; thread e
+// takes expert e's count, padded rows and work items, and the row offsets
+// and item positions come from a scan over the threads in expert order (a
+// lane scan per wavefront, then the sixteen wavefront totals); a pair's row
+// is offsets[e] + the tokens of e in earlier tiles + its rank in its tile.
+constexpr int PF_SMALL_T = 256, PF_SMALL_E = 1024;
+__global__ __launch_bounds__(1024) void pf_group_small_kernel(PfGroupArgs a) {
+  __shared__ unsigned long long bm[PF_SMALL_T / PF_T64][PF_SMALL_E];
+  __shared__ int off_lds[PF_SMALL_E];
+  __shared__ int wsum[2][16];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int E = a.E, T = a.T, k = a.k, n_tiles = (T + PF_T64 - 1) / PF_T64;
+  for (int i = tid; i < n_tiles * PF_SMALL_E; i += 1024) bm[i / PF_SMALL_E][i % PF_SMALL_E] = 0ull;
+  __syncthreads();
+  const int n_pairs = T * k;
+  for (int i = tid; i < n_pairs; i += 1024) {
+    const int t = i / k, e = a.idx[i];
+    if (e >= 0 && e < E) atomicOr(&bm[t / PF_T64][e], 1ull << (t % PF_T64));
+  }
+  __syncthreads();
+  const int e = tid;
+  int cnt = 0;
+  if (e < E)
+    for (int j = 0; j < n_tiles; ++j) cnt += __popcll(bm[j][e]);
+  const int pc = (cnt + a.pad - 1) / a.pad * a.pad;
+  const int ni = (pc + a.TM - 1) / a.TM;
+  int rs = pc, is = ni;  // inclusive scans within the wavefront
+  for (int o = 1; o < 64; o <<= 1) {
+    const int r2 = __shfl_up(rs, o, 64), i2 = __shfl_up(is, o, 64);
+    if (lane >= o) {
+      rs += r2;
+      is += i2;
+    }
+  }
+  if (lane == 63) {
+    wsum[0][wv] = rs;
+    wsum[1][wv] = is;
+  }
+  __syncthreads();
+  int rows_routed = 0, items_routed = 0, rb = 0, ib = 0;
+  for (int w = 0; w < 16; ++w) {
+    const int r = wsum[0][w], it = wsum[1][w];
+    if (w < wv) {
+      rb += r;
+      ib += it;
+    }
+    rows_routed += r;
+    items_routed += it;
+  }
+  const int roff = rb + rs - pc, ioff = ib + is - ni;
+  if (e < E) {
+    a.counts[e] = cnt;
+    a.offsets[e] = roff;
+    off_lds[e] = roff;
+    for (int p = roff + cnt; p < roff + pc; ++p) {
+      a.row_src[p] = -1;
+      if (a.row_tok) { a.row_tok[p] = 0; a.row_w[p] = 0.f; }
+    }
+    if (a.n_items)
+      for (int j = 0; j < ni; ++j) {
+        a.item_group[ioff + j] = e;
+        a.item_row0[ioff + j] = roff + j * a.TM;
+        a.item_rows[ioff + j] = min(a.TM, pc - j * a.TM);
+      }
+  }
+  const int rows_sh = a.has_shared ? (T + 15) / 16 * 16 : 0;
+  const int items_sh = (rows_sh + a.TM - 1) / a.TM;
+  if (tid == 0) {
+    a.offsets[E] = rows_routed;
+    if (a.n_items) {
+      a.offsets[E + 1] = rows_routed + rows_sh;
+      *a.n_items = items_routed + items_sh;
+    }
+  }
+  for (int t = tid; t < rows_sh; t += 1024) {
+    const int p = rows_routed + t;
+    a.row_src[p] = -1;
+    a.row_tok[p] = t < T ? t : 0;
+    a.row_w[p] = t < T ? 1.f : 0.f;
+  }
+  if (a.n_items)
+    for (int j = tid; j < items_sh; j += 1024) {
+      a.item_group[items_routed + j] = E;
+      a.item_row0[items_routed + j] = rows_routed + j * a.TM;
+      a.item_rows[items_routed + j] = min(a.TM, rows_sh - j * a.TM);
+    }
+  for (int p = rows_routed + tid; p < a.R_fill; p += 1024) a.row_src[p] = -1;
+  __syncthreads();  // every expert's offset in LDS
+  // a pair is used unless its id is outside [0, E) or repeats an earlier
+  // slot of the same token
+  for (int i = tid; i < n_pairs; i += 1024) {
+    const int t = i / k, r = i - t * k, ei = a.idx[i];
+    bool ok = ei >= 0 && ei < E;
+    for (int u = 0; u < r && ok; ++u) ok = a.idx[(size_t)t * k + u] != ei;
+    if (!ok) {
+      if (a.slot_pos) a.slot_pos[i] = -1;
+      continue;
+    }
+    const int tile = t / PF_T64, bit = t % PF_T64;
+    int p = off_lds[ei] + __popcll(bm[tile][ei] & ((1ull << bit) - 1ull));
+    for (int j = 0; j < tile; ++j) p += __popcll(bm[j][ei]);
+    a.row_src[p] = i;
+    if (a.row_tok) {
+      a.row_tok[p] = t;
+      a.row_w[p] = a.w ? a.w[i] : 1.f;
+    }
+    if (a.slot_pos) a.slot_pos[i] = p;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // gate/up grouped GEMM.  Workgroup: one work item (up to 128 rows of one
 // expert) x 128 intermediate columns; wave wv: all rows x columns
@@ -1109,6 +1222,10 @@ hipError_t launch_pf_router(const PfRouterArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_pf_group(const PfGroupArgs& a, hipStream_t s) {
+  if (a.T <= PF_SMALL_T && a.E <= PF_SMALL_E) {
+    hipLaunchKernelGGL(pf_group_small_kernel, dim3(1), dim3(1024), 0, s, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(pf_hist_kernel, dim3(a.n_tiles), dim3(64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -60,8 +60,12 @@ def _group(bqe, idx_np, E):
     return counts.cpu().numpy(), offsets.cpu().numpy(), perm.cpu().numpy()[:T * k]
 
 
+# chunks of up to 256 tokens with at most 1024 experts take the one-workgroup
+# grouping kernel, longer ones or more experts the three-kernel path: both
+# sides of each limit are here
 @pytest.mark.parametrize("T,E,k", [(9, 16, 2), (64, 16, 2), (65, 512, 10), (1000, 512, 10), (8192, 512, 10),
-                                   (300, 4096, 16), (77, 1, 1), (130, 3, 3)])
+                                   (300, 4096, 16), (77, 1, 1), (130, 3, 3), (17, 512, 10), (256, 512, 10),
+                                   (257, 512, 10), (256, 1024, 16), (100, 1025, 4)])
 def test_group_tokens_bitexact(bqe, T, E, k):
     say(f"[group] T={T} E={E} k={k}")
     if E == 512:
