@@ -587,14 +587,18 @@ int prefill_layer(const moe_layer* L, const float* x, int norm, float eps, int T
     ra.logits = (r && r->out_logits) ? r->out_logits : reinterpret_cast<float*>(ws + W.logits);
     ra.split = router_split(L, T);
     ra.part = reinterpret_cast<float*>(ws + W.rpart);
+    // a split router (short chunks) hands its slice sums straight to the
+    // selection kernel, which forms the logits and selects
+    const bool fused = pf_router_topk_ok(ra);
     timed_begin(5, s, &slot);
     serial_point(s);
-    HIPCHK(launch_pf_router(ra, s));
+    HIPCHK(launch_pf_router(ra, s, !fused));
     timed_end(slot, s);
     int32_t* oi = (r && r->out_idx) ? r->out_idx : reinterpret_cast<int32_t*>(ws + W.idx);
     float* ow = (r && r->out_w) ? r->out_w : reinterpret_cast<float*>(ws + W.w);
     serial_point(s);
-    HIPCHK(launch_topk(ra.logits, T, E, k, oi, ow, s));
+    if (fused) HIPCHK(launch_pf_router_topk(ra, k, oi, ow, s));
+    else HIPCHK(launch_topk(ra.logits, T, E, k, oi, ow, s));
     idx = oi;
     w = ow;
   }

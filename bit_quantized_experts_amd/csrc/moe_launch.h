@@ -313,7 +313,13 @@ hipError_t launch_pack_router(const float* W, int E, int d, _Float16* wh, _Float
 hipError_t launch_pack_hbound(const uint8_t* canon, int64_t canon_stride, int n_experts, int I, int d, int bits,
                               const uint8_t* grid, int32_t* hb, int32_t* ed, hipStream_t s);
 hipError_t launch_pf_prep(const PfPrepArgs& a, hipStream_t s);
-hipError_t launch_pf_router(const PfRouterArgs& a, hipStream_t s);
+// reduce = false leaves a split launch's slice sums in part for
+// launch_pf_router_topk (route.hip), which adds them, writes the logits and
+// selects; it takes split launches with E <= 512 and d <= 4096
+// (pf_router_topk_ok).
+hipError_t launch_pf_router(const PfRouterArgs& a, hipStream_t s, bool reduce = true);
+bool pf_router_topk_ok(const PfRouterArgs& a);
+hipError_t launch_pf_router_topk(const PfRouterArgs& a, int k, int32_t* idx, float* w, hipStream_t s);
 hipError_t launch_pf_group(const PfGroupArgs& a, hipStream_t s);
 hipError_t launch_pf_gate_up(const PfGemmArgs& a, int bits, int max_items, hipStream_t s);
 hipError_t launch_pf_down(const PfGemmArgs& a, int bits, int bk, int max_items, hipStream_t s);

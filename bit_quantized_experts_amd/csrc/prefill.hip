@@ -1211,10 +1211,10 @@ hipError_t launch_pf_prep(const PfPrepArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_pf_router(const PfRouterArgs& a, hipStream_t s) {
+hipError_t launch_pf_router(const PfRouterArgs& a, hipStream_t s, bool reduce) {
   MOE_LAUNCH(pf_router_kernel, dim3((a.T + 127) / 128, (a.E16 + PF_ET - 1) / PF_ET, a.split ? a.d / 256 : 1), dim3(512),
              0, s, a);
-  if (a.split) {
+  if (a.split && reduce) {
     const int64_t n = (int64_t)a.T * a.E;
     hipLaunchKernelGGL(pf_router_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
   }

@@ -27,6 +27,49 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   topk_wave_any(PtrRow{logits + (size_t)t * E}, E, k, idx + (size_t)t * k, w + (size_t)t * k, buf[threadIdx.x >> 6]);
 }
 
+// Split prefill router (short chunks), E <= 512: a token's partial sums
+// over the 256-column slices added in slice order from zero, scaled and
+// biased (the steps of the separate reduce kernel), written out, and the
+// token's top k taken from the wavefront's registers (as topk_kernel takes
+// it from memory); one wavefront per token, every load in flight at once.
+template <int MAXNS>
+__global__ __launch_bounds__(256) void pf_router_topk_kernel(PfRouterArgs a, int k, int32_t* __restrict__ idx,
+                                                             float* __restrict__ w) {
+  constexpr int NPER = 8;
+  __shared__ uint64_t buf[4][TOPK_BUF];
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6)), lane = threadIdx.x & 63;
+  if (t >= a.T) return;
+  const int E = a.E, ns = a.d / 256;
+  float v[NPER][MAXNS];
+  int ewv[NPER];
+  float bv[NPER];
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const int e = min(lane + 64 * i, E - 1);
+#pragma unroll
+    for (int z = 0; z < MAXNS; ++z) v[i][z] = a.part[((size_t)min(z, ns - 1) * a.T + t) * E + e];
+    ewv[i] = a.ew[e];
+    bv[i] = a.bias[e];
+  }
+  const int ext = a.ex[t];
+  uint64_t key[NPER];
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const int e = lane + 64 * i;
+    float tot = 0.f;
+#pragma unroll
+    for (int z = 0; z < MAXNS; ++z)
+      if (z < ns) tot += v[i][z];
+    const float l = ldexpf(tot, ext + ewv[i]) + bv[i];
+    key[i] = 0ull;  // 0: no expert
+    if (e < E) {
+      a.logits[(size_t)t * E + e] = l;
+      key[i] = sel_key(l, e);
+    }
+  }
+  topk_keys<NPER>(key, E, k, idx + (size_t)t * k, w + (size_t)t * k, buf[threadIdx.x >> 6]);
+}
+
 __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   __shared__ float ys[MOE_MAX_TOK_F16ACT][MOE_ROUTE_COLS];
   __shared__ int xe[MOE_MAX_TOK_F16ACT];  // slice exponent of each token
@@ -91,6 +134,17 @@ hipError_t launch_combine(const float* part, int S, int64_t stride, int T, int d
   const int n4 = T * d / 4;
   if (n4 == 0) return hipSuccess;
   hipLaunchKernelGGL(combine_kernel, dim3((n4 + 255) / 256), dim3(256), 0, s, part, S, stride, n4, y);
+  return hipGetLastError();
+}
+
+bool pf_router_topk_ok(const PfRouterArgs& a) { return a.split && a.E <= 512 && a.d / 256 <= 16; }
+
+hipError_t launch_pf_router_topk(const PfRouterArgs& a, int k, int32_t* idx, float* w, hipStream_t s) {
+  if (!pf_router_topk_ok(a) || k < 1 || k > a.E) return hipErrorInvalidValue;
+  if (a.T == 0) return hipSuccess;
+  const dim3 grid((a.T + 3) / 4), block(256);
+  if (a.d / 256 <= 10) hipLaunchKernelGGL(pf_router_topk_kernel<10>, grid, block, 0, s, a, k, idx, w);
+  else hipLaunchKernelGGL(pf_router_topk_kernel<16>, grid, block, 0, s, a, k, idx, w);
   return hipGetLastError();
 }
 
