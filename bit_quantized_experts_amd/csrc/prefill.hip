@@ -582,9 +582,10 @@ __global__ __launch_bounds__(256) void pf_permute_kernel(PfGroupArgs a) {
   if (a.slot_pos) a.slot_pos[i] = p;
 }
 
-// Short chunks (at most PF_SMALL_T tokens and PF_SMALL_E experts): the work
-// of the three kernels above in one workgroup of 1024 threads, with the same
-// results (short chunks pay mostly the fixed costs of the layer's kernels).
+// Short chunks (at most PF_SMALL_T tokens, PF_SMALL_E experts and MOE_MAX_K
+// ranks): the work of the three kernels above in one workgroup of 1024
+// threads, with the same results (short chunks pay mostly the fixed costs of
+// the layer's kernels).
 // The token bitmaps of every expert per 64-token tile stay in LDS; thread e
 // takes expert e's count, padded rows and work items, and the row offsets
 // and item positions come from a scan over the threads in expert order (a
@@ -592,17 +593,33 @@ __global__ __launch_bounds__(256) void pf_permute_kernel(PfGroupArgs a) {
 // is offsets[e] + the tokens of e in earlier tiles + its rank in its tile.
 constexpr int PF_SMALL_T = 256, PF_SMALL_E = 1024;
 __global__ __launch_bounds__(1024) void pf_group_small_kernel(PfGroupArgs a) {
+  constexpr int PP = PF_SMALL_T * MOE_MAX_K / 1024;  // pairs per thread
   __shared__ unsigned long long bm[PF_SMALL_T / PF_T64][PF_SMALL_E];
   __shared__ int off_lds[PF_SMALL_E];
+  __shared__ int ids[PF_SMALL_T * MOE_MAX_K];
   __shared__ int wsum[2][16];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int E = a.E, T = a.T, k = a.k, n_tiles = (T + PF_T64 - 1) / PF_T64;
-  for (int i = tid; i < n_tiles * PF_SMALL_E; i += 1024) bm[i / PF_SMALL_E][i % PF_SMALL_E] = 0ull;
-  __syncthreads();
   const int n_pairs = T * k;
-  for (int i = tid; i < n_pairs; i += 1024) {
-    const int t = i / k, e = a.idx[i];
-    if (e >= 0 && e < E) atomicOr(&bm[t / PF_T64][e], 1ull << (t % PF_T64));
+  // the ids (and gate weights) of this thread's pairs i = tid + 1024 j are
+  // loaded first and kept in registers; their loads overlap the clearing
+  int myid[PP];
+  float myw[PP];
+#pragma unroll
+  for (int j = 0; j < PP; ++j) {
+    const int i = min(tid + 1024 * j, max(n_pairs - 1, 0));
+    myid[j] = a.idx[i];
+    myw[j] = a.w ? a.w[i] : 1.f;
+  }
+  for (int i = tid; i < n_tiles * PF_SMALL_E; i += 1024) bm[i / PF_SMALL_E][i % PF_SMALL_E] = 0ull;
+#pragma unroll
+  for (int j = 0; j < PP; ++j)
+    if (tid + 1024 * j < n_pairs) ids[tid + 1024 * j] = myid[j];
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < PP; ++j) {
+    const int i = tid + 1024 * j, t = i / k, e = myid[j];
+    if (i < n_pairs && e >= 0 && e < E) atomicOr(&bm[t / PF_T64][e], 1ull << (t % PF_T64));
   }
   __syncthreads();
   const int e = tid;
@@ -675,10 +692,13 @@ __global__ __launch_bounds__(1024) void pf_group_small_kernel(PfGroupArgs a) {
   __syncthreads();  // every expert's offset in LDS
   // a pair is used unless its id is outside [0, E) or repeats an earlier
   // slot of the same token
-  for (int i = tid; i < n_pairs; i += 1024) {
-    const int t = i / k, r = i - t * k, ei = a.idx[i];
+#pragma unroll
+  for (int j = 0; j < PP; ++j) {
+    const int i = tid + 1024 * j;
+    if (i >= n_pairs) break;
+    const int t = i / k, r = i - t * k, ei = myid[j];
     bool ok = ei >= 0 && ei < E;
-    for (int u = 0; u < r && ok; ++u) ok = a.idx[(size_t)t * k + u] != ei;
+    for (int u = 0; u < r && ok; ++u) ok = ids[t * k + u] != ei;
     if (!ok) {
       if (a.slot_pos) a.slot_pos[i] = -1;
       continue;
@@ -689,7 +709,7 @@ __global__ __launch_bounds__(1024) void pf_group_small_kernel(PfGroupArgs a) {
     a.row_src[p] = i;
     if (a.row_tok) {
       a.row_tok[p] = t;
-      a.row_w[p] = a.w ? a.w[i] : 1.f;
+      a.row_w[p] = myw[j];
     }
     if (a.slot_pos) a.slot_pos[i] = p;
   }
@@ -1222,7 +1242,7 @@ hipError_t launch_pf_router(const PfRouterArgs& a, hipStream_t s, bool reduce) {
 }
 
 hipError_t launch_pf_group(const PfGroupArgs& a, hipStream_t s) {
-  if (a.T <= PF_SMALL_T && a.E <= PF_SMALL_E) {
+  if (a.T <= PF_SMALL_T && a.E <= PF_SMALL_E && a.k <= MOE_MAX_K) {
     hipLaunchKernelGGL(pf_group_small_kernel, dim3(1), dim3(1024), 0, s, a);
     return hipGetLastError();
   }
