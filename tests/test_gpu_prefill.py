@@ -126,9 +126,13 @@ def test_prefill_tiny(bqe, bits, Is, monkeypatch):
 
 
 def test_prefill_odd_shapes(bqe):
-    # E not a multiple of 16, intermediate sizes not multiples of 128, k = E
+    # E not a multiple of 16, intermediate sizes not multiples of 128, k = E;
+    # the short-chunk router selection with 16 column slices (d = 4096) and
+    # the separate reduce and top-k kernels it leaves to wider inputs
+    # (d = 4608) and to more than 512 experts
     for kw in (dict(E=20, k=3, I=96, Is=32), dict(E=1, k=1, I=32, Is=0), dict(E=5, k=5, I=160, Is=288),
-               dict(d=512, E=40, k=4, I=64, Is=64)):
+               dict(d=512, E=40, k=4, I=64, Is=64), dict(d=4096, E=64, k=4, I=64, Is=64),
+               dict(d=4608, E=48, k=3, I=64, Is=0), dict(d=512, E=520, k=6, I=64, Is=64)):
         wl = mi.small(mi.WORKLOADS["tiny"], zipf_s=None, **kw)
         L = packed_layer(wl, 0)
         x = mi.activations(wl, T=150, stream=17)
