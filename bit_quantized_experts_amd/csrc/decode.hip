@@ -13,8 +13,19 @@ template <int BITS, int NPER, int AM>
 __global__ __launch_bounds__(64 * GU_NW) void gu_decode_kernel(GuArgs a) {
   __shared__ GuLds L;
   load_grid<BITS>(a.X.grid16, threadIdx.x, 64 * GU_NW);  // (the selection's barriers publish it)
-  gu_select<BITS, NPER, AM>(a, L, blockIdx.x == 0, blockIdx.x == 0);
-  gu_items<BITS, AM>(a, L, blockIdx.x, gridDim.x, nullptr);
+  // the first sh_wgs workgroups run the shared expert's items (they do not
+  // depend on the routing, so no selection delays them); the others select
+  // and run the routed experts' items (with sh_wgs = 0, every workgroup
+  // selects and runs its share of all items)
+  const int nsh = a.sh_wgs;
+  if ((int)blockIdx.x < nsh) {
+    gu_prologue_shared<AM>(a, L);
+    gu_items<BITS, AM>(a, L, blockIdx.x, nsh, nullptr, 1);
+  } else {
+    const bool first = (int)blockIdx.x == nsh;
+    gu_select<BITS, NPER, AM>(a, L, first, first);
+    gu_items<BITS, AM>(a, L, blockIdx.x - nsh, gridDim.x - nsh, nullptr, nsh > 0 ? 2 : 0);
+  }
 }
 
 // down: workgroup = (row group, split), the slot list from the workspace.

@@ -419,12 +419,38 @@ DEVI void gu_select(const GuArgs& a, GuLds& L, bool publish_routing, bool publis
   }
 }
 
+// Workgroups that run only the shared expert's items need no selection:
+// their prologue loads the divisors, the slice exponents and the first
+// activation window, as gu_select does for the others.
+template <int AM>
+DEVI void gu_prologue_shared(const GuArgs& a, GuLds& L) {
+  const int tid = opaque_tid();
+  const int T = a.T, n_kg = a.n_kg, n_win = gu_windows<AM>(n_kg);
+  const float rnv = (tid >= 64 && tid < 64 + T) ? a.rnorm[tid - 64] : 1.0f;
+  const int n_sx = 16 * (a.d / MOE_ROUTE_COLS);
+  int sxv[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = min(tid + 512 * h, n_sx - 1);
+    sxv[h] = a.x.sx[(size_t)(i >> 4) * MOE_XSX_STRIDE + (i & 15)];
+  }
+  const int win_kg = (n_kg + n_win - 1) / n_win;
+  WindowRegs win;
+  window_load<AM>(win, a, 0, 8 * win_kg, tid);
+  window_store<AM>(win, L, 8 * win_kg, tid);
+  if (tid >= 64 && tid < 80) L.rn[tid - 64] = 1.0f / rnv;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    if (tid + 512 * h < n_sx) (&L.sx[0][0])[tid + 512 * h] = sxv[h];
+  lds_barrier();  // the window, divisors and exponents are staged
+}
+
 // The gate/up work items of one workgroup (wg of n_wg): a work item is
 // (slot u, tile t of 16 intermediate rows).  With h_ready, each finished
 // item adds one to its slot's counter (h_ready + u * MOE_CTR_STRIDE) once its
 // h values are stored (a consumer inside the same kernel waits on them).
 template <int BITS, int AM>
-DEVI void gu_items(const GuArgs& a, GuLds& L, int wg, int n_wg, uint32_t* h_ready) {
+DEVI void gu_items(const GuArgs& a, GuLds& L, int wg, int n_wg, uint32_t* h_ready, int cls = 0) {
   constexpr int64_t CB = moe_chunk_bytes(BITS);
   const int tid = opaque_tid(), lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -435,7 +461,11 @@ DEVI void gu_items(const GuArgs& a, GuLds& L, int wg, int n_wg, uint32_t* h_read
   const int n_kg = a.n_kg;
   const int n_win = gu_windows<AM>(n_kg);
   const int win_kg = (n_kg + n_win - 1) / n_win;  // k-groups per window
-  const int n_items = tiles_s + L.S.n_routed * tiles_r;
+  // items of this call: cls 0 all (shared first), 1 the shared expert's only
+  // (no slot list needed), 2 the routed experts' only
+  const int i_lo = cls == 2 ? tiles_s : 0;
+  const int i_hi = cls == 1 ? tiles_s : tiles_s + L.S.n_routed * tiles_r;
+  const int n_items = i_hi - i_lo;
   int KP = 8;
   while (KP > 1 && (KP > n_kg || n_items * KP > n_wg * GU_NW)) KP >>= 1;
   const int G = GU_NW / KP, jw = wv / KP, kp = wv - jw * KP;
@@ -443,8 +473,8 @@ DEVI void gu_items(const GuArgs& a, GuLds& L, int wg, int n_wg, uint32_t* h_read
   int staged = 0;  // the window in LDS (gu_select stages the first)
 
   for (int grp = wg; grp * G < n_items; grp += n_wg) {
-    const int item = grp * G + jw;
-    const bool valid = item < n_items;
+    const int item = i_lo + grp * G + jw;
+    const bool valid = item < i_hi;
     int u = 0, t = 0;
     const uint8_t* gate = nullptr;
     const uint8_t* up = nullptr;

@@ -493,6 +493,14 @@ int decode_layer(const moe_layer* L, const LayerInput& in, float eps, int T, flo
     int n_wg = env_int("MOE_GU_WGS", cu_count());
     if (n_wg > max_items) n_wg = max_items;
     if (n_wg < 1) n_wg = 1;
+    // workgroups set apart for the shared expert's items (one per four of
+    // its 16-row tiles: two k-parts per item), which then start without
+    // waiting for the selection
+    int sh = ga.has_shared ? env_int("MOE_GU_SHARED_WGS", (L->Is / 16 + 3) / 4) : 0;
+    if (sh < 0) sh = 0;
+    if (sh > L->Is / 16) sh = L->Is / 16;
+    if (sh > n_wg / 4) sh = n_wg / 4;
+    ga.sh_wgs = sh;
     timed_begin(0, s, &slot);
     serial_point(s);
     HIPCHK(launch_gu_decode(ga, n_wg, s));

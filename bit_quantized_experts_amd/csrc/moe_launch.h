@@ -111,6 +111,7 @@ struct GuArgs {
   float* hbuf;      // ws [MAX_SLOTS][hI/16][R][16] fp32 h = w silu(g) u, R = moe_am_tokens(am)
   int32_t E, I, Is, T, d, n_kg, bits, hI, code_off, has_shared;
   int32_t am;  // activation rows (MOE_AM_*)
+  int32_t sh_wgs;  // workgroups that run only the shared expert's items (0: none)
 };
 
 struct DownArgs {

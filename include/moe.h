@@ -325,6 +325,10 @@ int moe_workspace_status(const void *ws, size_t ws_bytes, int *status, void *str
  * the same value).  Defaults in brackets.
  *   MOE_GU_WGS       decode gate/up workgroups [the CU count, at most the
  *                    number of 16-row tiles]
+ *   MOE_GU_SHARED_WGS  of those, the workgroups that run only the shared
+ *                    expert's items, starting without the selection [one
+ *                    per four of its 16-row tiles; 0 = every workgroup
+ *                    selects and takes a share of all items]
  *   MOE_DOWN_SPLITS  decode down-projection splits [2 x CUs / row groups,
  *                    clamped to 1..8 and to the slot count]
  *   MOE_DOWN_WAVES   wavefronts per decode down workgroup [8; 1..8]
