@@ -295,6 +295,24 @@ def bench_prefill(args):
     achieved = flops[dom] / kdur[dom] / 1e12
     gemm_util = (gu_flops + dn_flops) / (kdur["gate_up"] + kdur["down"]) / 1e12 / MFMA_F16_PEAK_TFLOPS
     counts = np.bincount(idx_np.reshape(-1), minlength=wl.E)
+    # algorithmic bytes of the routing taken (each touched expert once); a
+    # short chunk's grouped GEMMs do too few flops per byte to be bound by the
+    # matrix cores (below 2.5 PFLOP/s / 8 TB/s = 312 flop/B): its roofline is
+    # then HBM, the dominant kernel's weight bytes over its duration
+    total_bytes, gu_b, dn_b = algorithmic_bytes_decode(wl, idx_np[None], T)
+    wbytes = {"gate_up": float(gu_b[0]), "down": float(dn_b[0])}
+    for n in ("gate_up", "down"):
+        kernels[n]["bytes_per_launch"] = wbytes[n]
+        kernels[n]["GBps"] = wbytes[n] / kdur[n] / 1e9
+    hbm_bound = flops[dom] / wbytes[dom] < MFMA_F16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if hbm_bound:
+        ach = wbytes[dom] / kdur[dom] / 1e9
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": ach / HBM_PEAK_GBS, "traffic": None}
+    else:
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": achieved / MFMA_F16_PEAK_TFLOPS,
+                    "traffic": measured_traffic(wl.name, dom) if T == wl.T else None}
 
     cpu = None
     if args.cpu_tokens > 0:
@@ -325,10 +343,10 @@ def bench_prefill(args):
                     "note": "512 MB written before each step (Infinity Cache emptied)"},
         "back_to_back": {"ms_per_step": sec_b2b * 1e3, "value": T / sec_b2b},
         "grouped_gemm_mfma_util": gemm_util,
+        "hbm_GBps": total_bytes / sec_per_step / 1e9,
+        "bytes_per_step": float(total_bytes),
         "tokens_per_expert": {"max": int(counts.max()), "empty_experts": int((counts == 0).sum())},
-        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / MFMA_F16_PEAK_TFLOPS,
-                     "traffic": measured_traffic(wl.name, dom) if T == wl.T else None},
+        "roofline": roofline,
         "kernels": kernels,
         "cpu_baseline": cpu,
     }
@@ -826,6 +844,15 @@ def main():
     log("prefill ...")
     configs["prefill_T8192"] = bench_prefill(args)
     torch.cuda.empty_cache()
+    # short chunks (several conversations decoded together, or a short
+    # prompt): the same layer over 32 and 256 tokens
+    for Ts in (32, 256):
+        log(f"prefill T={Ts} ...")
+        a_s = argparse.Namespace(**vars(args))
+        a_s.T = Ts
+        a_s.cpu_tokens = min(args.cpu_tokens, 16)
+        configs[f"prefill_T{Ts}"] = bench_prefill(a_s)
+        torch.cuda.empty_cache()
     log("layer_t1_cb3 ...")
     configs["layer_t1_cb3"] = bench_layer_t1(args, "layer_t1_cb3")
     torch.cuda.empty_cache()
